@@ -1,0 +1,125 @@
+"""Plant plausible mistakes in the oracle (on the CPU, by patching it) and
+check that at least one pin catches each of them."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.lora_oracle as O
+from oracle_pins import ALL_PINS
+
+
+def _caught(monkeypatch_ctx):
+    failures = 0
+    for pin in ALL_PINS:
+        try:
+            pin(O)
+        except Exception:
+            failures += 1
+    return failures
+
+
+def _orig(name):
+    return getattr(O, name)
+
+
+def mut_scale_padded_rank(wl_rank, alpha, rs):
+    # uses a fixed padded rank instead of the adapter's own rank
+    return alpha / (math.sqrt(64) if rs else 64)
+
+
+def mut_scale_no_sqrt(rank, alpha, rs):
+    return alpha / rank
+
+
+def mut_scale_inverted(rank, alpha, rs):
+    return (math.sqrt(rank) if rs else rank) / alpha
+
+
+def _forward_factory(kind):
+    base = O.lora_forward_rows
+
+    def fwd(wl, rows=None, y_in=None):
+        if rows is None:
+            rows = range(wl.T)
+        rows = list(rows)
+        src = wl.y_in if y_in is None else y_in
+        out = base(wl, rows, y_in=y_in)
+        d = out - np.asarray(src, np.float64)[rows]
+        if kind == "sign":
+            return np.asarray(src, np.float64)[rows] - d
+        if kind == "drop_delta_for_last_slice":
+            off = sum(wl.out_features[:-1])
+            out[:, off:] = np.asarray(src, np.float64)[rows][:, off:]
+            return out
+        if kind == "off_by_one_id":
+            wl2 = type(wl)(**{**wl.__dict__, "ids": np.where(wl.ids >= 0,
+                            (wl.ids + 1) % max(1, len(wl.slots)), wl.ids).astype(np.int32)})
+            return base(wl2, rows, y_in=y_in)
+        if kind == "none_rows_zeroed":
+            out[np.asarray(wl.ids)[rows] < 0] = 0.0
+            return out
+        raise AssertionError(kind)
+    return fwd
+
+
+def _meta_factory(kind):
+    base = O.build_meta
+
+    def bm(ids, prefill, R, bgmv_max_rank=64):
+        m = base(ids, prefill, R, bgmv_max_rank)
+        if kind == "unstable":
+            m["sgmv_perm"] = list(reversed(m["sgmv_perm"]))
+        elif kind == "rank_rule_ignored":
+            m = base(ids, prefill, 0, bgmv_max_rank)
+        elif kind == "prefill_ignored":
+            m = base(ids, [0] * len(ids), R, bgmv_max_rank)
+        elif kind == "seg_start_by_len":
+            m["seg_starts"] = list(m["seg_lens"])
+        return m
+    return bm
+
+
+def _pool_factory(kind):
+    base = O.expected_pool
+
+    def ep(wl):
+        p = base(wl)
+        for a in p:
+            if kind == "no_padding_zero":
+                r = wl.slots[a].rank
+                p[a]["A"][0][r:] = 1.0
+            elif kind == "unfolded":
+                p[a]["B"] = [b / p[a]["scale_f32"] for b in p[a]["B"]]
+        return p
+    return ep
+
+
+def _rne_trunc(a):
+    a32 = np.ascontiguousarray(np.asarray(a, np.float32))
+    return (a32.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+MUTATIONS = {
+    "scale_padded_rank": ("scaling", mut_scale_padded_rank),
+    "scale_no_sqrt": ("scaling", mut_scale_no_sqrt),
+    "scale_inverted": ("scaling", mut_scale_inverted),
+    "delta_sign": ("lora_forward_rows", _forward_factory("sign")),
+    "delta_dropped_last_slice": ("lora_forward_rows", _forward_factory("drop_delta_for_last_slice")),
+    "delta_wrong_adapter": ("lora_forward_rows", _forward_factory("off_by_one_id")),
+    "none_rows_zeroed": ("lora_forward_rows", _forward_factory("none_rows_zeroed")),
+    "builder_unstable": ("build_meta", _meta_factory("unstable")),
+    "builder_rank_rule_ignored": ("build_meta", _meta_factory("rank_rule_ignored")),
+    "builder_prefill_ignored": ("build_meta", _meta_factory("prefill_ignored")),
+    "builder_seg_starts": ("build_meta", _meta_factory("seg_start_by_len")),
+    "pool_padding_not_zero": ("expected_pool", _pool_factory("no_padding_zero")),
+    "pool_unfolded": ("expected_pool", _pool_factory("unfolded")),
+    "bf16_truncation": ("f32_to_bf16_rne", _rne_trunc),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    assert _caught(monkeypatch) > 0, f"no pin caught mutation {name}"
