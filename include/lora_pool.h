@@ -1,0 +1,244 @@
+/*
+ * lora_pool.h - C ABI of the MI355X (gfx950) multi-LoRA delta library.
+ *
+ * For a batch whose rows each name an adapter slot (or none), one shared base
+ * projection output y = W x is updated in place:
+ *
+ *     y[t, off_s : off_s + out_s] += s_a * B_{a,s} (A_{a,s} x_t)   for a = ids[t] >= 0
+ *
+ * as a two-stage grouped computation: shrink (x -> v, length R per slice) then
+ * expand (v -> out).  SGMV handles contiguous segments of tokens sharing an
+ * adapter (prefill), BGMV per-token adapter indices (decode).
+ *
+ * Pages this follows (cited by title and section):
+ *  [TGI]  "Text Generation Inference 多 LoRA 适配器服务实战: LORA_ADAPTERS 配置与
+ *         SGMV/BGMV 内核加速原理": implementation step 3 (scale alpha/r or
+ *         alpha/sqrt(r) for rsLoRA, folded into lora_B at load; rank padding for
+ *         the kernels' vector width), step 4 (prefill -> SGMV segments, decode ->
+ *         BGMV per token; SGMV whenever the rank exceeds the BGMV limit; the four
+ *         shrink/expand operations), step 5 (uneven q/k/v output slices).
+ *  [vLLM] "vLLM 怎么在离线推理中为单次请求挂载不同 LoRA 适配器": step 2
+ *         (max_loras pre-allocated slots, max_lora_rank slot size), LoRARequest
+ *         rules (a None request runs the base model), limits (the slot rank
+ *         must cover every adapter's rank).
+ *  [QA]   "Multi-LoRA serving: 一基座, 多 adapter": direct answer (delta W = B A;
+ *         the base GEMM runs once per batch and a grouped kernel adds each
+ *         row's B(Ax) by adapter id).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Ownership: every device buffer (pool, x, y, v, metadata, workspace) is
+ *    allocated and freed by the caller.  The library allocates no device
+ *    memory and keeps no device state between calls.
+ *  - Streams: `stream` is a hipStream_t (NULL = the null stream).  Device work
+ *    is enqueued asynchronously on it; no call synchronises except
+ *    lora_pool_load with host sources (documented there).
+ *  - Errors: functions return LORA_OK (0) or a negative lora_status; the
+ *    message of the last failure on the calling thread is returned by
+ *    lora_last_error().  All argument validation happens before any HIP call,
+ *    so every error path can be exercised without a GPU.  Device-resident
+ *    metadata cannot be validated on the host: kernels skip (never read or
+ *    write) rows whose token index is outside [0, T) or whose adapter slot is
+ *    outside [0, max_loras), and clamp segments to the row list.
+ *  - Aliasing: y is updated in place; x must not overlap y; v must not overlap
+ *    x, y or the pool.
+ *  - Alignment: in_features, every out_features[s] and max_lora_rank must be
+ *    multiples of 8; every device pointer must be 16-byte aligned.
+ *  - dtype: x, y, A_pool and B_pool share one element type (fp32 or bf16);
+ *    v and all accumulation are fp32; y is rounded once (nearest-even) to its
+ *    dtype after adding the fp32 delta to the fp32 value of y.
+ *
+ * Layouts (row-major; R = max_lora_rank, K = in_features, S = num_slices,
+ * O = sum of out_features, off_s = sum of out_features[0..s-1]):
+ *    x       [T][K]
+ *    y       [T][O]               slice s occupies columns off_s .. off_s+out_s-1
+ *    A_pool  [max_loras][S][R][K] rows r..R-1 of a slot/slice are zero
+ *    B_pool  [max_loras][O][R]    row off_s+j of slot a holds s_a * B_{a,s}[j][:]
+ *                                 (columns r..R-1 zero), i.e. the peft lora_B
+ *                                 [out, r] layout, scaled and zero-padded
+ *    v       [rows][S][R] fp32    row i belongs to the i-th entry of the row list
+ */
+#ifndef LORA_POOL_H
+#define LORA_POOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_POOL_ABI_VERSION 1
+#define LORA_MAX_SLICES 8
+/* [TGI] step 4 names a BGMV rank limit without a value; 64 covers the ranks
+ * the kernels are built for.  Pass bgmv_max_rank <= 0 to lora_build_meta /
+ * lora_apply to use it. */
+#define LORA_BGMV_MAX_RANK_DEFAULT 64
+
+typedef enum {
+  LORA_OK = 0,
+  LORA_E_ARG = -1,        /* null pointer, negative size, bad flag */
+  LORA_E_DTYPE = -2,      /* unknown dtype */
+  LORA_E_SHAPE = -3,      /* inconsistent sizes, too many slices, capacity too small */
+  LORA_E_ALIGN = -4,      /* size not a multiple of 8 or pointer not 16-byte aligned */
+  LORA_E_RANK = -5,       /* adapter rank > max_lora_rank ([vLLM] limits) or <= 0 */
+  LORA_E_ID = -6,         /* adapter id < -1 or >= max_loras, or bad slot index */
+  LORA_E_WORKSPACE = -7,  /* workspace or staging buffer too small */
+  LORA_E_HIP = -8         /* a HIP runtime call failed */
+} lora_status;
+
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+/* Geometry of one adapter pool (one projection, possibly fused slices). */
+typedef struct {
+  int32_t dtype;                             /* lora_dtype */
+  int32_t max_loras;                         /* slots ([vLLM] step 2), >= 1 */
+  int32_t max_lora_rank;                     /* R: rank every slot is padded to */
+  int32_t in_features;                       /* K */
+  int32_t num_slices;                        /* S in [1, LORA_MAX_SLICES] */
+  int32_t out_features[LORA_MAX_SLICES];     /* out_s, s < S */
+} lora_pool_desc;
+
+/* Host-side metadata produced by lora_build_meta ([TGI] step 4).  The caller
+ * owns all arrays; capacities: sgmv_perm, bgmv_tok, bgmv_ids >= T entries;
+ * seg_starts, seg_lens, seg_ids >= max_loras entries (one segment per distinct
+ * adapter at most, since a segment is a maximal run of equal id). */
+typedef struct {
+  int32_t num_sgmv_rows;  /* out: entries of sgmv_perm */
+  int32_t num_segs;       /* out: entries of seg_* */
+  int32_t num_bgmv_rows;  /* out: entries of bgmv_tok / bgmv_ids */
+  int32_t reserved;
+  int32_t* sgmv_perm;     /* token indices of SGMV rows sorted by (id, token) */
+  int32_t* seg_starts;    /* offset of each segment into sgmv_perm */
+  int32_t* seg_lens;      /* rows per segment (> 0) */
+  int32_t* seg_ids;       /* adapter slot per segment, strictly increasing */
+  int32_t* bgmv_tok;      /* token indices of BGMV rows sorted by (id, token) */
+  int32_t* bgmv_ids;      /* adapter slot per BGMV row */
+} lora_meta;
+
+/* ------------------------------------------------------------------ misc */
+
+/* Message of the last failure on this thread ("" if none).  Never NULL. */
+const char* lora_last_error(void);
+/* LORA_POOL_ABI_VERSION of the loaded library. */
+int32_t lora_abi_version(void);
+
+/* ------------------------------------------------------------------ pool */
+
+/* Check a descriptor: dtype, max_loras >= 1, 1 <= S <= 8, K, out_s and R
+ * positive multiples of 8.  Returns LORA_OK or an error. */
+int32_t lora_pool_validate(const lora_pool_desc* desc);
+
+/* Bytes of A_pool (max_loras*S*R*K*e) and B_pool (max_loras*O*R*e) for a valid
+ * descriptor ([vLLM] step 2: every slot is pre-allocated at the slot rank); a
+ * negative lora_status for an invalid one. */
+int64_t lora_pool_bytes_A(const lora_pool_desc* desc);
+int64_t lora_pool_bytes_B(const lora_pool_desc* desc);
+
+/* The scale an adapter's B is multiplied by at load ([TGI] step 3):
+ * alpha / r, or alpha / sqrt(r) with use_rslora, evaluated in double and
+ * rounded to float.  r is the adapter's own rank, never the padded rank.
+ * Returns NaN for r <= 0. */
+float lora_scaling(int32_t r, float alpha, int32_t use_rslora);
+
+/* Load one slice of one adapter into slot `slot` ([TGI] step 3; [vLLM] limits).
+ *   A_src  [r][K] in the pool dtype (peft lora_A.weight layout)
+ *   B_src  [out_s][r] in the pool dtype (peft lora_B.weight layout)
+ * Writes A_pool[slot][slice][0:r][:] = A_src and rows r..R-1 = 0;
+ * B_pool[slot][off_s + j][k] = round_dtype((float)B_src[j][k] * lora_scaling())
+ * for k < r (one fp32 multiply, one nearest-even rounding), 0 for k >= r.
+ * src_on_device = 1: A_src/B_src are device pointers; the work is one kernel
+ * on `stream` (asynchronous).  src_on_device = 0: host pointers; the padded,
+ * folded slices are staged in host memory and copied; the call returns after
+ * the copy has completed.  Errors: LORA_E_RANK if r <= 0 or r > R, LORA_E_ID if
+ * slot/slice is out of range, LORA_E_ARG on null pointers. */
+int32_t lora_pool_load(const lora_pool_desc* desc, void* A_pool, void* B_pool,
+                       int32_t slot, int32_t slice, const void* A_src, const void* B_src,
+                       int32_t r, float alpha, int32_t use_rslora, int32_t src_on_device,
+                       void* stream);
+
+/* Zero every slice of slot `slot` in A_pool and B_pool (asynchronous, on
+ * stream).  A cleared slot adds nothing. */
+int32_t lora_pool_clear(const lora_pool_desc* desc, void* A_pool, void* B_pool,
+                        int32_t slot, void* stream);
+
+/* ------------------------------------------------------------- metadata */
+
+/* Host-only, bit-exact metadata builder ([TGI] step 4).
+ *   ids[T]      adapter slot per token, -1 = no adapter ([vLLM] None request)
+ *   prefill[T]  1 for prefill tokens, 0 for decode tokens (may be NULL = all 0)
+ * A token with id >= 0 goes to SGMV if prefill[t] != 0 or
+ * max_lora_rank > bgmv_max_rank (<= 0 selects LORA_BGMV_MAX_RANK_DEFAULT),
+ * otherwise to BGMV.  Each set is ordered by (id, token index) (a stable
+ * counting sort); SGMV segments are maximal runs of equal id.
+ * Errors: LORA_E_ID for an id < -1 or >= max_loras (nothing is written),
+ * LORA_E_ARG for null arrays with T > 0.  T = 0 gives empty sets. */
+int32_t lora_build_meta(const int32_t* ids, const uint8_t* prefill, int32_t T,
+                        int32_t max_loras, int32_t max_lora_rank, int32_t bgmv_max_rank,
+                        lora_meta* out);
+
+/* ----------------------------------------------------- grouped kernels */
+/* All four take device pointers for x/y/v/pools/metadata and host scalars.
+ * T is the number of rows of x and y (bounds for token indices).
+ * n / num_rows = 0 is a no-op returning LORA_OK. */
+
+/* SGMV shrink ([TGI] step 4, prefill): for every segment g and row i in
+ * [seg_starts[g], seg_starts[g] + seg_lens[g]) (clamped to num_rows) with
+ * t = perm[i], a = seg_ids[g]:  v[i][s][k] = sum_j A_pool[a][s][k][j] * x[t][j]
+ * for all slices s and k < R (fp32 accumulation).  Long segments of a bf16
+ * pool run on MFMA tiles, short ones on the wavefront path. */
+int32_t lora_sgmv_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool,
+                         float* v, const int32_t* perm, const int32_t* seg_starts,
+                         const int32_t* seg_lens, const int32_t* seg_ids, int32_t num_segs,
+                         int32_t num_rows, int32_t T, void* stream);
+
+/* SGMV expand: for the same rows, y[t][off_s + j] = round_dtype((float)y[t][off_s + j]
+ * + sum_k B_pool[a][off_s + j][k] * v[i][s][k]) for every slice s, j < out_s. */
+int32_t lora_sgmv_expand(const lora_pool_desc* desc, const float* v, const void* B_pool,
+                         void* y, const int32_t* perm, const int32_t* seg_starts,
+                         const int32_t* seg_lens, const int32_t* seg_ids, int32_t num_segs,
+                         int32_t num_rows, int32_t T, void* stream);
+
+/* BGMV shrink ([TGI] step 4, decode): for every row i < n with t = tok[i],
+ * a = ids[i] (a = -1 rows are skipped and their v left untouched):
+ * v[i][s][k] = sum_j A_pool[a][s][k][j] * x[t][j].  Rows sorted by id (as
+ * lora_build_meta emits them) share each adapter's weight reads. */
+int32_t lora_bgmv_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool,
+                         float* v, const int32_t* tok, const int32_t* ids, int32_t n,
+                         int32_t T, void* stream);
+
+/* BGMV expand: y[t][off_s + j] += sum_k B_pool[a][off_s + j][k] * v[i][s][k]
+ * (rounded as above); rows with a = -1 are never read or written. */
+int32_t lora_bgmv_expand(const lora_pool_desc* desc, const float* v, const void* B_pool,
+                         void* y, const int32_t* tok, const int32_t* ids, int32_t n,
+                         int32_t T, void* stream);
+
+/* ------------------------------------------------------------ dispatcher */
+
+/* Device workspace lora_apply needs for a batch of T tokens (v for every row
+ * plus the device copy of the metadata), and the host staging size for the
+ * metadata.  Negative lora_status on an invalid descriptor or T < 0. */
+int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T);
+int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
+
+/* The whole delta path for one batch ([TGI] step 4; [QA] direct answer):
+ * validates ids, builds the metadata on the host into meta_host, copies it into
+ * ws on `stream`, then runs SGMV shrink, BGMV shrink, SGMV expand, BGMV expand
+ * on `stream`, updating y in place.  Rows with id -1 are never written.
+ *   ids_host[T], prefill_host[T] (NULL = all decode): host arrays.
+ *   ws: device workspace of >= lora_apply_workspace_bytes(desc, T) bytes.
+ *   meta_host: host staging of >= lora_apply_host_meta_bytes(desc, T) bytes.
+ *     If it is pinned (hipHostMalloc) the copy is asynchronous and the caller
+ *     must not rewrite it until the stream has passed this call; pageable
+ *     memory is copied before the call returns.
+ * Returns without synchronising.  T = 0 is a no-op. */
+int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
+                   const void* x, void* y, int32_t T, const int32_t* ids_host,
+                   const uint8_t* prefill_host, int32_t bgmv_max_rank, void* ws,
+                   int64_t ws_bytes, void* meta_host, int64_t meta_host_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_POOL_H */

@@ -1,0 +1,266 @@
+// C ABI entry points that touch the GPU: pool load / clear, the four grouped
+// shrink / expand operations and the lora_apply dispatcher.  Every argument is
+// validated before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "lora_internal.h"
+#include "lora_kernels.h"
+
+using namespace lora;
+
+namespace {
+
+uint16_t host_f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+float host_bf16_to_f32(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+int32_t hip_ok(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LORA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return LORA_OK;
+}
+
+int32_t need_ptr(const void* p, const char* name) {
+  if (!p) return fail(LORA_E_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(LORA_E_ALIGN, "%s is not 16-byte aligned", name);
+  return LORA_OK;
+}
+
+int32_t check_rows(int32_t n, int32_t T, const char* what) {
+  if (n < 0) return fail(LORA_E_ARG, "%s must be >= 0, got %d", what, n);
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  return LORA_OK;
+}
+
+int32_t check_common(const lora_pool_desc* desc, Geo* g, const void* act, const char* act_name,
+                     const void* pool, const char* pool_name, const void* v) {
+  if (int32_t e = check_desc(desc, g)) return e;
+  if (int32_t e = need_ptr(act, act_name)) return e;
+  if (int32_t e = need_ptr(pool, pool_name)) return e;
+  if (int32_t e = need_ptr(v, "v")) return e;
+  return LORA_OK;
+}
+
+int32_t sgmv_args(const int32_t* perm, const int32_t* seg_starts, const int32_t* seg_lens,
+                  const int32_t* seg_ids, int32_t num_segs) {
+  if (num_segs < 0) return fail(LORA_E_ARG, "num_segs must be >= 0, got %d", num_segs);
+  if (num_segs > (1 << 20)) return fail(LORA_E_SHAPE, "num_segs too large (%d)", num_segs);
+  if (!perm || !seg_starts || !seg_lens || !seg_ids)
+    return fail(LORA_E_ARG, "SGMV metadata pointers must not be NULL");
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_pool_load(const lora_pool_desc* desc, void* A_pool, void* B_pool, int32_t slot,
+                       int32_t slice, const void* A_src, const void* B_src, int32_t r,
+                       float alpha, int32_t use_rslora, int32_t src_on_device, void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (int32_t e = need_ptr(A_pool, "A_pool")) return e;
+  if (int32_t e = need_ptr(B_pool, "B_pool")) return e;
+  if (!A_src || !B_src) return fail(LORA_E_ARG, "A_src / B_src must not be NULL");
+  if (slot < 0 || slot >= g.max_loras)
+    return fail(LORA_E_ID, "slot %d is outside [0, %d)", slot, g.max_loras);
+  if (slice < 0 || slice >= g.S) return fail(LORA_E_ID, "slice %d is outside [0, %d)", slice, g.S);
+  if (r <= 0 || r > g.R)
+    return fail(LORA_E_RANK, "adapter rank %d must be in [1, max_lora_rank = %d]", r, g.R);
+  if (src_on_device != 0 && src_on_device != 1)
+    return fail(LORA_E_ARG, "src_on_device must be 0 or 1");
+  const float scale = lora_scaling(r, alpha, use_rslora);
+  if (!std::isfinite(scale)) return fail(LORA_E_ARG, "scale alpha/r is not finite");
+  const int64_t eb = elem_bytes(g.dtype);
+  const int out_s = g.out[slice];
+  char* Ad = (char*)A_pool + ((int64_t)slot * g.S + slice) * g.R * (int64_t)g.K * eb;
+  char* Bd = (char*)B_pool + ((int64_t)slot * g.O + g.off[slice]) * (int64_t)g.R * eb;
+  hipStream_t st = (hipStream_t)stream;
+  if (log_enabled())
+    std::fprintf(stderr, "lora_pool: loading adapter into slot %d slice %d (rank %d, scale %g)\n",
+                 slot, slice, r, (double)scale);
+  if (src_on_device) return run_pool_load(g, Ad, Bd, A_src, B_src, r, out_s, scale, st);
+
+  // host sources: pad and fold on the host, then copy
+  const size_t na = (size_t)g.R * g.K, nb = (size_t)out_s * g.R;
+  std::vector<unsigned char> Ah(na * eb, 0), Bh(nb * eb, 0);
+  std::memcpy(Ah.data(), A_src, (size_t)r * g.K * eb);
+  if (g.dtype == LORA_BF16) {
+    const uint16_t* Bs = (const uint16_t*)B_src;
+    uint16_t* Bo = (uint16_t*)Bh.data();
+    for (int j = 0; j < out_s; ++j)
+      for (int k = 0; k < r; ++k)
+        Bo[(size_t)j * g.R + k] = host_f32_to_bf16(host_bf16_to_f32(Bs[(size_t)j * r + k]) * scale);
+  } else {
+    const float* Bs = (const float*)B_src;
+    float* Bo = (float*)Bh.data();
+    for (int j = 0; j < out_s; ++j)
+      for (int k = 0; k < r; ++k) Bo[(size_t)j * g.R + k] = Bs[(size_t)j * r + k] * scale;
+  }
+  if (int32_t e = hip_ok(hipMemcpyAsync(Ad, Ah.data(), Ah.size(), hipMemcpyHostToDevice, st),
+                         "copy A slice")) return e;
+  if (int32_t e = hip_ok(hipMemcpyAsync(Bd, Bh.data(), Bh.size(), hipMemcpyHostToDevice, st),
+                         "copy B slice")) return e;
+  return hip_ok(hipStreamSynchronize(st), "pool load sync");
+}
+
+int32_t lora_pool_clear(const lora_pool_desc* desc, void* A_pool, void* B_pool, int32_t slot,
+                        void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (int32_t e = need_ptr(A_pool, "A_pool")) return e;
+  if (int32_t e = need_ptr(B_pool, "B_pool")) return e;
+  if (slot < 0 || slot >= g.max_loras)
+    return fail(LORA_E_ID, "slot %d is outside [0, %d)", slot, g.max_loras);
+  const int64_t eb = elem_bytes(g.dtype);
+  const int64_t abytes = (int64_t)g.S * g.R * g.K * eb, bbytes = (int64_t)g.O * g.R * eb;
+  hipStream_t st = (hipStream_t)stream;
+  if (int32_t e = hip_ok(hipMemsetAsync((char*)A_pool + slot * abytes, 0, abytes, st), "clear A"))
+    return e;
+  return hip_ok(hipMemsetAsync((char*)B_pool + slot * bbytes, 0, bbytes, st), "clear B");
+}
+
+int32_t lora_sgmv_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool, float* v,
+                         const int32_t* perm, const int32_t* seg_starts, const int32_t* seg_lens,
+                         const int32_t* seg_ids, int32_t num_segs, int32_t num_rows, int32_t T,
+                         void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_rows(num_rows, T, "num_rows")) return e;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (num_rows == 0 || num_segs == 0 || T == 0) return LORA_OK;
+  if (int32_t e = check_common(desc, &g, x, "x", A_pool, "A_pool", v)) return e;
+  if (int32_t e = sgmv_args(perm, seg_starts, seg_lens, seg_ids, num_segs)) return e;
+  g.T = T;
+  RowList L{perm, nullptr, seg_starts, seg_lens, seg_ids, num_segs, num_rows, 0, INT32_MAX};
+  return run_shrink(g, x, A_pool, v, L, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int32_t lora_sgmv_expand(const lora_pool_desc* desc, const float* v, const void* B_pool, void* y,
+                         const int32_t* perm, const int32_t* seg_starts, const int32_t* seg_lens,
+                         const int32_t* seg_ids, int32_t num_segs, int32_t num_rows, int32_t T,
+                         void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_rows(num_rows, T, "num_rows")) return e;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (num_rows == 0 || num_segs == 0 || T == 0) return LORA_OK;
+  if (int32_t e = check_common(desc, &g, y, "y", B_pool, "B_pool", v)) return e;
+  if (int32_t e = sgmv_args(perm, seg_starts, seg_lens, seg_ids, num_segs)) return e;
+  g.T = T;
+  RowList L{perm, nullptr, seg_starts, seg_lens, seg_ids, num_segs, num_rows, 0, INT32_MAX};
+  return run_expand(g, v, B_pool, y, L, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int32_t lora_bgmv_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool, float* v,
+                         const int32_t* tok, const int32_t* ids, int32_t n, int32_t T,
+                         void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_rows(n, T, "n")) return e;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (n == 0 || T == 0) return LORA_OK;
+  if (int32_t e = check_common(desc, &g, x, "x", A_pool, "A_pool", v)) return e;
+  if (!tok || !ids) return fail(LORA_E_ARG, "tok / ids must not be NULL");
+  g.T = T;
+  RowList L{tok, ids, nullptr, nullptr, nullptr, 0, n, 0, INT32_MAX};
+  return run_shrink(g, x, A_pool, v, L, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int32_t lora_bgmv_expand(const lora_pool_desc* desc, const float* v, const void* B_pool, void* y,
+                         const int32_t* tok, const int32_t* ids, int32_t n, int32_t T,
+                         void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_rows(n, T, "n")) return e;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (n == 0 || T == 0) return LORA_OK;
+  if (int32_t e = check_common(desc, &g, y, "y", B_pool, "B_pool", v)) return e;
+  if (!tok || !ids) return fail(LORA_E_ARG, "tok / ids must not be NULL");
+  g.T = T;
+  RowList L{tok, ids, nullptr, nullptr, nullptr, 0, n, 0, INT32_MAX};
+  return run_expand(g, v, B_pool, y, L, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
+                   const void* x, void* y, int32_t T, const int32_t* ids_host,
+                   const uint8_t* prefill_host, int32_t bgmv_max_rank, void* ws,
+                   int64_t ws_bytes, void* meta_host, int64_t meta_host_bytes, void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  if (T == 0) return LORA_OK;
+  if (int32_t e = need_ptr(A_pool, "A_pool")) return e;
+  if (int32_t e = need_ptr(B_pool, "B_pool")) return e;
+  if (int32_t e = need_ptr(x, "x")) return e;
+  if (int32_t e = need_ptr(y, "y")) return e;
+  if (int32_t e = need_ptr(ws, "ws")) return e;
+  if (!ids_host) return fail(LORA_E_ARG, "ids_host is NULL");
+  if (!meta_host) return fail(LORA_E_ARG, "meta_host is NULL");
+  if ((uintptr_t)meta_host % 4) return fail(LORA_E_ALIGN, "meta_host is not 4-byte aligned");
+  const MetaLayout ml = meta_layout(T, g.max_loras);
+  const int64_t meta_bytes = ml.total_ints * 4;
+  const int64_t v_off = align_up(meta_bytes, 256);
+  const int64_t need_ws = v_off + (int64_t)T * g.S * g.R * 4;
+  if (ws_bytes < need_ws)
+    return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
+                (long long)need_ws);
+  if (meta_host_bytes < meta_bytes)
+    return fail(LORA_E_WORKSPACE, "meta_host has %lld bytes, needs %lld",
+                (long long)meta_host_bytes, (long long)meta_bytes);
+  for (int32_t t = 0; t < T; ++t) {
+    if (ids_host[t] < -1 || ids_host[t] >= g.max_loras)
+      return fail(LORA_E_ID, "ids[%d] = %d is outside [-1, %d)", t, ids_host[t], g.max_loras);
+  }
+  int32_t* mh = (int32_t*)meta_host;
+  lora_meta m;
+  m.sgmv_perm = mh + ml.perm;
+  m.seg_starts = mh + ml.seg_starts;
+  m.seg_lens = mh + ml.seg_lens;
+  m.seg_ids = mh + ml.seg_ids;
+  m.bgmv_tok = mh + ml.bgmv_tok;
+  m.bgmv_ids = mh + ml.bgmv_ids;
+  build_meta_core(ids_host, prefill_host, T, g.max_loras, g.R, bgmv_max_rank, &m);
+  const int32_t ns = m.num_sgmv_rows, nb = m.num_bgmv_rows;
+  if (ns + nb == 0) return LORA_OK;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (int32_t e = hip_ok(hipMemcpyAsync(ws, meta_host, meta_bytes, hipMemcpyHostToDevice, st),
+                         "metadata copy")) return e;
+  const int32_t* md = (const int32_t*)ws;
+  float* v = (float*)((char*)ws + v_off);
+  float* v_b = v + (int64_t)ns * g.S * g.R;
+  g.T = T;
+  RowList Ls{md + ml.perm, nullptr, md + ml.seg_starts, md + ml.seg_lens, md + ml.seg_ids,
+             m.num_segs, ns, 0, INT32_MAX};
+  RowList Lb{md + ml.bgmv_tok, md + ml.bgmv_ids, nullptr, nullptr, nullptr, 0, nb, 0, INT32_MAX};
+  if (ns > 0)
+    if (int32_t e = run_shrink(g, x, A_pool, v, Ls, m.seg_starts, m.seg_lens, st)) return e;
+  if (nb > 0)
+    if (int32_t e = run_shrink(g, x, A_pool, v_b, Lb, nullptr, nullptr, st)) return e;
+  if (ns > 0)
+    if (int32_t e = run_expand(g, v, B_pool, y, Ls, m.seg_starts, m.seg_lens, st)) return e;
+  if (nb > 0)
+    if (int32_t e = run_expand(g, v_b, B_pool, y, Lb, nullptr, nullptr, st)) return e;
+  return LORA_OK;
+}
+
+}  // extern "C"

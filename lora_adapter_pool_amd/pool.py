@@ -1,0 +1,90 @@
+"""A rank-padded adapter pool in HBM plus the per-call workspace of lora_apply.
+
+Thin owner of device memory (torch tensors) around the C ABI: it allocates the
+pool once ([vLLM] step 2 of the vLLM offline multi-LoRA article: max_loras
+slots pre-allocated at max_lora_rank), loads adapters through lora_pool_load and
+calls lora_apply with a device workspace and a small ring of pinned host
+staging buffers (a buffer is reused only after the stream has passed the call
+that last read it).
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from . import _lib as L
+
+
+class LoraPool:
+    def __init__(self, dtype: str, max_loras: int, max_lora_rank: int, in_features: int,
+                 out_features: Sequence[int], device: str = "cuda", staging_slots: int = 3):
+        import torch
+
+        self.torch = torch
+        self.dtype = "bf16" if dtype in ("bf16", "bfloat16") else "f32"
+        self.tdtype = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        self.desc = L.make_desc(self.dtype, max_loras, max_lora_rank, in_features, out_features)
+        L.lora_pool_validate(self.desc)
+        eb = 2 if self.dtype == "bf16" else 4
+        self.max_loras = int(max_loras)
+        self.R = int(max_lora_rank)
+        self.K = int(in_features)
+        self.out_features = [int(o) for o in out_features]
+        self.O = sum(self.out_features)
+        self.device = device
+        self.A = torch.zeros(L.lora_pool_bytes_A(self.desc) // eb, dtype=self.tdtype, device=device)
+        self.B = torch.zeros(L.lora_pool_bytes_B(self.desc) // eb, dtype=self.tdtype, device=device)
+        self._ws = None
+        self._staging: List[list] = [[None, None] for _ in range(max(1, staging_slots))]
+        self._next = 0
+
+    # views in the documented layouts
+    def A_view(self):
+        return self.A.view(self.max_loras, len(self.out_features), self.R, self.K)
+
+    def B_view(self):
+        return self.B.view(self.max_loras, self.O, self.R)
+
+    def load(self, slot: int, slice_: int, A_src, B_src, rank: int, alpha: float,
+             use_rslora: bool = False, stream=None) -> None:
+        L.lora_pool_load(self.desc, self.A, self.B, slot, slice_, A_src, B_src, rank, alpha,
+                         use_rslora, stream=stream)
+
+    def clear(self, slot: int, stream=None) -> None:
+        L.lora_pool_clear(self.desc, self.A, self.B, slot, stream=stream)
+
+    def workspace(self, T: int):
+        need = L.lora_apply_workspace_bytes(self.desc, T)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = self.torch.empty(max(need, 256), dtype=self.torch.uint8, device=self.device)
+        return self._ws
+
+    def _staging_buffer(self, T: int, stream):
+        need = L.lora_apply_host_meta_bytes(self.desc, T)
+        slot = self._staging[self._next]
+        self._next = (self._next + 1) % len(self._staging)
+        buf, ev = slot
+        if ev is not None:
+            ev.synchronize()  # the stream has passed the call that last read this buffer
+        if buf is None or buf.numel() < need:
+            buf = self.torch.empty(max(need, 64), dtype=self.torch.uint8, pin_memory=True)
+            slot[0] = buf
+        return slot, buf, need
+
+    def apply(self, x, y, ids, prefill=None, bgmv_max_rank: int = 0, stream=None) -> None:
+        """y (in place) += per-row LoRA delta for x; ids int32 per row (-1 = none)."""
+        torch = self.torch
+        T = int(x.shape[0])
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        pre = None if prefill is None else np.ascontiguousarray(np.asarray(prefill, dtype=np.uint8))
+        if ids.shape[0] != T or (pre is not None and pre.shape[0] != T):
+            raise L.LoraError(L.LORA_E_SHAPE, "ids / prefill length must equal the token count")
+        ws = self.workspace(T)
+        slot, buf, need = self._staging_buffer(T, stream)
+        st = torch.cuda.current_stream() if stream is None else stream
+        L.lora_apply(self.desc, self.A, self.B, x, y, T, ids, pre, bgmv_max_rank, ws, ws.numel(),
+                     buf, buf.numel(), stream=st)
+        ev = slot[1] or torch.cuda.Event()
+        ev.record(st)
+        slot[1] = ev

@@ -1,0 +1,123 @@
+"""Helpers of the GPU parity tests: load a workload's adapters into a pool,
+run the HIP path through the C ABI, compare with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import lora_adapter_pool_amd as L
+import oracle
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_dev(a, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch_dtype(dtype)).cuda()
+
+
+def make_pool(wl, R=None, host_source=False):
+    pool = L.LoraPool(wl.dtype, wl.max_loras, R or wl.max_lora_rank, wl.in_features,
+                      wl.out_features)
+    for a, ad in sorted(wl.slots.items()):
+        for s in range(wl.num_slices):
+            if host_source:
+                import torch
+                A = torch.from_numpy(np.ascontiguousarray(ad.A[s])).to(torch_dtype(wl.dtype))
+                B = torch.from_numpy(np.ascontiguousarray(ad.B[s])).to(torch_dtype(wl.dtype))
+                pool.load(a, s, A.contiguous(), B.contiguous(), ad.rank, ad.alpha, ad.use_rslora)
+            else:
+                pool.load(a, s, to_dev(ad.A[s], wl.dtype), to_dev(ad.B[s], wl.dtype), ad.rank,
+                          ad.alpha, ad.use_rslora)
+    return pool
+
+
+def y_to_np(y):
+    import torch
+    return y.to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def run_apply(wl, pool=None, bgmv_max_rank=0, x=None, ids=None, prefill=None, y=None):
+    import torch
+    pool = pool or make_pool(wl)
+    xd = to_dev(wl.x if x is None else x, wl.dtype)
+    yd = to_dev(wl.y_in, wl.dtype) if y is None else y
+    pool.apply(xd, yd, wl.ids if ids is None else ids, wl.prefill if prefill is None else prefill,
+               bgmv_max_rank=bgmv_max_rank)
+    torch.cuda.synchronize()
+    return yd
+
+
+def run_entry_points(wl, pool, mode, bgmv_max_rank=0):
+    """Drive the four grouped entry points directly with device metadata from
+    the library's host builder; returns (y, v_sgmv, v_bgmv, meta)."""
+    import torch
+    m = L.lora_build_meta(wl.ids, wl.prefill, wl.max_loras, pool.R, bgmv_max_rank)
+    xd = to_dev(wl.x, wl.dtype)
+    yd = to_dev(wl.y_in, wl.dtype)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v.astype(np.int32))).cuda() if v.size else
+           torch.zeros(1, dtype=torch.int32, device="cuda") for k, v in m.items()}
+    S, R, T = wl.num_slices, pool.R, wl.T
+    ns, nb = int(m["sgmv_perm"].size), int(m["bgmv_tok"].size)
+    vs = torch.full((max(ns, 1), S * R), float("nan"), dtype=torch.float32, device="cuda")
+    vb = torch.full((max(nb, 1), S * R), float("nan"), dtype=torch.float32, device="cuda")
+    nseg = int(m["seg_ids"].size)
+    if mode in ("both", "sgmv"):
+        L.lora_sgmv_shrink(pool.desc, xd, pool.A, vs, dev["sgmv_perm"], dev["seg_starts"],
+                           dev["seg_lens"], dev["seg_ids"], nseg, ns, T)
+    if mode in ("both", "bgmv"):
+        L.lora_bgmv_shrink(pool.desc, xd, pool.A, vb, dev["bgmv_tok"], dev["bgmv_ids"], nb, T)
+    if mode in ("both", "sgmv"):
+        L.lora_sgmv_expand(pool.desc, vs, pool.B, yd, dev["sgmv_perm"], dev["seg_starts"],
+                           dev["seg_lens"], dev["seg_ids"], nseg, ns, T)
+    if mode in ("both", "bgmv"):
+        L.lora_bgmv_expand(pool.desc, vb, pool.B, yd, dev["bgmv_tok"], dev["bgmv_ids"], nb, T)
+    torch.cuda.synchronize()
+    return yd, vs, vb, m
+
+
+def sample_rows(wl, n=64, seed=0):
+    """Rows for full-size checks: first/last row of every adapter run plus random
+    rows (active and none)."""
+    rng = np.random.default_rng(seed)
+    ids = wl.ids
+    edges = [0, wl.T - 1]
+    change = np.where(np.diff(ids) != 0)[0]
+    edges += change.tolist() + (change + 1).tolist()
+    rows = set(int(r) for r in edges[: n // 2])
+    rows.update(int(r) for r in rng.choice(wl.T, size=min(wl.T, n), replace=False))
+    return sorted(rows)[: max(n, 8)]
+
+
+def check_rows(wl, y_gpu, rows=None, tol=None, label=""):
+    """Active rows within tolerance of the oracle; none rows bit-identical."""
+    import torch
+    rows = list(range(wl.T)) if rows is None else list(rows)
+    idx = torch.as_tensor(rows, dtype=torch.long, device=y_gpu.device)
+    yg = y_to_np(y_gpu.index_select(0, idx))
+    ref = oracle.lora_forward_rows(wl, rows)
+    act = np.asarray([wl.ids[r] >= 0 for r in rows])
+    tol = TOL[wl.dtype] if tol is None else tol
+    err = oracle.rel_err_rows(yg[act], ref[act]) if act.any() else 0.0
+    if (~act).any():
+        y_in_bits = torch.from_numpy(np.ascontiguousarray(wl.y_in[np.asarray(rows)[~act]])).to(
+            torch_dtype(wl.dtype))
+        got_bits = y_gpu.index_select(0, idx[torch.as_tensor(~act, device=y_gpu.device)]).cpu()
+        assert torch.equal(got_bits.view(torch.int16) if wl.dtype == "bf16" else
+                           got_bits.view(torch.int32),
+                           y_in_bits.view(torch.int16) if wl.dtype == "bf16" else
+                           y_in_bits.view(torch.int32)), f"{label}: a row without adapter changed"
+    say(f"  {label}: rows={len(rows)} active={int(act.sum())} rel_err={err:.3e} tol={tol:.0e}")
+    assert err <= tol, f"{label}: rel err {err} > {tol}"
+    return err

@@ -1,0 +1,193 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, the host metadata builder is bit-exact against the oracle's,
+and every validation error is returned before any HIP call."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import lora_adapter_pool_amd as L
+from lora_adapter_pool_amd import _lib
+import oracle
+from oracle_pins import META_KEYS, _load, check_meta_properties
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def test_library_exports_every_header_function(lib):
+    names = _lib.header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
+    assert lib.lora_abi_version() == 1
+
+
+def test_pool_geometry_and_bytes():
+    d = L.make_desc("bf16", 64, 16, 4096, [4096, 1024, 1024])
+    assert L.lora_pool_bytes_A(d) == 64 * 3 * 16 * 4096 * 2
+    assert L.lora_pool_bytes_B(d) == 64 * 16 * 6144 * 2
+    a, b = oracle.pool_bytes(64, 3, 16, 4096, 6144, 2)
+    assert (a, b) == (L.lora_pool_bytes_A(d), L.lora_pool_bytes_B(d))
+    d = L.make_desc("f32", 4, 8, 256, [256])
+    assert L.lora_pool_bytes_A(d) == 4 * 8 * 256 * 4
+
+
+@pytest.mark.parametrize("r,alpha,rs", [(8, 16.0, 0), (16, 32.0, 0), (16, 16.0, 1), (64, 128.0, 0),
+                                        (4, 8.0, 1), (3, 1.0, 0), (7, 5.0, 1), (2, 4.0, 1)])
+def test_scaling_matches_oracle(r, alpha, rs):
+    got = L.lora_scaling(r, alpha, rs)
+    assert got == np.float32(oracle.scaling(r, alpha, bool(rs)))
+    assert math.isnan(L.lora_scaling(0, 1.0, 0))
+
+
+def test_builder_golden_cases():
+    for case in _load("builder_tiny.json")["cases"]:
+        m = L.lora_build_meta(case["ids"], case["prefill"], 8, case["max_lora_rank"], 64)
+        for k in META_KEYS:
+            assert m[k].tolist() == case[k], (case["name"], k)
+
+
+def test_builder_bit_exact_vs_oracle_fuzz():
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        T = int(rng.integers(0, 700))
+        n = int(rng.integers(1, 70))
+        ids = rng.integers(-1, n, size=T).astype(np.int32)
+        if trial % 4 == 0:
+            ids = np.sort(ids)
+        pre = rng.integers(0, 2, size=T).astype(np.uint8)
+        if trial % 5 == 0:
+            pre[:] = 1
+        R = int(rng.choice([8, 16, 32, 64, 72, 128]))
+        lim = int(rng.choice([0, 16, 64, 100]))
+        got = L.lora_build_meta(ids, pre, n, R, lim)
+        ref = oracle.build_meta(ids.tolist(), pre.tolist(), R, lim if lim > 0 else 64)
+        for k in META_KEYS:
+            assert got[k].tolist() == list(ref[k]), (trial, k)
+        check_meta_properties(ids, pre, R, got, lim if lim > 0 else 64)
+
+
+def test_builder_named_workload_shapes():
+    import workloads as W
+    wl = W.config_sgmv_prefill(seed=0, K=64, O=64)
+    m = L.lora_build_meta(wl.ids, wl.prefill, wl.max_loras, wl.max_lora_rank)
+    assert m["sgmv_perm"].tolist() == list(range(wl.T))   # laid out by adapter already
+    assert m["seg_ids"].tolist() == list(range(16)) and m["bgmv_tok"].size == 0
+    gu, _ = W.config_mlp_mixed(seed=0, hidden=64, inter=64)
+    m = L.lora_build_meta(gu.ids, gu.prefill, gu.max_loras, gu.max_lora_rank)
+    ref = oracle.build_meta(gu.ids.tolist(), gu.prefill.tolist(), gu.max_lora_rank)
+    for k in META_KEYS:
+        assert m[k].tolist() == list(ref[k])
+    assert m["bgmv_tok"].size == int(((gu.ids >= 0) & (gu.prefill == 0)).sum())
+
+
+def test_builder_null_prefill_means_decode():
+    m = L.lora_build_meta([1, 0, 1], None, 2, 16)
+    assert m["bgmv_tok"].tolist() == [1, 0, 2] and m["sgmv_perm"].size == 0
+
+
+def test_builder_rejects_bad_ids():
+    with pytest.raises(L.LoraError) as e:
+        L.lora_build_meta([0, 5], [0, 0], 4, 16)
+    assert e.value.status == _lib.LORA_E_ID and "ids[1]" in str(e.value)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_build_meta([-2], [0], 4, 16)
+    assert e.value.status == _lib.LORA_E_ID
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), _lib.LORA_E_DTYPE),
+    (dict(max_loras=0), _lib.LORA_E_SHAPE),
+    (dict(max_lora_rank=12), _lib.LORA_E_ALIGN),
+    (dict(max_lora_rank=0), _lib.LORA_E_RANK),
+    (dict(in_features=100), _lib.LORA_E_ALIGN),
+    (dict(in_features=0), _lib.LORA_E_SHAPE),
+    (dict(num_slices=0), _lib.LORA_E_SHAPE),
+    (dict(num_slices=9), _lib.LORA_E_SHAPE),
+    (dict(out0=20), _lib.LORA_E_ALIGN),
+])
+def test_descriptor_validation(kw, status):
+    d = L.make_desc("bf16", 4, 16, 256, [256])
+    for k, v in kw.items():
+        if k == "out0":
+            d.out_features[0] = v
+        else:
+            setattr(d, k, v)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_validate(d)
+    assert e.value.status == status
+
+
+FAKE = 1 << 20  # non-null, 16-byte aligned; never dereferenced (validation fails first)
+
+
+def _status(fn, *a):
+    try:
+        fn(*a)
+        return 0
+    except L.LoraError as e:
+        return e.status
+
+
+def test_pool_load_errors_before_hip():
+    d = L.make_desc("bf16", 4, 16, 256, [256])
+    args = lambda **k: [d, k.get("A", FAKE), k.get("B", FAKE), k.get("slot", 0),
+                        k.get("sl", 0), FAKE, FAKE, k.get("r", 8), 16.0, False]
+    assert _status(L.lora_pool_load, *args(r=17), True, 0) == _lib.LORA_E_RANK
+    assert _status(L.lora_pool_load, *args(r=0), True, 0) == _lib.LORA_E_RANK
+    assert _status(L.lora_pool_load, *args(slot=4), True, 0) == _lib.LORA_E_ID
+    assert _status(L.lora_pool_load, *args(slot=-1), True, 0) == _lib.LORA_E_ID
+    assert _status(L.lora_pool_load, *args(sl=1), True, 0) == _lib.LORA_E_ID
+    assert _status(L.lora_pool_load, *args(A=FAKE + 8), True, 0) == _lib.LORA_E_ALIGN
+    assert _status(L.lora_pool_load, *args(A=0), True, 0) == _lib.LORA_E_ARG
+    assert _status(L.lora_pool_clear, d, FAKE, FAKE, 9, 0) == _lib.LORA_E_ID
+
+
+def test_kernel_entry_points_validate_before_hip():
+    d = L.make_desc("bf16", 4, 16, 256, [256])
+    # zero rows: a no-op that touches nothing
+    assert _status(L.lora_bgmv_shrink, d, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 5, 0) == 0
+    assert _status(L.lora_sgmv_expand, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 5, 0) == 0
+    assert _status(L.lora_bgmv_shrink, d, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 5, 0) == _lib.LORA_E_ARG
+    assert _status(L.lora_bgmv_expand, d, FAKE, FAKE, FAKE + 4, FAKE, FAKE, 3, 5, 0) == _lib.LORA_E_ALIGN
+    assert _status(L.lora_bgmv_expand, d, FAKE, FAKE, FAKE, 0, FAKE, 3, 5, 0) == _lib.LORA_E_ARG
+    assert _status(L.lora_sgmv_shrink, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -2, 4, 5,
+                   0) == _lib.LORA_E_ARG
+    assert _status(L.lora_sgmv_shrink, d, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1, 4, 5,
+                   0) == _lib.LORA_E_ARG
+    bad = L.make_desc("bf16", 4, 20, 256, [256])
+    assert _status(L.lora_bgmv_shrink, bad, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 5, 0) == _lib.LORA_E_ALIGN
+
+
+def test_apply_validation_before_hip():
+    d = L.make_desc("bf16", 4, 16, 256, [256])
+    T = 6
+    ws_need = L.lora_apply_workspace_bytes(d, T)
+    mh_need = L.lora_apply_host_meta_bytes(d, T)
+    assert mh_need == 4 * (3 * T + 3 * 4)
+    assert ws_need == ((mh_need + 255) // 256) * 256 + T * 16 * 4
+    ids = np.array([0, 1, -1, 3, 2, 0], np.int32)
+    meta = np.zeros(mh_need // 4, np.int32)
+    ok = [d, FAKE, FAKE, FAKE, FAKE + 64, T, ids, None, 0, FAKE, ws_need, meta, mh_need, 0]
+
+    def with_(i, v):
+        a = list(ok)
+        a[i] = v
+        return a
+    assert _status(L.lora_apply, *with_(9, FAKE)[:10], ws_need - 1, meta, mh_need, 0) == _lib.LORA_E_WORKSPACE
+    assert _status(L.lora_apply, *ok[:12], mh_need - 4, 0) == _lib.LORA_E_WORKSPACE
+    bad_ids = ids.copy()
+    bad_ids[3] = 4
+    assert _status(L.lora_apply, *with_(6, bad_ids)) == _lib.LORA_E_ID
+    assert _status(L.lora_apply, *with_(3, FAKE + 2)) == _lib.LORA_E_ALIGN
+    assert _status(L.lora_apply, *with_(5, -1)) == _lib.LORA_E_ARG
+    assert _status(L.lora_apply, *with_(5, 0)) == 0          # T = 0: no-op
+    assert _status(L.lora_apply, *with_(6, None)) == _lib.LORA_E_ARG
+    # last_error carries a message for the most recent failure
+    _status(L.lora_apply, *with_(6, bad_ids))
+    assert "ids[3]" in L.last_error()

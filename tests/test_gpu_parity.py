@@ -1,0 +1,294 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on the named workloads
+(full size or sampled rows), reduced sizes spanning several tiles with ragged
+tails, edge cases and exact-arithmetic invariants."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import lora_adapter_pool_amd as L
+import oracle
+import workloads as W
+from gpu_helpers import (TOL, check_rows, make_pool, run_apply, run_entry_points, sample_rows, say,
+                         to_dev, torch_dtype, y_to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"[gpu] {request.node.name}")
+    yield
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+# ------------------------------------------------------------ tiny fp32
+
+@pytest.mark.parametrize("R", [8, 16])
+@pytest.mark.parametrize("prefill", [True, False])
+def test_tiny_fp32_apply(prefill, R):
+    wl = W.config_tiny_fp32(seed=0, max_lora_rank=R, prefill=prefill)
+    y = run_apply(wl)
+    check_rows(wl, y, label=f"tiny prefill={prefill} R={R}")
+
+
+@pytest.mark.parametrize("mode", ["sgmv", "bgmv"])
+def test_tiny_fp32_entry_points(mode):
+    wl = W.config_tiny_fp32(seed=1, prefill=(mode == "sgmv"))
+    pool = make_pool(wl)
+    y, vs, vb, m = run_entry_points(wl, pool, "both")
+    check_rows(wl, y, label=f"tiny entry {mode}")
+    # shrink output alone: v rows vs A x
+    perm = m["sgmv_perm"] if mode == "sgmv" else m["bgmv_tok"]
+    v = (vs if mode == "sgmv" else vb).cpu().numpy()[: perm.size]
+    ref = oracle.lora_shrink_rows(wl, perm.tolist())
+    err = np.max(np.abs(v - ref)) / np.max(np.abs(ref))
+    say(f"  shrink v rel err {err:.2e}")
+    assert err < 1e-5
+
+
+# ------------------------------------------------- named workloads, full
+
+def test_bgmv_decode_full():
+    wl = W.config_bgmv_decode(seed=0)
+    y = run_apply(wl)
+    check_rows(wl, y, label="bgmv_decode full (all rows)")
+
+
+def test_sgmv_prefill_full_sampled():
+    wl = W.config_sgmv_prefill(seed=0)
+    y = run_apply(wl)
+    check_rows(wl, y, rows=sample_rows(wl, 96), label="sgmv_prefill full (sampled)")
+
+
+def test_qkv_decode_full():
+    wl = W.config_qkv_decode(seed=0)
+    y = run_apply(wl)
+    check_rows(wl, y, label="qkv_decode full (all rows)")
+
+
+def test_mlp_mixed_full_sampled():
+    gu, dn = W.config_mlp_mixed(seed=0)
+    for wl in (gu, dn):
+        y = run_apply(wl)
+        check_rows(wl, y, rows=sample_rows(wl, 64), label=f"{wl.name} full (sampled)")
+        del y
+
+
+# ------------------------------------------------- reduced sizes, all rows
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_sgmv_prefill_small(seed):
+    # segments from 1 to 90 rows: short ones on the wavefront path, long on MFMA
+    wl = W.config_sgmv_prefill(seed=seed, n_seqs=9, len_lo=1, len_hi=90, K=520, O=264,
+                               n_adapters=9, rank_choices=(8, 16, 32, 64), max_lora_rank=64)
+    y = run_apply(wl)
+    check_rows(wl, y, label=f"sgmv small seed={seed} lens={wl.info['seq_lens']}")
+
+
+def test_sgmv_random_assignment_merges_segments():
+    wl = W.config_sgmv_prefill(seed=3, n_seqs=12, len_lo=3, len_hi=40, K=256, O=136, n_adapters=5,
+                               random_assignment=True)
+    y = run_apply(wl)
+    check_rows(wl, y, label="sgmv merged segments")
+
+
+def test_qkv_small_slices():
+    wl = W.config_qkv_decode(seed=2, T=77, K=264, outs=(264, 72, 72), n_adapters=16, rank=16)
+    y = run_apply(wl)
+    check_rows(wl, y, label="qkv small")
+
+
+def test_mlp_mixed_small():
+    gu, dn = W.config_mlp_mixed(seed=1, n_prefill=3, len_lo=5, len_hi=70, n_decode=37,
+                                hidden=264, inter=520, n_adapters=8)
+    for wl in (gu, dn):
+        y = run_apply(wl)
+        check_rows(wl, y, label=f"{wl.name} small")
+
+
+@pytest.mark.parametrize("mode", ["sgmv", "bgmv"])
+def test_entry_points_bf16(mode):
+    wl = W.config_qkv_decode(seed=4, T=50, K=520, outs=(136, 264), n_adapters=7, rank=16)
+    if mode == "sgmv":
+        wl = dataclasses.replace(wl, prefill=np.ones(wl.T, np.uint8))
+    pool = make_pool(wl)
+    y, vs, vb, m = run_entry_points(wl, pool, "both")
+    check_rows(wl, y, label=f"entry points bf16 {mode}")
+
+
+# ------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("R", [24, 80, 128])
+def test_unusual_ranks(R):
+    # 24: SGMV stays on the wavefront path; 80: one full MFMA rank block plus a
+    # 16-rank remainder; 128: above the BGMV limit, so decode rows go SGMV too
+    wl = W.config_mlp_mixed(seed=2, n_prefill=2, len_lo=20, len_hi=60, n_decode=11, hidden=136,
+                            inter=264, n_adapters=4, rank_choices=(8, 16), max_lora_rank=R)[0]
+    y = run_apply(wl)
+    check_rows(wl, y, label=f"R={R}")
+
+
+def test_all_rows_without_adapter_and_empty_batch():
+    import torch
+    wl = W.config_bgmv_decode(seed=5, T=20, K=64, O=64, n_adapters=2, p_none=1.0)
+    assert np.all(wl.ids < 0)
+    y = run_apply(wl)
+    check_rows(wl, y, label="all none")
+    pool = make_pool(wl)
+    x0 = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    pool.apply(x0, x0.clone(), np.zeros(0, np.int32))
+
+
+def test_single_token():
+    for pre in (0, 1):
+        wl = W.config_bgmv_decode(seed=6, T=1, K=520, O=136, n_adapters=3, p_none=0.0)
+        wl = dataclasses.replace(wl, prefill=np.full(1, pre, np.uint8))
+        y = run_apply(wl)
+        check_rows(wl, y, label=f"single token prefill={pre}")
+
+
+def test_none_rows_never_written_poison():
+    """Rows without adapter hold a signalling-NaN pattern; any write (even of
+    y + 0) would quiet it."""
+    import torch
+    wl = W.config_mlp_mixed(seed=3, n_prefill=2, len_lo=30, len_hi=40, n_decode=40, hidden=264,
+                            inter=264, n_adapters=4, p_none=0.3)[0]
+    none = np.where(wl.ids < 0)[0]
+    assert none.size > 0
+    yd = to_dev(wl.y_in, "bf16")
+    poison = torch.full((none.size, wl.O), 0x7F81, dtype=torch.int16, device="cuda")
+    yd.view(torch.int16)[torch.as_tensor(none, device="cuda")] = poison
+    y = run_apply(wl, y=yd)
+    after = y.view(torch.int16)[torch.as_tensor(none, device="cuda")]
+    assert torch.equal(after, poison)
+    act = np.where(wl.ids >= 0)[0]
+    check_rows(wl, y, rows=act.tolist(), label="poison: active rows")
+
+
+def test_zero_B_leaves_y_unchanged():
+    wl = W.with_zero_B(W.config_mlp_mixed(seed=4, n_prefill=3, len_lo=10, len_hi=50, n_decode=20,
+                                          hidden=136, inter=264, n_adapters=5)[0])
+    y = run_apply(wl)
+    assert np.array_equal(y_to_np(y), wl.y_in.astype(np.float64))
+
+
+# ----------------------------------------------- exact-arithmetic invariants
+
+def _integer_workload(dtype, rslora=False, seed=0):
+    # segment lengths chosen to hit both SGMV paths and ragged tails
+    ranks = (16, 64) if rslora else (8, 16, 64, 32, 48, 64)
+    wl = W.config_integer(seed=seed, T=300, K=520, outs=(264, 136), max_loras=6,
+                          max_lora_rank=64, ranks=ranks, dtype=dtype, rslora=rslora)
+    lens = [1, 3, 15, 16, 17, 33, 70]
+    ids = np.full(wl.T, -1, np.int32)
+    pre = np.zeros(wl.T, np.uint8)
+    pos = 0
+    for i, n in enumerate(lens):
+        ids[pos:pos + n] = i % 6
+        pre[pos:pos + n] = 1
+        pos += n
+    rng = np.random.default_rng(seed + 100)
+    ids[pos:] = rng.integers(-1, 6, size=wl.T - pos)
+    return dataclasses.replace(wl, ids=ids, prefill=pre)
+
+
+def _exact_expected(wl):
+    ref = oracle.lora_forward_rows(wl)
+    return oracle.round_exact_to_dtype(ref, wl.dtype)
+
+
+@pytest.mark.parametrize("dtype,rslora", [("bf16", False), ("f32", False), ("bf16", True)])
+def test_exact_integer_bit_identical(dtype, rslora):
+    wl = _integer_workload(dtype, rslora)
+    exp = _exact_expected(wl)
+    y = run_apply(wl).float().cpu().numpy()
+    bad = np.argwhere(y != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
+def test_sgmv_equals_bgmv_exactly():
+    import torch
+    wl = _integer_workload("bf16", seed=1)
+    pool = make_pool(wl)
+    dec = dataclasses.replace(wl, prefill=np.zeros(wl.T, np.uint8))
+    y_b = run_apply(dec, pool=pool)                     # everything BGMV
+    y_s = run_apply(dec, pool=pool, bgmv_max_rank=8)    # R = 64 > 8: everything SGMV
+    assert torch.equal(_bits(y_b), _bits(y_s))
+    pre = dataclasses.replace(wl, prefill=np.ones(wl.T, np.uint8))
+    y_p = run_apply(pre, pool=pool)                     # everything SGMV via prefill
+    assert torch.equal(_bits(y_b), _bits(y_p))
+
+
+def test_permutation_equivariance_exact():
+    import torch
+    wl = _integer_workload("bf16", seed=2)
+    y = run_apply(wl)
+    p = np.random.default_rng(0).permutation(wl.T)
+    wlp = dataclasses.replace(wl, ids=wl.ids[p], prefill=wl.prefill[p], x=wl.x[p], y_in=wl.y_in[p])
+    yp = run_apply(wlp)
+    assert torch.equal(_bits(yp), _bits(y[torch.as_tensor(p, device="cuda")]))
+
+
+def test_linearity_exact_fp32():
+    wl = _integer_workload("f32", seed=3)
+    wl0 = dataclasses.replace(wl, y_in=np.zeros_like(wl.y_in))
+    y1 = run_apply(wl0).cpu().numpy()
+    y2 = run_apply(dataclasses.replace(wl0, x=wl0.x * 2)).cpu().numpy()
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_padding_inert_exact():
+    wl = _integer_workload("bf16", seed=4)
+    small = dataclasses.replace(wl, max_lora_rank=64)
+    import torch
+    outs = []
+    for R in (64, 80, 128):
+        outs.append(_bits(run_apply(dataclasses.replace(small, max_lora_rank=R))).clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_merged_weight_closed_form():
+    """y_in = W x for a random base weight; the path must reach (W + s B A) x."""
+    wl = W.config_qkv_decode(seed=7, T=40, K=264, outs=(136, 72), n_adapters=6, rank=16,
+                             dtype="f32")
+    Wb = np.random.default_rng(1).standard_normal((wl.O, wl.in_features)) / 16
+    y_base = (wl.x.astype(np.float64) @ Wb.T).astype(np.float32)
+    wl2 = dataclasses.replace(wl, y_in=y_base)
+    y = y_to_np(run_apply(wl2))
+    ref = oracle.merged_weight_rows(Wb, wl2, range(wl.T))
+    err = oracle.rel_err_rows(y, ref)
+    say(f"  merged closed form rel err {err:.2e}")
+    assert err < 1e-5
+
+
+# ------------------------------------------------------------ pool load
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("host_source", [False, True])
+def test_pool_contents_bit_exact(dtype, host_source):
+    # alpha 3 / r 8 = 0.375: the fold really rounds in bf16; rsLoRA r 3 too
+    wl = W.config_sgmv_prefill(seed=5, n_seqs=4, len_lo=2, len_hi=4, K=136, O=72, n_adapters=4,
+                               rank_choices=(8,), max_lora_rank=16,
+                               alpha_per_rank=3.0 / 8.0, dtype=dtype)
+    slots = dict(wl.slots)
+    rng = np.random.default_rng(9)
+    A3 = W.to_dtype_values(rng.standard_normal((3, 136)) / 11, dtype)
+    B3 = W.to_dtype_values(rng.standard_normal((72, 3)) * 0.02, dtype)
+    # rank 3 with rsLoRA: 1.75 / sqrt(3) is rounded to fp32 the same way on both sides
+    slots[3] = W.AdapterSpec(rank=3, alpha=1.75, use_rslora=True, A=[A3], B=[B3])
+    wl = dataclasses.replace(wl, slots=slots)
+    pool = make_pool(wl, host_source=host_source)
+    exp = oracle.expected_pool(wl)
+    Av = pool.A_view().float().cpu().numpy()
+    Bv = pool.B_view().float().cpu().numpy()
+    for a, e in exp.items():
+        assert np.array_equal(Av[a, 0].view(np.uint32), e["A"][0].view(np.uint32)), a
+        assert np.array_equal(Bv[a].view(np.uint32), e["B"][0].view(np.uint32)), a
+    # a cleared slot adds nothing
+    pool.clear(1)
+    assert not pool.A_view()[1].any() and not pool.B_view()[1].any()
