@@ -1,0 +1,459 @@
+"""Benchmark of the multi-LoRA delta path on one MI355X.
+
+A step is one lora_apply call (host metadata build, metadata copy, shrink and
+expand kernels) over one synthetic batch.  Default workload: decode batch of
+64 single-token rows, in = out = 3072, 8 adapters of rank 16 (bf16, 10% rows
+without adapter).  The adapter pool, x and y are replicated enough times
+(>= 1 GiB in total) that every step reads cold HBM; steps rotate replicas.
+
+Prints one JSON line.  Besides the headline numbers it reports:
+  roofline      the dominant kernel's algorithmic bytes / its average launch time
+                (HIP events around back-to-back launches on the launch stream)
+  secondary     the same measurement for the long-prefill SGMV workload
+                (in = out = 4096, 16 sequences of 64..1024 tokens, ranks padded to 64)
+  cpu_baseline  the fp64 oracle timed on the host for a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SRC = os.path.join(ROOT, "lora_adapter_pool_amd", "csrc", "lora_kernels.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--workload", default="bgmv_decode",
+                   choices=["bgmv_decode", "sgmv_prefill", "qkv_decode", "mlp_mixed"])
+    p.add_argument("--replica-mib", type=float, default=1024.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+
+def make_workloads(name, seed):
+    import workloads as W
+    if name == "bgmv_decode":
+        return [W.config_bgmv_decode(seed=seed)]
+    if name == "sgmv_prefill":
+        return [W.config_sgmv_prefill(seed=seed)]
+    if name == "qkv_decode":
+        return [W.config_qkv_decode(seed=seed)]
+    gu, dn = W.config_mlp_mixed(seed=seed)
+    return [gu, dn]
+
+
+def algorithmic(wl):
+    """Bytes and flops the method must move / do for one call (each active
+    adapter's padded A and B once, x once per active row, v written and read in
+    fp32, y read and written per active row), split by kernel stage."""
+    e = 2 if wl.dtype == "bf16" else 4
+    act = wl.ids >= 0
+    Ta = int(act.sum())
+    nact = len(set(wl.ids[act].tolist()))
+    K, R, S, O = wl.in_features, wl.max_lora_rank, wl.num_slices, wl.O
+    shrink = Ta * K * e + nact * S * R * K * e + Ta * S * R * 4
+    expand = nact * R * O * e + Ta * S * R * 4 + 2 * Ta * O * e
+    flops = 2 * Ta * R * (S * K + O)
+    return {"Ta": Ta, "n_act": nact, "shrink_bytes": shrink, "expand_bytes": expand,
+            "bytes": shrink + expand, "flops": flops, "shrink_flops": 2 * Ta * R * S * K,
+            "expand_flops": 2 * Ta * R * O}
+
+
+class Setup:
+    """Replicated pool / x / y for one workload, plus prebuilt device metadata."""
+
+    def __init__(self, wl, replica_bytes):
+        import torch
+        import lora_adapter_pool_amd as L
+        self.wl = wl
+        self.L = L
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(tdt).cuda()  # noqa: E731
+        pool = L.LoraPool(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features,
+                          wl.out_features)
+        for a, ad in sorted(wl.slots.items()):
+            for s in range(wl.num_slices):
+                pool.load(a, s, dev(ad.A[s]), dev(ad.B[s]), ad.rank, ad.alpha, ad.use_rslora)
+        self.desc = pool.desc
+        x0, y0 = dev(wl.x), dev(wl.y_in)
+        per = (pool.A.numel() + pool.B.numel() + x0.numel() + y0.numel()) * x0.element_size()
+        self.nrep = max(1, min(4096, int(np.ceil(replica_bytes / per))))
+        self.A = [pool.A] + [pool.A.clone() for _ in range(self.nrep - 1)]
+        self.B = [pool.B] + [pool.B.clone() for _ in range(self.nrep - 1)]
+        self.x = [x0] + [x0.clone() for _ in range(self.nrep - 1)]
+        self.y = [y0] + [y0.clone() for _ in range(self.nrep - 1)]
+        self.pA = [t.data_ptr() for t in self.A]
+        self.pB = [t.data_ptr() for t in self.B]
+        self.px = [t.data_ptr() for t in self.x]
+        self.py = [t.data_ptr() for t in self.y]
+        self.T = wl.T
+        self.ids = np.ascontiguousarray(wl.ids.astype(np.int32))
+        self.pre = np.ascontiguousarray(wl.prefill.astype(np.uint8))
+        self.ws_bytes = L.lora_apply_workspace_bytes(self.desc, self.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.mh_bytes = L.lora_apply_host_meta_bytes(self.desc, self.T)
+        self.nstage = 8
+        self.stage = [torch.empty(self.mh_bytes, dtype=torch.uint8, pin_memory=True)
+                      for _ in range(self.nstage)]
+        self.stage_ev = [None] * self.nstage
+        # prebuilt device metadata for the kernel-only loops
+        m = L.lora_build_meta(self.ids, self.pre, wl.max_loras, wl.max_lora_rank)
+        self.meta = m
+        tt = lambda a: torch.from_numpy(np.ascontiguousarray(a.astype(np.int32)) if a.size else  # noqa
+                                        np.zeros(1, np.int32)).cuda()
+        self.dm = {k: tt(v) for k, v in m.items()}
+        S, R = wl.num_slices, wl.max_lora_rank
+        self.ns, self.nb = int(m["sgmv_perm"].size), int(m["bgmv_tok"].size)
+        self.v_s = torch.zeros((max(self.ns, 1), S * R), dtype=torch.float32, device="cuda")
+        self.v_b = torch.zeros((max(self.nb, 1), S * R), dtype=torch.float32, device="cuda")
+        self.bytes_per_rep = per
+        torch.cuda.synchronize()
+
+    def apply_step(self, i, stream_ptr):
+        import torch
+        L = self.L
+        r = i % self.nrep
+        j = i % self.nstage
+        if self.stage_ev[j] is not None:
+            self.stage_ev[j].synchronize()
+        lib = L.lib()
+        st = lib.lora_apply(ctypes.byref(self.desc), self.pA[r], self.pB[r], self.px[r],
+                            self.py[r], self.T, self.ids.ctypes.data, self.pre.ctypes.data, 0,
+                            self.ws.data_ptr(), self.ws_bytes, self.stage[j].data_ptr(),
+                            self.mh_bytes, stream_ptr)
+        if st != 0:
+            raise RuntimeError(f"lora_apply failed: {L.last_error()}")
+        ev = self.stage_ev[j] or torch.cuda.Event()
+        ev.record()
+        self.stage_ev[j] = ev
+
+    def kernel_launch(self, which, i, stream_ptr):
+        L = self.L
+        lib = L.lib()
+        r = i % self.nrep
+        d = ctypes.byref(self.desc)
+        dm = self.dm
+        if which == "bgmv_shrink":
+            st = lib.lora_bgmv_shrink(d, self.px[r], self.pA[r], self.v_b.data_ptr(),
+                                      dm["bgmv_tok"].data_ptr(), dm["bgmv_ids"].data_ptr(),
+                                      self.nb, self.T, stream_ptr)
+        elif which == "bgmv_expand":
+            st = lib.lora_bgmv_expand(d, self.v_b.data_ptr(), self.pB[r], self.py[r],
+                                      dm["bgmv_tok"].data_ptr(), dm["bgmv_ids"].data_ptr(),
+                                      self.nb, self.T, stream_ptr)
+        elif which == "sgmv_shrink":
+            st = lib.lora_sgmv_shrink(d, self.px[r], self.pA[r], self.v_s.data_ptr(),
+                                      dm["sgmv_perm"].data_ptr(), dm["seg_starts"].data_ptr(),
+                                      dm["seg_lens"].data_ptr(), dm["seg_ids"].data_ptr(),
+                                      int(self.meta["seg_ids"].size), self.ns, self.T, stream_ptr)
+        else:
+            st = lib.lora_sgmv_expand(d, self.v_s.data_ptr(), self.pB[r], self.py[r],
+                                      dm["sgmv_perm"].data_ptr(), dm["seg_starts"].data_ptr(),
+                                      dm["seg_lens"].data_ptr(), dm["seg_ids"].data_ptr(),
+                                      int(self.meta["seg_ids"].size), self.ns, self.T, stream_ptr)
+        if st != 0:
+            raise RuntimeError(f"{which} failed: {L.last_error()}")
+
+    def kernels(self):
+        ks = []
+        if self.ns:
+            ks += ["sgmv_shrink", "sgmv_expand"]
+        if self.nb:
+            ks += ["bgmv_shrink", "bgmv_expand"]
+        return ks
+
+
+def time_kernel(setups, which, launches, warm, stream_ptr):
+    """Average duration of back-to-back launches of one entry point, from HIP
+    events recorded on the launch stream around the loop."""
+    import torch
+    for i in range(warm):
+        for s in setups:
+            if which in s.kernels():
+                s.kernel_launch(which, i, stream_ptr)
+    n = 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(launches):
+        for s in setups:
+            if which in s.kernels():
+                s.kernel_launch(which, warm + i, stream_ptr)
+                n += 1
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / max(n, 1)  # us per launch
+
+
+def measure(setups, steps, warmup, stream_ptr):
+    """Whole steps (every call of the workload) timed between two synchronizes."""
+    import torch
+    for i in range(warmup):
+        for s in setups:
+            s.apply_step(i, stream_ptr)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for s in setups:
+            s.apply_step(warmup + i, stream_ptr)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def copy_bandwidth():
+    import torch
+    n = 1 << 28  # 256 Mi bf16 = 512 MiB per buffer
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    reps = 10
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    return 2 * n * 2 / sec / 1e9, 2 * n * 2
+
+
+def kernel_roofline(setups, stream_ptr, launches):
+    """Per-kernel average launch time and algorithmic-bytes rate; returns the
+    dominant kernel (largest total time per step)."""
+    algs = [algorithmic(s.wl) for s in setups]
+    res = {}
+    for which in ("sgmv_shrink", "sgmv_expand", "bgmv_shrink", "bgmv_expand"):
+        parts = [(s, a) for s, a in zip(setups, algs) if which in s.kernels()]
+        if not parts:
+            continue
+        us = time_kernel([p[0] for p in parts], which, launches, 10, stream_ptr)
+        by = 0
+        fl = 0
+        for s, a in parts:
+            stage = "shrink" if which.endswith("shrink") else "expand"
+            # bytes of the rows this kernel covers (weights of the adapters it touches)
+            ids = s.wl.ids
+            rows = ids[(ids >= 0) & (((s.wl.prefill == 1) | (s.wl.max_lora_rank > 64))
+                                     if which.startswith("sgmv") else
+                                     ~((s.wl.prefill == 1) | (s.wl.max_lora_rank > 64)))]
+            e = 2 if s.wl.dtype == "bf16" else 4
+            Ta, nact = int(rows.size), len(set(rows.tolist()))
+            K, R, S, O = s.wl.in_features, s.wl.max_lora_rank, s.wl.num_slices, s.wl.O
+            if stage == "shrink":
+                by += Ta * K * e + nact * S * R * K * e + Ta * S * R * 4
+                fl += 2 * Ta * R * S * K
+            else:
+                by += nact * R * O * e + Ta * S * R * 4 + 2 * Ta * O * e
+                fl += 2 * Ta * R * O
+        per_launch_bytes = by / len(parts)
+        per_launch_flops = fl / len(parts)
+        res[which] = {"us": us, "bytes": per_launch_bytes, "flops": per_launch_flops,
+                      "GBs": per_launch_bytes / (us * 1e-6) / 1e9,
+                      "TFLOPs": per_launch_flops / (us * 1e-6) / 1e12,
+                      "step_us": us * len(parts)}
+    dom = max(res, key=lambda k: res[k]["step_us"])
+    return dom, res
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters, valid only while the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+        ent = data.get(f"{workload}:{kernel}")
+        if not ent or ent.get("kernel_source_sha") != sha:
+            return None
+        return float(ent["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl, seconds):
+    """The fp64 oracle as it stands, single BLAS thread, over whole batches of
+    the same workload until `seconds` of CPU time are used."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        rows = list(range(wl.T))
+        Ta = int((wl.ids >= 0).sum())
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            oracle.lora_forward_rows(wl, rows)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        el = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": n * Ta / el, "unit": "LoRA-delta tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full batches of the same workload ({n * Ta} active tokens) through "
+                      f"the per-token fp64 oracle in {el:.1f} s; one BLAS thread; host CPU: {cpu}; "
+                      f"{len(os.sched_getaffinity(0))} cores visible"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(token rows are independent, so data parallelism needs no "
+                                   "exchange; see the sharding notes in the design document)"}))
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream_ptr = torch.cuda.current_stream().cuda_stream
+    t_start = time.perf_counter()
+
+    wls = make_workloads(args.workload, args.seed)
+    log(f"[bench] workload {args.workload}: T={wls[0].T} dtype={wls[0].dtype}")
+    rep_bytes = args.replica_mib * 2 ** 20 / len(wls)
+    setups = [Setup(wl, rep_bytes) for wl in wls]
+    log(f"[bench] replicas {[s.nrep for s in setups]} ({sum(s.nrep * s.bytes_per_rep for s in setups) / 2**20:.0f} MiB)")
+
+    el = measure(setups, args.steps, args.warmup, stream_ptr)
+    algs = [algorithmic(s.wl) for s in setups]
+    Ta = sum(a["Ta"] for a in algs)
+    step_s = el / args.steps
+    value = Ta / step_s
+    log(f"[bench] {args.steps} steps in {el:.3f} s: {step_s * 1e6:.1f} us/step")
+
+    launches = max(50, min(400, args.steps))
+    dom, per_kernel = kernel_roofline(setups, stream_ptr, launches)
+    for k, r in per_kernel.items():
+        log(f"[bench] {k}: {r['us']:.2f} us/launch, {r['GBs']:.0f} GB/s algorithmic, "
+            f"{r['TFLOPs']:.1f} TFLOP/s")
+    d = per_kernel[dom]
+    traffic = load_traffic(dom, args.workload)
+    copy_gbs, _ = copy_bandwidth()
+    log(f"[bench] device copy bandwidth {copy_gbs:.0f} GB/s")
+    kernel_us_step = sum(r["step_us"] for r in per_kernel.values())
+    total_bytes = sum(a["bytes"] for a in algs)
+
+    out = {
+        "metric": "LoRA-delta tokens/s + achieved HBM GB/s (% peak), BGMV decode and SGMV prefill",
+        "value": value,
+        "unit": "LoRA-delta tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wls[0].dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": {"bgmv_decode": "BGMV decode bf16: in=out=3072, 64 single-token rows, "
+                                        "8 adapters rank 16 alpha 32, 10% rows without adapter",
+                         "sgmv_prefill": "SGMV prefill bf16: in=out=4096, 16 sequences of 64..1024 "
+                                         "tokens, 16 adapters ranks {8,16,32,64} padded to 64",
+                         "qkv_decode": "fused QKV decode bf16: in=4096, q/k/v=4096/1024/1024, 256 "
+                                       "tokens, 64 adapters rank 16 Zipf(1.1), rsLoRA",
+                         "mlp_mixed": "mixed MLP bf16: gate_up 4096->2x14336 and down 14336->4096, "
+                                      "8 prefill sequences + 256 decode tokens, 32 adapters"
+                         }[args.workload],
+            "tokens": wls[0].T, "active_tokens": Ta, "adapters_active": algs[0]["n_act"],
+            "replicas": setups[0].nrep, "seed": args.seed,
+        },
+        "achieved_GBs_step": total_bytes / step_s / 1e9,
+        "frac_hbm_peak_step": total_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+        "kernel_us_per_step": kernel_us_step,
+        "achieved_GBs_kernels": total_bytes / (kernel_us_step * 1e-6) / 1e9,
+        "copy_GBs_measured": copy_gbs,
+        "per_kernel": {k: {"us": round(r["us"], 3), "GBs": round(r["GBs"], 1),
+                           "TFLOPs": round(r["TFLOPs"], 2)} for k, r in per_kernel.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": d["GBs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": d["GBs"] / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": d["bytes"],
+                     "avg_launch_us": d["us"]},
+    }
+    del setups
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.workload != "sgmv_prefill":
+        wl2 = make_workloads("sgmv_prefill", args.seed)
+        s2 = [Setup(w, args.replica_mib * 2 ** 20) for w in wl2]
+        el2 = measure(s2, max(20, args.steps // 10), 5, stream_ptr)
+        st2 = el2 / max(20, args.steps // 10)
+        a2 = algorithmic(wl2[0])
+        dom2, pk2 = kernel_roofline(s2, stream_ptr, 50)
+        kus = sum(r["step_us"] for r in pk2.values())
+        out["secondary"] = {
+            "workload": "SGMV prefill bf16: in=out=4096, 16 sequences of 64..1024 tokens, "
+                        "16 adapters ranks {8,16,32,64} padded to 64",
+            "tokens_per_s": a2["Ta"] / st2, "ms_per_step": st2 * 1e3,
+            "achieved_GBs_step": a2["bytes"] / st2 / 1e9,
+            "achieved_GBs_kernels": a2["bytes"] / (kus * 1e-6) / 1e9,
+            "frac_hbm_peak_kernels": a2["bytes"] / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "mfma_tflops_kernels": a2["flops"] / (kus * 1e-6) / 1e12,
+            "mfma_util_of_peak": a2["flops"] / (kus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "per_kernel": {k: {"us": round(r["us"], 2), "GBs": round(r["GBs"], 1),
+                               "TFLOPs": round(r["TFLOPs"], 1)} for k, r in pk2.items()},
+            "dominant_kernel": dom2,
+        }
+        for k, r in pk2.items():
+            log(f"[bench] prefill {k}: {r['us']:.2f} us/launch, {r['GBs']:.0f} GB/s, "
+                f"{r['TFLOPs']:.1f} TFLOP/s")
+        del s2
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(wls[0], args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    out["wall_s"] = time.perf_counter() - t_start
+    out["host"] = platform.node()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,29 +53,40 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Element access: 8 consecutive elements travel as one Raw (16 bytes of bf16
+// or 32 bytes of fp32) and are widened to fp32 only where they are used.
 template <typename E> struct El;
 
 template <> struct El<float> {
-  static __device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 4);
-    o[0] = __uint_as_float(a.x); o[1] = __uint_as_float(a.y);
-    o[2] = __uint_as_float(a.z); o[3] = __uint_as_float(a.w);
-    o[4] = __uint_as_float(b.x); o[5] = __uint_as_float(b.y);
-    o[6] = __uint_as_float(b.z); o[7] = __uint_as_float(b.w);
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  struct Raw { u32x4 a, b; };
+  static __device__ __forceinline__ Raw raw8(const float* p) { return {ld16(p), ld16(p + 4)}; }
+  static __device__ __forceinline__ void mask(Raw& r, uint32_t m) { r.a &= m; r.b &= m; }
+  static __device__ __forceinline__ void unpack(const Raw& r, float (&o)[8]) {
+    o[0] = __uint_as_float(r.a.x); o[1] = __uint_as_float(r.a.y);
+    o[2] = __uint_as_float(r.a.z); o[3] = __uint_as_float(r.a.w);
+    o[4] = __uint_as_float(r.b.x); o[5] = __uint_as_float(r.b.y);
+    o[6] = __uint_as_float(r.b.z); o[7] = __uint_as_float(r.b.w);
   }
+  static __device__ __forceinline__ void load8(const float* p, float (&o)[8]) { unpack(raw8(p), o); }
   static __device__ __forceinline__ float get(float v) { return v; }
   static __device__ __forceinline__ float put(float v) { return v; }
 };
 
 template <> struct El<uint16_t> {
-  static __device__ __forceinline__ void load8(const uint16_t* p, float (&o)[8]) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-    o[0] = __uint_as_float(a.x << 16); o[1] = __uint_as_float(a.x & 0xffff0000u);
-    o[2] = __uint_as_float(a.y << 16); o[3] = __uint_as_float(a.y & 0xffff0000u);
-    o[4] = __uint_as_float(a.z << 16); o[5] = __uint_as_float(a.z & 0xffff0000u);
-    o[6] = __uint_as_float(a.w << 16); o[7] = __uint_as_float(a.w & 0xffff0000u);
+  static constexpr int kVec = 8;
+  struct Raw { u32x4 a; };
+  static __device__ __forceinline__ Raw raw8(const uint16_t* p) { return {ld16(p)}; }
+  static __device__ __forceinline__ void mask(Raw& r, uint32_t m) { r.a &= m; }
+  static __device__ __forceinline__ void unpack(const Raw& r, float (&o)[8]) {
+    o[0] = __uint_as_float(r.a.x << 16); o[1] = __uint_as_float(r.a.x & 0xffff0000u);
+    o[2] = __uint_as_float(r.a.y << 16); o[3] = __uint_as_float(r.a.y & 0xffff0000u);
+    o[4] = __uint_as_float(r.a.z << 16); o[5] = __uint_as_float(r.a.z & 0xffff0000u);
+    o[6] = __uint_as_float(r.a.w << 16); o[7] = __uint_as_float(r.a.w & 0xffff0000u);
   }
+  static __device__ __forceinline__ void load8(const uint16_t* p, float (&o)[8]) { unpack(raw8(p), o); }
   static __device__ __forceinline__ float get(uint16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
   }
@@ -92,9 +103,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * q + min(x, r) + k;
 }
 
-// Locate tile `f` of a row list.  BGMV: fixed row ranges of TM rows.  SGMV:
-// tiles of TM rows inside each segment whose (clamped) length lies in
-// [seg_min, seg_max], in segment order.  Returns false past the last tile.
+// Locate tile `f` of a row list (called by every thread of a workgroup of up
+// to 1024 threads).
+// BGMV: fixed row ranges of TM rows.  SGMV: tiles of TM rows inside each
+// segment whose (clamped) length lies in [seg_min, seg_max], in segment order.
+// The segment arrays are read in parallel, one segment per thread per pass,
+// and a block-wide prefix sum of tile counts finds the segment holding
+// tile f, so the lookup costs one memory round trip rather than one per
+// segment.  Returns false (uniformly) past the last tile.
 template <int TM>
 __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int& cnt, int& sid) {
   if (L.ids) {
@@ -104,22 +120,58 @@ __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int&
     sid = -1;
     return true;
   }
-  for (int gi = 0; gi < L.num_segs; ++gi) {
-    const int st = L.seg_starts[gi];
-    int ln = L.seg_lens[gi];
-    if (st < 0 || st >= L.num_rows || ln <= 0) continue;
-    ln = min(ln, L.num_rows - st);
-    if (ln < L.seg_min || ln > L.seg_max) continue;
-    const int nt = (ln + TM - 1) / TM;
-    if (f < nt) {
-      r0 = st + f * TM;
-      cnt = min(TM, ln - f * TM);
-      sid = L.seg_ids[gi];
-      return true;
+  __shared__ int s_found[4];
+  __shared__ int s_wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nthr = blockDim.x, nw = nthr >> 6;
+  if (tid == 0) s_found[3] = 0;
+  int base = 0;
+  bool found = false;
+  for (int c0 = 0; c0 < L.num_segs; c0 += nthr) {
+    const int gi = c0 + tid;
+    int nt = 0, st = 0, ln = 0, id = -1;
+    if (gi < L.num_segs) {
+      st = L.seg_starts[gi];
+      ln = L.seg_lens[gi];
+      id = L.seg_ids[gi];
+      if (st >= 0 && st < L.num_rows && ln > 0) {
+        ln = min(ln, L.num_rows - st);
+        if (ln >= L.seg_min && ln <= L.seg_max) nt = (ln + TM - 1) / TM;
+      }
     }
-    f -= nt;
+    int inc = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (lane == 63) s_wsum[wv] = inc;
+    __syncthreads();
+    int wbase = 0, total = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int ws = s_wsum[w];
+      wbase += w < wv ? ws : 0;
+      total += ws;
+    }
+    const int excl = base + wbase + inc - nt;
+    if (nt > 0 && f >= excl && f < excl + nt) {
+      const int j = f - excl;
+      s_found[0] = st + j * TM;
+      s_found[1] = min(TM, ln - j * TM);
+      s_found[2] = id;
+      s_found[3] = 1;
+    }
+    __syncthreads();
+    found = s_found[3] != 0;
+    base += total;
+    if (found || f < base) break;
+    __syncthreads();  // s_wsum is rewritten by the next pass
   }
-  return false;
+  if (!found) return false;
+  r0 = s_found[0];
+  cnt = s_found[1];
+  sid = s_found[2];
+  return true;
 }
 
 // Token and adapter slot of each tile row; bit r of the result marks row r valid.
@@ -190,17 +242,22 @@ __device__ __forceinline__ float wave_sum_many(float (&val)[V], int lane) {
 
 // ------------------------------------------------------------ shrink (VALU)
 //
-// grid.x = tiles * S * (R / RC).  Workgroup (tile, slice s, rank chunk c)
-// computes v[row][s][c*RC .. c*RC+RC) for the tile's rows.  Wave w covers the
-// K chunks w, w+4, ... of 512 elements (8 per lane).
+// grid.x = tiles * S * (R / RC), blockDim = 64 * W with W = min(16, K / 512
+// rounded up).  Workgroup (tile, slice s, rank chunk c) computes
+// v[row][s][c*RC .. c*RC+RC) for the tile's rows.  Wave w covers the 512-wide
+// K chunks w, w + W, ... (8 elements per lane, one 16-byte load per row and
+// adapter row), so for K <= 8192 each wave issues all of its loads at once.
+// Loads are unconditional (out-of-range lanes read a clamped address and are
+// zeroed), which keeps the memory counters exact and the loads in flight.
 template <typename E, int TM, int RC>
-__global__ __launch_bounds__(256) void shrink_wave_kernel(const E* __restrict__ x,
-                                                          const E* __restrict__ A,
-                                                          float* __restrict__ v, RowList L,
-                                                          Geo g) {
+__global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__ x,
+                                                           const E* __restrict__ A,
+                                                           float* __restrict__ v, RowList L,
+                                                           Geo g) {
   constexpr int V = RC * TM;
   constexpr int P = Log2<V>::value;
-  __shared__ float red[4][V];
+  __shared__ float red[16][V];
+  const int W = blockDim.x >> 6;
   const int nrc = g.R / RC;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_tile = g.S * nrc;
@@ -215,6 +272,7 @@ __global__ __launch_bounds__(256) void shrink_wave_kernel(const E* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int SR = g.S * g.R;
+  const int nchunk = (g.K + 511) / 512;
 
   while (todo) {
     int a;
@@ -224,20 +282,31 @@ __global__ __launch_bounds__(256) void shrink_wave_kernel(const E* __restrict__ 
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
     const E* Ab = A + ((size_t)(a * g.S + s) * g.R + (size_t)c * RC) * g.K;
-    for (int k0 = wave * 512 + lane * 8; k0 < g.K; k0 += 4 * 512) {
-      float av[RC][8];
+    for (int q = wave; q < nchunk; q += W) {
+      const int k0 = q * 512 + lane * 8;
+      const bool kin = k0 < g.K;
+      const int kc = kin ? k0 : 0;
+      const uint32_t kmask = kin ? 0xffffffffu : 0u;
+      typename El<E>::Raw ar[RC], xr[TM];
 #pragma unroll
-      for (int rr = 0; rr < RC; ++rr) El<E>::load8(Ab + (size_t)rr * g.K + k0, av[rr]);
+      for (int rr = 0; rr < RC; ++rr) ar[rr] = El<E>::raw8(Ab + (size_t)rr * g.K + kc);
+#pragma unroll
+      for (int r = 0; r < TM; ++r) xr[r] = El<E>::raw8(x + (size_t)tok[r] * g.K + kc);
+      float af[RC][8];
+#pragma unroll
+      for (int rr = 0; rr < RC; ++rr) {
+        El<E>::mask(ar[rr], kmask);  // lanes past K contribute zero
+        El<E>::unpack(ar[rr], af[rr]);
+      }
 #pragma unroll
       for (int r = 0; r < TM; ++r) {
-        if (!((m >> r) & 1u)) continue;
-        float xv[8];
-        El<E>::load8(x + (size_t)tok[r] * g.K + k0, xv);
+        float xf[8];
+        El<E>::unpack(xr[r], xf);
 #pragma unroll
         for (int rr = 0; rr < RC; ++rr) {
           float d = acc[rr * TM + r];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) d = fmaf(av[rr][e], xv[e], d);
+          for (int e = 0; e < 8; ++e) d = fmaf(af[rr][e], xf[e], d);
           acc[rr * TM + r] = d;
         }
       }
@@ -249,7 +318,8 @@ __global__ __launch_bounds__(256) void shrink_wave_kernel(const E* __restrict__ 
       const int idx = threadIdx.x;
       const int rr = idx / TM, r = idx - rr * TM;
       if ((m >> r) & 1u) {
-        const float tot = ((red[0][idx] + red[1][idx]) + red[2][idx]) + red[3][idx];
+        float tot = 0.f;
+        for (int w = 0; w < W; ++w) tot += red[w][idx];
         v[(size_t)(r0 + r) * SR + s * g.R + c * RC + rr] = tot;
       }
     }
@@ -260,8 +330,11 @@ __global__ __launch_bounds__(256) void shrink_wave_kernel(const E* __restrict__ 
 // ------------------------------------------------------------ expand (VALU)
 //
 // grid.x = tiles * column chunks (kExpandCols columns of one slice each).
-// Thread j owns output column col0 + j; the tile's B block is staged in LDS
-// 64 ranks at a time, v rows are staged once.
+// Thread j owns output column col0 + j.  Per adapter group the tile's B block
+// (64 ranks per pass) and the group's v rows are staged in LDS: every thread
+// first issues all of its global loads (contiguous 16-byte vectors), then
+// writes LDS, so the copy costs one memory round trip.  B rows are padded by
+// 16 bytes in LDS, which makes the row-per-thread reads conflict-free.
 template <typename E, int TM>
 __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restrict__ v,
                                                           const E* __restrict__ B,
@@ -269,11 +342,16 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
                                                           Chunks ch) {
   constexpr int NC = kExpandCols;      // 256 columns per workgroup
   constexpr int KB = 64;               // ranks staged per pass
-  constexpr int PAD = 16 / sizeof(E);  // row padding: 16 bytes
+  constexpr int VEC = El<E>::kVec;     // elements per 16-byte vector
+  constexpr int PAD = VEC;             // row padding: 16 bytes
   constexpr int LDB = KB + PAD;
+  constexpr int MAXV = NC * KB / VEC / 256;  // B vectors per thread per pass
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  E* Bs = reinterpret_cast<E*>(lds_raw);                                   // [NC][LDB]
-  float* vs = reinterpret_cast<float*>(lds_raw + sizeof(E) * NC * LDB);    // [TM][R]
+  // Bs: NC staged rows plus one dump row that absorbs stores of idle lanes (so
+  // no store, and hence no load feeding it, sits under a branch); vs: TM rows
+  // of v plus a 16-byte dump slot
+  E* Bs = reinterpret_cast<E*>(lds_raw);                                       // [NC + 1][LDB]
+  float* vs = reinterpret_cast<float*>(lds_raw + sizeof(E) * (NC + 1) * LDB);  // [TM * R + 4]
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / ch.total;
@@ -291,33 +369,73 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
   const int tid = threadIdx.x;
   const int R = g.R;
   const int SR = g.S * R;
+  // y of every valid row is read up front so its latency overlaps the B / v
+  // staging; each row is written exactly once, by the group that owns it
+  const int colc = tid < ncv ? tid : 0;
+  E* yb = y + g.off[s] + col0 + colc;
+  float yv[TM];
+#pragma unroll
+  for (int r = 0; r < TM; ++r) yv[r] = El<E>::get(yb[(size_t)tok[r] * g.O]);
 
   while (todo) {
     int a;
     const uint32_t m = next_group<TM>(todo, aid, a);
     todo &= ~m;
-    // v rows of this group (zeros for rows outside it)
-    for (int i = tid; i < TM * R; i += 256) {
-      const int r = i / R, k = i - r * R;
-      vs[i] = ((m >> r) & 1u) ? v[(size_t)(r0 + r) * SR + s * R + k] : 0.f;
-    }
     float acc[TM];
 #pragma unroll
     for (int r = 0; r < TM; ++r) acc[r] = 0.f;
     const E* Bg = B + ((size_t)a * g.O + g.off[s] + col0) * R;
     for (int kb = 0; kb < R; kb += KB) {
       const int kw = min(KB, R - kb);   // multiple of 8
-      const int vpr = kw / 8;           // 8-element vectors per staged row
-      __syncthreads();                  // previous readers of Bs are done
-      for (int i = tid; i < ncv * vpr; i += 256) {
-        const int row = i / vpr, q = i - row * vpr;
-        const E* src = Bg + (size_t)row * R + kb + q * 8;
-        E* dst = Bs + row * LDB + q * 8;
-        if constexpr (sizeof(E) == 2) {
-          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-        } else {
-          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-          *reinterpret_cast<u32x4*>(dst + 4) = *reinterpret_cast<const u32x4*>(src + 4);
+      const int vpr = kw / VEC;         // vectors per staged row
+      const int nvec = ncv * vpr;
+      u32x4 braw[MAXV];
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int idx = tid + 256 * j;
+        const bool ok = idx < nvec;
+        const int row = ok ? idx / vpr : 0;
+        const int q = ok ? idx - row * vpr : 0;
+        braw[j] = ld16(Bg + (size_t)row * R + kb + q * VEC);
+      }
+      // v rows of this group (zeros for rows outside it), on the first pass
+      constexpr int NVV = (TM * 256 / 4 + 255) / 256;  // up to R = 256 in one go
+      f32x4 vraw[NVV];
+      const int nv4 = TM * R / 4;
+      if (kb == 0) {
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+          const int i = tid + 256 * j;
+          const int r = i < nv4 ? (i * 4) / R : 0;
+          const bool mem = i < nv4 && ((m >> r) & 1u);
+          const int k = mem ? i * 4 - r * R : 0;
+          const u32x4 raw = ld16(v + (size_t)(r0 + (mem ? r : 0)) * SR + s * R + k) &
+                            (mem ? 0xffffffffu : 0u);
+          vraw[j] = __builtin_bit_cast(f32x4, raw);
+        }
+      }
+      __syncthreads();                  // previous readers of Bs / vs are done
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int idx = tid + 256 * j;
+        const bool ok = idx < nvec;
+        const int row = ok ? idx / vpr : NC;
+        const int q = ok ? idx - row * vpr : 0;
+        *reinterpret_cast<u32x4*>(Bs + row * LDB + q * VEC) = braw[j];
+      }
+      if (kb == 0) {
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+          const int i = tid + 256 * j;
+          *reinterpret_cast<f32x4*>(vs + (i < nv4 ? i * 4 : nv4 * 4)) = vraw[j];
+        }
+        for (int i = tid + 256 * NVV; i < nv4; i += 256) {  // R > 256: rare, plain loop
+          const int r = (i * 4) / R;
+          const bool mem = (m >> r) & 1u;
+          const int k = i * 4 - r * R;
+          *reinterpret_cast<f32x4*>(vs + i * 4) =
+              mem ? *reinterpret_cast<const f32x4*>(v + (size_t)(r0 + r) * SR + s * R + k)
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
       __syncthreads();
@@ -327,7 +445,6 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
           El<E>::load8(Bs + tid * LDB + k, b);
 #pragma unroll
           for (int r = 0; r < TM; ++r) {
-            if (!((m >> r) & 1u)) continue;
             const float* vr = vs + r * R + kb + k;
             float d = acc[r];
 #pragma unroll
@@ -340,93 +457,104 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
     if (tid < ncv) {
 #pragma unroll
       for (int r = 0; r < TM; ++r) {
-        if (!((m >> r) & 1u)) continue;
-        E* yp = y + (size_t)tok[r] * g.O + g.off[s] + col0 + tid;
-        *yp = El<E>::put(El<E>::get(*yp) + acc[r]);
+        if ((m >> r) & 1u) yb[(size_t)tok[r] * g.O] = El<E>::put(yv[r] + acc[r]);
       }
     }
-    __syncthreads();  // vs is rewritten by the next group
+    __syncthreads();  // Bs / vs are rewritten by the next group
   }
 }
 
 // ------------------------------------------------------------ shrink (MFMA)
 //
 // bf16 only.  grid.x = tiles(32 rows) * S, grid.y = rank blocks of 64.
-// Wave (wm, wk): rows 16*wm .. +16 of the tile, K steps of 128 with index
-// congruent to wk mod 2.  Per step each lane loads 4 x 16 bytes of its x row
-// and of each of NT adapter rows; MFMA p covers k in [k0 + 32p, k0 + 32p + 32),
+// Wave (wm, wr) computes rows 16*wm .. +16 of the tile against ranks
+// 32*wr .. +32 of the block (two 16-rank MFMA tiles), over the whole K range in
+// steps of 128.  Per step each lane loads 64 bytes of its x row and 64 bytes of
+// each of its two adapter rows; MFMA p covers k in [k0 + 32p, k0 + 32p + 32),
 // lane group g = lane / 16 holding k0 + 32p + 8g .. +8 of both operands.
-template <int NT>
+// Loads run three steps ahead of the MFMAs (register ring), which is what
+// keeps HBM busy when only about one workgroup per CU exists.  Ranks >= R are
+// masked (no load, no store), so any R that is a multiple of 8 is accepted.
 __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ A,
                                                           float* __restrict__ v, RowList L,
                                                           Geo g) {
   constexpr int TMR = 32;
-  __shared__ f32x4 part[2][NT][64];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / g.S;
   const int s = bid - f * g.S;
-  const int rank0 = blockIdx.y * 64;
   int r0, cnt, sid;
   if (!find_tile<TMR>(L, f, r0, cnt, sid)) return;
   if (sid < 0 || sid >= g.max_loras) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wk = wave >> 1;
+  const int wm = wave & 1, wr = wave >> 1;
   const int i16 = lane & 15, grp = lane >> 4;
-  const int row = 16 * wm + i16;  // operand row of this lane
+  const int row = 16 * wm + i16;  // x-operand row of this lane
   int t = -1;
   if (row < cnt) t = L.tok[r0 + row];
   const bool xrow_ok = t >= 0 && t < g.T;
   const uint16_t* xr = x + (size_t)(xrow_ok ? t : 0) * g.K;
-  const uint16_t* Ab = A + ((size_t)(sid * g.S + s) * g.R + rank0 + i16) * g.K;
+  const int rbase = blockIdx.y * 64 + 32 * wr;  // first rank of this wave
+  const bool rk_ok0 = rbase + i16 < g.R, rk_ok1 = rbase + 16 + i16 < g.R;
+  const uint16_t* A0 =
+      A + ((size_t)(sid * g.S + s) * g.R + (rk_ok0 ? rbase + i16 : 0)) * g.K;
+  const uint16_t* A1 =
+      A + ((size_t)(sid * g.S + s) * g.R + (rk_ok1 ? rbase + 16 + i16 : 0)) * g.K;
 
-  f32x4 acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = wk * 128; k0 < g.K; k0 += 256) {
-    u32x4 xf[4];
-    u32x4 af[NT][4];
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  u32x4 xs[3][4], as0[3][4], as1[3][4];
+  // masks instead of selects: a select on a loaded value lets the compiler
+  // sink the load into a branch, which serialises the pipeline
+  const uint32_t xmask = xrow_ok ? 0xffffffffu : 0u;
+  const uint32_t amask0 = rk_ok0 ? 0xffffffffu : 0u, amask1 = rk_ok1 ? 0xffffffffu : 0u;
+  // loads are unconditional (clamped address, value masked afterwards) so the
+  // compiler can keep several steps in flight with exact wait counts
+  auto load_step = [&](int k0, u32x4(&xf)[4], u32x4(&a0)[4], u32x4(&a1)[4]) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int kp = k0 + 32 * p + 8 * grp;
       const bool in = kp < g.K;
-      xf[p] = (in && xrow_ok) ? *reinterpret_cast<const u32x4*>(xr + kp) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        af[n][p] = in ? *reinterpret_cast<const u32x4*>(Ab + (size_t)(16 * n) * g.K + kp)
-                      : u32x4{0, 0, 0, 0};
+      const int kc = in ? kp : 0;
+      const uint32_t kin = in ? 0xffffffffu : 0u;
+      xf[p] = ld16(xr + kc) & (kin & xmask);
+      a0[p] = ld16(A0 + kc) & (kin & amask0);
+      a1[p] = ld16(A1 + kc) & (kin & amask1);
     }
+  };
+  auto mma_step = [&](const u32x4(&xf)[4], const u32x4(&a0)[4], const u32x4(&a1)[4]) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const bf16x8 xa = __builtin_bit_cast(bf16x8, xf[p]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, af[n][p]),
-                                                         acc[n], 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, a0[p]), acc0,
+                                                     0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, a1[p]), acc1,
+                                                     0, 0, 0);
     }
+  };
+  const int nsteps = (g.K + 127) / 128;
+  load_step(0, xs[0], as0[0], as1[0]);
+  load_step(128, xs[1], as0[1], as1[1]);
+  for (int i = 0; i < nsteps; i += 3) {
+    load_step((i + 2) * 128, xs[2], as0[2], as1[2]);
+    mma_step(xs[0], as0[0], as1[0]);
+    if (i + 1 >= nsteps) break;
+    load_step((i + 3) * 128, xs[0], as0[0], as1[0]);
+    mma_step(xs[1], as0[1], as1[1]);
+    if (i + 2 >= nsteps) break;
+    load_step((i + 4) * 128, xs[1], as0[1], as1[1]);
+    mma_step(xs[2], as0[2], as1[2]);
   }
-  if (wk == 1) {
+  // D layout: lane holds rows 4*grp + j (j < 4) of column i16
+  const int SR = g.S * g.R;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) part[wm][n][lane] = acc[n];
-  }
-  __syncthreads();
-  if (wk == 0) {
-    const int SR = g.S * g.R;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const f32x4 o = part[wm][n][lane];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int orow = 16 * wm + 4 * grp + j;  // D row of this lane
-        if (orow < cnt) {
-          const int tt = L.tok[r0 + orow];
-          if (tt >= 0 && tt < g.T)
-            v[(size_t)(r0 + orow) * SR + s * g.R + rank0 + 16 * n + i16] = acc[n][j] + o[j];
-        }
-      }
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int orow = 16 * wm + 4 * grp + j;
+    const bool ok = __shfl(xrow_ok ? 1 : 0, 4 * grp + j, 16) != 0;  // row's token is valid
+    if (!ok || orow >= cnt) continue;
+    float* vr = v + (size_t)(r0 + orow) * SR + s * g.R;
+    if (rk_ok0) vr[rbase + i16] = acc0[j];
+    if (rk_ok1) vr[rbase + 16 + i16] = acc1[j];
   }
 }
 
@@ -479,6 +607,22 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
     ccol[nt] = cbase + 32 * q + 8 * (m16 >> 2) + 4 * hi + (m16 & 3);
   }
 
+  // y words of this lane (issued before the MFMA loop so the latency overlaps)
+  uint16_t* yr = y + (size_t)(tok_ok ? t : 0) * g.O + g.off[s];
+  u32x4 yw[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = cbase + 32 * q + 8 * grp;
+    yw[q] = ld16(yr + (c < out_s ? c : 0));
+  }
+
+  // validity as bit masks (a select on a loaded value lets the compiler sink
+  // the load into a branch and serialise the loop)
+  const uint32_t tmask = tok_ok ? 0xffffffffu : 0u;
+  uint32_t cmask[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) cmask[nt] = ccol[nt] < out_s ? 0xffffffffu : 0u;
+
   f32x4 acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -487,11 +631,19 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
     const int kk = kb + 8 * grp;
     const bool kin = kk < R;
     // v (fp32) -> hi + lo bf16
-    u32x4 vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
-    if (kin && tok_ok) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(vr + kk);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(vr + kk + 4);
-      const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    u32x4 vh, vl;
+    u32x4 bw[4];
+    {
+      const int kc = kin ? kk : 0;
+      const uint32_t kmask = kin ? 0xffffffffu : 0u;
+      const u32x4 a = ld16(vr + kc) & (kmask & tmask);
+      const u32x4 b = ld16(vr + kc + 4) & (kmask & tmask);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        bw[nt] = ld16(Bb + (size_t)(ccol[nt] < out_s ? ccol[nt] : 0) * R + kc) & (kmask & cmask[nt]);
+      const float e[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                          __uint_as_float(a.w), __uint_as_float(b.x), __uint_as_float(b.y),
+                          __uint_as_float(b.z), __uint_as_float(b.w)};
       uint32_t h[8], l[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -505,23 +657,19 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
     const bf16x8 bl = __builtin_bit_cast(bf16x8, vl);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      u32x4 bw = {0, 0, 0, 0};
-      if (kin && ccol[nt] < out_s) bw = *reinterpret_cast<const u32x4*>(Bb + (size_t)ccol[nt] * R + kk);
-      const bf16x8 ba = __builtin_bit_cast(bf16x8, bw);
+      const bf16x8 ba = __builtin_bit_cast(bf16x8, bw[nt]);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bh, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bl, acc[nt], 0, 0, 0);
     }
   }
   if (!tok_ok) return;
-  uint16_t* yr = y + (size_t)t * g.O + g.off[s];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int c = cbase + 32 * q + 8 * grp;
     if (c >= out_s) continue;
-    u32x4 yw = *reinterpret_cast<const u32x4*>(yr + c);
     const f32x4 d0 = acc[2 * q], d1 = acc[2 * q + 1];
     const float add[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-    uint32_t w[4] = {yw.x, yw.y, yw.z, yw.w};
+    uint32_t w[4] = {yw[q].x, yw[q].y, yw[q].z, yw[q].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float lo = __uint_as_float(w[i] << 16) + add[2 * i];
@@ -581,8 +729,13 @@ static Chunks make_chunks(const Geo& g, int nc) {
 // segment lengths, otherwise an upper bound (surplus workgroups exit at once).
 static int64_t count_tiles(const RowList& L, int tm, const int32_t* host_seg_starts,
                            const int32_t* host_seg_lens) {
-  if (L.ids) return (L.num_rows + tm - 1) / tm;
-  if (!host_seg_lens) return (int64_t)(L.num_rows + tm - 1) / tm + L.num_segs;
+  if (L.ids) return ((int64_t)L.num_rows + tm - 1) / tm;
+  if (!host_seg_lens) {
+    int64_t n = ((int64_t)L.num_rows + tm - 1) / tm + L.num_segs;
+    if (L.seg_max < INT32_MAX)  // every covered segment is at most seg_max rows long
+      n = std::min<int64_t>(n, (int64_t)L.num_segs * (((int64_t)L.seg_max + tm - 1) / tm));
+    return n;
+  }
   int64_t n = 0;
   for (int i = 0; i < L.num_segs; ++i) {
     const int st = host_seg_starts[i];
@@ -604,23 +757,18 @@ static int sgmv_mfma_min_rows() {
   return v;
 }
 
-static bool mfma_eligible(const Geo& g) { return g.dtype == LORA_BF16 && g.R % 16 == 0; }
+static bool mfma_eligible(const Geo& g) { return g.dtype == LORA_BF16; }
 
 template <typename E>
 static int32_t launch_shrink_wave(const Geo& g, const void* x, const void* A, float* v,
                                   const RowList& L, int64_t tiles, hipStream_t st) {
   if (tiles <= 0) return LORA_OK;
-  if (g.R % 8 == 0 && g.R >= 64) {
-    const int64_t grid = tiles * g.S * (g.R / 8);
-    if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
-    hipLaunchKernelGGL((shrink_wave_kernel<E, kWaveTileRows, 8>), dim3((unsigned)grid), dim3(256),
-                       0, st, (const E*)x, (const E*)A, v, L, g);
-  } else {
-    const int64_t grid = tiles * g.S * (g.R / 4);
-    if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
-    hipLaunchKernelGGL((shrink_wave_kernel<E, kWaveTileRows, 4>), dim3((unsigned)grid), dim3(256),
-                       0, st, (const E*)x, (const E*)A, v, L, g);
-  }
+  const int waves = std::min(16, (g.K + 511) / 512);
+  const dim3 block(64 * waves);
+  const int64_t grid = tiles * g.S * (g.R / 4);
+  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
+  hipLaunchKernelGGL((shrink_wave_kernel<E, kWaveTileRows, 4>), dim3((unsigned)grid), block, 0,
+                     st, (const E*)x, (const E*)A, v, L, g);
   return hip_check("shrink_wave launch");
 }
 
@@ -631,8 +779,8 @@ static int32_t launch_expand_wave(const Geo& g, const float* v, const void* B, v
   const Chunks ch = make_chunks(g, kExpandCols);
   const int64_t grid = tiles * ch.total;
   if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
-  const size_t lds = sizeof(E) * kExpandCols * (64 + 16 / sizeof(E)) +
-                     sizeof(float) * kWaveTileRows * g.R;
+  const size_t lds = sizeof(E) * (kExpandCols + 1) * (64 + 16 / sizeof(E)) +
+                     sizeof(float) * (kWaveTileRows * g.R + 4);
   if (lds > 160 * 1024) return fail(LORA_E_SHAPE, "max_lora_rank too large for the expand kernel");
   hipLaunchKernelGGL((expand_wave_kernel<E, kWaveTileRows>), dim3((unsigned)grid), dim3(256), lds,
                      st, v, (const E*)B, (E*)y, L, g, ch);
@@ -644,30 +792,10 @@ static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, fl
   if (tiles <= 0) return LORA_OK;
   const int64_t gx = tiles * g.S;
   if (gx > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
-  const int full = g.R / 64, rest = (g.R % 64) / 16;
-  if (full > 0) {
-    hipLaunchKernelGGL((shrink_mfma_kernel<4>), dim3((unsigned)gx, full), dim3(256), 0, st,
-                       (const uint16_t*)x, (const uint16_t*)A, v, L, g);
-    if (int32_t e = hip_check("shrink_mfma launch")) return e;
-  }
-  if (rest > 0) {
-    // remaining ranks: shift A and v by the full blocks via blockIdx.y offset
-    Geo g2 = g;
-    const int off = full * 64;
-    // A rows and v columns start at rank `off`; kernels index rank0 = blockIdx.y*64 = 0
-    const uint16_t* A2 = (const uint16_t*)A + (size_t)off * g.K;
-    float* v2 = v + off;
-    switch (rest) {
-      case 1: hipLaunchKernelGGL((shrink_mfma_kernel<1>), dim3((unsigned)gx, 1), dim3(256), 0, st,
-                                 (const uint16_t*)x, A2, v2, L, g2); break;
-      case 2: hipLaunchKernelGGL((shrink_mfma_kernel<2>), dim3((unsigned)gx, 1), dim3(256), 0, st,
-                                 (const uint16_t*)x, A2, v2, L, g2); break;
-      default: hipLaunchKernelGGL((shrink_mfma_kernel<3>), dim3((unsigned)gx, 1), dim3(256), 0, st,
-                                  (const uint16_t*)x, A2, v2, L, g2); break;
-    }
-    if (int32_t e = hip_check("shrink_mfma launch")) return e;
-  }
-  return LORA_OK;
+  const unsigned gy = (unsigned)((g.R + 63) / 64);
+  hipLaunchKernelGGL(shrink_mfma_kernel, dim3((unsigned)gx, gy), dim3(256), 0, st,
+                     (const uint16_t*)x, (const uint16_t*)A, v, L, g);
+  return hip_check("shrink_mfma launch");
 }
 
 static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, void* y,
