@@ -122,16 +122,14 @@ class Setup:
         self.stage = [torch.empty(self.mh_bytes, dtype=torch.uint8, pin_memory=True)
                       for _ in range(self.nstage)]
         self.stage_ev = [None] * self.nstage
-        # prebuilt device metadata for the kernel-only loops
-        m = L.lora_build_meta(self.ids, self.pre, wl.max_loras, wl.max_lora_rank)
-        self.meta = m
-        tt = lambda a: torch.from_numpy(np.ascontiguousarray(a.astype(np.int32)) if a.size else  # noqa
-                                        np.zeros(1, np.int32)).cuda()
-        self.dm = {k: tt(v) for k, v in m.items()}
+        # the batch's tile plan, copied once, for the kernel-only loops (the same
+        # launches lora_apply makes after its own plan copy)
+        self.plan_d, img, _ = L.lora_apply_plan(self.desc, self.ids, self.pre)
+        self.plan = L.plan_struct(self.plan_d)
+        self.image = torch.from_numpy(img if img.size else np.zeros(4, np.int32)).cuda()
+        rows = self.plan_d["num_sgmv_rows"] + self.plan_d["num_bgmv_rows"]
         S, R = wl.num_slices, wl.max_lora_rank
-        self.ns, self.nb = int(m["sgmv_perm"].size), int(m["bgmv_tok"].size)
-        self.v_s = torch.zeros((max(self.ns, 1), S * R), dtype=torch.float32, device="cuda")
-        self.v_b = torch.zeros((max(self.nb, 1), S * R), dtype=torch.float32, device="cuda")
+        self.v = torch.zeros((max(rows, 1), S * R), dtype=torch.float32, device="cuda")
         self.bytes_per_rep = per
         torch.cuda.synchronize()
 
@@ -154,61 +152,55 @@ class Setup:
         self.stage_ev[j] = ev
 
     def kernel_launch(self, which, i, stream_ptr):
+        """One launch group of the plan: 'shrink' or 'expand' (replica i)."""
         L = self.L
         lib = L.lib()
         r = i % self.nrep
         d = ctypes.byref(self.desc)
-        dm = self.dm
-        if which == "bgmv_shrink":
-            st = lib.lora_bgmv_shrink(d, self.px[r], self.pA[r], self.v_b.data_ptr(),
-                                      dm["bgmv_tok"].data_ptr(), dm["bgmv_ids"].data_ptr(),
-                                      self.nb, self.T, stream_ptr)
-        elif which == "bgmv_expand":
-            st = lib.lora_bgmv_expand(d, self.v_b.data_ptr(), self.pB[r], self.py[r],
-                                      dm["bgmv_tok"].data_ptr(), dm["bgmv_ids"].data_ptr(),
-                                      self.nb, self.T, stream_ptr)
-        elif which == "sgmv_shrink":
-            st = lib.lora_sgmv_shrink(d, self.px[r], self.pA[r], self.v_s.data_ptr(),
-                                      dm["sgmv_perm"].data_ptr(), dm["seg_starts"].data_ptr(),
-                                      dm["seg_lens"].data_ptr(), dm["seg_ids"].data_ptr(),
-                                      int(self.meta["seg_ids"].size), self.ns, self.T, stream_ptr)
+        if which == "shrink":
+            st = lib.lora_plan_shrink(d, self.px[r], self.pA[r], self.v.data_ptr(), self.T,
+                                      ctypes.byref(self.plan), self.image.data_ptr(), stream_ptr)
         else:
-            st = lib.lora_sgmv_expand(d, self.v_s.data_ptr(), self.pB[r], self.py[r],
-                                      dm["sgmv_perm"].data_ptr(), dm["seg_starts"].data_ptr(),
-                                      dm["seg_lens"].data_ptr(), dm["seg_ids"].data_ptr(),
-                                      int(self.meta["seg_ids"].size), self.ns, self.T, stream_ptr)
+            st = lib.lora_plan_expand(d, self.v.data_ptr(), self.pB[r], self.py[r], self.T,
+                                      ctypes.byref(self.plan), self.image.data_ptr(), stream_ptr)
         if st != 0:
             raise RuntimeError(f"{which} failed: {L.last_error()}")
 
     def kernels(self):
-        ks = []
-        if self.ns:
-            ks += ["sgmv_shrink", "sgmv_expand"]
-        if self.nb:
-            ks += ["bgmv_shrink", "bgmv_expand"]
-        return ks
+        """Names of the kernels each launch group runs for this batch."""
+        p = self.plan_d
+        bf = self.wl.dtype == "bf16"
+        tag = "unsigned short" if bf else "float"
+        kb = 16 if self.wl.max_lora_rank <= 16 else 64
+        out = {"shrink": [], "expand": []}
+        if p["mfma_tiles"]:
+            out["shrink"].append("shrink_mfma_kernel<2>")
+            out["expand"].append("expand_mfma_kernel<2>")
+        if p["wave_tiles"]:
+            out["shrink"].append(f"shrink_wave_kernel<{tag}, 8, 4, 2>")
+            out["expand"].append(f"expand_wave_kernel<{tag}, 8, {kb}, 2>")
+        return out
 
 
 def time_kernel(setups, which, launches, warm, stream_ptr):
-    """Average duration of back-to-back launches of one entry point, from HIP
-    events recorded on the launch stream around the loop."""
+    """Average duration of one launch group ('shrink' / 'expand') over
+    back-to-back launches, from HIP events recorded on the launch stream (the
+    stream torch's events use) around the loop."""
     import torch
     for i in range(warm):
         for s in setups:
-            if which in s.kernels():
-                s.kernel_launch(which, i, stream_ptr)
+            s.kernel_launch(which, i, stream_ptr)
     n = 0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for i in range(launches):
         for s in setups:
-            if which in s.kernels():
-                s.kernel_launch(which, warm + i, stream_ptr)
-                n += 1
+            s.kernel_launch(which, warm + i, stream_ptr)
+            n += 1
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / max(n, 1)  # us per launch
+    return e0.elapsed_time(e1) * 1e3 / max(n, 1)  # us per launch group
 
 
 def measure(setups, steps, warmup, stream_ptr):
@@ -247,39 +239,22 @@ def copy_bandwidth():
 
 
 def kernel_roofline(setups, stream_ptr, launches):
-    """Per-kernel average launch time and algorithmic-bytes rate; returns the
-    dominant kernel (largest total time per step)."""
-    algs = [algorithmic(s.wl) for s in setups]
+    """Per launch group (shrink, expand): average time and algorithmic-bytes
+    rate; returns the dominant group (larger time per step)."""
     res = {}
-    for which in ("sgmv_shrink", "sgmv_expand", "bgmv_shrink", "bgmv_expand"):
-        parts = [(s, a) for s, a in zip(setups, algs) if which in s.kernels()]
-        if not parts:
-            continue
-        us = time_kernel([p[0] for p in parts], which, launches, 10, stream_ptr)
-        by = 0
-        fl = 0
-        for s, a in parts:
-            stage = "shrink" if which.endswith("shrink") else "expand"
-            # bytes of the rows this kernel covers (weights of the adapters it touches)
-            ids = s.wl.ids
-            rows = ids[(ids >= 0) & (((s.wl.prefill == 1) | (s.wl.max_lora_rank > 64))
-                                     if which.startswith("sgmv") else
-                                     ~((s.wl.prefill == 1) | (s.wl.max_lora_rank > 64)))]
-            e = 2 if s.wl.dtype == "bf16" else 4
-            Ta, nact = int(rows.size), len(set(rows.tolist()))
-            K, R, S, O = s.wl.in_features, s.wl.max_lora_rank, s.wl.num_slices, s.wl.O
-            if stage == "shrink":
-                by += Ta * K * e + nact * S * R * K * e + Ta * S * R * 4
-                fl += 2 * Ta * R * S * K
-            else:
-                by += nact * R * O * e + Ta * S * R * 4 + 2 * Ta * O * e
-                fl += 2 * Ta * R * O
-        per_launch_bytes = by / len(parts)
-        per_launch_flops = fl / len(parts)
-        res[which] = {"us": us, "bytes": per_launch_bytes, "flops": per_launch_flops,
-                      "GBs": per_launch_bytes / (us * 1e-6) / 1e9,
-                      "TFLOPs": per_launch_flops / (us * 1e-6) / 1e12,
-                      "step_us": us * len(parts)}
+    for which in ("shrink", "expand"):
+        us = time_kernel(setups, which, launches, 10, stream_ptr)
+        by = fl = 0
+        names = []
+        for s in setups:
+            a = algorithmic(s.wl)
+            by += a[f"{which}_bytes"]
+            fl += a[f"{which}_flops"]
+            names += s.kernels()[which]
+        n = len(setups)
+        res[which] = {"us": us, "bytes": by / n, "flops": fl / n,
+                      "GBs": by / n / (us * 1e-6) / 1e9, "TFLOPs": fl / n / (us * 1e-6) / 1e12,
+                      "step_us": us * n, "kernels": sorted(set(names))}
     dom = max(res, key=lambda k: res[k]["step_us"])
     return dom, res
 
@@ -409,8 +384,10 @@ def main():
         "achieved_GBs_kernels": total_bytes / (kernel_us_step * 1e-6) / 1e9,
         "copy_GBs_measured": copy_gbs,
         "per_kernel": {k: {"us": round(r["us"], 3), "GBs": round(r["GBs"], 1),
-                           "TFLOPs": round(r["TFLOPs"], 2)} for k, r in per_kernel.items()},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": d["GBs"], "peak": HBM_PEAK_GBS,
+                           "TFLOPs": round(r["TFLOPs"], 2), "kernels": r["kernels"]}
+                       for k, r in per_kernel.items()},
+        "roofline": {"bound": "hbm", "kernel": " + ".join(d["kernels"]), "stage": dom,
+                     "achieved": d["GBs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": d["GBs"] / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": d["bytes"],
                      "avg_launch_us": d["us"]},

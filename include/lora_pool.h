@@ -216,15 +216,78 @@ int32_t lora_bgmv_expand(const lora_pool_desc* desc, const float* v, const void*
 /* ------------------------------------------------------------ dispatcher */
 
 /* Device workspace lora_apply needs for a batch of T tokens (v for every row
- * plus the device copy of the metadata), and the host staging size for the
- * metadata.  Negative lora_status on an invalid descriptor or T < 0. */
+ * plus the device copy of the tile plan), and the host staging size for the
+ * plan.  Negative lora_status on an invalid descriptor or T < 0. */
 int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T);
 int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
 
+/* Rows per wavefront-path tile and per MFMA tile of a plan. */
+#define LORA_PLAN_WAVE_ROWS 8
+#define LORA_PLAN_MFMA_ROWS 32
+/* int32 words per tile record of a plan */
+#define LORA_PLAN_WAVE_WORDS 16
+#define LORA_PLAN_MFMA_WORDS 4
+
+/* Tile plan of one batch, as lora_apply_plan lays it out in meta_host.
+ *
+ * The rows of the batch are the rows of lora_build_meta: the SGMV rows
+ * (sgmv_perm order) are v rows 0 .. num_sgmv_rows - 1 and the BGMV rows
+ * (bgmv_tok order) follow them.  Every tile covers consecutive v rows of one
+ * adapter: wavefront tiles cut each short SGMV segment and each run of equal
+ * ids of the BGMV rows into pieces of LORA_PLAN_WAVE_ROWS rows; MFMA tiles cut
+ * the SGMV segments of at least mfma_min_rows rows (bf16 pools only) into
+ * pieces of LORA_PLAN_MFMA_ROWS rows.
+ *
+ * The device image starts image_offset bytes into meta_host and is
+ * image_bytes long; offsets below count int32 words from its start:
+ *   perm [num_sgmv_rows]              token of each SGMV row
+ *   wave [wave_tiles][16]             slot, rows, first v row, 0, token of
+ *                                     each row (-1 past the last row), -1 ...
+ *   mfma [mfma_tiles][4]              slot, rows, first v row, 0          */
+typedef struct {
+  int32_t num_sgmv_rows;
+  int32_t num_bgmv_rows;
+  int32_t num_segs;
+  int32_t wave_tiles;
+  int32_t mfma_tiles;
+  int32_t mfma_min_rows;   /* INT32_MAX when no segment uses MFMA tiles */
+  int64_t image_offset;    /* bytes from meta_host to the device image (16-byte aligned) */
+  int64_t image_bytes;
+  int64_t off_perm;        /* int32 offsets inside the image */
+  int64_t off_wave;
+  int64_t off_mfma;
+} lora_plan;
+
+/* Host half of lora_apply: validates the arguments, builds the metadata
+ * (lora_build_meta's arrays, in the front of meta_host) and packs the tile
+ * plan's device image behind it.  No HIP call; deterministic.  Returns
+ * LORA_OK, LORA_E_ID for an id outside [-1, max_loras), LORA_E_WORKSPACE if
+ * meta_host_bytes < lora_apply_host_meta_bytes(desc, T), LORA_E_ARG for NULL
+ * pointers or T < 0. */
+int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* ids_host,
+                        const uint8_t* prefill_host, int32_t bgmv_max_rank, void* meta_host,
+                        int64_t meta_host_bytes, lora_plan* plan);
+
+/* Device half of a plan, for a plan whose image the caller has copied to the
+ * GPU (`image`: device pointer, 16-byte aligned, plan->image_bytes long), so
+ * one plan can serve every layer of a batch.  v: device fp32
+ * [num_sgmv_rows + num_bgmv_rows][S][R] (row order of the plan).
+ *   lora_plan_shrink:  v[row][s][k] = sum_j A_pool[a][s][k][j] * x[t][j] for
+ *                      every row of every tile ([TGI] step 4, shrink)
+ *   lora_plan_expand:  y[t][off_s + j] = round_dtype((float)y[t][off_s + j] +
+ *                      sum_k B_pool[a][off_s + j][k] * v[row][s][k])
+ * Rows whose token, slot or row index is out of range are skipped.  Returns
+ * LORA_E_ARG for NULL pointers or a malformed plan, LORA_E_ALIGN for a
+ * misaligned image, LORA_E_DTYPE for MFMA tiles on an fp32 pool. */
+int32_t lora_plan_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool, float* v,
+                         int32_t T, const lora_plan* plan, const void* image, void* stream);
+int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void* B_pool, void* y,
+                         int32_t T, const lora_plan* plan, const void* image, void* stream);
+
 /* The whole delta path for one batch ([TGI] step 4; [QA] direct answer):
- * validates ids, builds the metadata on the host into meta_host, copies it into
- * ws on `stream`, then runs SGMV shrink, BGMV shrink, SGMV expand, BGMV expand
- * on `stream`, updating y in place.  Rows with id -1 are never written.
+ * lora_apply_plan into meta_host, one copy of the plan's device image into ws
+ * on `stream`, then lora_plan_shrink and lora_plan_expand on `stream`,
+ * updating y in place.  Rows with id -1 are never read or written.
  *   ids_host[T], prefill_host[T] (NULL = all decode): host arrays.
  *   ws: device workspace of >= lora_apply_workspace_bytes(desc, T) bytes.
  *   meta_host: host staging of >= lora_apply_host_meta_bytes(desc, T) bytes.

@@ -61,6 +61,20 @@ class lora_meta(ctypes.Structure):
                 ("bgmv_ids", ctypes.POINTER(ctypes.c_int32))]
 
 
+class lora_plan(ctypes.Structure):
+    _fields_ = [("num_sgmv_rows", ctypes.c_int32), ("num_bgmv_rows", ctypes.c_int32),
+                ("num_segs", ctypes.c_int32), ("wave_tiles", ctypes.c_int32),
+                ("mfma_tiles", ctypes.c_int32), ("mfma_min_rows", ctypes.c_int32),
+                ("image_offset", ctypes.c_int64), ("image_bytes", ctypes.c_int64),
+                ("off_perm", ctypes.c_int64), ("off_wave", ctypes.c_int64),
+                ("off_mfma", ctypes.c_int64)]
+
+
+PLAN_WAVE_ROWS = 8
+PLAN_MFMA_ROWS = 32
+PLAN_WAVE_WORDS = 16
+PLAN_MFMA_WORDS = 4
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -83,6 +97,9 @@ _SIGNATURES = {
     "lora_bgmv_expand": (_I32, [_DP, _P, _P, _P, _P, _P, _I32, _I32, _P]),
     "lora_apply_workspace_bytes": (_I64, [_DP, _I32]),
     "lora_apply_host_meta_bytes": (_I64, [_DP, _I32]),
+    "lora_apply_plan": (_I32, [_DP, _I32, _P, _P, _I32, _P, _I64, ctypes.POINTER(lora_plan)]),
+    "lora_plan_shrink": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P]),
+    "lora_plan_expand": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P]),
     "lora_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P, _I64, _P]),
 }
 
@@ -253,6 +270,50 @@ def lora_apply_workspace_bytes(desc, T: int) -> int:
 
 def lora_apply_host_meta_bytes(desc, T: int) -> int:
     return _check(lib().lora_apply_host_meta_bytes(ctypes.byref(desc), int(T)))
+
+
+def lora_apply_plan(desc, ids, prefill=None, bgmv_max_rank: int = 0):
+    """Host tile plan of one batch: (plan fields as a dict, device image as an
+    int32 array with 'perm', 'wave' [n, 16] and 'mfma' [n, 4] views)."""
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    T = int(ids.shape[0])
+    pre = None if prefill is None else np.ascontiguousarray(np.asarray(prefill, dtype=np.uint8))
+    nbytes = lora_apply_host_meta_bytes(desc, T)
+    raw = np.zeros(nbytes // 4 + 16, np.int32)
+    off = (-raw.ctypes.data % 64) // 4
+    stage = raw[off:off + nbytes // 4]
+    p = lora_plan()
+    _check(lib().lora_apply_plan(ctypes.byref(desc), T, ids.ctypes.data if T else None,
+                                 None if pre is None else pre.ctypes.data, int(bgmv_max_rank),
+                                 stage.ctypes.data, nbytes, ctypes.byref(p)))
+    d = {k: getattr(p, k) for k, _ in lora_plan._fields_}
+    img = stage[p.image_offset // 4: (p.image_offset + p.image_bytes) // 4].copy()
+    views = {
+        "perm": img[p.off_perm:p.off_perm + p.num_sgmv_rows],
+        "wave": img[p.off_wave:p.off_wave + PLAN_WAVE_WORDS * p.wave_tiles].reshape(-1, PLAN_WAVE_WORDS),
+        "mfma": img[p.off_mfma:p.off_mfma + PLAN_MFMA_WORDS * p.mfma_tiles].reshape(-1, PLAN_MFMA_WORDS),
+    }
+    return d, img, views
+
+
+def plan_struct(d: dict) -> "lora_plan":
+    """lora_plan from the dict lora_apply_plan returns."""
+    p = lora_plan()
+    for k, _ in lora_plan._fields_:
+        setattr(p, k, int(d[k]))
+    return p
+
+
+def lora_plan_shrink(desc, x, A_pool, v, T, plan, image, stream=None) -> None:
+    p = plan if isinstance(plan, lora_plan) else plan_struct(plan)
+    _check(lib().lora_plan_shrink(ctypes.byref(desc), _ptr(x), _ptr(A_pool), _ptr(v), int(T),
+                                  ctypes.byref(p), _ptr(image), _stream(stream)))
+
+
+def lora_plan_expand(desc, v, B_pool, y, T, plan, image, stream=None) -> None:
+    p = plan if isinstance(plan, lora_plan) else plan_struct(plan)
+    _check(lib().lora_plan_expand(ctypes.byref(desc), _ptr(v), _ptr(B_pool), _ptr(y), int(T),
+                                  ctypes.byref(p), _ptr(image), _stream(stream)))
 
 
 def lora_apply(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgmv_max_rank, ws,

@@ -65,6 +65,33 @@ int32_t sgmv_args(const int32_t* perm, const int32_t* seg_starts, const int32_t*
   return LORA_OK;
 }
 
+// Validates a caller's plan against its image and builds the device view.
+int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, TilePlan* tp) {
+  if (!p) return fail(LORA_E_ARG, "plan is NULL");
+  if (p->num_sgmv_rows < 0 || p->num_bgmv_rows < 0 || p->wave_tiles < 0 || p->mfma_tiles < 0 ||
+      p->off_perm < 0 || p->off_wave < 0 || p->off_mfma < 0 || p->image_bytes < 0)
+    return fail(LORA_E_ARG, "malformed plan (negative count or offset)");
+  if ((int64_t)p->num_sgmv_rows + p->num_bgmv_rows > INT32_MAX)
+    return fail(LORA_E_ARG, "malformed plan (row count)");
+  if (p->off_wave % 4 || p->off_mfma % 4)
+    return fail(LORA_E_ALIGN, "plan sections must start on 16-byte boundaries");
+  const int64_t words = p->image_bytes / 4;
+  if (p->off_perm + p->num_sgmv_rows > words ||
+      p->off_wave + (int64_t)LORA_PLAN_WAVE_WORDS * p->wave_tiles > words ||
+      p->off_mfma + (int64_t)LORA_PLAN_MFMA_WORDS * p->mfma_tiles > words)
+    return fail(LORA_E_ARG, "malformed plan (sections exceed image_bytes)");
+  if (p->mfma_tiles > 0 && g.dtype != LORA_BF16)
+    return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
+  const bool any = p->wave_tiles > 0 || p->mfma_tiles > 0;
+  if (any) {
+    if (int32_t e = need_ptr(image, "image")) return e;
+  }
+  const int32_t* img = (const int32_t*)image;
+  *tp = TilePlan{img + p->off_perm, img + p->off_wave, p->wave_tiles, img + p->off_mfma,
+                 p->mfma_tiles, p->num_sgmv_rows, p->num_sgmv_rows + p->num_bgmv_rows};
+  return LORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,8 +176,9 @@ int32_t lora_sgmv_shrink(const lora_pool_desc* desc, const void* x, const void* 
   if (int32_t e = check_common(desc, &g, x, "x", A_pool, "A_pool", v)) return e;
   if (int32_t e = sgmv_args(perm, seg_starts, seg_lens, seg_ids, num_segs)) return e;
   g.T = T;
-  RowList L{perm, nullptr, seg_starts, seg_lens, seg_ids, num_segs, num_rows, 0, INT32_MAX};
-  return run_shrink(g, x, A_pool, v, L, nullptr, nullptr, (hipStream_t)stream);
+  return run_shrink(g, x, A_pool, v,
+                    segments_list(perm, seg_starts, seg_lens, seg_ids, num_segs, num_rows),
+                    (hipStream_t)stream);
 }
 
 int32_t lora_sgmv_expand(const lora_pool_desc* desc, const float* v, const void* B_pool, void* y,
@@ -165,8 +193,9 @@ int32_t lora_sgmv_expand(const lora_pool_desc* desc, const float* v, const void*
   if (int32_t e = check_common(desc, &g, y, "y", B_pool, "B_pool", v)) return e;
   if (int32_t e = sgmv_args(perm, seg_starts, seg_lens, seg_ids, num_segs)) return e;
   g.T = T;
-  RowList L{perm, nullptr, seg_starts, seg_lens, seg_ids, num_segs, num_rows, 0, INT32_MAX};
-  return run_expand(g, v, B_pool, y, L, nullptr, nullptr, (hipStream_t)stream);
+  return run_expand(g, v, B_pool, y,
+                    segments_list(perm, seg_starts, seg_lens, seg_ids, num_segs, num_rows),
+                    (hipStream_t)stream);
 }
 
 int32_t lora_bgmv_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool, float* v,
@@ -180,8 +209,7 @@ int32_t lora_bgmv_shrink(const lora_pool_desc* desc, const void* x, const void* 
   if (int32_t e = check_common(desc, &g, x, "x", A_pool, "A_pool", v)) return e;
   if (!tok || !ids) return fail(LORA_E_ARG, "tok / ids must not be NULL");
   g.T = T;
-  RowList L{tok, ids, nullptr, nullptr, nullptr, 0, n, 0, INT32_MAX};
-  return run_shrink(g, x, A_pool, v, L, nullptr, nullptr, (hipStream_t)stream);
+  return run_shrink(g, x, A_pool, v, rows_list(tok, ids, n), (hipStream_t)stream);
 }
 
 int32_t lora_bgmv_expand(const lora_pool_desc* desc, const float* v, const void* B_pool, void* y,
@@ -195,8 +223,35 @@ int32_t lora_bgmv_expand(const lora_pool_desc* desc, const float* v, const void*
   if (int32_t e = check_common(desc, &g, y, "y", B_pool, "B_pool", v)) return e;
   if (!tok || !ids) return fail(LORA_E_ARG, "tok / ids must not be NULL");
   g.T = T;
-  RowList L{tok, ids, nullptr, nullptr, nullptr, 0, n, 0, INT32_MAX};
-  return run_expand(g, v, B_pool, y, L, nullptr, nullptr, (hipStream_t)stream);
+  return run_expand(g, v, B_pool, y, rows_list(tok, ids, n), (hipStream_t)stream);
+}
+
+int32_t lora_plan_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool, float* v,
+                         int32_t T, const lora_plan* plan, const void* image, void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  TilePlan tp;
+  if (int32_t e = plan_view(g, plan, image, &tp)) return e;
+  if (T == 0 || (tp.wave_tiles == 0 && tp.mfma_tiles == 0)) return LORA_OK;
+  if (int32_t e = check_common(desc, &g, x, "x", A_pool, "A_pool", v)) return e;
+  g.T = T;
+  return run_plan_shrink(g, x, A_pool, v, tp, (hipStream_t)stream);
+}
+
+int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void* B_pool, void* y,
+                         int32_t T, const lora_plan* plan, const void* image, void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  TilePlan tp;
+  if (int32_t e = plan_view(g, plan, image, &tp)) return e;
+  if (T == 0 || (tp.wave_tiles == 0 && tp.mfma_tiles == 0)) return LORA_OK;
+  if (int32_t e = check_common(desc, &g, y, "y", B_pool, "B_pool", v)) return e;
+  g.T = T;
+  return run_plan_expand(g, v, B_pool, y, tp, (hipStream_t)stream);
 }
 
 int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
@@ -213,54 +268,26 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
   if (int32_t e = need_ptr(x, "x")) return e;
   if (int32_t e = need_ptr(y, "y")) return e;
   if (int32_t e = need_ptr(ws, "ws")) return e;
-  if (!ids_host) return fail(LORA_E_ARG, "ids_host is NULL");
-  if (!meta_host) return fail(LORA_E_ARG, "meta_host is NULL");
-  if ((uintptr_t)meta_host % 4) return fail(LORA_E_ALIGN, "meta_host is not 4-byte aligned");
-  const MetaLayout ml = meta_layout(T, g.max_loras);
-  const int64_t meta_bytes = ml.total_ints * 4;
-  const int64_t v_off = align_up(meta_bytes, 256);
+  const StageLayout sl = stage_layout(T, g.max_loras);
+  const int64_t v_off = align_up(sl.image_max_words * 4, 256);
   const int64_t need_ws = v_off + (int64_t)T * g.S * g.R * 4;
   if (ws_bytes < need_ws)
     return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
                 (long long)need_ws);
-  if (meta_host_bytes < meta_bytes)
-    return fail(LORA_E_WORKSPACE, "meta_host has %lld bytes, needs %lld",
-                (long long)meta_host_bytes, (long long)meta_bytes);
-  for (int32_t t = 0; t < T; ++t) {
-    if (ids_host[t] < -1 || ids_host[t] >= g.max_loras)
-      return fail(LORA_E_ID, "ids[%d] = %d is outside [-1, %d)", t, ids_host[t], g.max_loras);
-  }
-  int32_t* mh = (int32_t*)meta_host;
-  lora_meta m;
-  m.sgmv_perm = mh + ml.perm;
-  m.seg_starts = mh + ml.seg_starts;
-  m.seg_lens = mh + ml.seg_lens;
-  m.seg_ids = mh + ml.seg_ids;
-  m.bgmv_tok = mh + ml.bgmv_tok;
-  m.bgmv_ids = mh + ml.bgmv_ids;
-  build_meta_core(ids_host, prefill_host, T, g.max_loras, g.R, bgmv_max_rank, &m);
-  const int32_t ns = m.num_sgmv_rows, nb = m.num_bgmv_rows;
-  if (ns + nb == 0) return LORA_OK;
-
+  lora_plan p;
+  if (int32_t e = lora_apply_plan(desc, T, ids_host, prefill_host, bgmv_max_rank, meta_host,
+                                  meta_host_bytes, &p))
+    return e;
+  const int32_t rows = p.num_sgmv_rows + p.num_bgmv_rows;
+  if (rows == 0) return LORA_OK;
   hipStream_t st = (hipStream_t)stream;
-  if (int32_t e = hip_ok(hipMemcpyAsync(ws, meta_host, meta_bytes, hipMemcpyHostToDevice, st),
-                         "metadata copy")) return e;
-  const int32_t* md = (const int32_t*)ws;
+  if (int32_t e = hip_ok(hipMemcpyAsync(ws, (const char*)meta_host + p.image_offset,
+                                        (size_t)p.image_bytes, hipMemcpyHostToDevice, st),
+                         "plan copy"))
+    return e;
   float* v = (float*)((char*)ws + v_off);
-  float* v_b = v + (int64_t)ns * g.S * g.R;
-  g.T = T;
-  RowList Ls{md + ml.perm, nullptr, md + ml.seg_starts, md + ml.seg_lens, md + ml.seg_ids,
-             m.num_segs, ns, 0, INT32_MAX};
-  RowList Lb{md + ml.bgmv_tok, md + ml.bgmv_ids, nullptr, nullptr, nullptr, 0, nb, 0, INT32_MAX};
-  if (ns > 0)
-    if (int32_t e = run_shrink(g, x, A_pool, v, Ls, m.seg_starts, m.seg_lens, st)) return e;
-  if (nb > 0)
-    if (int32_t e = run_shrink(g, x, A_pool, v_b, Lb, nullptr, nullptr, st)) return e;
-  if (ns > 0)
-    if (int32_t e = run_expand(g, v, B_pool, y, Ls, m.seg_starts, m.seg_lens, st)) return e;
-  if (nb > 0)
-    if (int32_t e = run_expand(g, v_b, B_pool, y, Lb, nullptr, nullptr, st)) return e;
-  return LORA_OK;
+  if (int32_t e = lora_plan_shrink(desc, x, A_pool, v, T, &p, ws, stream)) return e;
+  return lora_plan_expand(desc, v, B_pool, y, T, &p, ws, stream);
 }
 
 }  // extern "C"

@@ -1,6 +1,8 @@
 // Host-side logic of the C ABI: error state, descriptor validation, pool sizing,
 // scaling, the SGMV/BGMV metadata builder and workspace sizing.  Nothing here
 // touches the GPU, so every path is testable on a machine without one.
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -82,16 +84,33 @@ int32_t check_desc(const lora_pool_desc* d, Geo* g) {
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-MetaLayout meta_layout(int32_t T, int32_t max_loras) {
-  MetaLayout m;
+StageLayout stage_layout(int32_t T, int32_t max_loras) {
+  StageLayout m;
+  const int64_t t = T, ml = max_loras;
   m.perm = 0;
-  m.seg_starts = m.perm + T;
-  m.seg_lens = m.seg_starts + max_loras;
-  m.seg_ids = m.seg_lens + max_loras;
-  m.bgmv_tok = m.seg_ids + max_loras;
-  m.bgmv_ids = m.bgmv_tok + T;
-  m.total_ints = m.bgmv_ids + T;
+  m.seg_starts = m.perm + t;
+  m.seg_lens = m.seg_starts + ml;
+  m.seg_ids = m.seg_lens + ml;
+  m.bgmv_tok = m.seg_ids + ml;
+  m.bgmv_ids = m.bgmv_tok + t;
+  m.image = align_up(m.bgmv_ids + t, 4);
+  // Every segment and every run of equal BGMV ids adds at most one partial
+  // tile: wave tiles <= ceil(T / 8) + 2 max_loras, MFMA tiles <= ceil(T / 32)
+  // + max_loras.
+  const int64_t wave = (t + LORA_PLAN_WAVE_ROWS - 1) / LORA_PLAN_WAVE_ROWS + 2 * ml;
+  const int64_t mfma = (t + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS + ml;
+  m.image_max_words = align_up(t, 4) + LORA_PLAN_WAVE_WORDS * wave + LORA_PLAN_MFMA_WORDS * mfma;
+  m.total_words = m.image + m.image_max_words;
   return m;
+}
+
+int32_t sgmv_mfma_min_rows() {
+  static const int32_t v = [] {
+    const char* e = std::getenv("LORA_SGMV_MFMA_MIN_ROWS");
+    const long x = e ? std::strtol(e, nullptr, 10) : 16;
+    return (int32_t)(x < 1 ? 1 : x > INT32_MAX ? INT32_MAX : x);
+  }();
+  return v;
 }
 
 // Stable counting sort of the two row sets by adapter id.  Bucket sizes are a
@@ -140,6 +159,86 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
   out->num_segs = nseg;
   out->num_bgmv_rows = nb;
   out->reserved = 0;
+  return LORA_OK;
+}
+
+// Tile plan ([TGI] step 4: rows grouped by adapter, one adapter per tile).
+// Short SGMV segments and the runs of equal ids among the BGMV rows (already
+// sorted by id) are cut into wavefront tiles of LORA_PLAN_WAVE_ROWS rows; SGMV
+// segments of at least mfma_min_rows rows (bf16) into MFMA tiles of
+// LORA_PLAN_MFMA_ROWS rows.  v row numbering: SGMV rows first, then BGMV rows.
+int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* prefill,
+                  int32_t bgmv_max_rank, int32_t* stage, lora_plan* p) {
+  const StageLayout sl = stage_layout(T, g.max_loras);
+  lora_meta m;
+  m.sgmv_perm = stage + sl.perm;
+  m.seg_starts = stage + sl.seg_starts;
+  m.seg_lens = stage + sl.seg_lens;
+  m.seg_ids = stage + sl.seg_ids;
+  m.bgmv_tok = stage + sl.bgmv_tok;
+  m.bgmv_ids = stage + sl.bgmv_ids;
+  if (int32_t e = build_meta_core(ids, prefill, T, g.max_loras, g.R, bgmv_max_rank, &m)) return e;
+  const int32_t ns = m.num_sgmv_rows, nb = m.num_bgmv_rows;
+  const int32_t thr = g.dtype == LORA_BF16 ? sgmv_mfma_min_rows() : INT32_MAX;
+  int32_t* img = stage + sl.image;
+  const int64_t off_wave = align_up(ns, 4);
+  std::memcpy(img, m.sgmv_perm, sizeof(int32_t) * (size_t)ns);
+  for (int64_t i = ns; i < off_wave; ++i) img[i] = -1;
+  int32_t* wave = img + off_wave;
+  int64_t nw = 0;
+  auto emit_wave = [&](int32_t slot, int32_t first, int32_t rows, const int32_t* tok) {
+    int32_t* r = wave + nw * LORA_PLAN_WAVE_WORDS;
+    r[0] = slot;
+    r[1] = rows;
+    r[2] = first;
+    r[3] = 0;
+    for (int i = 4; i < LORA_PLAN_WAVE_WORDS; ++i) r[i] = -1;
+    for (int i = 0; i < rows; ++i) r[4 + i] = tok[i];
+    ++nw;
+  };
+  for (int32_t s = 0; s < m.num_segs; ++s) {
+    const int32_t st = m.seg_starts[s], ln = m.seg_lens[s];
+    if (ln >= thr) continue;
+    for (int32_t j = 0; j < ln; j += LORA_PLAN_WAVE_ROWS)
+      emit_wave(m.seg_ids[s], st + j, std::min(LORA_PLAN_WAVE_ROWS, ln - j), m.sgmv_perm + st + j);
+  }
+  for (int32_t i = 0; i < nb;) {
+    int32_t j = i + 1;
+    while (j < nb && m.bgmv_ids[j] == m.bgmv_ids[i]) ++j;
+    for (int32_t k = i; k < j; k += LORA_PLAN_WAVE_ROWS)
+      emit_wave(m.bgmv_ids[i], ns + k, std::min(LORA_PLAN_WAVE_ROWS, j - k), m.bgmv_tok + k);
+    i = j;
+  }
+  const int64_t off_mfma = off_wave + nw * LORA_PLAN_WAVE_WORDS;
+  int32_t* mt = img + off_mfma;
+  int64_t nm = 0;
+  for (int32_t s = 0; s < m.num_segs; ++s) {
+    const int32_t st = m.seg_starts[s], ln = m.seg_lens[s];
+    if (ln < thr) continue;
+    for (int32_t j = 0; j < ln; j += LORA_PLAN_MFMA_ROWS) {
+      int32_t* r = mt + nm * LORA_PLAN_MFMA_WORDS;
+      r[0] = m.seg_ids[s];
+      r[1] = std::min(LORA_PLAN_MFMA_ROWS, ln - j);
+      r[2] = st + j;
+      r[3] = 0;
+      ++nm;
+    }
+  }
+  const int64_t words = off_mfma + nm * LORA_PLAN_MFMA_WORDS;
+  if (words > sl.image_max_words)  // cannot happen: the bounds above hold for any batch
+    return fail(LORA_E_WORKSPACE, "tile plan overflow (%lld words > %lld)", (long long)words,
+                (long long)sl.image_max_words);
+  p->num_sgmv_rows = ns;
+  p->num_bgmv_rows = nb;
+  p->num_segs = m.num_segs;
+  p->wave_tiles = (int32_t)nw;
+  p->mfma_tiles = (int32_t)nm;
+  p->mfma_min_rows = thr;
+  p->image_offset = sl.image * 4;
+  p->image_bytes = words * 4;
+  p->off_perm = 0;
+  p->off_wave = off_wave;
+  p->off_mfma = off_mfma;
   return LORA_OK;
 }
 
@@ -206,7 +305,7 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T) {
   int32_t st = check_desc(desc, &g);
   if (st) return st;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
-  return meta_layout(T, g.max_loras).total_ints * 4;
+  return stage_layout(T, g.max_loras).total_words * 4;
 }
 
 int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T) {
@@ -215,8 +314,30 @@ int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T) {
   int32_t st = check_desc(desc, &g);
   if (st) return st;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
-  const int64_t meta = align_up(meta_layout(T, g.max_loras).total_ints * 4, 256);
-  return meta + (int64_t)T * g.S * g.R * 4;
+  const int64_t img = align_up(stage_layout(T, g.max_loras).image_max_words * 4, 256);
+  return img + (int64_t)T * g.S * g.R * 4;
+}
+
+int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* ids_host,
+                        const uint8_t* prefill_host, int32_t bgmv_max_rank, void* meta_host,
+                        int64_t meta_host_bytes, lora_plan* plan) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  if (!plan) return fail(LORA_E_ARG, "plan is NULL");
+  if (T > 0 && !ids_host) return fail(LORA_E_ARG, "ids_host is NULL");
+  if (!meta_host) return fail(LORA_E_ARG, "meta_host is NULL");
+  if ((uintptr_t)meta_host % 16) return fail(LORA_E_ALIGN, "meta_host is not 16-byte aligned");
+  const int64_t need = stage_layout(T, g.max_loras).total_words * 4;
+  if (meta_host_bytes < need)
+    return fail(LORA_E_WORKSPACE, "meta_host has %lld bytes, needs %lld",
+                (long long)meta_host_bytes, (long long)need);
+  for (int32_t t = 0; t < T; ++t) {
+    if (ids_host[t] < -1 || ids_host[t] >= g.max_loras)
+      return fail(LORA_E_ID, "ids[%d] = %d is outside [-1, %d)", t, ids_host[t], g.max_loras);
+  }
+  return plan_core(g, T, ids_host, prefill_host, bgmv_max_rank, (int32_t*)meta_host, plan);
 }
 
 }  // extern "C"

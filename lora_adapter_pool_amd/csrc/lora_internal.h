@@ -31,17 +31,30 @@ int32_t check_desc(const lora_pool_desc* desc, Geo* g);
 inline int64_t elem_bytes(int32_t dtype) { return dtype == LORA_BF16 ? 2 : 4; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Host metadata staging layout used by lora_apply (int32 offsets).
-struct MetaLayout {
-  int64_t perm, seg_starts, seg_lens, seg_ids, bgmv_tok, bgmv_ids, total_ints;
+// lora_apply's host staging (int32 words): the builder's arrays, then the
+// plan's device image (16-byte aligned), which is what gets copied to the GPU.
+struct StageLayout {
+  int64_t perm, seg_starts, seg_lens, seg_ids, bgmv_tok, bgmv_ids;
+  int64_t image;            // first word of the device image
+  int64_t image_max_words;  // capacity of the device image
+  int64_t total_words;
 };
-MetaLayout meta_layout(int32_t T, int32_t max_loras);
+StageLayout stage_layout(int32_t T, int32_t max_loras);
 int64_t align_up(int64_t v, int64_t a);
+
+// SGMV segments at least this long run on MFMA tiles (bf16 pools); the
+// environment variable LORA_SGMV_MFMA_MIN_ROWS overrides the default of 16.
+int32_t sgmv_mfma_min_rows();
 
 // Builder core (no argument checks beyond what lora_build_meta does).
 int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
                         int32_t max_loras, int32_t max_lora_rank, int32_t bgmv_max_rank,
                         lora_meta* out);
+
+// Host half of lora_apply on validated arguments: metadata and tile plan into
+// `stage` (stage_layout(T, g.max_loras).total_words words).
+int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* prefill,
+                  int32_t bgmv_max_rank, int32_t* stage, lora_plan* plan);
 
 bool log_enabled();
 

@@ -13,27 +13,41 @@
 namespace lora {
 
 constexpr int kNumXcd = 8;             // XCDs on MI355X; workgroups are dealt round-robin
-constexpr int kWaveTileRows = 8;       // rows per tile of the VALU kernels
+constexpr int kWaveTileRows = LORA_PLAN_WAVE_ROWS;  // rows per tile of the VALU kernels
+constexpr int kMfmaTileRows = LORA_PLAN_MFMA_ROWS;  // rows per tile of the MFMA kernels
 constexpr int kExpandCols = 256;       // output columns per VALU expand workgroup
 constexpr int kExpandMfmaCols = 128;   // output columns per MFMA expand workgroup
-constexpr int kSgmvMfmaMinRows = 16;   // SGMV segments this long or longer use MFMA (bf16)
 
 // A list of rows to process.  Row i reads token tok[i] of x / y and writes row i
-// of v.  BGMV: ids != nullptr gives the adapter slot of every row.  SGMV:
-// ids == nullptr; segments give [start, start + len) ranges of rows sharing
-// seg_ids[g]; only segments whose clamped length is in [seg_min, seg_max] are
-// covered by a given launch.
+// of v.  Three ways to cut it into tiles, one adapter per tile:
+//   segments  (ids == tiles == nullptr): [seg_starts[g], + seg_lens[g]) share
+//             seg_ids[g]; a launch covers the segments whose clamped length is
+//             in [seg_min, seg_max]; tiles are found on the device.
+//   rows      (ids != nullptr): fixed ranges of rows; ids[i] is row i's adapter.
+//   tile list (tiles != nullptr): num_tiles host-built records (the plan's
+//             layout); tok is the plan's perm (used by the MFMA kernels).
 struct RowList {
   const int32_t* tok;
   const int32_t* ids;
   const int32_t* seg_starts;
   const int32_t* seg_lens;
   const int32_t* seg_ids;
+  const int32_t* tiles;
   int32_t num_segs;
   int32_t num_rows;
+  int32_t num_tiles;
   int32_t seg_min;
   int32_t seg_max;
 };
+
+inline RowList segments_list(const int32_t* perm, const int32_t* starts, const int32_t* lens,
+                             const int32_t* sids, int32_t num_segs, int32_t num_rows) {
+  return RowList{perm, nullptr, starts, lens, sids, nullptr, num_segs, num_rows, 0, 0, INT32_MAX};
+}
+
+inline RowList rows_list(const int32_t* tok, const int32_t* ids, int32_t n) {
+  return RowList{tok, ids, nullptr, nullptr, nullptr, nullptr, 0, n, 0, 0, INT32_MAX};
+}
 
 // Column chunks of the fused output: chunk c belongs to slice s when
 // start[s] <= c < start[s + 1].
@@ -42,12 +56,29 @@ struct Chunks {
   int32_t start[LORA_MAX_SLICES + 1];
 };
 
-// Enqueue the shrink / expand of one row list on `st`.  host_seg_* (nullable)
-// are host copies of the segment arrays; with them the grids are exact.
+// Device copy of a lora_plan image (pointers into the workspace).
+struct TilePlan {
+  const int32_t* perm;
+  const int32_t* wave;
+  int32_t wave_tiles;
+  const int32_t* mfma;
+  int32_t mfma_tiles;
+  int32_t num_sgmv_rows;  // rows of perm; MFMA tiles lie inside them
+  int32_t num_rows;       // v rows: SGMV rows + BGMV rows
+};
+
+// Enqueue the shrink / expand of one row list (segments or rows) on `st`;
+// grids are upper bounds, surplus workgroups exit after the tile lookup.
 int32_t run_shrink(const Geo& g, const void* x, const void* A, float* v, RowList L,
-                   const int32_t* host_seg_starts, const int32_t* host_seg_lens, hipStream_t st);
+                   hipStream_t st);
 int32_t run_expand(const Geo& g, const float* v, const void* B, void* y, RowList L,
-                   const int32_t* host_seg_starts, const int32_t* host_seg_lens, hipStream_t st);
+                   hipStream_t st);
+// The shrink (MFMA tiles, then wavefront tiles) or expand launches of a tile
+// plan, exact grids.
+int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, const TilePlan& p,
+                        hipStream_t st);
+int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, const TilePlan& p,
+                        hipStream_t st);
 int32_t run_pool_load(const Geo& g, void* A_slot_slice, void* B_slot_slice, const void* Asrc,
                       const void* Bsrc, int r, int out_s, float scale, hipStream_t st);
 

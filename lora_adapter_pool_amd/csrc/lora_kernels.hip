@@ -1,27 +1,27 @@
 // gfx950 (MI355X) kernels of the multi-LoRA delta path.
 //
-// Two stages per row list ([TGI] step 4 of the TGI multi-LoRA article: shrink
+// Two stages per row list (step 4 of the TGI multi-LoRA article: shrink
 // x -> r, then expand r -> out, grouped by adapter):
 //   shrink: v[i][s][k]   = sum_j A_pool[a][s][k][j] * x[t][j]          (fp32 acc)
 //   expand: y[t][off_s+j] = rne(y[t][off_s+j] + sum_k B_pool[a][off_s+j][k] * v[i][s][k])
 //
-// Row lists are either SGMV segments (rows perm[seg_start .. +len), one adapter
-// per segment) or BGMV rows (tok[i], ids[i] per row).  Work is cut into tiles of
-// consecutive rows; a BGMV tile may hold several adapters and processes each
-// distinct adapter once (rows come sorted by adapter, so usually one).
+// Work is cut into tiles of consecutive rows of one adapter.  Three ways to
+// find a workgroup's tile: a host-built tile list (lora_apply's plan: one
+// 64-byte record load), SGMV segments (block-parallel prefix sum over the
+// segment arrays on the device) or BGMV rows with per-row ids (fixed row
+// ranges; a tile then processes each distinct adapter once).
 //
 // Kernels:
-//   shrink_wave   VALU, 4 waves split K, 8 contiguous elements per lane
-//                 (16-byte loads), rank chunks across workgroups; the K
+//   shrink_wave   VALU, up to 16 waves split K, 8 contiguous elements per
+//                 lane (16-byte loads), rank chunks across workgroups; the K
 //                 reduction is a wavefront transpose-reduce plus a fixed-order
-//                 sum of the four waves' partials in LDS (deterministic).
+//                 sum of the waves' partials in LDS (deterministic).
 //   expand_wave   VALU, one output column per thread; the B block of the tile
 //                 is copied from HBM into LDS with contiguous 16-byte loads and
 //                 read back row-per-thread (padded rows, no bank conflicts);
 //                 v rows are LDS broadcasts.
 //   shrink_mfma   bf16 MFMA 16x16x32 for long SGMV segments: x rows are the
-//                 A operand, adapter A rows the B operand, fp32 accumulators;
-//                 two waves split K, partials summed in fixed order.
+//                 A operand, adapter A rows the B operand, fp32 accumulators.
 //   expand_mfma   bf16 MFMA 16x16x32 computing (B_pool tile) x v^T so that each
 //                 lane ends with 8 consecutive output columns of one token
 //                 (16-byte y read-modify-write); fp32 v enters as a hi + lo
@@ -31,8 +31,9 @@
 // weights and, across rank chunks, x rows) land on the same XCD's L2: the
 // hardware deals workgroups round-robin over the 8 XCDs.
 //
-// Every token index and adapter slot read from device metadata is bounds-checked
-// against T and max_loras; rows that fail are skipped, never dereferenced.
+// Every token index, adapter slot and row index read from device metadata is
+// bounds-checked against T, max_loras and the row count; rows that fail are
+// skipped, never dereferenced.
 #include <hip/hip_runtime.h>
 
 #include "lora_internal.h"
@@ -103,23 +104,15 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * q + min(x, r) + k;
 }
 
-// Locate tile `f` of a row list (called by every thread of a workgroup of up
-// to 1024 threads).
-// BGMV: fixed row ranges of TM rows.  SGMV: tiles of TM rows inside each
-// segment whose (clamped) length lies in [seg_min, seg_max], in segment order.
-// The segment arrays are read in parallel, one segment per thread per pass,
-// and a block-wide prefix sum of tile counts finds the segment holding
-// tile f, so the lookup costs one memory round trip rather than one per
-// segment.  Returns false (uniformly) past the last tile.
+// Segments mode: locate tile `f` (tiles of TM rows inside each segment whose
+// clamped length lies in [seg_min, seg_max], in segment order).  Called by
+// every thread of a workgroup of up to 1024 threads.  The segment arrays are
+// read in parallel, one segment per thread per pass, and a block-wide prefix
+// sum of tile counts finds the segment holding tile f, so the lookup costs one
+// memory round trip rather than one per segment.  Returns false (uniformly)
+// past the last tile; the results are the same in every lane.
 template <int TM>
 __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int& cnt, int& sid) {
-  if (L.ids) {
-    r0 = f * TM;
-    if (r0 >= L.num_rows) return false;
-    cnt = min(TM, L.num_rows - r0);
-    sid = -1;
-    return true;
-  }
   __shared__ int s_found[4];
   __shared__ int s_wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -174,28 +167,79 @@ __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int&
   return true;
 }
 
-// Token and adapter slot of each tile row; bit r of the result marks row r valid.
-template <int TM>
-__device__ __forceinline__ uint32_t load_tile_rows(const RowList& L, const Geo& g, int r0, int cnt,
-                                                   int sid, int (&tok)[TM], int (&aid)[TM]) {
+enum { kSegs = 0, kRows = 1, kList = 2 };  // how a kernel finds its tile
+
+// Rows of one tile, the same in every lane (scalar registers).  Row r is v row
+// vrow0 + r, reads token tok[r] and uses adapter aid[r]; bit r of `valid` is
+// set when the row exists and its token and adapter are in range.
+template <int TM> struct TileRows {
+  int vrow0;
+  int cnt;
+  uint32_t valid;
+  int tok[TM];
+  int aid[TM];
+};
+
+// Tile f of a row list.  Lane r (< TM) fetches row r with one unconditional
+// load (a clamped index for lanes past the last row) and the values are
+// broadcast with readlane, so all rows cost one memory round trip.
+//   kList: the host-built record (slot, rows, first v row, 0, tokens...) is
+//          one 64-byte load, 16 lanes one word each.
+//   kSegs: find_tile, then the tokens from tok[].
+//   kRows: rows f*TM .. of the list, tokens and adapters from tok[] / ids[].
+template <int TM, int MODE>
+__device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
+                                          TileRows<TM>& tr) {
+  static_assert(TM <= LORA_PLAN_WAVE_WORDS - 4, "a tile record holds at most 12 tokens");
+  const int lane = threadIdx.x & 63;
+  if constexpr (MODE == kList) {
+    if (f >= L.num_tiles) return false;
+    const int w = L.tiles[(size_t)f * LORA_PLAN_WAVE_WORDS + (lane & 15)];
+    const int sid = __builtin_amdgcn_readlane(w, 0);
+    tr.cnt = __builtin_amdgcn_readlane(w, 1);
+    tr.vrow0 = __builtin_amdgcn_readlane(w, 2);
+#pragma unroll
+    for (int r = 0; r < TM; ++r) {
+      tr.tok[r] = __builtin_amdgcn_readlane(w, 4 + r);
+      tr.aid[r] = sid;
+    }
+  } else {
+    int r0, cnt, sid = -1;
+    if constexpr (MODE == kSegs) {
+      if (!find_tile<TM>(L, f, r0, cnt, sid)) return false;
+      r0 = __builtin_amdgcn_readfirstlane(r0);
+      cnt = __builtin_amdgcn_readfirstlane(cnt);
+      sid = __builtin_amdgcn_readfirstlane(sid);
+    } else {
+      r0 = f * TM;
+      if (r0 >= L.num_rows) return false;
+      cnt = min(TM, L.num_rows - r0);
+    }
+    const int ri = r0 + min(lane, max(cnt, 1) - 1);
+    const int tv = L.tok[ri];
+    const int av = MODE == kRows ? L.ids[ri] : sid;
+    tr.cnt = cnt;
+    tr.vrow0 = r0;
+#pragma unroll
+    for (int r = 0; r < TM; ++r) {
+      tr.tok[r] = __builtin_amdgcn_readlane(tv, r);
+      tr.aid[r] = MODE == kRows ? __builtin_amdgcn_readlane(av, r) : sid;
+    }
+  }
   uint32_t valid = 0;
 #pragma unroll
   for (int r = 0; r < TM; ++r) {
-    int t = -1, a = -1;
-    if (r < cnt) {
-      t = L.tok[r0 + r];
-      a = L.ids ? L.ids[r0 + r] : sid;
-    }
-    const bool ok = t >= 0 && t < g.T && a >= 0 && a < g.max_loras;
-    tok[r] = ok ? t : 0;
-    aid[r] = ok ? a : -1;
+    const bool ok = r < tr.cnt && tr.vrow0 >= 0 && tr.vrow0 + r < L.num_rows && tr.tok[r] >= 0 &&
+                    tr.tok[r] < g.T && tr.aid[r] >= 0 && tr.aid[r] < g.max_loras;
     valid |= (ok ? 1u : 0u) << r;
+    if (!ok) tr.tok[r] = 0;
   }
-  return valid;
+  tr.valid = valid;
+  return true;
 }
 
 // Next adapter group of a tile: the adapter of the lowest pending row and the
-// mask of pending rows that use it.
+// mask of pending rows that use it (one group per tile except in rows mode).
 template <int TM>
 __device__ __forceinline__ uint32_t next_group(uint32_t todo, const int (&aid)[TM], int& a) {
   const int first = __builtin_ctz(todo);
@@ -249,7 +293,7 @@ __device__ __forceinline__ float wave_sum_many(float (&val)[V], int lane) {
 // adapter row), so for K <= 8192 each wave issues all of its loads at once.
 // Loads are unconditional (out-of-range lanes read a clamped address and are
 // zeroed), which keeps the memory counters exact and the loads in flight.
-template <typename E, int TM, int RC>
+template <typename E, int TM, int RC, int MODE>
 __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__ x,
                                                            const E* __restrict__ A,
                                                            float* __restrict__ v, RowList L,
@@ -265,19 +309,16 @@ __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__
   const int rem = bid - f * per_tile;
   const int s = rem / nrc;
   const int c = rem - s * nrc;
-  int r0, cnt, sid;
-  if (!find_tile<TM>(L, f, r0, cnt, sid)) return;
-  int tok[TM], aid[TM];
-  uint32_t todo = load_tile_rows<TM>(L, g, r0, cnt, sid, tok, aid);
+  TileRows<TM> tr;
+  if (!tile_rows<TM, MODE>(L, g, f, tr)) return;
+  uint32_t todo = tr.valid;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int SR = g.S * g.R;
   const int nchunk = (g.K + 511) / 512;
 
-  while (todo) {
-    int a;
-    const uint32_t m = next_group<TM>(todo, aid, a);
-    todo &= ~m;
+  // rows m of the tile that use adapter a
+  auto group = [&](uint32_t m, int a) {
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
@@ -291,7 +332,7 @@ __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__
 #pragma unroll
       for (int rr = 0; rr < RC; ++rr) ar[rr] = El<E>::raw8(Ab + (size_t)rr * g.K + kc);
 #pragma unroll
-      for (int r = 0; r < TM; ++r) xr[r] = El<E>::raw8(x + (size_t)tok[r] * g.K + kc);
+      for (int r = 0; r < TM; ++r) xr[r] = El<E>::raw8(x + (size_t)tr.tok[r] * g.K + kc);
       float af[RC][8];
 #pragma unroll
       for (int rr = 0; rr < RC; ++rr) {
@@ -320,10 +361,20 @@ __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__
       if ((m >> r) & 1u) {
         float tot = 0.f;
         for (int w = 0; w < W; ++w) tot += red[w][idx];
-        v[(size_t)(r0 + r) * SR + s * g.R + c * RC + rr] = tot;
+        v[(size_t)(tr.vrow0 + r) * SR + s * g.R + c * RC + rr] = tot;
       }
     }
-    __syncthreads();
+  };
+  if constexpr (MODE == kRows) {
+    while (todo) {
+      int a;
+      const uint32_t m = next_group<TM>(todo, tr.aid, a);
+      todo &= ~m;
+      group(m, a);
+      __syncthreads();  // red is rewritten by the next group
+    }
+  } else if (todo) {
+    group(todo, tr.aid[0]);  // one adapter per tile
   }
 }
 
@@ -331,21 +382,25 @@ __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__
 //
 // grid.x = tiles * column chunks (kExpandCols columns of one slice each).
 // Thread j owns output column col0 + j.  Per adapter group the tile's B block
-// (64 ranks per pass) and the group's v rows are staged in LDS: every thread
+// (KB ranks per pass) and the group's v rows are staged in LDS: every thread
 // first issues all of its global loads (contiguous 16-byte vectors), then
 // writes LDS, so the copy costs one memory round trip.  B rows are padded by
-// 16 bytes in LDS, which makes the row-per-thread reads conflict-free.
-template <typename E, int TM>
+// 16 bytes in LDS, which makes the row-per-thread reads conflict-free.  KB is
+// the pool's rank rounded up to 16 or 64, so no thread loads vectors that are
+// never used.
+template <typename E, int TM, int KB, int MODE>
 __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restrict__ v,
                                                           const E* __restrict__ B,
                                                           E* __restrict__ y, RowList L, Geo g,
                                                           Chunks ch) {
   constexpr int NC = kExpandCols;      // 256 columns per workgroup
-  constexpr int KB = 64;               // ranks staged per pass
   constexpr int VEC = El<E>::kVec;     // elements per 16-byte vector
-  constexpr int PAD = VEC;             // row padding: 16 bytes
-  constexpr int LDB = KB + PAD;
+  constexpr int LDB = KB + VEC;        // LDS row stride: 16 bytes of padding
   constexpr int MAXV = NC * KB / VEC / 256;  // B vectors per thread per pass
+  // v vectors per thread staged in one go: all of R for R <= KB (KB = 16) or
+  // R <= 256 (KB = 64); larger R goes through a plain loop
+  constexpr int NVV = (TM * (KB == 64 ? 256 : KB) / 4 + 255) / 256;
+  static_assert(KB % VEC == 0 && MAXV >= 1, "rank block must hold whole vectors");
   extern __shared__ __align__(16) unsigned char lds_raw[];
   // Bs: NC staged rows plus one dump row that absorbs stores of idle lanes (so
   // no store, and hence no load feeding it, sits under a branch); vs: TM rows
@@ -362,25 +417,23 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
     if (i < g.S && cidx >= ch.start[i]) s = i;
   const int col0 = (cidx - ch.start[s]) * NC;
   const int ncv = min(NC, g.out[s] - col0);
-  int r0, cnt, sid;
-  if (!find_tile<TM>(L, f, r0, cnt, sid)) return;
-  int tok[TM], aid[TM];
-  uint32_t todo = load_tile_rows<TM>(L, g, r0, cnt, sid, tok, aid);
+  TileRows<TM> tr;
+  if (!tile_rows<TM, MODE>(L, g, f, tr)) return;
+  uint32_t todo = tr.valid;
   const int tid = threadIdx.x;
   const int R = g.R;
   const int SR = g.S * R;
+  const int r0 = tr.vrow0;
   // y of every valid row is read up front so its latency overlaps the B / v
   // staging; each row is written exactly once, by the group that owns it
   const int colc = tid < ncv ? tid : 0;
   E* yb = y + g.off[s] + col0 + colc;
-  float yv[TM];
+  E yv[TM];
 #pragma unroll
-  for (int r = 0; r < TM; ++r) yv[r] = El<E>::get(yb[(size_t)tok[r] * g.O]);
+  for (int r = 0; r < TM; ++r) yv[r] = yb[(size_t)tr.tok[r] * g.O];
 
-  while (todo) {
-    int a;
-    const uint32_t m = next_group<TM>(todo, aid, a);
-    todo &= ~m;
+  // rows m of the tile that use adapter a
+  auto group = [&](uint32_t m, int a) {
     float acc[TM];
 #pragma unroll
     for (int r = 0; r < TM; ++r) acc[r] = 0.f;
@@ -399,7 +452,6 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
         braw[j] = ld16(Bg + (size_t)row * R + kb + q * VEC);
       }
       // v rows of this group (zeros for rows outside it), on the first pass
-      constexpr int NVV = (TM * 256 / 4 + 255) / 256;  // up to R = 256 in one go
       f32x4 vraw[NVV];
       const int nv4 = TM * R / 4;
       if (kb == 0) {
@@ -429,7 +481,7 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
           const int i = tid + 256 * j;
           *reinterpret_cast<f32x4*>(vs + (i < nv4 ? i * 4 : nv4 * 4)) = vraw[j];
         }
-        for (int i = tid + 256 * NVV; i < nv4; i += 256) {  // R > 256: rare, plain loop
+        for (int i = tid + 256 * NVV; i < nv4; i += 256) {  // large R: rare, plain loop
           const int r = (i * 4) / R;
           const bool mem = (m >> r) & 1u;
           const int k = i * 4 - r * R;
@@ -457,11 +509,42 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
     if (tid < ncv) {
 #pragma unroll
       for (int r = 0; r < TM; ++r) {
-        if ((m >> r) & 1u) yb[(size_t)tok[r] * g.O] = El<E>::put(yv[r] + acc[r]);
+        if ((m >> r) & 1u) yb[(size_t)tr.tok[r] * g.O] = El<E>::put(El<E>::get(yv[r]) + acc[r]);
       }
     }
-    __syncthreads();  // Bs / vs are rewritten by the next group
+  };
+  if constexpr (MODE == kRows) {
+    while (todo) {
+      int a;
+      const uint32_t m = next_group<TM>(todo, tr.aid, a);
+      todo &= ~m;
+      group(m, a);
+      __syncthreads();  // Bs / vs are rewritten by the next group
+    }
+  } else if (todo) {
+    group(todo, tr.aid[0]);  // one adapter per tile
   }
+}
+
+// Tile lookup of the MFMA kernels (segments or tile-list mode): first row r0
+// of the row list, row count and adapter slot, the same in every lane.  The
+// tile-list record is (slot, rows, first row, 0).
+template <int TMR, int MODE>
+__device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int& cnt, int& sid) {
+  if constexpr (MODE == kList) {
+    if (f >= L.num_tiles) return false;
+    const int w = L.tiles[(size_t)f * LORA_PLAN_MFMA_WORDS + (threadIdx.x & 3)];
+    sid = __builtin_amdgcn_readlane(w, 0);
+    cnt = __builtin_amdgcn_readlane(w, 1);
+    r0 = __builtin_amdgcn_readlane(w, 2);
+  } else {
+    if (!find_tile<TMR>(L, f, r0, cnt, sid)) return false;
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    cnt = __builtin_amdgcn_readfirstlane(cnt);
+    sid = __builtin_amdgcn_readfirstlane(sid);
+  }
+  cnt = min(cnt, TMR);
+  return true;
 }
 
 // ------------------------------------------------------------ shrink (MFMA)
@@ -475,17 +558,18 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
 // Loads run three steps ahead of the MFMAs (register ring), which is what
 // keeps HBM busy when only about one workgroup per CU exists.  Ranks >= R are
 // masked (no load, no store), so any R that is a multiple of 8 is accepted.
+template <int MODE>
 __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ A,
                                                           float* __restrict__ v, RowList L,
                                                           Geo g) {
-  constexpr int TMR = 32;
+  constexpr int TMR = kMfmaTileRows;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / g.S;
   const int s = bid - f * g.S;
   int r0, cnt, sid;
-  if (!find_tile<TMR>(L, f, r0, cnt, sid)) return;
-  if (sid < 0 || sid >= g.max_loras) return;
+  if (!mfma_tile<TMR, MODE>(L, f, r0, cnt, sid)) return;
+  if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1, wr = wave >> 1;
@@ -566,11 +650,12 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
 // columns, columns = tokens).  Inside a pair, MFMA row n of tile 2q maps to
 // column 32q + 8(n/4) + n%4 and of tile 2q+1 to the same + 4, so lane (g, m)
 // ends with columns 32q + 8g .. +8 of token m: one 16-byte y access.
+template <int MODE>
 __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restrict__ v,
                                                           const uint16_t* __restrict__ B,
                                                           uint16_t* __restrict__ y, RowList L,
                                                           Geo g, Chunks ch) {
-  constexpr int TMR = 32;
+  constexpr int TMR = kMfmaTileRows;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / ch.total;
   const int cidx = bid - f * ch.total;
@@ -580,8 +665,8 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
     if (i < g.S && cidx >= ch.start[i]) s = i;
   const int col0 = (cidx - ch.start[s]) * kExpandMfmaCols;
   int r0, cnt, sid;
-  if (!find_tile<TMR>(L, f, r0, cnt, sid)) return;
-  if (sid < 0 || sid >= g.max_loras) return;
+  if (!mfma_tile<TMR, MODE>(L, f, r0, cnt, sid)) return;
+  if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wt = wave & 1, wc = wave >> 1;
@@ -725,140 +810,153 @@ static Chunks make_chunks(const Geo& g, int nc) {
   return c;
 }
 
-// Number of tiles of `tm` rows for a row list; exact when the host knows the
-// segment lengths, otherwise an upper bound (surplus workgroups exit at once).
-static int64_t count_tiles(const RowList& L, int tm, const int32_t* host_seg_starts,
-                           const int32_t* host_seg_lens) {
+static unsigned grid_of(int64_t n) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(n, (int64_t)1 << 31));
+}
+
+// Upper bound on the tiles of `tm` rows in a device row list (segments or rows
+// mode); surplus workgroups exit after the lookup.
+static int64_t count_tiles(const RowList& L, int tm) {
   if (L.ids) return ((int64_t)L.num_rows + tm - 1) / tm;
-  if (!host_seg_lens) {
-    int64_t n = ((int64_t)L.num_rows + tm - 1) / tm + L.num_segs;
-    if (L.seg_max < INT32_MAX)  // every covered segment is at most seg_max rows long
-      n = std::min<int64_t>(n, (int64_t)L.num_segs * (((int64_t)L.seg_max + tm - 1) / tm));
-    return n;
-  }
-  int64_t n = 0;
-  for (int i = 0; i < L.num_segs; ++i) {
-    const int st = host_seg_starts[i];
-    int ln = host_seg_lens[i];
-    if (st < 0 || st >= L.num_rows || ln <= 0) continue;
-    ln = std::min(ln, L.num_rows - st);
-    if (ln < L.seg_min || ln > L.seg_max) continue;
-    n += (ln + tm - 1) / tm;
-  }
+  int64_t n = ((int64_t)L.num_rows + tm - 1) / tm + L.num_segs;
+  if (L.seg_max < INT32_MAX)  // every covered segment is at most seg_max rows long
+    n = std::min<int64_t>(n, (int64_t)L.num_segs * (((int64_t)L.seg_max + tm - 1) / tm));
   return n;
 }
 
-static int sgmv_mfma_min_rows() {
-  static int v = [] {
-    const char* e = std::getenv("LORA_SGMV_MFMA_MIN_ROWS");
-    int x = e ? std::atoi(e) : kSgmvMfmaMinRows;
-    return x < 1 ? 1 : x;
-  }();
-  return v;
-}
-
-static bool mfma_eligible(const Geo& g) { return g.dtype == LORA_BF16; }
-
-template <typename E>
+template <typename E, int MODE>
 static int32_t launch_shrink_wave(const Geo& g, const void* x, const void* A, float* v,
                                   const RowList& L, int64_t tiles, hipStream_t st) {
   if (tiles <= 0) return LORA_OK;
   const int waves = std::min(16, (g.K + 511) / 512);
-  const dim3 block(64 * waves);
   const int64_t grid = tiles * g.S * (g.R / 4);
-  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
-  hipLaunchKernelGGL((shrink_wave_kernel<E, kWaveTileRows, 4>), dim3((unsigned)grid), block, 0,
-                     st, (const E*)x, (const E*)A, v, L, g);
+  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one shrink launch");
+  hipLaunchKernelGGL((shrink_wave_kernel<E, kWaveTileRows, 4, MODE>), dim3(grid_of(grid)),
+                     dim3(64 * waves), 0, st, (const E*)x, (const E*)A, v, L, g);
   return hip_check("shrink_wave launch");
 }
 
-template <typename E>
-static int32_t launch_expand_wave(const Geo& g, const float* v, const void* B, void* y,
-                                  const RowList& L, int64_t tiles, hipStream_t st) {
-  if (tiles <= 0) return LORA_OK;
+template <typename E, int KB, int MODE>
+static int32_t launch_expand_wave_kb(const Geo& g, const float* v, const void* B, void* y,
+                                     const RowList& L, int64_t tiles, hipStream_t st) {
   const Chunks ch = make_chunks(g, kExpandCols);
   const int64_t grid = tiles * ch.total;
-  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
-  const size_t lds = sizeof(E) * (kExpandCols + 1) * (64 + 16 / sizeof(E)) +
+  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one expand launch");
+  const size_t lds = sizeof(E) * (kExpandCols + 1) * (KB + 16 / sizeof(E)) +
                      sizeof(float) * (kWaveTileRows * g.R + 4);
   if (lds > 160 * 1024) return fail(LORA_E_SHAPE, "max_lora_rank too large for the expand kernel");
-  hipLaunchKernelGGL((expand_wave_kernel<E, kWaveTileRows>), dim3((unsigned)grid), dim3(256), lds,
-                     st, v, (const E*)B, (E*)y, L, g, ch);
+  hipLaunchKernelGGL((expand_wave_kernel<E, kWaveTileRows, KB, MODE>), dim3(grid_of(grid)),
+                     dim3(256), lds, st, v, (const E*)B, (E*)y, L, g, ch);
   return hip_check("expand_wave launch");
 }
 
+template <typename E, int MODE>
+static int32_t launch_expand_wave(const Geo& g, const float* v, const void* B, void* y,
+                                  const RowList& L, int64_t tiles, hipStream_t st) {
+  if (tiles <= 0) return LORA_OK;
+  return g.R <= 16 ? launch_expand_wave_kb<E, 16, MODE>(g, v, B, y, L, tiles, st)
+                   : launch_expand_wave_kb<E, 64, MODE>(g, v, B, y, L, tiles, st);
+}
+
+template <int MODE>
 static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, float* v,
                                   const RowList& L, int64_t tiles, hipStream_t st) {
   if (tiles <= 0) return LORA_OK;
-  const int64_t gx = tiles * g.S;
-  if (gx > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
+  if (tiles * g.S > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
   const unsigned gy = (unsigned)((g.R + 63) / 64);
-  hipLaunchKernelGGL(shrink_mfma_kernel, dim3((unsigned)gx, gy), dim3(256), 0, st,
+  hipLaunchKernelGGL(shrink_mfma_kernel<MODE>, dim3(grid_of(tiles * g.S), gy), dim3(256), 0, st,
                      (const uint16_t*)x, (const uint16_t*)A, v, L, g);
   return hip_check("shrink_mfma launch");
 }
 
+template <int MODE>
 static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, void* y,
                                   const RowList& L, int64_t tiles, hipStream_t st) {
   if (tiles <= 0) return LORA_OK;
   const Chunks ch = make_chunks(g, kExpandMfmaCols);
-  const int64_t grid = tiles * ch.total;
-  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large");
-  hipLaunchKernelGGL(expand_mfma_kernel, dim3((unsigned)grid), dim3(256), 0, st, v,
-                     (const uint16_t*)B, (uint16_t*)y, L, g, ch);
+  if (tiles * ch.total > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
+  hipLaunchKernelGGL(expand_mfma_kernel<MODE>, dim3(grid_of(tiles * ch.total)), dim3(256), 0, st,
+                     v, (const uint16_t*)B, (uint16_t*)y, L, g, ch);
   return hip_check("expand_mfma launch");
 }
 
 int32_t run_shrink(const Geo& g, const void* x, const void* A, float* v, RowList L,
-                   const int32_t* host_seg_starts, const int32_t* host_seg_lens, hipStream_t st) {
+                   hipStream_t st) {
   if (L.num_rows <= 0) return LORA_OK;
-  if (L.ids) {  // BGMV
-    L.seg_min = 0;
-    L.seg_max = INT32_MAX;
-    const int64_t tiles = count_tiles(L, kWaveTileRows, nullptr, nullptr);
-    return g.dtype == LORA_BF16 ? launch_shrink_wave<uint16_t>(g, x, A, v, L, tiles, st)
-                                : launch_shrink_wave<float>(g, x, A, v, L, tiles, st);
+  const bool bf = g.dtype == LORA_BF16;
+  if (L.ids) {  // BGMV rows
+    const int64_t tiles = count_tiles(L, kWaveTileRows);
+    return bf ? launch_shrink_wave<uint16_t, kRows>(g, x, A, v, L, tiles, st)
+              : launch_shrink_wave<float, kRows>(g, x, A, v, L, tiles, st);
   }
   if (L.num_segs <= 0) return LORA_OK;
-  const int thr = mfma_eligible(g) ? sgmv_mfma_min_rows() : INT32_MAX;
+  const int thr = bf ? sgmv_mfma_min_rows() : INT32_MAX;
   RowList Lm = L, Lw = L;
   Lm.seg_min = thr;
   Lm.seg_max = INT32_MAX;
   Lw.seg_min = 0;
   Lw.seg_max = thr - 1;
   if (thr != INT32_MAX) {
-    const int64_t tm = count_tiles(Lm, 32, host_seg_starts, host_seg_lens);
-    if (int32_t e = launch_shrink_mfma(g, x, A, v, Lm, tm, st)) return e;
+    if (int32_t e = launch_shrink_mfma<kSegs>(g, x, A, v, Lm, count_tiles(Lm, kMfmaTileRows), st))
+      return e;
   }
-  const int64_t tw = count_tiles(Lw, kWaveTileRows, host_seg_starts, host_seg_lens);
-  return g.dtype == LORA_BF16 ? launch_shrink_wave<uint16_t>(g, x, A, v, Lw, tw, st)
-                              : launch_shrink_wave<float>(g, x, A, v, Lw, tw, st);
+  const int64_t tw = count_tiles(Lw, kWaveTileRows);
+  return bf ? launch_shrink_wave<uint16_t, kSegs>(g, x, A, v, Lw, tw, st)
+            : launch_shrink_wave<float, kSegs>(g, x, A, v, Lw, tw, st);
 }
 
 int32_t run_expand(const Geo& g, const float* v, const void* B, void* y, RowList L,
-                   const int32_t* host_seg_starts, const int32_t* host_seg_lens, hipStream_t st) {
+                   hipStream_t st) {
   if (L.num_rows <= 0) return LORA_OK;
+  const bool bf = g.dtype == LORA_BF16;
   if (L.ids) {
-    L.seg_min = 0;
-    L.seg_max = INT32_MAX;
-    const int64_t tiles = count_tiles(L, kWaveTileRows, nullptr, nullptr);
-    return g.dtype == LORA_BF16 ? launch_expand_wave<uint16_t>(g, v, B, y, L, tiles, st)
-                                : launch_expand_wave<float>(g, v, B, y, L, tiles, st);
+    const int64_t tiles = count_tiles(L, kWaveTileRows);
+    return bf ? launch_expand_wave<uint16_t, kRows>(g, v, B, y, L, tiles, st)
+              : launch_expand_wave<float, kRows>(g, v, B, y, L, tiles, st);
   }
   if (L.num_segs <= 0) return LORA_OK;
-  const int thr = mfma_eligible(g) ? sgmv_mfma_min_rows() : INT32_MAX;
+  const int thr = bf ? sgmv_mfma_min_rows() : INT32_MAX;
   RowList Lm = L, Lw = L;
   Lm.seg_min = thr;
   Lm.seg_max = INT32_MAX;
   Lw.seg_min = 0;
   Lw.seg_max = thr - 1;
   if (thr != INT32_MAX) {
-    const int64_t tm = count_tiles(Lm, 32, host_seg_starts, host_seg_lens);
-    if (int32_t e = launch_expand_mfma(g, v, B, y, Lm, tm, st)) return e;
+    if (int32_t e = launch_expand_mfma<kSegs>(g, v, B, y, Lm, count_tiles(Lm, kMfmaTileRows), st))
+      return e;
   }
-  const int64_t tw = count_tiles(Lw, kWaveTileRows, host_seg_starts, host_seg_lens);
-  return g.dtype == LORA_BF16 ? launch_expand_wave<uint16_t>(g, v, B, y, Lw, tw, st)
-                              : launch_expand_wave<float>(g, v, B, y, Lw, tw, st);
+  const int64_t tw = count_tiles(Lw, kWaveTileRows);
+  return bf ? launch_expand_wave<uint16_t, kSegs>(g, v, B, y, Lw, tw, st)
+            : launch_expand_wave<float, kSegs>(g, v, B, y, Lw, tw, st);
+}
+
+static void plan_lists(const TilePlan& p, RowList& Lw, RowList& Lm) {
+  Lw = RowList{p.perm, nullptr, nullptr, nullptr, nullptr, p.wave, 0, p.num_rows, p.wave_tiles,
+               0, INT32_MAX};
+  Lm = RowList{p.perm, nullptr, nullptr, nullptr, nullptr, p.mfma, 0, p.num_sgmv_rows,
+               p.mfma_tiles, 0, INT32_MAX};
+}
+
+int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, const TilePlan& p,
+                        hipStream_t st) {
+  const bool bf = g.dtype == LORA_BF16;
+  if (p.mfma_tiles > 0 && !bf) return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
+  RowList Lw, Lm;
+  plan_lists(p, Lw, Lm);
+  if (int32_t e = launch_shrink_mfma<kList>(g, x, A, v, Lm, p.mfma_tiles, st)) return e;
+  return bf ? launch_shrink_wave<uint16_t, kList>(g, x, A, v, Lw, p.wave_tiles, st)
+            : launch_shrink_wave<float, kList>(g, x, A, v, Lw, p.wave_tiles, st);
+}
+
+int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, const TilePlan& p,
+                        hipStream_t st) {
+  const bool bf = g.dtype == LORA_BF16;
+  if (p.mfma_tiles > 0 && !bf) return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
+  RowList Lw, Lm;
+  plan_lists(p, Lw, Lm);
+  if (int32_t e = launch_expand_mfma<kList>(g, v, B, y, Lm, p.mfma_tiles, st)) return e;
+  return bf ? launch_expand_wave<uint16_t, kList>(g, v, B, y, Lw, p.wave_tiles, st)
+            : launch_expand_wave<float, kList>(g, v, B, y, Lw, p.wave_tiles, st);
 }
 
 int32_t run_pool_load(const Geo& g, void* A_slot_slice, void* B_slot_slice, const void* Asrc,

@@ -164,15 +164,26 @@ def test_kernel_entry_points_validate_before_hip():
     assert _status(L.lora_bgmv_shrink, bad, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 5, 0) == _lib.LORA_E_ALIGN
 
 
+def _aligned_i32(n):
+    raw = np.zeros(n + 16, np.int32)
+    off = (-raw.ctypes.data % 64) // 4
+    return raw[off:off + n]
+
+
 def test_apply_validation_before_hip():
     d = L.make_desc("bf16", 4, 16, 256, [256])
     T = 6
     ws_need = L.lora_apply_workspace_bytes(d, T)
     mh_need = L.lora_apply_host_meta_bytes(d, T)
-    assert mh_need == 4 * (3 * T + 3 * 4)
-    assert ws_need == ((mh_need + 255) // 256) * 256 + T * 16 * 4
+    # staging: builder arrays (3T + 3 max_loras words, padded to 4), then the
+    # plan image: perm (T, padded to 4), <= ceil(T/8) + 2 max_loras wave tiles
+    # of 16 words, <= ceil(T/32) + max_loras MFMA tiles of 4 words
+    up4 = lambda n: (n + 3) // 4 * 4  # noqa: E731
+    image = up4(T) + 16 * (-(-T // 8) + 2 * 4) + 4 * (-(-T // 32) + 4)
+    assert mh_need == 4 * (up4(3 * T + 3 * 4) + image)
+    assert ws_need == ((4 * image + 255) // 256) * 256 + T * 16 * 4
     ids = np.array([0, 1, -1, 3, 2, 0], np.int32)
-    meta = np.zeros(mh_need // 4, np.int32)
+    meta = _aligned_i32(mh_need // 4)
     ok = [d, FAKE, FAKE, FAKE, FAKE + 64, T, ids, None, 0, FAKE, ws_need, meta, mh_need, 0]
 
     def with_(i, v):

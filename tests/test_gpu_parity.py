@@ -292,3 +292,34 @@ def test_pool_contents_bit_exact(dtype, host_source):
     # a cleared slot adds nothing
     pool.clear(1)
     assert not pool.A_view()[1].any() and not pool.B_view()[1].any()
+
+
+# ------------------------------------------------ plan reused across layers
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_plan_reused_across_layers(dtype):
+    """One host plan, copied to the GPU once, drives two layers (different x
+    and y, the same batch) through lora_plan_shrink / lora_plan_expand: SGMV
+    MFMA tiles (bf16), short-segment and BGMV wavefront tiles."""
+    import torch
+    wl, _ = W.config_mlp_mixed(seed=4, n_prefill=3, len_lo=5, len_hi=70, n_decode=23,
+                               hidden=520, inter=264, n_adapters=5, dtype=dtype)
+    pool = make_pool(wl)
+    plan, img, views = L.lora_apply_plan(pool.desc, wl.ids, wl.prefill)
+    if dtype == "bf16":
+        assert plan["mfma_tiles"] > 0
+    assert plan["wave_tiles"] > 0
+    image = torch.from_numpy(img).cuda()
+    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
+    v = torch.full((max(rows, 1), wl.num_slices * pool.R), float("nan"), dtype=torch.float32,
+                   device="cuda")
+    rng = np.random.default_rng(11)
+    layers = [wl, dataclasses.replace(
+        wl, x=W.to_dtype_values(rng.standard_normal((wl.T, wl.in_features)), dtype),
+        y_in=W.to_dtype_values(rng.standard_normal((wl.T, wl.O)), dtype))]
+    for i, lw in enumerate(layers):
+        xd, yd = to_dev(lw.x, dtype), to_dev(lw.y_in, dtype)
+        L.lora_plan_shrink(pool.desc, xd, pool.A, v, wl.T, plan, image)
+        L.lora_plan_expand(pool.desc, v, pool.B, yd, wl.T, plan, image)
+        torch.cuda.synchronize()
+        check_rows(lw, yd, label=f"plan layer {i} {dtype}")

@@ -1,0 +1,143 @@
+"""lora_apply's host tile plan (CPU only): every SGMV and BGMV row of the batch
+is covered exactly once by the shrink tiles and once by the expand tiles, each
+tile holds consecutive rows of one adapter, and the records carry the tokens
+the metadata builder assigns to those rows."""
+import numpy as np
+import pytest
+
+import lora_adapter_pool_amd as L
+import workloads as W
+
+WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS = 8, 32, 16
+
+
+def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
+    ids = np.asarray(ids, np.int32)
+    R = desc.max_lora_rank
+    p, img, v = L.lora_apply_plan(desc, ids, prefill, bgmv_max_rank)
+    m = L.lora_build_meta(ids, prefill, desc.max_loras, R, bgmv_max_rank)
+    ns, nb = m["sgmv_perm"].size, m["bgmv_tok"].size
+    assert (p["num_sgmv_rows"], p["num_bgmv_rows"], p["num_segs"]) == (ns, nb, m["seg_ids"].size)
+    assert p["image_offset"] % 16 == 0 and p["off_wave"] % 4 == 0
+    np.testing.assert_array_equal(v["perm"], m["sgmv_perm"])
+    # token and adapter of every v row, in the builder's order
+    row_tok = np.concatenate([m["sgmv_perm"], m["bgmv_tok"]]).astype(np.int64)
+    row_ids = ids[row_tok] if row_tok.size else np.zeros(0, np.int32)
+    seg_len_of_row = np.zeros(ns, np.int64)
+    for st, ln in zip(m["seg_starts"], m["seg_lens"]):
+        seg_len_of_row[st:st + ln] = ln
+    bf16 = desc.dtype == L.LORA_BF16
+    thr = MFMA_MIN_ROWS if bf16 else np.iinfo(np.int32).max
+    assert p["mfma_min_rows"] == (MFMA_MIN_ROWS if bf16 else np.iinfo(np.int32).max)
+
+    shrink_cover = np.zeros(ns + nb, np.int64)
+    for rec in v["wave"]:
+        slot, rows, first, zero = (int(x) for x in rec[:4])
+        assert zero == 0 and 1 <= rows <= WAVE_ROWS and 0 <= slot < desc.max_loras
+        assert 0 <= first and first + rows <= ns + nb
+        np.testing.assert_array_equal(rec[4:4 + rows], row_tok[first:first + rows])
+        assert np.all(rec[4 + rows:] == -1)
+        assert np.all(row_ids[first:first + rows] == slot)
+        if first < ns:  # SGMV tiles stay inside the SGMV rows, short segments only
+            assert first + rows <= ns and np.all(seg_len_of_row[first:first + rows] < thr)
+        shrink_cover[first:first + rows] += 1
+    for rec in v["mfma"]:
+        slot, rows, first, zero = (int(x) for x in rec)
+        assert bf16 and zero == 0 and 1 <= rows <= MFMA_ROWS and first + rows <= ns
+        assert np.all(row_ids[first:first + rows] == slot)
+        assert np.all(seg_len_of_row[first:first + rows] >= thr)
+        shrink_cover[first:first + rows] += 1
+    np.testing.assert_array_equal(shrink_cover, np.ones(ns + nb, np.int64))
+    # tile counts: each segment / BGMV run cut into ceil(len / tile rows) pieces
+    want_wave = want_mfma = 0
+    for ln in m["seg_lens"]:
+        if ln >= thr:
+            want_mfma += -(-int(ln) // MFMA_ROWS)
+        else:
+            want_wave += -(-int(ln) // WAVE_ROWS)
+    b = m["bgmv_ids"]
+    i = 0
+    while i < nb:
+        j = i
+        while j < nb and b[j] == b[i]:
+            j += 1
+        want_wave += -(-(j - i) // WAVE_ROWS)
+        i = j
+    assert (p["wave_tiles"], p["mfma_tiles"]) == (want_wave, want_mfma)
+    assert p["image_bytes"] == 4 * (p["off_mfma"] + 4 * p["mfma_tiles"])
+    assert p["image_bytes"] + p["image_offset"] <= L.lora_apply_host_meta_bytes(desc, ids.size)
+    return p
+
+
+@pytest.mark.parametrize("prefill", [True, False])
+def test_plan_tiny(prefill):
+    wl = W.config_tiny_fp32(seed=0, prefill=prefill)
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    p = _check_plan(d, wl.ids, wl.prefill)
+    # three adapters with 8 rows each: three full wavefront tiles either way
+    assert p["wave_tiles"] == 3 and p["mfma_tiles"] == 0
+
+
+def test_plan_named_workloads():
+    cases = [W.config_bgmv_decode(seed=0), W.config_sgmv_prefill(seed=0),
+             W.config_qkv_decode(seed=0)] + list(W.config_mlp_mixed(seed=0))
+    for wl in cases:
+        d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features,
+                        wl.out_features)
+        _check_plan(d, wl.ids, wl.prefill)
+
+
+def test_plan_fuzz():
+    rng = np.random.default_rng(7)
+    for it in range(300):
+        ml = int(rng.integers(1, 70))
+        T = int(rng.integers(0, 400))
+        R = int(rng.choice([8, 16, 64, 80]))
+        dtype = "bf16" if it % 3 else "f32"
+        d = L.make_desc(dtype, ml, R, 64, [64, 32])
+        ids = rng.integers(-1, ml, size=T).astype(np.int32)
+        if it % 4 == 0:  # long runs of one adapter
+            ids = np.sort(ids)
+        pre = (rng.random(T) < rng.random()).astype(np.uint8)
+        _check_plan(d, ids, pre if it % 5 else None, bgmv_max_rank=int(rng.choice([0, 8, 128])))
+
+
+def test_plan_errors():
+    d = L.make_desc("bf16", 4, 16, 64, [64])
+    with pytest.raises(L.LoraError) as e:
+        L.lora_apply_plan(d, np.array([0, 4], np.int32))
+    assert e.value.status == -6
+    p, _, _ = L.lora_apply_plan(d, np.zeros(0, np.int32))
+    assert p["wave_tiles"] == p["mfma_tiles"] == 0 and p["image_bytes"] == 0
+
+
+def test_plan_entry_validation_before_hip():
+    """Malformed plans are rejected on the host, before any GPU call."""
+    import lora_adapter_pool_amd._lib as _lib
+    FAKE = 1 << 20
+    d = L.make_desc("bf16", 4, 16, 64, [64])
+    ids = np.array([0, 0, 1, 3, -1, 2], np.int32)
+    p, _, _ = L.lora_apply_plan(d, ids, np.ones(6, np.uint8))
+
+    def status(fn, plan, image=FAKE, T=6, desc=d):
+        try:
+            fn(desc, FAKE, FAKE, FAKE, T, plan, image, 0)
+            return 0
+        except L.LoraError as e:
+            return e.status
+
+    for fn in (L.lora_plan_shrink, L.lora_plan_expand):
+        for key, val in (("wave_tiles", -1), ("off_wave", -4), ("num_bgmv_rows", -2)):
+            assert status(fn, dict(p, **{key: val})) == _lib.LORA_E_ARG
+        assert status(fn, dict(p, image_bytes=p["image_bytes"] - 4)) == _lib.LORA_E_ARG
+        assert status(fn, p, image=FAKE + 4) == _lib.LORA_E_ALIGN
+        assert status(fn, dict(p, off_wave=p["off_wave"] + 1)) == _lib.LORA_E_ALIGN
+        assert status(fn, p, image=0) == _lib.LORA_E_ARG
+        assert status(fn, p, T=0) == 0  # no rows: no-op, nothing launched
+        empty = dict(p, wave_tiles=0, mfma_tiles=0)
+        assert status(fn, empty) == 0
+    # MFMA tiles need a bf16 pool
+    d32 = L.make_desc("f32", 4, 16, 64, [64])
+    pm, _, _ = L.lora_apply_plan(d, np.zeros(40, np.int32), np.ones(40, np.uint8))
+    assert pm["mfma_tiles"] > 0
+    assert status(L.lora_plan_shrink, pm, desc=d32, T=40) == _lib.LORA_E_DTYPE
