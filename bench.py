@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--record-traffic", metavar="PMC_DIR", default=None,
+                   help="write profiles/traffic.json from rocprofv3 counter runs and exit")
     return p.parse_args()
 
 
@@ -127,6 +129,8 @@ class Setup:
         self.plan_d, img, _ = L.lora_apply_plan(self.desc, self.ids, self.pre)
         self.plan = L.plan_struct(self.plan_d)
         self.image = torch.from_numpy(img if img.size else np.zeros(4, np.int32)).cuda()
+        # host copy: a small plan then travels in the kernel arguments, as in lora_apply
+        self.image_host = np.ascontiguousarray(img if img.size else np.zeros(4, np.int32))
         rows = self.plan_d["num_sgmv_rows"] + self.plan_d["num_bgmv_rows"]
         S, R = wl.num_slices, wl.max_lora_rank
         self.v = torch.zeros((max(rows, 1), S * R), dtype=torch.float32, device="cuda")
@@ -159,27 +163,18 @@ class Setup:
         d = ctypes.byref(self.desc)
         if which == "shrink":
             st = lib.lora_plan_shrink(d, self.px[r], self.pA[r], self.v.data_ptr(), self.T,
-                                      ctypes.byref(self.plan), self.image.data_ptr(), stream_ptr)
+                                      ctypes.byref(self.plan), self.image.data_ptr(),
+                                      self.image_host.ctypes.data, stream_ptr)
         else:
             st = lib.lora_plan_expand(d, self.v.data_ptr(), self.pB[r], self.py[r], self.T,
-                                      ctypes.byref(self.plan), self.image.data_ptr(), stream_ptr)
+                                      ctypes.byref(self.plan), self.image.data_ptr(),
+                                      self.image_host.ctypes.data, stream_ptr)
         if st != 0:
             raise RuntimeError(f"{which} failed: {L.last_error()}")
 
     def kernels(self):
         """Names of the kernels each launch group runs for this batch."""
-        p = self.plan_d
-        bf = self.wl.dtype == "bf16"
-        tag = "unsigned short" if bf else "float"
-        kb = 16 if self.wl.max_lora_rank <= 16 else 64
-        out = {"shrink": [], "expand": []}
-        if p["mfma_tiles"]:
-            out["shrink"].append("shrink_mfma_kernel<2>")
-            out["expand"].append("expand_mfma_kernel<2>")
-        if p["wave_tiles"]:
-            out["shrink"].append(f"shrink_wave_kernel<{tag}, 8, 4, 2>")
-            out["expand"].append(f"expand_wave_kernel<{tag}, 8, {kb}, 2>")
-        return out
+        return stage_kernels(self.wl)
 
 
 def time_kernel(setups, which, launches, warm, stream_ptr):
@@ -259,22 +254,95 @@ def kernel_roofline(setups, stream_ptr, launches):
     return dom, res
 
 
-def load_traffic(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    counters, valid only while the kernel source is unchanged."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 2 * (1 << 28)  # the device-copy measurement moves 512 MiB each way
+
+
+def kernel_source_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(stage, workload):
+    """HBM bytes per launch group from committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters, valid only while the kernel source is unchanged."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        with open(path) as f:
-            data = json.load(f)
-        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-        ent = data.get(f"{workload}:{kernel}")
-        if not ent or ent.get("kernel_source_sha") != sha:
+        with open(TRAFFIC_JSON) as f:
+            ent = json.load(f).get(f"{workload}:{stage}")
+        if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
             return None
         return float(ent["hbm_bytes_per_launch"])
-    except Exception:
+    except (OSError, ValueError, KeyError):
         return None
+
+
+def stage_kernels(wl):
+    """Kernel names of each launch group for a workload's batch (host-side
+    plan only, no GPU)."""
+    import lora_adapter_pool_amd as L
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    p, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    tag = "unsigned short" if wl.dtype == "bf16" else "float"
+    kb = 16 if wl.max_lora_rank <= 16 else 64
+    out = {"shrink": [], "expand": []}
+    if p["mfma_tiles"]:
+        out["shrink"].append("shrink_mfma_kernel<2>")
+        out["expand"].append("expand_mfma_kernel<2>")
+    if p["wave_tiles"]:
+        # mode 3: records in the kernel arguments (small plans), 2: device image
+        mode = 3 if not p["mfma_tiles"] and p["wave_tiles"] * 16 <= 512 else 2
+        out["shrink"].append(f"shrink_wave_kernel<{tag}, 8, 4, {mode}>")
+        out["expand"].append(f"expand_wave_kernel<{tag}, 8, {kb}, {mode}>")
+    return out
+
+
+def record_traffic(pmc_dir, workload, seed):
+    """Write profiles/traffic.json entries for `workload` from two rocprofv3
+    counter runs of this script: <pmc_dir>/fetch (--pmc FETCH_SIZE) and
+    <pmc_dir>/write (--pmc WRITE_SIZE).  Both counters are scaled by what they
+    read for the device-to-device copy of known size that every run makes."""
+    import csv
+    import glob
+
+    def per_kernel(sub, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(pmc_dir, sub, "*_counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("lora::", "")
+                vals.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    # the copies of the bandwidth measurement are the largest copyBuffer dispatches
+    cf = COPY_BYTES / max(fetch["__amd_rocclr_copyBuffer"])
+    cw = COPY_BYTES / max(write["__amd_rocclr_copyBuffer"])
+    data = {}
+    if os.path.exists(TRAFFIC_JSON):
+        data = json.load(open(TRAFFIC_JSON))
+    sha = kernel_source_sha()
+    wls = make_workloads(workload, seed)
+    kern = {"shrink": set(), "expand": set()}
+    for wl in wls:
+        for k, v in stage_kernels(wl).items():
+            kern[k].update(v)
+    for stage, names in kern.items():
+        # one launch group = one dispatch of each of its kernels; averaged over
+        # the workload's calls like the algorithmic bytes
+        tot = 0.0
+        for n in names:
+            f, w = fetch.get(n), write.get(n)
+            if not f or not w:
+                raise SystemExit(f"no counters for {n} in {pmc_dir}")
+            tot += (sum(f) / len(f)) * cf + (sum(w) / len(w)) * cw
+        data[f"{workload}:{stage}"] = {
+            "hbm_bytes_per_launch": tot, "kernels": sorted(names),
+            "fetch_scale": cf, "write_scale": cw, "kernel_source_sha": sha}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({k: v for k, v in data.items() if k.startswith(workload + ":")}, indent=1))
 
 
 def cpu_baseline(wl, seconds):
@@ -316,6 +384,9 @@ def cpu_baseline(wl, seconds):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.record_traffic, args.workload, args.seed)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(token rows are independent, so data parallelism needs no "

@@ -268,26 +268,35 @@ int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* id
                         const uint8_t* prefill_host, int32_t bgmv_max_rank, void* meta_host,
                         int64_t meta_host_bytes, lora_plan* plan);
 
-/* Device half of a plan, for a plan whose image the caller has copied to the
- * GPU (`image`: device pointer, 16-byte aligned, plan->image_bytes long), so
- * one plan can serve every layer of a batch.  v: device fp32
- * [num_sgmv_rows + num_bgmv_rows][S][R] (row order of the plan).
+/* Device half of a plan, so one plan can serve every layer of a batch.
+ *   image:      device copy of the plan's image (16-byte aligned,
+ *               plan->image_bytes long), or NULL when image_host is given and
+ *               the plan is small.
+ *   image_host: host copy of the image (as lora_apply_plan leaves it in
+ *               meta_host), or NULL.  A small plan (no MFMA tiles, at most 32
+ *               wavefront tiles) with a host copy travels in the kernel
+ *               arguments and `image` is not read; otherwise `image` is used.
+ *   v:          device fp32 [num_sgmv_rows + num_bgmv_rows][S][R] (plan row
+ *               order).
  *   lora_plan_shrink:  v[row][s][k] = sum_j A_pool[a][s][k][j] * x[t][j] for
  *                      every row of every tile ([TGI] step 4, shrink)
  *   lora_plan_expand:  y[t][off_s + j] = round_dtype((float)y[t][off_s + j] +
  *                      sum_k B_pool[a][off_s + j][k] * v[row][s][k])
  * Rows whose token, slot or row index is out of range are skipped.  Returns
  * LORA_E_ARG for NULL pointers or a malformed plan, LORA_E_ALIGN for a
- * misaligned image, LORA_E_DTYPE for MFMA tiles on an fp32 pool. */
+ * misaligned image, LORA_E_DTYPE for MFMA tiles on an fp32 pool.  The host
+ * image is read before the call returns. */
 int32_t lora_plan_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool, float* v,
-                         int32_t T, const lora_plan* plan, const void* image, void* stream);
+                         int32_t T, const lora_plan* plan, const void* image,
+                         const void* image_host, void* stream);
 int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void* B_pool, void* y,
-                         int32_t T, const lora_plan* plan, const void* image, void* stream);
+                         int32_t T, const lora_plan* plan, const void* image,
+                         const void* image_host, void* stream);
 
 /* The whole delta path for one batch ([TGI] step 4; [QA] direct answer):
  * lora_apply_plan into meta_host, one copy of the plan's device image into ws
- * on `stream`, then lora_plan_shrink and lora_plan_expand on `stream`,
- * updating y in place.  Rows with id -1 are never read or written.
+ * on `stream` (skipped for a small plan, which goes in the kernel arguments),
+ * then lora_plan_shrink and lora_plan_expand on `stream`, updating y in place.  Rows with id -1 are never read or written.
  *   ids_host[T], prefill_host[T] (NULL = all decode): host arrays.
  *   ws: device workspace of >= lora_apply_workspace_bytes(desc, T) bytes.
  *   meta_host: host staging of >= lora_apply_host_meta_bytes(desc, T) bytes.

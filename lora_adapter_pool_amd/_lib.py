@@ -98,8 +98,8 @@ _SIGNATURES = {
     "lora_apply_workspace_bytes": (_I64, [_DP, _I32]),
     "lora_apply_host_meta_bytes": (_I64, [_DP, _I32]),
     "lora_apply_plan": (_I32, [_DP, _I32, _P, _P, _I32, _P, _I64, ctypes.POINTER(lora_plan)]),
-    "lora_plan_shrink": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P]),
-    "lora_plan_expand": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P]),
+    "lora_plan_shrink": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P]),
+    "lora_plan_expand": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P]),
     "lora_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P, _I64, _P]),
 }
 
@@ -304,16 +304,18 @@ def plan_struct(d: dict) -> "lora_plan":
     return p
 
 
-def lora_plan_shrink(desc, x, A_pool, v, T, plan, image, stream=None) -> None:
+def lora_plan_shrink(desc, x, A_pool, v, T, plan, image, image_host=None, stream=None) -> None:
     p = plan if isinstance(plan, lora_plan) else plan_struct(plan)
     _check(lib().lora_plan_shrink(ctypes.byref(desc), _ptr(x), _ptr(A_pool), _ptr(v), int(T),
-                                  ctypes.byref(p), _ptr(image), _stream(stream)))
+                                  ctypes.byref(p), _ptr(image), _ptr(image_host),
+                                  _stream(stream)))
 
 
-def lora_plan_expand(desc, v, B_pool, y, T, plan, image, stream=None) -> None:
+def lora_plan_expand(desc, v, B_pool, y, T, plan, image, image_host=None, stream=None) -> None:
     p = plan if isinstance(plan, lora_plan) else plan_struct(plan)
     _check(lib().lora_plan_expand(ctypes.byref(desc), _ptr(v), _ptr(B_pool), _ptr(y), int(T),
-                                  ctypes.byref(p), _ptr(image), _stream(stream)))
+                                  ctypes.byref(p), _ptr(image), _ptr(image_host),
+                                  _stream(stream)))
 
 
 def lora_apply(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgmv_max_rank, ws,

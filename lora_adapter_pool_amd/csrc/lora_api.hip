@@ -65,8 +65,12 @@ int32_t sgmv_args(const int32_t* perm, const int32_t* seg_starts, const int32_t*
   return LORA_OK;
 }
 
-// Validates a caller's plan against its image and builds the device view.
-int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, TilePlan* tp) {
+// Validates a caller's plan against its image(s) and builds the device view.
+// `image` is the device copy; `image_host` (nullable) the host copy, which lets
+// a small plan travel in the kernel arguments, in which case `image` is not
+// read and may be NULL.
+int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const void* image_host,
+                  TilePlan* tp) {
   if (!p) return fail(LORA_E_ARG, "plan is NULL");
   if (p->num_sgmv_rows < 0 || p->num_bgmv_rows < 0 || p->wave_tiles < 0 || p->mfma_tiles < 0 ||
       p->off_perm < 0 || p->off_wave < 0 || p->off_mfma < 0 || p->image_bytes < 0)
@@ -82,13 +86,17 @@ int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, TilePlan*
     return fail(LORA_E_ARG, "malformed plan (sections exceed image_bytes)");
   if (p->mfma_tiles > 0 && g.dtype != LORA_BF16)
     return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
-  const bool any = p->wave_tiles > 0 || p->mfma_tiles > 0;
-  if (any) {
+  const int32_t* host = (const int32_t*)image_host;
+  const bool small = host && p->mfma_tiles == 0 &&
+                     (int64_t)p->wave_tiles * LORA_PLAN_WAVE_WORDS <= kSmallPlanWords;
+  if ((p->wave_tiles > 0 || p->mfma_tiles > 0) && !small) {
     if (int32_t e = need_ptr(image, "image")) return e;
   }
   const int32_t* img = (const int32_t*)image;
-  *tp = TilePlan{img + p->off_perm, img + p->off_wave, p->wave_tiles, img + p->off_mfma,
-                 p->mfma_tiles, p->num_sgmv_rows, p->num_sgmv_rows + p->num_bgmv_rows};
+  *tp = TilePlan{img ? img + p->off_perm : nullptr, img ? img + p->off_wave : nullptr,
+                 p->wave_tiles, img ? img + p->off_mfma : nullptr, p->mfma_tiles,
+                 host ? host + p->off_wave : nullptr, p->num_sgmv_rows,
+                 p->num_sgmv_rows + p->num_bgmv_rows};
   return LORA_OK;
 }
 
@@ -227,13 +235,14 @@ int32_t lora_bgmv_expand(const lora_pool_desc* desc, const float* v, const void*
 }
 
 int32_t lora_plan_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool, float* v,
-                         int32_t T, const lora_plan* plan, const void* image, void* stream) {
+                         int32_t T, const lora_plan* plan, const void* image,
+                         const void* image_host, void* stream) {
   clear_error();
   Geo g;
   if (int32_t e = check_desc(desc, &g)) return e;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
   TilePlan tp;
-  if (int32_t e = plan_view(g, plan, image, &tp)) return e;
+  if (int32_t e = plan_view(g, plan, image, image_host, &tp)) return e;
   if (T == 0 || (tp.wave_tiles == 0 && tp.mfma_tiles == 0)) return LORA_OK;
   if (int32_t e = check_common(desc, &g, x, "x", A_pool, "A_pool", v)) return e;
   g.T = T;
@@ -241,13 +250,14 @@ int32_t lora_plan_shrink(const lora_pool_desc* desc, const void* x, const void* 
 }
 
 int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void* B_pool, void* y,
-                         int32_t T, const lora_plan* plan, const void* image, void* stream) {
+                         int32_t T, const lora_plan* plan, const void* image,
+                         const void* image_host, void* stream) {
   clear_error();
   Geo g;
   if (int32_t e = check_desc(desc, &g)) return e;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
   TilePlan tp;
-  if (int32_t e = plan_view(g, plan, image, &tp)) return e;
+  if (int32_t e = plan_view(g, plan, image, image_host, &tp)) return e;
   if (T == 0 || (tp.wave_tiles == 0 && tp.mfma_tiles == 0)) return LORA_OK;
   if (int32_t e = check_common(desc, &g, y, "y", B_pool, "B_pool", v)) return e;
   g.T = T;
@@ -280,14 +290,18 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
     return e;
   const int32_t rows = p.num_sgmv_rows + p.num_bgmv_rows;
   if (rows == 0) return LORA_OK;
-  hipStream_t st = (hipStream_t)stream;
-  if (int32_t e = hip_ok(hipMemcpyAsync(ws, (const char*)meta_host + p.image_offset,
-                                        (size_t)p.image_bytes, hipMemcpyHostToDevice, st),
-                         "plan copy"))
-    return e;
+  const char* image_host = (const char*)meta_host + p.image_offset;
+  const bool small = p.mfma_tiles == 0 &&
+                     (int64_t)p.wave_tiles * LORA_PLAN_WAVE_WORDS <= kSmallPlanWords;
+  if (!small) {  // small plans travel in the kernel arguments instead
+    if (int32_t e = hip_ok(hipMemcpyAsync(ws, image_host, (size_t)p.image_bytes,
+                                          hipMemcpyHostToDevice, (hipStream_t)stream),
+                           "plan copy"))
+      return e;
+  }
   float* v = (float*)((char*)ws + v_off);
-  if (int32_t e = lora_plan_shrink(desc, x, A_pool, v, T, &p, ws, stream)) return e;
-  return lora_plan_expand(desc, v, B_pool, y, T, &p, ws, stream);
+  if (int32_t e = lora_plan_shrink(desc, x, A_pool, v, T, &p, ws, image_host, stream)) return e;
+  return lora_plan_expand(desc, v, B_pool, y, T, &p, ws, image_host, stream);
 }
 
 }  // extern "C"

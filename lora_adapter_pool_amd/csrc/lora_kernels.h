@@ -17,6 +17,7 @@ constexpr int kWaveTileRows = LORA_PLAN_WAVE_ROWS;  // rows per tile of the VALU
 constexpr int kMfmaTileRows = LORA_PLAN_MFMA_ROWS;  // rows per tile of the MFMA kernels
 constexpr int kExpandCols = 256;       // output columns per VALU expand workgroup
 constexpr int kExpandMfmaCols = 128;   // output columns per MFMA expand workgroup
+constexpr int kSmallPlanWords = 512;   // plans up to 32 wavefront tiles go by value (2 KB)
 
 // A list of rows to process.  Row i reads token tok[i] of x / y and writes row i
 // of v.  Three ways to cut it into tiles, one adapter per tile:
@@ -63,6 +64,7 @@ struct TilePlan {
   int32_t wave_tiles;
   const int32_t* mfma;
   int32_t mfma_tiles;
+  const int32_t* wave_host;  // host copy of the wave records, or nullptr
   int32_t num_sgmv_rows;  // rows of perm; MFMA tiles lie inside them
   int32_t num_rows;       // v rows: SGMV rows + BGMV rows
 };

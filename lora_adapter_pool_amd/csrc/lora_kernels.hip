@@ -167,7 +167,13 @@ __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int&
   return true;
 }
 
-enum { kSegs = 0, kRows = 1, kList = 2 };  // how a kernel finds its tile
+enum { kSegs = 0, kRows = 1, kList = 2, kArg = 3 };  // how a kernel finds its tile
+
+// Tile records passed by value (kArg): a small plan travels in the kernel
+// arguments, which the wavefronts read with scalar loads, so no copy of the
+// plan precedes the launch.  Other modes carry an empty struct.
+template <int MODE> struct PlanArg {};
+template <> struct PlanArg<kArg> { int32_t w[kSmallPlanWords]; };
 
 // Rows of one tile, the same in every lane (scalar registers).  Row r is v row
 // vrow0 + r, reads token tok[r] and uses adapter aid[r]; bit r of `valid` is
@@ -189,10 +195,21 @@ template <int TM> struct TileRows {
 //   kRows: rows f*TM .. of the list, tokens and adapters from tok[] / ids[].
 template <int TM, int MODE>
 __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
-                                          TileRows<TM>& tr) {
+                                          const PlanArg<MODE>& pa, TileRows<TM>& tr) {
   static_assert(TM <= LORA_PLAN_WAVE_WORDS - 4, "a tile record holds at most 12 tokens");
   const int lane = threadIdx.x & 63;
-  if constexpr (MODE == kList) {
+  if constexpr (MODE == kArg) {
+    if (f >= L.num_tiles || f >= kSmallPlanWords / LORA_PLAN_WAVE_WORDS) return false;
+    const int32_t* rec = pa.w + f * LORA_PLAN_WAVE_WORDS;
+    const int sid = rec[0];
+    tr.cnt = rec[1];
+    tr.vrow0 = rec[2];
+#pragma unroll
+    for (int r = 0; r < TM; ++r) {
+      tr.tok[r] = rec[4 + r];
+      tr.aid[r] = sid;
+    }
+  } else if constexpr (MODE == kList) {
     if (f >= L.num_tiles) return false;
     const int w = L.tiles[(size_t)f * LORA_PLAN_WAVE_WORDS + (lane & 15)];
     const int sid = __builtin_amdgcn_readlane(w, 0);
@@ -297,7 +314,7 @@ template <typename E, int TM, int RC, int MODE>
 __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__ x,
                                                            const E* __restrict__ A,
                                                            float* __restrict__ v, RowList L,
-                                                           Geo g) {
+                                                           Geo g, PlanArg<MODE> pa) {
   constexpr int V = RC * TM;
   constexpr int P = Log2<V>::value;
   __shared__ float red[16][V];
@@ -310,7 +327,7 @@ __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__
   const int s = rem / nrc;
   const int c = rem - s * nrc;
   TileRows<TM> tr;
-  if (!tile_rows<TM, MODE>(L, g, f, tr)) return;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr)) return;
   uint32_t todo = tr.valid;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -392,7 +409,7 @@ template <typename E, int TM, int KB, int MODE>
 __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restrict__ v,
                                                           const E* __restrict__ B,
                                                           E* __restrict__ y, RowList L, Geo g,
-                                                          Chunks ch) {
+                                                          Chunks ch, PlanArg<MODE> pa) {
   constexpr int NC = kExpandCols;      // 256 columns per workgroup
   constexpr int VEC = El<E>::kVec;     // elements per 16-byte vector
   constexpr int LDB = KB + VEC;        // LDS row stride: 16 bytes of padding
@@ -418,7 +435,7 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
   const int col0 = (cidx - ch.start[s]) * NC;
   const int ncv = min(NC, g.out[s] - col0);
   TileRows<TM> tr;
-  if (!tile_rows<TM, MODE>(L, g, f, tr)) return;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr)) return;
   uint32_t todo = tr.valid;
   const int tid = threadIdx.x;
   const int R = g.R;
@@ -826,19 +843,21 @@ static int64_t count_tiles(const RowList& L, int tm) {
 
 template <typename E, int MODE>
 static int32_t launch_shrink_wave(const Geo& g, const void* x, const void* A, float* v,
-                                  const RowList& L, int64_t tiles, hipStream_t st) {
+                                  const RowList& L, int64_t tiles, hipStream_t st,
+                                  const PlanArg<MODE>& pa = PlanArg<MODE>{}) {
   if (tiles <= 0) return LORA_OK;
   const int waves = std::min(16, (g.K + 511) / 512);
   const int64_t grid = tiles * g.S * (g.R / 4);
   if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one shrink launch");
   hipLaunchKernelGGL((shrink_wave_kernel<E, kWaveTileRows, 4, MODE>), dim3(grid_of(grid)),
-                     dim3(64 * waves), 0, st, (const E*)x, (const E*)A, v, L, g);
+                     dim3(64 * waves), 0, st, (const E*)x, (const E*)A, v, L, g, pa);
   return hip_check("shrink_wave launch");
 }
 
 template <typename E, int KB, int MODE>
 static int32_t launch_expand_wave_kb(const Geo& g, const float* v, const void* B, void* y,
-                                     const RowList& L, int64_t tiles, hipStream_t st) {
+                                     const RowList& L, int64_t tiles, hipStream_t st,
+                                     const PlanArg<MODE>& pa) {
   const Chunks ch = make_chunks(g, kExpandCols);
   const int64_t grid = tiles * ch.total;
   if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one expand launch");
@@ -846,16 +865,17 @@ static int32_t launch_expand_wave_kb(const Geo& g, const float* v, const void* B
                      sizeof(float) * (kWaveTileRows * g.R + 4);
   if (lds > 160 * 1024) return fail(LORA_E_SHAPE, "max_lora_rank too large for the expand kernel");
   hipLaunchKernelGGL((expand_wave_kernel<E, kWaveTileRows, KB, MODE>), dim3(grid_of(grid)),
-                     dim3(256), lds, st, v, (const E*)B, (E*)y, L, g, ch);
+                     dim3(256), lds, st, v, (const E*)B, (E*)y, L, g, ch, pa);
   return hip_check("expand_wave launch");
 }
 
 template <typename E, int MODE>
 static int32_t launch_expand_wave(const Geo& g, const float* v, const void* B, void* y,
-                                  const RowList& L, int64_t tiles, hipStream_t st) {
+                                  const RowList& L, int64_t tiles, hipStream_t st,
+                                  const PlanArg<MODE>& pa = PlanArg<MODE>{}) {
   if (tiles <= 0) return LORA_OK;
-  return g.R <= 16 ? launch_expand_wave_kb<E, 16, MODE>(g, v, B, y, L, tiles, st)
-                   : launch_expand_wave_kb<E, 64, MODE>(g, v, B, y, L, tiles, st);
+  return g.R <= 16 ? launch_expand_wave_kb<E, 16, MODE>(g, v, B, y, L, tiles, st, pa)
+                   : launch_expand_wave_kb<E, 64, MODE>(g, v, B, y, L, tiles, st, pa);
 }
 
 template <int MODE>
@@ -937,12 +957,31 @@ static void plan_lists(const TilePlan& p, RowList& Lw, RowList& Lm) {
                p.mfma_tiles, 0, INT32_MAX};
 }
 
+// Small plans (wavefront tiles only, at most kSmallPlanWords words of records)
+// with host records go by value.
+static bool small_plan(const TilePlan& p) {
+  return p.wave_host != nullptr && p.mfma_tiles == 0 &&
+         (int64_t)p.wave_tiles * LORA_PLAN_WAVE_WORDS <= kSmallPlanWords;
+}
+
+static PlanArg<kArg> small_arg(const TilePlan& p) {
+  PlanArg<kArg> a;
+  const int n = p.wave_tiles * LORA_PLAN_WAVE_WORDS;
+  for (int i = 0; i < kSmallPlanWords; ++i) a.w[i] = i < n ? p.wave_host[i] : -1;
+  return a;
+}
+
 int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, const TilePlan& p,
                         hipStream_t st) {
   const bool bf = g.dtype == LORA_BF16;
   if (p.mfma_tiles > 0 && !bf) return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
   RowList Lw, Lm;
   plan_lists(p, Lw, Lm);
+  if (small_plan(p)) {
+    const PlanArg<kArg> a = small_arg(p);
+    return bf ? launch_shrink_wave<uint16_t, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a)
+              : launch_shrink_wave<float, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a);
+  }
   if (int32_t e = launch_shrink_mfma<kList>(g, x, A, v, Lm, p.mfma_tiles, st)) return e;
   return bf ? launch_shrink_wave<uint16_t, kList>(g, x, A, v, Lw, p.wave_tiles, st)
             : launch_shrink_wave<float, kList>(g, x, A, v, Lw, p.wave_tiles, st);
@@ -954,6 +993,11 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
   if (p.mfma_tiles > 0 && !bf) return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
   RowList Lw, Lm;
   plan_lists(p, Lw, Lm);
+  if (small_plan(p)) {
+    const PlanArg<kArg> a = small_arg(p);
+    return bf ? launch_expand_wave<uint16_t, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a)
+              : launch_expand_wave<float, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a);
+  }
   if (int32_t e = launch_expand_mfma<kList>(g, v, B, y, Lm, p.mfma_tiles, st)) return e;
   return bf ? launch_expand_wave<uint16_t, kList>(g, v, B, y, Lw, p.wave_tiles, st)
             : launch_expand_wave<float, kList>(g, v, B, y, Lw, p.wave_tiles, st);

@@ -323,3 +323,30 @@ def test_plan_reused_across_layers(dtype):
         L.lora_plan_expand(pool.desc, v, pool.B, yd, wl.T, plan, image)
         torch.cuda.synchronize()
         check_rows(lw, yd, label=f"plan layer {i} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_plan_by_value(dtype):
+    """A decode plan of at most 32 wavefront tiles travels in the kernel
+    arguments (host image given, device image NULL): same bits as the
+    device-image path, within tolerance of the oracle."""
+    import torch
+    wl = W.config_bgmv_decode(seed=8, T=64, K=520, O=264, n_adapters=6, rank=16,
+                              dtype=dtype)
+    pool = make_pool(wl)
+    plan, img, views = L.lora_apply_plan(pool.desc, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] == 0 and 0 < plan["wave_tiles"] <= 32
+    image = torch.from_numpy(img).cuda()
+    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
+    outs = []
+    for by_value in (True, False):
+        xd, yd = to_dev(wl.x, dtype), to_dev(wl.y_in, dtype)
+        v = torch.full((rows, pool.R), float("nan"), dtype=torch.float32, device="cuda")
+        dev_img = None if by_value else image
+        host_img = img if by_value else None
+        L.lora_plan_shrink(pool.desc, xd, pool.A, v, wl.T, plan, dev_img, host_img)
+        L.lora_plan_expand(pool.desc, v, pool.B, yd, wl.T, plan, dev_img, host_img)
+        torch.cuda.synchronize()
+        check_rows(wl, yd, label=f"small plan by_value={by_value} {dtype}")
+        outs.append(yd.clone())
+    assert torch.equal(_bits(outs[0]), _bits(outs[1]))

@@ -121,7 +121,7 @@ def test_plan_entry_validation_before_hip():
 
     def status(fn, plan, image=FAKE, T=6, desc=d):
         try:
-            fn(desc, FAKE, FAKE, FAKE, T, plan, image, 0)
+            fn(desc, FAKE, FAKE, FAKE, T, plan, image, None, 0)
             return 0
         except L.LoraError as e:
             return e.status
