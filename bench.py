@@ -133,7 +133,8 @@ class Setup:
         self.image_host = np.ascontiguousarray(img if img.size else np.zeros(4, np.int32))
         rows = self.plan_d["num_sgmv_rows"] + self.plan_d["num_bgmv_rows"]
         S, R = wl.num_slices, wl.max_lora_rank
-        self.v = torch.zeros((max(rows, 1), S * R), dtype=torch.float32, device="cuda")
+        self.v = torch.zeros((self.plan_d["ksplit"] * max(rows, 1), S * R), dtype=torch.float32,
+                             device="cuda")
         self.bytes_per_rep = per
         torch.cuda.synchronize()
 

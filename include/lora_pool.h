@@ -223,7 +223,9 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
 
 /* Rows per wavefront-path tile and per MFMA tile of a plan. */
 #define LORA_PLAN_WAVE_ROWS 8
-#define LORA_PLAN_MFMA_ROWS 32
+#define LORA_PLAN_MFMA_ROWS 64
+/* most partial sums the MFMA shrink splits K into */
+#define LORA_PLAN_MAX_KSPLIT 4
 /* int32 words per tile record of a plan */
 #define LORA_PLAN_WAVE_WORDS 16
 #define LORA_PLAN_MFMA_WORDS 4
@@ -243,7 +245,12 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
  *   perm [num_sgmv_rows]              token of each SGMV row
  *   wave [wave_tiles][16]             slot, rows, first v row, 0, token of
  *                                     each row (-1 past the last row), -1 ...
- *   mfma [mfma_tiles][4]              slot, rows, first v row, 0          */
+ *   mfma [mfma_tiles][4]              slot, rows, first v row, 0
+ *
+ * ksplit: the MFMA shrink splits K into this many contiguous ranges and writes
+ * one partial of v per range (the MFMA expand sums them in order 0, 1, ...);
+ * the plan picks it so that the MFMA launches fill the GPU.  Wavefront rows
+ * have a single partial (index 0). */
 typedef struct {
   int32_t num_sgmv_rows;
   int32_t num_bgmv_rows;
@@ -251,6 +258,8 @@ typedef struct {
   int32_t wave_tiles;
   int32_t mfma_tiles;
   int32_t mfma_min_rows;   /* INT32_MAX when no segment uses MFMA tiles */
+  int32_t ksplit;          /* in [1, LORA_PLAN_MAX_KSPLIT] */
+  int32_t reserved;
   int64_t image_offset;    /* bytes from meta_host to the device image (16-byte aligned) */
   int64_t image_bytes;
   int64_t off_perm;        /* int32 offsets inside the image */
@@ -276,8 +285,9 @@ int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* id
  *               meta_host), or NULL.  A small plan (no MFMA tiles, at most 32
  *               wavefront tiles) with a host copy travels in the kernel
  *               arguments and `image` is not read; otherwise `image` is used.
- *   v:          device fp32 [num_sgmv_rows + num_bgmv_rows][S][R] (plan row
- *               order).
+ *   v:          device fp32 [ksplit][num_sgmv_rows + num_bgmv_rows][S][R]
+ *               (plan row order; partial p of row i at
+ *               ((p * rows + i) * S + s) * R + k).
  *   lora_plan_shrink:  v[row][s][k] = sum_j A_pool[a][s][k][j] * x[t][j] for
  *                      every row of every tile ([TGI] step 4, shrink)
  *   lora_plan_expand:  y[t][off_s + j] = round_dtype((float)y[t][off_s + j] +

@@ -65,13 +65,15 @@ class lora_plan(ctypes.Structure):
     _fields_ = [("num_sgmv_rows", ctypes.c_int32), ("num_bgmv_rows", ctypes.c_int32),
                 ("num_segs", ctypes.c_int32), ("wave_tiles", ctypes.c_int32),
                 ("mfma_tiles", ctypes.c_int32), ("mfma_min_rows", ctypes.c_int32),
+                ("ksplit", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("image_offset", ctypes.c_int64), ("image_bytes", ctypes.c_int64),
                 ("off_perm", ctypes.c_int64), ("off_wave", ctypes.c_int64),
                 ("off_mfma", ctypes.c_int64)]
 
 
 PLAN_WAVE_ROWS = 8
-PLAN_MFMA_ROWS = 32
+PLAN_MFMA_ROWS = 64
+PLAN_MAX_KSPLIT = 4
 PLAN_WAVE_WORDS = 16
 PLAN_MFMA_WORDS = 4
 

@@ -72,6 +72,9 @@ int32_t sgmv_args(const int32_t* perm, const int32_t* seg_starts, const int32_t*
 int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const void* image_host,
                   TilePlan* tp) {
   if (!p) return fail(LORA_E_ARG, "plan is NULL");
+  if (p->ksplit < 1 || p->ksplit > LORA_PLAN_MAX_KSPLIT)
+    return fail(LORA_E_ARG, "malformed plan (ksplit %d outside [1, %d])", p->ksplit,
+                LORA_PLAN_MAX_KSPLIT);
   if (p->num_sgmv_rows < 0 || p->num_bgmv_rows < 0 || p->wave_tiles < 0 || p->mfma_tiles < 0 ||
       p->off_perm < 0 || p->off_wave < 0 || p->off_mfma < 0 || p->image_bytes < 0)
     return fail(LORA_E_ARG, "malformed plan (negative count or offset)");
@@ -95,7 +98,7 @@ int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const voi
   const int32_t* img = (const int32_t*)image;
   *tp = TilePlan{img ? img + p->off_perm : nullptr, img ? img + p->off_wave : nullptr,
                  p->wave_tiles, img ? img + p->off_mfma : nullptr, p->mfma_tiles,
-                 host ? host + p->off_wave : nullptr, p->num_sgmv_rows,
+                 host ? host + p->off_wave : nullptr, p->ksplit, p->num_sgmv_rows,
                  p->num_sgmv_rows + p->num_bgmv_rows};
   return LORA_OK;
 }
@@ -280,7 +283,7 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
   if (int32_t e = need_ptr(ws, "ws")) return e;
   const StageLayout sl = stage_layout(T, g.max_loras);
   const int64_t v_off = align_up(sl.image_max_words * 4, 256);
-  const int64_t need_ws = v_off + (int64_t)T * g.S * g.R * 4;
+  const int64_t need_ws = v_off + (int64_t)LORA_PLAN_MAX_KSPLIT * T * g.S * g.R * 4;
   if (ws_bytes < need_ws)
     return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
                 (long long)need_ws);

@@ -225,6 +225,16 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
     }
   }
   const int64_t words = off_mfma + nm * LORA_PLAN_MFMA_WORDS;
+  // K split of the MFMA shrink: double it while the launch has fewer than two
+  // workgroups per compute unit (256 CUs) and every split keeps at least four
+  // 64-wide K steps
+  int32_t ksplit = 1;
+  if (nm > 0) {
+    const int64_t wgs = nm * g.S * ((g.R + 63) / 64);
+    const int64_t ksteps = (g.K + 63) / 64;
+    while (ksplit < LORA_PLAN_MAX_KSPLIT && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4)
+      ksplit *= 2;
+  }
   if (words > sl.image_max_words)  // cannot happen: the bounds above hold for any batch
     return fail(LORA_E_WORKSPACE, "tile plan overflow (%lld words > %lld)", (long long)words,
                 (long long)sl.image_max_words);
@@ -234,6 +244,8 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   p->wave_tiles = (int32_t)nw;
   p->mfma_tiles = (int32_t)nm;
   p->mfma_min_rows = thr;
+  p->ksplit = ksplit;
+  p->reserved = 0;
   p->image_offset = sl.image * 4;
   p->image_bytes = words * 4;
   p->off_perm = 0;
@@ -315,7 +327,7 @@ int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T) {
   if (st) return st;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
   const int64_t img = align_up(stage_layout(T, g.max_loras).image_max_words * 4, 256);
-  return img + (int64_t)T * g.S * g.R * 4;
+  return img + (int64_t)LORA_PLAN_MAX_KSPLIT * T * g.S * g.R * 4;
 }
 
 int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* ids_host,

@@ -18,6 +18,7 @@ constexpr int kMfmaTileRows = LORA_PLAN_MFMA_ROWS;  // rows per tile of the MFMA
 constexpr int kExpandCols = 256;       // output columns per VALU expand workgroup
 constexpr int kExpandMfmaCols = 128;   // output columns per MFMA expand workgroup
 constexpr int kSmallPlanWords = 512;   // plans up to 32 wavefront tiles go by value (2 KB)
+constexpr int kMaxKsplit = LORA_PLAN_MAX_KSPLIT;  // K splits of the MFMA shrink
 
 // A list of rows to process.  Row i reads token tok[i] of x / y and writes row i
 // of v.  Three ways to cut it into tiles, one adapter per tile:
@@ -65,6 +66,7 @@ struct TilePlan {
   const int32_t* mfma;
   int32_t mfma_tiles;
   const int32_t* wave_host;  // host copy of the wave records, or nullptr
+  int32_t ksplit;            // partials of the MFMA shrink (v holds ksplit x num_rows rows)
   int32_t num_sgmv_rows;  // rows of perm; MFMA tiles lie inside them
   int32_t num_rows;       // v rows: SGMV rows + BGMV rows
 };

@@ -42,6 +42,7 @@
 namespace lora {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -55,6 +56,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// All-ones or all-zeros, to zero a loaded value with a bit-AND: a select on a
+// loaded value lets the compiler sink the load under a branch, after which it
+// has to drain every outstanding load before continuing.
+__device__ __forceinline__ uint32_t all_or_none(bool b) { return b ? 0xffffffffu : 0u; }
 
 // Element access: 8 consecutive elements travel as one Raw (16 bytes of bf16
 // or 32 bytes of fp32) and are widened to fp32 only where they are used.
@@ -566,113 +572,168 @@ __device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int&
 
 // ------------------------------------------------------------ shrink (MFMA)
 //
-// bf16 only.  grid.x = tiles(32 rows) * S, grid.y = rank blocks of 64.
-// Wave (wm, wr) computes rows 16*wm .. +16 of the tile against ranks
-// 32*wr .. +32 of the block (two 16-rank MFMA tiles), over the whole K range in
-// steps of 128.  Per step each lane loads 64 bytes of its x row and 64 bytes of
-// each of its two adapter rows; MFMA p covers k in [k0 + 32p, k0 + 32p + 32),
-// lane group g = lane / 16 holding k0 + 32p + 8g .. +8 of both operands.
-// Loads run three steps ahead of the MFMAs (register ring), which is what
-// keeps HBM busy when only about one workgroup per CU exists.  Ranks >= R are
-// masked (no load, no store), so any R that is a multiple of 8 is accepted.
+// bf16 only.  grid.x = tiles * S * ksplit, grid.y = ceil(R / 64).  A workgroup
+// computes the 64 rows of its tile against ranks 64 * blockIdx.y .. +64 over the
+// K range of its split (a contiguous run of 64-wide K steps) and writes partial
+// `part` of v:  v[(part * v_rows + row) * S * R + s * R + rank].
+// Per K step the x tile [64 rows][64 k] and the adapter tile [64 ranks][64 k]
+// move HBM -> registers -> LDS with coalesced 16-byte loads (8 lanes per
+// 128-byte row piece); loads run two steps ahead and LDS is double-buffered,
+// with one barrier per step.  Wave (wm, wr) multiplies rows 32 wm .. +32 by
+// ranks 32 wr .. +32 as 2 x 2 MFMA tiles of 16 x 16, two k-chunks of 32 per
+// step; fragments are 16-byte LDS reads (rows padded to 144 bytes).
 template <int MODE>
 __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ A,
                                                           float* __restrict__ v, RowList L,
-                                                          Geo g) {
-  constexpr int TMR = kMfmaTileRows;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int f = bid / g.S;
-  const int s = bid - f * g.S;
-  int r0, cnt, sid;
-  if (!mfma_tile<TMR, MODE>(L, f, r0, cnt, sid)) return;
-  if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+                                                          Geo g, int ksplit, int v_rows) {
+  constexpr int TM = kMfmaTileRows, NR = 64, KS = 64, LDS_ROW = KS + 8;
+  static_assert(TM == 64, "staging covers 64 rows");
+  __shared__ __align__(16) uint16_t xs[2][TM * LDS_ROW];
+  __shared__ __align__(16) uint16_t as[2][NR * LDS_ROW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wr = wave >> 1;
   const int i16 = lane & 15, grp = lane >> 4;
-  const int row = 16 * wm + i16;  // x-operand row of this lane
-  int t = -1;
-  if (row < cnt) t = L.tok[r0 + row];
-  const bool xrow_ok = t >= 0 && t < g.T;
-  const uint16_t* xr = x + (size_t)(xrow_ok ? t : 0) * g.K;
-  const int rbase = blockIdx.y * 64 + 32 * wr;  // first rank of this wave
-  const bool rk_ok0 = rbase + i16 < g.R, rk_ok1 = rbase + 16 + i16 < g.R;
-  const uint16_t* A0 =
-      A + ((size_t)(sid * g.S + s) * g.R + (rk_ok0 ? rbase + i16 : 0)) * g.K;
-  const uint16_t* A1 =
-      A + ((size_t)(sid * g.S + s) * g.R + (rk_ok1 ? rbase + 16 + i16 : 0)) * g.K;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_tile = g.S * ksplit;
+  const int f = bid / per_tile;
+  const int rem = bid - f * per_tile;
+  const int s = rem / ksplit;
+  const int part = rem - s * ksplit;
+  int r0, cnt, sid;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid)) return;
+  if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
+  const int rank0 = blockIdx.y * NR;
+  // K steps of this split
+  const int nsteps = (g.K + KS - 1) / KS;
+  const int per = (nsteps + ksplit - 1) / ksplit;
+  const int st0 = min(nsteps, part * per), st1 = min(nsteps, st0 + per);
 
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  u32x4 xs[3][4], as0[3][4], as1[3][4];
-  // masks instead of selects: a select on a loaded value lets the compiler
-  // sink the load into a branch, which serialises the pipeline
-  const uint32_t xmask = xrow_ok ? 0xffffffffu : 0u;
-  const uint32_t amask0 = rk_ok0 ? 0xffffffffu : 0u, amask1 = rk_ok1 ? 0xffffffffu : 0u;
-  // loads are unconditional (clamped address, value masked afterwards) so the
-  // compiler can keep several steps in flight with exact wait counts
-  auto load_step = [&](int k0, u32x4(&xf)[4], u32x4(&a0)[4], u32x4(&a1)[4]) {
+  // staging: thread t carries 16 bytes at k = 8 (t % 8) of rows / ranks t / 8
+  // and t / 8 + 32
+  const int c8 = tid & 7, srow = tid >> 3;
+  const uint16_t* xp[2];
+  const uint16_t* ap[2];
+  uint32_t xm[2], am[2];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int kp = k0 + 32 * p + 8 * grp;
-      const bool in = kp < g.K;
-      const int kc = in ? kp : 0;
-      const uint32_t kin = in ? 0xffffffffu : 0u;
-      xf[p] = ld16(xr + kc) & (kin & xmask);
-      a0[p] = ld16(A0 + kc) & (kin & amask0);
-      a1[p] = ld16(A1 + kc) & (kin & amask1);
-    }
-  };
-  auto mma_step = [&](const u32x4(&xf)[4], const u32x4(&a0)[4], const u32x4(&a1)[4]) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const bf16x8 xa = __builtin_bit_cast(bf16x8, xf[p]);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, a0[p]), acc0,
-                                                     0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, a1[p]), acc1,
-                                                     0, 0, 0);
-    }
-  };
-  const int nsteps = (g.K + 127) / 128;
-  load_step(0, xs[0], as0[0], as1[0]);
-  load_step(128, xs[1], as0[1], as1[1]);
-  for (int i = 0; i < nsteps; i += 3) {
-    load_step((i + 2) * 128, xs[2], as0[2], as1[2]);
-    mma_step(xs[0], as0[0], as1[0]);
-    if (i + 1 >= nsteps) break;
-    load_step((i + 3) * 128, xs[0], as0[0], as1[0]);
-    mma_step(xs[1], as0[1], as1[1]);
-    if (i + 2 >= nsteps) break;
-    load_step((i + 4) * 128, xs[1], as0[1], as1[1]);
-    mma_step(xs[2], as0[2], as1[2]);
+  for (int j = 0; j < 2; ++j) {
+    const int r = srow + 32 * j;
+    const int tk = L.tok[r0 + min(r, cnt - 1)];
+    const bool ok = r < cnt && tk >= 0 && tk < g.T;
+    xp[j] = x + (size_t)(ok ? tk : 0) * g.K;
+    xm[j] = all_or_none(ok);
+    const int rk = rank0 + r;
+    const bool rok = rk < g.R;
+    ap[j] = A + ((size_t)(sid * g.S + s) * g.R + (rok ? rk : 0)) * g.K;
+    am[j] = all_or_none(rok);
   }
-  // D layout: lane holds rows 4*grp + j (j < 4) of column i16
-  const int SR = g.S * g.R;
+  // loads of K step `st` (a step at or past the K range reads clamped
+  // addresses and is zeroed)
+  auto gload = [&](int st, u32x4(&r)[4]) {
+    const int kk = st * KS + 8 * c8;
+    const bool in = kk < g.K;
+    const int kc = in ? kk : 0;
+    const uint32_t km = all_or_none(in);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int orow = 16 * wm + 4 * grp + j;
-    const bool ok = __shfl(xrow_ok ? 1 : 0, 4 * grp + j, 16) != 0;  // row's token is valid
-    if (!ok || orow >= cnt) continue;
-    float* vr = v + (size_t)(r0 + orow) * SR + s * g.R;
-    if (rk_ok0) vr[rbase + i16] = acc0[j];
-    if (rk_ok1) vr[rbase + 16 + i16] = acc1[j];
+    for (int j = 0; j < 2; ++j) r[j] = ld16(xp[j] + kc) & (km & xm[j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r[2 + j] = ld16(ap[j] + kc) & (km & am[j]);
+  };
+  auto lstore = [&](int b, const u32x4(&r)[4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<u32x4*>(&xs[b][(srow + 32 * j) * LDS_ROW + 8 * c8]) = r[j];
+      *reinterpret_cast<u32x4*>(&as[b][(srow + 32 * j) * LDS_ROW + 8 * c8]) = r[2 + j];
+    }
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](int b) {
+#pragma unroll
+    for (int kc = 0; kc < KS; kc += 32) {
+      bf16x8 xa[2], ab[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        xa[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                &xs[b][(32 * wm + 16 * mt + i16) * LDS_ROW + kc + 8 * grp]));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        ab[nt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                &as[b][(32 * wr + 16 * nt + i16) * LDS_ROW + kc + 8 * grp]));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], ab[nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+  u32x4 ra[4], rb[4];
+  gload(st0, ra);
+  gload(st0 + 1, rb);
+  for (int st = st0; st < st1; st += 2) {
+    lstore(0, ra);
+    gload(st + 2, ra);
+    __syncthreads();
+    mma(0);
+    if (st + 1 >= st1) break;
+    lstore(1, rb);
+    gload(st + 3, rb);
+    __syncthreads();
+    mma(1);
+  }
+  // D layout: lane (grp, i16) holds rows 4 grp + j (j < 4) of rank column i16
+  const int SR = g.S * g.R;
+  float* vp = v + ((size_t)part * v_rows + r0) * SR + s * g.R;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int rk = rank0 + 32 * wr + 16 * nt + i16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 32 * wm + 16 * mt + 4 * grp + j;
+        if (row < cnt && rk < g.R) vp[(size_t)row * SR + rk] = acc[mt][nt][j];
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------ expand (MFMA)
 //
-// bf16 only.  grid.x = tiles(32 rows) * column chunks of 128 (one slice each).
-// Wave (wt, wc): tokens 16*wt .. +16, columns 64*wc .. +64 of the chunk, as two
-// pairs of 16-column MFMA tiles.  The MFMA computes D = Bt * v^T (rows = output
-// columns, columns = tokens).  Inside a pair, MFMA row n of tile 2q maps to
-// column 32q + 8(n/4) + n%4 and of tile 2q+1 to the same + 4, so lane (g, m)
-// ends with columns 32q + 8g .. +8 of token m: one 16-byte y access.
+// bf16 only.  grid.x = tiles * column chunks of 128 (one slice each).  The
+// workgroup's y tile [64 tokens][128 columns] and, per pass of 64 ranks, the B
+// tile [128 columns][64 ranks] (contiguous in the pool) and the v tile
+// [64 rows][64 ranks] are staged in LDS with coalesced 16-byte loads, all of a
+// pass issued before any LDS store.  v is the sum of the shrink's ksplit
+// partials, split into hi = rne_bf16(v) and lo = rne_bf16(v - hi), which keeps
+// about 16 mantissa bits of the fp32 intermediate.  Wave w computes
+// D = Btile * v^T for tokens 16 w .. +16: eight 16 x 16 tiles, two MFMAs (hi,
+// lo) per tile and 32-rank chunk.  Inside a pair of tiles, MFMA row n of tile
+// 2q maps to column 32 q + 8 (n / 4) + n % 4 and of tile 2q+1 to the same + 4,
+// so lane (g, m) ends with columns 32 q + 8 g .. +8 of token m and updates
+// them in LDS with one 16-byte read and write; the tile then leaves with
+// coalesced 16-byte stores (16 lanes per 256-byte row piece).
 template <int MODE>
 __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restrict__ v,
                                                           const uint16_t* __restrict__ B,
                                                           uint16_t* __restrict__ y, RowList L,
-                                                          Geo g, Chunks ch) {
-  constexpr int TMR = kMfmaTileRows;
+                                                          Geo g, Chunks ch, int ksplit,
+                                                          int v_rows) {
+  constexpr int TM = kMfmaTileRows, NC = kExpandMfmaCols, KB = 64;
+  constexpr int LDK = KB + 8, LDY = NC + 8;
+  static_assert(TM == 64 && NC == 128, "staging covers 64 tokens x 128 columns");
+  __shared__ __align__(16) uint16_t bs[NC * LDK];
+  __shared__ __align__(16) uint16_t vh[TM * LDK];
+  __shared__ __align__(16) uint16_t vl[TM * LDK];
+  __shared__ __align__(16) uint16_t ys[TM * LDY];
+  __shared__ int s_tok[TM];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int m16 = lane & 15, grp = lane >> 4;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / ch.total;
   const int cidx = bid - f * ch.total;
@@ -680,105 +741,125 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
 #pragma unroll
   for (int i = 1; i < LORA_MAX_SLICES; ++i)
     if (i < g.S && cidx >= ch.start[i]) s = i;
-  const int col0 = (cidx - ch.start[s]) * kExpandMfmaCols;
+  const int col0 = (cidx - ch.start[s]) * NC;
+  const int out_s = g.out[s];
   int r0, cnt, sid;
-  if (!mfma_tile<TMR, MODE>(L, f, r0, cnt, sid)) return;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wt = wave & 1, wc = wave >> 1;
-  const int m16 = lane & 15, grp = lane >> 4;
   const int R = g.R;
   const int SR = g.S * R;
-  const int out_s = g.out[s];
-
-  // B-operand token of this lane (column m16 of the MFMA)
-  const int trow = 16 * wt + m16;
-  int t = -1;
-  if (trow < cnt) t = L.tok[r0 + trow];
-  const bool tok_ok = t >= 0 && t < g.T;
-  const float* vr = v + (size_t)(r0 + (trow < cnt ? trow : 0)) * SR + s * R;
-
-  // A-operand rows: output columns of this lane for each of the 4 tiles
-  const int cbase = col0 + 64 * wc;
-  const uint16_t* Bb = B + ((size_t)sid * g.O + g.off[s]) * R;
-  int ccol[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int q = nt >> 1, hi = nt & 1;
-    ccol[nt] = cbase + 32 * q + 8 * (m16 >> 2) + 4 * hi + (m16 & 3);
+  if (tid < TM) {
+    const int tk = L.tok[r0 + min(tid, cnt - 1)];
+    s_tok[tid] = (tid < cnt && tk >= 0 && tk < g.T) ? tk : -1;
   }
-
-  // y words of this lane (issued before the MFMA loop so the latency overlaps)
-  uint16_t* yr = y + (size_t)(tok_ok ? t : 0) * g.O + g.off[s];
-  u32x4 yw[2];
+  __syncthreads();
+  // y / v staging: row (t / 16) + 16 j; y columns col0 + 8 (t % 16) .. +8,
+  // v ranks 4 (t % 16) .. +4 of the pass
+  const int q16 = tid & 15, srow = tid >> 4;
+  const int ycol = col0 + 8 * q16;
+  const bool ycol_ok = ycol < out_s;
+  u32x4 yr[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = cbase + 32 * q + 8 * grp;
-    yw[q] = ld16(yr + (c < out_s ? c : 0));
+  for (int j = 0; j < 4; ++j) {
+    const int tk = s_tok[srow + 16 * j];
+    yr[j] = ld16(y + (size_t)(tk >= 0 ? tk : 0) * g.O + g.off[s] + (ycol_ok ? ycol : 0));
   }
-
-  // validity as bit masks (a select on a loaded value lets the compiler sink
-  // the load into a branch and serialise the loop)
-  const uint32_t tmask = tok_ok ? 0xffffffffu : 0u;
-  uint32_t cmask[4];
+  f32x4 acc[8];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) cmask[nt] = ccol[nt] < out_s ? 0xffffffffu : 0u;
-
-  f32x4 acc[4];
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* Bt = B + ((size_t)sid * g.O + g.off[s] + col0) * R;
+  // B staging: column (t / 8) + 32 j, ranks 8 (t % 8) .. +8 of the pass
+  const int b8 = tid & 7, bcol = tid >> 3;
+  for (int kb0 = 0; kb0 < R; kb0 += KB) {
+    const int kw = min(KB, R - kb0);  // multiple of 8
+    u32x4 vr[4][kMaxKsplit];
+    const bool vk_ok = 4 * q16 < kw;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = 0; kb < R; kb += 32) {
-    const int kk = kb + 8 * grp;
-    const bool kin = kk < R;
-    // v (fp32) -> hi + lo bf16
-    u32x4 vh, vl;
-    u32x4 bw[4];
-    {
-      const int kc = kin ? kk : 0;
-      const uint32_t kmask = kin ? 0xffffffffu : 0u;
-      const u32x4 a = ld16(vr + kc) & (kmask & tmask);
-      const u32x4 b = ld16(vr + kc + 4) & (kmask & tmask);
+    for (int j = 0; j < 4; ++j) {
+      const int row = srow + 16 * j;
+      const bool ok = vk_ok && s_tok[row] >= 0;
+      const uint32_t m = all_or_none(ok);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        bw[nt] = ld16(Bb + (size_t)(ccol[nt] < out_s ? ccol[nt] : 0) * R + kc) & (kmask & cmask[nt]);
-      const float e[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
-                          __uint_as_float(a.w), __uint_as_float(b.x), __uint_as_float(b.y),
-                          __uint_as_float(b.z), __uint_as_float(b.w)};
-      uint32_t h[8], l[8];
+      for (int p = 0; p < kMaxKsplit; ++p) {
+        const bool pin = p < ksplit;
+        const size_t off = ((size_t)(pin ? p : 0) * v_rows + r0 + (ok ? row : 0)) * SR + s * R +
+                           kb0 + (ok ? 4 * q16 : 0);
+        vr[j][p] = ld16(v + off) & (m & all_or_none(pin));
+      }
+    }
+    u32x4 br[4];
+    const bool bk_ok = 8 * b8 < kw;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < 4; ++j) {
+      const int c = bcol + 32 * j;
+      const bool ok = bk_ok && col0 + c < out_s;
+      br[j] = ld16(Bt + (size_t)(ok ? c : 0) * R + kb0 + (ok ? 8 * b8 : 0)) & all_or_none(ok);
+    }
+    if (kb0 > 0) __syncthreads();  // MFMA readers of the previous pass are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(&bs[(bcol + 32 * j) * LDK + 8 * b8]) = br[j];
+      float e[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < kMaxKsplit; ++p) {  // fixed order: partial 0, 1, ...
+        e[0] += __uint_as_float(vr[j][p].x);
+        e[1] += __uint_as_float(vr[j][p].y);
+        e[2] += __uint_as_float(vr[j][p].z);
+        e[3] += __uint_as_float(vr[j][p].w);
+      }
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         h[i] = f32_to_bf16_bits(e[i]);
         l[i] = f32_to_bf16_bits(e[i] - __uint_as_float(h[i] << 16));
       }
-      vh = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-      vl = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+      const int vo = (srow + 16 * j) * LDK + 4 * q16;
+      *reinterpret_cast<u32x2*>(&vh[vo]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<u32x2*>(&vl[vo]) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      if (kb0 == 0) *reinterpret_cast<u32x4*>(&ys[(srow + 16 * j) * LDY + 8 * q16]) = yr[j];
     }
-    const bf16x8 bh = __builtin_bit_cast(bf16x8, vh);
-    const bf16x8 bl = __builtin_bit_cast(bf16x8, vl);
+    __syncthreads();
+    for (int kk = 0; kk < kw; kk += 32) {
+      const int vo = (16 * wave + m16) * LDK + kk + 8 * grp;
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vh[vo]));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vl[vo]));
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const bf16x8 ba = __builtin_bit_cast(bf16x8, bw[nt]);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bh, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bl, acc[nt], 0, 0, 0);
+      for (int nt = 0; nt < 8; ++nt) {
+        const int q = nt >> 1, hi = nt & 1;
+        const int crow = 32 * q + 8 * (m16 >> 2) + 4 * hi + (m16 & 3);
+        const bf16x8 ba = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&bs[crow * LDK + kk + 8 * grp]));
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bh, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bl, acc[nt], 0, 0, 0);
+      }
     }
   }
-  if (!tok_ok) return;
+  // y update in LDS: lane (grp, m16) owns token row 16 wave + m16, columns
+  // 32 q + 8 grp .. +8 of pair q
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = cbase + 32 * q + 8 * grp;
-    if (c >= out_s) continue;
+  for (int q = 0; q < 4; ++q) {
+    uint16_t* yp = &ys[(16 * wave + m16) * LDY + 32 * q + 8 * grp];
+    const u32x4 w = *reinterpret_cast<const u32x4*>(yp);
     const f32x4 d0 = acc[2 * q], d1 = acc[2 * q + 1];
     const float add[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-    uint32_t w[4] = {yw[q].x, yw[q].y, yw[q].z, yw[q].w};
+    const uint32_t wi[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float lo = __uint_as_float(w[i] << 16) + add[2 * i];
-      const float hi = __uint_as_float(w[i] & 0xffff0000u) + add[2 * i + 1];
-      w[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+      const float lo = __uint_as_float(wi[i] << 16) + add[2 * i];
+      const float hi = __uint_as_float(wi[i] & 0xffff0000u) + add[2 * i + 1];
+      o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
     }
-    *reinterpret_cast<u32x4*>(yr + c) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(yp) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = srow + 16 * j;
+    const int tk = s_tok[row];
+    if (tk >= 0 && ycol_ok)
+      *reinterpret_cast<u32x4*>(y + (size_t)tk * g.O + g.off[s] + ycol) =
+          *reinterpret_cast<const u32x4*>(&ys[row * LDY + 8 * q16]);
   }
 }
 
@@ -880,23 +961,27 @@ static int32_t launch_expand_wave(const Geo& g, const float* v, const void* B, v
 
 template <int MODE>
 static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, float* v,
-                                  const RowList& L, int64_t tiles, hipStream_t st) {
+                                  const RowList& L, int64_t tiles, int ksplit, int v_rows,
+                                  hipStream_t st) {
   if (tiles <= 0) return LORA_OK;
-  if (tiles * g.S > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
+  if (ksplit < 1 || ksplit > kMaxKsplit) return fail(LORA_E_ARG, "bad K split %d", ksplit);
+  if (tiles * g.S * ksplit > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
   const unsigned gy = (unsigned)((g.R + 63) / 64);
-  hipLaunchKernelGGL(shrink_mfma_kernel<MODE>, dim3(grid_of(tiles * g.S), gy), dim3(256), 0, st,
-                     (const uint16_t*)x, (const uint16_t*)A, v, L, g);
+  hipLaunchKernelGGL(shrink_mfma_kernel<MODE>, dim3(grid_of(tiles * g.S * ksplit), gy), dim3(256),
+                     0, st, (const uint16_t*)x, (const uint16_t*)A, v, L, g, ksplit, v_rows);
   return hip_check("shrink_mfma launch");
 }
 
 template <int MODE>
 static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, void* y,
-                                  const RowList& L, int64_t tiles, hipStream_t st) {
+                                  const RowList& L, int64_t tiles, int ksplit, int v_rows,
+                                  hipStream_t st) {
   if (tiles <= 0) return LORA_OK;
+  if (ksplit < 1 || ksplit > kMaxKsplit) return fail(LORA_E_ARG, "bad K split %d", ksplit);
   const Chunks ch = make_chunks(g, kExpandMfmaCols);
   if (tiles * ch.total > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
   hipLaunchKernelGGL(expand_mfma_kernel<MODE>, dim3(grid_of(tiles * ch.total)), dim3(256), 0, st,
-                     v, (const uint16_t*)B, (uint16_t*)y, L, g, ch);
+                     v, (const uint16_t*)B, (uint16_t*)y, L, g, ch, ksplit, v_rows);
   return hip_check("expand_mfma launch");
 }
 
@@ -917,7 +1002,8 @@ int32_t run_shrink(const Geo& g, const void* x, const void* A, float* v, RowList
   Lw.seg_min = 0;
   Lw.seg_max = thr - 1;
   if (thr != INT32_MAX) {
-    if (int32_t e = launch_shrink_mfma<kSegs>(g, x, A, v, Lm, count_tiles(Lm, kMfmaTileRows), st))
+    if (int32_t e = launch_shrink_mfma<kSegs>(g, x, A, v, Lm, count_tiles(Lm, kMfmaTileRows), 1,
+                                              L.num_rows, st))
       return e;
   }
   const int64_t tw = count_tiles(Lw, kWaveTileRows);
@@ -942,7 +1028,8 @@ int32_t run_expand(const Geo& g, const float* v, const void* B, void* y, RowList
   Lw.seg_min = 0;
   Lw.seg_max = thr - 1;
   if (thr != INT32_MAX) {
-    if (int32_t e = launch_expand_mfma<kSegs>(g, v, B, y, Lm, count_tiles(Lm, kMfmaTileRows), st))
+    if (int32_t e = launch_expand_mfma<kSegs>(g, v, B, y, Lm, count_tiles(Lm, kMfmaTileRows), 1,
+                                              L.num_rows, st))
       return e;
   }
   const int64_t tw = count_tiles(Lw, kWaveTileRows);
@@ -982,7 +1069,9 @@ int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, co
     return bf ? launch_shrink_wave<uint16_t, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a)
               : launch_shrink_wave<float, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a);
   }
-  if (int32_t e = launch_shrink_mfma<kList>(g, x, A, v, Lm, p.mfma_tiles, st)) return e;
+  if (int32_t e = launch_shrink_mfma<kList>(g, x, A, v, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
+                                            st))
+    return e;
   return bf ? launch_shrink_wave<uint16_t, kList>(g, x, A, v, Lw, p.wave_tiles, st)
             : launch_shrink_wave<float, kList>(g, x, A, v, Lw, p.wave_tiles, st);
 }
@@ -998,7 +1087,9 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
     return bf ? launch_expand_wave<uint16_t, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a)
               : launch_expand_wave<float, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a);
   }
-  if (int32_t e = launch_expand_mfma<kList>(g, v, B, y, Lm, p.mfma_tiles, st)) return e;
+  if (int32_t e = launch_expand_mfma<kList>(g, v, B, y, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
+                                            st))
+    return e;
   return bf ? launch_expand_wave<uint16_t, kList>(g, v, B, y, Lw, p.wave_tiles, st)
             : launch_expand_wave<float, kList>(g, v, B, y, Lw, p.wave_tiles, st);
 }

@@ -177,11 +177,12 @@ def test_apply_validation_before_hip():
     mh_need = L.lora_apply_host_meta_bytes(d, T)
     # staging: builder arrays (3T + 3 max_loras words, padded to 4), then the
     # plan image: perm (T, padded to 4), <= ceil(T/8) + 2 max_loras wave tiles
-    # of 16 words, <= ceil(T/32) + max_loras MFMA tiles of 4 words
+    # of 16 words, <= ceil(T/64) + max_loras MFMA tiles of 4 words
     up4 = lambda n: (n + 3) // 4 * 4  # noqa: E731
-    image = up4(T) + 16 * (-(-T // 8) + 2 * 4) + 4 * (-(-T // 32) + 4)
+    image = up4(T) + 16 * (-(-T // 8) + 2 * 4) + 4 * (-(-T // 64) + 4)
     assert mh_need == 4 * (up4(3 * T + 3 * 4) + image)
-    assert ws_need == ((4 * image + 255) // 256) * 256 + T * 16 * 4
+    # v: up to 4 K-split partials of T rows x S x R fp32
+    assert ws_need == ((4 * image + 255) // 256) * 256 + 4 * T * 16 * 4
     ids = np.array([0, 1, -1, 3, 2, 0], np.int32)
     meta = _aligned_i32(mh_need // 4)
     ok = [d, FAKE, FAKE, FAKE, FAKE + 64, T, ids, None, 0, FAKE, ws_need, meta, mh_need, 0]

@@ -179,12 +179,11 @@ def test_zero_B_leaves_y_unchanged():
 
 # ----------------------------------------------- exact-arithmetic invariants
 
-def _integer_workload(dtype, rslora=False, seed=0):
+def _integer_workload(dtype, rslora=False, seed=0, K=520, T=300, lens=(1, 3, 15, 16, 17, 33, 70)):
     # segment lengths chosen to hit both SGMV paths and ragged tails
     ranks = (16, 64) if rslora else (8, 16, 64, 32, 48, 64)
-    wl = W.config_integer(seed=seed, T=300, K=520, outs=(264, 136), max_loras=6,
+    wl = W.config_integer(seed=seed, T=T, K=K, outs=(264, 136), max_loras=6,
                           max_lora_rank=64, ranks=ranks, dtype=dtype, rslora=rslora)
-    lens = [1, 3, 15, 16, 17, 33, 70]
     ids = np.full(wl.T, -1, np.int32)
     pre = np.zeros(wl.T, np.uint8)
     pos = 0
@@ -205,6 +204,19 @@ def _exact_expected(wl):
 @pytest.mark.parametrize("dtype,rslora", [("bf16", False), ("f32", False), ("bf16", True)])
 def test_exact_integer_bit_identical(dtype, rslora):
     wl = _integer_workload(dtype, rslora)
+    exp = _exact_expected(wl)
+    y = run_apply(wl).float().cpu().numpy()
+    bad = np.argwhere(y != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
+def test_exact_integer_split_k():
+    """Long segments and K = 2056: the MFMA shrink splits K into four partials
+    (summed by the MFMA expand); integer inputs make the result exact."""
+    wl = _integer_workload("bf16", seed=5, K=2056, T=420, lens=(64, 65, 130, 100, 16))
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    plan, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert plan["ksplit"] == 4 and plan["mfma_tiles"] >= 5
     exp = _exact_expected(wl)
     y = run_apply(wl).float().cpu().numpy()
     bad = np.argwhere(y != exp)
@@ -311,8 +323,8 @@ def test_plan_reused_across_layers(dtype):
     assert plan["wave_tiles"] > 0
     image = torch.from_numpy(img).cuda()
     rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
-    v = torch.full((max(rows, 1), wl.num_slices * pool.R), float("nan"), dtype=torch.float32,
-                   device="cuda")
+    v = torch.full((plan["ksplit"] * max(rows, 1), wl.num_slices * pool.R), float("nan"),
+                   dtype=torch.float32, device="cuda")
     rng = np.random.default_rng(11)
     layers = [wl, dataclasses.replace(
         wl, x=W.to_dtype_values(rng.standard_normal((wl.T, wl.in_features)), dtype),

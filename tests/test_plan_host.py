@@ -8,7 +8,7 @@ import pytest
 import lora_adapter_pool_amd as L
 import workloads as W
 
-WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS = 8, 32, 16
+WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS, MAX_KSPLIT = 8, 64, 16, 4
 
 
 def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
@@ -65,6 +65,15 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
         i = j
     assert (p["wave_tiles"], p["mfma_tiles"]) == (want_wave, want_mfma)
     assert p["image_bytes"] == 4 * (p["off_mfma"] + 4 * p["mfma_tiles"])
+    # K split: doubled while the MFMA shrink has < 512 workgroups and each
+    # split keeps >= 4 steps of 64
+    want_split = 1
+    if p["mfma_tiles"]:
+        wgs = p["mfma_tiles"] * desc.num_slices * -(-R // 64)
+        ksteps = -(-desc.in_features // 64)
+        while want_split < MAX_KSPLIT and wgs * want_split < 512 and ksteps // (2 * want_split) >= 4:
+            want_split *= 2
+    assert p["ksplit"] == want_split
     assert p["image_bytes"] + p["image_offset"] <= L.lora_apply_host_meta_bytes(desc, ids.size)
     return p
 
@@ -127,7 +136,8 @@ def test_plan_entry_validation_before_hip():
             return e.status
 
     for fn in (L.lora_plan_shrink, L.lora_plan_expand):
-        for key, val in (("wave_tiles", -1), ("off_wave", -4), ("num_bgmv_rows", -2)):
+        for key, val in (("wave_tiles", -1), ("off_wave", -4), ("num_bgmv_rows", -2), ("ksplit", 0),
+                         ("ksplit", MAX_KSPLIT + 1)):
             assert status(fn, dict(p, **{key: val})) == _lib.LORA_E_ARG
         assert status(fn, dict(p, image_bytes=p["image_bytes"] - 4)) == _lib.LORA_E_ARG
         assert status(fn, p, image=FAKE + 4) == _lib.LORA_E_ALIGN
