@@ -62,6 +62,19 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 // has to drain every outstanding load before continuing.
 __device__ __forceinline__ uint32_t all_or_none(bool b) { return b ? 0xffffffffu : 0u; }
 
+// Raw buffer over `bytes` bytes at `base` (gfx9 descriptor word 3: 32-bit
+// untyped data, no swizzle).  A 16-byte store at a byte offset at or past the
+// end is dropped by the hardware, so lanes with nothing to write still issue
+// the store instruction: the compiler can then count outstanding memory
+// operations exactly across a loop instead of draining them all.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kDropOffset = 0x80000000u;  // past every buffer made by make_rsrc
+__device__ __forceinline__ void st16_buf(u32x4 val, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(val, r, (int)off, 0, 0);
+}
+
 // Element access: 8 consecutive elements travel as one Raw (16 bytes of bf16
 // or 32 bytes of fp32) and are widened to fp32 only where they are used.
 template <typename E> struct El;
@@ -863,6 +876,179 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
   }
 }
 
+// ------------------------------------------------------------ expand (MFMA, R <= 64)
+//
+// bf16, pools of rank R <= 64.  Like expand_mfma_kernel, but a workgroup covers
+// a group of up to `cpw` consecutive column chunks of one slice of its tile
+// (gr.start[s] is the first group of slice s): v (the sum of the shrink's
+// partials, as hi + lo bf16) is staged in LDS once for all of them, and the B
+// and y tiles of the next chunk are loaded into registers while the current
+// chunk is computed, so each chunk costs one round trip of latency less and
+// the partials are read cpw times less often.  y leaves through raw buffer
+// stores (y must span less than 2 GiB): lanes without a row store to a dropped
+// offset, so no store sits under a branch and the next chunk's loads are not
+// held up by the previous chunk's stores.
+template <int MODE>
+__global__ __launch_bounds__(256) void expand_mfma_chunks_kernel(
+    const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
+    RowList L, Geo g, Chunks ch, Chunks gr, int ksplit, int v_rows, int cpw) {
+  constexpr int TM = kMfmaTileRows, NC = kExpandMfmaCols, KB = 64;
+  constexpr int LDK = KB + 8, LDY = NC + 8;
+  static_assert(TM == 64 && NC == 128, "staging covers 64 tokens x 128 columns");
+  __shared__ __align__(16) uint16_t bs[NC * LDK];
+  __shared__ __align__(16) uint16_t vh[TM * LDK];
+  __shared__ __align__(16) uint16_t vl[TM * LDK];
+  __shared__ __align__(16) uint16_t ys[TM * LDY];
+  __shared__ int s_tok[TM];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int m16 = lane & 15, grp = lane >> 4;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int f = bid / gr.total;
+  const int gidx = bid - f * gr.total;
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < LORA_MAX_SLICES; ++i)
+    if (i < g.S && gidx >= gr.start[i]) s = i;
+  const int c_begin = ch.start[s] + (gidx - gr.start[s]) * cpw;
+  const int c_end = min(ch.start[s + 1], c_begin + cpw);
+  const int out_s = g.out[s];
+  int r0, cnt, sid;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid)) return;
+  if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
+  const int R = g.R;  // <= 64, a multiple of 8
+  const int SR = g.S * R;
+  const __amdgpu_buffer_rsrc_t yb = make_rsrc(y, (uint32_t)((size_t)g.T * g.O * sizeof(uint16_t)));
+  if (tid < TM) {
+    const int tk = L.tok[r0 + min(tid, cnt - 1)];
+    s_tok[tid] = (tid < cnt && tk >= 0 && tk < g.T) ? tk : -1;
+  }
+  __syncthreads();
+  // staging lanes: y / v row (t / 16) + 16 j with y columns 8 (t % 16) .. +8 or
+  // v ranks 4 (t % 16) .. +4; B column (t / 8) + 32 j with ranks 8 (t % 8) .. +8
+  const int q16 = tid & 15, srow = tid >> 4;
+  const int b8 = tid & 7, bcol = tid >> 3;
+  // loads of chunk c; B values are masked (bm) where they are written to LDS,
+  // so no wait for them sits here
+  auto load_chunk = [&](int c, u32x4(&br)[4], uint32_t(&bm)[4], u32x4(&yr)[4]) {
+    const int col0 = (c - ch.start[s]) * NC;
+    const uint16_t* Bt = B + ((size_t)sid * g.O + g.off[s] + col0) * R;
+    const bool bk_ok = 8 * b8 < R;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cc = bcol + 32 * j;
+      const bool ok = bk_ok && col0 + cc < out_s;
+      br[j] = ld16(Bt + (size_t)(ok ? cc : 0) * R + (ok ? 8 * b8 : 0));
+      bm[j] = all_or_none(ok);
+    }
+    const int ycol = col0 + 8 * q16;
+    const bool ycol_ok = ycol < out_s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tk = s_tok[srow + 16 * j];
+      yr[j] = ld16(y + (size_t)(tk >= 0 ? tk : 0) * g.O + g.off[s] + (ycol_ok ? ycol : 0));
+    }
+  };
+  u32x4 br[4], yr[4];
+  uint32_t bm[4];
+  load_chunk(c_begin, br, bm, yr);
+  {  // v: sum of the partials in fixed order, split into hi + lo, once per workgroup
+    u32x4 vr[4][kMaxKsplit];
+    const bool vk_ok = 4 * q16 < R;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = srow + 16 * j;
+      const bool ok = vk_ok && s_tok[row] >= 0;
+      const uint32_t m = all_or_none(ok);
+#pragma unroll
+      for (int p = 0; p < kMaxKsplit; ++p) {
+        const bool pin = p < ksplit;
+        const size_t off = ((size_t)(pin ? p : 0) * v_rows + r0 + (ok ? row : 0)) * SR + s * R +
+                           (ok ? 4 * q16 : 0);
+        vr[j][p] = ld16(v + off) & (m & all_or_none(pin));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float e[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < kMaxKsplit; ++p) {
+        e[0] += __uint_as_float(vr[j][p].x);
+        e[1] += __uint_as_float(vr[j][p].y);
+        e[2] += __uint_as_float(vr[j][p].z);
+        e[3] += __uint_as_float(vr[j][p].w);
+      }
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = f32_to_bf16_bits(e[i]);
+        l[i] = f32_to_bf16_bits(e[i] - __uint_as_float(h[i] << 16));
+      }
+      const int vo = (srow + 16 * j) * LDK + 4 * q16;
+      *reinterpret_cast<u32x2*>(&vh[vo]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<u32x2*>(&vl[vo]) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    }
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int col0 = (c - ch.start[s]) * NC;
+    const int ycol = col0 + 8 * q16;
+    const bool ycol_ok = ycol < out_s;
+    if (c > c_begin) __syncthreads();  // readers of bs / ys of the previous chunk are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(&bs[(bcol + 32 * j) * LDK + 8 * b8]) = br[j] & bm[j];
+      *reinterpret_cast<u32x4*>(&ys[(srow + 16 * j) * LDY + 8 * q16]) = yr[j];
+    }
+    // the next chunk's loads overlap this one (the last chunk reloads itself:
+    // unconditional loads keep the memory counters exact)
+    load_chunk(min(c + 1, c_end - 1), br, bm, yr);
+    __syncthreads();
+    f32x4 acc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < R; kk += 32) {
+      const int vo = (16 * wave + m16) * LDK + kk + 8 * grp;
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vh[vo]));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vl[vo]));
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int q = nt >> 1, hi = nt & 1;
+        const int crow = 32 * q + 8 * (m16 >> 2) + 4 * hi + (m16 & 3);
+        const bf16x8 ba = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&bs[crow * LDK + kk + 8 * grp]));
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bh, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bl, acc[nt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint16_t* yp = &ys[(16 * wave + m16) * LDY + 32 * q + 8 * grp];
+      const u32x4 w = *reinterpret_cast<const u32x4*>(yp);
+      const f32x4 d0 = acc[2 * q], d1 = acc[2 * q + 1];
+      const float add[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      const uint32_t wi[4] = {w.x, w.y, w.z, w.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(wi[i] << 16) + add[2 * i];
+        const float hi = __uint_as_float(wi[i] & 0xffff0000u) + add[2 * i + 1];
+        o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+      }
+      *reinterpret_cast<u32x4*>(yp) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = srow + 16 * j;
+      const int tk = s_tok[row];
+      const uint32_t off = (tk >= 0 && ycol_ok)
+                               ? (uint32_t)(((size_t)tk * g.O + g.off[s] + ycol) * sizeof(uint16_t))
+                               : kDropOffset;
+      st16_buf(*reinterpret_cast<const u32x4*>(&ys[row * LDY + 8 * q16]), yb, off);
+    }
+  }
+}
+
 // ------------------------------------------------------------ pool load
 //
 // One slice of one adapter into its slot: A rows copied and zero-padded to R;
@@ -972,6 +1158,22 @@ static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, fl
   return hip_check("shrink_mfma launch");
 }
 
+// Column groups of up to cpw chunks of one slice: group gi belongs to slice s
+// when start[s] <= gi < start[s + 1].
+static Chunks make_groups(const Geo& g, int cpw) {
+  Chunks c;
+  int acc = 0;
+  for (int s = 0; s < LORA_MAX_SLICES + 1; ++s) c.start[s] = 0;
+  for (int s = 0; s < g.S; ++s) {
+    c.start[s] = acc;
+    const int chunks = (g.out[s] + kExpandMfmaCols - 1) / kExpandMfmaCols;
+    acc += (chunks + cpw - 1) / cpw;
+  }
+  for (int s = g.S; s <= LORA_MAX_SLICES; ++s) c.start[s] = acc;
+  c.total = acc;
+  return c;
+}
+
 template <int MODE>
 static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, void* y,
                                   const RowList& L, int64_t tiles, int ksplit, int v_rows,
@@ -980,6 +1182,21 @@ static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, v
   if (ksplit < 1 || ksplit > kMaxKsplit) return fail(LORA_E_ARG, "bad K split %d", ksplit);
   const Chunks ch = make_chunks(g, kExpandMfmaCols);
   if (tiles * ch.total > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
+  if (g.R <= 64 && (int64_t)g.T * g.O * 2 < (int64_t)kDropOffset) {
+    // chunks per workgroup: enough workgroups to fill the GPU several times over
+    // (about 1024), at most 8 chunks each
+    const int64_t work = tiles * ch.total;
+    int cpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, work / 1024));
+    if (const char* e = std::getenv("LORA_EXPAND_MFMA_CPW")) {  // tuning / test override
+      const long o = std::strtol(e, nullptr, 10);
+      if (o >= 1 && o <= 8) cpw = (int)o;
+    }
+    const Chunks gr = make_groups(g, cpw);
+    hipLaunchKernelGGL(expand_mfma_chunks_kernel<MODE>, dim3(grid_of(tiles * gr.total)), dim3(256),
+                       0, st, v, (const uint16_t*)B, (uint16_t*)y, L, g, ch, gr, ksplit, v_rows,
+                       cpw);
+    return hip_check("expand_mfma_chunks launch");
+  }
   hipLaunchKernelGGL(expand_mfma_kernel<MODE>, dim3(grid_of(tiles * ch.total)), dim3(256), 0, st,
                      v, (const uint16_t*)B, (uint16_t*)y, L, g, ch, ksplit, v_rows);
   return hip_check("expand_mfma launch");

@@ -210,9 +210,14 @@ def test_exact_integer_bit_identical(dtype, rslora):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
 
 
-def test_exact_integer_split_k():
+@pytest.mark.parametrize("cpw", [None, "3"])
+def test_exact_integer_split_k(cpw, monkeypatch):
     """Long segments and K = 2056: the MFMA shrink splits K into four partials
-    (summed by the MFMA expand); integer inputs make the result exact."""
+    (summed by the MFMA expand); integer inputs make the result exact.  With
+    cpw = 3 the MFMA expand covers three column chunks per workgroup (groups
+    of 3 and 2 chunks in the two slices)."""
+    if cpw:
+        monkeypatch.setenv("LORA_EXPAND_MFMA_CPW", cpw)
     wl = _integer_workload("bf16", seed=5, K=2056, T=420, lens=(64, 65, 130, 100, 16))
     d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
     plan, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
