@@ -238,7 +238,7 @@ def kernel_roofline(setups, stream_ptr, launches):
     """Per launch group (shrink, expand): average time and algorithmic-bytes
     rate; returns the dominant group (larger time per step)."""
     res = {}
-    for which in ("shrink", "expand"):
+    for which in setups[0].kernels():
         us = time_kernel(setups, which, launches, 10, stream_ptr)
         by = fl = 0
         names = []
@@ -289,7 +289,8 @@ def stage_kernels(wl):
     out = {"shrink": [], "expand": []}
     if p["mfma_tiles"]:
         out["shrink"].append("shrink_mfma_kernel<2>")
-        out["expand"].append("expand_mfma_kernel<2>")
+        chunks = wl.max_lora_rank <= 64 and wl.T * wl.O * 2 < 2 ** 31
+        out["expand"].append("expand_mfma_chunks_kernel<2>" if chunks else "expand_mfma_kernel<2>")
     if p["wave_tiles"]:
         # mode 3: records in the kernel arguments (small plans), 2: device image
         mode = 3 if not p["mfma_tiles"] and p["wave_tiles"] * 16 <= 512 else 2
@@ -325,10 +326,10 @@ def record_traffic(pmc_dir, workload, seed):
         data = json.load(open(TRAFFIC_JSON))
     sha = kernel_source_sha()
     wls = make_workloads(workload, seed)
-    kern = {"shrink": set(), "expand": set()}
+    kern = {}
     for wl in wls:
         for k, v in stage_kernels(wl).items():
-            kern[k].update(v)
+            kern.setdefault(k, set()).update(v)
     for stage, names in kern.items():
         # one launch group = one dispatch of each of its kernels; averaged over
         # the workload's calls like the algorithmic bytes
