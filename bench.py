@@ -128,6 +128,8 @@ class Setup:
         # launches lora_apply makes after its own plan copy)
         self.plan_d, img, _ = L.lora_apply_plan(self.desc, self.ids, self.pre)
         self.plan = L.plan_struct(self.plan_d)
+        # lora_apply skips the plan copy for plans of at most 48 wavefront tiles
+        self.small_plan = self.plan_d["mfma_tiles"] == 0 and self.plan_d["wave_tiles"] <= 48
         self.image = torch.from_numpy(img if img.size else np.zeros(4, np.int32)).cuda()
         # host copy: a small plan then travels in the kernel arguments, as in lora_apply
         self.image_host = np.ascontiguousarray(img if img.size else np.zeros(4, np.int32))
@@ -142,6 +144,16 @@ class Setup:
         import torch
         L = self.L
         r = i % self.nrep
+        if self.small_plan:
+            # the plan travels in the kernel arguments: the GPU never reads the
+            # staging buffer, so one buffer serves every call without events
+            st = L.lib().lora_apply(ctypes.byref(self.desc), self.pA[r], self.pB[r], self.px[r],
+                                    self.py[r], self.T, self.ids.ctypes.data, self.pre.ctypes.data,
+                                    0, self.ws.data_ptr(), self.ws_bytes, self.stage[0].data_ptr(),
+                                    self.mh_bytes, stream_ptr)
+            if st != 0:
+                raise RuntimeError(f"lora_apply failed: {L.last_error()}")
+            return
         j = i % self.nstage
         if self.stage_ev[j] is not None:
             self.stage_ev[j].synchronize()
@@ -292,8 +304,10 @@ def stage_kernels(wl):
         chunks = wl.max_lora_rank <= 64 and wl.T * wl.O * 2 < 2 ** 31
         out["expand"].append("expand_mfma_chunks_kernel<2>" if chunks else "expand_mfma_kernel<2>")
     if p["wave_tiles"]:
-        # mode 3: records in the kernel arguments (small plans), 2: device image
-        mode = 3 if not p["mfma_tiles"] and p["wave_tiles"] * 16 <= 512 else 2
+        # modes 3 / 4: records in the kernel arguments (up to 12 / 48 tiles),
+        # 2: device image
+        small = not p["mfma_tiles"]
+        mode = (3 if p["wave_tiles"] <= 12 else 4 if p["wave_tiles"] <= 48 else 2) if small else 2
         out["shrink"].append(f"shrink_wave_kernel<{tag}, 8, 4, {mode}>")
         out["expand"].append(f"expand_wave_kernel<{tag}, 8, {kb}, {mode}>")
     return out

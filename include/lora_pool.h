@@ -282,9 +282,10 @@ int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* id
  *               plan->image_bytes long), or NULL when image_host is given and
  *               the plan is small.
  *   image_host: host copy of the image (as lora_apply_plan leaves it in
- *               meta_host), or NULL.  A small plan (no MFMA tiles, at most 32
- *               wavefront tiles) with a host copy travels in the kernel
- *               arguments and `image` is not read; otherwise `image` is used.
+ *               meta_host), or NULL.  A small plan (no MFMA tiles, at most 48
+ *               wavefront tiles, max_loras <= 2^28) with a host copy travels
+ *               in the kernel arguments and `image` is not read; otherwise
+ *               `image` is used.
  *   v:          device fp32 [ksplit][num_sgmv_rows + num_bgmv_rows][S][R]
  *               (plan row order; partial p of row i at
  *               ((p * rows + i) * S + s) * R + k).

@@ -90,8 +90,8 @@ int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const voi
   if (p->mfma_tiles > 0 && g.dtype != LORA_BF16)
     return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
   const int32_t* host = (const int32_t*)image_host;
-  const bool small = host && p->mfma_tiles == 0 &&
-                     (int64_t)p->wave_tiles * LORA_PLAN_WAVE_WORDS <= kSmallPlanWords;
+  const bool small = host && p->mfma_tiles == 0 && p->wave_tiles <= kArgTilesL &&
+                     g.max_loras <= (1 << 28);
   if ((p->wave_tiles > 0 || p->mfma_tiles > 0) && !small) {
     if (int32_t e = need_ptr(image, "image")) return e;
   }
@@ -294,8 +294,7 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
   const int32_t rows = p.num_sgmv_rows + p.num_bgmv_rows;
   if (rows == 0) return LORA_OK;
   const char* image_host = (const char*)meta_host + p.image_offset;
-  const bool small = p.mfma_tiles == 0 &&
-                     (int64_t)p.wave_tiles * LORA_PLAN_WAVE_WORDS <= kSmallPlanWords;
+  const bool small = p.mfma_tiles == 0 && p.wave_tiles <= kArgTilesL && g.max_loras <= (1 << 28);
   if (!small) {  // small plans travel in the kernel arguments instead
     if (int32_t e = hip_ok(hipMemcpyAsync(ws, image_host, (size_t)p.image_bytes,
                                           hipMemcpyHostToDevice, (hipStream_t)stream),

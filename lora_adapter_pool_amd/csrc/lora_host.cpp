@@ -122,14 +122,21 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
                         lora_meta* out) {
   const int32_t limit = bgmv_max_rank > 0 ? bgmv_max_rank : LORA_BGMV_MAX_RANK_DEFAULT;
   const bool all_sgmv = max_lora_rank > limit;
-  std::vector<int32_t> cnt_s(max_loras, 0), cnt_b(max_loras, 0);
+  // per-slot counters and positions: four arrays of max_loras ints, kept per
+  // thread and reused, so a call allocates nothing once it has seen its pool size
+  static thread_local std::vector<int32_t> scratch;
+  if (scratch.size() < 4 * (size_t)max_loras) scratch.resize(4 * (size_t)max_loras);
+  int32_t* cnt_s = scratch.data();
+  int32_t* cnt_b = cnt_s + max_loras;
+  int32_t* pos_s = cnt_b + max_loras;
+  int32_t* pos_b = pos_s + max_loras;
+  std::fill(cnt_s, cnt_s + 2 * (size_t)max_loras, 0);
   for (int32_t t = 0; t < T; ++t) {
     const int32_t a = ids[t];
     if (a < 0) continue;
     const bool sg = all_sgmv || (prefill && prefill[t]);
     (sg ? cnt_s : cnt_b)[a]++;
   }
-  std::vector<int32_t> pos_s(max_loras), pos_b(max_loras);
   int32_t ns = 0, nb = 0, nseg = 0;
   for (int32_t a = 0; a < max_loras; ++a) {
     pos_s[a] = ns;

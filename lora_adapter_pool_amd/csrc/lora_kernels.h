@@ -17,7 +17,11 @@ constexpr int kWaveTileRows = LORA_PLAN_WAVE_ROWS;  // rows per tile of the VALU
 constexpr int kMfmaTileRows = LORA_PLAN_MFMA_ROWS;  // rows per tile of the MFMA kernels
 constexpr int kExpandCols = 256;       // output columns per VALU expand workgroup
 constexpr int kExpandMfmaCols = 128;   // output columns per MFMA expand workgroup
-constexpr int kSmallPlanWords = 512;   // plans up to 32 wavefront tiles go by value (2 KB)
+// Plans of wavefront tiles only go by value in the kernel arguments: packed
+// records of kArgWords words, up to kArgTilesS (480 bytes) or kArgTilesL tiles.
+constexpr int kArgWords = 2 + LORA_PLAN_WAVE_ROWS;
+constexpr int kArgTilesS = 12;
+constexpr int kArgTilesL = 48;
 constexpr int kMaxKsplit = LORA_PLAN_MAX_KSPLIT;  // K splits of the MFMA shrink
 
 // A list of rows to process.  Row i reads token tok[i] of x / y and writes row i

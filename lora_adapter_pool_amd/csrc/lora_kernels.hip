@@ -186,13 +186,20 @@ __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int&
   return true;
 }
 
-enum { kSegs = 0, kRows = 1, kList = 2, kArg = 3 };  // how a kernel finds its tile
+// How a kernel finds its tile: device segments, device rows with ids, the
+// plan's device image, or records passed by value in two capacities.
+enum { kSegs = 0, kRows = 1, kList = 2, kArg = 3, kArgL = 4 };
 
-// Tile records passed by value (kArg): a small plan travels in the kernel
-// arguments, which the wavefronts read with scalar loads, so no copy of the
-// plan precedes the launch.  Other modes carry an empty struct.
+// Tile records passed by value (kArg, kArgL): a small plan travels in the
+// kernel arguments, which the wavefronts read with scalar loads, so no copy of
+// the plan precedes the launch.  Records are packed to kArgWords words (slot
+// in bits 0..27 and rows in bits 28..31 of word 0, first v row, tokens), and
+// the smaller capacity keeps the arguments short: the launch cost grows with
+// their size.  Other modes carry an empty struct.
 template <int MODE> struct PlanArg {};
-template <> struct PlanArg<kArg> { int32_t w[kSmallPlanWords]; };
+template <> struct PlanArg<kArg> { int32_t w[kArgTilesS * kArgWords]; };
+template <> struct PlanArg<kArgL> { int32_t w[kArgTilesL * kArgWords]; };
+template <int MODE> constexpr int arg_tiles() { return MODE == kArg ? kArgTilesS : kArgTilesL; }
 
 // Rows of one tile, the same in every lane (scalar registers).  Row r is v row
 // vrow0 + r, reads token tok[r] and uses adapter aid[r]; bit r of `valid` is
@@ -217,15 +224,16 @@ __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
                                           const PlanArg<MODE>& pa, TileRows<TM>& tr) {
   static_assert(TM <= LORA_PLAN_WAVE_WORDS - 4, "a tile record holds at most 12 tokens");
   const int lane = threadIdx.x & 63;
-  if constexpr (MODE == kArg) {
-    if (f >= L.num_tiles || f >= kSmallPlanWords / LORA_PLAN_WAVE_WORDS) return false;
-    const int32_t* rec = pa.w + f * LORA_PLAN_WAVE_WORDS;
-    const int sid = rec[0];
-    tr.cnt = rec[1];
-    tr.vrow0 = rec[2];
+  if constexpr (MODE == kArg || MODE == kArgL) {
+    static_assert(TM <= kArgWords - 2, "a packed record holds kArgWords - 2 tokens");
+    if (f >= L.num_tiles || f >= arg_tiles<MODE>()) return false;
+    const int32_t* rec = pa.w + f * kArgWords;
+    const int sid = rec[0] & 0x0fffffff;
+    tr.cnt = (int)((uint32_t)rec[0] >> 28);
+    tr.vrow0 = rec[1];
 #pragma unroll
     for (int r = 0; r < TM; ++r) {
-      tr.tok[r] = rec[4 + r];
+      tr.tok[r] = rec[2 + r];
       tr.aid[r] = sid;
     }
   } else if constexpr (MODE == kList) {
@@ -1261,17 +1269,23 @@ static void plan_lists(const TilePlan& p, RowList& Lw, RowList& Lm) {
                p.mfma_tiles, 0, INT32_MAX};
 }
 
-// Small plans (wavefront tiles only, at most kSmallPlanWords words of records)
-// with host records go by value.
-static bool small_plan(const TilePlan& p) {
-  return p.wave_host != nullptr && p.mfma_tiles == 0 &&
-         (int64_t)p.wave_tiles * LORA_PLAN_WAVE_WORDS <= kSmallPlanWords;
+// Small plans (wavefront tiles only, at most kArgTilesL records, slots below
+// 2^28) with host records go by value, in the smaller capacity that fits.
+static bool small_plan(const TilePlan& p, const Geo& g) {
+  return p.wave_host != nullptr && p.mfma_tiles == 0 && p.wave_tiles <= kArgTilesL &&
+         g.max_loras <= (1 << 28);
 }
 
-static PlanArg<kArg> small_arg(const TilePlan& p) {
-  PlanArg<kArg> a;
-  const int n = p.wave_tiles * LORA_PLAN_WAVE_WORDS;
-  for (int i = 0; i < kSmallPlanWords; ++i) a.w[i] = i < n ? p.wave_host[i] : -1;
+template <int MODE> static PlanArg<MODE> pack_arg(const TilePlan& p) {
+  PlanArg<MODE> a;
+  for (int i = 0; i < arg_tiles<MODE>() * kArgWords; ++i) a.w[i] = -1;
+  for (int f = 0; f < p.wave_tiles; ++f) {
+    const int32_t* rec = p.wave_host + (size_t)f * LORA_PLAN_WAVE_WORDS;
+    int32_t* o = a.w + f * kArgWords;
+    o[0] = (int32_t)(((uint32_t)rec[1] << 28) | ((uint32_t)rec[0] & 0x0fffffffu));
+    o[1] = rec[2];
+    for (int r = 0; r < kArgWords - 2; ++r) o[2 + r] = rec[4 + r];
+  }
   return a;
 }
 
@@ -1281,10 +1295,15 @@ int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, co
   if (p.mfma_tiles > 0 && !bf) return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
   RowList Lw, Lm;
   plan_lists(p, Lw, Lm);
-  if (small_plan(p)) {
-    const PlanArg<kArg> a = small_arg(p);
-    return bf ? launch_shrink_wave<uint16_t, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a)
-              : launch_shrink_wave<float, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a);
+  if (small_plan(p, g)) {
+    if (p.wave_tiles <= kArgTilesS) {
+      const PlanArg<kArg> a = pack_arg<kArg>(p);
+      return bf ? launch_shrink_wave<uint16_t, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a)
+                : launch_shrink_wave<float, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a);
+    }
+    const PlanArg<kArgL> a = pack_arg<kArgL>(p);
+    return bf ? launch_shrink_wave<uint16_t, kArgL>(g, x, A, v, Lw, p.wave_tiles, st, a)
+              : launch_shrink_wave<float, kArgL>(g, x, A, v, Lw, p.wave_tiles, st, a);
   }
   if (int32_t e = launch_shrink_mfma<kList>(g, x, A, v, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
                                             st))
@@ -1299,10 +1318,15 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
   if (p.mfma_tiles > 0 && !bf) return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
   RowList Lw, Lm;
   plan_lists(p, Lw, Lm);
-  if (small_plan(p)) {
-    const PlanArg<kArg> a = small_arg(p);
-    return bf ? launch_expand_wave<uint16_t, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a)
-              : launch_expand_wave<float, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a);
+  if (small_plan(p, g)) {
+    if (p.wave_tiles <= kArgTilesS) {
+      const PlanArg<kArg> a = pack_arg<kArg>(p);
+      return bf ? launch_expand_wave<uint16_t, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a)
+                : launch_expand_wave<float, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a);
+    }
+    const PlanArg<kArgL> a = pack_arg<kArgL>(p);
+    return bf ? launch_expand_wave<uint16_t, kArgL>(g, v, B, y, Lw, p.wave_tiles, st, a)
+              : launch_expand_wave<float, kArgL>(g, v, B, y, Lw, p.wave_tiles, st, a);
   }
   if (int32_t e = launch_expand_mfma<kList>(g, v, B, y, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
                                             st))

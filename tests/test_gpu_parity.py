@@ -342,17 +342,18 @@ def test_plan_reused_across_layers(dtype):
         check_rows(lw, yd, label=f"plan layer {i} {dtype}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_small_plan_by_value(dtype):
-    """A decode plan of at most 32 wavefront tiles travels in the kernel
-    arguments (host image given, device image NULL): same bits as the
-    device-image path, within tolerance of the oracle."""
+@pytest.mark.parametrize("dtype,T,n_adapters", [("bf16", 64, 6), ("f32", 64, 6), ("bf16", 200, 20)])
+def test_small_plan_by_value(dtype, T, n_adapters):
+    """A decode plan of at most 48 wavefront tiles travels in the kernel
+    arguments as packed records (up to 12 or up to 48 tiles; host image given,
+    device image NULL): same bits as the device-image path, within tolerance
+    of the oracle."""
     import torch
-    wl = W.config_bgmv_decode(seed=8, T=64, K=520, O=264, n_adapters=6, rank=16,
+    wl = W.config_bgmv_decode(seed=8, T=T, K=520, O=264, n_adapters=n_adapters, rank=16,
                               dtype=dtype)
     pool = make_pool(wl)
     plan, img, views = L.lora_apply_plan(pool.desc, wl.ids, wl.prefill)
-    assert plan["mfma_tiles"] == 0 and 0 < plan["wave_tiles"] <= 32
+    assert plan["mfma_tiles"] == 0 and 0 < plan["wave_tiles"] <= 48
     image = torch.from_numpy(img).cuda()
     rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
     outs = []
