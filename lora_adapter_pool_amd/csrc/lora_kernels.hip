@@ -886,27 +886,33 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
 
 // ------------------------------------------------------------ expand (MFMA, R <= 64)
 //
-// bf16, pools of rank R <= 64.  Like expand_mfma_kernel, but a workgroup covers
-// a group of up to `cpw` consecutive column chunks of one slice of its tile
-// (gr.start[s] is the first group of slice s): v (the sum of the shrink's
-// partials, as hi + lo bf16) is staged in LDS once for all of them, and the B
-// and y tiles of the next chunk are loaded into registers while the current
-// chunk is computed, so each chunk costs one round trip of latency less and
-// the partials are read cpw times less often.  y leaves through raw buffer
-// stores (y must span less than 2 GiB): lanes without a row store to a dropped
-// offset, so no store sits under a branch and the next chunk's loads are not
-// held up by the previous chunk's stores.
+// bf16, pools of rank R <= 64.  A workgroup covers a group of up to `cpw`
+// consecutive column chunks of 128 columns of one slice of its tile
+// (gr.start[s] is the first group of slice s).  v (the sum of the shrink's
+// partials in fixed order, split into hi + lo bf16) is staged in LDS once for
+// the group; per chunk only the B tile [128 columns][R] goes through LDS
+// (coalesced 16-byte loads, 8 lanes per 128-byte row).  Wave w computes
+// D = Btile * v^T for tokens 16 w .. +16 as eight 16 x 16 tiles, two MFMAs (hi,
+// lo) per tile and 32-rank chunk; inside a pair of tiles, MFMA row n of tile 2q
+// maps to column 32 q + 8 (n / 4) + n % 4 and of tile 2q+1 to the same + 4, so
+// lane (g, m) ends with columns 32 q + 8 g .. +8 of token m.  The lane reads
+// and writes those 8 y values directly (16 bytes; four lanes cover 64
+// contiguous bytes of a row), so y never passes through LDS and the workgroup
+// needs 36 KB of LDS, four per compute unit.  The next chunk's B and y are
+// loaded while the current one is computed; y leaves through raw buffer
+// stores (y must span less than 2 GiB): lanes without a row store to a
+// dropped offset, so no store sits under a branch and the next chunk's loads
+// are not held up by the previous chunk's stores.
 template <int MODE>
-__global__ __launch_bounds__(256) void expand_mfma_chunks_kernel(
+__global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
     const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
     RowList L, Geo g, Chunks ch, Chunks gr, int ksplit, int v_rows, int cpw) {
   constexpr int TM = kMfmaTileRows, NC = kExpandMfmaCols, KB = 64;
-  constexpr int LDK = KB + 8, LDY = NC + 8;
-  static_assert(TM == 64 && NC == 128, "staging covers 64 tokens x 128 columns");
+  constexpr int LDK = KB + 8;
+  static_assert(TM == 64 && NC == 128, "64 tokens x 128 columns per chunk");
   __shared__ __align__(16) uint16_t bs[NC * LDK];
   __shared__ __align__(16) uint16_t vh[TM * LDK];
   __shared__ __align__(16) uint16_t vl[TM * LDK];
-  __shared__ __align__(16) uint16_t ys[TM * LDY];
   __shared__ int s_tok[TM];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -932,12 +938,15 @@ __global__ __launch_bounds__(256) void expand_mfma_chunks_kernel(
     s_tok[tid] = (tid < cnt && tk >= 0 && tk < g.T) ? tk : -1;
   }
   __syncthreads();
-  // staging lanes: y / v row (t / 16) + 16 j with y columns 8 (t % 16) .. +8 or
-  // v ranks 4 (t % 16) .. +4; B column (t / 8) + 32 j with ranks 8 (t % 8) .. +8
+  // this lane's token (MFMA column m16 of wave w) and its y row
+  const int my_tok = s_tok[16 * wave + m16];
+  const uint16_t* yrow = y + (size_t)(my_tok >= 0 ? my_tok : 0) * g.O + g.off[s];
+  const size_t yrow_off = ((size_t)(my_tok >= 0 ? my_tok : 0) * g.O + g.off[s]) * sizeof(uint16_t);
+  // staging lanes: v row (t / 16) + 16 j with ranks 4 (t % 16) .. +4; B column
+  // (t / 8) + 32 j with ranks 8 (t % 8) .. +8
   const int q16 = tid & 15, srow = tid >> 4;
   const int b8 = tid & 7, bcol = tid >> 3;
-  // loads of chunk c; B values are masked (bm) where they are written to LDS,
-  // so no wait for them sits here
+  // loads of chunk c: B (masked where written to LDS) and this lane's y
   auto load_chunk = [&](int c, u32x4(&br)[4], uint32_t(&bm)[4], u32x4(&yr)[4]) {
     const int col0 = (c - ch.start[s]) * NC;
     const uint16_t* Bt = B + ((size_t)sid * g.O + g.off[s] + col0) * R;
@@ -949,17 +958,15 @@ __global__ __launch_bounds__(256) void expand_mfma_chunks_kernel(
       br[j] = ld16(Bt + (size_t)(ok ? cc : 0) * R + (ok ? 8 * b8 : 0));
       bm[j] = all_or_none(ok);
     }
-    const int ycol = col0 + 8 * q16;
-    const bool ycol_ok = ycol < out_s;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tk = s_tok[srow + 16 * j];
-      yr[j] = ld16(y + (size_t)(tk >= 0 ? tk : 0) * g.O + g.off[s] + (ycol_ok ? ycol : 0));
+    for (int q = 0; q < 4; ++q) {
+      const int col = col0 + 32 * q + 8 * grp;
+      yr[q] = ld16(yrow + (col < out_s ? col : 0));
     }
   };
-  u32x4 br[4], yr[4];
+  u32x4 br[4], yn[4];
   uint32_t bm[4];
-  load_chunk(c_begin, br, bm, yr);
+  load_chunk(c_begin, br, bm, yn);
   {  // v: sum of the partials in fixed order, split into hi + lo, once per workgroup
     u32x4 vr[4][kMaxKsplit];
     const bool vk_ok = 4 * q16 < R;
@@ -999,17 +1006,16 @@ __global__ __launch_bounds__(256) void expand_mfma_chunks_kernel(
   }
   for (int c = c_begin; c < c_end; ++c) {
     const int col0 = (c - ch.start[s]) * NC;
-    const int ycol = col0 + 8 * q16;
-    const bool ycol_ok = ycol < out_s;
-    if (c > c_begin) __syncthreads();  // readers of bs / ys of the previous chunk are done
+    u32x4 yc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int q = 0; q < 4; ++q) yc[q] = yn[q];
+    if (c > c_begin) __syncthreads();  // MFMA readers of the previous chunk's bs are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
       *reinterpret_cast<u32x4*>(&bs[(bcol + 32 * j) * LDK + 8 * b8]) = br[j] & bm[j];
-      *reinterpret_cast<u32x4*>(&ys[(srow + 16 * j) * LDY + 8 * q16]) = yr[j];
-    }
     // the next chunk's loads overlap this one (the last chunk reloads itself:
     // unconditional loads keep the memory counters exact)
-    load_chunk(min(c + 1, c_end - 1), br, bm, yr);
+    load_chunk(min(c + 1, c_end - 1), br, bm, yn);
     __syncthreads();
     f32x4 acc[8];
 #pragma unroll
@@ -1028,13 +1034,13 @@ __global__ __launch_bounds__(256) void expand_mfma_chunks_kernel(
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bl, acc[nt], 0, 0, 0);
       }
     }
+    // y update in registers: lane (grp, m16) owns token 16 wave + m16, columns
+    // col0 + 32 q + 8 grp .. +8 of pair q
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint16_t* yp = &ys[(16 * wave + m16) * LDY + 32 * q + 8 * grp];
-      const u32x4 w = *reinterpret_cast<const u32x4*>(yp);
       const f32x4 d0 = acc[2 * q], d1 = acc[2 * q + 1];
       const float add[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-      const uint32_t wi[4] = {w.x, w.y, w.z, w.w};
+      const uint32_t wi[4] = {yc[q].x, yc[q].y, yc[q].z, yc[q].w};
       uint32_t o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1042,17 +1048,11 @@ __global__ __launch_bounds__(256) void expand_mfma_chunks_kernel(
         const float hi = __uint_as_float(wi[i] & 0xffff0000u) + add[2 * i + 1];
         o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
       }
-      *reinterpret_cast<u32x4*>(yp) = u32x4{o[0], o[1], o[2], o[3]};
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = srow + 16 * j;
-      const int tk = s_tok[row];
-      const uint32_t off = (tk >= 0 && ycol_ok)
-                               ? (uint32_t)(((size_t)tk * g.O + g.off[s] + ycol) * sizeof(uint16_t))
+      const int col = col0 + 32 * q + 8 * grp;
+      const uint32_t off = (my_tok >= 0 && col < out_s)
+                               ? (uint32_t)(yrow_off + (size_t)col * sizeof(uint16_t))
                                : kDropOffset;
-      st16_buf(*reinterpret_cast<const u32x4*>(&ys[row * LDY + 8 * q16]), yb, off);
+      st16_buf(u32x4{o[0], o[1], o[2], o[3]}, yb, off);
     }
   }
 }
