@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--sweep", action="store_true",
+                   help="also sweep BGMV decode over batch size, adapter count and rank")
     p.add_argument("--record-traffic", metavar="PMC_DIR", default=None,
                    help="write profiles/traffic.json from rocprofv3 counter runs and exit")
     return p.parse_args()
@@ -398,6 +400,34 @@ def cpu_baseline(wl, seconds):
                       f"{len(os.sched_getaffinity(0))} cores visible"}
 
 
+def bgmv_sweep(seed, stream_ptr):
+    """BGMV decode at in = out = 4096 over batch size T, adapters in the batch
+    and rank: per launch group, average time and algorithmic GB/s, to show
+    where the decode kernels leave the launch-latency regime."""
+    import torch
+    import workloads as W
+    rows = []
+    for rank, n_adapters in ((16, 8), (16, 64), (64, 8)):
+        for T in (64, 256, 1024, 4096):
+            wl = W.config_bgmv_decode(seed=seed, T=T, K=4096, O=4096, n_adapters=n_adapters,
+                                      rank=rank, alpha=2.0 * rank, p_none=0.0)
+            s = Setup(wl, 1024 * 2 ** 20)
+            el = measure([s], 50, 5, stream_ptr)
+            dom, res = kernel_roofline([s], stream_ptr, 50)
+            a = algorithmic(wl)
+            row = {"T": T, "adapters": n_adapters, "rank": rank, "step_us": el / 50 * 1e6,
+                   "bytes_per_step": a["bytes"],
+                   "stages": {k: {"us": round(r["us"], 2), "GBs": round(r["GBs"], 1),
+                                  "frac": round(r["GBs"] / HBM_PEAK_GBS, 3), "kernels": r["kernels"]}
+                              for k, r in res.items()}}
+            rows.append(row)
+            log(f"[bench] sweep T={T} adapters={n_adapters} R={rank}: step {row['step_us']:.1f} us, "
+                + ", ".join(f"{k} {v['us']:.1f} us {v['GBs']:.0f} GB/s" for k, v in row["stages"].items()))
+            del s
+            torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -508,6 +538,9 @@ def main():
                 f"{r['TFLOPs']:.1f} TFLOP/s")
         del s2
         torch.cuda.empty_cache()
+
+    if args.sweep:
+        out["bgmv_sweep"] = bgmv_sweep(args.seed, stream_ptr)
 
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")

@@ -234,15 +234,18 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
  *
  * The rows of the batch are the rows of lora_build_meta: the SGMV rows
  * (sgmv_perm order) are v rows 0 .. num_sgmv_rows - 1 and the BGMV rows
- * (bgmv_tok order) follow them.  Every tile covers consecutive v rows of one
- * adapter: wavefront tiles cut each short SGMV segment and each run of equal
- * ids of the BGMV rows into pieces of LORA_PLAN_WAVE_ROWS rows; MFMA tiles cut
- * the SGMV segments of at least mfma_min_rows rows (bf16 pools only) into
- * pieces of LORA_PLAN_MFMA_ROWS rows.
+ * (bgmv_tok order, sorted by id) follow them.  Every tile covers consecutive v
+ * rows of one adapter, cut from a run of rows of that adapter (an SGMV
+ * segment or a run of equal ids among the BGMV rows):
+ *   - MFMA tiles (bf16 pools only), pieces of LORA_PLAN_MFMA_ROWS rows: SGMV
+ *     segments of at least mfma_min_rows rows, and BGMV runs of at least
+ *     bgmv_mfma_min_rows rows (a threshold the plan sets only for batches in
+ *     which such runs hold many rows);
+ *   - wavefront tiles, pieces of LORA_PLAN_WAVE_ROWS rows: every other run.
  *
  * The device image starts image_offset bytes into meta_host and is
  * image_bytes long; offsets below count int32 words from its start:
- *   perm [num_sgmv_rows]              token of each SGMV row
+ *   perm [num_sgmv_rows + num_bgmv_rows]  token of each v row
  *   wave [wave_tiles][16]             slot, rows, first v row, 0, token of
  *                                     each row (-1 past the last row), -1 ...
  *   mfma [mfma_tiles][4]              slot, rows, first v row, 0
@@ -259,7 +262,7 @@ typedef struct {
   int32_t mfma_tiles;
   int32_t mfma_min_rows;   /* INT32_MAX when no segment uses MFMA tiles */
   int32_t ksplit;          /* in [1, LORA_PLAN_MAX_KSPLIT] */
-  int32_t reserved;
+  int32_t bgmv_mfma_min_rows;  /* INT32_MAX when no BGMV run uses MFMA tiles */
   int64_t image_offset;    /* bytes from meta_host to the device image (16-byte aligned) */
   int64_t image_bytes;
   int64_t off_perm;        /* int32 offsets inside the image */
@@ -305,15 +308,18 @@ int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void*
                          const void* image_host, void* stream);
 
 /* The whole delta path for one batch ([TGI] step 4; [QA] direct answer):
- * lora_apply_plan into meta_host, one copy of the plan's device image into ws
- * on `stream` (skipped for a small plan, which goes in the kernel arguments),
- * then lora_plan_shrink and lora_plan_expand on `stream`, updating y in place.  Rows with id -1 are never read or written.
+ * lora_apply_plan into meta_host, then lora_plan_shrink and lora_plan_expand
+ * on `stream`, updating y in place.  Rows with id -1 are never read or written.
+ * The plan reaches the kernels in one of three ways: a small plan goes in the
+ * kernel arguments; otherwise, if meta_host is pinned (hipHostMalloc), the
+ * kernels read the plan's image from meta_host itself; otherwise the image is
+ * copied into ws.
  *   ids_host[T], prefill_host[T] (NULL = all decode): host arrays.
  *   ws: device workspace of >= lora_apply_workspace_bytes(desc, T) bytes.
- *   meta_host: host staging of >= lora_apply_host_meta_bytes(desc, T) bytes.
- *     If it is pinned (hipHostMalloc) the copy is asynchronous and the caller
- *     must not rewrite it until the stream has passed this call; pageable
- *     memory is copied before the call returns.
+ *   meta_host: host staging of >= lora_apply_host_meta_bytes(desc, T) bytes,
+ *     16-byte aligned.  If it is pinned the caller must not rewrite it until
+ *     the stream has passed this call; pageable memory may be reused as soon
+ *     as the call returns.
  * Returns without synchronising.  T = 0 is a no-op. */
 int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
                    const void* x, void* y, int32_t T, const int32_t* ids_host,

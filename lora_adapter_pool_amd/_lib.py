@@ -65,7 +65,7 @@ class lora_plan(ctypes.Structure):
     _fields_ = [("num_sgmv_rows", ctypes.c_int32), ("num_bgmv_rows", ctypes.c_int32),
                 ("num_segs", ctypes.c_int32), ("wave_tiles", ctypes.c_int32),
                 ("mfma_tiles", ctypes.c_int32), ("mfma_min_rows", ctypes.c_int32),
-                ("ksplit", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ksplit", ctypes.c_int32), ("bgmv_mfma_min_rows", ctypes.c_int32),
                 ("image_offset", ctypes.c_int64), ("image_bytes", ctypes.c_int64),
                 ("off_perm", ctypes.c_int64), ("off_wave", ctypes.c_int64),
                 ("off_mfma", ctypes.c_int64)]
@@ -291,7 +291,7 @@ def lora_apply_plan(desc, ids, prefill=None, bgmv_max_rank: int = 0):
     d = {k: getattr(p, k) for k, _ in lora_plan._fields_}
     img = stage[p.image_offset // 4: (p.image_offset + p.image_bytes) // 4].copy()
     views = {
-        "perm": img[p.off_perm:p.off_perm + p.num_sgmv_rows],
+        "perm": img[p.off_perm:p.off_perm + p.num_sgmv_rows + p.num_bgmv_rows],
         "wave": img[p.off_wave:p.off_wave + PLAN_WAVE_WORDS * p.wave_tiles].reshape(-1, PLAN_WAVE_WORDS),
         "mfma": img[p.off_mfma:p.off_mfma + PLAN_MFMA_WORDS * p.mfma_tiles].reshape(-1, PLAN_MFMA_WORDS),
     }

@@ -83,7 +83,7 @@ int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const voi
   if (p->off_wave % 4 || p->off_mfma % 4)
     return fail(LORA_E_ALIGN, "plan sections must start on 16-byte boundaries");
   const int64_t words = p->image_bytes / 4;
-  if (p->off_perm + p->num_sgmv_rows > words ||
+  if (p->off_perm + p->num_sgmv_rows + p->num_bgmv_rows > words ||
       p->off_wave + (int64_t)LORA_PLAN_WAVE_WORDS * p->wave_tiles > words ||
       p->off_mfma + (int64_t)LORA_PLAN_MFMA_WORDS * p->mfma_tiles > words)
     return fail(LORA_E_ARG, "malformed plan (sections exceed image_bytes)");
@@ -98,7 +98,7 @@ int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const voi
   const int32_t* img = (const int32_t*)image;
   *tp = TilePlan{img ? img + p->off_perm : nullptr, img ? img + p->off_wave : nullptr,
                  p->wave_tiles, img ? img + p->off_mfma : nullptr, p->mfma_tiles,
-                 host ? host + p->off_wave : nullptr, p->ksplit, p->num_sgmv_rows,
+                 host ? host + p->off_wave : nullptr, p->ksplit,
                  p->num_sgmv_rows + p->num_bgmv_rows};
   return LORA_OK;
 }
@@ -267,6 +267,19 @@ int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void*
   return run_plan_expand(g, v, B_pool, y, tp, (hipStream_t)stream);
 }
 
+// `host` itself when it is pinned host memory (hipHostMalloc) that the device
+// reaches at the same address, else nullptr (pageable memory, or a mapping at
+// another address: the caller then copies).  Kernels that read a plan there
+// see every write the host made before their launch.
+static const void* device_alias(const void* host) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, host) != hipSuccess) {
+    (void)hipGetLastError();  // pageable memory is not an error here
+    return nullptr;
+  }
+  return a.type == hipMemoryTypeHost && a.devicePointer == host ? host : nullptr;
+}
+
 int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
                    const void* x, void* y, int32_t T, const int32_t* ids_host,
                    const uint8_t* prefill_host, int32_t bgmv_max_rank, void* ws,
@@ -295,15 +308,19 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
   if (rows == 0) return LORA_OK;
   const char* image_host = (const char*)meta_host + p.image_offset;
   const bool small = p.mfma_tiles == 0 && p.wave_tiles <= kArgTilesL && g.max_loras <= (1 << 28);
+  const void* image = ws;
   if (!small) {  // small plans travel in the kernel arguments instead
-    if (int32_t e = hip_ok(hipMemcpyAsync(ws, image_host, (size_t)p.image_bytes,
-                                          hipMemcpyHostToDevice, (hipStream_t)stream),
-                           "plan copy"))
+    if (const void* mapped = device_alias(image_host)) {
+      image = mapped;  // pinned staging: the kernels read the plan where it lies
+    } else if (int32_t e = hip_ok(hipMemcpyAsync(ws, image_host, (size_t)p.image_bytes,
+                                                 hipMemcpyHostToDevice, (hipStream_t)stream),
+                                  "plan copy")) {
       return e;
+    }
   }
   float* v = (float*)((char*)ws + v_off);
-  if (int32_t e = lora_plan_shrink(desc, x, A_pool, v, T, &p, ws, image_host, stream)) return e;
-  return lora_plan_expand(desc, v, B_pool, y, T, &p, ws, image_host, stream);
+  if (int32_t e = lora_plan_shrink(desc, x, A_pool, v, T, &p, image, image_host, stream)) return e;
+  return lora_plan_expand(desc, v, B_pool, y, T, &p, image, image_host, stream);
 }
 
 }  // extern "C"

@@ -94,22 +94,34 @@ StageLayout stage_layout(int32_t T, int32_t max_loras) {
   m.bgmv_tok = m.seg_ids + ml;
   m.bgmv_ids = m.bgmv_tok + t;
   m.image = align_up(m.bgmv_ids + t, 4);
-  // Every segment and every run of equal BGMV ids adds at most one partial
-  // tile: wave tiles <= ceil(T / 8) + 2 max_loras, MFMA tiles <= ceil(T / 32)
-  // + max_loras.
+  // Every segment (at most max_loras) and every run of equal BGMV ids (at most
+  // max_loras) adds at most one partial tile: wave tiles <= ceil(T / 8) +
+  // 2 max_loras, MFMA tiles <= ceil(T / 64) + 2 max_loras.
   const int64_t wave = (t + LORA_PLAN_WAVE_ROWS - 1) / LORA_PLAN_WAVE_ROWS + 2 * ml;
-  const int64_t mfma = (t + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS + ml;
+  const int64_t mfma = (t + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS + 2 * ml;
   m.image_max_words = align_up(t, 4) + LORA_PLAN_WAVE_WORDS * wave + LORA_PLAN_MFMA_WORDS * mfma;
   m.total_words = m.image + m.image_max_words;
   return m;
 }
 
+static int32_t env_rows(const char* name, long dflt) {
+  const char* e = std::getenv(name);
+  const long x = e ? std::strtol(e, nullptr, 10) : dflt;
+  return (int32_t)(x < 1 ? 1 : x > INT32_MAX ? INT32_MAX : x);
+}
+
 int32_t sgmv_mfma_min_rows() {
-  static const int32_t v = [] {
-    const char* e = std::getenv("LORA_SGMV_MFMA_MIN_ROWS");
-    const long x = e ? std::strtol(e, nullptr, 10) : 16;
-    return (int32_t)(x < 1 ? 1 : x > INT32_MAX ? INT32_MAX : x);
-  }();
+  static const int32_t v = env_rows("LORA_SGMV_MFMA_MIN_ROWS", 16);
+  return v;
+}
+
+int32_t bgmv_mfma_min_rows() {
+  static const int32_t v = env_rows("LORA_BGMV_MFMA_MIN_ROWS", 48);
+  return v;
+}
+
+int32_t bgmv_mfma_min_total() {
+  static const int32_t v = env_rows("LORA_BGMV_MFMA_MIN_TOTAL", 1024);
   return v;
 }
 
@@ -170,10 +182,16 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
 }
 
 // Tile plan ([TGI] step 4: rows grouped by adapter, one adapter per tile).
-// Short SGMV segments and the runs of equal ids among the BGMV rows (already
-// sorted by id) are cut into wavefront tiles of LORA_PLAN_WAVE_ROWS rows; SGMV
-// segments of at least mfma_min_rows rows (bf16) into MFMA tiles of
-// LORA_PLAN_MFMA_ROWS rows.  v row numbering: SGMV rows first, then BGMV rows.
+// Runs of rows of one adapter (SGMV segments, and the runs of equal ids among
+// the BGMV rows, which the builder sorts by id) are cut into tiles:
+//   - MFMA tiles of LORA_PLAN_MFMA_ROWS rows (bf16 pools): SGMV segments of at
+//     least sgmv_mfma_min_rows rows, and BGMV runs of at least
+//     bgmv_mfma_min_rows rows when such runs hold at least bgmv_mfma_min_total
+//     rows of the batch (a large decode batch; in a small one the extra MFMA
+//     launches cost more than the dense tiles save);
+//   - wavefront tiles of LORA_PLAN_WAVE_ROWS rows: every other run.
+// v row numbering: SGMV rows first, then BGMV rows; perm holds the token of
+// every v row.
 int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* prefill,
                   int32_t bgmv_max_rank, int32_t* stage, lora_plan* p) {
   const StageLayout sl = stage_layout(T, g.max_loras);
@@ -186,11 +204,29 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   m.bgmv_ids = stage + sl.bgmv_ids;
   if (int32_t e = build_meta_core(ids, prefill, T, g.max_loras, g.R, bgmv_max_rank, &m)) return e;
   const int32_t ns = m.num_sgmv_rows, nb = m.num_bgmv_rows;
-  const int32_t thr = g.dtype == LORA_BF16 ? sgmv_mfma_min_rows() : INT32_MAX;
+  const bool bf = g.dtype == LORA_BF16;
+  const int32_t thr = bf ? sgmv_mfma_min_rows() : INT32_MAX;
+  // end of the BGMV run starting at row i
+  auto run_end = [&](int32_t i) {
+    int32_t j = i + 1;
+    while (j < nb && m.bgmv_ids[j] == m.bgmv_ids[i]) ++j;
+    return j;
+  };
+  int32_t bthr = INT32_MAX;
+  if (bf) {
+    int64_t long_rows = 0;
+    for (int32_t i = 0; i < nb;) {
+      const int32_t j = run_end(i);
+      if (j - i >= bgmv_mfma_min_rows()) long_rows += j - i;
+      i = j;
+    }
+    if (long_rows > 0 && long_rows >= bgmv_mfma_min_total()) bthr = bgmv_mfma_min_rows();
+  }
   int32_t* img = stage + sl.image;
-  const int64_t off_wave = align_up(ns, 4);
+  const int64_t off_wave = align_up((int64_t)ns + nb, 4);
   std::memcpy(img, m.sgmv_perm, sizeof(int32_t) * (size_t)ns);
-  for (int64_t i = ns; i < off_wave; ++i) img[i] = -1;
+  std::memcpy(img + ns, m.bgmv_tok, sizeof(int32_t) * (size_t)nb);
+  for (int64_t i = (int64_t)ns + nb; i < off_wave; ++i) img[i] = -1;
   int32_t* wave = img + off_wave;
   int64_t nw = 0;
   auto emit_wave = [&](int32_t slot, int32_t first, int32_t rows, const int32_t* tok) {
@@ -210,26 +246,33 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
       emit_wave(m.seg_ids[s], st + j, std::min(LORA_PLAN_WAVE_ROWS, ln - j), m.sgmv_perm + st + j);
   }
   for (int32_t i = 0; i < nb;) {
-    int32_t j = i + 1;
-    while (j < nb && m.bgmv_ids[j] == m.bgmv_ids[i]) ++j;
-    for (int32_t k = i; k < j; k += LORA_PLAN_WAVE_ROWS)
-      emit_wave(m.bgmv_ids[i], ns + k, std::min(LORA_PLAN_WAVE_ROWS, j - k), m.bgmv_tok + k);
+    const int32_t j = run_end(i);
+    if (j - i < bthr) {
+      for (int32_t k = i; k < j; k += LORA_PLAN_WAVE_ROWS)
+        emit_wave(m.bgmv_ids[i], ns + k, std::min(LORA_PLAN_WAVE_ROWS, j - k), m.bgmv_tok + k);
+    }
     i = j;
   }
   const int64_t off_mfma = off_wave + nw * LORA_PLAN_WAVE_WORDS;
   int32_t* mt = img + off_mfma;
   int64_t nm = 0;
-  for (int32_t s = 0; s < m.num_segs; ++s) {
-    const int32_t st = m.seg_starts[s], ln = m.seg_lens[s];
-    if (ln < thr) continue;
-    for (int32_t j = 0; j < ln; j += LORA_PLAN_MFMA_ROWS) {
+  auto emit_mfma = [&](int32_t slot, int32_t first, int32_t len) {
+    for (int32_t j = 0; j < len; j += LORA_PLAN_MFMA_ROWS) {
       int32_t* r = mt + nm * LORA_PLAN_MFMA_WORDS;
-      r[0] = m.seg_ids[s];
-      r[1] = std::min(LORA_PLAN_MFMA_ROWS, ln - j);
-      r[2] = st + j;
+      r[0] = slot;
+      r[1] = std::min(LORA_PLAN_MFMA_ROWS, len - j);
+      r[2] = first + j;
       r[3] = 0;
       ++nm;
     }
+  };
+  for (int32_t s = 0; s < m.num_segs; ++s) {
+    if (m.seg_lens[s] >= thr) emit_mfma(m.seg_ids[s], m.seg_starts[s], m.seg_lens[s]);
+  }
+  for (int32_t i = 0; i < nb;) {
+    const int32_t j = run_end(i);
+    if (j - i >= bthr) emit_mfma(m.bgmv_ids[i], ns + i, j - i);
+    i = j;
   }
   const int64_t words = off_mfma + nm * LORA_PLAN_MFMA_WORDS;
   // K split of the MFMA shrink: double it while the launch has fewer than two
@@ -252,7 +295,7 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   p->mfma_tiles = (int32_t)nm;
   p->mfma_min_rows = thr;
   p->ksplit = ksplit;
-  p->reserved = 0;
+  p->bgmv_mfma_min_rows = bthr;
   p->image_offset = sl.image * 4;
   p->image_bytes = words * 4;
   p->off_perm = 0;

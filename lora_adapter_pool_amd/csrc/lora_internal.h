@@ -45,6 +45,12 @@ int64_t align_up(int64_t v, int64_t a);
 // SGMV segments at least this long run on MFMA tiles (bf16 pools); the
 // environment variable LORA_SGMV_MFMA_MIN_ROWS overrides the default of 16.
 int32_t sgmv_mfma_min_rows();
+// BGMV runs of one adapter at least bgmv_mfma_min_rows long (default 48,
+// LORA_BGMV_MFMA_MIN_ROWS) run on MFMA tiles when such runs hold at least
+// bgmv_mfma_min_total rows of the batch (default 1024,
+// LORA_BGMV_MFMA_MIN_TOTAL).
+int32_t bgmv_mfma_min_rows();
+int32_t bgmv_mfma_min_total();
 
 // Builder core (no argument checks beyond what lora_build_meta does).
 int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,

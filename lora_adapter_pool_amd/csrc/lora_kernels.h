@@ -71,8 +71,7 @@ struct TilePlan {
   int32_t mfma_tiles;
   const int32_t* wave_host;  // host copy of the wave records, or nullptr
   int32_t ksplit;            // partials of the MFMA shrink (v holds ksplit x num_rows rows)
-  int32_t num_sgmv_rows;  // rows of perm; MFMA tiles lie inside them
-  int32_t num_rows;       // v rows: SGMV rows + BGMV rows
+  int32_t num_rows;          // v rows (SGMV rows, then BGMV rows) = entries of perm
 };
 
 // Enqueue the shrink / expand of one row list (segments or rows) on `st`;

@@ -1265,7 +1265,7 @@ int32_t run_expand(const Geo& g, const float* v, const void* B, void* y, RowList
 static void plan_lists(const TilePlan& p, RowList& Lw, RowList& Lm) {
   Lw = RowList{p.perm, nullptr, nullptr, nullptr, nullptr, p.wave, 0, p.num_rows, p.wave_tiles,
                0, INT32_MAX};
-  Lm = RowList{p.perm, nullptr, nullptr, nullptr, nullptr, p.mfma, 0, p.num_sgmv_rows,
+  Lm = RowList{p.perm, nullptr, nullptr, nullptr, nullptr, p.mfma, 0, p.num_rows,
                p.mfma_tiles, 0, INT32_MAX};
 }
 

@@ -177,9 +177,10 @@ def test_apply_validation_before_hip():
     mh_need = L.lora_apply_host_meta_bytes(d, T)
     # staging: builder arrays (3T + 3 max_loras words, padded to 4), then the
     # plan image: perm (T, padded to 4), <= ceil(T/8) + 2 max_loras wave tiles
-    # of 16 words, <= ceil(T/64) + max_loras MFMA tiles of 4 words
+    # of 16 words, <= ceil(T/64) + 2 max_loras MFMA tiles of 4 words (each
+    # segment and each BGMV run adds at most one partial tile)
     up4 = lambda n: (n + 3) // 4 * 4  # noqa: E731
-    image = up4(T) + 16 * (-(-T // 8) + 2 * 4) + 4 * (-(-T // 64) + 4)
+    image = up4(T) + 16 * (-(-T // 8) + 2 * 4) + 4 * (-(-T // 64) + 2 * 4)
     assert mh_need == 4 * (up4(3 * T + 3 * 4) + image)
     # v: up to 4 K-split partials of T rows x S x R fp32
     assert ws_need == ((4 * image + 255) // 256) * 256 + 4 * T * 16 * 4

@@ -368,3 +368,65 @@ def test_small_plan_by_value(dtype, T, n_adapters):
         check_rows(wl, yd, label=f"small plan by_value={by_value} {dtype}")
         outs.append(yd.clone())
     assert torch.equal(_bits(outs[0]), _bits(outs[1]))
+
+
+def test_large_decode_batch_mfma_tiles():
+    """A large decode batch with long runs of one adapter: those runs go to MFMA
+    tiles (v rows in the BGMV range, K split into partials), short runs stay on
+    wavefront tiles; integer inputs make every output exact."""
+    wl = _integer_workload("bf16", seed=7, K=1032, T=1500, lens=())
+    rng = np.random.default_rng(77)
+    # 1500 decode rows: adapters 0..3 on long runs (several 64-row tiles and a
+    # ragged tail after sorting), adapter 4 on a short run, some rows without
+    ids = rng.choice(np.array([0, 1, 2, 3, 4, -1], np.int32), size=wl.T,
+                     p=[0.3, 0.25, 0.2, 0.2, 0.02, 0.03]).astype(np.int32)
+    wl = dataclasses.replace(wl, ids=ids, prefill=np.zeros(wl.T, np.uint8))
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    plan, _, views = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert plan["num_sgmv_rows"] == 0 and plan["mfma_tiles"] >= 20 and plan["wave_tiles"] >= 1
+    assert plan["bgmv_mfma_min_rows"] == 48 and plan["ksplit"] >= 2
+    exp = _exact_expected(wl)
+    y = run_apply(wl).float().cpu().numpy()
+    bad = np.argwhere(y != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
+def test_large_decode_batch_random_values():
+    """Same routing on random values, within tolerance of the fp64 oracle."""
+    wl = W.config_bgmv_decode(seed=3, T=1200, K=1040, O=520, n_adapters=3, rank=32,
+                              alpha=64.0, p_none=0.05)
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    plan, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] > 0 and plan["num_sgmv_rows"] == 0
+    y = run_apply(wl)
+    check_rows(wl, y, label="large decode batch on MFMA tiles")
+
+
+@pytest.mark.parametrize("offset", [0, 48])
+def test_plan_staging_pinned_and_pageable(offset):
+    """A plan too large for the kernel arguments reaches the kernels either in
+    place (pinned staging, also at an offset inside a larger pinned buffer) or
+    through a copy into the workspace (pageable staging): same bits, within
+    tolerance of the oracle."""
+    import torch
+    wl = W.config_mlp_mixed(seed=4, n_prefill=3, len_lo=30, len_hi=140, n_decode=40, hidden=264,
+                            inter=520, n_adapters=5, rank_choices=(16, 64))[0]
+    pool = make_pool(wl)
+    plan, _, _ = L.lora_apply_plan(pool.desc, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] > 0 and plan["wave_tiles"] > 0
+    ws = torch.empty(L.lora_apply_workspace_bytes(pool.desc, wl.T), dtype=torch.uint8, device="cuda")
+    need = L.lora_apply_host_meta_bytes(pool.desc, wl.T)
+    pinned = torch.empty(need + 64 + offset, dtype=torch.uint8, pin_memory=True)
+    base = (-pinned.data_ptr()) % 16
+    pinned_view = pinned[base + offset: base + offset + need]
+    raw = np.zeros(need + 64, np.uint8)
+    page = raw[(-raw.ctypes.data) % 16:][:need]
+    outs = []
+    for mh in (pinned_view, page):
+        xd, yd = to_dev(wl.x, wl.dtype), to_dev(wl.y_in, wl.dtype)
+        L.lora_apply(pool.desc, pool.A, pool.B, xd, yd, wl.T, wl.ids, wl.prefill, 0, ws, ws.numel(),
+                     mh, need)
+        torch.cuda.synchronize()
+        check_rows(wl, yd, label=f"staging {'pinned' if mh is pinned_view else 'pageable'}")
+        outs.append(yd.clone())
+    assert torch.equal(_bits(outs[0]), _bits(outs[1]))

@@ -9,6 +9,20 @@ import lora_adapter_pool_amd as L
 import workloads as W
 
 WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS, MAX_KSPLIT = 8, 64, 16, 4
+BGMV_MFMA_MIN_ROWS, BGMV_MFMA_MIN_TOTAL = 48, 1024
+INT32_MAX = np.iinfo(np.int32).max
+
+
+def _bgmv_runs(b):
+    """(start, length) of each run of equal ids among the BGMV rows."""
+    runs, i = [], 0
+    while i < b.size:
+        j = i
+        while j < b.size and b[j] == b[i]:
+            j += 1
+        runs.append((i, j - i))
+        i = j
+    return runs
 
 
 def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
@@ -19,16 +33,28 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
     ns, nb = m["sgmv_perm"].size, m["bgmv_tok"].size
     assert (p["num_sgmv_rows"], p["num_bgmv_rows"], p["num_segs"]) == (ns, nb, m["seg_ids"].size)
     assert p["image_offset"] % 16 == 0 and p["off_wave"] % 4 == 0
-    np.testing.assert_array_equal(v["perm"], m["sgmv_perm"])
     # token and adapter of every v row, in the builder's order
     row_tok = np.concatenate([m["sgmv_perm"], m["bgmv_tok"]]).astype(np.int64)
+    np.testing.assert_array_equal(v["perm"], row_tok)
     row_ids = ids[row_tok] if row_tok.size else np.zeros(0, np.int32)
     seg_len_of_row = np.zeros(ns, np.int64)
     for st, ln in zip(m["seg_starts"], m["seg_lens"]):
         seg_len_of_row[st:st + ln] = ln
     bf16 = desc.dtype == L.LORA_BF16
-    thr = MFMA_MIN_ROWS if bf16 else np.iinfo(np.int32).max
-    assert p["mfma_min_rows"] == (MFMA_MIN_ROWS if bf16 else np.iinfo(np.int32).max)
+    thr = MFMA_MIN_ROWS if bf16 else INT32_MAX
+    assert p["mfma_min_rows"] == thr
+    # BGMV runs take MFMA tiles only in bf16 batches whose long runs hold many rows
+    runs = _bgmv_runs(m["bgmv_ids"])
+    long_rows = sum(ln for _, ln in runs if ln >= BGMV_MFMA_MIN_ROWS)
+    bthr = BGMV_MFMA_MIN_ROWS if bf16 and long_rows >= max(1, BGMV_MFMA_MIN_TOTAL) else INT32_MAX
+    assert p["bgmv_mfma_min_rows"] == bthr
+    run_len_of_row = np.zeros(nb, np.int64)
+    for st, ln in runs:
+        run_len_of_row[st:st + ln] = ln
+    # length of the run (segment or BGMV run) each v row belongs to, and whether
+    # that run goes to MFMA tiles
+    run_len = np.concatenate([seg_len_of_row, run_len_of_row])
+    is_mfma = np.concatenate([seg_len_of_row >= thr, run_len_of_row >= bthr])
 
     shrink_cover = np.zeros(ns + nb, np.int64)
     for rec in v["wave"]:
@@ -38,14 +64,16 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
         np.testing.assert_array_equal(rec[4:4 + rows], row_tok[first:first + rows])
         assert np.all(rec[4 + rows:] == -1)
         assert np.all(row_ids[first:first + rows] == slot)
-        if first < ns:  # SGMV tiles stay inside the SGMV rows, short segments only
-            assert first + rows <= ns and np.all(seg_len_of_row[first:first + rows] < thr)
+        if first < ns:  # SGMV tiles stay inside the SGMV rows
+            assert first + rows <= ns
+        assert not np.any(is_mfma[first:first + rows])
         shrink_cover[first:first + rows] += 1
     for rec in v["mfma"]:
         slot, rows, first, zero = (int(x) for x in rec)
-        assert bf16 and zero == 0 and 1 <= rows <= MFMA_ROWS and first + rows <= ns
+        assert bf16 and zero == 0 and 1 <= rows <= MFMA_ROWS and first + rows <= ns + nb
+        assert first >= ns or first + rows <= ns  # never across the SGMV / BGMV boundary
         assert np.all(row_ids[first:first + rows] == slot)
-        assert np.all(seg_len_of_row[first:first + rows] >= thr)
+        assert np.all(is_mfma[first:first + rows])
         shrink_cover[first:first + rows] += 1
     np.testing.assert_array_equal(shrink_cover, np.ones(ns + nb, np.int64))
     # tile counts: each segment / BGMV run cut into ceil(len / tile rows) pieces
@@ -55,14 +83,11 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
             want_mfma += -(-int(ln) // MFMA_ROWS)
         else:
             want_wave += -(-int(ln) // WAVE_ROWS)
-    b = m["bgmv_ids"]
-    i = 0
-    while i < nb:
-        j = i
-        while j < nb and b[j] == b[i]:
-            j += 1
-        want_wave += -(-(j - i) // WAVE_ROWS)
-        i = j
+    for _, ln in runs:
+        if ln >= bthr:
+            want_mfma += -(-ln // MFMA_ROWS)
+        else:
+            want_wave += -(-ln // WAVE_ROWS)
     assert (p["wave_tiles"], p["mfma_tiles"]) == (want_wave, want_mfma)
     assert p["image_bytes"] == 4 * (p["off_mfma"] + 4 * p["mfma_tiles"])
     # K split: doubled while the MFMA shrink has < 512 workgroups and each
@@ -101,6 +126,9 @@ def test_plan_fuzz():
     for it in range(300):
         ml = int(rng.integers(1, 70))
         T = int(rng.integers(0, 400))
+        if it % 10 == 0:  # large decode batches: long BGMV runs may take MFMA tiles
+            ml = int(rng.integers(1, 24))
+            T = int(rng.integers(1000, 3000))
         R = int(rng.choice([8, 16, 64, 80]))
         dtype = "bf16" if it % 3 else "f32"
         d = L.make_desc(dtype, ml, R, 64, [64, 32])
@@ -109,6 +137,22 @@ def test_plan_fuzz():
             ids = np.sort(ids)
         pre = (rng.random(T) < rng.random()).astype(np.uint8)
         _check_plan(d, ids, pre if it % 5 else None, bgmv_max_rank=int(rng.choice([0, 8, 128])))
+
+
+@pytest.mark.parametrize("T,n,want_mfma", [(64, 8, False), (512, 4, False), (1024, 8, True),
+                                           (1024, 64, False), (4096, 64, True)])
+def test_plan_bgmv_runs_on_mfma(T, n, want_mfma):
+    """Decode batches: sorted runs of one adapter go to MFMA tiles only when
+    the batch is large and its runs are long."""
+    wl = W.config_bgmv_decode(seed=1, T=T, K=256, O=256, n_adapters=n, rank=16, p_none=0.0)
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    p = _check_plan(d, wl.ids, wl.prefill)
+    assert (p["mfma_tiles"] > 0) == want_mfma
+    assert (p["bgmv_mfma_min_rows"] != INT32_MAX) == want_mfma
+    # an fp32 pool never uses MFMA tiles
+    d32 = L.make_desc("f32", wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    p32 = _check_plan(d32, wl.ids, wl.prefill)
+    assert p32["mfma_tiles"] == 0
 
 
 def test_plan_errors():
