@@ -86,7 +86,7 @@ def algorithmic(wl):
     flops = 2 * Ta * R * (S * K + O)
     return {"Ta": Ta, "n_act": nact, "shrink_bytes": shrink, "expand_bytes": expand,
             "bytes": shrink + expand, "flops": flops, "shrink_flops": 2 * Ta * R * S * K,
-            "expand_flops": 2 * Ta * R * O}
+            "expand_flops": 2 * Ta * R * O, "apply_bytes": shrink + expand, "apply_flops": flops}
 
 
 class Setup:
@@ -171,12 +171,19 @@ class Setup:
         self.stage_ev[j] = ev
 
     def kernel_launch(self, which, i, stream_ptr):
-        """One launch group of the plan: 'shrink' or 'expand' (replica i)."""
+        """One launch group of the plan (replica i): 'shrink', 'expand', or
+        'apply' (both stages in the one launch lora_apply makes for a small
+        decode plan)."""
         L = self.L
         lib = L.lib()
         r = i % self.nrep
         d = ctypes.byref(self.desc)
-        if which == "shrink":
+        if which == "apply":
+            st = lib.lora_plan_apply(d, self.px[r], self.pA[r], self.pB[r], self.py[r], self.T,
+                                     ctypes.byref(self.plan), self.image.data_ptr(),
+                                     self.image_host.ctypes.data, self.ws.data_ptr(),
+                                     self.ws_bytes, stream_ptr)
+        elif which == "shrink":
             st = lib.lora_plan_shrink(d, self.px[r], self.pA[r], self.v.data_ptr(), self.T,
                                       ctypes.byref(self.plan), self.image.data_ptr(),
                                       self.image_host.ctypes.data, stream_ptr)
@@ -292,6 +299,15 @@ def load_traffic(stage, workload):
         return None
 
 
+def one_launch(wl, p):
+    """Whether lora_apply runs this batch's plan as one launch: no MFMA tiles,
+    at most 12 wavefront tiles, a bf16 pool and max_lora_rank <= 32."""
+    if os.environ.get("LORA_ONEPASS_DECODE", "1").startswith("0"):
+        return False
+    return (wl.dtype == "bf16" and not p["mfma_tiles"] and 0 < p["wave_tiles"] <= 12
+            and wl.max_loras <= 2 ** 28 and wl.max_lora_rank <= 32)
+
+
 def stage_kernels(wl):
     """Kernel names of each launch group for a workload's batch (host-side
     plan only, no GPU)."""
@@ -300,6 +316,11 @@ def stage_kernels(wl):
     p, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
     tag = "unsigned short" if wl.dtype == "bf16" else "float"
     kb = 16 if wl.max_lora_rank <= 16 else 64
+    if one_launch(wl, p):
+        nt = 1 if wl.max_lora_rank <= 16 else 2
+        share = -(-(-(-wl.in_features // 32)) // 8)
+        cb = min(-(-share // 4) * 4, 16 if nt == 1 else 8)
+        return {"apply": [f"decode_onepass_kernel<{nt}, {cb}, 3>"]}
     out = {"shrink": [], "expand": []}
     if p["mfma_tiles"]:
         out["shrink"].append("shrink_mfma_kernel<2>")

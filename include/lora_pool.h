@@ -215,9 +215,9 @@ int32_t lora_bgmv_expand(const lora_pool_desc* desc, const float* v, const void*
 
 /* ------------------------------------------------------------ dispatcher */
 
-/* Device workspace lora_apply needs for a batch of T tokens (v for every row
- * plus the device copy of the tile plan), and the host staging size for the
- * plan.  Negative lora_status on an invalid descriptor or T < 0. */
+/* Device workspace lora_apply needs for a batch of T tokens (the device copy
+ * of the tile plan, then v for every row and K split), and the host staging
+ * size for the plan.  Negative lora_status on an invalid descriptor or T < 0. */
 int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T);
 int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
 
@@ -307,9 +307,27 @@ int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void*
                          int32_t T, const lora_plan* plan, const void* image,
                          const void* image_host, void* stream);
 
+/* Both stages of a plan on `stream` ([TGI] step 4: shrink, then expand), so
+ * one plan serves every layer of a batch: y[t] += B_a (A_a x[t]) for every
+ * row of every tile, the result of lora_plan_shrink followed by
+ * lora_plan_expand.
+ *   image, image_host: as for lora_plan_shrink.
+ *   ws: device workspace of >= lora_apply_workspace_bytes(desc, T) bytes,
+ *     16-byte aligned (v of the two-launch form).
+ * A plan of at most 12 wavefront tiles (and no MFMA tiles) on a bf16 pool with
+ * max_lora_rank <= 32 runs as ONE launch in which every workgroup computes
+ * its tile's v (MFMA) and applies it to its output columns; otherwise the stages are lora_plan_shrink and
+ * lora_plan_expand.  LORA_ONEPASS_DECODE=0 in the environment turns the
+ * one-launch form off.  Returns as lora_plan_shrink, plus LORA_E_WORKSPACE
+ * for a short ws. */
+int32_t lora_plan_apply(const lora_pool_desc* desc, const void* x, const void* A_pool,
+                        const void* B_pool, void* y, int32_t T, const lora_plan* plan,
+                        const void* image, const void* image_host, void* ws, int64_t ws_bytes,
+                        void* stream);
+
 /* The whole delta path for one batch ([TGI] step 4; [QA] direct answer):
- * lora_apply_plan into meta_host, then lora_plan_shrink and lora_plan_expand
- * on `stream`, updating y in place.  Rows with id -1 are never read or written.
+ * lora_apply_plan into meta_host, then lora_plan_apply on `stream`, updating y
+ * in place.  Rows with id -1 are never read or written.
  * The plan reaches the kernels in one of three ways: a small plan goes in the
  * kernel arguments; otherwise, if meta_host is pinned (hipHostMalloc), the
  * kernels read the plan's image from meta_host itself; otherwise the image is

@@ -102,6 +102,8 @@ _SIGNATURES = {
     "lora_apply_plan": (_I32, [_DP, _I32, _P, _P, _I32, _P, _I64, ctypes.POINTER(lora_plan)]),
     "lora_plan_shrink": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P]),
     "lora_plan_expand": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P]),
+    "lora_plan_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P,
+                               _I64, _P]),
     "lora_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P, _I64, _P]),
 }
 
@@ -318,6 +320,15 @@ def lora_plan_expand(desc, v, B_pool, y, T, plan, image, image_host=None, stream
     _check(lib().lora_plan_expand(ctypes.byref(desc), _ptr(v), _ptr(B_pool), _ptr(y), int(T),
                                   ctypes.byref(p), _ptr(image), _ptr(image_host),
                                   _stream(stream)))
+
+
+def lora_plan_apply(desc, x, A_pool, B_pool, y, T, plan, image, image_host=None, ws=None,
+                    ws_bytes=0, stream=None) -> None:
+    """Both stages of a plan (one launch for small plans); ws as for lora_apply."""
+    p = plan if isinstance(plan, lora_plan) else plan_struct(plan)
+    _check(lib().lora_plan_apply(ctypes.byref(desc), _ptr(x), _ptr(A_pool), _ptr(B_pool), _ptr(y),
+                                 int(T), ctypes.byref(p), _ptr(image), _ptr(image_host), _ptr(ws),
+                                 int(ws_bytes), _stream(stream)))
 
 
 def lora_apply(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgmv_max_rank, ws,

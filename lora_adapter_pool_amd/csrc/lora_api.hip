@@ -267,6 +267,33 @@ int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void*
   return run_plan_expand(g, v, B_pool, y, tp, (hipStream_t)stream);
 }
 
+int32_t lora_plan_apply(const lora_pool_desc* desc, const void* x, const void* A_pool,
+                        const void* B_pool, void* y, int32_t T, const lora_plan* plan,
+                        const void* image, const void* image_host, void* ws, int64_t ws_bytes,
+                        void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  TilePlan tp;
+  if (int32_t e = plan_view(g, plan, image, image_host, &tp)) return e;
+  if (T == 0 || (tp.wave_tiles == 0 && tp.mfma_tiles == 0)) return LORA_OK;
+  if (int32_t e = need_ptr(A_pool, "A_pool")) return e;
+  if (int32_t e = need_ptr(B_pool, "B_pool")) return e;
+  if (int32_t e = need_ptr(x, "x")) return e;
+  if (int32_t e = need_ptr(y, "y")) return e;
+  if (int32_t e = need_ptr(ws, "ws")) return e;
+  const WorkspaceLayout wl = workspace_layout(g, T);
+  if (ws_bytes < wl.total)
+    return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
+                (long long)wl.total);
+  if ((int64_t)tp.ksplit * tp.num_rows > (int64_t)LORA_PLAN_MAX_KSPLIT * T)
+    return fail(LORA_E_ARG, "malformed plan (%d rows for %d tokens)", tp.num_rows, T);
+  g.T = T;
+  return run_plan_apply(g, x, A_pool, B_pool, y, tp, (float*)((char*)ws + wl.v),
+                        (hipStream_t)stream);
+}
+
 // `host` itself when it is pinned host memory (hipHostMalloc) that the device
 // reaches at the same address, else nullptr (pageable memory, or a mapping at
 // another address: the caller then copies).  Kernels that read a plan there
@@ -294,12 +321,10 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
   if (int32_t e = need_ptr(x, "x")) return e;
   if (int32_t e = need_ptr(y, "y")) return e;
   if (int32_t e = need_ptr(ws, "ws")) return e;
-  const StageLayout sl = stage_layout(T, g.max_loras);
-  const int64_t v_off = align_up(sl.image_max_words * 4, 256);
-  const int64_t need_ws = v_off + (int64_t)LORA_PLAN_MAX_KSPLIT * T * g.S * g.R * 4;
-  if (ws_bytes < need_ws)
+  const WorkspaceLayout wl = workspace_layout(g, T);
+  if (ws_bytes < wl.total)
     return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
-                (long long)need_ws);
+                (long long)wl.total);
   lora_plan p;
   if (int32_t e = lora_apply_plan(desc, T, ids_host, prefill_host, bgmv_max_rank, meta_host,
                                   meta_host_bytes, &p))
@@ -318,9 +343,8 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
       return e;
     }
   }
-  float* v = (float*)((char*)ws + v_off);
-  if (int32_t e = lora_plan_shrink(desc, x, A_pool, v, T, &p, image, image_host, stream)) return e;
-  return lora_plan_expand(desc, v, B_pool, y, T, &p, image, image_host, stream);
+  return lora_plan_apply(desc, x, A_pool, B_pool, y, T, &p, image, image_host, ws, ws_bytes,
+                         stream);
 }
 
 }  // extern "C"

@@ -110,6 +110,13 @@ static int32_t env_rows(const char* name, long dflt) {
   return (int32_t)(x < 1 ? 1 : x > INT32_MAX ? INT32_MAX : x);
 }
 
+WorkspaceLayout workspace_layout(const Geo& g, int32_t T) {
+  WorkspaceLayout w;
+  w.v = align_up(stage_layout(T, g.max_loras).image_max_words * 4, 256);
+  w.total = w.v + (int64_t)LORA_PLAN_MAX_KSPLIT * T * g.S * g.R * 4;
+  return w;
+}
+
 int32_t sgmv_mfma_min_rows() {
   static const int32_t v = env_rows("LORA_SGMV_MFMA_MIN_ROWS", 16);
   return v;
@@ -376,8 +383,7 @@ int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T) {
   int32_t st = check_desc(desc, &g);
   if (st) return st;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
-  const int64_t img = align_up(stage_layout(T, g.max_loras).image_max_words * 4, 256);
-  return img + (int64_t)LORA_PLAN_MAX_KSPLIT * T * g.S * g.R * 4;
+  return workspace_layout(g, T).total;
 }
 
 int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* ids_host,

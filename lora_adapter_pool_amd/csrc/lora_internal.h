@@ -40,6 +40,13 @@ struct StageLayout {
   int64_t total_words;
 };
 StageLayout stage_layout(int32_t T, int32_t max_loras);
+
+// lora_apply's device workspace (byte offsets): the plan image (when it is
+// copied), then v (LORA_PLAN_MAX_KSPLIT partials of T rows x S x R fp32).
+struct WorkspaceLayout {
+  int64_t v, total;
+};
+WorkspaceLayout workspace_layout(const Geo& g, int32_t T);
 int64_t align_up(int64_t v, int64_t a);
 
 // SGMV segments at least this long run on MFMA tiles (bf16 pools); the

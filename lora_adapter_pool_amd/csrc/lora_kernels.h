@@ -86,6 +86,13 @@ int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, co
                         hipStream_t st);
 int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, const TilePlan& p,
                         hipStream_t st);
+// Both stages of a plan: one launch (each workgroup computes its tile's v with
+// MFMA and applies it to its columns) for bf16 decode plans of at most
+// kArgTilesS tiles with R <= 32, else run_plan_shrink then run_plan_expand
+// (v: the plan's rows).
+bool plan_is_onepass(const Geo& g, const TilePlan& p);
+int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
+                       const TilePlan& p, float* v, hipStream_t st);
 int32_t run_pool_load(const Geo& g, void* A_slot_slice, void* B_slot_slice, const void* Asrc,
                       const void* Bsrc, int r, int out_s, float scale, hipStream_t st);
 

@@ -570,6 +570,158 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
   }
 }
 
+// ------------------------------------------ decode in one launch (bf16, MFMA)
+//
+// For small decode plans (records passed by value, bf16, R <= 32): a
+// workgroup computes its tile's v = x A_a^T itself and applies it to
+// kOnepassCols output columns of one slice, so no workgroup depends on
+// another and one launch covers both stages.  Each column chunk of a tile
+// re-reads the tile's x rows and the adapter's A rows (from L2 after the
+// first); for a decode batch those are a few hundred KB, against the cost of a
+// second launch and a grid-wide dependency.
+//
+// grid = tiles * column chunks, 512 threads (8 waves).
+//   shrink: D[m][n] = sum_k x[tok[m]][k] A[a][s][n][k] as v_mfma_f32_16x16x32_bf16
+//           tiles (rows m = tokens, 8 of 16 used; columns n = ranks, NT tiles
+//           of 16), the 32-wide K chunks dealt round-robin over the waves, CB
+//           chunks per wave loaded at once (CB = the wave's share of K, up to
+//           16 / NT); the waves' partial tiles are summed in a fixed order in
+//           LDS.
+// Every workgroup pulls the adapter's A rows and the tile's x rows through one
+// compute unit, whose few outstanding misses bound the rate, so the form only
+// pays where a second launch costs more: plans of at most kArgTilesS tiles.
+//   expand: thread j owns column col0 + j: its B row (R bf16) comes straight
+//           from HBM (consecutive threads read consecutive rows), v from LDS
+//           (broadcast reads), and y of each valid row is read before the
+//           shrink and written once at the end.
+constexpr int kOnepassCols = 512;
+constexpr int kOnepassWaves = kOnepassCols / 64;
+
+template <int NT, int CB, int MODE>
+__global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    uint16_t* __restrict__ y, RowList L, Geo g, Chunks ch, PlanArg<MODE> pa) {
+  constexpr int TM = kWaveTileRows;
+  constexpr int RM = 16 * NT;          // ranks covered by the MFMA tiles (>= R)
+  static_assert(CB * (1 + NT) <= 32, "a batch keeps at most 32 loads per lane in flight");
+  static_assert(TM <= 16, "tile rows fit one MFMA tile");
+  __shared__ float red[kOnepassWaves][16][RM + 1];
+  __shared__ float vs[TM][RM];
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int f = bid / ch.total;
+  const int cidx = bid - f * ch.total;
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < LORA_MAX_SLICES; ++i)
+    if (i < g.S && cidx >= ch.start[i]) s = i;
+  const int col0 = (cidx - ch.start[s]) * kOnepassCols;
+  const int ncv = min(kOnepassCols, g.out[s] - col0);
+  TileRows<TM> tr;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.valid == 0) return;
+  const int a = tr.aid[0];  // one adapter per tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = g.R;
+
+  // shrink: lane l feeds row m = l % 16 and K offset kq = 8 (l / 16) of each
+  // 32-wide chunk; rows past the tile repeat row 0 and ranks past R repeat
+  // rank R - 1 (their outputs are never used)
+  const int m = lane & 15, kq = (lane >> 4) * 8;
+  int tk = tr.tok[0];
+#pragma unroll
+  for (int r = 1; r < TM; ++r)
+    if (m == r) tk = tr.tok[r];
+  const uint16_t* xp = x + (size_t)tk * g.K + kq;
+  const uint16_t* ap[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    ap[t] = A + ((size_t)(a * g.S + s) * R + min(16 * t + m, R - 1)) * g.K + kq;
+  f32x4 d[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = (g.K + 31) / 32;
+  u32x4 xv[CB], av[CB][NT];
+  uint32_t msk[CB];
+  // every load of a batch is issued before the first MFMA waits on one, so a
+  // batch costs one memory round trip
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int k = (c0 + u * kOnepassWaves) * 32;
+      const bool ok = k + kq < g.K;
+      const int kc = ok ? k : 0;
+      msk[u] = all_or_none(ok);
+      xv[u] = ld16(xp + kc);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) av[u][t] = ld16(ap[t] + kc);
+    }
+  };
+  auto mma_batch = [&] {
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const bf16x8 xo = __builtin_bit_cast(bf16x8, xv[u] & msk[u]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            xo, __builtin_bit_cast(bf16x8, av[u][t] & msk[u]), d[t], 0, 0, 0);
+    }
+  };
+  constexpr int kStride = kOnepassWaves * CB;
+  load_batch(wave);
+
+  // y of the tile's rows and this thread's B row (needed last, issued after
+  // the first batch so that waiting on the batch does not wait on them)
+  const int colc = tid < ncv ? tid : 0;
+  uint16_t* yb = y + g.off[s] + col0 + colc;
+  uint16_t yv[TM];
+#pragma unroll
+  for (int r = 0; r < TM; ++r) yv[r] = yb[(size_t)tr.tok[r] * g.O];
+  const uint16_t* Bg = B + ((size_t)a * g.O + g.off[s] + col0 + colc) * R;
+  u32x4 braw[2 * NT];
+#pragma unroll
+  for (int q = 0; q < 2 * NT; ++q) braw[q] = ld16(Bg + min(8 * q, R - 8)) & all_or_none(8 * q < R);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_batch();
+  for (int c0 = wave + kStride; c0 < nk; c0 += kStride) {
+    load_batch(c0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_batch();
+  }
+  // lane l holds D[4 (l / 16) + j][l % 16] of each rank tile
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wave][4 * (lane >> 4) + j][16 * t + m] = d[t][j];
+  __syncthreads();
+  if (tid < TM * RM) {
+    const int r = tid / RM, n = tid - r * RM;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kOnepassWaves; ++w) acc += red[w][r][n];
+    vs[r][n] = n < R ? acc : 0.f;
+  }
+  __syncthreads();
+
+  // expand
+  if (tid < ncv) {
+    float b[RM];
+#pragma unroll
+    for (int q = 0; q < 2 * NT; ++q) {
+      float t8[8];
+      El<uint16_t>::unpack({braw[q]}, t8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[8 * q + e] = t8[e];
+    }
+#pragma unroll
+    for (int r = 0; r < TM; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < RM; ++k) acc = fmaf(b[k], vs[r][k], acc);
+      if ((tr.valid >> r) & 1u)
+        yb[(size_t)tr.tok[r] * g.O] = El<uint16_t>::put(El<uint16_t>::get(yv[r]) + acc);
+    }
+  }
+}
+
 // Tile lookup of the MFMA kernels (segments or tile-list mode): first row r0
 // of the row list, row count and adapter slot, the same in every lane.  The
 // tile-list record is (slot, rows, first row, 0).
@@ -1153,6 +1305,38 @@ static int32_t launch_expand_wave(const Geo& g, const float* v, const void* B, v
                    : launch_expand_wave_kb<E, 64, MODE>(g, v, B, y, L, tiles, st, pa);
 }
 
+template <int NT, int CB, int MODE>
+static int32_t launch_onepass_cb(const Geo& g, const void* x, const void* A, const void* B,
+                                 void* y, const RowList& L, int tiles, hipStream_t st,
+                                 const PlanArg<MODE>& pa) {
+  const Chunks ch = make_chunks(g, kOnepassCols);
+  const int64_t grid = (int64_t)tiles * ch.total;
+  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
+  hipLaunchKernelGGL((decode_onepass_kernel<NT, CB, MODE>), dim3(grid_of(grid)),
+                     dim3(kOnepassCols), 0, st, (const uint16_t*)x, (const uint16_t*)A,
+                     (const uint16_t*)B, (uint16_t*)y, L, g, ch, pa);
+  return hip_check("decode_onepass launch");
+}
+
+// CB: 32-wide K chunks per wave per batch, the wave's share of K rounded up to
+// 4, at most 16 (R <= 16) or 8 (R <= 32)
+template <int MODE>
+static int32_t launch_onepass(const Geo& g, const void* x, const void* A, const void* B, void* y,
+                              const RowList& L, int tiles, hipStream_t st, const PlanArg<MODE>& pa) {
+  const int share = ((g.K + 31) / 32 + kOnepassWaves - 1) / kOnepassWaves;
+  const int cb = std::min((share + 3) / 4 * 4, g.R <= 16 ? 16 : 8);
+  if (g.R <= 16) {
+    switch (cb) {
+      case 4: return launch_onepass_cb<1, 4, MODE>(g, x, A, B, y, L, tiles, st, pa);
+      case 8: return launch_onepass_cb<1, 8, MODE>(g, x, A, B, y, L, tiles, st, pa);
+      case 12: return launch_onepass_cb<1, 12, MODE>(g, x, A, B, y, L, tiles, st, pa);
+      default: return launch_onepass_cb<1, 16, MODE>(g, x, A, B, y, L, tiles, st, pa);
+    }
+  }
+  return cb == 4 ? launch_onepass_cb<2, 4, MODE>(g, x, A, B, y, L, tiles, st, pa)
+                 : launch_onepass_cb<2, 8, MODE>(g, x, A, B, y, L, tiles, st, pa);
+}
+
 template <int MODE>
 static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, float* v,
                                   const RowList& L, int64_t tiles, int ksplit, int v_rows,
@@ -1333,6 +1517,33 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
     return e;
   return bf ? launch_expand_wave<uint16_t, kList>(g, v, B, y, Lw, p.wave_tiles, st)
             : launch_expand_wave<float, kList>(g, v, B, y, Lw, p.wave_tiles, st);
+}
+
+// One launch for both stages (decode_onepass_kernel) when the plan goes by
+// value in the small tier (at most kArgTilesS tiles), the pool is bf16 and
+// R <= 32; LORA_ONEPASS_DECODE=0 turns it off.
+static bool onepass_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("LORA_ONEPASS_DECODE");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
+bool plan_is_onepass(const Geo& g, const TilePlan& p) {
+  return onepass_enabled() && g.dtype == LORA_BF16 && small_plan(p, g) && p.wave_tiles > 0 &&
+         p.wave_tiles <= kArgTilesS && g.R <= 32;
+}
+
+int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
+                       const TilePlan& p, float* v, hipStream_t st) {
+  if (!plan_is_onepass(g, p)) {
+    if (int32_t e = run_plan_shrink(g, x, A, v, p, st)) return e;
+    return run_plan_expand(g, v, B, y, p, st);
+  }
+  RowList Lw, Lm;
+  plan_lists(p, Lw, Lm);
+  return launch_onepass<kArg>(g, x, A, B, y, Lw, p.wave_tiles, st, pack_arg<kArg>(p));
 }
 
 int32_t run_pool_load(const Geo& g, void* A_slot_slice, void* B_slot_slice, const void* Asrc,

@@ -182,7 +182,8 @@ def test_apply_validation_before_hip():
     up4 = lambda n: (n + 3) // 4 * 4  # noqa: E731
     image = up4(T) + 16 * (-(-T // 8) + 2 * 4) + 4 * (-(-T // 64) + 2 * 4)
     assert mh_need == 4 * (up4(3 * T + 3 * 4) + image)
-    # v: up to 4 K-split partials of T rows x S x R fp32
+    # workspace: the plan image (padded to 256 bytes), then v (up to 4 K-split
+    # partials of T rows x S x R fp32)
     assert ws_need == ((4 * image + 255) // 256) * 256 + 4 * T * 16 * 4
     ids = np.array([0, 1, -1, 3, 2, 0], np.int32)
     meta = _aligned_i32(mh_need // 4)

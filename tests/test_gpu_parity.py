@@ -430,3 +430,120 @@ def test_plan_staging_pinned_and_pageable(offset):
         check_rows(wl, yd, label=f"staging {'pinned' if mh is pinned_view else 'pageable'}")
         outs.append(yd.clone())
     assert torch.equal(_bits(outs[0]), _bits(outs[1]))
+
+
+def _decode_integer_workload(seed, T=70):
+    """Decode rows only (random ids incl. none) on integer inputs: exact sums."""
+    wl = _integer_workload("bf16", seed=seed, K=1032, T=T, lens=())
+    assert not wl.prefill.any()
+    return wl
+
+
+@pytest.mark.parametrize("T", [70, 96])
+def test_one_launch_decode_matches_two_launches(T):
+    """lora_plan_apply runs a small bf16 decode plan as one launch (every
+    workgroup computes its tile's v with MFMA and applies it to its columns);
+    on integer inputs it gives the same bits as lora_plan_shrink +
+    lora_plan_expand and as the exact result, call after call.  T = 70 gives
+    10 tiles (the 12-record argument tier), T = 96 gives 13 (the 48-record
+    tier); max_lora_rank 64 here, so this plan takes two launches and the
+    rank-16 adapters below take one."""
+    import torch
+    wl = _decode_integer_workload(11, T=T)
+    pool = make_pool(wl)
+    plan, img, _ = L.lora_apply_plan(pool.desc, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] == 0 and plan["wave_tiles"] == {70: 10, 96: 13}[T]
+    exp = _exact_expected(wl)
+    ws = torch.zeros(L.lora_apply_workspace_bytes(pool.desc, wl.T), dtype=torch.uint8, device="cuda")
+    xd = to_dev(wl.x, wl.dtype)
+    outs = []
+    for call in range(3):
+        yd = to_dev(wl.y_in, wl.dtype)
+        L.lora_plan_apply(pool.desc, xd, pool.A, pool.B, yd, wl.T, plan, None, img, ws, ws.numel())
+        torch.cuda.synchronize()
+        outs.append(yd.clone())
+        bad = np.argwhere(yd.float().cpu().numpy() != exp)
+        assert bad.size == 0, f"call {call}: {len(bad)} mismatches, first {bad[:3]}"
+    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
+    v = torch.zeros((rows, wl.num_slices * pool.R), dtype=torch.float32, device="cuda")
+    y2 = to_dev(wl.y_in, wl.dtype)
+    L.lora_plan_shrink(pool.desc, xd, pool.A, v, wl.T, plan, None, img)
+    L.lora_plan_expand(pool.desc, v, pool.B, y2, wl.T, plan, None, img)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y2), _bits(outs[0]))
+
+
+@pytest.mark.parametrize("R", [8, 16, 24, 32])
+@pytest.mark.parametrize("K", [264, 1064, 3080])
+def test_one_launch_decode_exact(R, K):
+    """The one-launch decode form (bf16, max_lora_rank <= 32: one or two rank
+    tiles of 16, ranks past R padding; K sizes that give one batch of 4, 8 or
+    16 chunks per wave, or two batches) on integer inputs, two slices, K not a
+    multiple of 32 and a ragged last column chunk: exact, and the same bits as
+    the two-launch stages."""
+    import torch
+    T = 40
+    wl = W.config_integer(seed=20 + R, T=T, K=K, outs=(520, 136), max_loras=5,
+                          max_lora_rank=R, ranks=(R, R // 2 // 8 * 8 or 8), dtype="bf16")
+    rng = np.random.default_rng(R + K)
+    ids = rng.integers(-1, 5, size=T).astype(np.int32)
+    wl = dataclasses.replace(wl, ids=ids, prefill=np.zeros(T, np.uint8))
+    pool = make_pool(wl)
+    plan, img, _ = L.lora_apply_plan(pool.desc, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] == 0 and 0 < plan["wave_tiles"] <= 12
+    exp = _exact_expected(wl)
+    y = run_apply(wl, pool=pool)
+    bad = np.argwhere(y.float().cpu().numpy() != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
+    v = torch.zeros((rows, wl.num_slices * pool.R), dtype=torch.float32, device="cuda")
+    xd, y2 = to_dev(wl.x, wl.dtype), to_dev(wl.y_in, wl.dtype)
+    L.lora_plan_shrink(pool.desc, xd, pool.A, v, wl.T, plan, None, img)
+    L.lora_plan_expand(pool.desc, v, pool.B, y2, wl.T, plan, None, img)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y2), _bits(y))
+
+
+@pytest.mark.parametrize("dtype,R", [("bf16", 16), ("bf16", 32), ("bf16", 64), ("f32", 16)])
+def test_one_launch_decode_random(dtype, R):
+    """Small decode plans on random values (one launch for bf16 with R <= 32
+    and at most 12 tiles, two launches otherwise), within tolerance of the
+    fp64 oracle."""
+    wl = W.config_bgmv_decode(seed=13, T=56, K=1040, O=520, n_adapters=6, rank=R, dtype=dtype)
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    plan, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] == 0 and plan["wave_tiles"] <= 48
+    y = run_apply(wl)
+    check_rows(wl, y, label=f"small decode plan {dtype} R={R}")
+
+
+def test_graph_capture_replays():
+    """lora_apply of a small decode plan captured into a graph: every replay,
+    with eager work and synchronisation between replays, gives the exact
+    result."""
+    import torch
+    wl = W.config_integer(seed=12, T=70, K=1032, outs=(264, 136), max_loras=6, max_lora_rank=16,
+                          ranks=(16, 8), dtype="bf16")
+    ids = np.random.default_rng(12).integers(-1, 6, size=wl.T).astype(np.int32)
+    wl = dataclasses.replace(wl, ids=ids, prefill=np.zeros(wl.T, np.uint8))
+    pool = make_pool(wl)
+    exp = _exact_expected(wl)
+    ws = torch.zeros(L.lora_apply_workspace_bytes(pool.desc, wl.T), dtype=torch.uint8, device="cuda")
+    need = L.lora_apply_host_meta_bytes(pool.desc, wl.T)
+    raw = np.zeros(need + 64, np.uint8)
+    meta = raw[(-raw.ctypes.data) % 16:][:need]
+    xd = to_dev(wl.x, wl.dtype)
+    y0 = to_dev(wl.y_in, wl.dtype)
+    yd = y0.clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.lora_apply(pool.desc, pool.A, pool.B, xd, yd, wl.T, wl.ids, wl.prefill, 0, ws, ws.numel(),
+                     meta, need)
+    for rep in range(3):
+        yd.copy_(y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        bad = np.argwhere(yd.float().cpu().numpy() != exp)
+        assert bad.size == 0, f"replay {rep}: {len(bad)} mismatches, first {bad[:3]}"
