@@ -291,6 +291,10 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
     const int64_t ksteps = (g.K + 63) / 64;
     while (ksplit < LORA_PLAN_MAX_KSPLIT && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4)
       ksplit *= 2;
+    if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1, 2 or 4
+      const long o = std::strtol(e, nullptr, 10);
+      if (o == 1 || o == 2 || o == 4) ksplit = (int32_t)o;
+    }
   }
   if (words > sl.image_max_words)  // cannot happen: the bounds above hold for any batch
     return fail(LORA_E_WORKSPACE, "tile plan overflow (%lld words > %lld)", (long long)words,

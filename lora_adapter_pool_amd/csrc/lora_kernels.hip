@@ -1375,10 +1375,10 @@ static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, v
   const Chunks ch = make_chunks(g, kExpandMfmaCols);
   if (tiles * ch.total > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
   if (g.R <= 64 && (int64_t)g.T * g.O * 2 < (int64_t)kDropOffset) {
-    // chunks per workgroup: enough workgroups to fill the GPU several times over
-    // (about 1024), at most 8 chunks each
+    // chunks per workgroup: at most about one resident round of workgroups
+    // (four per compute unit, 1024), at most 8 chunks each
     const int64_t work = tiles * ch.total;
-    int cpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, work / 1024));
+    int cpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, (work + 1023) / 1024));
     if (const char* e = std::getenv("LORA_EXPAND_MFMA_CPW")) {  // tuning / test override
       const long o = std::strtol(e, nullptr, 10);
       if (o >= 1 && o <= 8) cpw = (int)o;
