@@ -137,7 +137,8 @@ class Setup:
         self.image_host = np.ascontiguousarray(img if img.size else np.zeros(4, np.int32))
         rows = self.plan_d["num_sgmv_rows"] + self.plan_d["num_bgmv_rows"]
         S, R = wl.num_slices, wl.max_lora_rank
-        self.v = torch.zeros((self.plan_d["ksplit"] * max(rows, 1), S * R), dtype=torch.float32,
+        parts = max(self.plan_d["ksplit"], self.plan_d["ksplit_wave"])
+        self.v = torch.zeros((parts * max(rows, 1), S * R), dtype=torch.float32,
                              device="cuda")
         self.bytes_per_rep = per
         torch.cuda.synchronize()
@@ -331,8 +332,22 @@ def stage_kernels(wl):
         # 2: device image
         small = not p["mfma_tiles"]
         mode = (3 if p["wave_tiles"] <= 12 else 4 if p["wave_tiles"] <= 48 else 2) if small else 2
-        out["shrink"].append(f"shrink_wave_kernel<{tag}, 8, 4, {mode}>")
-        out["expand"].append(f"expand_wave_kernel<{tag}, 8, {kb}, {mode}>")
+        R = wl.max_lora_rank
+        if wl.dtype == "bf16" and R <= 64 and os.environ.get("LORA_TILE_MFMA_SHRINK", "1") != "0":
+            # MFMA tiles of 8 rows: rank tiles of 16 and K chunks per batch,
+            # partials of v summed by the expand (loaded in powers of two)
+            nt = 1 if R <= 16 else 2 if R <= 32 else 4
+            cb = {1: 8, 2: 6, 4: 4}[nt]
+            kp = p["ksplit_wave"]
+            kp2 = 1 if kp == 1 else 2 if kp == 2 else 4 if kp <= 4 else 8
+            out["shrink"].append(f"shrink_tile_mfma_kernel<{nt}, {cb}, {mode}>")
+            if os.environ.get("LORA_TILE_MFMA_EXPAND", "1") != "0" and wl.T * wl.O * 2 < 2 ** 31:
+                out["expand"].append(f"expand_tile_mfma_kernel<{1 if R <= 32 else 2}, {kp2}, {mode}>")
+            else:
+                out["expand"].append(f"expand_wave_kernel<{tag}, 8, {kb}, {kp2}, {mode}>")
+        else:
+            out["shrink"].append(f"shrink_wave_kernel<{tag}, 8, 4, {mode}>")
+            out["expand"].append(f"expand_wave_kernel<{tag}, 8, {kb}, 1, {mode}>")
     return out
 
 

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define LORA_POOL_ABI_VERSION 1
+#define LORA_POOL_ABI_VERSION 2
 #define LORA_MAX_SLICES 8
 /* [TGI] step 4 names a BGMV rank limit without a value; 64 covers the ranks
  * the kernels are built for.  Pass bgmv_max_rank <= 0 to lora_build_meta /
@@ -224,8 +224,10 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
 /* Rows per wavefront-path tile and per MFMA tile of a plan. */
 #define LORA_PLAN_WAVE_ROWS 8
 #define LORA_PLAN_MFMA_ROWS 64
-/* most partial sums the MFMA shrink splits K into */
-#define LORA_PLAN_MAX_KSPLIT 4
+/* most K-split partials of v a plan uses (LORA_PLAN_MAX_KSPLIT_MFMA for MFMA
+ * tiles, LORA_PLAN_MAX_KSPLIT for wavefront tiles) */
+#define LORA_PLAN_MAX_KSPLIT 8
+#define LORA_PLAN_MAX_KSPLIT_MFMA 4
 /* int32 words per tile record of a plan */
 #define LORA_PLAN_WAVE_WORDS 16
 #define LORA_PLAN_MFMA_WORDS 4
@@ -250,10 +252,11 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
  *                                     each row (-1 past the last row), -1 ...
  *   mfma [mfma_tiles][4]              slot, rows, first v row, 0
  *
- * ksplit: the MFMA shrink splits K into this many contiguous ranges and writes
- * one partial of v per range (the MFMA expand sums them in order 0, 1, ...);
- * the plan picks it so that the MFMA launches fill the GPU.  Wavefront rows
- * have a single partial (index 0). */
+ * ksplit: the shrink of the MFMA tiles splits K into this many contiguous
+ * ranges and writes one partial of v per range (the expand sums them in order
+ * 0, 1, ...); ksplit_wave does the same for the wavefront tiles (bf16 pools
+ * with R <= 64; 1 otherwise).  The plan picks both so that the launches fill
+ * the GPU. */
 typedef struct {
   int32_t num_sgmv_rows;
   int32_t num_bgmv_rows;
@@ -261,8 +264,10 @@ typedef struct {
   int32_t wave_tiles;
   int32_t mfma_tiles;
   int32_t mfma_min_rows;   /* INT32_MAX when no segment uses MFMA tiles */
-  int32_t ksplit;          /* in [1, LORA_PLAN_MAX_KSPLIT] */
+  int32_t ksplit;          /* in [1, LORA_PLAN_MAX_KSPLIT_MFMA] */
   int32_t bgmv_mfma_min_rows;  /* INT32_MAX when no BGMV run uses MFMA tiles */
+  int32_t ksplit_wave;     /* in [1, LORA_PLAN_MAX_KSPLIT] */
+  int32_t reserved;        /* 0 */
   int64_t image_offset;    /* bytes from meta_host to the device image (16-byte aligned) */
   int64_t image_bytes;
   int64_t off_perm;        /* int32 offsets inside the image */
@@ -289,7 +294,8 @@ int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* id
  *               wavefront tiles, max_loras <= 2^28) with a host copy travels
  *               in the kernel arguments and `image` is not read; otherwise
  *               `image` is used.
- *   v:          device fp32 [ksplit][num_sgmv_rows + num_bgmv_rows][S][R]
+ *   v:          device fp32 [max(ksplit, ksplit_wave)][num_sgmv_rows +
+ *               num_bgmv_rows][S][R]
  *               (plan row order; partial p of row i at
  *               ((p * rows + i) * S + s) * R + k).
  *   lora_plan_shrink:  v[row][s][k] = sum_j A_pool[a][s][k][j] * x[t][j] for

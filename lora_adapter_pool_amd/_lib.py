@@ -66,6 +66,7 @@ class lora_plan(ctypes.Structure):
                 ("num_segs", ctypes.c_int32), ("wave_tiles", ctypes.c_int32),
                 ("mfma_tiles", ctypes.c_int32), ("mfma_min_rows", ctypes.c_int32),
                 ("ksplit", ctypes.c_int32), ("bgmv_mfma_min_rows", ctypes.c_int32),
+                ("ksplit_wave", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("image_offset", ctypes.c_int64), ("image_bytes", ctypes.c_int64),
                 ("off_perm", ctypes.c_int64), ("off_wave", ctypes.c_int64),
                 ("off_mfma", ctypes.c_int64)]
@@ -73,7 +74,8 @@ class lora_plan(ctypes.Structure):
 
 PLAN_WAVE_ROWS = 8
 PLAN_MFMA_ROWS = 64
-PLAN_MAX_KSPLIT = 4
+PLAN_MAX_KSPLIT = 8        # partials of v (wavefront tiles)
+PLAN_MAX_KSPLIT_MFMA = 4   # partials of v (MFMA tiles)
 PLAN_WAVE_WORDS = 16
 PLAN_MFMA_WORDS = 4
 

@@ -72,8 +72,11 @@ int32_t sgmv_args(const int32_t* perm, const int32_t* seg_starts, const int32_t*
 int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const void* image_host,
                   TilePlan* tp) {
   if (!p) return fail(LORA_E_ARG, "plan is NULL");
-  if (p->ksplit < 1 || p->ksplit > LORA_PLAN_MAX_KSPLIT)
+  if (p->ksplit < 1 || p->ksplit > LORA_PLAN_MAX_KSPLIT_MFMA)
     return fail(LORA_E_ARG, "malformed plan (ksplit %d outside [1, %d])", p->ksplit,
+                LORA_PLAN_MAX_KSPLIT_MFMA);
+  if (p->ksplit_wave < 1 || p->ksplit_wave > LORA_PLAN_MAX_KSPLIT)
+    return fail(LORA_E_ARG, "malformed plan (ksplit_wave %d outside [1, %d])", p->ksplit_wave,
                 LORA_PLAN_MAX_KSPLIT);
   if (p->num_sgmv_rows < 0 || p->num_bgmv_rows < 0 || p->wave_tiles < 0 || p->mfma_tiles < 0 ||
       p->off_perm < 0 || p->off_wave < 0 || p->off_mfma < 0 || p->image_bytes < 0)
@@ -99,7 +102,7 @@ int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const voi
   *tp = TilePlan{img ? img + p->off_perm : nullptr, img ? img + p->off_wave : nullptr,
                  p->wave_tiles, img ? img + p->off_mfma : nullptr, p->mfma_tiles,
                  host ? host + p->off_wave : nullptr, p->ksplit,
-                 p->num_sgmv_rows + p->num_bgmv_rows};
+                 p->num_sgmv_rows + p->num_bgmv_rows, p->ksplit_wave};
   return LORA_OK;
 }
 
@@ -287,7 +290,8 @@ int32_t lora_plan_apply(const lora_pool_desc* desc, const void* x, const void* A
   if (ws_bytes < wl.total)
     return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
                 (long long)wl.total);
-  if ((int64_t)tp.ksplit * tp.num_rows > (int64_t)LORA_PLAN_MAX_KSPLIT * T)
+  if ((int64_t)std::max(tp.ksplit, tp.ksplit_wave) * tp.num_rows >
+      (int64_t)LORA_PLAN_MAX_KSPLIT * T)
     return fail(LORA_E_ARG, "malformed plan (%d rows for %d tokens)", tp.num_rows, T);
   g.T = T;
   return run_plan_apply(g, x, A_pool, B_pool, y, tp, (float*)((char*)ws + wl.v),

@@ -289,11 +289,27 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   if (nm > 0) {
     const int64_t wgs = nm * g.S * ((g.R + 63) / 64);
     const int64_t ksteps = (g.K + 63) / 64;
-    while (ksplit < LORA_PLAN_MAX_KSPLIT && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4)
+    while (ksplit < LORA_PLAN_MAX_KSPLIT_MFMA && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4)
       ksplit *= 2;
     if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1, 2 or 4
       const long o = std::strtol(e, nullptr, 10);
       if (o == 1 || o == 2 || o == 4) ksplit = (int32_t)o;
+    }
+  }
+  // K split of the wavefront tiles' MFMA shrink (bf16, R <= 64): grow it while
+  // the launch has fewer than four workgroups per compute unit and every part
+  // keeps at least one full load batch for each of the workgroup's waves
+  int32_t ksplit_wave = 1;
+  if (bf && nw > 0 && g.R <= 64) {
+    const int64_t nk = (g.K + 31) / 32;
+    const int64_t batch = (int64_t)kTileShrinkWaves * tile_shrink_cb(g.R);
+    const int64_t wgs = nw * g.S;
+    while (ksplit_wave < tile_kparts_max(g.R) && wgs * ksplit_wave < 1024 &&
+           nk / (ksplit_wave + 1) >= batch)
+      ++ksplit_wave;
+    if (const char* e = std::getenv("LORA_WAVE_KSPLIT")) {  // tuning override
+      const long o = std::strtol(e, nullptr, 10);
+      if (o >= 1 && o <= tile_kparts_max(g.R)) ksplit_wave = (int32_t)o;
     }
   }
   if (words > sl.image_max_words)  // cannot happen: the bounds above hold for any batch
@@ -307,6 +323,8 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   p->mfma_min_rows = thr;
   p->ksplit = ksplit;
   p->bgmv_mfma_min_rows = bthr;
+  p->ksplit_wave = ksplit_wave;
+  p->reserved = 0;
   p->image_offset = sl.image * 4;
   p->image_bytes = words * 4;
   p->off_perm = 0;

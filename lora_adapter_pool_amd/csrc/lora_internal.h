@@ -59,6 +59,18 @@ int32_t sgmv_mfma_min_rows();
 int32_t bgmv_mfma_min_rows();
 int32_t bgmv_mfma_min_total();
 
+// MFMA shrink of wavefront tiles (bf16 pools, R <= 64): rank tiles of 16 it
+// computes (R = 48 takes 4) and the 32-wide K chunks each wave loads per batch.
+constexpr int32_t tile_shrink_rank_tiles(int32_t R) { return R <= 16 ? 1 : R <= 32 ? 2 : 4; }
+constexpr int32_t tile_shrink_cb(int32_t R) {
+  return tile_shrink_rank_tiles(R) == 1 ? 8 : tile_shrink_rank_tiles(R) == 2 ? 6 : 4;
+}
+constexpr int32_t kTileShrinkWaves = 4;  // waves per workgroup of that shrink
+// Most partials of v that shrink writes: 8 (LORA_PLAN_MAX_KSPLIT) for R <= 16,
+// else 4 (the expand's staging of 8 partials of 64 ranks needs too many
+// scalar registers).
+constexpr int32_t tile_kparts_max(int32_t R) { return R <= 16 ? LORA_PLAN_MAX_KSPLIT : 4; }
+
 // Builder core (no argument checks beyond what lora_build_meta does).
 int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
                         int32_t max_loras, int32_t max_lora_rank, int32_t bgmv_max_rank,

@@ -22,7 +22,8 @@ constexpr int kExpandMfmaCols = 128;   // output columns per MFMA expand workgro
 constexpr int kArgWords = 2 + LORA_PLAN_WAVE_ROWS;
 constexpr int kArgTilesS = 12;
 constexpr int kArgTilesL = 48;
-constexpr int kMaxKsplit = LORA_PLAN_MAX_KSPLIT;  // K splits of the MFMA shrink
+constexpr int kMaxKsplit = LORA_PLAN_MAX_KSPLIT_MFMA;  // K splits of the MFMA shrink
+constexpr int kMaxKsplitWave = LORA_PLAN_MAX_KSPLIT;   // K splits of the wavefront tiles
 
 // A list of rows to process.  Row i reads token tok[i] of x / y and writes row i
 // of v.  Three ways to cut it into tiles, one adapter per tile:
@@ -70,8 +71,9 @@ struct TilePlan {
   const int32_t* mfma;
   int32_t mfma_tiles;
   const int32_t* wave_host;  // host copy of the wave records, or nullptr
-  int32_t ksplit;            // partials of the MFMA shrink (v holds ksplit x num_rows rows)
+  int32_t ksplit;            // partials of the MFMA tiles' shrink
   int32_t num_rows;          // v rows (SGMV rows, then BGMV rows) = entries of perm
+  int32_t ksplit_wave;       // partials of the wavefront tiles' shrink (bf16, R <= 64)
 };
 
 // Enqueue the shrink / expand of one row list (segments or rows) on `st`;

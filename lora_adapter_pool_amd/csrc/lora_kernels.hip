@@ -431,19 +431,23 @@ __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__
 // writes LDS, so the copy costs one memory round trip.  B rows are padded by
 // 16 bytes in LDS, which makes the row-per-thread reads conflict-free.  KB is
 // the pool's rank rounded up to 16 or 64, so no thread loads vectors that are
-// never used.
-template <typename E, int TM, int KB, int MODE>
+// never used.  v is the sum of the shrink's kparts partials (row i of partial
+// p at p * v_rows + i), added in order 0, 1, ...; KP >= kparts partials are
+// loaded, those past kparts as zeros, so all loads are issued at once.
+template <typename E, int TM, int KB, int KP, int MODE>
 __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restrict__ v,
                                                           const E* __restrict__ B,
                                                           E* __restrict__ y, RowList L, Geo g,
-                                                          Chunks ch, PlanArg<MODE> pa) {
+                                                          Chunks ch, int kparts, int v_rows,
+                                                          PlanArg<MODE> pa) {
   constexpr int NC = kExpandCols;      // 256 columns per workgroup
   constexpr int VEC = El<E>::kVec;     // elements per 16-byte vector
   constexpr int LDB = KB + VEC;        // LDS row stride: 16 bytes of padding
   constexpr int MAXV = NC * KB / VEC / 256;  // B vectors per thread per pass
   // v vectors per thread staged in one go: all of R for R <= KB (KB = 16) or
-  // R <= 256 (KB = 64); larger R goes through a plain loop
-  constexpr int NVV = (TM * (KB == 64 ? 256 : KB) / 4 + 255) / 256;
+  // R <= 256 (KB = 64; R <= 64 when partials are summed, which only pools of
+  // R <= 64 have); larger R goes through a plain loop
+  constexpr int NVV = (TM * (KB == 64 ? (KP > 1 ? 64 : 256) : KB) / 4 + 255) / 256;
   static_assert(KB % VEC == 0 && MAXV >= 1, "rank block must hold whole vectors");
   extern __shared__ __align__(16) unsigned char lds_raw[];
   // Bs: NC staged rows plus one dump row that absorbs stores of idle lanes (so
@@ -468,6 +472,7 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
   const int R = g.R;
   const int SR = g.S * R;
   const int r0 = tr.vrow0;
+  const int np = KP == 1 ? 1 : kparts;  // partials of v (one unless KP > 1)
   // y of every valid row is read up front so its latency overlaps the B / v
   // staging; each row is written exactly once, by the group that owns it
   const int colc = tid < ncv ? tid : 0;
@@ -505,9 +510,16 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
           const int r = i < nv4 ? (i * 4) / R : 0;
           const bool mem = i < nv4 && ((m >> r) & 1u);
           const int k = mem ? i * 4 - r * R : 0;
-          const u32x4 raw = ld16(v + (size_t)(r0 + (mem ? r : 0)) * SR + s * R + k) &
-                            (mem ? 0xffffffffu : 0u);
-          vraw[j] = __builtin_bit_cast(f32x4, raw);
+          const size_t off = (size_t)(r0 + (mem ? r : 0)) * SR + s * R + k;
+          u32x4 raw[KP];
+#pragma unroll
+          for (int p = 0; p < KP; ++p)
+            raw[p] = ld16(v + off + (size_t)(p < np ? p : 0) * v_rows * SR) &
+                     all_or_none(mem && p < np);
+          f32x4 sum = __builtin_bit_cast(f32x4, raw[0]);
+#pragma unroll
+          for (int p = 1; p < KP; ++p) sum += __builtin_bit_cast(f32x4, raw[p]);
+          vraw[j] = sum;
         }
       }
       __syncthreads();                  // previous readers of Bs / vs are done
@@ -529,9 +541,11 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
           const int r = (i * 4) / R;
           const bool mem = (m >> r) & 1u;
           const int k = i * 4 - r * R;
-          *reinterpret_cast<f32x4*>(vs + i * 4) =
-              mem ? *reinterpret_cast<const f32x4*>(v + (size_t)(r0 + r) * SR + s * R + k)
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int p = 0; mem && p < np; ++p)
+            sum += *reinterpret_cast<const f32x4*>(v + ((size_t)p * v_rows + r0 + r) * SR +
+                                                   s * R + k);
+          *reinterpret_cast<f32x4*>(vs + i * 4) = sum;
         }
       }
       __syncthreads();
@@ -630,11 +644,14 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
 #pragma unroll
   for (int r = 1; r < TM; ++r)
     if (m == r) tk = tr.tok[r];
-  const uint16_t* xp = x + (size_t)tk * g.K + kq;
+  // (a lane with kq >= K only ever loads masked chunks; kqa keeps its address
+  // inside the row, which holds K >= 8 elements)
+  const int kqa = min(kq, g.K - 8);
+  const uint16_t* xp = x + (size_t)tk * g.K + kqa;
   const uint16_t* ap[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    ap[t] = A + ((size_t)(a * g.S + s) * R + min(16 * t + m, R - 1)) * g.K + kq;
+    ap[t] = A + ((size_t)(a * g.S + s) * R + min(16 * t + m, R - 1)) * g.K + kqa;
   f32x4 d[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -719,6 +736,251 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
       if ((tr.valid >> r) & 1u)
         yb[(size_t)tr.tok[r] * g.O] = El<uint16_t>::put(El<uint16_t>::get(yv[r]) + acc);
     }
+  }
+}
+
+// ------------------------------- shrink (MFMA, wavefront tiles, bf16, R <= 64)
+//
+// grid = tiles * S * kparts, 256 threads (4 waves).  Workgroup (tile, slice s,
+// part p) writes partial p of v for the tile's rows: the sum over the part's
+// contiguous range of 32-wide K chunks of
+//   D[m][n] = sum_k x[tok[m]][k] * A_pool[a][s][n][k]
+// as v_mfma_f32_16x16x32_bf16 tiles (rows m = the tile's tokens, 8 of 16 used;
+// columns n = ranks, NT tiles of 16).  Every rank of the slice comes out of one
+// pass over x, where the VALU shrink reads x once per 4-rank chunk.  The
+// part's chunks are dealt round-robin over the waves; a wave issues the loads
+// of CB chunks before the first MFMA of the batch waits on them.  The waves'
+// partial tiles are summed in a fixed order in LDS, so the result does not
+// depend on timing.  Splitting K over workgroups spreads the x and A loads
+// over more compute units, each of which issues only so many loads per cycle.
+template <int NT, int CB, int MODE>
+__global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, float* __restrict__ v,
+    RowList L, Geo g, int kparts, int v_rows, PlanArg<MODE> pa) {
+  constexpr int TM = kWaveTileRows, NW = kTileShrinkWaves, RM = 16 * NT;
+  static_assert(TM <= 16 && TM % 4 == 0, "tile rows fit one MFMA tile");
+  static_assert(CB * (1 + NT) <= 24, "a batch keeps at most 24 loads per lane in flight");
+  __shared__ float red[NW][TM][RM + 1];
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_tile = g.S * kparts;
+  const int f = bid / per_tile;
+  const int rem = bid - f * per_tile;
+  const int s = rem / kparts;
+  const int part = rem - s * kparts;
+  TileRows<TM> tr;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.valid == 0) return;
+  const int a = tr.aid[0];  // one adapter per tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = g.R;
+  const int nk = (g.K + 31) / 32;
+  const int per = (nk + kparts - 1) / kparts;
+  const int c_lo = min(nk, part * per), c_hi = min(nk, c_lo + per);
+
+  // lane l feeds row m = l % 16 and K offset kq = 8 (l / 16) of each chunk;
+  // rows past the tile repeat row 0 and ranks past R repeat rank R - 1 (their
+  // outputs are never used)
+  const int m = lane & 15, kq = (lane >> 4) * 8;
+  int tk = tr.tok[0];
+#pragma unroll
+  for (int r = 1; r < TM; ++r)
+    if (m == r) tk = tr.tok[r];
+  // (a lane with kq >= K only ever loads masked chunks; kqa keeps its address
+  // inside the row, which holds K >= 8 elements)
+  const int kqa = min(kq, g.K - 8);
+  const uint16_t* xp = x + (size_t)tk * g.K + kqa;
+  const uint16_t* ap[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    ap[t] = A + ((size_t)(a * g.S + s) * R + min(16 * t + m, R - 1)) * g.K + kqa;
+  f32x4 d[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = c_lo + wave; c0 < c_hi; c0 += NW * CB) {
+    u32x4 xv[CB], av[CB][NT];
+    uint32_t msk[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int c = c0 + u * NW;
+      const bool ok = c < c_hi && c * 32 + kq < g.K;
+      const int kc = ok ? c * 32 : 0;
+      msk[u] = all_or_none(ok);
+      xv[u] = ld16(xp + kc);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) av[u][t] = ld16(ap[t] + kc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const bf16x8 xo = __builtin_bit_cast(bf16x8, xv[u] & msk[u]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            xo, __builtin_bit_cast(bf16x8, av[u][t] & msk[u]), d[t], 0, 0, 0);
+    }
+  }
+  // lane l holds D[4 (l / 16) + j][l % 16] of each rank tile; lanes 0 .. 4 TM - 1
+  // hold the tile's rows
+  if (lane < 4 * TM) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wave][4 * (lane >> 4) + j][16 * t + m] = d[t][j];
+  }
+  __syncthreads();
+  const int SR = g.S * R;
+  for (int i = tid; i < TM * RM; i += 64 * NW) {
+    const int r = i / RM, n = i - r * RM;
+    if (n < R && ((tr.valid >> r) & 1u)) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc += red[w][r][n];
+      v[((size_t)part * v_rows + tr.vrow0 + r) * SR + s * R + n] = acc;
+    }
+  }
+}
+
+// ------------------------------- expand (MFMA, wavefront tiles, bf16, R <= 64)
+//
+// grid = tiles * column chunks (kTileExpandCols columns of one slice each),
+// 256 threads (4 waves).  For a tile of at most 8 rows, D = Btile * v^T as
+// v_mfma_f32_16x16x32_bf16 tiles: rows = output columns, columns = the tile's
+// tokens (8 of 16 used), K = ranks in chunks of 32; two MFMAs per tile and
+// chunk take the hi and lo bf16 halves of the fp32 v.  Wave w covers the
+// pairs of 16-column tiles w, w + 4, ... of the chunk.  Inside a pair, MFMA
+// row n of the first tile reads B column 8 (n / 4) + n % 4 and of the second
+// the same + 4, so lane (g, m) ends with columns 8 g .. 8 g + 8 of token m and
+// reads and writes them as one 16-byte access.  The B rows (32 contiguous
+// bytes of ranks per column and chunk) and y of all of the wave's pairs are
+// loaded before v is needed; v (the sum of the shrink's kparts partials in
+// order 0, 1, ..., split into hi + lo) is staged once in LDS.  y leaves
+// through raw buffer stores; lanes without a row store to a dropped offset.
+constexpr int kTileExpandWaves = 4;
+constexpr int kTileExpandPairs = 4;  // pairs of 16-column tiles per wave
+constexpr int kTileExpandCols = 32 * kTileExpandPairs * kTileExpandWaves;
+
+template <int NKC, int KP, int MODE>
+__global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel(
+    const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
+    RowList L, Geo g, Chunks ch, int kparts, int v_rows, PlanArg<MODE> pa) {
+  constexpr int TM = kWaveTileRows, PPW = kTileExpandPairs, NW = kTileExpandWaves;
+  constexpr int LDV = 32 * NKC + 8;  // LDS row of v in bf16 (ranks covered + padding)
+  static_assert(TM <= 16 && TM * 64 / 4 <= 64 * NW, "one v vector per thread");
+  __shared__ __align__(16) uint16_t vh[TM * LDV];
+  __shared__ __align__(16) uint16_t vl[TM * LDV];
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int f = bid / ch.total;
+  const int cidx = bid - f * ch.total;
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < LORA_MAX_SLICES; ++i)
+    if (i < g.S && cidx >= ch.start[i]) s = i;
+  const int col0 = (cidx - ch.start[s]) * kTileExpandCols;
+  const int out_s = g.out[s];
+  TileRows<TM> tr;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.valid == 0) return;
+  const int a = tr.aid[0];  // one adapter per tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const int R = g.R;
+  const int np = KP == 1 ? 1 : kparts;
+  const __amdgpu_buffer_rsrc_t yb = make_rsrc(y, (uint32_t)((size_t)g.T * g.O * sizeof(uint16_t)));
+
+  // this lane's token (MFMA column i16) and its y row
+  int my_tok = tr.tok[0];
+#pragma unroll
+  for (int r = 1; r < TM; ++r)
+    if (i16 == r) my_tok = tr.tok[r];
+  const bool tok_ok = i16 < TM && ((tr.valid >> i16) & 1u);
+  const size_t yrow = (size_t)my_tok * g.O + g.off[s];
+
+  // B rows and y of the wave's pairs: they do not depend on v, so they go first
+  const uint16_t* Ba = B + ((size_t)a * g.O + g.off[s]) * R;
+  u32x4 bt[PPW][2][NKC], yr[PPW];
+#pragma unroll
+  for (int q = 0; q < PPW; ++q) {
+    const int pc = col0 + 32 * (wave + NW * q);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = pc + 8 * (i16 >> 2) + 4 * h + (i16 & 3);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int k = 32 * kc + 8 * g4;
+        const bool ok = c < out_s && k < R;
+        bt[q][h][kc] = ld16(Ba + (size_t)(ok ? c : 0) * R + (ok ? k : 0)) & all_or_none(ok);
+      }
+    }
+    const int yc = pc + 8 * g4;
+    yr[q] = ld16(y + yrow + (yc < out_s ? yc : 0));
+  }
+
+  // v of the tile's rows: the sum of the partials, split into hi + lo bf16
+  // (rows without a valid token are zero)
+  const int SR = g.S * R;
+  if (tid < TM * R / 4) {
+    const int r = (tid * 4) / R, k = tid * 4 - r * R;
+    const bool ok = (tr.valid >> r) & 1u;
+    const size_t off = ((size_t)tr.vrow0 + (ok ? r : 0)) * SR + s * R + k;
+    u32x4 raw[KP];
+#pragma unroll
+    for (int p = 0; p < KP; ++p)
+      raw[p] = ld16(v + off + (size_t)(p < np ? p : 0) * v_rows * SR) & all_or_none(ok && p < np);
+    float e[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {  // fixed order: partial 0, 1, ...
+      e[0] += __uint_as_float(raw[p].x);
+      e[1] += __uint_as_float(raw[p].y);
+      e[2] += __uint_as_float(raw[p].z);
+      e[3] += __uint_as_float(raw[p].w);
+    }
+    uint32_t hb[4], lb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hb[i] = f32_to_bf16_bits(e[i]);
+      lb[i] = f32_to_bf16_bits(e[i] - __uint_as_float(hb[i] << 16));
+    }
+    *reinterpret_cast<u32x2*>(&vh[r * LDV + k]) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+    *reinterpret_cast<u32x2*>(&vl[r * LDV + k]) = u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+  }
+  __syncthreads();
+  // MFMA B operand: lane (g, m) holds ranks 32 kc + 8 g .. +8 of token row m
+  // (zero past the tile's rows and past R)
+  bf16x8 vhi[NKC], vlo[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    const int k = 32 * kc + 8 * g4;
+    const bool ok = i16 < TM && k < R;
+    const int o = (ok ? i16 : 0) * LDV + (ok ? k : 0);
+    const uint32_t msk = all_or_none(ok);
+    vhi[kc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vh[o]) & msk);
+    vlo[kc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vl[o]) & msk);
+  }
+#pragma unroll
+  for (int q = 0; q < PPW; ++q) {
+    f32x4 d0 = f32x4{0.f, 0.f, 0.f, 0.f}, d1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, bt[q][0][kc]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, bt[q][1][kc]);
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, vhi[kc], d0, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, vlo[kc], d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, vhi[kc], d1, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, vlo[kc], d1, 0, 0, 0);
+    }
+    // lane (g, m): d0[j] is column 8 g + j and d1[j] column 8 g + 4 + j of token m
+    const float add[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+    const uint32_t wi[4] = {yr[q].x, yr[q].y, yr[q].z, yr[q].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(wi[i] << 16) + add[2 * i];
+      const float hi = __uint_as_float(wi[i] & 0xffff0000u) + add[2 * i + 1];
+      o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    }
+    const int yc = col0 + 32 * (wave + NW * q) + 8 * g4;
+    const uint32_t off = (tok_ok && yc < out_s)
+                             ? (uint32_t)((yrow + (size_t)yc) * sizeof(uint16_t))
+                             : kDropOffset;
+    st16_buf(u32x4{o[0], o[1], o[2], o[3]}, yb, off);
   }
 }
 
@@ -1281,28 +1543,119 @@ static int32_t launch_shrink_wave(const Geo& g, const void* x, const void* A, fl
   return hip_check("shrink_wave launch");
 }
 
-template <typename E, int KB, int MODE>
+template <typename E, int KB, int KP, int MODE>
 static int32_t launch_expand_wave_kb(const Geo& g, const float* v, const void* B, void* y,
-                                     const RowList& L, int64_t tiles, hipStream_t st,
-                                     const PlanArg<MODE>& pa) {
+                                     const RowList& L, int64_t tiles, int kparts, int v_rows,
+                                     hipStream_t st, const PlanArg<MODE>& pa) {
   const Chunks ch = make_chunks(g, kExpandCols);
   const int64_t grid = tiles * ch.total;
   if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one expand launch");
   const size_t lds = sizeof(E) * (kExpandCols + 1) * (KB + 16 / sizeof(E)) +
                      sizeof(float) * (kWaveTileRows * g.R + 4);
   if (lds > 160 * 1024) return fail(LORA_E_SHAPE, "max_lora_rank too large for the expand kernel");
-  hipLaunchKernelGGL((expand_wave_kernel<E, kWaveTileRows, KB, MODE>), dim3(grid_of(grid)),
-                     dim3(256), lds, st, v, (const E*)B, (E*)y, L, g, ch, pa);
+  hipLaunchKernelGGL((expand_wave_kernel<E, kWaveTileRows, KB, KP, MODE>), dim3(grid_of(grid)),
+                     dim3(256), lds, st, v, (const E*)B, (E*)y, L, g, ch, kparts, v_rows, pa);
   return hip_check("expand_wave launch");
 }
 
+template <typename E, int KP, int MODE>
+static int32_t launch_expand_wave_kp(const Geo& g, const float* v, const void* B, void* y,
+                                     const RowList& L, int64_t tiles, int kparts, int v_rows,
+                                     hipStream_t st, const PlanArg<MODE>& pa) {
+  return g.R <= 16
+             ? launch_expand_wave_kb<E, 16, KP, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa)
+             : launch_expand_wave_kb<E, 64, KP, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+}
+
+// kparts: partials of v to sum (1 for the VALU shrink; only bf16 plans use more)
 template <typename E, int MODE>
 static int32_t launch_expand_wave(const Geo& g, const float* v, const void* B, void* y,
                                   const RowList& L, int64_t tiles, hipStream_t st,
-                                  const PlanArg<MODE>& pa = PlanArg<MODE>{}) {
+                                  const PlanArg<MODE>& pa = PlanArg<MODE>{}, int kparts = 1,
+                                  int v_rows = 0) {
   if (tiles <= 0) return LORA_OK;
-  return g.R <= 16 ? launch_expand_wave_kb<E, 16, MODE>(g, v, B, y, L, tiles, st, pa)
-                   : launch_expand_wave_kb<E, 64, MODE>(g, v, B, y, L, tiles, st, pa);
+  if (kparts < 1 || kparts > kMaxKsplitWave) return fail(LORA_E_ARG, "bad K split %d", kparts);
+  if constexpr (sizeof(E) == 2 && (MODE == kList || MODE == kArg || MODE == kArgL)) {
+    if (kparts > tile_kparts_max(g.R)) return fail(LORA_E_ARG, "bad K split %d", kparts);
+    if (kparts > 4)
+      return launch_expand_wave_kb<E, 16, 8, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+    if (kparts > 2)
+      return launch_expand_wave_kp<E, 4, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+    if (kparts > 1)
+      return launch_expand_wave_kp<E, 2, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+  } else {
+    if (kparts > 1) return fail(LORA_E_ARG, "one partial of v expected");
+  }
+  return launch_expand_wave_kp<E, 1, MODE>(g, v, B, y, L, tiles, 1, v_rows, st, pa);
+}
+
+// MFMA expand of wavefront tiles (bf16, R <= 64, y under 2 GiB), kparts
+// partials of v.
+template <int NKC, int KP, int MODE>
+static int32_t launch_expand_tile_k(const Geo& g, const float* v, const void* B, void* y,
+                                    const RowList& L, int64_t tiles, int kparts, int v_rows,
+                                    hipStream_t st, const PlanArg<MODE>& pa) {
+  const Chunks ch = make_chunks(g, kTileExpandCols);
+  const int64_t grid = tiles * ch.total;
+  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one expand launch");
+  hipLaunchKernelGGL((expand_tile_mfma_kernel<NKC, KP, MODE>), dim3(grid_of(grid)),
+                     dim3(64 * kTileExpandWaves), 0, st, v, (const uint16_t*)B, (uint16_t*)y, L,
+                     g, ch, kparts, v_rows, pa);
+  return hip_check("expand_tile_mfma launch");
+}
+
+template <int NKC, int MODE>
+static int32_t launch_expand_tile_nkc(const Geo& g, const float* v, const void* B, void* y,
+                                      const RowList& L, int64_t tiles, int kparts, int v_rows,
+                                      hipStream_t st, const PlanArg<MODE>& pa) {
+  if (kparts > 4)
+    return launch_expand_tile_k<NKC, 8, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+  if (kparts > 2)
+    return launch_expand_tile_k<NKC, 4, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+  if (kparts > 1)
+    return launch_expand_tile_k<NKC, 2, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+  return launch_expand_tile_k<NKC, 1, MODE>(g, v, B, y, L, tiles, 1, v_rows, st, pa);
+}
+
+template <int MODE>
+static int32_t launch_expand_tile(const Geo& g, const float* v, const void* B, void* y,
+                                  const RowList& L, int64_t tiles, int kparts, int v_rows,
+                                  hipStream_t st, const PlanArg<MODE>& pa = PlanArg<MODE>{}) {
+  if (tiles <= 0) return LORA_OK;
+  if (kparts < 1 || kparts > tile_kparts_max(g.R)) return fail(LORA_E_ARG, "bad K split %d", kparts);
+  if (g.R > 64 || (int64_t)g.T * g.O * 2 >= (int64_t)kDropOffset)
+    return fail(LORA_E_SHAPE, "the MFMA tile expand needs R <= 64 and y under 2 GiB");
+  return g.R <= 32
+             ? launch_expand_tile_nkc<1, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa)
+             : launch_expand_tile_nkc<2, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+}
+
+// MFMA shrink of wavefront tiles (bf16, R <= 64), kparts partials of v.
+template <int NT, int MODE>
+static int32_t launch_shrink_tile_nt(const Geo& g, const void* x, const void* A, float* v,
+                                     const RowList& L, int64_t tiles, int kparts, int v_rows,
+                                     hipStream_t st, const PlanArg<MODE>& pa) {
+  constexpr int CB = tile_shrink_cb(16 * NT);
+  const int64_t grid = tiles * g.S * kparts;
+  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one shrink launch");
+  hipLaunchKernelGGL((shrink_tile_mfma_kernel<NT, CB, MODE>), dim3(grid_of(grid)),
+                     dim3(64 * kTileShrinkWaves), 0, st, (const uint16_t*)x, (const uint16_t*)A,
+                     v, L, g, kparts, v_rows, pa);
+  return hip_check("shrink_tile_mfma launch");
+}
+
+template <int MODE>
+static int32_t launch_shrink_tile(const Geo& g, const void* x, const void* A, float* v,
+                                  const RowList& L, int64_t tiles, int kparts, int v_rows,
+                                  hipStream_t st, const PlanArg<MODE>& pa = PlanArg<MODE>{}) {
+  if (tiles <= 0) return LORA_OK;
+  if (kparts < 1 || kparts > tile_kparts_max(g.R)) return fail(LORA_E_ARG, "bad K split %d", kparts);
+  static_assert(kMaxKsplitWave == 8, "launchers cover up to 8 partials");
+  switch (tile_shrink_rank_tiles(g.R)) {
+    case 1: return launch_shrink_tile_nt<1, MODE>(g, x, A, v, L, tiles, kparts, v_rows, st, pa);
+    case 2: return launch_shrink_tile_nt<2, MODE>(g, x, A, v, L, tiles, kparts, v_rows, st, pa);
+    default: return launch_shrink_tile_nt<4, MODE>(g, x, A, v, L, tiles, kparts, v_rows, st, pa);
+  }
 }
 
 template <int NT, int CB, int MODE>
@@ -1473,6 +1826,57 @@ template <int MODE> static PlanArg<MODE> pack_arg(const TilePlan& p) {
   return a;
 }
 
+// Wavefront tiles of bf16 pools with R <= 64 take the MFMA shrink
+// (LORA_TILE_MFMA_SHRINK=0 turns it off), which writes the plan's ksplit_wave
+// partials of v; the VALU shrink writes one.
+static bool tile_mfma_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("LORA_TILE_MFMA_SHRINK");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+static bool use_tile_mfma(const Geo& g) {
+  return g.dtype == LORA_BF16 && g.R <= 64 && tile_mfma_enabled();
+}
+static int wave_kparts(const Geo& g, const TilePlan& p) {
+  return use_tile_mfma(g) ? p.ksplit_wave : 1;
+}
+// ... and the MFMA expand when y spans less than 2 GiB (raw buffer stores;
+// LORA_TILE_MFMA_EXPAND=0 turns it off)
+static bool use_tile_mfma_expand(const Geo& g) {
+  static const bool on = [] {
+    const char* e = std::getenv("LORA_TILE_MFMA_EXPAND");
+    return !(e && e[0] == '0');
+  }();
+  return on && use_tile_mfma(g) && (int64_t)g.T * g.O * 2 < (int64_t)kDropOffset;
+}
+
+template <int MODE>
+static int32_t launch_plan_wave_expand(const Geo& g, const float* v, const void* B, void* y,
+                                       const RowList& Lw, const TilePlan& p, hipStream_t st,
+                                       const PlanArg<MODE>& pa = PlanArg<MODE>{}) {
+  if (use_tile_mfma_expand(g))
+    return launch_expand_tile<MODE>(g, v, B, y, Lw, p.wave_tiles, wave_kparts(g, p), p.num_rows,
+                                    st, pa);
+  return g.dtype == LORA_BF16
+             ? launch_expand_wave<uint16_t, MODE>(g, v, B, y, Lw, p.wave_tiles, st, pa,
+                                                  wave_kparts(g, p), p.num_rows)
+             : launch_expand_wave<float, MODE>(g, v, B, y, Lw, p.wave_tiles, st, pa);
+}
+
+template <int MODE>
+static int32_t launch_plan_wave_shrink(const Geo& g, const void* x, const void* A, float* v,
+                                       const RowList& Lw, const TilePlan& p, hipStream_t st,
+                                       const PlanArg<MODE>& pa = PlanArg<MODE>{}) {
+  if (use_tile_mfma(g))
+    return launch_shrink_tile<MODE>(g, x, A, v, Lw, p.wave_tiles, p.ksplit_wave, p.num_rows, st,
+                                    pa);
+  return g.dtype == LORA_BF16
+             ? launch_shrink_wave<uint16_t, MODE>(g, x, A, v, Lw, p.wave_tiles, st, pa)
+             : launch_shrink_wave<float, MODE>(g, x, A, v, Lw, p.wave_tiles, st, pa);
+}
+
 int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, const TilePlan& p,
                         hipStream_t st) {
   const bool bf = g.dtype == LORA_BF16;
@@ -1480,20 +1884,14 @@ int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, co
   RowList Lw, Lm;
   plan_lists(p, Lw, Lm);
   if (small_plan(p, g)) {
-    if (p.wave_tiles <= kArgTilesS) {
-      const PlanArg<kArg> a = pack_arg<kArg>(p);
-      return bf ? launch_shrink_wave<uint16_t, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a)
-                : launch_shrink_wave<float, kArg>(g, x, A, v, Lw, p.wave_tiles, st, a);
-    }
-    const PlanArg<kArgL> a = pack_arg<kArgL>(p);
-    return bf ? launch_shrink_wave<uint16_t, kArgL>(g, x, A, v, Lw, p.wave_tiles, st, a)
-              : launch_shrink_wave<float, kArgL>(g, x, A, v, Lw, p.wave_tiles, st, a);
+    if (p.wave_tiles <= kArgTilesS)
+      return launch_plan_wave_shrink<kArg>(g, x, A, v, Lw, p, st, pack_arg<kArg>(p));
+    return launch_plan_wave_shrink<kArgL>(g, x, A, v, Lw, p, st, pack_arg<kArgL>(p));
   }
   if (int32_t e = launch_shrink_mfma<kList>(g, x, A, v, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
                                             st))
     return e;
-  return bf ? launch_shrink_wave<uint16_t, kList>(g, x, A, v, Lw, p.wave_tiles, st)
-            : launch_shrink_wave<float, kList>(g, x, A, v, Lw, p.wave_tiles, st);
+  return launch_plan_wave_shrink<kList>(g, x, A, v, Lw, p, st);
 }
 
 int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, const TilePlan& p,
@@ -1503,20 +1901,14 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
   RowList Lw, Lm;
   plan_lists(p, Lw, Lm);
   if (small_plan(p, g)) {
-    if (p.wave_tiles <= kArgTilesS) {
-      const PlanArg<kArg> a = pack_arg<kArg>(p);
-      return bf ? launch_expand_wave<uint16_t, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a)
-                : launch_expand_wave<float, kArg>(g, v, B, y, Lw, p.wave_tiles, st, a);
-    }
-    const PlanArg<kArgL> a = pack_arg<kArgL>(p);
-    return bf ? launch_expand_wave<uint16_t, kArgL>(g, v, B, y, Lw, p.wave_tiles, st, a)
-              : launch_expand_wave<float, kArgL>(g, v, B, y, Lw, p.wave_tiles, st, a);
+    if (p.wave_tiles <= kArgTilesS)
+      return launch_plan_wave_expand<kArg>(g, v, B, y, Lw, p, st, pack_arg<kArg>(p));
+    return launch_plan_wave_expand<kArgL>(g, v, B, y, Lw, p, st, pack_arg<kArgL>(p));
   }
   if (int32_t e = launch_expand_mfma<kList>(g, v, B, y, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
                                             st))
     return e;
-  return bf ? launch_expand_wave<uint16_t, kList>(g, v, B, y, Lw, p.wave_tiles, st)
-            : launch_expand_wave<float, kList>(g, v, B, y, Lw, p.wave_tiles, st);
+  return launch_plan_wave_expand<kList>(g, v, B, y, Lw, p, st);
 }
 
 // One launch for both stages (decode_onepass_kernel) when the plan goes by

@@ -87,6 +87,14 @@ def run_entry_points(wl, pool, mode, bgmv_max_rank=0):
     return yd, vs, vb, m
 
 
+def plan_v(plan, S, R, fill=0.0):
+    """fp32 v for a plan's stages: every K-split partial of every row."""
+    import torch
+    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
+    parts = max(plan["ksplit"], plan["ksplit_wave"])
+    return torch.full((parts * max(rows, 1), S * R), fill, dtype=torch.float32, device="cuda")
+
+
 def sample_rows(wl, n=64, seed=0):
     """Rows for full-size checks: first/last row of every adapter run plus random
     rows (active and none)."""

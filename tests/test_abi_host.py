@@ -24,7 +24,7 @@ def test_library_exports_every_header_function(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
-    assert lib.lora_abi_version() == 1
+    assert lib.lora_abi_version() == 2
 
 
 def test_pool_geometry_and_bytes():
@@ -182,9 +182,9 @@ def test_apply_validation_before_hip():
     up4 = lambda n: (n + 3) // 4 * 4  # noqa: E731
     image = up4(T) + 16 * (-(-T // 8) + 2 * 4) + 4 * (-(-T // 64) + 2 * 4)
     assert mh_need == 4 * (up4(3 * T + 3 * 4) + image)
-    # workspace: the plan image (padded to 256 bytes), then v (up to 4 K-split
+    # workspace: the plan image (padded to 256 bytes), then v (up to 8 K-split
     # partials of T rows x S x R fp32)
-    assert ws_need == ((4 * image + 255) // 256) * 256 + 4 * T * 16 * 4
+    assert ws_need == ((4 * image + 255) // 256) * 256 + 8 * T * 16 * 4
     ids = np.array([0, 1, -1, 3, 2, 0], np.int32)
     meta = _aligned_i32(mh_need // 4)
     ok = [d, FAKE, FAKE, FAKE, FAKE + 64, T, ids, None, 0, FAKE, ws_need, meta, mh_need, 0]

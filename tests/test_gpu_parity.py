@@ -9,8 +9,8 @@ import pytest
 import lora_adapter_pool_amd as L
 import oracle
 import workloads as W
-from gpu_helpers import (TOL, check_rows, make_pool, run_apply, run_entry_points, sample_rows, say,
-                         to_dev, torch_dtype, y_to_np)
+from gpu_helpers import (TOL, check_rows, make_pool, plan_v, run_apply, run_entry_points,
+                         sample_rows, say, to_dev, torch_dtype, y_to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -327,9 +327,7 @@ def test_plan_reused_across_layers(dtype):
         assert plan["mfma_tiles"] > 0
     assert plan["wave_tiles"] > 0
     image = torch.from_numpy(img).cuda()
-    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
-    v = torch.full((plan["ksplit"] * max(rows, 1), wl.num_slices * pool.R), float("nan"),
-                   dtype=torch.float32, device="cuda")
+    v = plan_v(plan, wl.num_slices, pool.R, float("nan"))
     rng = np.random.default_rng(11)
     layers = [wl, dataclasses.replace(
         wl, x=W.to_dtype_values(rng.standard_normal((wl.T, wl.in_features)), dtype),
@@ -359,7 +357,7 @@ def test_small_plan_by_value(dtype, T, n_adapters):
     outs = []
     for by_value in (True, False):
         xd, yd = to_dev(wl.x, dtype), to_dev(wl.y_in, dtype)
-        v = torch.full((rows, pool.R), float("nan"), dtype=torch.float32, device="cuda")
+        v = plan_v(plan, wl.num_slices, pool.R, float("nan"))
         dev_img = None if by_value else image
         host_img = img if by_value else None
         L.lora_plan_shrink(pool.desc, xd, pool.A, v, wl.T, plan, dev_img, host_img)
@@ -464,8 +462,7 @@ def test_one_launch_decode_matches_two_launches(T):
         outs.append(yd.clone())
         bad = np.argwhere(yd.float().cpu().numpy() != exp)
         assert bad.size == 0, f"call {call}: {len(bad)} mismatches, first {bad[:3]}"
-    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
-    v = torch.zeros((rows, wl.num_slices * pool.R), dtype=torch.float32, device="cuda")
+    v = plan_v(plan, wl.num_slices, pool.R)
     y2 = to_dev(wl.y_in, wl.dtype)
     L.lora_plan_shrink(pool.desc, xd, pool.A, v, wl.T, plan, None, img)
     L.lora_plan_expand(pool.desc, v, pool.B, y2, wl.T, plan, None, img)
@@ -495,8 +492,7 @@ def test_one_launch_decode_exact(R, K):
     y = run_apply(wl, pool=pool)
     bad = np.argwhere(y.float().cpu().numpy() != exp)
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
-    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
-    v = torch.zeros((rows, wl.num_slices * pool.R), dtype=torch.float32, device="cuda")
+    v = plan_v(plan, wl.num_slices, pool.R)
     xd, y2 = to_dev(wl.x, wl.dtype), to_dev(wl.y_in, wl.dtype)
     L.lora_plan_shrink(pool.desc, xd, pool.A, v, wl.T, plan, None, img)
     L.lora_plan_expand(pool.desc, v, pool.B, y2, wl.T, plan, None, img)
@@ -547,3 +543,45 @@ def test_graph_capture_replays():
         torch.cuda.synchronize()
         bad = np.argwhere(yd.float().cpu().numpy() != exp)
         assert bad.size == 0, f"replay {rep}: {len(bad)} mismatches, first {bad[:3]}"
+
+
+@pytest.mark.parametrize("R,T,parts", [(16, 200, "1"), (16, 200, "3"), (16, 600, "8"),
+                                       (16, 600, None), (32, 200, "4"), (48, 80, "2"),
+                                       (64, 600, None), (64, 40, "1")])
+def test_tile_mfma_shrink_split_exact(R, T, parts, monkeypatch):
+    """Decode batches on the wavefront tiles' MFMA shrink (bf16, R <= 64): K
+    split into 1 .. 8 partials (summed by the expand), plans by value (<= 48
+    tiles) and as a device image (> 48 tiles), rank tiles of 16 with ranks
+    past R as padding (R = 48), K = 1064 (not a multiple of 32) and a ragged
+    last column chunk.  Integer inputs make every order of summation exact, so
+    the result equals the oracle bit for bit."""
+    if parts:
+        monkeypatch.setenv("LORA_WAVE_KSPLIT", parts)
+    wl = W.config_integer(seed=40 + R, T=T, K=1064, outs=(520, 136), max_loras=30,
+                          max_lora_rank=R, ranks=(R, R // 2 // 8 * 8 or 8), dtype="bf16")
+    rng = np.random.default_rng(T + R)
+    ids = rng.integers(-1, 30, size=T).astype(np.int32)
+    wl = dataclasses.replace(wl, ids=ids, prefill=np.zeros(T, np.uint8))
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    plan, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] == 0 and plan["wave_tiles"] > 12 or R > 32
+    if parts:
+        assert plan["ksplit_wave"] == int(parts)
+    say(f"  R={R} T={T} wave tiles={plan['wave_tiles']} ksplit_wave={plan['ksplit_wave']}")
+    exp = _exact_expected(wl)
+    y = run_apply(wl).float().cpu().numpy()
+    bad = np.argwhere(y != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
+@pytest.mark.parametrize("R", [16, 64])
+def test_tile_mfma_shrink_random(R):
+    """The same path on random values at the fused QKV decode shape (reduced
+    batch): within tolerance of the fp64 oracle."""
+    wl = W.config_qkv_decode(seed=3, T=120) if R == 16 else \
+        W.config_bgmv_decode(seed=14, T=200, K=4096, O=2048, n_adapters=24, rank=R)
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    plan, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] == 0 and plan["ksplit_wave"] > 1
+    y = run_apply(wl)
+    check_rows(wl, y, label=f"tile MFMA shrink R={R} ksplit_wave={plan['ksplit_wave']}")

@@ -6,9 +6,10 @@ import numpy as np
 import pytest
 
 import lora_adapter_pool_amd as L
+from lora_adapter_pool_amd import _lib
 import workloads as W
 
-WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS, MAX_KSPLIT = 8, 64, 16, 4
+WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS, MAX_KSPLIT, MAX_KSPLIT_MFMA = 8, 64, 16, 8, 4
 BGMV_MFMA_MIN_ROWS, BGMV_MFMA_MIN_TOTAL = 48, 1024
 INT32_MAX = np.iinfo(np.int32).max
 
@@ -96,9 +97,21 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
     if p["mfma_tiles"]:
         wgs = p["mfma_tiles"] * desc.num_slices * -(-R // 64)
         ksteps = -(-desc.in_features // 64)
-        while want_split < MAX_KSPLIT and wgs * want_split < 512 and ksteps // (2 * want_split) >= 4:
+        while want_split < MAX_KSPLIT_MFMA and wgs * want_split < 512 and ksteps // (2 * want_split) >= 4:
             want_split *= 2
     assert p["ksplit"] == want_split
+    # K split of the wavefront tiles (bf16, R <= 64): grown while the launch has
+    # < 1024 workgroups and each part keeps one load batch (4 waves x CB chunks
+    # of 32; CB = 8, 6, 4 for R <= 16, 32, 64), up to 8 (R <= 16) or 4 parts
+    want_wave = 1
+    if desc.dtype == _lib.LORA_BF16 and p["wave_tiles"] and R <= 64:
+        cb = 8 if R <= 16 else 6 if R <= 32 else 4
+        nk = -(-desc.in_features // 32)
+        wgs = p["wave_tiles"] * desc.num_slices
+        top = MAX_KSPLIT if R <= 16 else 4
+        while want_wave < top and wgs * want_wave < 1024 and nk // (want_wave + 1) >= 4 * cb:
+            want_wave += 1
+    assert p["ksplit_wave"] == want_wave and p["reserved"] == 0
     assert p["image_bytes"] + p["image_offset"] <= L.lora_apply_host_meta_bytes(desc, ids.size)
     return p
 
@@ -181,7 +194,8 @@ def test_plan_entry_validation_before_hip():
 
     for fn in (L.lora_plan_shrink, L.lora_plan_expand):
         for key, val in (("wave_tiles", -1), ("off_wave", -4), ("num_bgmv_rows", -2), ("ksplit", 0),
-                         ("ksplit", MAX_KSPLIT + 1)):
+                         ("ksplit", MAX_KSPLIT_MFMA + 1), ("ksplit_wave", 0),
+                         ("ksplit_wave", MAX_KSPLIT + 1)):
             assert status(fn, dict(p, **{key: val})) == _lib.LORA_E_ARG
         assert status(fn, dict(p, image_bytes=p["image_bytes"] - 4)) == _lib.LORA_E_ARG
         assert status(fn, p, image=FAKE + 4) == _lib.LORA_E_ALIGN
