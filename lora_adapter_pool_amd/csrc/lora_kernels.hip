@@ -115,6 +115,15 @@ template <> struct El<uint16_t> {
   }
 };
 
+// Lane i of each row of 16 lanes takes the value of lane (i + 8) % 16 (DPP
+// row_ror:8).
+__device__ __forceinline__ u32x4 rot8_rows16(u32x4 v) {
+  return u32x4{(uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0x128, 0xf, 0xf, false),
+               (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0x128, 0xf, 0xf, false),
+               (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, 0x128, 0xf, 0xf, false),
+               (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, 0x128, 0xf, 0xf, false)};
+}
+
 // Workgroups are dealt round-robin over the XCDs; give each XCD a contiguous
 // range of logical ids (a bijection on [0, n)).
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -584,6 +593,33 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
   }
 }
 
+// One 64-wide K step of the decode-tile shrink, loaded as whole 128-byte
+// lines: lane l holds 8 elements at k = 8 (l / 8) of token row l % 8 (xv) and
+// of ranks 16 t + 8 j + l % 8 (av[t][j]); msk zeroes a lane past K.  An MFMA
+// sums over its 32 k in any order, so the step is two MFMAs over the halves
+// S0 = {16 g .. 16 g + 8} and S1 = {16 g + 8 .. 16 g + 16} (g = l / 16, the
+// operand's k group): the S1 half of rows 0..7 (and the S0 half of ranks
+// 8..15) sits 8 lanes away and a DPP rotate within each row of 16 lanes brings
+// it over.  MFMA rows 8..15 are never used.
+template <int NT>
+__device__ __forceinline__ void tile_step_mfma(const u32x4& xv, const u32x4 (&av)[NT][2],
+                                               uint32_t msk, bool lo8, f32x4 (&d)[NT]) {
+  const u32x4 xm = xv & msk;
+  const bf16x8 x0 = __builtin_bit_cast(bf16x8, xm);
+  const bf16x8 x1 = __builtin_bit_cast(bf16x8, rot8_rows16(xm));
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const u32x4 a0 = av[t][0] & msk, a1 = av[t][1] & msk;
+    const u32x4 r0 = rot8_rows16(a0), r1 = rot8_rows16(a1);
+    const u32x4 b0 = lo8 ? a0 : r1;  // ranks at S0
+    const u32x4 b1 = lo8 ? r0 : a1;  // ranks at S1
+    d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, __builtin_bit_cast(bf16x8, b0), d[t], 0, 0,
+                                                   0);
+    d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, __builtin_bit_cast(bf16x8, b1), d[t], 0, 0,
+                                                   0);
+  }
+}
+
 // ------------------------------------------ decode in one launch (bf16, MFMA)
 //
 // For small decode plans (records passed by value, bf16, R <= 32): a
@@ -597,10 +633,11 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
 // grid = tiles * column chunks, 512 threads (8 waves).
 //   shrink: D[m][n] = sum_k x[tok[m]][k] A[a][s][n][k] as v_mfma_f32_16x16x32_bf16
 //           tiles (rows m = tokens, 8 of 16 used; columns n = ranks, NT tiles
-//           of 16), the 32-wide K chunks dealt round-robin over the waves, CB
-//           chunks per wave loaded at once (CB = the wave's share of K, up to
-//           16 / NT); the waves' partial tiles are summed in a fixed order in
-//           LDS.
+//           of 16), loads of whole 128-byte lines (tile_step_mfma), the
+//           64-wide K steps dealt round-robin over the waves, CB / 2 steps per
+//           wave loaded at once (CB = the wave's share of K in 32-wide chunks,
+//           up to 16 / NT); the waves' partial tiles are summed in a fixed
+//           order in LDS.
 // Every workgroup pulls the adapter's A rows and the tile's x rows through one
 // compute unit, whose few outstanding misses bound the rate, so the form only
 // pays where a second launch costs more: plans of at most kArgTilesS tiles.
@@ -617,7 +654,8 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
     uint16_t* __restrict__ y, RowList L, Geo g, Chunks ch, PlanArg<MODE> pa) {
   constexpr int TM = kWaveTileRows;
   constexpr int RM = 16 * NT;          // ranks covered by the MFMA tiles (>= R)
-  static_assert(CB * (1 + NT) <= 32, "a batch keeps at most 32 loads per lane in flight");
+  static_assert(CB % 2 == 0 && CB / 2 * (1 + 2 * NT) <= 24,
+                "a batch keeps at most 24 loads per lane in flight");
   static_assert(TM <= 16, "tile rows fit one MFMA tile");
   __shared__ float red[kOnepassWaves][16][RM + 1];
   __shared__ float vs[TM][RM];
@@ -636,53 +674,54 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = g.R;
 
-  // shrink: lane l feeds row m = l % 16 and K offset kq = 8 (l / 16) of each
-  // 32-wide chunk; rows past the tile repeat row 0 and ranks past R repeat
+  // shrink: whole 128-byte lines per load, two MFMAs per 64-wide K step
+  // (tile_step_mfma); rows past the tile repeat row 0 and ranks past R repeat
   // rank R - 1 (their outputs are never used)
-  const int m = lane & 15, kq = (lane >> 4) * 8;
+  constexpr int SB = CB / 2;  // K steps of 64 per wave per batch
+  const int m = lane & 15;
+  const int r8 = lane & 7, kx = (lane >> 3) * 8;
+  // (a lane with kx >= K only ever loads masked steps; kxa keeps its address
+  // inside the row, which holds K >= 8 elements)
+  const int kxa = min(kx, g.K - 8);
   int tk = tr.tok[0];
 #pragma unroll
   for (int r = 1; r < TM; ++r)
-    if (m == r) tk = tr.tok[r];
-  // (a lane with kq >= K only ever loads masked chunks; kqa keeps its address
-  // inside the row, which holds K >= 8 elements)
-  const int kqa = min(kq, g.K - 8);
-  const uint16_t* xp = x + (size_t)tk * g.K + kqa;
-  const uint16_t* ap[NT];
+    if (r8 == r) tk = tr.tok[r];
+  const uint16_t* xp = x + (size_t)tk * g.K + kxa;
+  const uint16_t* ap[NT][2];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    ap[t] = A + ((size_t)(a * g.S + s) * R + min(16 * t + m, R - 1)) * g.K + kqa;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      ap[t][j] = A + ((size_t)(a * g.S + s) * R + min(16 * t + 8 * j + r8, R - 1)) * g.K + kxa;
+  const bool lo8 = m < 8;
   f32x4 d[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nk = (g.K + 31) / 32;
-  u32x4 xv[CB], av[CB][NT];
-  uint32_t msk[CB];
+  const int nst = (g.K + 63) / 64;
+  u32x4 xv[SB], av[SB][NT][2];
+  uint32_t msk[SB];
   // every load of a batch is issued before the first MFMA waits on one, so a
   // batch costs one memory round trip
   auto load_batch = [&](int c0) {
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const int k = (c0 + u * kOnepassWaves) * 32;
-      const bool ok = k + kq < g.K;
+    for (int u = 0; u < SB; ++u) {
+      const int k = (c0 + u * kOnepassWaves) * 64;
+      const bool ok = k + kx < g.K;
       const int kc = ok ? k : 0;
       msk[u] = all_or_none(ok);
       xv[u] = ld16(xp + kc);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) av[u][t] = ld16(ap[t] + kc);
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) av[u][t][j] = ld16(ap[t][j] + kc);
     }
   };
   auto mma_batch = [&] {
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const bf16x8 xo = __builtin_bit_cast(bf16x8, xv[u] & msk[u]);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            xo, __builtin_bit_cast(bf16x8, av[u][t] & msk[u]), d[t], 0, 0, 0);
-    }
+    for (int u = 0; u < SB; ++u) tile_step_mfma<NT>(xv[u], av[u], msk[u], lo8, d);
   };
-  constexpr int kStride = kOnepassWaves * CB;
+  constexpr int kStride = kOnepassWaves * SB;
   load_batch(wave);
 
   // y of the tile's rows and this thread's B row (needed last, issued after
@@ -698,7 +737,7 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
   for (int q = 0; q < 2 * NT; ++q) braw[q] = ld16(Bg + min(8 * q, R - 8)) & all_or_none(8 * q < R);
   __builtin_amdgcn_sched_barrier(0);
   mma_batch();
-  for (int c0 = wave + kStride; c0 < nk; c0 += kStride) {
+  for (int c0 = wave + kStride; c0 < nst; c0 += kStride) {
     load_batch(c0);
     __builtin_amdgcn_sched_barrier(0);
     mma_batch();
@@ -743,23 +782,32 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
 //
 // grid = tiles * S * kparts, 256 threads (4 waves).  Workgroup (tile, slice s,
 // part p) writes partial p of v for the tile's rows: the sum over the part's
-// contiguous range of 32-wide K chunks of
+// contiguous range of 64-wide K steps of
 //   D[m][n] = sum_k x[tok[m]][k] * A_pool[a][s][n][k]
-// as v_mfma_f32_16x16x32_bf16 tiles (rows m = the tile's tokens, 8 of 16 used;
-// columns n = ranks, NT tiles of 16).  Every rank of the slice comes out of one
-// pass over x, where the VALU shrink reads x once per 4-rank chunk.  The
-// part's chunks are dealt round-robin over the waves; a wave issues the loads
-// of CB chunks before the first MFMA of the batch waits on them.  The waves'
-// partial tiles are summed in a fixed order in LDS, so the result does not
-// depend on timing.  Splitting K over workgroups spreads the x and A loads
-// over more compute units, each of which issues only so many loads per cycle.
+// as v_mfma_f32_16x16x32_bf16 tiles (rows m = the tile's tokens, columns n =
+// ranks, NT tiles of 16).  Every rank of the slice comes out of one pass over
+// x, where the VALU shrink reads x once per 4-rank chunk.
+//
+// Loads cover whole 128-byte lines: per K step, lane l loads 8 elements at
+// k = 8 (l / 8) of row l % 8 (one instruction for the 8 token rows of x, two
+// per 16 ranks of A).  An MFMA sums over its 32 k in any order, so each step
+// is two MFMAs over the halves S0 = {16 g .. 16 g + 8} and S1 = {16 g + 8 ..
+// 16 g + 16} (g = l / 16, the operand's k group); a DPP rotate by 8 lanes
+// within each row of 16 moves the S1 half of rows 0..7 (and of ranks 8..15)
+// to the lanes the MFMA reads it from.  MFMA rows 8..15 are never used.
+//
+// The part's steps are dealt round-robin over the waves; a wave issues the
+// loads of CB / 2 steps before the first MFMA of the batch waits on them.  The
+// waves' partial tiles are summed in a fixed order in LDS, so the result does
+// not depend on timing.  Splitting K over workgroups spreads the x and A
+// loads over more compute units.
 template <int NT, int CB, int MODE>
 __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, float* __restrict__ v,
     RowList L, Geo g, int kparts, int v_rows, PlanArg<MODE> pa) {
-  constexpr int TM = kWaveTileRows, NW = kTileShrinkWaves, RM = 16 * NT;
-  static_assert(TM <= 16 && TM % 4 == 0, "tile rows fit one MFMA tile");
-  static_assert(CB * (1 + NT) <= 24, "a batch keeps at most 24 loads per lane in flight");
+  constexpr int TM = kWaveTileRows, NW = kTileShrinkWaves, RM = 16 * NT, SB = CB / 2;
+  static_assert(TM == 8, "x rows fill lanes l % 8");
+  static_assert(SB >= 1 && SB * (1 + 2 * NT) <= 18, "a batch keeps at most 18 loads per lane in flight");
   __shared__ float red[NW][TM][RM + 1];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_tile = g.S * kparts;
@@ -772,51 +820,48 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
   const int a = tr.aid[0];  // one adapter per tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = g.R;
-  const int nk = (g.K + 31) / 32;
-  const int per = (nk + kparts - 1) / kparts;
-  const int c_lo = min(nk, part * per), c_hi = min(nk, c_lo + per);
+  const int nst = (g.K + 63) / 64;
+  const int per = (nst + kparts - 1) / kparts;
+  const int s_lo = min(nst, part * per), s_hi = min(nst, s_lo + per);
 
-  // lane l feeds row m = l % 16 and K offset kq = 8 (l / 16) of each chunk;
-  // rows past the tile repeat row 0 and ranks past R repeat rank R - 1 (their
-  // outputs are never used)
-  const int m = lane & 15, kq = (lane >> 4) * 8;
+  // load roles: row l % 8 (token, or rank 8 j + l % 8 of a rank tile), k offset
+  // 8 (l / 8) of the step (kept inside the row for K < 64: lanes past K only
+  // ever load masked steps)
+  const int r8 = lane & 7, kx = (lane >> 3) * 8;
+  const int kxa = min(kx, g.K - 8);
   int tk = tr.tok[0];
 #pragma unroll
   for (int r = 1; r < TM; ++r)
-    if (m == r) tk = tr.tok[r];
-  // (a lane with kq >= K only ever loads masked chunks; kqa keeps its address
-  // inside the row, which holds K >= 8 elements)
-  const int kqa = min(kq, g.K - 8);
-  const uint16_t* xp = x + (size_t)tk * g.K + kqa;
-  const uint16_t* ap[NT];
+    if (r8 == r) tk = tr.tok[r];
+  const uint16_t* xp = x + (size_t)tk * g.K + kxa;
+  const uint16_t* ap[NT][2];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    ap[t] = A + ((size_t)(a * g.S + s) * R + min(16 * t + m, R - 1)) * g.K + kqa;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      ap[t][j] = A + ((size_t)(a * g.S + s) * R + min(16 * t + 8 * j + r8, R - 1)) * g.K + kxa;
+  const bool lo8 = (lane & 15) < 8;  // operand rows / ranks 0..7 of a tile
   f32x4 d[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = c_lo + wave; c0 < c_hi; c0 += NW * CB) {
-    u32x4 xv[CB], av[CB][NT];
-    uint32_t msk[CB];
+  for (int c0 = s_lo + wave; c0 < s_hi; c0 += NW * SB) {
+    u32x4 xv[SB], av[SB][NT][2];
+    uint32_t msk[SB];
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const int c = c0 + u * NW;
-      const bool ok = c < c_hi && c * 32 + kq < g.K;
-      const int kc = ok ? c * 32 : 0;
+    for (int u = 0; u < SB; ++u) {
+      const int st = c0 + u * NW;
+      const bool ok = st < s_hi && st * 64 + kx < g.K;
+      const int kc = ok ? st * 64 : 0;
       msk[u] = all_or_none(ok);
       xv[u] = ld16(xp + kc);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) av[u][t] = ld16(ap[t] + kc);
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) av[u][t][j] = ld16(ap[t][j] + kc);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const bf16x8 xo = __builtin_bit_cast(bf16x8, xv[u] & msk[u]);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            xo, __builtin_bit_cast(bf16x8, av[u][t] & msk[u]), d[t], 0, 0, 0);
-    }
+    for (int u = 0; u < SB; ++u) tile_step_mfma<NT>(xv[u], av[u], msk[u], lo8, d);
   }
   // lane l holds D[4 (l / 16) + j][l % 16] of each rank tile; lanes 0 .. 4 TM - 1
   // hold the tile's rows
@@ -824,7 +869,7 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) red[wave][4 * (lane >> 4) + j][16 * t + m] = d[t][j];
+      for (int j = 0; j < 4; ++j) red[wave][4 * (lane >> 4) + j][16 * t + (lane & 15)] = d[t][j];
   }
   __syncthreads();
   const int SR = g.S * R;
