@@ -45,15 +45,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- helpers
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                   // nearest, ties to even
-  return u >> 16;
+// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32 converts two values per instruction; lo lands in bits
+// 0..15, hi in bits 16..31.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -1019,7 +1022,7 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
     for (int i = 0; i < 4; ++i) {
       const float lo = __uint_as_float(wi[i] << 16) + add[2 * i];
       const float hi = __uint_as_float(wi[i] & 0xffff0000u) + add[2 * i + 1];
-      o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+      o[i] = pack_bf16x2(lo, hi);
     }
     const int yc = col0 + 32 * (wave + NW * q) + 8 * g4;
     const uint32_t off = (tok_ok && yc < out_s)
@@ -1328,7 +1331,7 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
     for (int i = 0; i < 4; ++i) {
       const float lo = __uint_as_float(wi[i] << 16) + add[2 * i];
       const float hi = __uint_as_float(wi[i] & 0xffff0000u) + add[2 * i + 1];
-      o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+      o[i] = pack_bf16x2(lo, hi);
     }
     *reinterpret_cast<u32x4*>(yp) = u32x4{o[0], o[1], o[2], o[3]};
   }
@@ -1505,7 +1508,7 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
       for (int i = 0; i < 4; ++i) {
         const float lo = __uint_as_float(wi[i] << 16) + add[2 * i];
         const float hi = __uint_as_float(wi[i] & 0xffff0000u) + add[2 * i + 1];
-        o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+        o[i] = pack_bf16x2(lo, hi);
       }
       const int col = col0 + 32 * q + 8 * grp;
       const uint32_t off = (my_tok >= 0 && col < out_s)
