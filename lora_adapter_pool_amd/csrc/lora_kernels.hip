@@ -119,13 +119,18 @@ template <> struct El<uint16_t> {
 };
 
 // Lane i of each row of 16 lanes takes the value of lane (i + 8) % 16 (DPP
-// row_ror:8).
+// row_ror:8).  A DPP move reads its source lane whether or not that lane is
+// active, and an inactive source gives no defined value, so the moves must run
+// with every lane active: results are combined with pick() (bit masks), never
+// with a conditional the compiler could turn into a branch around the move.
 __device__ __forceinline__ u32x4 rot8_rows16(u32x4 v) {
   return u32x4{(uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0x128, 0xf, 0xf, false),
                (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0x128, 0xf, 0xf, false),
                (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, 0x128, 0xf, 0xf, false),
                (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, 0x128, 0xf, 0xf, false)};
 }
+// a where the lane mask m is all ones, b where it is zero (no branch)
+__device__ __forceinline__ u32x4 pick(uint32_t m, u32x4 a, u32x4 b) { return (a & m) | (b & ~m); }
 
 // Workgroups are dealt round-robin over the XCDs; give each XCD a contiguous
 // range of logical ids (a bijection on [0, n)).
@@ -606,7 +611,7 @@ __global__ __launch_bounds__(256) void expand_wave_kernel(const float* __restric
 // it over.  MFMA rows 8..15 are never used.
 template <int NT>
 __device__ __forceinline__ void tile_step_mfma(const u32x4& xv, const u32x4 (&av)[NT][2],
-                                               uint32_t msk, bool lo8, f32x4 (&d)[NT]) {
+                                               uint32_t msk, uint32_t lo8, f32x4 (&d)[NT]) {
   const u32x4 xm = xv & msk;
   const bf16x8 x0 = __builtin_bit_cast(bf16x8, xm);
   const bf16x8 x1 = __builtin_bit_cast(bf16x8, rot8_rows16(xm));
@@ -614,8 +619,8 @@ __device__ __forceinline__ void tile_step_mfma(const u32x4& xv, const u32x4 (&av
   for (int t = 0; t < NT; ++t) {
     const u32x4 a0 = av[t][0] & msk, a1 = av[t][1] & msk;
     const u32x4 r0 = rot8_rows16(a0), r1 = rot8_rows16(a1);
-    const u32x4 b0 = lo8 ? a0 : r1;  // ranks at S0
-    const u32x4 b1 = lo8 ? r0 : a1;  // ranks at S1
+    const u32x4 b0 = pick(lo8, a0, r1);  // ranks at S0
+    const u32x4 b1 = pick(lo8, r0, a1);  // ranks at S1
     d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, __builtin_bit_cast(bf16x8, b0), d[t], 0, 0,
                                                    0);
     d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, __builtin_bit_cast(bf16x8, b1), d[t], 0, 0,
@@ -674,7 +679,8 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
   TileRows<TM> tr;
   if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.valid == 0) return;
   const int a = tr.aid[0];  // one adapter per tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int R = g.R;
 
   // shrink: whole 128-byte lines per load, two MFMAs per 64-wide K step
@@ -697,7 +703,7 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       ap[t][j] = A + ((size_t)(a * g.S + s) * R + min(16 * t + 8 * j + r8, R - 1)) * g.K + kxa;
-  const bool lo8 = m < 8;
+  const uint32_t lo8 = all_or_none(m < 8);
   f32x4 d[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -821,7 +827,8 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
   TileRows<TM> tr;
   if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.valid == 0) return;
   const int a = tr.aid[0];  // one adapter per tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int R = g.R;
   const int nst = (g.K + 63) / 64;
   const int per = (nst + kparts - 1) / kparts;
@@ -843,7 +850,7 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       ap[t][j] = A + ((size_t)(a * g.S + s) * R + min(16 * t + 8 * j + r8, R - 1)) * g.K + kxa;
-  const bool lo8 = (lane & 15) < 8;  // operand rows / ranks 0..7 of a tile
+  const uint32_t lo8 = all_or_none((lane & 15) < 8);  // operand rows / ranks 0..7 of a tile
   f32x4 d[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -927,7 +934,8 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
   TileRows<TM> tr;
   if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.valid == 0) return;
   const int a = tr.aid[0];  // one adapter per tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int i16 = lane & 15, g4 = lane >> 4;
   const int R = g.R;
   const int np = KP == 1 ? 1 : kparts;
@@ -1075,7 +1083,8 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
   __shared__ __align__(16) uint16_t xs[2][TM * LDS_ROW];
   __shared__ __align__(16) uint16_t as[2][NR * LDS_ROW];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int wm = wave & 1, wr = wave >> 1;
   const int i16 = lane & 15, grp = lane >> 4;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -1215,7 +1224,8 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
   __shared__ __align__(16) uint16_t ys[TM * LDY];
   __shared__ int s_tok[TM];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int m16 = lane & 15, grp = lane >> 4;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / ch.total;
@@ -1377,7 +1387,8 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
   __shared__ __align__(16) uint16_t vl[TM * LDK];
   __shared__ int s_tok[TM];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int m16 = lane & 15, grp = lane >> 4;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / gr.total;
