@@ -127,9 +127,12 @@ int32_t bgmv_mfma_min_rows() {
   return v;
 }
 
-int32_t bgmv_mfma_min_total() {
-  static const int32_t v = env_rows("LORA_BGMV_MFMA_MIN_TOTAL", 1024);
-  return v;
+int32_t bgmv_mfma_min_total(int32_t R) {
+  // 0: no override; a 64-row tile reads each adapter row once where eight
+  // 8-row tiles read it eight times, which pays sooner the more ranks there are
+  static const int32_t v = env_rows("LORA_BGMV_MFMA_MIN_TOTAL", INT32_MAX);
+  if (v != INT32_MAX) return v;
+  return R <= 16 ? 2048 : 1024;
 }
 
 // Stable counting sort of the two row sets by adapter id.  Bucket sizes are a
@@ -227,7 +230,7 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
       if (j - i >= bgmv_mfma_min_rows()) long_rows += j - i;
       i = j;
     }
-    if (long_rows > 0 && long_rows >= bgmv_mfma_min_total()) bthr = bgmv_mfma_min_rows();
+    if (long_rows > 0 && long_rows >= bgmv_mfma_min_total(g.R)) bthr = bgmv_mfma_min_rows();
   }
   int32_t* img = stage + sl.image;
   const int64_t off_wave = align_up((int64_t)ns + nb, 4);

@@ -53,11 +53,11 @@ int64_t align_up(int64_t v, int64_t a);
 // environment variable LORA_SGMV_MFMA_MIN_ROWS overrides the default of 16.
 int32_t sgmv_mfma_min_rows();
 // BGMV runs of one adapter at least bgmv_mfma_min_rows long (default 48,
-// LORA_BGMV_MFMA_MIN_ROWS) run on MFMA tiles when such runs hold at least
-// bgmv_mfma_min_total rows of the batch (default 1024,
-// LORA_BGMV_MFMA_MIN_TOTAL).
+// LORA_BGMV_MFMA_MIN_ROWS) run on 64-row MFMA tiles when such runs hold at
+// least bgmv_mfma_min_total(R) rows of the batch (default 2048 for pools of
+// rank R <= 16, else 1024; LORA_BGMV_MFMA_MIN_TOTAL overrides both).
 int32_t bgmv_mfma_min_rows();
-int32_t bgmv_mfma_min_total();
+int32_t bgmv_mfma_min_total(int32_t R);
 
 // MFMA shrink of wavefront tiles (bf16 pools, R <= 64): rank tiles of 16 it
 // computes (R = 48 takes 4) and the 32-wide K chunks each wave loads per batch.

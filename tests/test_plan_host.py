@@ -10,7 +10,14 @@ from lora_adapter_pool_amd import _lib
 import workloads as W
 
 WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS, MAX_KSPLIT, MAX_KSPLIT_MFMA = 8, 64, 16, 8, 4
-BGMV_MFMA_MIN_ROWS, BGMV_MFMA_MIN_TOTAL = 48, 1024
+BGMV_MFMA_MIN_ROWS = 48
+
+
+def bgmv_mfma_min_total(R):
+    """Rows in long runs a decode batch needs before those runs take 64-row
+    MFMA tiles: 2048 for pools of rank <= 16, else 1024."""
+    return 2048 if R <= 16 else 1024
+
 INT32_MAX = np.iinfo(np.int32).max
 
 
@@ -47,7 +54,8 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
     # BGMV runs take MFMA tiles only in bf16 batches whose long runs hold many rows
     runs = _bgmv_runs(m["bgmv_ids"])
     long_rows = sum(ln for _, ln in runs if ln >= BGMV_MFMA_MIN_ROWS)
-    bthr = BGMV_MFMA_MIN_ROWS if bf16 and long_rows >= max(1, BGMV_MFMA_MIN_TOTAL) else INT32_MAX
+    bthr = (BGMV_MFMA_MIN_ROWS if bf16 and long_rows >= bgmv_mfma_min_total(desc.max_lora_rank)
+            else INT32_MAX)
     assert p["bgmv_mfma_min_rows"] == bthr
     run_len_of_row = np.zeros(nb, np.int64)
     for st, ln in runs:
@@ -152,12 +160,14 @@ def test_plan_fuzz():
         _check_plan(d, ids, pre if it % 5 else None, bgmv_max_rank=int(rng.choice([0, 8, 128])))
 
 
-@pytest.mark.parametrize("T,n,want_mfma", [(64, 8, False), (512, 4, False), (1024, 8, True),
-                                           (1024, 64, False), (4096, 64, True)])
-def test_plan_bgmv_runs_on_mfma(T, n, want_mfma):
+@pytest.mark.parametrize("T,n,rank,want_mfma", [(64, 8, 16, False), (512, 4, 16, False),
+                                                (1024, 8, 16, False), (2048, 8, 16, True),
+                                                (1024, 8, 64, True), (1024, 64, 64, False),
+                                                (4096, 64, 16, True)])
+def test_plan_bgmv_runs_on_mfma(T, n, rank, want_mfma):
     """Decode batches: sorted runs of one adapter go to MFMA tiles only when
-    the batch is large and its runs are long."""
-    wl = W.config_bgmv_decode(seed=1, T=T, K=256, O=256, n_adapters=n, rank=16, p_none=0.0)
+    the batch is large (sooner for a higher pool rank) and its runs are long."""
+    wl = W.config_bgmv_decode(seed=1, T=T, K=256, O=256, n_adapters=n, rank=rank, p_none=0.0)
     d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
     p = _check_plan(d, wl.ids, wl.prefill)
     assert (p["mfma_tiles"] > 0) == want_mfma
