@@ -102,7 +102,7 @@ int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const voi
   *tp = TilePlan{img ? img + p->off_perm : nullptr, img ? img + p->off_wave : nullptr,
                  p->wave_tiles, img ? img + p->off_mfma : nullptr, p->mfma_tiles,
                  host ? host + p->off_wave : nullptr, p->ksplit,
-                 p->num_sgmv_rows + p->num_bgmv_rows, p->ksplit_wave};
+                 p->num_sgmv_rows + p->num_bgmv_rows, p->ksplit_wave, nullptr, nullptr, nullptr};
   return LORA_OK;
 }
 
@@ -270,11 +270,18 @@ int32_t lora_plan_expand(const lora_pool_desc* desc, const float* v, const void*
   return run_plan_expand(g, v, B_pool, y, tp, (hipStream_t)stream);
 }
 
-int32_t lora_plan_apply(const lora_pool_desc* desc, const void* x, const void* A_pool,
+}  // extern "C"
+
+namespace {
+
+// lora_plan_apply, plus: with copy_to set (device memory of at least
+// plan->image_bytes, the workspace's image region) the shrink launches copy
+// the plan records and MFMA-tile tokens they read into copy_to (the image's
+// offsets) and the expand launches read that copy.
+int32_t plan_apply_impl(const lora_pool_desc* desc, const void* x, const void* A_pool,
                         const void* B_pool, void* y, int32_t T, const lora_plan* plan,
                         const void* image, const void* image_host, void* ws, int64_t ws_bytes,
-                        void* stream) {
-  clear_error();
+                        void* stream, int32_t* copy_to) {
   Geo g;
   if (int32_t e = check_desc(desc, &g)) return e;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
@@ -293,9 +300,27 @@ int32_t lora_plan_apply(const lora_pool_desc* desc, const void* x, const void* A
   if ((int64_t)std::max(tp.ksplit, tp.ksplit_wave) * tp.num_rows >
       (int64_t)LORA_PLAN_MAX_KSPLIT * T)
     return fail(LORA_E_ARG, "malformed plan (%d rows for %d tokens)", tp.num_rows, T);
+  if (copy_to) {
+    tp.copy_perm = copy_to + plan->off_perm;
+    tp.copy_wave = copy_to + plan->off_wave;
+    tp.copy_mfma = copy_to + plan->off_mfma;
+  }
   g.T = T;
   return run_plan_apply(g, x, A_pool, B_pool, y, tp, (float*)((char*)ws + wl.v),
                         (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_plan_apply(const lora_pool_desc* desc, const void* x, const void* A_pool,
+                        const void* B_pool, void* y, int32_t T, const lora_plan* plan,
+                        const void* image, const void* image_host, void* ws, int64_t ws_bytes,
+                        void* stream) {
+  clear_error();
+  return plan_apply_impl(desc, x, A_pool, B_pool, y, T, plan, image, image_host, ws, ws_bytes,
+                         stream, nullptr);
 }
 
 // `host` itself when it is pinned host memory (hipHostMalloc) that the device
@@ -338,17 +363,21 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
   const char* image_host = (const char*)meta_host + p.image_offset;
   const bool small = p.mfma_tiles == 0 && p.wave_tiles <= kArgTilesL && g.max_loras <= (1 << 28);
   const void* image = ws;
+  int32_t* copy_to = nullptr;
   if (!small) {  // small plans travel in the kernel arguments instead
     if (const void* mapped = device_alias(image_host)) {
-      image = mapped;  // pinned staging: the kernels read the plan where it lies
+      // pinned staging: the shrink launches read the plan where it lies and
+      // leave a copy in the workspace's image region for the expand launches
+      image = mapped;
+      copy_to = (int32_t*)ws;
     } else if (int32_t e = hip_ok(hipMemcpyAsync(ws, image_host, (size_t)p.image_bytes,
                                                  hipMemcpyHostToDevice, (hipStream_t)stream),
                                   "plan copy")) {
       return e;
     }
   }
-  return lora_plan_apply(desc, x, A_pool, B_pool, y, T, &p, image, image_host, ws, ws_bytes,
-                         stream);
+  return plan_apply_impl(desc, x, A_pool, B_pool, y, T, &p, image, image_host, ws, ws_bytes,
+                         stream, copy_to);
 }
 
 }  // extern "C"

@@ -33,6 +33,11 @@ constexpr int kMaxKsplitWave = LORA_PLAN_MAX_KSPLIT;   // K splits of the wavefr
 //   rows      (ids != nullptr): fixed ranges of rows; ids[i] is row i's adapter.
 //   tile list (tiles != nullptr): num_tiles host-built records (the plan's
 //             layout); tok is the plan's perm (used by the MFMA kernels).
+// In tile-list mode the shrink kernels can also copy what they read of the
+// list into device memory (copy_tiles: the records; copy_tok: the tokens of
+// MFMA tile rows) so that the expand launch reads the copy instead: lora_apply
+// passes a list that lives in pinned host memory, where every read crosses
+// PCIe.
 struct RowList {
   const int32_t* tok;
   const int32_t* ids;
@@ -45,6 +50,8 @@ struct RowList {
   int32_t num_tiles;
   int32_t seg_min;
   int32_t seg_max;
+  int32_t* copy_tiles;
+  int32_t* copy_tok;
 };
 
 inline RowList segments_list(const int32_t* perm, const int32_t* starts, const int32_t* lens,
@@ -74,6 +81,11 @@ struct TilePlan {
   int32_t ksplit;            // partials of the MFMA tiles' shrink
   int32_t num_rows;          // v rows (SGMV rows, then BGMV rows) = entries of perm
   int32_t ksplit_wave;       // partials of the wavefront tiles' shrink (bf16, R <= 64)
+  // device copy of the image (same offsets) that the shrink launches write and
+  // the expand launches read, or nullptr: the expand reads perm / wave / mfma
+  int32_t* copy_perm;
+  int32_t* copy_wave;
+  int32_t* copy_mfma;
 };
 
 // Enqueue the shrink / expand of one row list (segments or rows) on `st`;

@@ -238,7 +238,8 @@ template <int TM> struct TileRows {
 //   kRows: rows f*TM .. of the list, tokens and adapters from tok[] / ids[].
 template <int TM, int MODE>
 __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
-                                          const PlanArg<MODE>& pa, TileRows<TM>& tr) {
+                                          const PlanArg<MODE>& pa, TileRows<TM>& tr,
+                                          bool copy = false) {
   static_assert(TM <= LORA_PLAN_WAVE_WORDS - 4, "a tile record holds at most 12 tokens");
   const int lane = threadIdx.x & 63;
   if constexpr (MODE == kArg || MODE == kArgL) {
@@ -256,6 +257,8 @@ __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
   } else if constexpr (MODE == kList) {
     if (f >= L.num_tiles) return false;
     const int w = L.tiles[(size_t)f * LORA_PLAN_WAVE_WORDS + (lane & 15)];
+    if (copy && L.copy_tiles && threadIdx.x < LORA_PLAN_WAVE_WORDS)
+      L.copy_tiles[(size_t)f * LORA_PLAN_WAVE_WORDS + threadIdx.x] = w;
     const int sid = __builtin_amdgcn_readlane(w, 0);
     tr.cnt = __builtin_amdgcn_readlane(w, 1);
     tr.vrow0 = __builtin_amdgcn_readlane(w, 2);
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(1024) void shrink_wave_kernel(const E* __restrict__
   const int s = rem / nrc;
   const int c = rem - s * nrc;
   TileRows<TM> tr;
-  if (!tile_rows<TM, MODE>(L, g, f, pa, tr)) return;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr, s == 0 && c == 0)) return;
   uint32_t todo = tr.valid;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -825,7 +828,7 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
   const int s = rem / kparts;
   const int part = rem - s * kparts;
   TileRows<TM> tr;
-  if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.valid == 0) return;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr, s == 0 && part == 0) || tr.valid == 0) return;
   const int a = tr.aid[0];  // one adapter per tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
@@ -1044,10 +1047,13 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
 // of the row list, row count and adapter slot, the same in every lane.  The
 // tile-list record is (slot, rows, first row, 0).
 template <int TMR, int MODE>
-__device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int& cnt, int& sid) {
+__device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int& cnt, int& sid,
+                                          bool copy = false) {
   if constexpr (MODE == kList) {
     if (f >= L.num_tiles) return false;
     const int w = L.tiles[(size_t)f * LORA_PLAN_MFMA_WORDS + (threadIdx.x & 3)];
+    if (copy && L.copy_tiles && threadIdx.x < LORA_PLAN_MFMA_WORDS)
+      L.copy_tiles[(size_t)f * LORA_PLAN_MFMA_WORDS + threadIdx.x] = w;
     sid = __builtin_amdgcn_readlane(w, 0);
     cnt = __builtin_amdgcn_readlane(w, 1);
     r0 = __builtin_amdgcn_readlane(w, 2);
@@ -1094,7 +1100,8 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
   const int s = rem / ksplit;
   const int part = rem - s * ksplit;
   int r0, cnt, sid;
-  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid)) return;
+  const bool copy = s == 0 && part == 0 && blockIdx.y == 0;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, copy)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int rank0 = blockIdx.y * NR;
   // K steps of this split
@@ -1112,6 +1119,7 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
   for (int j = 0; j < 2; ++j) {
     const int r = srow + 32 * j;
     const int tk = L.tok[r0 + min(r, cnt - 1)];
+    if (copy && L.copy_tok && c8 == 0 && r < cnt) L.copy_tok[r0 + r] = tk;
     const bool ok = r < cnt && tk >= 0 && tk < g.T;
     xp[j] = x + (size_t)(ok ? tk : 0) * g.K;
     xm[j] = all_or_none(ok);
@@ -1858,11 +1866,20 @@ int32_t run_expand(const Geo& g, const float* v, const void* B, void* y, RowList
             : launch_expand_wave<float, kSegs>(g, v, B, y, Lw, tw, st);
 }
 
-static void plan_lists(const TilePlan& p, RowList& Lw, RowList& Lm) {
-  Lw = RowList{p.perm, nullptr, nullptr, nullptr, nullptr, p.wave, 0, p.num_rows, p.wave_tiles,
-               0, INT32_MAX};
-  Lm = RowList{p.perm, nullptr, nullptr, nullptr, nullptr, p.mfma, 0, p.num_rows,
-               p.mfma_tiles, 0, INT32_MAX};
+// Row lists of a plan's wavefront and MFMA tiles.  for_shrink: the lists read
+// the image and copy it to p.copy_* (when set); else they read the copy.
+static void plan_lists(const TilePlan& p, RowList& Lw, RowList& Lm, bool for_shrink = true) {
+  const bool use_copy = !for_shrink && p.copy_perm && p.copy_wave && p.copy_mfma;
+  const int32_t* perm = use_copy ? p.copy_perm : p.perm;
+  Lw = RowList{perm, nullptr, nullptr, nullptr, nullptr, use_copy ? p.copy_wave : p.wave, 0,
+               p.num_rows, p.wave_tiles, 0, INT32_MAX, nullptr, nullptr};
+  Lm = RowList{perm, nullptr, nullptr, nullptr, nullptr, use_copy ? p.copy_mfma : p.mfma, 0,
+               p.num_rows, p.mfma_tiles, 0, INT32_MAX, nullptr, nullptr};
+  if (for_shrink) {
+    Lw.copy_tiles = p.copy_wave;
+    Lm.copy_tiles = p.copy_mfma;
+    Lm.copy_tok = p.copy_perm;
+  }
 }
 
 // Small plans (wavefront tiles only, at most kArgTilesL records, slots below
@@ -1958,7 +1975,7 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
   const bool bf = g.dtype == LORA_BF16;
   if (p.mfma_tiles > 0 && !bf) return fail(LORA_E_DTYPE, "MFMA tiles need a bf16 pool");
   RowList Lw, Lm;
-  plan_lists(p, Lw, Lm);
+  plan_lists(p, Lw, Lm, /*for_shrink=*/false);
   if (small_plan(p, g)) {
     if (p.wave_tiles <= kArgTilesS)
       return launch_plan_wave_expand<kArg>(g, v, B, y, Lw, p, st, pack_arg<kArg>(p));
