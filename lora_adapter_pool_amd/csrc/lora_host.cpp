@@ -135,6 +135,22 @@ int32_t bgmv_mfma_min_total(int32_t R) {
   return R <= 16 ? 2048 : 1024;
 }
 
+// Every id in [-1, max_loras): a min / max pass (vectorisable), then the
+// first offending row for the message.
+static int32_t check_ids(const int32_t* ids, int32_t T, int32_t max_loras) {
+  int32_t lo = -1, hi = -1;
+  for (int32_t t = 0; t < T; ++t) {
+    lo = std::min(lo, ids[t]);
+    hi = std::max(hi, ids[t]);
+  }
+  if (lo >= -1 && hi < max_loras) return LORA_OK;
+  for (int32_t t = 0; t < T; ++t) {
+    if (ids[t] < -1 || ids[t] >= max_loras)
+      return fail(LORA_E_ID, "ids[%d] = %d is outside [-1, %d)", t, ids[t], max_loras);
+  }
+  return LORA_OK;
+}
+
 // Stable counting sort of the two row sets by adapter id.  Bucket sizes are a
 // histogram over max_loras slots; an exclusive scan gives each id's first
 // position; tokens are then placed in increasing index order, which keeps the
@@ -153,11 +169,41 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
   int32_t* pos_s = cnt_b + max_loras;
   int32_t* pos_b = pos_s + max_loras;
   std::fill(cnt_s, cnt_s + 2 * (size_t)max_loras, 0);
-  for (int32_t t = 0; t < T; ++t) {
+  // rows go by runs of equal (id, set): one counter update per run rather than
+  // one per row, whose store-to-load chain on a single counter would
+  // serialise a sorted prefill batch.  Once a run's second row matches, the
+  // rest of the run is found 16 rows at a time (a compare the compiler
+  // vectorises), so long runs cost little and runs of one row cost one test.
+  const bool per_row_set = !all_sgmv && prefill != nullptr;
+  auto in_sgmv = [&](int32_t t) { return all_sgmv || (prefill && prefill[t]); };
+  auto run_end = [&](int32_t t) {
     const int32_t a = ids[t];
-    if (a < 0) continue;
-    const bool sg = all_sgmv || (prefill && prefill[t]);
-    (sg ? cnt_s : cnt_b)[a]++;
+    const bool sg = in_sgmv(t);
+    int32_t u = t + 1;
+    if (u < T && ids[u] == a && in_sgmv(u) == sg) {
+      ++u;
+      while (u + 16 <= T) {
+        int32_t diff = 0;
+        for (int i = 0; i < 16; ++i) diff |= ids[u + i] ^ a;
+        if (per_row_set) {  // 16 flag bytes: all nonzero (SGMV run) or all zero
+          uint64_t w[2];
+          std::memcpy(w, prefill + u, sizeof(w));
+          const uint64_t ones = 0x0101010101010101ull, highs = 0x8080808080808080ull;
+          const bool any_zero_byte = (((w[0] - ones) & ~w[0]) | ((w[1] - ones) & ~w[1])) & highs;
+          diff |= sg ? any_zero_byte : ((w[0] | w[1]) != 0);
+        }
+        if (diff) break;
+        u += 16;
+      }
+      while (u < T && ids[u] == a && in_sgmv(u) == sg) ++u;
+    }
+    return u;
+  };
+  for (int32_t t = 0; t < T;) {
+    const int32_t u = run_end(t);
+    const int32_t a = ids[t];
+    if (a >= 0) (in_sgmv(t) ? cnt_s : cnt_b)[a] += u - t;
+    t = u;
   }
   int32_t ns = 0, nb = 0, nseg = 0;
   for (int32_t a = 0; a < max_loras; ++a) {
@@ -172,17 +218,27 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
     ns += cnt_s[a];
     nb += cnt_b[a];
   }
-  for (int32_t t = 0; t < T; ++t) {
+  int32_t* const perm = out->sgmv_perm;
+  int32_t* const btok = out->bgmv_tok;
+  int32_t* const bids = out->bgmv_ids;
+  for (int32_t t = 0; t < T;) {
+    const int32_t u = run_end(t);
     const int32_t a = ids[t];
-    if (a < 0) continue;
-    const bool sg = all_sgmv || (prefill && prefill[t]);
-    if (sg) {
-      out->sgmv_perm[pos_s[a]++] = t;
-    } else {
-      const int32_t p = pos_b[a]++;
-      out->bgmv_tok[p] = t;
-      out->bgmv_ids[p] = a;
+    if (a >= 0) {
+      if (in_sgmv(t)) {
+        const int32_t p = pos_s[a];
+        for (int32_t v = t; v < u; ++v) perm[p + (v - t)] = v;
+        pos_s[a] = p + (u - t);
+      } else {
+        const int32_t p = pos_b[a];
+        for (int32_t v = t; v < u; ++v) {
+          btok[p + (v - t)] = v;
+          bids[p + (v - t)] = a;
+        }
+        pos_b[a] = p + (u - t);
+      }
     }
+    t = u;
   }
   out->num_sgmv_rows = ns;
   out->num_segs = nseg;
@@ -386,10 +442,7 @@ int32_t lora_build_meta(const int32_t* ids, const uint8_t* prefill, int32_t T,
     return fail(LORA_E_ARG, "segment arrays must not be NULL");
   if (T > 0 && (!out->sgmv_perm || !out->bgmv_tok || !out->bgmv_ids))
     return fail(LORA_E_ARG, "row arrays must not be NULL");
-  for (int32_t t = 0; t < T; ++t) {
-    if (ids[t] < -1 || ids[t] >= max_loras)
-      return fail(LORA_E_ID, "ids[%d] = %d is outside [-1, %d)", t, ids[t], max_loras);
-  }
+  if (int32_t e = check_ids(ids, T, max_loras)) return e;
   return build_meta_core(ids, prefill, T, max_loras, max_lora_rank, bgmv_max_rank, out);
 }
 
@@ -426,10 +479,7 @@ int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* id
   if (meta_host_bytes < need)
     return fail(LORA_E_WORKSPACE, "meta_host has %lld bytes, needs %lld",
                 (long long)meta_host_bytes, (long long)need);
-  for (int32_t t = 0; t < T; ++t) {
-    if (ids_host[t] < -1 || ids_host[t] >= g.max_loras)
-      return fail(LORA_E_ID, "ids[%d] = %d is outside [-1, %d)", t, ids_host[t], g.max_loras);
-  }
+  if (int32_t e = check_ids(ids_host, T, g.max_loras)) return e;
   return plan_core(g, T, ids_host, prefill_host, bgmv_max_rank, (int32_t*)meta_host, plan);
 }
 

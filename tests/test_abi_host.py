@@ -72,6 +72,28 @@ def test_builder_bit_exact_vs_oracle_fuzz():
         check_meta_properties(ids, pre, R, got, lim if lim > 0 else 64)
 
 
+def test_builder_long_runs_vs_oracle_fuzz():
+    """Long runs of one adapter and one prefill flag (the builder scans them 16
+    rows at a time), flags other than 0 / 1, and flips inside runs at every
+    offset of a 16-row block."""
+    rng = np.random.default_rng(8)
+    for trial in range(150):
+        n = int(rng.integers(1, 20))
+        lens = rng.integers(1, 90, size=int(rng.integers(1, 12)))
+        ids = np.concatenate([np.full(ln, rng.integers(-1, n), np.int32) for ln in lens])
+        flags = rng.choice(np.array([0, 1, 7, 255], np.uint8), size=len(lens))
+        pre = np.concatenate([np.full(ln, f, np.uint8) for ln, f in zip(lens, flags)])
+        for _ in range(int(rng.integers(0, 3))):
+            if ids.size:
+                pre[int(rng.integers(0, ids.size))] ^= np.uint8(rng.choice([1, 128]))
+        R = int(rng.choice([16, 64, 128]))
+        got = L.lora_build_meta(ids, pre, n, R, 0)
+        ref = oracle.build_meta(ids.tolist(), [int(v != 0) for v in pre], R, 64)
+        for k in META_KEYS:
+            assert got[k].tolist() == list(ref[k]), (trial, k)
+        check_meta_properties(ids, (pre != 0).astype(np.uint8), R, got, 64)
+
+
 def test_builder_named_workload_shapes():
     import workloads as W
     wl = W.config_sgmv_prefill(seed=0, K=64, O=64)
