@@ -250,7 +250,10 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
  *   perm [num_sgmv_rows + num_bgmv_rows]  token of each v row
  *   wave [wave_tiles][16]             slot, rows, first v row, 0, token of
  *                                     each row (-1 past the last row), -1 ...
- *   mfma [mfma_tiles][4]              slot, rows, first v row, 0
+ *   mfma [mfma_tiles][4]              slot, rows, first v row, first token
+ *                                     when the tile's tokens are consecutive
+ *                                     (perm[first + i] = first token + i),
+ *                                     else -1
  *
  * ksplit: the shrink of the MFMA tiles splits K into this many contiguous
  * ranges and writes one partial of v per range (the expand sums them in order

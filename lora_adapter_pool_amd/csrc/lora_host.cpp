@@ -322,13 +322,19 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   const int64_t off_mfma = off_wave + nw * LORA_PLAN_WAVE_WORDS;
   int32_t* mt = img + off_mfma;
   int64_t nm = 0;
+  // word 3: the tile's first token when its tokens are consecutive (a prefill
+  // sequence usually is), so the kernels need not read them from perm; else -1
   auto emit_mfma = [&](int32_t slot, int32_t first, int32_t len) {
     for (int32_t j = 0; j < len; j += LORA_PLAN_MFMA_ROWS) {
       int32_t* r = mt + nm * LORA_PLAN_MFMA_WORDS;
+      const int32_t rows = std::min(LORA_PLAN_MFMA_ROWS, len - j);
+      const int32_t* tok = img + first + j;
+      bool consecutive = true;
+      for (int32_t i = 1; i < rows; ++i) consecutive &= tok[i] == tok[0] + i;
       r[0] = slot;
-      r[1] = std::min(LORA_PLAN_MFMA_ROWS, len - j);
+      r[1] = rows;
       r[2] = first + j;
-      r[3] = 0;
+      r[3] = consecutive ? tok[0] : -1;
       ++nm;
     }
   };

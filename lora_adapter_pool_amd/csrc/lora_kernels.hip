@@ -1045,10 +1045,13 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
 
 // Tile lookup of the MFMA kernels (segments or tile-list mode): first row r0
 // of the row list, row count and adapter slot, the same in every lane.  The
-// tile-list record is (slot, rows, first row, 0).
+// tile-list record is (slot, rows, first row, tok0); tok0 >= 0 says the tile's
+// tokens are tok0, tok0 + 1, ... (row r0 + i reads token tok0 + i) and need
+// not be read from the list; segments mode gives tok0 = -1.
 template <int TMR, int MODE>
 __device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int& cnt, int& sid,
-                                          bool copy = false) {
+                                          int& tok0, bool copy = false) {
+  tok0 = -1;
   if constexpr (MODE == kList) {
     if (f >= L.num_tiles) return false;
     const int w = L.tiles[(size_t)f * LORA_PLAN_MFMA_WORDS + (threadIdx.x & 3)];
@@ -1057,6 +1060,7 @@ __device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int&
     sid = __builtin_amdgcn_readlane(w, 0);
     cnt = __builtin_amdgcn_readlane(w, 1);
     r0 = __builtin_amdgcn_readlane(w, 2);
+    tok0 = __builtin_amdgcn_readlane(w, 3);
   } else {
     if (!find_tile<TMR>(L, f, r0, cnt, sid)) return false;
     r0 = __builtin_amdgcn_readfirstlane(r0);
@@ -1099,9 +1103,9 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
   const int rem = bid - f * per_tile;
   const int s = rem / ksplit;
   const int part = rem - s * ksplit;
-  int r0, cnt, sid;
+  int r0, cnt, sid, tok0;
   const bool copy = s == 0 && part == 0 && blockIdx.y == 0;
-  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, copy)) return;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0, copy)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int rank0 = blockIdx.y * NR;
   // K steps of this split
@@ -1118,8 +1122,8 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = srow + 32 * j;
-    const int tk = L.tok[r0 + min(r, cnt - 1)];
-    if (copy && L.copy_tok && c8 == 0 && r < cnt) L.copy_tok[r0 + r] = tk;
+    const int tk = tok0 >= 0 ? tok0 + min(r, cnt - 1) : L.tok[r0 + min(r, cnt - 1)];
+    if (copy && L.copy_tok && tok0 < 0 && c8 == 0 && r < cnt) L.copy_tok[r0 + r] = tk;
     const bool ok = r < cnt && tk >= 0 && tk < g.T;
     xp[j] = x + (size_t)(ok ? tk : 0) * g.K;
     xm[j] = all_or_none(ok);
@@ -1244,13 +1248,13 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
     if (i < g.S && cidx >= ch.start[i]) s = i;
   const int col0 = (cidx - ch.start[s]) * NC;
   const int out_s = g.out[s];
-  int r0, cnt, sid;
-  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid)) return;
+  int r0, cnt, sid, tok0;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int R = g.R;
   const int SR = g.S * R;
   if (tid < TM) {
-    const int tk = L.tok[r0 + min(tid, cnt - 1)];
+    const int tk = tok0 >= 0 ? tok0 + min(tid, cnt - 1) : L.tok[r0 + min(tid, cnt - 1)];
     s_tok[tid] = (tid < cnt && tk >= 0 && tk < g.T) ? tk : -1;
   }
   __syncthreads();
@@ -1408,14 +1412,14 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
   const int c_begin = ch.start[s] + (gidx - gr.start[s]) * cpw;
   const int c_end = min(ch.start[s + 1], c_begin + cpw);
   const int out_s = g.out[s];
-  int r0, cnt, sid;
-  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid)) return;
+  int r0, cnt, sid, tok0;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int R = g.R;  // <= 64, a multiple of 8
   const int SR = g.S * R;
   const __amdgpu_buffer_rsrc_t yb = make_rsrc(y, (uint32_t)((size_t)g.T * g.O * sizeof(uint16_t)));
   if (tid < TM) {
-    const int tk = L.tok[r0 + min(tid, cnt - 1)];
+    const int tk = tok0 >= 0 ? tok0 + min(tid, cnt - 1) : L.tok[r0 + min(tid, cnt - 1)];
     s_tok[tid] = (tid < cnt && tk >= 0 && tk < g.T) ? tk : -1;
   }
   __syncthreads();

@@ -78,8 +78,12 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
         assert not np.any(is_mfma[first:first + rows])
         shrink_cover[first:first + rows] += 1
     for rec in v["mfma"]:
-        slot, rows, first, zero = (int(x) for x in rec)
-        assert bf16 and zero == 0 and 1 <= rows <= MFMA_ROWS and first + rows <= ns + nb
+        slot, rows, first, tok0 = (int(x) for x in rec)
+        assert bf16 and 1 <= rows <= MFMA_ROWS and first + rows <= ns + nb
+        # word 3: first token when the tile's tokens are consecutive, else -1
+        toks = v["perm"][first:first + rows]
+        consecutive = bool(np.all(toks == toks[0] + np.arange(rows)))
+        assert tok0 == (int(toks[0]) if consecutive else -1)
         assert first >= ns or first + rows <= ns  # never across the SGMV / BGMV boundary
         assert np.all(row_ids[first:first + rows] == slot)
         assert np.all(is_mfma[first:first + rows])
