@@ -236,6 +236,74 @@ def measure(setups, steps, warmup, stream_ptr):
     return time.perf_counter() - t0
 
 
+def device_meta_leg(s, steps, stream_ptr):
+    """The delta path driven from device metadata: lora_build_meta_device, then
+    the four grouped entry points with upper-bound sizes (num_segs = max_loras,
+    rows = T), no host work per step and graph-capturable.  Reports the
+    builder's own time (HIP events over back-to-back launches) and whole steps
+    over the rotating replicas (wall clock between two synchronizes)."""
+    import torch
+    L = s.L
+    lib = L.lib()
+    wl, T, ML, R = s.wl, s.T, s.wl.max_loras, s.wl.max_lora_rank
+    rows = {"sgmv_perm": T, "bgmv_tok": T, "bgmv_ids": T}
+    meta = {k: torch.zeros(max(rows.get(k, ML), 1), dtype=torch.int32, device="cuda")
+            for k in ("sgmv_perm", "seg_starts", "seg_lens", "seg_ids", "bgmv_tok", "bgmv_ids")}
+    m = L._lib.lora_meta()
+    for k, t in meta.items():
+        setattr(m, k, ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32)))
+    counts = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ids_d = torch.from_numpy(s.ids).cuda()
+    pre_d = torch.from_numpy(s.pre).cuda()
+    SR = wl.num_slices * R
+    v_s = torch.zeros((max(T, 1), SR), dtype=torch.float32, device="cuda")
+    v_b = torch.zeros((max(T, 1), SR), dtype=torch.float32, device="cuda")
+    d = ctypes.byref(s.desc)
+    P = {k: t.data_ptr() for k, t in meta.items()}
+
+    def build():
+        return lib.lora_build_meta_device(ids_d.data_ptr(), pre_d.data_ptr(), T, ML, R, 0,
+                                          ctypes.byref(m), counts.data_ptr(), stream_ptr)
+
+    def step(i):
+        r = i % s.nrep
+        sts = [build(),
+               lib.lora_sgmv_shrink(d, s.px[r], s.pA[r], v_s.data_ptr(), P["sgmv_perm"],
+                                    P["seg_starts"], P["seg_lens"], P["seg_ids"], ML, T, T,
+                                    stream_ptr),
+               lib.lora_bgmv_shrink(d, s.px[r], s.pA[r], v_b.data_ptr(), P["bgmv_tok"],
+                                    P["bgmv_ids"], T, T, stream_ptr),
+               lib.lora_sgmv_expand(d, v_s.data_ptr(), s.pB[r], s.py[r], P["sgmv_perm"],
+                                    P["seg_starts"], P["seg_lens"], P["seg_ids"], ML, T, T,
+                                    stream_ptr),
+               lib.lora_bgmv_expand(d, v_b.data_ptr(), s.pB[r], s.py[r], P["bgmv_tok"],
+                                    P["bgmv_ids"], T, T, stream_ptr)]
+        if any(sts):
+            raise RuntimeError(f"device-metadata step failed: {L.last_error()}")
+
+    for _ in range(10):
+        build()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(100):
+        build()
+    e1.record()
+    torch.cuda.synchronize()
+    builder_us = e0.elapsed_time(e1) * 1e3 / 100
+    for i in range(10):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(10 + i)
+    torch.cuda.synchronize()
+    step_us = (time.perf_counter() - t0) / steps * 1e6
+    a = algorithmic(wl)
+    return {"builder_us": round(builder_us, 2), "step_us": round(step_us, 2),
+            "tokens_per_s": a["Ta"] / (step_us * 1e-6), "launches_per_step": 5,
+            "counts": counts.cpu().tolist()[:3]}
+
+
 def copy_bandwidth():
     import torch
     n = 1 << 28  # 256 Mi bf16 = 512 MiB per buffer
@@ -545,6 +613,10 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": d["bytes"],
                      "avg_launch_us": d["us"]},
     }
+    dm = device_meta_leg(setups[0], max(20, args.steps // 4), stream_ptr)
+    out["device_meta"] = dict(dm, workload=setups[0].wl.name)
+    log(f"[bench] device metadata: builder {dm['builder_us']:.2f} us, step {dm['step_us']:.2f} us "
+        f"(5 launches)")
     del setups
     torch.cuda.empty_cache()
 

@@ -177,6 +177,32 @@ int32_t lora_build_meta(const int32_t* ids, const uint8_t* prefill, int32_t T,
                         int32_t max_loras, int32_t max_lora_rank, int32_t bgmv_max_rank,
                         lora_meta* out);
 
+/* Most adapter slots lora_build_meta_device handles (its per-slot counters
+ * live in LDS). */
+#define LORA_META_DEVICE_MAX_LORAS 8192
+
+/* The same metadata built on the GPU ([TGI] step 4), asynchronously on
+ * `stream`, so a batch needs no host round trip (and the delta path can be
+ * captured in a graph).
+ *   ids, prefill  device arrays of T entries (prefill may be NULL = all 0)
+ *   out           device arrays with the capacities of lora_build_meta; the
+ *                 num_* fields of *out are not read or written
+ *   counts        device int32[4]: num_sgmv_rows, num_segs, num_bgmv_rows and
+ *                 the number of ids < -1 or >= max_loras (those rows are
+ *                 left out, as if their id were -1)
+ * The arrays equal lora_build_meta's bit for bit up to those counts, and are
+ * padded behind them so the grouped entry points can take upper-bound sizes
+ * (num_segs = max_loras, num_rows = n = T): seg_lens = 0 past num_segs,
+ * bgmv_ids = -1 (and bgmv_tok = 0) past num_bgmv_rows, sgmv_perm = 0 past
+ * num_sgmv_rows.  Errors (before any HIP call): LORA_E_ARG for null pointers
+ * or T < 0, LORA_E_SHAPE for max_loras outside [1, LORA_META_DEVICE_MAX_LORAS].
+ * One workgroup does the work: a histogram, scans over the slots, then one
+ * wavefront places the rows in token order. */
+int32_t lora_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
+                               int32_t max_loras, int32_t max_lora_rank,
+                               int32_t bgmv_max_rank, const lora_meta* out, int32_t* counts,
+                               void* stream);
+
 /* ----------------------------------------------------- grouped kernels */
 /* All four take device pointers for x/y/v/pools/metadata and host scalars.
  * T is the number of rows of x and y (bounds for token indices).

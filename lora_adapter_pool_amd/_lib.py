@@ -95,6 +95,8 @@ _SIGNATURES = {
                               _P]),
     "lora_pool_clear": (_I32, [_DP, _P, _P, _I32, _P]),
     "lora_build_meta": (_I32, [_P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(lora_meta)]),
+    "lora_build_meta_device": (_I32, [_P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(lora_meta),
+                                      _P, _P]),
     "lora_sgmv_shrink": (_I32, [_DP, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
     "lora_sgmv_expand": (_I32, [_DP, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
     "lora_bgmv_shrink": (_I32, [_DP, _P, _P, _P, _P, _P, _I32, _I32, _P]),
@@ -256,6 +258,22 @@ def lora_sgmv_expand(desc, v, B_pool, y, perm, seg_starts, seg_lens, seg_ids, nu
     _check(lib().lora_sgmv_expand(ctypes.byref(desc), _ptr(v), _ptr(B_pool), _ptr(y), _ptr(perm),
                                   _ptr(seg_starts), _ptr(seg_lens), _ptr(seg_ids), int(num_segs),
                                   int(num_rows), int(T), _stream(stream)))
+
+
+META_DEVICE_MAX_LORAS = 8192
+
+
+def lora_build_meta_device(ids, prefill, T, max_loras, max_lora_rank, bgmv_max_rank, arrays,
+                           counts, stream=None) -> None:
+    """Device-side builder: `arrays` maps the lora_meta array names (sgmv_perm,
+    seg_starts, seg_lens, seg_ids, bgmv_tok, bgmv_ids) to device int32 tensors;
+    `counts` is a device int32[4] (rows, segments, BGMV rows, rejected ids)."""
+    m = lora_meta()
+    for k in ("sgmv_perm", "seg_starts", "seg_lens", "seg_ids", "bgmv_tok", "bgmv_ids"):
+        setattr(m, k, ctypes.cast(_ptr(arrays.get(k)), ctypes.POINTER(ctypes.c_int32)))
+    _check(lib().lora_build_meta_device(_ptr(ids), _ptr(prefill), int(T), int(max_loras),
+                                        int(max_lora_rank), int(bgmv_max_rank), ctypes.byref(m),
+                                        _ptr(counts), _stream(stream)))
 
 
 def lora_bgmv_shrink(desc, x, A_pool, v, tok, ids, n, T, stream=None) -> None:

@@ -178,6 +178,25 @@ int32_t lora_pool_clear(const lora_pool_desc* desc, void* A_pool, void* B_pool, 
   return hip_ok(hipMemsetAsync((char*)B_pool + slot * bbytes, 0, bbytes, st), "clear B");
 }
 
+int32_t lora_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
+                               int32_t max_loras, int32_t max_lora_rank,
+                               int32_t bgmv_max_rank, const lora_meta* out, int32_t* counts,
+                               void* stream) {
+  clear_error();
+  if (!out || !counts) return fail(LORA_E_ARG, "out / counts must not be NULL");
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  if (max_loras < 1 || max_loras > LORA_META_DEVICE_MAX_LORAS)
+    return fail(LORA_E_SHAPE, "max_loras must be in [1, %d], got %d", LORA_META_DEVICE_MAX_LORAS,
+                max_loras);
+  if (!out->seg_starts || !out->seg_lens || !out->seg_ids)
+    return fail(LORA_E_ARG, "segment arrays must not be NULL");
+  if (T > 0 && (!ids || !out->sgmv_perm || !out->bgmv_tok || !out->bgmv_ids))
+    return fail(LORA_E_ARG, "ids and row arrays must not be NULL");
+  const int32_t limit = bgmv_max_rank > 0 ? bgmv_max_rank : LORA_BGMV_MAX_RANK_DEFAULT;
+  return run_build_meta_device(ids, prefill, T, max_loras, max_lora_rank > limit, *out, counts,
+                               (hipStream_t)stream);
+}
+
 int32_t lora_sgmv_shrink(const lora_pool_desc* desc, const void* x, const void* A_pool, float* v,
                          const int32_t* perm, const int32_t* seg_starts, const int32_t* seg_lens,
                          const int32_t* seg_ids, int32_t num_segs, int32_t num_rows, int32_t T,

@@ -107,6 +107,12 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
 bool plan_is_onepass(const Geo& g, const TilePlan& p);
 int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
                        const TilePlan& p, float* v, hipStream_t st);
+// Device-side builder (csrc/lora_meta.hip): lora_build_meta's arrays from
+// device ids, one workgroup on `st`; counts[4] = rows, segments, BGMV rows,
+// rejected ids.
+int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
+                              int32_t max_loras, bool all_sgmv, const lora_meta& m,
+                              int32_t* counts, hipStream_t st);
 int32_t run_pool_load(const Geo& g, void* A_slot_slice, void* B_slot_slice, const void* Asrc,
                       const void* Bsrc, int r, int out_s, float scale, hipStream_t st);
 

@@ -1,0 +1,190 @@
+// Device-side metadata builder: the arrays of lora_build_meta ([TGI] step 4:
+// the rows of a batch sorted by adapter id, SGMV rows into segments of one
+// adapter, BGMV rows into a per-row list) computed on the GPU from device ids,
+// so a batch needs no host round trip and the whole delta path can be
+// captured in a graph.  One workgroup:
+//   1. a histogram of the SGMV and BGMV rows per adapter (LDS atomics: counts
+//      do not depend on their order);
+//   2. exclusive scans of both histograms and of the non-empty SGMV bins give
+//      every adapter its first position and its segment;
+//   3. the rows' keys are staged in LDS by blocks, and one wavefront places
+//      the rows in token order, 64 at a time: lanes with the same (adapter,
+//      set) key take consecutive positions in lane order, so the sort is
+//      stable and the result is the host builder's, bit for bit.
+// Arrays are padded so the grouped entry points can take upper-bound sizes:
+// segments past num_segs have length 0, BGMV rows past num_bgmv_rows have
+// id -1 (skipped by the kernels), and sgmv_perm past num_sgmv_rows is 0.
+#include <hip/hip_runtime.h>
+
+#include "lora_internal.h"
+#include "lora_kernels.h"
+
+namespace lora {
+
+constexpr int kMetaThreads = 1024;
+
+__global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ prefill, int32_t T,
+    int32_t max_loras, int32_t all_sgmv, lora_meta m, int32_t* __restrict__ counts,
+    int32_t kcap) {
+  // [max_loras] SGMV bins, [max_loras] BGMV bins, then the keys of a block of
+  // kcap rows (int16: 2 id + set, or -1)
+  extern __shared__ int32_t lds[];
+  __shared__ int32_t s_bad;
+  __shared__ int32_t s_wsum[kMetaThreads / 64][3];
+  int32_t* cs = lds;
+  int32_t* cb = lds + max_loras;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = kMetaThreads / 64;
+  for (int a = tid; a < max_loras; a += kMetaThreads) {
+    cs[a] = 0;
+    cb[a] = 0;
+  }
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+
+  // 1. histogram
+  for (int t = tid; t < T; t += kMetaThreads) {
+    const int a = ids[t];
+    if (a < -1 || a >= max_loras) {
+      atomicAdd(&s_bad, 1);
+      continue;
+    }
+    if (a < 0) continue;
+    const bool sg = all_sgmv || (prefill && prefill[t]);
+    atomicAdd(sg ? &cs[a] : &cb[a], 1);
+  }
+  __syncthreads();
+
+  // 2. exclusive scans over the bins; thread tid owns bins [a0, a1)
+  const int per = (max_loras + kMetaThreads - 1) / kMetaThreads;
+  const int a0 = min(max_loras, tid * per), a1 = min(max_loras, a0 + per);
+  int v[3] = {0, 0, 0};  // SGMV rows, BGMV rows, SGMV segments
+  for (int a = a0; a < a1; ++a) {
+    v[0] += cs[a];
+    v[1] += cb[a];
+    v[2] += cs[a] > 0;
+  }
+  int inc[3] = {v[0], v[1], v[2]};
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int u = __shfl_up(inc[i], o, 64);
+      if (lane >= o) inc[i] += u;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) s_wsum[wave][i] = inc[i];
+  }
+  __syncthreads();
+  int base[3] = {0, 0, 0}, tot[3] = {0, 0, 0};
+  for (int w = 0; w < nw; ++w) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      base[i] += w < wave ? s_wsum[w][i] : 0;
+      tot[i] += s_wsum[w][i];
+    }
+  }
+  int es = base[0] + inc[0] - v[0], eb = base[1] + inc[1] - v[1], eg = base[2] + inc[2] - v[2];
+  for (int a = a0; a < a1; ++a) {
+    const int c = cs[a], d = cb[a];
+    if (c > 0) {
+      m.seg_starts[eg] = es;
+      m.seg_lens[eg] = c;
+      m.seg_ids[eg] = a;
+      ++eg;
+    }
+    cs[a] = es;  // the bins become the next free position of each adapter
+    es += c;
+    cb[a] = eb;
+    eb += d;
+  }
+  const int ns = tot[0], nb = tot[1], nseg = tot[2];
+  if (tid == 0) {
+    counts[0] = ns;
+    counts[1] = nseg;
+    counts[2] = nb;
+  }
+  for (int i = nseg + tid; i < max_loras; i += kMetaThreads) {
+    m.seg_starts[i] = ns;
+    m.seg_lens[i] = 0;
+    m.seg_ids[i] = 0;
+  }
+  for (int i = ns + tid; i < T; i += kMetaThreads) m.sgmv_perm[i] = 0;
+  for (int i = nb + tid; i < T; i += kMetaThreads) {
+    m.bgmv_tok[i] = 0;
+    m.bgmv_ids[i] = -1;
+  }
+  __syncthreads();
+  if (tid == 0) counts[3] = s_bad;
+
+  // 3. stable placement, by blocks of kcap rows: every thread stages the
+  // block's keys in LDS, then one wavefront places the rows 64 at a time.  A
+  // chunk gathers the next free position of each lane's key, ranks equal keys
+  // by lane order with ballots (registers only), and the first lane of each
+  // key writes the key's new next free position.
+  int16_t* keys = reinterpret_cast<int16_t*>(lds + 2 * max_loras);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b0 = 0; b0 < T; b0 += kcap) {
+    const int nbk = min(kcap, T - b0);
+    __syncthreads();  // the previous block's keys are placed
+    for (int i = tid; i < nbk; i += kMetaThreads) {
+      const int t = b0 + i;
+      const int a = ids[t];
+      const bool ok = a >= 0 && a < max_loras;
+      keys[i] = (int16_t)(ok ? 2 * a + ((all_sgmv || (prefill && prefill[t])) ? 1 : 0) : -1);
+    }
+    __syncthreads();
+    if (wave != 0) continue;
+    for (int c = 0; c < nbk; c += 64) {
+      const int i = c + lane;
+      const int key = i < nbk ? keys[i] : -1;
+      int32_t* pos = (key & 1) ? &cs[key >> 1] : &cb[key >> 1];
+      const int p0 = key >= 0 ? *pos : 0;
+      uint64_t pending = __ballot(key >= 0);
+      int rank = 0, cnt = 0;
+      bool first = false;
+      while (pending) {
+        const int leader = __builtin_ctzll(pending);
+        const int k = __builtin_amdgcn_readlane(key, leader);
+        const uint64_t mk = __ballot(key == k);
+        if (key == k) {
+          rank = __popcll(mk & below);
+          cnt = __popcll(mk);
+          first = lane == leader;
+        }
+        pending &= ~mk;
+      }
+      if (key >= 0) {
+        const int t = b0 + i;
+        const int p = p0 + rank;
+        if (key & 1) {
+          m.sgmv_perm[p] = t;
+        } else {
+          m.bgmv_tok[p] = t;
+          m.bgmv_ids[p] = key >> 1;
+        }
+      }
+      if (first) *pos = p0 + cnt;
+    }
+  }
+}
+
+int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
+                              int32_t max_loras, bool all_sgmv, const lora_meta& m,
+                              int32_t* counts, hipStream_t st) {
+  // LDS: the bins, then up to 128 KB in all with the keys of a block of rows
+  const int64_t bins = (int64_t)2 * max_loras * sizeof(int32_t);
+  int64_t kcap = ((int64_t)128 * 1024 - bins) / (int64_t)sizeof(int16_t) / 64 * 64;
+  kcap = std::max<int64_t>(64, std::min<int64_t>(kcap, ((int64_t)T + 63) / 64 * 64));
+  hipLaunchKernelGGL(build_meta_kernel, dim3(1), dim3(kMetaThreads),
+                     (size_t)(bins + kcap * (int64_t)sizeof(int16_t)), st, ids, prefill, T,
+                     max_loras, all_sgmv ? 1 : 0, m, counts, (int32_t)kcap);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(LORA_E_HIP, "build_meta launch: %s", hipGetErrorString(e));
+  return LORA_OK;
+}
+
+}  // namespace lora

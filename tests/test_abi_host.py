@@ -94,6 +94,31 @@ def test_builder_long_runs_vs_oracle_fuzz():
         check_meta_properties(ids, (pre != 0).astype(np.uint8), R, got, 64)
 
 
+def test_device_builder_validates_before_hip():
+    """lora_build_meta_device rejects bad arguments before any HIP call."""
+    import ctypes
+    lib = _lib.lib()
+    FAKE = 1 << 20
+    good = {k: FAKE for k in ("sgmv_perm", "seg_starts", "seg_lens", "seg_ids", "bgmv_tok",
+                              "bgmv_ids")}
+
+    def status(T=8, max_loras=4, ids=FAKE, counts=FAKE, drop=None, out=True):
+        m = _lib.lora_meta()
+        for k, p in good.items():
+            setattr(m, k, ctypes.cast(None if k == drop else p, ctypes.POINTER(ctypes.c_int32)))
+        return lib.lora_build_meta_device(ids, None, T, max_loras, 16, 0,
+                                          ctypes.byref(m) if out else None, counts, None)
+
+    assert status(out=False) == _lib.LORA_E_ARG
+    assert status(counts=None) == _lib.LORA_E_ARG
+    assert status(T=-1) == _lib.LORA_E_ARG
+    assert status(max_loras=0) == _lib.LORA_E_SHAPE
+    assert status(max_loras=_lib.META_DEVICE_MAX_LORAS + 1) == _lib.LORA_E_SHAPE
+    assert status(drop="seg_lens") == _lib.LORA_E_ARG
+    assert status(drop="bgmv_ids") == _lib.LORA_E_ARG
+    assert status(ids=None) == _lib.LORA_E_ARG
+
+
 def test_builder_named_workload_shapes():
     import workloads as W
     wl = W.config_sgmv_prefill(seed=0, K=64, O=64)

@@ -1,4 +1,4 @@
-"""Properties of the gfx950 code the compiler makes from the kernel source
+"""Properties of the gfx950 code the compiler makes from the kernel sources
 (CPU only: hipcc cross-compiles to assembly, nothing runs).
 
 - Every DPP lane move (v_mov_b32_dpp) runs with the full execution mask: a DPP
@@ -29,12 +29,16 @@ def asm(tmp_path_factory):
     cc = _hipcc()
     if not cc:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "lora_kernels.s"
-    cmd = [cc, "-O3", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-x", "hip",
-           "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, "lora_kernels.hip")]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
-    return out.read_text()
+    text = []
+    for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
+        out = tmp_path_factory.mktemp("isa") / (src + ".s")
+        cmd = [cc, "-O3", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-x",
+               "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "--cuda-device-only", "-S", "-o", str(out),
+               os.path.join(CSRC, src)]
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+        text.append(out.read_text())
+    return "\n".join(text)
 
 
 def _kernels(text):
