@@ -304,6 +304,44 @@ def device_meta_leg(s, steps, stream_ptr):
             "counts": counts.cpu().tolist()[:3]}
 
 
+def slot_load_leg(seed):
+    """Adapter slots: time to make an adapter resident (pinned host copy ->
+    device on the side stream, then the pad-and-fold kernel), cycling four
+    adapters through two slots so every batch loads one; for a q_proj-like
+    adapter (3072 -> 3072, rank 16) and a gate_up-like one (4096 -> 2 x 14336,
+    rank 64)."""
+    import torch
+    import workloads as W
+    from lora_adapter_pool_amd.slots import AdapterSlots
+    import lora_adapter_pool_amd as L
+    res = {}
+    for name, K, outs, r in (("q_proj 3072x3072 r16", 3072, [3072], 16),
+                             ("gate_up 4096x2x14336 r64", 4096, [14336, 14336], 64)):
+        rng = np.random.default_rng(seed)
+        ids = [1, 2, 3, 4]
+        ads = W._draw_slots(rng, "bf16", K, outs, {a: r for a in ids},
+                            {a: 2.0 * r for a in ids}, rslora=False)
+        pool = L.LoraPool("bf16", 2, r, K, outs)
+        sl = AdapterSlots(pool, max_cpu_loras=4)
+        for a in ids:
+            sl.register(a, f"a{a}", ads[a].A, ads[a].B, r, 2.0 * r)
+        host_bytes = 2 * r * (K * len(outs) + sum(outs))
+        for i in range(4):
+            sl.prepare([ids[i % 4]])
+        torch.cuda.synchronize()
+        n = 40
+        t0 = time.perf_counter()
+        for i in range(n):
+            sl.prepare([ids[i % 4]])
+            torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / n * 1e6
+        res[name] = {"load_us": round(us, 1), "adapter_bytes": host_bytes,
+                     "GBs": round(host_bytes / (us * 1e-6) / 1e9, 2)}
+        del sl, pool
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_bandwidth():
     import torch
     n = 1 << 28  # 256 Mi bf16 = 512 MiB per buffer
@@ -613,6 +651,8 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": d["bytes"],
                      "avg_launch_us": d["us"]},
     }
+    out["slot_load"] = slot_load_leg(args.seed)
+    log(f"[bench] slot loads: {out['slot_load']}")
     dm = device_meta_leg(setups[0], max(20, args.steps // 4), stream_ptr)
     out["device_meta"] = dict(dm, workload=setups[0].wl.name)
     log(f"[bench] device metadata: builder {dm['builder_us']:.2f} us, step {dm['step_us']:.2f} us "

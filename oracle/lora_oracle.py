@@ -321,6 +321,44 @@ def rel_err_rows(y_test, y_ref) -> float:
     return float(np.max(num / den))
 
 
+# ----------------------------------------------------------------------------
+# Adapter slots ([vLLM] LoRARequest rules, step 2, limits)
+# ----------------------------------------------------------------------------
+
+def slot_residency(batches: Sequence[Sequence[Optional[int]]], max_loras: int) -> List[tuple]:
+    """(adapters resident in the GPU slots after the batch, least recently used
+    first; adapters the batch had to load, in load order) for each batch,
+    under the reading that a batch of at most max_loras distinct adapters
+    makes each of them resident, in order of first use in the batch, evicting
+    the least recently used adapter the batch does not use when no slot is
+    free; every adapter of the batch then becomes most recently used, in order
+    of first use.  ([vLLM] step 2: max_loras is the number of distinct
+    adapters one batch can use; the article does not fix the eviction order,
+    least recently used is the reading.)"""
+    resident: List[int] = []          # LRU first
+    out = []
+    for batch in batches:
+        wanted: List[int] = []
+        for a in batch:
+            if a is not None and a != -1 and a not in wanted:
+                wanted.append(int(a))
+        assert len(wanted) <= max_loras
+        loaded = []
+        for a in wanted:
+            if a in resident:
+                continue
+            if len(resident) == max_loras:
+                victim = [b for b in resident if b not in wanted][0]
+                resident.remove(victim)
+            resident.append(a)
+            loaded.append(a)
+        for a in wanted:
+            resident.remove(a)
+            resident.append(a)
+        out.append((list(resident), loaded))
+    return out
+
+
 # What pins each function (tests/test_oracle_pins.py):
 PINS = {
     "scaling": "closed-form values (alpha/r, alpha/sqrt(r)); rsLoRA vs standard ratio",
@@ -336,4 +374,6 @@ PINS = {
                   "argsort; property checks",
     "pool_bytes": "r(d+k) parameter count per matrix",
     "rel_err_rows": "hand values",
+    "slot_residency": "hand-worked sequence (tests/test_oracle_pins.py); capacity and "
+                      "membership invariants on random sequences",
 }

@@ -256,5 +256,33 @@ def pin_rel_err(O):
     assert O.rel_err_rows(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
 
 
+def pin_slot_residency(O):
+    """Hand-worked: max_loras = 2.  [1] loads 1; [2] loads 2 -> {1, 2}; [3]
+    evicts 1 (least recently used) -> {2, 3}; [None, 2] loads nothing, touches
+    2 -> {3, 2}; [1, 2] evicts 3 (not in the batch) -> {1, 2}, 2 most recent
+    (order of first use); [2, 2, None] -> {1, 2}; [4, 1] evicts 2, the one not
+    in the batch, and leaves 1 most recent -> {4, 1}; [3, 4] evicts 1 and
+    keeps 4, which the batch uses, though 4 is the least recently used."""
+    got = O.slot_residency([[1], [2], [3], [None, 2], [1, 2], [2, 2, None], [4, 1], [3, 4]], 2)
+    assert got == [([1], [1]), ([1, 2], [2]), ([2, 3], [3]), ([3, 2], []), ([1, 2], [1]),
+                   ([1, 2], []), ([4, 1], [4]), ([3, 4], [3])]
+    # max_loras = 1 serialises adapters: each new adapter replaces the last
+    assert O.slot_residency([[5], [6], [6], [5]], 1) == [([5], [5]), ([6], [6]), ([6], []),
+                                                          ([5], [5])]
+    # invariants on random sequences: capacity; every adapter of a batch
+    # resident after it; loads are exactly the adapters that were not resident
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        m = int(rng.integers(1, 5))
+        batches = [list(rng.choice(np.arange(8), size=int(rng.integers(0, m + 1)),
+                                   replace=False)) for _ in range(20)]
+        prev = []
+        for b, (res, loaded) in zip(batches, O.slot_residency(batches, m)):
+            assert len(res) <= m and len(set(res)) == len(res)
+            assert set(int(a) for a in b) <= set(res)
+            assert sorted(loaded) == sorted(set(int(a) for a in b) - set(prev))
+            prev = res
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")
             and isinstance(v, types.FunctionType)]

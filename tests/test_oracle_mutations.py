@@ -123,3 +123,50 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(O, attr, fn)
     assert _caught(monkeypatch) > 0, f"no pin caught mutation {name}"
+
+
+def test_slot_residency_mutations_are_caught(monkeypatch):
+    """Plausible slips in the residency model: evicting the most recently used
+    adapter, or evicting one the batch itself uses."""
+    def mru(batches, max_loras):
+        resident, out = [], []
+        for batch in batches:
+            wanted = []
+            for a in batch:
+                if a is not None and a != -1 and a not in wanted:
+                    wanted.append(int(a))
+            loaded = []
+            for a in wanted:
+                if a not in resident:
+                    if len(resident) == max_loras:
+                        resident.remove([b for b in resident if b not in wanted][-1])
+                    resident.append(a)
+                    loaded.append(a)
+            for a in wanted:
+                resident.remove(a)
+                resident.append(a)
+            out.append((list(resident), loaded))
+        return out
+
+    def any_victim(batches, max_loras):
+        resident, out = [], []
+        for batch in batches:
+            loaded = []
+            for a in batch:
+                if a is None or a == -1:
+                    continue
+                if a in resident:
+                    resident.remove(a)
+                else:
+                    if len(resident) == max_loras:
+                        resident.pop(0)
+                    loaded.append(int(a))
+                resident.append(int(a))
+            out.append((list(resident), loaded))
+        return out
+
+    for bad in (mru, any_victim):
+        monkeypatch.setattr(O, "slot_residency", bad)
+        with pytest.raises(AssertionError):
+            from oracle_pins import pin_slot_residency
+            pin_slot_residency(O)
