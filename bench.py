@@ -412,7 +412,7 @@ def one_launch(wl, p):
     if os.environ.get("LORA_ONEPASS_DECODE", "1").startswith("0"):
         return False
     return (wl.dtype == "bf16" and not p["mfma_tiles"] and 0 < p["wave_tiles"] <= 12
-            and wl.max_loras <= 2 ** 28 and wl.max_lora_rank <= 32)
+            and wl.max_loras <= 2 ** 28 and wl.max_lora_rank <= 32 and wl.T < 65536)
 
 
 def stage_kernels(wl):
@@ -427,7 +427,7 @@ def stage_kernels(wl):
         nt = 1 if wl.max_lora_rank <= 16 else 2
         share = -(-(-(-wl.in_features // 32)) // 8)
         cb = min(-(-share // 4) * 4, 16 if nt == 1 else 8)
-        return {"apply": [f"decode_onepass_kernel<{nt}, {cb}, 3>"]}
+        return {"apply": [f"decode_onepass_kernel<{nt}, {cb}, 5>"]}
     out = {"shrink": [], "expand": []}
     if p["mfma_tiles"]:
         out["shrink"].append("shrink_mfma_kernel<2>")

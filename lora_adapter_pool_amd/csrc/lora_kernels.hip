@@ -205,7 +205,7 @@ __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int&
 
 // How a kernel finds its tile: device segments, device rows with ids, the
 // plan's device image, or records passed by value in two capacities.
-enum { kSegs = 0, kRows = 1, kList = 2, kArg = 3, kArgL = 4 };
+enum { kSegs = 0, kRows = 1, kList = 2, kArg = 3, kArgL = 4, kArgC = 5 };
 
 // Tile records passed by value (kArg, kArgL): a small plan travels in the
 // kernel arguments, which the wavefronts read with scalar loads, so no copy of
@@ -216,7 +216,12 @@ enum { kSegs = 0, kRows = 1, kList = 2, kArg = 3, kArgL = 4 };
 template <int MODE> struct PlanArg {};
 template <> struct PlanArg<kArg> { int32_t w[kArgTilesS * kArgWords]; };
 template <> struct PlanArg<kArgL> { int32_t w[kArgTilesL * kArgWords]; };
-template <int MODE> constexpr int arg_tiles() { return MODE == kArg ? kArgTilesS : kArgTilesL; }
+// Compact records for the one-launch decode kernel, which never touches v:
+// word 0 as above, then the tokens as 16-bit halves (batches of T < 65536),
+// 20 bytes a tile instead of 40.
+constexpr int kArgCWords = 1 + kWaveTileRows / 2;
+template <> struct PlanArg<kArgC> { uint32_t w[kArgTilesS * kArgCWords]; };
+template <int MODE> constexpr int arg_tiles() { return MODE == kArgL ? kArgTilesL : kArgTilesS; }
 
 // Rows of one tile, the same in every lane (scalar registers).  Row r is v row
 // vrow0 + r, reads token tok[r] and uses adapter aid[r]; bit r of `valid` is
@@ -252,6 +257,18 @@ __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
 #pragma unroll
     for (int r = 0; r < TM; ++r) {
       tr.tok[r] = rec[2 + r];
+      tr.aid[r] = sid;
+    }
+  } else if constexpr (MODE == kArgC) {
+    static_assert(TM <= 2 * (kArgCWords - 1), "a compact record holds 2 tokens a word");
+    if (f >= L.num_tiles || f >= arg_tiles<MODE>()) return false;
+    const uint32_t* rec = pa.w + f * kArgCWords;
+    const int sid = (int)(rec[0] & 0x0fffffffu);
+    tr.cnt = (int)(rec[0] >> 28);
+    tr.vrow0 = 0;  // no v rows: the kernel reading this form keeps v on chip
+#pragma unroll
+    for (int r = 0; r < TM; ++r) {
+      tr.tok[r] = (int)((rec[1 + r / 2] >> (16 * (r & 1))) & 0xffffu);  // 0xffff: past T
       tr.aid[r] = sid;
     }
   } else if constexpr (MODE == kList) {
@@ -1992,8 +2009,8 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
 }
 
 // One launch for both stages (decode_onepass_kernel) when the plan goes by
-// value in the small tier (at most kArgTilesS tiles), the pool is bf16 and
-// R <= 32; LORA_ONEPASS_DECODE=0 turns it off.
+// value in the small tier (at most kArgTilesS tiles, compact records), the
+// pool is bf16, R <= 32 and T < 65536; LORA_ONEPASS_DECODE=0 turns it off.
 static bool onepass_enabled() {
   static const bool on = [] {
     const char* e = std::getenv("LORA_ONEPASS_DECODE");
@@ -2004,7 +2021,24 @@ static bool onepass_enabled() {
 
 bool plan_is_onepass(const Geo& g, const TilePlan& p) {
   return onepass_enabled() && g.dtype == LORA_BF16 && small_plan(p, g) && p.wave_tiles > 0 &&
-         p.wave_tiles <= kArgTilesS && g.R <= 32;
+         p.wave_tiles <= kArgTilesS && g.R <= 32 && g.T < 65536;
+}
+
+// The compact by-value records of the one-launch decode kernel (tokens below
+// 65536, so 0xffff marks a row past the tile).
+static PlanArg<kArgC> pack_arg_compact(const TilePlan& p) {
+  PlanArg<kArgC> a;
+  for (int i = 0; i < kArgTilesS * kArgCWords; ++i) a.w[i] = 0xffffffffu;
+  for (int f = 0; f < p.wave_tiles && f < kArgTilesS; ++f) {
+    const int32_t* rec = p.wave_host + (size_t)f * LORA_PLAN_WAVE_WORDS;
+    uint32_t* o = a.w + f * kArgCWords;
+    o[0] = ((uint32_t)rec[1] << 28) | ((uint32_t)rec[0] & 0x0fffffffu);
+    for (int r = 0; r < kWaveTileRows; ++r) {
+      const uint32_t t = rec[4 + r] >= 0 ? (uint32_t)rec[4 + r] & 0xffffu : 0xffffu;
+      o[1 + r / 2] = (o[1 + r / 2] & ~(0xffffu << (16 * (r & 1)))) | (t << (16 * (r & 1)));
+    }
+  }
+  return a;
 }
 
 int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
@@ -2015,7 +2049,7 @@ int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B
   }
   RowList Lw, Lm;
   plan_lists(p, Lw, Lm);
-  return launch_onepass<kArg>(g, x, A, B, y, Lw, p.wave_tiles, st, pack_arg<kArg>(p));
+  return launch_onepass<kArgC>(g, x, A, B, y, Lw, p.wave_tiles, st, pack_arg_compact(p));
 }
 
 int32_t run_pool_load(const Geo& g, void* A_slot_slice, void* B_slot_slice, const void* Asrc,
