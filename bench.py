@@ -92,7 +92,7 @@ def algorithmic(wl):
 class Setup:
     """Replicated pool / x / y for one workload, plus prebuilt device metadata."""
 
-    def __init__(self, wl, replica_bytes):
+    def __init__(self, wl, replica_bytes, ragged=False):
         import torch
         import lora_adapter_pool_amd as L
         self.wl = wl
@@ -105,6 +105,8 @@ class Setup:
             for s in range(wl.num_slices):
                 pool.load(a, s, dev(ad.A[s]), dev(ad.B[s]), ad.rank, ad.alpha, ad.use_rslora)
         self.desc = pool.desc
+        # ragged: each slot's true rank goes to lora_apply_ranked
+        self.slot_ranks = pool.slot_ranks() if ragged else None
         x0, y0 = dev(wl.x), dev(wl.y_in)
         per = (pool.A.numel() + pool.B.numel() + x0.numel() + y0.numel()) * x0.element_size()
         self.nrep = max(1, min(4096, int(np.ceil(replica_bytes / per))))
@@ -128,7 +130,8 @@ class Setup:
         self.stage_ev = [None] * self.nstage
         # the batch's tile plan, copied once, for the kernel-only loops (the same
         # launches lora_apply makes after its own plan copy)
-        self.plan_d, img, _ = L.lora_apply_plan(self.desc, self.ids, self.pre)
+        self.plan_d, img, _ = L.lora_apply_plan(self.desc, self.ids, self.pre,
+                                                slot_ranks=self.slot_ranks)
         self.plan = L.plan_struct(self.plan_d)
         # lora_apply skips the plan copy for plans of at most 48 wavefront tiles
         self.small_plan = self.plan_d["mfma_tiles"] == 0 and self.plan_d["wave_tiles"] <= 48
@@ -143,6 +146,19 @@ class Setup:
         self.bytes_per_rep = per
         torch.cuda.synchronize()
 
+    def _apply(self, r, stage_ptr, stream_ptr):
+        lib = self.L.lib()
+        if self.slot_ranks is None:
+            return lib.lora_apply(ctypes.byref(self.desc), self.pA[r], self.pB[r], self.px[r],
+                                  self.py[r], self.T, self.ids.ctypes.data, self.pre.ctypes.data,
+                                  0, self.ws.data_ptr(), self.ws_bytes, stage_ptr, self.mh_bytes,
+                                  stream_ptr)
+        return lib.lora_apply_ranked(ctypes.byref(self.desc), self.pA[r], self.pB[r], self.px[r],
+                                     self.py[r], self.T, self.ids.ctypes.data,
+                                     self.pre.ctypes.data, 0, self.slot_ranks.ctypes.data,
+                                     self.ws.data_ptr(), self.ws_bytes, stage_ptr, self.mh_bytes,
+                                     stream_ptr)
+
     def apply_step(self, i, stream_ptr):
         import torch
         L = self.L
@@ -150,21 +166,14 @@ class Setup:
         if self.small_plan:
             # the plan travels in the kernel arguments: the GPU never reads the
             # staging buffer, so one buffer serves every call without events
-            st = L.lib().lora_apply(ctypes.byref(self.desc), self.pA[r], self.pB[r], self.px[r],
-                                    self.py[r], self.T, self.ids.ctypes.data, self.pre.ctypes.data,
-                                    0, self.ws.data_ptr(), self.ws_bytes, self.stage[0].data_ptr(),
-                                    self.mh_bytes, stream_ptr)
+            st = self._apply(r, self.stage[0].data_ptr(), stream_ptr)
             if st != 0:
                 raise RuntimeError(f"lora_apply failed: {L.last_error()}")
             return
         j = i % self.nstage
         if self.stage_ev[j] is not None:
             self.stage_ev[j].synchronize()
-        lib = L.lib()
-        st = lib.lora_apply(ctypes.byref(self.desc), self.pA[r], self.pB[r], self.px[r],
-                            self.py[r], self.T, self.ids.ctypes.data, self.pre.ctypes.data, 0,
-                            self.ws.data_ptr(), self.ws_bytes, self.stage[j].data_ptr(),
-                            self.mh_bytes, stream_ptr)
+        st = self._apply(r, self.stage[j].data_ptr(), stream_ptr)
         if st != 0:
             raise RuntimeError(f"lora_apply failed: {L.last_error()}")
         ev = self.stage_ev[j] or torch.cuda.Event()
@@ -685,6 +694,22 @@ def main():
             log(f"[bench] prefill {k}: {r['us']:.2f} us/launch, {r['GBs']:.0f} GB/s, "
                 f"{r['TFLOPs']:.1f} TFLOP/s")
         del s2
+        torch.cuda.empty_cache()
+        # the same batch with each slot's true rank (lora_apply_ranked): the
+        # padded ranks' weights are neither read nor multiplied
+        s3 = [Setup(w, args.replica_mib * 2 ** 20, ragged=True) for w in wl2]
+        el3 = measure(s3, max(20, args.steps // 10), 5, stream_ptr)
+        st3 = el3 / max(20, args.steps // 10)
+        _, pk3 = kernel_roofline(s3, stream_ptr, 50)
+        out["secondary"]["ragged"] = {
+            "slot_ranks": s3[0].slot_ranks.tolist(),
+            "tokens_per_s": a2["Ta"] / st3, "ms_per_step": st3 * 1e3,
+            "speedup_vs_padded": st2 / st3,
+            "per_kernel": {k: {"us": round(r["us"], 2)} for k, r in pk3.items()},
+        }
+        log(f"[bench] prefill ragged ranks: {st3 * 1e6:.1f} us/step vs padded {st2 * 1e6:.1f} "
+            + ", ".join(f"{k} {r['us']:.2f} us" for k, r in pk3.items()))
+        del s3
         torch.cuda.empty_cache()
 
     if args.sweep:

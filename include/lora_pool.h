@@ -274,9 +274,12 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
  * The device image starts image_offset bytes into meta_host and is
  * image_bytes long; offsets below count int32 words from its start:
  *   perm [num_sgmv_rows + num_bgmv_rows]  token of each v row
- *   wave [wave_tiles][16]             slot, rows, first v row, 0, token of
- *                                     each row (-1 past the last row), -1 ...
- *   mfma [mfma_tiles][4]              slot, rows, first v row, first token
+ *   wave [wave_tiles][16]             slot, rows, first v row, rank (0 =
+ *                                     max_lora_rank; see lora_apply_plan_ranked),
+ *                                     token of each row (-1 past the last
+ *                                     row), -1 ...
+ *   mfma [mfma_tiles][4]              slot, rows | rank << 16 (rank as
+ *                                     above), first v row, first token
  *                                     when the tile's tokens are consecutive
  *                                     (perm[first + i] = first token + i),
  *                                     else -1
@@ -313,6 +316,20 @@ typedef struct {
 int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* ids_host,
                         const uint8_t* prefill_host, int32_t bgmv_max_rank, void* meta_host,
                         int64_t meta_host_bytes, lora_plan* plan);
+
+/* lora_apply_plan for pools whose slots hold adapters of smaller rank than
+ * max_lora_rank ([TGI] step 3 pads every adapter to the slot rank; this
+ * variant skips the padding).  slot_ranks: host int32[max_loras], the rank of
+ * the adapter in each slot, 0 = max_lora_rank; the tile records then carry it
+ * (rounded up to 8) and the bf16 MFMA kernels skip the padded ranks' weight
+ * loads and products, which are zero: the result equals lora_apply_plan's.
+ * Plans that travel in the kernel arguments (at most 48 wavefront tiles) and
+ * the fp32 and R > 64 kernels use max_lora_rank.  LORA_E_RANK for an entry
+ * outside [0, max_lora_rank]; otherwise as lora_apply_plan. */
+int32_t lora_apply_plan_ranked(const lora_pool_desc* desc, int32_t T, const int32_t* ids_host,
+                               const uint8_t* prefill_host, int32_t bgmv_max_rank,
+                               const int32_t* slot_ranks, void* meta_host,
+                               int64_t meta_host_bytes, lora_plan* plan);
 
 /* Device half of a plan, so one plan can serve every layer of a batch.
  *   image:      device copy of the plan's image (16-byte aligned,
@@ -378,6 +395,14 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
                    const void* x, void* y, int32_t T, const int32_t* ids_host,
                    const uint8_t* prefill_host, int32_t bgmv_max_rank, void* ws,
                    int64_t ws_bytes, void* meta_host, int64_t meta_host_bytes, void* stream);
+
+/* lora_apply with each slot's true rank (slot_ranks as in
+ * lora_apply_plan_ranked, nullable): same result, padded ranks skipped. */
+int32_t lora_apply_ranked(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
+                          const void* x, void* y, int32_t T, const int32_t* ids_host,
+                          const uint8_t* prefill_host, int32_t bgmv_max_rank,
+                          const int32_t* slot_ranks, void* ws, int64_t ws_bytes,
+                          void* meta_host, int64_t meta_host_bytes, void* stream);
 
 #ifdef __cplusplus
 }

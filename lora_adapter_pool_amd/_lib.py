@@ -104,11 +104,15 @@ _SIGNATURES = {
     "lora_apply_workspace_bytes": (_I64, [_DP, _I32]),
     "lora_apply_host_meta_bytes": (_I64, [_DP, _I32]),
     "lora_apply_plan": (_I32, [_DP, _I32, _P, _P, _I32, _P, _I64, ctypes.POINTER(lora_plan)]),
+    "lora_apply_plan_ranked": (_I32, [_DP, _I32, _P, _P, _I32, _P, _P, _I64,
+                                      ctypes.POINTER(lora_plan)]),
     "lora_plan_shrink": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P]),
     "lora_plan_expand": (_I32, [_DP, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P]),
     "lora_plan_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P,
                                _I64, _P]),
     "lora_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P, _I64, _P]),
+    "lora_apply_ranked": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P, _I64,
+                                 _P]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -296,9 +300,11 @@ def lora_apply_host_meta_bytes(desc, T: int) -> int:
     return _check(lib().lora_apply_host_meta_bytes(ctypes.byref(desc), int(T)))
 
 
-def lora_apply_plan(desc, ids, prefill=None, bgmv_max_rank: int = 0):
+def lora_apply_plan(desc, ids, prefill=None, bgmv_max_rank: int = 0, slot_ranks=None):
     """Host tile plan of one batch: (plan fields as a dict, device image as an
-    int32 array with 'perm', 'wave' [n, 16] and 'mfma' [n, 4] views)."""
+    int32 array with 'perm', 'wave' [n, 16] and 'mfma' [n, 4] views).  With
+    slot_ranks (int32[max_loras], 0 = max_lora_rank) the tile records carry each
+    slot's rank (lora_apply_plan_ranked)."""
     ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
     T = int(ids.shape[0])
     pre = None if prefill is None else np.ascontiguousarray(np.asarray(prefill, dtype=np.uint8))
@@ -307,9 +313,20 @@ def lora_apply_plan(desc, ids, prefill=None, bgmv_max_rank: int = 0):
     off = (-raw.ctypes.data % 64) // 4
     stage = raw[off:off + nbytes // 4]
     p = lora_plan()
-    _check(lib().lora_apply_plan(ctypes.byref(desc), T, ids.ctypes.data if T else None,
-                                 None if pre is None else pre.ctypes.data, int(bgmv_max_rank),
-                                 stage.ctypes.data, nbytes, ctypes.byref(p)))
+    if slot_ranks is None:
+        _check(lib().lora_apply_plan(ctypes.byref(desc), T, ids.ctypes.data if T else None,
+                                     None if pre is None else pre.ctypes.data,
+                                     int(bgmv_max_rank), stage.ctypes.data, nbytes,
+                                     ctypes.byref(p)))
+    else:
+        sr = np.ascontiguousarray(np.asarray(slot_ranks, dtype=np.int32))
+        if sr.shape != (desc.max_loras,):
+            raise ValueError(f"slot_ranks has shape {sr.shape}, needs ({desc.max_loras},)")
+        _check(lib().lora_apply_plan_ranked(ctypes.byref(desc), T,
+                                            ids.ctypes.data if T else None,
+                                            None if pre is None else pre.ctypes.data,
+                                            int(bgmv_max_rank), sr.ctypes.data,
+                                            stage.ctypes.data, nbytes, ctypes.byref(p)))
     d = {k: getattr(p, k) for k, _ in lora_plan._fields_}
     img = stage[p.image_offset // 4: (p.image_offset + p.image_bytes) // 4].copy()
     views = {
@@ -357,3 +374,14 @@ def lora_apply(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgmv_max_r
                             int(T), _ptr(ids_host), _ptr(prefill_host), int(bgmv_max_rank),
                             _ptr(ws), int(ws_bytes), _ptr(meta_host), int(meta_host_bytes),
                             _stream(stream)))
+
+
+def lora_apply_ranked(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgmv_max_rank,
+                      slot_ranks_host, ws, ws_bytes, meta_host, meta_host_bytes,
+                      stream=None) -> None:
+    """lora_apply with each slot's true rank (host int32[max_loras], 0 = max_lora_rank)."""
+    _check(lib().lora_apply_ranked(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), _ptr(x),
+                                   _ptr(y), int(T), _ptr(ids_host), _ptr(prefill_host),
+                                   int(bgmv_max_rank), _ptr(slot_ranks_host), _ptr(ws),
+                                   int(ws_bytes), _ptr(meta_host), int(meta_host_bytes),
+                                   _stream(stream)))

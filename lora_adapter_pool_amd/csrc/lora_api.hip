@@ -359,6 +359,15 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
                    const void* x, void* y, int32_t T, const int32_t* ids_host,
                    const uint8_t* prefill_host, int32_t bgmv_max_rank, void* ws,
                    int64_t ws_bytes, void* meta_host, int64_t meta_host_bytes, void* stream) {
+  return lora_apply_ranked(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgmv_max_rank,
+                           nullptr, ws, ws_bytes, meta_host, meta_host_bytes, stream);
+}
+
+int32_t lora_apply_ranked(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
+                          const void* x, void* y, int32_t T, const int32_t* ids_host,
+                          const uint8_t* prefill_host, int32_t bgmv_max_rank,
+                          const int32_t* slot_ranks, void* ws, int64_t ws_bytes,
+                          void* meta_host, int64_t meta_host_bytes, void* stream) {
   clear_error();
   Geo g;
   if (int32_t e = check_desc(desc, &g)) return e;
@@ -374,8 +383,8 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
     return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
                 (long long)wl.total);
   lora_plan p;
-  if (int32_t e = lora_apply_plan(desc, T, ids_host, prefill_host, bgmv_max_rank, meta_host,
-                                  meta_host_bytes, &p))
+  if (int32_t e = lora_apply_plan_ranked(desc, T, ids_host, prefill_host, bgmv_max_rank,
+                                         slot_ranks, meta_host, meta_host_bytes, &p))
     return e;
   const int32_t rows = p.num_sgmv_rows + p.num_bgmv_rows;
   if (rows == 0) return LORA_OK;

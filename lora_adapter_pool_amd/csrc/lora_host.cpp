@@ -258,8 +258,26 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
 //   - wavefront tiles of LORA_PLAN_WAVE_ROWS rows: every other run.
 // v row numbering: SGMV rows first, then BGMV rows; perm holds the token of
 // every v row.
+int32_t check_slot_ranks(const Geo& g, const int32_t* slot_ranks) {
+  if (!slot_ranks) return LORA_OK;
+  for (int32_t a = 0; a < g.max_loras; ++a) {
+    if (slot_ranks[a] < 0 || slot_ranks[a] > g.R)
+      return fail(LORA_E_RANK, "slot_ranks[%d] = %d is outside [0, max_lora_rank = %d]", a,
+                  slot_ranks[a], g.R);
+  }
+  return LORA_OK;
+}
+
 int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* prefill,
-                  int32_t bgmv_max_rank, int32_t* stage, lora_plan* p) {
+                  int32_t bgmv_max_rank, int32_t* stage, lora_plan* p,
+                  const int32_t* slot_ranks) {
+  // rank a tile record carries: 0 = the pool's R, else the slot's rank
+  // rounded up to 8 (the kernels' vector width), below R
+  auto rank_of = [&](int32_t slot) -> int32_t {
+    if (!slot_ranks || slot_ranks[slot] <= 0) return 0;
+    const int32_t r8 = (slot_ranks[slot] + 7) / 8 * 8;
+    return r8 < g.R ? r8 : 0;
+  };
   const StageLayout sl = stage_layout(T, g.max_loras);
   lora_meta m;
   m.sgmv_perm = stage + sl.perm;
@@ -300,7 +318,7 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
     r[0] = slot;
     r[1] = rows;
     r[2] = first;
-    r[3] = 0;
+    r[3] = rank_of(slot);
     for (int i = 4; i < LORA_PLAN_WAVE_WORDS; ++i) r[i] = -1;
     for (int i = 0; i < rows; ++i) r[4 + i] = tok[i];
     ++nw;
@@ -332,7 +350,7 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
       bool consecutive = true;
       for (int32_t i = 1; i < rows; ++i) consecutive &= tok[i] == tok[0] + i;
       r[0] = slot;
-      r[1] = rows;
+      r[1] = rows | (rank_of(slot) << 16);
       r[2] = first + j;
       r[3] = consecutive ? tok[0] : -1;
       ++nm;
@@ -473,6 +491,14 @@ int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T) {
 int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* ids_host,
                         const uint8_t* prefill_host, int32_t bgmv_max_rank, void* meta_host,
                         int64_t meta_host_bytes, lora_plan* plan) {
+  return lora_apply_plan_ranked(desc, T, ids_host, prefill_host, bgmv_max_rank, nullptr,
+                                meta_host, meta_host_bytes, plan);
+}
+
+int32_t lora_apply_plan_ranked(const lora_pool_desc* desc, int32_t T, const int32_t* ids_host,
+                               const uint8_t* prefill_host, int32_t bgmv_max_rank,
+                               const int32_t* slot_ranks, void* meta_host,
+                               int64_t meta_host_bytes, lora_plan* plan) {
   clear_error();
   Geo g;
   if (int32_t e = check_desc(desc, &g)) return e;
@@ -486,7 +512,9 @@ int32_t lora_apply_plan(const lora_pool_desc* desc, int32_t T, const int32_t* id
     return fail(LORA_E_WORKSPACE, "meta_host has %lld bytes, needs %lld",
                 (long long)meta_host_bytes, (long long)need);
   if (int32_t e = check_ids(ids_host, T, g.max_loras)) return e;
-  return plan_core(g, T, ids_host, prefill_host, bgmv_max_rank, (int32_t*)meta_host, plan);
+  if (int32_t e = check_slot_ranks(g, slot_ranks)) return e;
+  return plan_core(g, T, ids_host, prefill_host, bgmv_max_rank, (int32_t*)meta_host, plan,
+                   slot_ranks);
 }
 
 }  // extern "C"

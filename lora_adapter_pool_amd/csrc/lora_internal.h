@@ -77,9 +77,15 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
                         lora_meta* out);
 
 // Host half of lora_apply on validated arguments: metadata and tile plan into
-// `stage` (stage_layout(T, g.max_loras).total_words words).
+// `stage` (stage_layout(T, g.max_loras).total_words words).  slot_ranks
+// (nullable, max_loras entries in [0, R], 0 = R) gives each slot's true rank:
+// tile records then carry it (rounded up to 8) so the MFMA kernels skip the
+// padded ranks.
 int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* prefill,
-                  int32_t bgmv_max_rank, int32_t* stage, lora_plan* plan);
+                  int32_t bgmv_max_rank, int32_t* stage, lora_plan* plan,
+                  const int32_t* slot_ranks = nullptr);
+// slot_ranks entries in [0, R]
+int32_t check_slot_ranks(const Geo& g, const int32_t* slot_ranks);
 
 bool log_enabled();
 

@@ -229,6 +229,7 @@ template <int MODE> constexpr int arg_tiles() { return MODE == kArgL ? kArgTiles
 template <int TM> struct TileRows {
   int vrow0;
   int cnt;
+  int rank;  // ranks the tile's adapter uses: the record's rank, else the pool's R
   uint32_t valid;
   int tok[TM];
   int aid[TM];
@@ -247,6 +248,7 @@ __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
                                           bool copy = false) {
   static_assert(TM <= LORA_PLAN_WAVE_WORDS - 4, "a tile record holds at most 12 tokens");
   const int lane = threadIdx.x & 63;
+  tr.rank = g.R;
   if constexpr (MODE == kArg || MODE == kArgL) {
     static_assert(TM <= kArgWords - 2, "a packed record holds kArgWords - 2 tokens");
     if (f >= L.num_tiles || f >= arg_tiles<MODE>()) return false;
@@ -279,6 +281,8 @@ __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
     const int sid = __builtin_amdgcn_readlane(w, 0);
     tr.cnt = __builtin_amdgcn_readlane(w, 1);
     tr.vrow0 = __builtin_amdgcn_readlane(w, 2);
+    const int rk = __builtin_amdgcn_readlane(w, 3);
+    tr.rank = rk > 0 && rk < g.R ? rk : g.R;
 #pragma unroll
     for (int r = 0; r < TM; ++r) {
       tr.tok[r] = __builtin_amdgcn_readlane(w, 4 + r);
@@ -868,8 +872,8 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      ap[t][j] = A + ((size_t)(a * g.S + s) * R + min(16 * t + 8 * j + r8, R - 1)) * g.K + kxa;
+    for (int j = 0; j < 2; ++j)  // ranks past the adapter's re-read its last row (cache-hot)
+      ap[t][j] = A + ((size_t)(a * g.S + s) * R + min(16 * t + 8 * j + r8, tr.rank - 1)) * g.K + kxa;
   const uint32_t lo8 = all_or_none((lane & 15) < 8);  // operand rows / ranks 0..7 of a tile
   f32x4 d[NT];
 #pragma unroll
@@ -909,7 +913,7 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
       float acc = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) acc += red[w][r][n];
-      v[((size_t)part * v_rows + tr.vrow0 + r) * SR + s * R + n] = acc;
+      v[((size_t)part * v_rows + tr.vrow0 + r) * SR + s * R + n] = n < tr.rank ? acc : 0.f;
     }
   }
 }
@@ -981,7 +985,7 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const int k = 32 * kc + 8 * g4;
-        const bool ok = c < out_s && k < R;
+        const bool ok = c < out_s && k < tr.rank;  // ranks past the adapter's are zero
         bt[q][h][kc] = ld16(Ba + (size_t)(ok ? c : 0) * R + (ok ? k : 0)) & all_or_none(ok);
       }
     }
@@ -1067,15 +1071,18 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
 // not be read from the list; segments mode gives tok0 = -1.
 template <int TMR, int MODE>
 __device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int& cnt, int& sid,
-                                          int& tok0, bool copy = false) {
+                                          int& tok0, int& rk, bool copy = false) {
   tok0 = -1;
+  rk = 0;
   if constexpr (MODE == kList) {
     if (f >= L.num_tiles) return false;
     const int w = L.tiles[(size_t)f * LORA_PLAN_MFMA_WORDS + (threadIdx.x & 3)];
     if (copy && L.copy_tiles && threadIdx.x < LORA_PLAN_MFMA_WORDS)
       L.copy_tiles[(size_t)f * LORA_PLAN_MFMA_WORDS + threadIdx.x] = w;
     sid = __builtin_amdgcn_readlane(w, 0);
-    cnt = __builtin_amdgcn_readlane(w, 1);
+    const int w1 = __builtin_amdgcn_readlane(w, 1);
+    cnt = w1 & 0xffff;
+    rk = (int)((uint32_t)w1 >> 16);
     r0 = __builtin_amdgcn_readlane(w, 2);
     tok0 = __builtin_amdgcn_readlane(w, 3);
   } else {
@@ -1122,8 +1129,10 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
   const int part = rem - s * ksplit;
   int r0, cnt, sid, tok0;
   const bool copy = s == 0 && part == 0 && blockIdx.y == 0;
-  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0, copy)) return;
+  int rk_rec;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0, rk_rec, copy)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
+  const int rr = rk_rec > 0 && rk_rec < g.R ? rk_rec : g.R;  // the adapter's ranks
   const int rank0 = blockIdx.y * NR;
   // K steps of this split
   const int nsteps = (g.K + KS - 1) / KS;
@@ -1145,7 +1154,7 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
     xp[j] = x + (size_t)(ok ? tk : 0) * g.K;
     xm[j] = all_or_none(ok);
     const int rk = rank0 + r;
-    const bool rok = rk < g.R;
+    const bool rok = rk < rr;  // ranks past the adapter's are zero: not loaded
     ap[j] = A + ((size_t)(sid * g.S + s) * g.R + (rok ? rk : 0)) * g.K;
     am[j] = all_or_none(rok);
   }
@@ -1217,7 +1226,7 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 32 * wm + 16 * mt + 4 * grp + j;
-        if (row < cnt && rk < g.R) vp[(size_t)row * SR + rk] = acc[mt][nt][j];
+        if (row < cnt && rk < g.R) vp[(size_t)row * SR + rk] = rk < rr ? acc[mt][nt][j] : 0.f;
       }
     }
   }
@@ -1266,7 +1275,8 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
   const int col0 = (cidx - ch.start[s]) * NC;
   const int out_s = g.out[s];
   int r0, cnt, sid, tok0;
-  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0)) return;
+  int rk_rec;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0, rk_rec)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int R = g.R;
   const int SR = g.S * R;
@@ -1430,9 +1440,11 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
   const int c_end = min(ch.start[s + 1], c_begin + cpw);
   const int out_s = g.out[s];
   int r0, cnt, sid, tok0;
-  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0)) return;
+  int rk_rec;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0, rk_rec)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int R = g.R;  // <= 64, a multiple of 8
+  const int rr = rk_rec > 0 && rk_rec < R ? rk_rec : R;  // the adapter's ranks
   const int SR = g.S * R;
   const __amdgpu_buffer_rsrc_t yb = make_rsrc(y, (uint32_t)((size_t)g.T * g.O * sizeof(uint16_t)));
   if (tid < TM) {
@@ -1452,7 +1464,7 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
   auto load_chunk = [&](int c, u32x4(&br)[4], uint32_t(&bm)[4], u32x4(&yr)[4]) {
     const int col0 = (c - ch.start[s]) * NC;
     const uint16_t* Bt = B + ((size_t)sid * g.O + g.off[s] + col0) * R;
-    const bool bk_ok = 8 * b8 < R;
+    const bool bk_ok = 8 * b8 < rr;  // ranks past the adapter's are zero: not loaded
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cc = bcol + 32 * j;
@@ -1522,7 +1534,7 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
     f32x4 acc[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < R; kk += 32) {
+    for (int kk = 0; kk < rr; kk += 32) {
       const int vo = (16 * wave + m16) * LDK + kk + 8 * grp;
       const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vh[vo]));
       const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vl[vo]));

@@ -5,7 +5,8 @@ pool once ([vLLM] step 2 of the vLLM offline multi-LoRA article: max_loras
 slots pre-allocated at max_lora_rank), loads adapters through lora_pool_load and
 calls lora_apply with a device workspace and a small ring of pinned host
 staging buffers (a buffer is reused only after the stream has passed the call
-that last read it).
+that last read it).  It records the rank loaded into each slot and slice, so
+apply(..., ragged=True) can pass each slot's true rank to lora_apply_ranked.
 """
 from __future__ import annotations
 
@@ -35,6 +36,8 @@ class LoraPool:
         self.device = device
         self.A = torch.zeros(L.lora_pool_bytes_A(self.desc) // eb, dtype=self.tdtype, device=device)
         self.B = torch.zeros(L.lora_pool_bytes_B(self.desc) // eb, dtype=self.tdtype, device=device)
+        # rank last loaded into each (slot, slice); 0 = nothing loaded (zeros)
+        self.loaded_ranks = np.zeros((self.max_loras, len(self.out_features)), np.int32)
         self._ws = None
         self._staging: List[list] = [[None, None] for _ in range(max(1, staging_slots))]
         self._next = 0
@@ -50,9 +53,16 @@ class LoraPool:
              use_rslora: bool = False, stream=None) -> None:
         L.lora_pool_load(self.desc, self.A, self.B, slot, slice_, A_src, B_src, rank, alpha,
                          use_rslora, stream=stream)
+        self.loaded_ranks[slot, slice_] = rank
 
     def clear(self, slot: int, stream=None) -> None:
         L.lora_pool_clear(self.desc, self.A, self.B, slot, stream=stream)
+        self.loaded_ranks[slot, :] = 0
+
+    def slot_ranks(self) -> np.ndarray:
+        """int32[max_loras]: the largest rank loaded into each slot; a slot with
+        nothing loaded holds zeros and reports 1 (any rank gives a zero delta)."""
+        return np.maximum(self.loaded_ranks.max(axis=1), 1).astype(np.int32)
 
     def workspace(self, T: int):
         need = L.lora_apply_workspace_bytes(self.desc, T)
@@ -72,8 +82,10 @@ class LoraPool:
             slot[0] = buf
         return slot, buf, need
 
-    def apply(self, x, y, ids, prefill=None, bgmv_max_rank: int = 0, stream=None) -> None:
-        """y (in place) += per-row LoRA delta for x; ids int32 per row (-1 = none)."""
+    def apply(self, x, y, ids, prefill=None, bgmv_max_rank: int = 0, stream=None,
+              ragged: bool = False) -> None:
+        """y (in place) += per-row LoRA delta for x; ids int32 per row (-1 = none).
+        ragged: skip each slot's padded ranks (same result)."""
         torch = self.torch
         T = int(x.shape[0])
         ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
@@ -83,8 +95,12 @@ class LoraPool:
         ws = self.workspace(T)
         slot, buf, need = self._staging_buffer(T, stream)
         st = torch.cuda.current_stream() if stream is None else stream
-        L.lora_apply(self.desc, self.A, self.B, x, y, T, ids, pre, bgmv_max_rank, ws, ws.numel(),
-                     buf, buf.numel(), stream=st)
+        if ragged:
+            L.lora_apply_ranked(self.desc, self.A, self.B, x, y, T, ids, pre, bgmv_max_rank,
+                                self.slot_ranks(), ws, ws.numel(), buf, buf.numel(), stream=st)
+        else:
+            L.lora_apply(self.desc, self.A, self.B, x, y, T, ids, pre, bgmv_max_rank, ws,
+                         ws.numel(), buf, buf.numel(), stream=st)
         ev = slot[1] or torch.cuda.Event()
         ev.record(st)
         slot[1] = ev

@@ -252,3 +252,29 @@ def test_apply_validation_before_hip():
     # last_error carries a message for the most recent failure
     _status(L.lora_apply, *with_(6, bad_ids))
     assert "ids[3]" in L.last_error()
+
+
+def test_apply_ranked_validation_before_hip():
+    """lora_apply_ranked checks slot_ranks (and everything lora_apply checks)
+    on the host before any GPU call."""
+    d = L.make_desc("bf16", 4, 16, 256, [256])
+    T = 6
+    ws_need = L.lora_apply_workspace_bytes(d, T)
+    mh_need = L.lora_apply_host_meta_bytes(d, T)
+    ids = np.array([0, 1, -1, 3, 2, 0], np.int32)
+    meta = _aligned_i32(mh_need // 4)
+    ranks = np.array([8, 16, 0, 4], np.int32)
+    ok = [d, FAKE, FAKE, FAKE, FAKE + 64, T, ids, None, 0, ranks, FAKE, ws_need, meta, mh_need, 0]
+
+    def with_(i, v):
+        a = list(ok)
+        a[i] = v
+        return a
+    for bad in ([8, 16, 17, 4], [8, -2, 0, 4]):
+        assert _status(L.lora_apply_ranked, *with_(9, np.array(bad, np.int32))) == _lib.LORA_E_RANK
+    assert "slot_ranks" in L.last_error()
+    bad_ids = ids.copy()
+    bad_ids[3] = 4
+    assert _status(L.lora_apply_ranked, *with_(6, bad_ids)) == _lib.LORA_E_ID
+    assert _status(L.lora_apply_ranked, *with_(11, ws_need - 1)) == _lib.LORA_E_WORKSPACE
+    assert _status(L.lora_apply_ranked, *with_(5, 0)) == 0  # T = 0: no-op

@@ -33,10 +33,19 @@ def _bgmv_runs(b):
     return runs
 
 
-def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
+def record_rank(desc, slot_ranks, slot):
+    """Rank a tile record carries: the slot's rank rounded up to 8, or 0 (the
+    pool rank) without slot ranks, for rank 0 or when the rounding reaches it."""
+    if slot_ranks is None or slot_ranks[slot] <= 0:
+        return 0
+    r8 = -(-int(slot_ranks[slot]) // 8) * 8
+    return r8 if r8 < desc.max_lora_rank else 0
+
+
+def _check_plan(desc, ids, prefill, bgmv_max_rank=0, slot_ranks=None):
     ids = np.asarray(ids, np.int32)
     R = desc.max_lora_rank
-    p, img, v = L.lora_apply_plan(desc, ids, prefill, bgmv_max_rank)
+    p, img, v = L.lora_apply_plan(desc, ids, prefill, bgmv_max_rank, slot_ranks=slot_ranks)
     m = L.lora_build_meta(ids, prefill, desc.max_loras, R, bgmv_max_rank)
     ns, nb = m["sgmv_perm"].size, m["bgmv_tok"].size
     assert (p["num_sgmv_rows"], p["num_bgmv_rows"], p["num_segs"]) == (ns, nb, m["seg_ids"].size)
@@ -67,8 +76,9 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
 
     shrink_cover = np.zeros(ns + nb, np.int64)
     for rec in v["wave"]:
-        slot, rows, first, zero = (int(x) for x in rec[:4])
-        assert zero == 0 and 1 <= rows <= WAVE_ROWS and 0 <= slot < desc.max_loras
+        slot, rows, first, rank = (int(x) for x in rec[:4])
+        assert 1 <= rows <= WAVE_ROWS and 0 <= slot < desc.max_loras
+        assert rank == record_rank(desc, slot_ranks, slot)
         assert 0 <= first and first + rows <= ns + nb
         np.testing.assert_array_equal(rec[4:4 + rows], row_tok[first:first + rows])
         assert np.all(rec[4 + rows:] == -1)
@@ -78,7 +88,9 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0):
         assert not np.any(is_mfma[first:first + rows])
         shrink_cover[first:first + rows] += 1
     for rec in v["mfma"]:
-        slot, rows, first, tok0 = (int(x) for x in rec)
+        slot, rows_rank, first, tok0 = (int(x) for x in rec)
+        rows = rows_rank & 0xffff  # rows | rank << 16
+        assert rows_rank >> 16 == record_rank(desc, slot_ranks, slot)
         assert bf16 and 1 <= rows <= MFMA_ROWS and first + rows <= ns + nb
         # word 3: first token when the tile's tokens are consecutive, else -1
         toks = v["perm"][first:first + rows]
@@ -162,6 +174,47 @@ def test_plan_fuzz():
             ids = np.sort(ids)
         pre = (rng.random(T) < rng.random()).astype(np.uint8)
         _check_plan(d, ids, pre if it % 5 else None, bgmv_max_rank=int(rng.choice([0, 8, 128])))
+
+
+def test_plan_ragged_ranks():
+    """With slot ranks the plan is the padded plan with each record's rank
+    field set: same tiles, rows, tokens and K splits."""
+    rng = np.random.default_rng(11)
+    for it in range(120):
+        ml = int(rng.integers(1, 40))
+        R = int(rng.choice([8, 16, 32, 64, 128]))
+        T = int(rng.integers(0, 600)) if it % 6 else int(rng.integers(1500, 2600))
+        d = L.make_desc("bf16" if it % 4 else "f32", ml, R, 128, [64, 96])
+        ids = rng.integers(-1, ml, size=T).astype(np.int32)
+        if it % 3 == 0:
+            ids = np.sort(ids)
+        pre = (rng.random(T) < 0.5).astype(np.uint8) if it % 2 else None
+        ranks = rng.integers(0, R + 1, size=ml).astype(np.int32)
+        p0, img0, v0 = L.lora_apply_plan(d, ids, pre)
+        p1 = _check_plan(d, ids, pre, slot_ranks=ranks)
+        _, img1, v1 = L.lora_apply_plan(d, ids, pre, slot_ranks=ranks)
+        assert p0 == p1
+        np.testing.assert_array_equal(v0["perm"], v1["perm"])
+        w0, w1 = v0["wave"].copy(), v1["wave"].copy()
+        w0[:, 3] = w1[:, 3] = 0
+        np.testing.assert_array_equal(w0, w1)
+        np.testing.assert_array_equal(v0["mfma"][:, 1], v1["mfma"][:, 1] & 0xffff)
+        np.testing.assert_array_equal(np.delete(v0["mfma"], 1, axis=1),
+                                      np.delete(v1["mfma"], 1, axis=1))
+
+
+def test_plan_ragged_rank_errors():
+    d = L.make_desc("bf16", 4, 16, 64, [64])
+    ids = np.array([0, 1, 2, 3], np.int32)
+    for bad in ([0, 0, 0, 17], [-1, 0, 0, 0]):
+        with pytest.raises(L.LoraError) as e:
+            L.lora_apply_plan(d, ids, slot_ranks=np.array(bad, np.int32))
+        assert e.value.status == _lib.LORA_E_RANK
+    with pytest.raises(ValueError):
+        L.lora_apply_plan(d, ids, slot_ranks=np.zeros(3, np.int32))
+    # a full rank, or a rank that rounds up to the pool's, reads as 0
+    _, _, v = L.lora_apply_plan(d, ids, slot_ranks=np.array([16, 9, 8, 1], np.int32))
+    assert list(v["wave"][:, 3]) == [0, 0, 8, 8]
 
 
 @pytest.mark.parametrize("T,n,rank,want_mfma", [(64, 8, 16, False), (512, 4, 16, False),
