@@ -245,6 +245,104 @@ def measure(setups, steps, warmup, stream_ptr):
     return time.perf_counter() - t0
 
 
+def ragged_decode_leg(seed, steps, stream_ptr, replica_bytes):
+    """Decode batch whose adapters (rank 16) sit in a pool sized for rank 64:
+    lora_apply with the padded slots against lora_apply_ranked with each slot's
+    true rank; the padded ranks are most of the weight bytes here."""
+    import dataclasses
+    import torch
+    import workloads as W
+    wl = W.config_bgmv_decode(seed=seed, T=256, K=4096, O=4096, n_adapters=64, rank=16)
+    wl = dataclasses.replace(wl, max_lora_rank=64)
+    res = {"workload": "BGMV decode bf16: in=out=4096, 256 tokens, 64 adapters rank 16 in a "
+                       "pool of rank 64, 10% rows without adapter"}
+    for ragged in (False, True):
+        st = [Setup(wl, replica_bytes, ragged=ragged)]
+        t = measure(st, steps, 10, stream_ptr) / steps
+        _, pk = kernel_roofline(st, stream_ptr, 50)
+        res["ragged" if ragged else "padded"] = {
+            "us_per_step": round(t * 1e6, 2),
+            "per_kernel_us": {k: round(r["us"], 2) for k, r in pk.items()}}
+        del st
+        torch.cuda.empty_cache()
+    res["speedup"] = res["padded"]["us_per_step"] / res["ragged"]["us_per_step"]
+    return res
+
+
+def merge_leg(seed, stream_ptr):
+    """Merged-weight mode: lora_merge_weights on one projection's weight (rank
+    64 pool), timed with HIP events over back-to-back launches, against the
+    bytes it must move (W read and written, the slot's A and B read once); and
+    a single-adapter prefill batch run both ways: base GEMM then lora_apply, or
+    the base GEMM on the merged weight alone (torch's GEMM for the base)."""
+    import torch
+    import lora_adapter_pool_amd as L
+    import workloads as W
+    res = {}
+    for name, out_s, K in (("4096x4096", 4096, 4096), ("14336x4096", 14336, 4096)):
+        pool = L.LoraPool("bf16", 2, 64, K, [out_s])
+        rng = np.random.default_rng(seed)
+        A = torch.from_numpy(rng.standard_normal((64, K), np.float32) / np.sqrt(K)).to(
+            torch.bfloat16).cuda()
+        B = torch.from_numpy(rng.standard_normal((out_s, 64), np.float32) * 0.02).to(
+            torch.bfloat16).cuda()
+        pool.load(0, 0, A, B, 64, 128.0)
+        W0 = torch.from_numpy(W.draw_base_weight(seed, out_s, K, "bf16")).to(torch.bfloat16).cuda()
+        # enough replicas of (W, W_out) that no launch finds its weights in a cache
+        nrep = max(2, int(np.ceil(2 ** 30 / (2 * W0.numel() * 2))))
+        Ws = [W0] + [W0.clone() for _ in range(nrep - 1)]
+        Wos = [torch.empty_like(W0) for _ in range(nrep)]
+        for i in range(5):
+            L.lora_merge_weights(pool.desc, pool.A, pool.B, 0, 0, Ws[i % nrep], Wos[i % nrep],
+                                 stream=stream_ptr)
+        n = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            L.lora_merge_weights(pool.desc, pool.A, pool.B, 0, 0, Ws[i % nrep], Wos[i % nrep],
+                                 stream=stream_ptr)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        nbytes = 2 * out_s * K * 2 + 64 * K * 2 + out_s * 64 * 2
+        res[name] = {"us": round(us, 2), "GBs": round(nbytes / us / 1e3, 1),
+                     "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3),
+                     "kernel": "merge_mfma_kernel"}
+        del pool, A, B, W0, Ws, Wos
+        torch.cuda.empty_cache()
+    # one adapter for the whole batch: 16 sequences of 64..1024 tokens, in = out = 4096
+    wl = W.config_sgmv_prefill(seed=seed, n_adapters=1, rank_choices=(16,), max_lora_rank=16)
+    pool = L.LoraPool("bf16", 1, 16, 4096, [4096])
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()  # noqa
+    ad = wl.slots[0]
+    pool.load(0, 0, dev(ad.A[0]), dev(ad.B[0]), ad.rank, ad.alpha)
+    Wb = dev(W.draw_base_weight(seed, 4096, 4096, "bf16"))
+    Wt = Wb.t().contiguous()
+    Wmt = pool.merge(0, 0, Wb).t().contiguous()
+    x = dev(wl.x)
+
+    def runtime():
+        y = x @ Wt
+        pool.apply(x, y, wl.ids, wl.prefill)
+        return y
+
+    def merged():
+        return x @ Wmt
+
+    out = {}
+    for label, fn in (("base_gemm_plus_delta", runtime), ("merged_gemm", merged)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        out[label] = round((time.perf_counter() - t0) / 20 * 1e6, 1)
+    res["single_adapter_prefill_us"] = dict(out, tokens=int(wl.T))
+    return res
+
+
 def device_meta_leg(s, steps, stream_ptr):
     """The delta path driven from device metadata: lora_build_meta_device, then
     the four grouped entry points with upper-bound sizes (num_segs = max_loras,
@@ -668,6 +766,13 @@ def main():
         f"(5 launches)")
     del setups
     torch.cuda.empty_cache()
+    if not args.no_secondary:
+        out["ragged_decode"] = ragged_decode_leg(args.seed, max(50, args.steps // 4), stream_ptr,
+                                                 args.replica_mib * 2 ** 20)
+        log(f"[bench] ragged decode: {out['ragged_decode']}")
+        out["merge"] = merge_leg(args.seed, stream_ptr)
+        log(f"[bench] merged weights: {out['merge']}")
+        torch.cuda.empty_cache()
 
     if not args.no_secondary and args.workload != "sgmv_prefill":
         wl2 = make_workloads("sgmv_prefill", args.seed)

@@ -162,6 +162,28 @@ int32_t lora_pool_load(const lora_pool_desc* desc, void* A_pool, void* B_pool,
 int32_t lora_pool_clear(const lora_pool_desc* desc, void* A_pool, void* B_pool,
                         int32_t slot, void* stream);
 
+/* Merged-weight mode ([QA] "Multi-LoRA serving", the follow-up on merging an
+ * adapter into the base: a server running one fine-tune merges it and pays no
+ * per-request delta; serving many adapters keeps the runtime path).  For slot
+ * `slot`, slice `slice` (width out_s = out_features[slice]):
+ *   W_out[o][k] = round(W[o][k] + sum_{r<R} B_pool[slot][off_s + o][r] *
+ *                                           A_pool[slot][slice][r][k])
+ * i.e. W + s_a B A with the scale already folded into the pool's B; fp32
+ * accumulation and one rounding to the pool dtype (nearest, ties to even).
+ *   W, W_out: device [out_s][in_features] of the pool dtype, row-major (the
+ *             base projection's weight rows for this slice), 16-byte aligned.
+ *             W_out == W merges in place; other overlaps are rejected.  Merging
+ *             is not undone by subtracting (the rounding is not invertible):
+ *             keep the base W and merge the next adapter from it.
+ * One kernel on `stream` (asynchronous; bf16 pools use MFMA).  Errors:
+ * LORA_E_ID for slot / slice out of range, LORA_E_RANK if max_lora_rank >
+ * LORA_MERGE_MAX_RANK, LORA_E_ALIGN, LORA_E_ARG on NULL or overlapping
+ * buffers, all before any HIP call. */
+#define LORA_MERGE_MAX_RANK 512
+int32_t lora_merge_weights(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
+                           int32_t slot, int32_t slice, const void* W, void* W_out,
+                           void* stream);
+
 /* ------------------------------------------------------------- metadata */
 
 /* Host-only, bit-exact metadata builder ([TGI] step 4).

@@ -111,6 +111,7 @@ _SIGNATURES = {
     "lora_plan_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P,
                                _I64, _P]),
     "lora_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P, _I64, _P]),
+    "lora_merge_weights": (_I32, [_DP, _P, _P, _I32, _I32, _P, _P, _P]),
     "lora_apply_ranked": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P, _I64,
                                  _P]),
 }
@@ -385,3 +386,10 @@ def lora_apply_ranked(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgm
                                    int(bgmv_max_rank), _ptr(slot_ranks_host), _ptr(ws),
                                    int(ws_bytes), _ptr(meta_host), int(meta_host_bytes),
                                    _stream(stream)))
+
+
+def lora_merge_weights(desc, A_pool, B_pool, slot, slice_, W, W_out, stream=None) -> None:
+    """W_out = round(W + B_fold A) for one slot and slice (W, W_out [out_s, K]
+    device tensors of the pool dtype; W_out may be W)."""
+    _check(lib().lora_merge_weights(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), int(slot),
+                                    int(slice_), _ptr(W), _ptr(W_out), _stream(stream)))

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblora_pool.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["lora_host.cpp", "lora_kernels.hip", "lora_meta.hip", "lora_api.hip"]
+SOURCES = ["lora_host.cpp", "lora_kernels.hip", "lora_meta.hip", "lora_merge.hip", "lora_api.hip"]
 ARCH = os.environ.get("LORA_POOL_ARCH", "gfx950")
 
 

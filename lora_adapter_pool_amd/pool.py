@@ -59,6 +59,20 @@ class LoraPool:
         L.lora_pool_clear(self.desc, self.A, self.B, slot, stream=stream)
         self.loaded_ranks[slot, :] = 0
 
+    def merge(self, slot: int, slice_: int, W, W_out=None, stream=None):
+        """Merged-weight mode: W_out (default: a new tensor) = W + s B A of the
+        adapter in `slot`, for the base weight W [out_s, in] of slice `slice_`."""
+        if W.dtype != self.tdtype or not W.is_contiguous():
+            raise L.LoraError(L.LORA_E_DTYPE, "W must be a contiguous tensor of the pool dtype")
+        if tuple(W.shape) != (self.out_features[slice_], self.K):
+            raise L.LoraError(L.LORA_E_SHAPE, f"W must be [{self.out_features[slice_]}, {self.K}]")
+        out = self.torch.empty_like(W) if W_out is None else W_out
+        if out.dtype != W.dtype or out.shape != W.shape or not out.is_contiguous():
+            raise L.LoraError(L.LORA_E_SHAPE, "W_out must match W")
+        st = self.torch.cuda.current_stream() if stream is None else stream
+        L.lora_merge_weights(self.desc, self.A, self.B, slot, slice_, W, out, stream=st)
+        return out
+
     def slot_ranks(self) -> np.ndarray:
         """int32[max_loras]: the largest rank loaded into each slot; a slot with
         nothing loaded holds zeros and reports 1 (any rank gives a zero delta)."""

@@ -186,6 +186,31 @@ def f32_to_bf16_rne(a) -> np.ndarray:
     return out
 
 
+def f64_to_bf16_rne(a) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 in one step, ties to even
+    (finite inputs).  Rounding through float32 first is not the same: a value
+    just above a bfloat16 midpoint can land on the midpoint in float32 and
+    then tie to even.  Method: take the float32-then-bfloat16 candidate and its
+    two bfloat16 neighbours, keep the one nearest in float64, ties to the even
+    bit pattern.  Returns float64 holding the rounded values."""
+    v = np.asarray(a, dtype=np.float64)
+    c = f32_to_bf16_rne(v.astype(np.float32)).view(np.uint32) >> np.uint32(16)
+    best = None
+    best_err = None
+    for d in (0, -1, 1):  # the float32-route candidate first: it is always finite
+        bits = (c.astype(np.int64) + d).astype(np.uint32)
+        val = (bits << np.uint32(16)).astype(np.uint32).view(np.float32).astype(np.float64)
+        err = np.abs(val - v)
+        if best is None:
+            best, best_err, best_bits = val, err, bits
+            continue
+        take = (err < best_err) | ((err == best_err) & ((bits & 1) == 0) & ((best_bits & 1) == 1))
+        best = np.where(take, val, best)
+        best_bits = np.where(take, bits, best_bits)
+        best_err = np.where(take, err, best_err)
+    return best
+
+
 def round_exact_to_dtype(values_fp64, dtype: str) -> np.ndarray:
     """Single rounding of values that are exactly representable in fp32 (e.g.
     integers below 2^24) to the storage dtype."""
@@ -253,6 +278,18 @@ def forward_from_pool_rows(wl, pool: Dict[int, dict], rows: Iterable[int]) -> np
                 y[off:off + width] += pool[a]["B"][sl].astype(np.float64) @ v
         out[i] = y
     return out
+
+
+def merged_weight(W, pool_slot: dict, sl: int, dtype: str) -> np.ndarray:
+    """Merged-weight mode ([QA] follow-up on merging an adapter into the base):
+    W' = W + B_fold A_pad for one slice of one pool slot (B_fold holds the
+    scale, so this is W + s_a B A), formed in fp64 and rounded once to the
+    dtype, nearest with ties to even.  W is [out_s, K]."""
+    Wm = np.asarray(W, np.float64) + (np.asarray(pool_slot["B"][sl], np.float64)
+                                      @ np.asarray(pool_slot["A"][sl], np.float64))
+    if dtype == "bf16":
+        return f64_to_bf16_rne(Wm)
+    return Wm.astype(np.float32).astype(np.float64)
 
 
 def pool_bytes(max_loras: int, num_slices: int, R: int, K: int, out_total: int,
@@ -368,6 +405,10 @@ PINS = {
     "brute_force_rows": "hand worked example (tests/golden/delta_hand.json)",
     "merged_weight_rows": "hand worked example; agrees with lora_forward_rows",
     "f32_to_bf16_rne": "torch's float32 -> bfloat16 cast (a library routine), ties",
+    "f64_to_bf16_rne": "equals f32_to_bf16_rne on float32 values; hand double-rounding "
+                       "cases; brute-force nearest over all bfloat16 values near 1",
+    "merged_weight": "merged weight times x equals the runtime delta (forward_from_pool); "
+                     "hand 2x2 example; exact on integer inputs",
     "expected_pool": "padding inert (forward_from_pool == forward for power-of-two "
                      "scales); fold rounding bounded by 2^-8",
     "build_meta": "worked example (tests/golden/builder_tiny.json); numpy stable "

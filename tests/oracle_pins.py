@@ -200,6 +200,54 @@ def pin_bf16_rne(O):
     assert np.isnan(O.f32_to_bf16_rne(np.array([np.nan], np.float32))[0])
 
 
+def pin_f64_to_bf16_rne(O):
+    import torch
+    # float32 inputs: one rounding, so torch's float32 -> bfloat16 cast decides
+    rng = np.random.default_rng(1)
+    a = np.concatenate([rng.standard_normal(5000).astype(np.float32) * np.float32(7.0),
+                        np.array([1.00390625, 1.01171875, -1.00390625, 3.0], np.float32)])
+    ref = torch.from_numpy(a.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.f64_to_bf16_rne(a.astype(np.float64)), ref)
+    # hand cases where rounding through float32 first goes wrong: just above,
+    # just below and exactly on the midpoint between 1 and 1 + 2^-7
+    got = O.f64_to_bf16_rne(np.array([1 + 2 ** -8 + 2 ** -30, 1 + 2 ** -8 - 2 ** -30, 1 + 2 ** -8,
+                                      -(1 + 2 ** -8 + 2 ** -30), 1 + 3 * 2 ** -8]))
+    assert list(got) == [1 + 2 ** -7, 1.0, 1.0, -(1 + 2 ** -7), 1 + 2 ** -6]
+    # brute force: nearest of the 129 bfloat16 values in [1, 2], ties to even
+    grid = 1.0 + np.arange(129) / 128.0
+    v = 1.0 + rng.random(3000)
+    v[:200] = 1.0 + (rng.integers(0, 128, 200) + 0.5) / 128.0  # exact midpoints
+    d = np.abs(v[:, None] - grid[None, :])
+    best = d.min(axis=1, keepdims=True)
+    want = []
+    for i in range(v.size):
+        cand = np.nonzero(d[i] == best[i, 0])[0]
+        want.append(grid[cand[0]] if cand.size == 1 else grid[[c for c in cand if c % 2 == 0][0]])
+    assert np.array_equal(O.f64_to_bf16_rne(v), np.asarray(want))
+
+
+def pin_merged_weight(O):
+    # hand 2 x 2: W + B A with B = [[2], [0.5]], A = [[1, -1]] (rank 1 padded to 2)
+    slot = {"A": [np.array([[1.0, -1.0], [0.0, 0.0]])], "B": [np.array([[2.0, 0.0], [0.5, 0.0]])]}
+    W0 = np.array([[1.0, 2.0], [3.0, 4.0]])
+    for dt in ("f32", "bf16"):
+        assert np.array_equal(O.merged_weight(W0, slot, 0, dt), [[3.0, 0.0], [3.5, 3.5]])
+    # exact integer inputs: the merged weight applied to x equals the base
+    # product plus the runtime delta from the same pool, slice by slice
+    wl = W.config_integer(seed=5, T=24, K=72, outs=(40, 24), max_loras=4, max_lora_rank=16,
+                          ranks=(8, 16, 8, 16), dtype="bf16")
+    pool = O.expected_pool(wl)
+    offs = O.slice_offsets(wl.out_features)
+    rows = [t for t in range(wl.T) if wl.ids[t] >= 0]
+    delta = O.forward_from_pool_rows(wl, pool, rows) - wl.y_in[rows].astype(np.float64)
+    for sl, (off, width) in enumerate(zip(offs, wl.out_features)):
+        Wb = W.draw_base_weight(9 + sl, width, wl.in_features, "bf16", integer_values=True)
+        for i, t in enumerate(rows):
+            Wm = O.merged_weight(Wb, pool[int(wl.ids[t])], sl, "bf16")
+            x = wl.x[t].astype(np.float64)
+            assert np.array_equal(Wm @ x, Wb.astype(np.float64) @ x + delta[i, off:off + width])
+
+
 # --- builder ----------------------------------------------------------------
 
 META_KEYS = ("sgmv_perm", "seg_starts", "seg_lens", "seg_ids", "bgmv_tok", "bgmv_ids")

@@ -278,3 +278,26 @@ def test_apply_ranked_validation_before_hip():
     assert _status(L.lora_apply_ranked, *with_(6, bad_ids)) == _lib.LORA_E_ID
     assert _status(L.lora_apply_ranked, *with_(11, ws_need - 1)) == _lib.LORA_E_WORKSPACE
     assert _status(L.lora_apply_ranked, *with_(5, 0)) == 0  # T = 0: no-op
+
+
+def test_merge_validation_before_hip():
+    """lora_merge_weights rejects bad slots, slices, ranks, alignment and
+    overlapping buffers on the host, before any GPU call."""
+    d = L.make_desc("bf16", 4, 16, 64, [64, 32])
+    nbytes = 64 * 64 * 2
+
+    def st(*a):
+        try:
+            L.lora_merge_weights(*a, stream=0)
+            return 0
+        except L.LoraError as e:
+            return e.status
+    assert st(d, FAKE, FAKE, 4, 0, FAKE, FAKE + nbytes) == _lib.LORA_E_ID
+    assert st(d, FAKE, FAKE, -1, 0, FAKE, FAKE + nbytes) == _lib.LORA_E_ID
+    assert st(d, FAKE, FAKE, 0, 2, FAKE, FAKE + nbytes) == _lib.LORA_E_ID
+    assert st(d, FAKE, FAKE, 0, 0, FAKE + 2, FAKE + nbytes) == _lib.LORA_E_ALIGN
+    assert st(d, FAKE, FAKE, 0, 0, FAKE, FAKE + 1024) == _lib.LORA_E_ARG   # partial overlap
+    assert st(d, None, FAKE, 0, 0, FAKE, FAKE) == _lib.LORA_E_ARG
+    big = L.make_desc("bf16", 2, 520, 64, [64])
+    assert st(big, FAKE, FAKE, 0, 0, FAKE, FAKE) == _lib.LORA_E_RANK
+    assert "max_lora_rank" in L.last_error()

@@ -115,6 +115,15 @@ MUTATIONS = {
     "pool_padding_not_zero": ("expected_pool", _pool_factory("no_padding_zero")),
     "pool_unfolded": ("expected_pool", _pool_factory("unfolded")),
     "bf16_truncation": ("f32_to_bf16_rne", _rne_trunc),
+    "bf16_double_rounding": ("f64_to_bf16_rne",
+                             lambda a: O.f32_to_bf16_rne(np.asarray(a, np.float32)).astype(np.float64)),
+    "merge_sign": ("merged_weight",
+                   lambda W, ps, sl, dt: np.asarray(W, np.float64) - ps["B"][sl] @ ps["A"][sl]),
+    "merge_wrong_slice": ("merged_weight",
+                          lambda W, ps, sl, dt: np.asarray(W, np.float64)
+                          + ps["B"][sl] @ ps["A"][(sl + 1) % len(ps["A"])]
+                          if ps["A"][(sl + 1) % len(ps["A"])].shape == ps["A"][sl].shape
+                          else np.asarray(W, np.float64)),
 }
 
 

@@ -289,3 +289,16 @@ NAMED = {
     "qkv_decode": config_qkv_decode,
     "mlp_mixed": config_mlp_mixed,
 }
+
+
+def draw_base_weight(seed: int, out_features: int, K: int, dtype: str = "bf16",
+                     integer_values: bool = False) -> np.ndarray:
+    """A base projection weight [out_features, K] for the merged-weight mode:
+    entries N(0, 1/K) (the usual scale of a linear layer's weight), or integers
+    in [-8, 8] for exact-arithmetic checks; rounded to the dtype."""
+    rng = np.random.default_rng(seed)
+    if integer_values:
+        w = rng.integers(-8, 9, size=(out_features, K)).astype(np.float64)
+    else:
+        w = rng.standard_normal(size=(out_features, K)) / np.sqrt(K)
+    return to_dtype_values(w, dtype)
