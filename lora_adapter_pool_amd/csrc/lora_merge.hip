@@ -65,6 +65,17 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t* __restr
   const int k0 = blockIdx.x * kTileK, o0 = blockIdx.y * kTileO;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  // 0. this thread's 4 chunks of 8 columns of the W tile, loaded first so the
+  //    reads are in flight during the staging and the products
+  constexpr int kChunks = kTileO * (kTileK / 8) / 256;
+  m_u32x4 wreg[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = tid + 256 * i, row = c >> 3, j = c & 7, o = o0 + row, k = k0 + 8 * j;
+    const bool ok = o < out_s && k < K;
+    wreg[i] = load16(W + (ok ? (size_t)o * K + k : 0)) & mask_of(ok);
+  }
+
   // 1. A[r][k0 .. k0 + 64) -> At[k][r]; ranks R .. 32 nrc and columns past K are 0
   for (int c = tid; c < 32 * nrc * (kTileK / 8); c += 256) {
     const int r = c >> 3, j = c & 7, k = k0 + 8 * j;
@@ -114,11 +125,12 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t* __restr
   __syncthreads();
 
   // 3. W + products, rounded once; 8 columns a lane, 8 lanes a 128-byte row
-  for (int c = tid; c < kTileO * (kTileK / 8); c += 256) {
-    const int row = c >> 3, j = c & 7, o = o0 + row, k = k0 + 8 * j;
+#pragma unroll
+  for (int ci = 0; ci < kChunks; ++ci) {
+    const int c = tid + 256 * ci, row = c >> 3, j = c & 7, o = o0 + row, k = k0 + 8 * j;
     if (o >= out_s || k >= K) continue;
     const size_t at = (size_t)o * K + k;
-    const m_u32x4 w = load16(W + at);
+    const m_u32x4 w = wreg[ci];
     const float* d = &Dt[row * kLdd + 8 * j];
     m_u32x4 out;
 #pragma unroll
