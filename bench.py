@@ -269,7 +269,7 @@ def ragged_decode_leg(seed, steps, stream_ptr, replica_bytes):
     return res
 
 
-def merge_leg(seed, stream_ptr):
+def merge_leg(seed, stream_ptr, cpu=True):
     """Merged-weight mode: lora_merge_weights on one projection's weight (rank
     64 pool), timed with HIP events over back-to-back launches, against the
     bytes it must move (W read and written, the slot's A and B read once); and
@@ -340,6 +340,22 @@ def merge_leg(seed, stream_ptr):
         torch.cuda.synchronize()
         out[label] = round((time.perf_counter() - t0) / 20 * 1e6, 1)
     res["single_adapter_prefill_us"] = dict(out, tokens=int(wl.T))
+    if cpu:
+        # the oracle's merge (fp64 product, one rounding) on a 1024-row sample
+        # of the 4096 x 4096 rank-64 case, scaled to the whole weight
+        import oracle
+        rng = np.random.default_rng(seed)
+        slot = {"A": [rng.standard_normal((64, 4096)) / 64.0],
+                "B": [rng.standard_normal((1024, 64)) * 0.02]}
+        Ws = W.draw_base_weight(seed, 1024, 4096, "bf16")
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.merged_weight(Ws, slot, 0, "bf16")
+            el = time.perf_counter() - t0
+        res["cpu_oracle"] = {"us_4096x4096": round(el * 4 * 1e6, 1), "kind": "oracle",
+                             "sample": "1024 of 4096 rows, scaled x4; one BLAS thread",
+                             "cores": 1}
     return res
 
 
@@ -770,7 +786,7 @@ def main():
         out["ragged_decode"] = ragged_decode_leg(args.seed, max(50, args.steps // 4), stream_ptr,
                                                  args.replica_mib * 2 ** 20)
         log(f"[bench] ragged decode: {out['ragged_decode']}")
-        out["merge"] = merge_leg(args.seed, stream_ptr)
+        out["merge"] = merge_leg(args.seed, stream_ptr, cpu=not args.no_cpu_baseline)
         log(f"[bench] merged weights: {out['merge']}")
         torch.cuda.empty_cache()
 
