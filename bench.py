@@ -421,9 +421,30 @@ def device_meta_leg(s, steps, stream_ptr):
         step(10 + i)
     torch.cuda.synchronize()
     step_us = (time.perf_counter() - t0) / steps * 1e6
+    # lora_apply_device: the same device metadata, then a device-built plan of
+    # 8-row tiles and the tile kernels (4 launches, no host work per batch)
+    nws = L.lora_apply_device_workspace_bytes(s.desc, T)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+    def plan_step(i):
+        r = i % s.nrep
+        if lib.lora_apply_device(d, s.pA[r], s.pB[r], s.px[r], s.py[r], T, ids_d.data_ptr(),
+                                 pre_d.data_ptr(), 0, ws.data_ptr(), nws, stream_ptr):
+            raise RuntimeError(f"lora_apply_device failed: {L.last_error()}")
+
+    for i in range(10):
+        plan_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        plan_step(10 + i)
+    torch.cuda.synchronize()
+    plan_us = (time.perf_counter() - t0) / steps * 1e6
     a = algorithmic(wl)
     return {"builder_us": round(builder_us, 2), "step_us": round(step_us, 2),
             "tokens_per_s": a["Ta"] / (step_us * 1e-6), "launches_per_step": 5,
+            "device_plan_step_us": round(plan_us, 2),
+            "device_plan_tokens_per_s": a["Ta"] / (plan_us * 1e-6),
             "counts": counts.cpu().tolist()[:3]}
 
 
@@ -779,7 +800,7 @@ def main():
     dm = device_meta_leg(setups[0], max(20, args.steps // 4), stream_ptr)
     out["device_meta"] = dict(dm, workload=setups[0].wl.name)
     log(f"[bench] device metadata: builder {dm['builder_us']:.2f} us, step {dm['step_us']:.2f} us "
-        f"(5 launches)")
+        f"(5 launches); device plan (lora_apply_device) {dm['device_plan_step_us']:.2f} us")
     del setups
     torch.cuda.empty_cache()
     if not args.no_secondary:

@@ -418,6 +418,27 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
                    const uint8_t* prefill_host, int32_t bgmv_max_rank, void* ws,
                    int64_t ws_bytes, void* meta_host, int64_t meta_host_bytes, void* stream);
 
+/* The whole delta path from device ids, with no host work that depends on
+ * the batch (so the calls can be captured in a graph and replayed with new ids
+ * and flags written into the same buffers): lora_build_meta_device's
+ * metadata ([TGI] step 4), then a device-built plan of 8-row tiles of one
+ * adapter, then the tile kernels' shrink and expand, all on `stream`.
+ *   ids, prefill  device arrays of T entries (prefill may be NULL = all 0);
+ *                 ids outside [-1, max_loras) are skipped like -1 (the host
+ *                 path rejects them instead)
+ *   ws            device workspace of lora_apply_device_workspace_bytes(desc,
+ *                 T) bytes, 256-byte aligned: metadata, the tile records, v
+ * The result is lora_apply's (within rounding: the K split may differ).
+ * Long prefill segments run on the 8-row tiles too, so lora_apply is faster
+ * for prefill batches.  Errors (before any HIP call): LORA_E_SHAPE if
+ * max_loras > LORA_META_DEVICE_MAX_LORAS, LORA_E_WORKSPACE, LORA_E_ALIGN,
+ * LORA_E_ARG; T = 0 is a no-op. */
+int64_t lora_apply_device_workspace_bytes(const lora_pool_desc* desc, int32_t T);
+int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
+                          const void* x, void* y, int32_t T, const int32_t* ids,
+                          const uint8_t* prefill, int32_t bgmv_max_rank, void* ws,
+                          int64_t ws_bytes, void* stream);
+
 /* lora_apply with each slot's true rank (slot_ranks as in
  * lora_apply_plan_ranked, nullable): same result, padded ranks skipped. */
 int32_t lora_apply_ranked(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,

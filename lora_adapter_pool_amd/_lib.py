@@ -111,6 +111,8 @@ _SIGNATURES = {
     "lora_plan_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, ctypes.POINTER(lora_plan), _P, _P, _P,
                                _I64, _P]),
     "lora_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P, _I64, _P]),
+    "lora_apply_device_workspace_bytes": (_I64, [_DP, _I32]),
+    "lora_apply_device": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P]),
     "lora_merge_weights": (_I32, [_DP, _P, _P, _I32, _I32, _P, _P, _P]),
     "lora_apply_ranked": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P, _I64,
                                  _P]),
@@ -393,3 +395,16 @@ def lora_merge_weights(desc, A_pool, B_pool, slot, slice_, W, W_out, stream=None
     device tensors of the pool dtype; W_out may be W)."""
     _check(lib().lora_merge_weights(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), int(slot),
                                     int(slice_), _ptr(W), _ptr(W_out), _stream(stream)))
+
+
+def lora_apply_device_workspace_bytes(desc, T: int) -> int:
+    return _check(lib().lora_apply_device_workspace_bytes(ctypes.byref(desc), int(T)))
+
+
+def lora_apply_device(desc, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank, ws, ws_bytes,
+                      stream=None) -> None:
+    """The delta path from device ids / prefill flags (device metadata and a
+    device-built tile plan; graph-capturable)."""
+    _check(lib().lora_apply_device(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), _ptr(x),
+                                   _ptr(y), int(T), _ptr(ids), _ptr(prefill), int(bgmv_max_rank),
+                                   _ptr(ws), int(ws_bytes), _stream(stream)))

@@ -363,6 +363,58 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
                            nullptr, ws, ws_bytes, meta_host, meta_host_bytes, stream);
 }
 
+int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
+                          const void* x, void* y, int32_t T, const int32_t* ids,
+                          const uint8_t* prefill, int32_t bgmv_max_rank, void* ws,
+                          int64_t ws_bytes, void* stream) {
+  clear_error();
+  Geo g;
+  if (int32_t e = check_desc(desc, &g)) return e;
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  if (g.max_loras > LORA_META_DEVICE_MAX_LORAS)
+    return fail(LORA_E_SHAPE, "max_loras must be <= %d for the device plan, got %d",
+                LORA_META_DEVICE_MAX_LORAS, g.max_loras);
+  if (T == 0) return LORA_OK;
+  if (int32_t e = need_ptr(A_pool, "A_pool")) return e;
+  if (int32_t e = need_ptr(B_pool, "B_pool")) return e;
+  if (int32_t e = need_ptr(x, "x")) return e;
+  if (int32_t e = need_ptr(y, "y")) return e;
+  if (int32_t e = need_ptr(ids, "ids")) return e;
+  if (int32_t e = need_ptr(ws, "ws")) return e;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(A_pool) || !aligned16(B_pool) ||
+      ((uintptr_t)ws & 255u))
+    return fail(LORA_E_ALIGN, "x, y and the pool must be 16-byte aligned, ws 256-byte aligned");
+  g.T = T;
+  const DeviceLayout d = device_layout(g, T);
+  if (ws_bytes < d.total)
+    return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
+                (long long)d.total);
+  char* w = (char*)ws;
+  lora_meta m;
+  m.num_sgmv_rows = m.num_segs = m.num_bgmv_rows = m.reserved = 0;
+  m.sgmv_perm = (int32_t*)(w + d.sgmv_perm);
+  m.bgmv_tok = (int32_t*)(w + d.bgmv_tok);
+  m.bgmv_ids = (int32_t*)(w + d.bgmv_ids);
+  m.seg_starts = (int32_t*)(w + d.seg_starts);
+  m.seg_lens = (int32_t*)(w + d.seg_lens);
+  m.seg_ids = (int32_t*)(w + d.seg_ids);
+  int32_t* counts = (int32_t*)(w + d.counts);
+  int32_t* tiles = (int32_t*)(w + d.tiles);
+  hipStream_t st = (hipStream_t)stream;
+  const int32_t limit = bgmv_max_rank > 0 ? bgmv_max_rank : LORA_BGMV_MAX_RANK_DEFAULT;
+  if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, g.R > limit, m, counts, st))
+    return e;
+  const int32_t cap = device_tile_cap(T, g.max_loras);
+  if (int32_t e = run_build_tiles(m, counts, g.max_loras, cap, tiles, st)) return e;
+  // the plan's shape is known on the host only as capacities: cap records
+  // (surplus ones have 0 rows), T v rows, wavefront tiles only
+  TilePlan tp{nullptr, tiles, cap, nullptr, 0, nullptr, 1, T, wave_ksplit(g, cap),
+              nullptr, nullptr, nullptr};
+  float* v = (float*)(w + d.v);
+  if (int32_t e = run_plan_shrink(g, x, A_pool, v, tp, st)) return e;
+  return run_plan_expand(g, v, B_pool, y, tp, st);
+}
+
 int32_t lora_apply_ranked(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
                           const void* x, void* y, int32_t T, const int32_t* ids_host,
                           const uint8_t* prefill_host, int32_t bgmv_max_rank,

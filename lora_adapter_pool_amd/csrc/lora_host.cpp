@@ -117,6 +117,31 @@ WorkspaceLayout workspace_layout(const Geo& g, int32_t T) {
   return w;
 }
 
+DeviceLayout device_layout(const Geo& g, int32_t T) {
+  DeviceLayout d;
+  const int64_t rows = T > 0 ? T : 1, ml = g.max_loras;
+  int64_t o = 0;
+  d.counts = o;
+  o = align_up(o + 4 * 4, 256);
+  d.sgmv_perm = o;
+  o = align_up(o + rows * 4, 16);
+  d.bgmv_tok = o;
+  o = align_up(o + rows * 4, 16);
+  d.bgmv_ids = o;
+  o = align_up(o + rows * 4, 16);
+  d.seg_starts = o;
+  o = align_up(o + ml * 4, 16);
+  d.seg_lens = o;
+  o = align_up(o + ml * 4, 16);
+  d.seg_ids = o;
+  o = align_up(o + ml * 4, 256);
+  d.tiles = o;
+  o = align_up(o + (int64_t)device_tile_cap(T, g.max_loras) * LORA_PLAN_WAVE_WORDS * 4, 256);
+  d.v = o;
+  d.total = o + (int64_t)LORA_PLAN_MAX_KSPLIT * rows * g.S * g.R * 4;
+  return d;
+}
+
 int32_t sgmv_mfma_min_rows() {
   static const int32_t v = env_rows("LORA_SGMV_MFMA_MIN_ROWS", 16);
   return v;
@@ -258,6 +283,23 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
 //   - wavefront tiles of LORA_PLAN_WAVE_ROWS rows: every other run.
 // v row numbering: SGMV rows first, then BGMV rows; perm holds the token of
 // every v row.
+int32_t wave_ksplit(const Geo& g, int64_t nw) {
+  int32_t ksplit_wave = 1;
+  if (g.dtype == LORA_BF16 && nw > 0 && g.R <= 64) {
+    const int64_t nk = (g.K + 31) / 32;
+    const int64_t batch = (int64_t)kTileShrinkWaves * tile_shrink_cb(g.R);
+    const int64_t wgs = nw * g.S;
+    while (ksplit_wave < tile_kparts_max(g.R) && wgs * ksplit_wave < 1024 &&
+           nk / (ksplit_wave + 1) >= batch)
+      ++ksplit_wave;
+    if (const char* e = std::getenv("LORA_WAVE_KSPLIT")) {  // tuning override
+      const long o = std::strtol(e, nullptr, 10);
+      if (o >= 1 && o <= tile_kparts_max(g.R)) ksplit_wave = (int32_t)o;
+    }
+  }
+  return ksplit_wave;
+}
+
 int32_t check_slot_ranks(const Geo& g, const int32_t* slot_ranks) {
   if (!slot_ranks) return LORA_OK;
   for (int32_t a = 0; a < g.max_loras; ++a) {
@@ -382,19 +424,7 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   // K split of the wavefront tiles' MFMA shrink (bf16, R <= 64): grow it while
   // the launch has fewer than four workgroups per compute unit and every part
   // keeps at least one full load batch for each of the workgroup's waves
-  int32_t ksplit_wave = 1;
-  if (bf && nw > 0 && g.R <= 64) {
-    const int64_t nk = (g.K + 31) / 32;
-    const int64_t batch = (int64_t)kTileShrinkWaves * tile_shrink_cb(g.R);
-    const int64_t wgs = nw * g.S;
-    while (ksplit_wave < tile_kparts_max(g.R) && wgs * ksplit_wave < 1024 &&
-           nk / (ksplit_wave + 1) >= batch)
-      ++ksplit_wave;
-    if (const char* e = std::getenv("LORA_WAVE_KSPLIT")) {  // tuning override
-      const long o = std::strtol(e, nullptr, 10);
-      if (o >= 1 && o <= tile_kparts_max(g.R)) ksplit_wave = (int32_t)o;
-    }
-  }
+  const int32_t ksplit_wave = wave_ksplit(g, nw);
   if (words > sl.image_max_words)  // cannot happen: the bounds above hold for any batch
     return fail(LORA_E_WORKSPACE, "tile plan overflow (%lld words > %lld)", (long long)words,
                 (long long)sl.image_max_words);
@@ -477,6 +507,18 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T) {
   if (st) return st;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
   return stage_layout(T, g.max_loras).total_words * 4;
+}
+
+int64_t lora_apply_device_workspace_bytes(const lora_pool_desc* desc, int32_t T) {
+  clear_error();
+  Geo g;
+  int32_t st = check_desc(desc, &g);
+  if (st) return st;
+  if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
+  if (g.max_loras > LORA_META_DEVICE_MAX_LORAS)
+    return fail(LORA_E_SHAPE, "max_loras must be <= %d for the device plan, got %d",
+                LORA_META_DEVICE_MAX_LORAS, g.max_loras);
+  return device_layout(g, T).total;
 }
 
 int64_t lora_apply_workspace_bytes(const lora_pool_desc* desc, int32_t T) {

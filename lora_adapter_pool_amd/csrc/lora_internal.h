@@ -71,6 +71,24 @@ constexpr int32_t kTileShrinkWaves = 4;  // waves per workgroup of that shrink
 // scalar registers).
 constexpr int32_t tile_kparts_max(int32_t R) { return R <= 16 ? LORA_PLAN_MAX_KSPLIT : 4; }
 
+// K split of the wavefront tiles' MFMA shrink for a plan of nw such tiles
+// (bf16, R <= 64; else 1): grown while the launch has fewer than four
+// workgroups per compute unit and every part keeps one full load batch for
+// each of the workgroup's waves.
+int32_t wave_ksplit(const Geo& g, int64_t nw);
+
+// Device-built plan of lora_apply_device: capacity of its 8-row tile records
+// (each slot adds at most one partial tile to each of its two row sets) and
+// its workspace (byte offsets): the metadata arrays, the records, then v
+// (LORA_PLAN_MAX_KSPLIT partials of T rows x S x R fp32).
+inline int32_t device_tile_cap(int32_t T, int32_t max_loras) {
+  return (T + LORA_PLAN_WAVE_ROWS - 1) / LORA_PLAN_WAVE_ROWS + 2 * (T < max_loras ? T : max_loras);
+}
+struct DeviceLayout {
+  int64_t counts, sgmv_perm, bgmv_tok, bgmv_ids, seg_starts, seg_lens, seg_ids, tiles, v, total;
+};
+DeviceLayout device_layout(const Geo& g, int32_t T);
+
 // Builder core (no argument checks beyond what lora_build_meta does).
 int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
                         int32_t max_loras, int32_t max_lora_rank, int32_t bgmv_max_rank,

@@ -187,4 +187,124 @@ int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_
   return LORA_OK;
 }
 
+// Tile records of a device-built plan: lora_build_meta_device's arrays cut
+// into 8-row tiles of one adapter (the host plan's wavefront records: slot,
+// rows, first v row, 0, tokens, -1 past the last row; v rows are the SGMV rows,
+// then the BGMV rows).  The sort by adapter leaves each slot at most one SGMV
+// segment and one run of BGMV rows, so a slot's tiles follow from its two row
+// counts: a histogram of the BGMV ids, exclusive scans of the counts and of
+// the tiles per slot, then one thread per record finds its slot by binary
+// search.  Records from the last tile up to the capacity get 0 rows (the
+// kernels skip them), so the launches can take the capacity as their grid.
+__global__ __launch_bounds__(kMetaThreads) void build_tiles_kernel(
+    lora_meta m, const int32_t* __restrict__ counts, int32_t max_loras, int32_t cap,
+    int32_t* __restrict__ tiles) {
+  // [max_loras] first SGMV row, [max_loras] SGMV rows, [max_loras + 1] first
+  // BGMV row, [max_loras + 1] first tile, of each slot
+  extern __shared__ int32_t lds[];
+  __shared__ int32_t s_pt[kMetaThreads];
+  __shared__ int32_t s_pb[kMetaThreads];
+  int32_t* ss = lds;
+  int32_t* cs = lds + max_loras;
+  int32_t* bs = lds + 2 * max_loras;
+  int32_t* toff = lds + 3 * max_loras + 1;
+  const int tid = threadIdx.x;
+  const int ns = counts[0], nsegs = counts[1], nb = counts[2];
+  for (int a = tid; a < max_loras; a += kMetaThreads) {
+    ss[a] = 0;
+    cs[a] = 0;
+    bs[a] = 0;  // BGMV rows of slot a until the scan
+  }
+  __syncthreads();
+  for (int j = tid; j < nsegs; j += kMetaThreads) {
+    const int a = m.seg_ids[j];
+    if (a >= 0 && a < max_loras) {
+      ss[a] = m.seg_starts[j];
+      cs[a] = m.seg_lens[j];
+    }
+  }
+  for (int i = tid; i < nb; i += kMetaThreads) {
+    const int a = m.bgmv_ids[i];
+    if (a >= 0 && a < max_loras) atomicAdd(&bs[a], 1);
+  }
+  __syncthreads();
+
+  // exclusive scans of the tiles and of the BGMV rows per slot; thread tid
+  // owns slots [a0, a1)
+  const int per = (max_loras + kMetaThreads - 1) / kMetaThreads;
+  const int a0 = min(max_loras, tid * per), a1 = min(max_loras, a0 + per);
+  int st = 0, sb = 0;
+  for (int a = a0; a < a1; ++a) {
+    st += (cs[a] + 7) / 8 + (bs[a] + 7) / 8;
+    sb += bs[a];
+  }
+  s_pt[tid] = st;
+  s_pb[tid] = sb;
+  __syncthreads();
+  for (int d = 1; d < kMetaThreads; d <<= 1) {
+    const int vt = tid >= d ? s_pt[tid - d] : 0;
+    const int vb = tid >= d ? s_pb[tid - d] : 0;
+    __syncthreads();
+    s_pt[tid] += vt;
+    s_pb[tid] += vb;
+    __syncthreads();
+  }
+  int bt = s_pt[tid] - st, bb = s_pb[tid] - sb;
+  for (int a = a0; a < a1; ++a) {
+    const int nba = bs[a];
+    toff[a] = bt;
+    bs[a] = bb;
+    bt += (cs[a] + 7) / 8 + (nba + 7) / 8;
+    bb += nba;
+  }
+  if (tid == kMetaThreads - 1) {
+    toff[max_loras] = s_pt[tid];
+    bs[max_loras] = s_pb[tid];
+  }
+  __syncthreads();
+
+  const int ntiles = toff[max_loras];
+  for (int f = tid; f < cap; f += kMetaThreads) {
+    int32_t* r = tiles + (size_t)f * LORA_PLAN_WAVE_WORDS;
+    int slot = 0, rows = 0, vrow = 0;
+    const int32_t* src = nullptr;
+    if (f < ntiles) {
+      // the last slot whose first tile is at or before f owns it (empty slots
+      // before it have smaller indices)
+      int lo = 0, hi = max_loras - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (toff[mid] <= f) lo = mid; else hi = mid - 1;
+      }
+      slot = lo;
+      const int lt = f - toff[slot], tsg = (cs[slot] + 7) / 8;
+      if (lt < tsg) {
+        rows = min(LORA_PLAN_WAVE_ROWS, cs[slot] - LORA_PLAN_WAVE_ROWS * lt);
+        vrow = ss[slot] + LORA_PLAN_WAVE_ROWS * lt;
+        src = m.sgmv_perm + vrow;
+      } else {
+        const int lb = lt - tsg, first = bs[slot] + LORA_PLAN_WAVE_ROWS * lb;
+        rows = min(LORA_PLAN_WAVE_ROWS, bs[slot + 1] - first);
+        vrow = ns + first;
+        src = m.bgmv_tok + first;
+      }
+    }
+    r[0] = slot;
+    r[1] = rows;
+    r[2] = vrow;
+    r[3] = 0;
+    for (int i = 0; i < LORA_PLAN_WAVE_WORDS - 4; ++i) r[4 + i] = i < rows ? src[i] : -1;
+  }
+}
+
+int32_t run_build_tiles(const lora_meta& m, const int32_t* counts, int32_t max_loras,
+                        int32_t cap, int32_t* tiles, hipStream_t st) {
+  const size_t lds = (size_t)(4 * max_loras + 2) * sizeof(int32_t);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kMetaThreads), lds, st, m, counts,
+                     max_loras, cap, tiles);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(LORA_E_HIP, "build_tiles launch: %s", hipGetErrorString(e));
+  return LORA_OK;
+}
+
 }  // namespace lora

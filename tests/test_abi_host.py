@@ -301,3 +301,45 @@ def test_merge_validation_before_hip():
     big = L.make_desc("bf16", 2, 520, 64, [64])
     assert st(big, FAKE, FAKE, 0, 0, FAKE, FAKE) == _lib.LORA_E_RANK
     assert "max_lora_rank" in L.last_error()
+
+
+def test_apply_device_validation_before_hip():
+    """lora_apply_device: workspace size and every argument check on the host,
+    before any GPU call."""
+    d = L.make_desc("bf16", 6, 16, 256, [256, 128])
+    T = 100
+    need = L.lora_apply_device_workspace_bytes(d, T)
+    cap = -(-T // 8) + 2 * min(6, T)
+    up = lambda n, a: (n + a - 1) // a * a  # noqa: E731
+    meta = up(16, 256)
+    meta = up(meta + 4 * T, 16)
+    meta = up(meta + 4 * T, 16)
+    meta = up(meta + 4 * T, 16)
+    meta = up(meta + 4 * 6, 16)
+    meta = up(meta + 4 * 6, 16)
+    meta = up(meta + 4 * 6, 256)
+    tiles = up(meta + cap * 16 * 4, 256)
+    assert need == tiles + 8 * T * 2 * 16 * 4  # v: up to 8 partials of T x S x R fp32
+    ok = [d, FAKE, FAKE, FAKE, FAKE + 4096, T, FAKE, None, 0, FAKE, need]
+
+    def with_(i, v):
+        a = list(ok)
+        a[i] = v
+        return a
+
+    def st(*a):
+        try:
+            L.lora_apply_device(*a, stream=0)
+            return 0
+        except L.LoraError as e:
+            return e.status
+    assert st(*with_(10, need - 1)) == _lib.LORA_E_WORKSPACE
+    assert st(*with_(9, FAKE + 16)) == _lib.LORA_E_ALIGN      # ws must be 256-byte aligned
+    assert st(*with_(3, FAKE + 2)) == _lib.LORA_E_ALIGN
+    assert st(*with_(6, None)) == _lib.LORA_E_ARG
+    assert st(*with_(5, -1)) == _lib.LORA_E_ARG
+    assert st(*with_(5, 0)) == 0                               # T = 0: no-op
+    big = L.make_desc("bf16", 8193, 16, 256, [256])
+    assert st(*([big] + ok[1:])) == _lib.LORA_E_SHAPE
+    with pytest.raises(L.LoraError):
+        L.lora_apply_device_workspace_bytes(big, 10)

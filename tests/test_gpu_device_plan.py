@@ -1,0 +1,145 @@
+"""lora_apply_device: the delta path from device ids, through the device
+metadata builder, a device-built plan of 8-row tiles and the tile kernels,
+against the fp64 oracle (named workloads, exact integer inputs, fp32 pools,
+pool ranks above 64 and above the BGMV limit, ids outside the slot range,
+a workspace reused by batches of different sizes), and captured in a graph
+replayed with new ids."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import lora_adapter_pool_amd as L
+import oracle
+import workloads as W
+from gpu_helpers import check_rows, make_pool, sample_rows, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"[gpu] {request.node.name}")
+    yield
+
+
+def _ws(pool, T):
+    import torch
+    n = L.lora_apply_device_workspace_bytes(pool.desc, T)
+    return torch.empty(n, dtype=torch.uint8, device="cuda"), n
+
+
+def _run(wl, pool=None, ids=None, prefill=None, ws=None, bgmv_max_rank=0):
+    import torch
+    pool = pool or make_pool(wl)
+    ids = wl.ids if ids is None else ids
+    prefill = wl.prefill if prefill is None else prefill
+    xd, yd = to_dev(wl.x, wl.dtype), to_dev(wl.y_in, wl.dtype)
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    pre_d = torch.from_numpy(np.ascontiguousarray(prefill, dtype=np.uint8)).cuda()
+    buf, n = ws if ws is not None else _ws(pool, wl.T)
+    L.lora_apply_device(pool.desc, pool.A, pool.B, xd, yd, wl.T, ids_d, pre_d, bgmv_max_rank,
+                        buf, n)
+    torch.cuda.synchronize()
+    return yd
+
+
+def test_device_plan_bgmv_decode_full():
+    wl = W.config_bgmv_decode(seed=0)
+    check_rows(wl, _run(wl), label="bgmv decode, device plan")
+
+
+def test_device_plan_qkv_decode_full():
+    wl = W.config_qkv_decode(seed=0)
+    check_rows(wl, _run(wl), label="fused qkv decode, device plan")
+
+
+def test_device_plan_prefill_sampled():
+    wl = W.config_sgmv_prefill(seed=0)
+    check_rows(wl, _run(wl), rows=sample_rows(wl, 64), label="sgmv prefill, device plan")
+
+
+def test_device_plan_mixed_small():
+    gu, dn = W.config_mlp_mixed(seed=1, n_prefill=3, len_lo=5, len_hi=70, n_decode=37,
+                                hidden=264, inter=520, n_adapters=8)
+    for wl in (gu, dn):
+        check_rows(wl, _run(wl), label=f"{wl.name}, device plan")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_device_plan_exact_integer(dtype):
+    wl = W.config_integer(seed=21, T=300, K=520, outs=(264, 136), max_loras=6,
+                          max_lora_rank=64, dtype=dtype)
+    exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(wl), dtype)
+    bad = np.argwhere(_run(wl).float().cpu().numpy() != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
+@pytest.mark.parametrize("R", [80, 128])
+def test_device_plan_large_ranks(R):
+    # 80: the VALU kernels (R > 64); 128: above the BGMV limit, every row SGMV
+    wl = W.config_mlp_mixed(seed=2, n_prefill=2, len_lo=20, len_hi=60, n_decode=11, hidden=136,
+                            inter=264, n_adapters=4, rank_choices=(8, 16), max_lora_rank=R)[0]
+    check_rows(wl, _run(wl), label=f"device plan R={R}")
+
+
+def test_device_plan_skips_out_of_range_ids():
+    wl = W.config_integer(seed=22, T=120, K=264, outs=(136,), max_loras=4, max_lora_rank=16,
+                          ranks=(16, 8, 16, 8), dtype="bf16")
+    ids = wl.ids.copy()
+    ids[::7] = 9      # outside [-1, max_loras): skipped like -1
+    ids[3::11] = -5
+    y = _run(wl, ids=ids)
+    case = dataclasses.replace(wl, ids=np.where((ids < -1) | (ids >= 4), -1, ids).astype(np.int32))
+    exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(case), "bf16")
+    assert np.array_equal(y.float().cpu().numpy(), exp)
+
+
+def test_device_plan_workspace_reused_across_batches():
+    """A large batch then a small one on the same workspace: the small batch's
+    plan must not pick up the large batch's tile records."""
+    big = W.config_integer(seed=23, T=400, K=264, outs=(136,), max_loras=6, max_lora_rank=16,
+                           ranks=(16, 8, 16, 8, 16, 8), dtype="bf16")
+    pool = make_pool(big)
+    ws = _ws(pool, big.T)
+    for T in (400, 37, 5, 400):
+        wl = W.config_integer(seed=23 + T, T=T, K=264, outs=(136,), max_loras=6,
+                              max_lora_rank=16, ranks=(16, 8, 16, 8, 16, 8), dtype="bf16")
+        wl = dataclasses.replace(wl, slots=big.slots)
+        exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(wl), "bf16")
+        y = _run(wl, pool=pool, ws=ws)
+        bad = np.argwhere(y.float().cpu().numpy() != exp)
+        assert bad.size == 0, f"T={T}: {len(bad)} mismatches"
+
+
+def test_device_plan_graph_replays():
+    """lora_apply_device captured in one graph; new ids and prefill flags are
+    written into its input buffers between replays; every replay is exact."""
+    import torch
+    wl = W.config_integer(seed=24, T=200, K=520, outs=(264, 136), max_loras=6, max_lora_rank=16,
+                          ranks=(16, 8), dtype="bf16")
+    pool = make_pool(wl)
+    buf, n = _ws(pool, wl.T)
+    xd = to_dev(wl.x, wl.dtype)
+    y0 = to_dev(wl.y_in, wl.dtype)
+    yd = y0.clone()
+    ids_d = torch.zeros(wl.T, dtype=torch.int32, device="cuda")
+    pre_d = torch.zeros(wl.T, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.lora_apply_device(pool.desc, pool.A, pool.B, xd, yd, wl.T, ids_d, pre_d, 0, buf, n)
+    rng = np.random.default_rng(6)
+    for rep in range(4):
+        ids = rng.integers(-1, 6, size=wl.T).astype(np.int32)
+        pre = (rng.random(wl.T) < [0.0, 0.5, 1.0, 0.2][rep]).astype(np.uint8)
+        ids_d.copy_(torch.from_numpy(ids))
+        pre_d.copy_(torch.from_numpy(pre))
+        yd.copy_(y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        case = dataclasses.replace(wl, ids=ids, prefill=pre)
+        exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(case), wl.dtype)
+        bad = np.argwhere(yd.float().cpu().numpy() != exp)
+        assert bad.size == 0, f"replay {rep}: {len(bad)} mismatches, first {bad[:3]}"
