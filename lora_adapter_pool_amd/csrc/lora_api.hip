@@ -402,10 +402,10 @@ int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const 
   int32_t* tiles = (int32_t*)(w + d.tiles);
   hipStream_t st = (hipStream_t)stream;
   const int32_t limit = bgmv_max_rank > 0 ? bgmv_max_rank : LORA_BGMV_MAX_RANK_DEFAULT;
-  if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, g.R > limit, m, counts, st))
-    return e;
   const int32_t cap = device_tile_cap(T, g.max_loras);
-  if (int32_t e = run_build_tiles(m, counts, g.max_loras, cap, tiles, st)) return e;
+  if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, g.R > limit, m, counts, st,
+                                        tiles, cap))
+    return e;
   // the plan's shape is known on the host only as capacities: cap records
   // (surplus ones have 0 rows), T v rows, wavefront tiles only
   TilePlan tp{nullptr, tiles, cap, nullptr, 0, nullptr, 1, T, wave_ksplit(g, cap),

@@ -109,15 +109,12 @@ int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B
                        const TilePlan& p, float* v, hipStream_t st);
 // Device-side builder (csrc/lora_meta.hip): lora_build_meta's arrays from
 // device ids, one workgroup on `st`; counts[4] = rows, segments, BGMV rows,
-// rejected ids.
+// rejected ids.  With `tiles`, the same launch then writes cap 8-row tile
+// records of a device-built plan (records past the last tile have 0 rows).
 int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
                               int32_t max_loras, bool all_sgmv, const lora_meta& m,
-                              int32_t* counts, hipStream_t st);
-// Device-built tile plan (csrc/lora_meta.hip): cap 8-row tile records from
-// run_build_meta_device's arrays and counts, one workgroup on `st`; records
-// past the last tile have 0 rows.
-int32_t run_build_tiles(const lora_meta& m, const int32_t* counts, int32_t max_loras,
-                        int32_t cap, int32_t* tiles, hipStream_t st);
+                              int32_t* counts, hipStream_t st, int32_t* tiles = nullptr,
+                              int32_t cap = 0);
 int32_t run_pool_load(const Geo& g, void* A_slot_slice, void* B_slot_slice, const void* Asrc,
                       const void* Bsrc, int r, int out_s, float scale, hipStream_t st);
 

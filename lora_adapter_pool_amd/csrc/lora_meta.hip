@@ -26,7 +26,7 @@ constexpr int kMetaThreads = 1024;
 __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ prefill, int32_t T,
     int32_t max_loras, int32_t all_sgmv, lora_meta m, int32_t* __restrict__ counts,
-    int32_t kcap) {
+    int32_t kcap, int32_t* __restrict__ tiles, int32_t cap) {
   // [max_loras] SGMV bins, [max_loras] BGMV bins, then the keys of a block of
   // kcap rows (int16: 2 id + set, or -1)
   extern __shared__ int32_t lds[];
@@ -170,121 +170,67 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       if (first) *pos = p0 + cnt;
     }
   }
-}
+  if (tiles == nullptr) return;
 
-int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
-                              int32_t max_loras, bool all_sgmv, const lora_meta& m,
-                              int32_t* counts, hipStream_t st) {
-  // LDS: the bins, then up to 128 KB in all with the keys of a block of rows
-  const int64_t bins = (int64_t)2 * max_loras * sizeof(int32_t);
-  int64_t kcap = ((int64_t)128 * 1024 - bins) / (int64_t)sizeof(int16_t) / 64 * 64;
-  kcap = std::max<int64_t>(64, std::min<int64_t>(kcap, ((int64_t)T + 63) / 64 * 64));
-  hipLaunchKernelGGL(build_meta_kernel, dim3(1), dim3(kMetaThreads),
-                     (size_t)(bins + kcap * (int64_t)sizeof(int16_t)), st, ids, prefill, T,
-                     max_loras, all_sgmv ? 1 : 0, m, counts, (int32_t)kcap);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(LORA_E_HIP, "build_meta launch: %s", hipGetErrorString(e));
-  return LORA_OK;
-}
-
-// Tile records of a device-built plan: lora_build_meta_device's arrays cut
-// into 8-row tiles of one adapter (the host plan's wavefront records: slot,
-// rows, first v row, 0, tokens, -1 past the last row; v rows are the SGMV rows,
-// then the BGMV rows).  The sort by adapter leaves each slot at most one SGMV
-// segment and one run of BGMV rows, so a slot's tiles follow from its two row
-// counts: a histogram of the BGMV ids, exclusive scans of the counts and of
-// the tiles per slot, then one thread per record finds its slot by binary
-// search.  Records from the last tile up to the capacity get 0 rows (the
-// kernels skip them), so the launches can take the capacity as their grid.
-__global__ __launch_bounds__(kMetaThreads) void build_tiles_kernel(
-    lora_meta m, const int32_t* __restrict__ counts, int32_t max_loras, int32_t cap,
-    int32_t* __restrict__ tiles) {
-  // [max_loras] first SGMV row, [max_loras] SGMV rows, [max_loras + 1] first
-  // BGMV row, [max_loras + 1] first tile, of each slot
-  extern __shared__ int32_t lds[];
-  __shared__ int32_t s_pt[kMetaThreads];
-  __shared__ int32_t s_pb[kMetaThreads];
-  int32_t* ss = lds;
-  int32_t* cs = lds + max_loras;
-  int32_t* bs = lds + 2 * max_loras;
-  int32_t* toff = lds + 3 * max_loras + 1;
-  const int tid = threadIdx.x;
-  const int ns = counts[0], nsegs = counts[1], nb = counts[2];
-  for (int a = tid; a < max_loras; a += kMetaThreads) {
-    ss[a] = 0;
-    cs[a] = 0;
-    bs[a] = 0;  // BGMV rows of slot a until the scan
-  }
-  __syncthreads();
-  for (int j = tid; j < nsegs; j += kMetaThreads) {
-    const int a = m.seg_ids[j];
-    if (a >= 0 && a < max_loras) {
-      ss[a] = m.seg_starts[j];
-      cs[a] = m.seg_lens[j];
-    }
-  }
-  for (int i = tid; i < nb; i += kMetaThreads) {
-    const int a = m.bgmv_ids[i];
-    if (a >= 0 && a < max_loras) atomicAdd(&bs[a], 1);
-  }
-  __syncthreads();
-
-  // exclusive scans of the tiles and of the BGMV rows per slot; thread tid
-  // owns slots [a0, a1)
-  const int per = (max_loras + kMetaThreads - 1) / kMetaThreads;
-  const int a0 = min(max_loras, tid * per), a1 = min(max_loras, a0 + per);
-  int st = 0, sb = 0;
+  // 4. tile records of a device-built plan (lora_apply_device): the rows cut
+  // into 8-row tiles of one adapter, records as the host plan's wavefront
+  // records (slot, rows, first v row, 0, tokens, -1 past the last row; v rows
+  // are the SGMV rows, then the BGMV rows).  After placement each bin holds
+  // its slot's end position, and slots are laid out back to back, so a slot's
+  // rows run from the previous slot's end to its own.  An exclusive scan of
+  // the tiles per slot gives each slot's first record, and one thread per
+  // record finds its slot by binary search.  Records from the last tile up to
+  // cap get 0 rows (the kernels skip them), so launches can take cap as grid.
+  __syncthreads();  // placement (wavefront 0) is complete
+  int32_t* toff = lds + 2 * max_loras + kcap / 2;  // [max_loras + 1], after the keys
+  int nt = 0;
   for (int a = a0; a < a1; ++a) {
-    st += (cs[a] + 7) / 8 + (bs[a] + 7) / 8;
-    sb += bs[a];
+    const int sc = cs[a] - (a > 0 ? cs[a - 1] : 0), bc = cb[a] - (a > 0 ? cb[a - 1] : 0);
+    nt += (sc + 7) / 8 + (bc + 7) / 8;
   }
-  s_pt[tid] = st;
-  s_pb[tid] = sb;
+  int inct = nt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inct, o, 64);
+    if (lane >= o) inct += u;
+  }
+  if (lane == 63) s_wsum[wave][0] = inct;
   __syncthreads();
-  for (int d = 1; d < kMetaThreads; d <<= 1) {
-    const int vt = tid >= d ? s_pt[tid - d] : 0;
-    const int vb = tid >= d ? s_pb[tid - d] : 0;
-    __syncthreads();
-    s_pt[tid] += vt;
-    s_pb[tid] += vb;
-    __syncthreads();
+  int tb = 0, ttot = 0;
+  for (int w = 0; w < nw; ++w) {
+    tb += w < wave ? s_wsum[w][0] : 0;
+    ttot += s_wsum[w][0];
   }
-  int bt = s_pt[tid] - st, bb = s_pb[tid] - sb;
+  tb += inct - nt;
   for (int a = a0; a < a1; ++a) {
-    const int nba = bs[a];
-    toff[a] = bt;
-    bs[a] = bb;
-    bt += (cs[a] + 7) / 8 + (nba + 7) / 8;
-    bb += nba;
+    const int sc = cs[a] - (a > 0 ? cs[a - 1] : 0), bc = cb[a] - (a > 0 ? cb[a - 1] : 0);
+    toff[a] = tb;
+    tb += (sc + 7) / 8 + (bc + 7) / 8;
   }
-  if (tid == kMetaThreads - 1) {
-    toff[max_loras] = s_pt[tid];
-    bs[max_loras] = s_pb[tid];
-  }
+  if (tid == 0) toff[max_loras] = ttot;
   __syncthreads();
-
-  const int ntiles = toff[max_loras];
   for (int f = tid; f < cap; f += kMetaThreads) {
     int32_t* r = tiles + (size_t)f * LORA_PLAN_WAVE_WORDS;
     int slot = 0, rows = 0, vrow = 0;
     const int32_t* src = nullptr;
-    if (f < ntiles) {
-      // the last slot whose first tile is at or before f owns it (empty slots
-      // before it have smaller indices)
+    if (f < ttot) {
+      // the last slot whose first record is at or before f owns it (empty
+      // slots before it have smaller indices)
       int lo = 0, hi = max_loras - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (toff[mid] <= f) lo = mid; else hi = mid - 1;
       }
       slot = lo;
-      const int lt = f - toff[slot], tsg = (cs[slot] + 7) / 8;
+      const int s0 = slot > 0 ? cs[slot - 1] : 0, b0 = slot > 0 ? cb[slot - 1] : 0;
+      const int lt = f - toff[slot], tsg = (cs[slot] - s0 + 7) / 8;
       if (lt < tsg) {
-        rows = min(LORA_PLAN_WAVE_ROWS, cs[slot] - LORA_PLAN_WAVE_ROWS * lt);
-        vrow = ss[slot] + LORA_PLAN_WAVE_ROWS * lt;
+        vrow = s0 + LORA_PLAN_WAVE_ROWS * lt;
+        rows = min(LORA_PLAN_WAVE_ROWS, cs[slot] - vrow);
         src = m.sgmv_perm + vrow;
       } else {
-        const int lb = lt - tsg, first = bs[slot] + LORA_PLAN_WAVE_ROWS * lb;
-        rows = min(LORA_PLAN_WAVE_ROWS, bs[slot + 1] - first);
+        const int first = b0 + LORA_PLAN_WAVE_ROWS * (lt - tsg);
+        rows = min(LORA_PLAN_WAVE_ROWS, cb[slot] - first);
         vrow = ns + first;
         src = m.bgmv_tok + first;
       }
@@ -297,13 +243,21 @@ __global__ __launch_bounds__(kMetaThreads) void build_tiles_kernel(
   }
 }
 
-int32_t run_build_tiles(const lora_meta& m, const int32_t* counts, int32_t max_loras,
-                        int32_t cap, int32_t* tiles, hipStream_t st) {
-  const size_t lds = (size_t)(4 * max_loras + 2) * sizeof(int32_t);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kMetaThreads), lds, st, m, counts,
-                     max_loras, cap, tiles);
+int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
+                              int32_t max_loras, bool all_sgmv, const lora_meta& m,
+                              int32_t* counts, hipStream_t st, int32_t* tiles, int32_t cap) {
+  // LDS: the bins, the keys of a block of rows, then (with tiles) each slot's
+  // first record; up to 128 KB in all
+  const int64_t bins = (int64_t)2 * max_loras * sizeof(int32_t);
+  const int64_t toff = tiles ? (int64_t)(max_loras + 1) * sizeof(int32_t) : 0;
+  int64_t kcap = ((int64_t)128 * 1024 - bins - toff) / (int64_t)sizeof(int16_t) / 64 * 64;
+  kcap = std::max<int64_t>(64, std::min<int64_t>(kcap, ((int64_t)T + 63) / 64 * 64));
+  hipLaunchKernelGGL(build_meta_kernel, dim3(1), dim3(kMetaThreads),
+                     (size_t)(bins + kcap * (int64_t)sizeof(int16_t) + toff), st, ids, prefill,
+                     T, max_loras, all_sgmv ? 1 : 0, m, counts, (int32_t)kcap, tiles,
+                     tiles ? cap : 0);
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(LORA_E_HIP, "build_tiles launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(LORA_E_HIP, "build_meta launch: %s", hipGetErrorString(e));
   return LORA_OK;
 }
 
