@@ -410,6 +410,7 @@ int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const 
   // (surplus ones have 0 rows), T v rows, wavefront tiles only
   TilePlan tp{nullptr, tiles, cap, nullptr, 0, nullptr, 1, T, wave_ksplit(g, cap),
               nullptr, nullptr, nullptr};
+  if (device_plan_is_onepass(g, cap)) return run_plan_onepass_list(g, x, A_pool, B_pool, y, tp, st);
   float* v = (float*)(w + d.v);
   if (int32_t e = run_plan_shrink(g, x, A_pool, v, tp, st)) return e;
   return run_plan_expand(g, v, B_pool, y, tp, st);

@@ -105,6 +105,13 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
 // kArgTilesS tiles with R <= 32, else run_plan_shrink then run_plan_expand
 // (v: the plan's rows).
 bool plan_is_onepass(const Geo& g, const TilePlan& p);
+// A device-built plan of at most kDeviceOnepassCap records (bf16, R <= 32)
+// runs as that one launch too, reading its records from device memory
+// (records with 0 rows exit at once).
+constexpr int32_t kDeviceOnepassCap = 24;
+bool device_plan_is_onepass(const Geo& g, int32_t cap);
+int32_t run_plan_onepass_list(const Geo& g, const void* x, const void* A, const void* B, void* y,
+                              const TilePlan& p, hipStream_t st);
 int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
                        const TilePlan& p, float* v, hipStream_t st);
 // Device-side builder (csrc/lora_meta.hip): lora_build_meta's arrays from

@@ -2053,6 +2053,18 @@ static PlanArg<kArgC> pack_arg_compact(const TilePlan& p) {
   return a;
 }
 
+bool device_plan_is_onepass(const Geo& g, int32_t cap) {
+  return onepass_enabled() && g.dtype == LORA_BF16 && g.R <= 32 && cap > 0 &&
+         cap <= kDeviceOnepassCap;
+}
+
+int32_t run_plan_onepass_list(const Geo& g, const void* x, const void* A, const void* B, void* y,
+                              const TilePlan& p, hipStream_t st) {
+  RowList Lw, Lm;
+  plan_lists(p, Lw, Lm);
+  return launch_onepass<kList>(g, x, A, B, y, Lw, p.wave_tiles, st, PlanArg<kList>{});
+}
+
 int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
                        const TilePlan& p, float* v, hipStream_t st) {
   if (!plan_is_onepass(g, p)) {

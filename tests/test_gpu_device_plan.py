@@ -143,3 +143,47 @@ def test_device_plan_graph_replays():
         exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(case), wl.dtype)
         bad = np.argwhere(yd.float().cpu().numpy() != exp)
         assert bad.size == 0, f"replay {rep}: {len(bad)} mismatches, first {bad[:3]}"
+
+
+@pytest.mark.parametrize("R,T,n", [(16, 40, 4), (32, 64, 4), (16, 9, 8), (32, 1, 3)])
+def test_device_plan_one_launch_exact(R, T, n):
+    """Small bf16 plans (at most 24 records, R <= 32) run as the one-launch
+    decode kernel reading the device-built records: exact on integer inputs."""
+    ranks = tuple(8 if a % 2 else R for a in range(n))
+    wl = W.config_integer(seed=40 + R + T, T=T, K=1032, outs=(520, 264), max_loras=n,
+                          max_lora_rank=R, ranks=ranks, dtype="bf16")
+    assert -(-T // 8) + 2 * min(n, T) <= 24
+    exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(wl), "bf16")
+    bad = np.argwhere(_run(wl).float().cpu().numpy() != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
+def test_device_plan_one_launch_graph_replays():
+    import torch
+    wl = W.config_integer(seed=25, T=48, K=520, outs=(264, 136), max_loras=4, max_lora_rank=16,
+                          ranks=(16, 8, 16, 8), dtype="bf16")
+    pool = make_pool(wl)
+    buf, n = _ws(pool, wl.T)
+    xd = to_dev(wl.x, wl.dtype)
+    y0 = to_dev(wl.y_in, wl.dtype)
+    yd = y0.clone()
+    ids_d = torch.zeros(wl.T, dtype=torch.int32, device="cuda")
+    pre_d = torch.zeros(wl.T, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.lora_apply_device(pool.desc, pool.A, pool.B, xd, yd, wl.T, ids_d, pre_d, 0, buf, n)
+    rng = np.random.default_rng(7)
+    for rep in range(4):
+        ids = rng.integers(-1, 4, size=wl.T).astype(np.int32)
+        pre = (rng.random(wl.T) < [0.0, 0.5, 1.0, 0.2][rep]).astype(np.uint8)
+        ids_d.copy_(torch.from_numpy(ids))
+        pre_d.copy_(torch.from_numpy(pre))
+        yd.copy_(y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        case = dataclasses.replace(wl, ids=ids, prefill=pre)
+        exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(case), wl.dtype)
+        bad = np.argwhere(yd.float().cpu().numpy() != exp)
+        assert bad.size == 0, f"replay {rep}: {len(bad)} mismatches, first {bad[:3]}"
