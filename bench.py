@@ -448,6 +448,34 @@ def device_meta_leg(s, steps, stream_ptr):
             "counts": counts.cpu().tolist()[:3]}
 
 
+def device_plan_leg(s, steps, stream_ptr):
+    """lora_apply_device on a setup's batch: device ids -> device metadata and
+    plan -> tile kernels, whole steps over the rotating replicas."""
+    import torch
+    L = s.L
+    lib = L.lib()
+    d = ctypes.byref(s.desc)
+    ids_d = torch.from_numpy(s.ids).cuda()
+    pre_d = torch.from_numpy(s.pre).cuda()
+    nws = L.lora_apply_device_workspace_bytes(s.desc, s.T)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        r = i % s.nrep
+        if lib.lora_apply_device(d, s.pA[r], s.pB[r], s.px[r], s.py[r], s.T, ids_d.data_ptr(),
+                                 pre_d.data_ptr(), 0, ws.data_ptr(), nws, stream_ptr):
+            raise RuntimeError(f"lora_apply_device failed: {L.last_error()}")
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(5 + i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e6
+
+
 def slot_load_leg(seed):
     """Adapter slots: time to make an adapter resident (pinned host copy ->
     device on the side stream, then the pad-and-fold kernel), cycling four
@@ -835,6 +863,9 @@ def main():
         for k, r in pk2.items():
             log(f"[bench] prefill {k}: {r['us']:.2f} us/launch, {r['GBs']:.0f} GB/s, "
                 f"{r['TFLOPs']:.1f} TFLOP/s")
+        dp = device_plan_leg(s2[0], max(20, args.steps // 10), stream_ptr)
+        out["secondary"]["device_plan_step_us"] = round(dp, 2)
+        log(f"[bench] prefill from device ids (lora_apply_device): {dp:.1f} us/step")
         del s2
         torch.cuda.empty_cache()
         # the same batch with each slot's true rank (lora_apply_ranked): the

@@ -400,17 +400,26 @@ int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const 
   m.seg_ids = (int32_t*)(w + d.seg_ids);
   int32_t* counts = (int32_t*)(w + d.counts);
   int32_t* tiles = (int32_t*)(w + d.tiles);
+  int32_t* mtiles = (int32_t*)(w + d.mtiles);
+  int32_t* perm = (int32_t*)(w + d.perm);
   hipStream_t st = (hipStream_t)stream;
   const int32_t limit = bgmv_max_rank > 0 ? bgmv_max_rank : LORA_BGMV_MAX_RANK_DEFAULT;
+  // the plan's shape is known on the host only as capacities: cap 8-row
+  // records and mcap 64-row records (surplus ones have 0 rows), T v rows.
+  // Small plans take the one-launch kernel, which reads 8-row records only;
+  // other bf16 plans put SGMV segments of sgmv_mfma_min_rows() rows or more on
+  // 64-row MFMA tiles, as the host plan does
   const int32_t cap = device_tile_cap(T, g.max_loras);
+  const bool onepass = device_plan_is_onepass(g, cap);
+  const bool mfma = g.dtype == LORA_BF16 && !onepass;
+  const int32_t mcap = mfma ? device_mfma_cap(T, g.max_loras) : 0;
+  const DevicePlanOut po{tiles, cap, mtiles, mcap, mfma ? sgmv_mfma_min_rows() : INT32_MAX, perm};
   if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, g.R > limit, m, counts, st,
-                                        tiles, cap))
+                                        &po))
     return e;
-  // the plan's shape is known on the host only as capacities: cap records
-  // (surplus ones have 0 rows), T v rows, wavefront tiles only
-  TilePlan tp{nullptr, tiles, cap, nullptr, 0, nullptr, 1, T, wave_ksplit(g, cap),
-              nullptr, nullptr, nullptr};
-  if (device_plan_is_onepass(g, cap)) return run_plan_onepass_list(g, x, A_pool, B_pool, y, tp, st);
+  TilePlan tp{perm, tiles, cap, mtiles, mcap, nullptr, mfma_ksplit(g, mcap), T,
+              wave_ksplit(g, cap), nullptr, nullptr, nullptr};
+  if (onepass) return run_plan_onepass_list(g, x, A_pool, B_pool, y, tp, st);
   float* v = (float*)(w + d.v);
   if (int32_t e = run_plan_shrink(g, x, A_pool, v, tp, st)) return e;
   return run_plan_expand(g, v, B_pool, y, tp, st);

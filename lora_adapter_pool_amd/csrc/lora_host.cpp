@@ -134,9 +134,13 @@ DeviceLayout device_layout(const Geo& g, int32_t T) {
   d.seg_lens = o;
   o = align_up(o + ml * 4, 16);
   d.seg_ids = o;
-  o = align_up(o + ml * 4, 256);
+  o = align_up(o + ml * 4, 16);
+  d.perm = o;
+  o = align_up(o + rows * 4, 256);
   d.tiles = o;
   o = align_up(o + (int64_t)device_tile_cap(T, g.max_loras) * LORA_PLAN_WAVE_WORDS * 4, 256);
+  d.mtiles = o;
+  o = align_up(o + (int64_t)device_mfma_cap(T, g.max_loras) * LORA_PLAN_MFMA_WORDS * 4, 256);
   d.v = o;
   d.total = o + (int64_t)LORA_PLAN_MAX_KSPLIT * rows * g.S * g.R * 4;
   return d;
@@ -283,6 +287,24 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
 //   - wavefront tiles of LORA_PLAN_WAVE_ROWS rows: every other run.
 // v row numbering: SGMV rows first, then BGMV rows; perm holds the token of
 // every v row.
+// K split of the MFMA shrink: doubled while the launch has fewer than two
+// workgroups per compute unit (256 CUs) and every split keeps at least four
+// 64-wide K steps
+int32_t mfma_ksplit(const Geo& g, int64_t nm) {
+  int32_t ksplit = 1;
+  if (nm > 0) {
+    const int64_t wgs = nm * g.S * ((g.R + 63) / 64);
+    const int64_t ksteps = (g.K + 63) / 64;
+    while (ksplit < LORA_PLAN_MAX_KSPLIT_MFMA && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4)
+      ksplit *= 2;
+    if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1, 2 or 4
+      const long o = std::strtol(e, nullptr, 10);
+      if (o == 1 || o == 2 || o == 4) ksplit = (int32_t)o;
+    }
+  }
+  return ksplit;
+}
+
 int32_t wave_ksplit(const Geo& g, int64_t nw) {
   int32_t ksplit_wave = 1;
   if (g.dtype == LORA_BF16 && nw > 0 && g.R <= 64) {
@@ -407,23 +429,7 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
     i = j;
   }
   const int64_t words = off_mfma + nm * LORA_PLAN_MFMA_WORDS;
-  // K split of the MFMA shrink: double it while the launch has fewer than two
-  // workgroups per compute unit (256 CUs) and every split keeps at least four
-  // 64-wide K steps
-  int32_t ksplit = 1;
-  if (nm > 0) {
-    const int64_t wgs = nm * g.S * ((g.R + 63) / 64);
-    const int64_t ksteps = (g.K + 63) / 64;
-    while (ksplit < LORA_PLAN_MAX_KSPLIT_MFMA && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4)
-      ksplit *= 2;
-    if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1, 2 or 4
-      const long o = std::strtol(e, nullptr, 10);
-      if (o == 1 || o == 2 || o == 4) ksplit = (int32_t)o;
-    }
-  }
-  // K split of the wavefront tiles' MFMA shrink (bf16, R <= 64): grow it while
-  // the launch has fewer than four workgroups per compute unit and every part
-  // keeps at least one full load batch for each of the workgroup's waves
+  const int32_t ksplit = mfma_ksplit(g, nm);
   const int32_t ksplit_wave = wave_ksplit(g, nw);
   if (words > sl.image_max_words)  // cannot happen: the bounds above hold for any batch
     return fail(LORA_E_WORKSPACE, "tile plan overflow (%lld words > %lld)", (long long)words,

@@ -114,14 +114,25 @@ int32_t run_plan_onepass_list(const Geo& g, const void* x, const void* A, const 
                               const TilePlan& p, hipStream_t st);
 int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
                        const TilePlan& p, float* v, hipStream_t st);
+// Outputs of a device-built plan (lora_apply_device): cap 8-row tile records,
+// mcap 64-row MFMA tile records (SGMV segments of at least mfma_min rows; a
+// larger mfma_min than T disables them) and the v-row -> token map perm[T].
+// Records past the last tile have 0 rows.
+struct DevicePlanOut {
+  int32_t* tiles;
+  int32_t cap;
+  int32_t* mtiles;
+  int32_t mcap;
+  int32_t mfma_min;
+  int32_t* perm;
+};
 // Device-side builder (csrc/lora_meta.hip): lora_build_meta's arrays from
 // device ids, one workgroup on `st`; counts[4] = rows, segments, BGMV rows,
-// rejected ids.  With `tiles`, the same launch then writes cap 8-row tile
-// records of a device-built plan (records past the last tile have 0 rows).
+// rejected ids.  With `plan`, the same launch then writes a device-built plan.
 int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
                               int32_t max_loras, bool all_sgmv, const lora_meta& m,
-                              int32_t* counts, hipStream_t st, int32_t* tiles = nullptr,
-                              int32_t cap = 0);
+                              int32_t* counts, hipStream_t st,
+                              const DevicePlanOut* plan = nullptr);
 int32_t run_pool_load(const Geo& g, void* A_slot_slice, void* B_slot_slice, const void* Asrc,
                       const void* Bsrc, int r, int out_s, float scale, hipStream_t st);
 

@@ -26,7 +26,7 @@ constexpr int kMetaThreads = 1024;
 __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ prefill, int32_t T,
     int32_t max_loras, int32_t all_sgmv, lora_meta m, int32_t* __restrict__ counts,
-    int32_t kcap, int32_t* __restrict__ tiles, int32_t cap) {
+    int32_t kcap, DevicePlanOut plan) {
   // [max_loras] SGMV bins, [max_loras] BGMV bins, then the keys of a block of
   // kcap rows (int16: 2 id + set, or -1)
   extern __shared__ int32_t lds[];
@@ -170,60 +170,84 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       if (first) *pos = p0 + cnt;
     }
   }
-  if (tiles == nullptr) return;
+  if (plan.tiles == nullptr) return;
 
-  // 4. tile records of a device-built plan (lora_apply_device): the rows cut
-  // into 8-row tiles of one adapter, records as the host plan's wavefront
-  // records (slot, rows, first v row, 0, tokens, -1 past the last row; v rows
-  // are the SGMV rows, then the BGMV rows).  After placement each bin holds
-  // its slot's end position, and slots are laid out back to back, so a slot's
-  // rows run from the previous slot's end to its own.  An exclusive scan of
-  // the tiles per slot gives each slot's first record, and one thread per
-  // record finds its slot by binary search.  Records from the last tile up to
-  // cap get 0 rows (the kernels skip them), so launches can take cap as grid.
+  // 4. a device-built plan (lora_apply_device), records as the host plan's:
+  // 8-row tiles (slot, rows, first v row, 0, tokens, -1 past the last row) and
+  // 64-row MFMA tiles (slot, rows, first v row, first token when the tile's
+  // tokens are consecutive, else -1); v rows are the SGMV rows, then the BGMV
+  // rows.  After placement each bin holds its slot's end position, and slots
+  // are laid out back to back, so a slot's rows run from the previous slot's
+  // end to its own.  A slot's SGMV rows take MFMA tiles when there are at
+  // least mfma_min of them.  Exclusive scans of both tile counts per slot give
+  // each slot's first records, and one thread per record finds its slot by
+  // binary search.  Records from the last tile up to the capacity get 0 rows
+  // (the kernels skip them), so launches can take the capacities as grids.
   __syncthreads();  // placement (wavefront 0) is complete
   int32_t* toff = lds + 2 * max_loras + kcap / 2;  // [max_loras + 1], after the keys
-  int nt = 0;
+  int32_t* moff = toff + max_loras + 1;            // [max_loras + 1]
+  int nt = 0, nmf = 0;
   for (int a = a0; a < a1; ++a) {
     const int sc = cs[a] - (a > 0 ? cs[a - 1] : 0), bc = cb[a] - (a > 0 ? cb[a - 1] : 0);
-    nt += (sc + 7) / 8 + (bc + 7) / 8;
+    const bool mf = sc >= plan.mfma_min;
+    nt += (mf ? 0 : (sc + 7) / 8) + (bc + 7) / 8;
+    nmf += mf ? (sc + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS : 0;
   }
-  int inct = nt;
+  int inct = nt, incm = nmf;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(inct, o, 64);
-    if (lane >= o) inct += u;
+    const int ut = __shfl_up(inct, o, 64), um = __shfl_up(incm, o, 64);
+    if (lane >= o) {
+      inct += ut;
+      incm += um;
+    }
   }
-  if (lane == 63) s_wsum[wave][0] = inct;
+  if (lane == 63) {
+    s_wsum[wave][0] = inct;
+    s_wsum[wave][1] = incm;
+  }
   __syncthreads();
-  int tb = 0, ttot = 0;
+  int tb = 0, ttot = 0, mb = 0, mtot = 0;
   for (int w = 0; w < nw; ++w) {
     tb += w < wave ? s_wsum[w][0] : 0;
     ttot += s_wsum[w][0];
+    mb += w < wave ? s_wsum[w][1] : 0;
+    mtot += s_wsum[w][1];
   }
   tb += inct - nt;
+  mb += incm - nmf;
   for (int a = a0; a < a1; ++a) {
     const int sc = cs[a] - (a > 0 ? cs[a - 1] : 0), bc = cb[a] - (a > 0 ? cb[a - 1] : 0);
+    const bool mf = sc >= plan.mfma_min;
     toff[a] = tb;
-    tb += (sc + 7) / 8 + (bc + 7) / 8;
+    moff[a] = mb;
+    tb += (mf ? 0 : (sc + 7) / 8) + (bc + 7) / 8;
+    mb += mf ? (sc + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS : 0;
   }
-  if (tid == 0) toff[max_loras] = ttot;
+  if (tid == 0) {
+    toff[max_loras] = ttot;
+    moff[max_loras] = mtot;
+  }
   __syncthreads();
-  for (int f = tid; f < cap; f += kMetaThreads) {
-    int32_t* r = tiles + (size_t)f * LORA_PLAN_WAVE_WORDS;
+  // the last slot whose first record is at or before f owns record f (empty
+  // slots before it have smaller indices)
+  auto owner = [&](const int32_t* off, int f) {
+    int lo = 0, hi = max_loras - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= f) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  for (int f = tid; f < plan.cap; f += kMetaThreads) {
+    int32_t* r = plan.tiles + (size_t)f * LORA_PLAN_WAVE_WORDS;
     int slot = 0, rows = 0, vrow = 0;
     const int32_t* src = nullptr;
     if (f < ttot) {
-      // the last slot whose first record is at or before f owns it (empty
-      // slots before it have smaller indices)
-      int lo = 0, hi = max_loras - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (toff[mid] <= f) lo = mid; else hi = mid - 1;
-      }
-      slot = lo;
+      slot = owner(toff, f);
       const int s0 = slot > 0 ? cs[slot - 1] : 0, b0 = slot > 0 ? cb[slot - 1] : 0;
-      const int lt = f - toff[slot], tsg = (cs[slot] - s0 + 7) / 8;
+      const int sc = cs[slot] - s0;
+      const int lt = f - toff[slot], tsg = sc >= plan.mfma_min ? 0 : (sc + 7) / 8;
       if (lt < tsg) {
         vrow = s0 + LORA_PLAN_WAVE_ROWS * lt;
         rows = min(LORA_PLAN_WAVE_ROWS, cs[slot] - vrow);
@@ -241,21 +265,40 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     r[3] = 0;
     for (int i = 0; i < LORA_PLAN_WAVE_WORDS - 4; ++i) r[4 + i] = i < rows ? src[i] : -1;
   }
+  for (int f = tid; f < plan.mcap; f += kMetaThreads) {
+    int slot = 0, rows = 0, vrow = 0, tok0 = -1;
+    if (f < mtot) {
+      slot = owner(moff, f);
+      vrow = (slot > 0 ? cs[slot - 1] : 0) + LORA_PLAN_MFMA_ROWS * (f - moff[slot]);
+      rows = min(LORA_PLAN_MFMA_ROWS, cs[slot] - vrow);
+      const int t0 = m.sgmv_perm[vrow];
+      bool consecutive = true;
+      for (int i = 1; i < rows; ++i) consecutive &= m.sgmv_perm[vrow + i] == t0 + i;
+      tok0 = consecutive ? t0 : -1;
+    }
+    int32_t* r = plan.mtiles + (size_t)f * LORA_PLAN_MFMA_WORDS;
+    r[0] = slot;
+    r[1] = rows;
+    r[2] = vrow;
+    r[3] = tok0;
+  }
+  for (int i = tid; i < T; i += kMetaThreads)
+    plan.perm[i] = i < ns ? m.sgmv_perm[i] : i < ns + nb ? m.bgmv_tok[i - ns] : 0;
 }
 
 int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
                               int32_t max_loras, bool all_sgmv, const lora_meta& m,
-                              int32_t* counts, hipStream_t st, int32_t* tiles, int32_t cap) {
-  // LDS: the bins, the keys of a block of rows, then (with tiles) each slot's
-  // first record; up to 128 KB in all
+                              int32_t* counts, hipStream_t st, const DevicePlanOut* plan) {
+  // LDS: the bins, the keys of a block of rows, then (with a plan) each
+  // slot's first record of both kinds; up to 128 KB in all
   const int64_t bins = (int64_t)2 * max_loras * sizeof(int32_t);
-  const int64_t toff = tiles ? (int64_t)(max_loras + 1) * sizeof(int32_t) : 0;
+  const int64_t toff = plan ? (int64_t)2 * (max_loras + 1) * sizeof(int32_t) : 0;
   int64_t kcap = ((int64_t)128 * 1024 - bins - toff) / (int64_t)sizeof(int16_t) / 64 * 64;
   kcap = std::max<int64_t>(64, std::min<int64_t>(kcap, ((int64_t)T + 63) / 64 * 64));
   hipLaunchKernelGGL(build_meta_kernel, dim3(1), dim3(kMetaThreads),
                      (size_t)(bins + kcap * (int64_t)sizeof(int16_t) + toff), st, ids, prefill,
-                     T, max_loras, all_sgmv ? 1 : 0, m, counts, (int32_t)kcap, tiles,
-                     tiles ? cap : 0);
+                     T, max_loras, all_sgmv ? 1 : 0, m, counts, (int32_t)kcap,
+                     plan ? *plan : DevicePlanOut{nullptr, 0, nullptr, 0, 0, nullptr});
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(LORA_E_HIP, "build_meta launch: %s", hipGetErrorString(e));
   return LORA_OK;
