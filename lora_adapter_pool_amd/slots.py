@@ -190,12 +190,13 @@ class AdapterSlots:
         return bs.ids
 
     def apply(self, x, y, adapter_ids: Sequence[Optional[int]], prefill=None,
-              stream=None) -> np.ndarray:
-        """y += the LoRA delta of each row's adapter (None = base model)."""
+              stream=None, ragged: bool = False) -> np.ndarray:
+        """y += the LoRA delta of each row's adapter (None = base model).
+        ragged: skip each slot's padded ranks (LoraPool.apply; same result)."""
         torch = self.torch
         compute = stream or torch.cuda.current_stream()
         ids = self.prepare(adapter_ids, compute)
-        self.pool.apply(x, y, ids, prefill, stream=compute)
+        self.pool.apply(x, y, ids, prefill, stream=compute, ragged=ragged)
         done = torch.cuda.Event()
         done.record(compute)
         for slot in set(int(s) for s in ids if s >= 0):

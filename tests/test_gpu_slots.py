@@ -72,3 +72,35 @@ def test_slots_back_to_back_batches():
     slots.register(66, "adapter-66", ad.A, ad.B, ad.rank, ad.alpha)
     with pytest.raises(SlotError):
         slots.apply(to_dev(batches[0][2][:1], "bf16"), to_dev(batches[0][3][:1], "bf16"), [gone])
+
+
+def test_slots_ragged_equals_padded():
+    """Slots loaded and reused between batches, applied with each slot's true
+    rank: bit for bit the padded result, batch by batch (batches large enough
+    that the plan goes through device records, which carry the rank)."""
+    import torch
+    K, outs, R = 520, (264,), 32
+    user_ids = [1, 2, 3, 4]
+    rng = np.random.default_rng(22)
+    ranks = {a: int(rng.choice([8, 16])) for a in user_ids}
+    adapters = W._draw_slots(rng, "bf16", K, list(outs), ranks,
+                             {a: 2.0 * ranks[a] for a in user_ids}, rslora=False)
+    pools = [L.LoraPool("bf16", 2, R, K, list(outs)) for _ in range(2)]
+    runs = [AdapterSlots(p, max_cpu_loras=4) for p in pools]
+    for sl in runs:
+        for a in user_ids:
+            ad = adapters[a]
+            sl.register(a, f"adapter-{a}", ad.A, ad.B, ad.rank, ad.alpha)
+    for i in range(5):
+        T = int(rng.integers(600, 800))
+        use = list(rng.choice(user_ids, size=2, replace=False))
+        ids = [int(rng.choice(use)) if rng.random() > 0.1 else None for _ in range(T)]
+        x = to_dev(W.to_dtype_values(rng.standard_normal((T, K)), "bf16"), "bf16")
+        y = to_dev(W.to_dtype_values(rng.standard_normal((T, sum(outs))), "bf16"), "bf16")
+        ys = [y.clone(), y.clone()]
+        runs[0].apply(x, ys[0], ids)
+        runs[1].apply(x, ys[1], ids, ragged=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16)), f"batch {i}"
+        assert pools[1].slot_ranks().tolist() == [
+            ranks[a] for a in sorted(runs[1].table.gpu, key=lambda a: runs[1].table.gpu[a])]
