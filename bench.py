@@ -260,9 +260,14 @@ def ragged_decode_leg(seed, steps, stream_ptr, replica_bytes):
         st = [Setup(wl, replica_bytes, ragged=ragged)]
         t = measure(st, steps, 10, stream_ptr) / steps
         _, pk = kernel_roofline(st, stream_ptr, 50)
+        # algorithmic bytes: the padded path must move rank-64 weights and v,
+        # the ragged path only the adapters' rank 16
+        alg = algorithmic(dataclasses.replace(wl, max_lora_rank=16) if ragged else wl)
         res["ragged" if ragged else "padded"] = {
             "us_per_step": round(t * 1e6, 2),
-            "per_kernel_us": {k: round(r["us"], 2) for k, r in pk.items()}}
+            "per_kernel_us": {k: round(r["us"], 2) for k, r in pk.items()},
+            "per_kernel_GBs": {k: round(alg[f"{k}_bytes"] / (r["us"] * 1e3), 1)
+                               for k, r in pk.items()}}
         del st
         torch.cuda.empty_cache()
     res["speedup"] = res["padded"]["us_per_step"] / res["ragged"]["us_per_step"]

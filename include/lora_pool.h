@@ -429,8 +429,11 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
  *   ws            device workspace of lora_apply_device_workspace_bytes(desc,
  *                 T) bytes, 256-byte aligned: metadata, the tile records, v
  * The result is lora_apply's (within rounding: the K split may differ).
- * Long prefill segments run on the 8-row tiles too, so lora_apply is faster
- * for prefill batches.  Errors (before any HIP call): LORA_E_SHAPE if
+ * The plan follows the host plan's rules except that decode rows always take
+ * 8-row tiles; its record counts are known on the host only as capacities
+ * (surplus records have 0 rows).  The metadata is built by one workgroup, so
+ * large prefill batches are faster through lora_apply.  Errors (before any
+ * HIP call): LORA_E_SHAPE if
  * max_loras > LORA_META_DEVICE_MAX_LORAS, LORA_E_WORKSPACE, LORA_E_ALIGN,
  * LORA_E_ARG; T = 0 is a no-op. */
 int64_t lora_apply_device_workspace_bytes(const lora_pool_desc* desc, int32_t T);
