@@ -276,3 +276,43 @@ def test_plan_entry_validation_before_hip():
     pm, _, _ = L.lora_apply_plan(d, np.zeros(40, np.int32), np.ones(40, np.uint8))
     assert pm["mfma_tiles"] > 0
     assert status(L.lora_plan_shrink, pm, desc=d32, T=40) == _lib.LORA_E_DTYPE
+
+
+def _device_plan_counts(ids, prefill, max_loras, R, mfma_min, bgmv_max_rank=64):
+    """Records a device-built plan writes (lora_apply_device's rules): per slot,
+    SGMV rows on 64-row tiles when there are at least mfma_min of them, else
+    on 8-row tiles; BGMV rows always on 8-row tiles."""
+    m = L.lora_build_meta(ids, prefill, max_loras, R, bgmv_max_rank)
+    sc = np.zeros(max_loras, np.int64)
+    for a, ln in zip(m["seg_ids"], m["seg_lens"]):
+        sc[a] += ln
+    bc = np.bincount(m["bgmv_ids"], minlength=max_loras) if m["bgmv_ids"].size else \
+        np.zeros(max_loras, np.int64)
+    mf = sc >= mfma_min
+    wave = int(np.sum(np.where(mf, 0, -(-sc // 8)) + -(-bc // 8)))
+    mfma = int(np.sum(np.where(mf, -(-sc // 64), 0)))
+    return wave, mfma
+
+
+def test_device_plan_capacity_bounds():
+    """The device plan's record capacities, ceil(T/8) + 2 min(max_loras, T)
+    8-row records and ceil(T/64) + min(max_loras, T) 64-row records, cover
+    every batch: random mixes, one row per slot in each set, long runs."""
+    rng = np.random.default_rng(3)
+    cases = []
+    for _ in range(300):
+        ml = int(rng.integers(1, 80))
+        T = int(rng.integers(1, 700))
+        ids = rng.integers(-1, ml, size=T).astype(np.int32)
+        if rng.random() < 0.3:
+            ids = np.sort(ids)
+        cases.append((ml, ids, (rng.random(T) < rng.random()).astype(np.uint8)))
+    for ml in (1, 7, 64):  # every slot with one SGMV row and one BGMV row
+        ids = np.repeat(np.arange(ml, dtype=np.int32), 2)
+        cases.append((ml, ids, np.tile(np.array([1, 0], np.uint8), ml)))
+    for ml, ids, pre in cases:
+        T = ids.size
+        for mfma_min in (16, 1, 2 ** 31 - 1):
+            wave, mfma = _device_plan_counts(ids, pre, ml, 16, mfma_min)
+            assert wave <= -(-T // 8) + 2 * min(ml, T)
+            assert mfma <= -(-T // 64) + min(ml, T)
