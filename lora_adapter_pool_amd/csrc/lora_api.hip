@@ -407,13 +407,20 @@ int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const 
   // the plan's shape is known on the host only as capacities: cap 8-row
   // records and mcap 64-row records (surplus ones have 0 rows), T v rows.
   // Small plans take the one-launch kernel, which reads 8-row records only;
-  // other bf16 plans put SGMV segments of sgmv_mfma_min_rows() rows or more on
-  // 64-row MFMA tiles, as the host plan does
+  // other bf16 plans put long SGMV segments and, in large decode batches, long
+  // BGMV runs on 64-row MFMA tiles by the host plan's rules
   const int32_t cap = device_tile_cap(T, g.max_loras);
   const bool onepass = device_plan_is_onepass(g, cap);
   const bool mfma = g.dtype == LORA_BF16 && !onepass;
   const int32_t mcap = mfma ? device_mfma_cap(T, g.max_loras) : 0;
-  const DevicePlanOut po{tiles, cap, mtiles, mcap, mfma ? sgmv_mfma_min_rows() : INT32_MAX, perm};
+  const DevicePlanOut po{tiles,
+                         cap,
+                         mtiles,
+                         mcap,
+                         mfma ? sgmv_mfma_min_rows() : INT32_MAX,
+                         mfma ? bgmv_mfma_min_rows() : INT32_MAX,
+                         bgmv_mfma_min_total(g.R),
+                         perm};
   if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, g.R > limit, m, counts, st,
                                         &po))
     return e;

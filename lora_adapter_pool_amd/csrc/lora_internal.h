@@ -82,16 +82,17 @@ int32_t wave_ksplit(const Geo& g, int64_t nw);
 int32_t mfma_ksplit(const Geo& g, int64_t nm);
 
 // Device-built plan of lora_apply_device: capacities of its 8-row tile
-// records (each slot adds at most one partial tile to each of its two row
-// sets) and of its 64-row MFMA tile records (SGMV segments only: at most one
-// partial tile per slot), and its workspace (byte offsets): the metadata
+// records and of its 64-row MFMA tile records (each slot adds at most one
+// partial tile of each size to each of its two row sets), and its workspace
+// (byte offsets): the metadata
 // arrays, the v-row -> token map, both record arrays, then v
 // (LORA_PLAN_MAX_KSPLIT partials of T rows x S x R fp32).
 inline int32_t device_tile_cap(int32_t T, int32_t max_loras) {
   return (T + LORA_PLAN_WAVE_ROWS - 1) / LORA_PLAN_WAVE_ROWS + 2 * (T < max_loras ? T : max_loras);
 }
 inline int32_t device_mfma_cap(int32_t T, int32_t max_loras) {
-  return (T + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS + (T < max_loras ? T : max_loras);
+  return (T + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS +
+         2 * (T < max_loras ? T : max_loras);
 }
 struct DeviceLayout {
   int64_t counts, sgmv_perm, bgmv_tok, bgmv_ids, seg_starts, seg_lens, seg_ids, perm, tiles,

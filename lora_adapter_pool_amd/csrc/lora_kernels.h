@@ -115,15 +115,19 @@ int32_t run_plan_onepass_list(const Geo& g, const void* x, const void* A, const 
 int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
                        const TilePlan& p, float* v, hipStream_t st);
 // Outputs of a device-built plan (lora_apply_device): cap 8-row tile records,
-// mcap 64-row MFMA tile records (SGMV segments of at least mfma_min rows; a
-// larger mfma_min than T disables them) and the v-row -> token map perm[T].
-// Records past the last tile have 0 rows.
+// mcap 64-row MFMA tile records and the v-row -> token map perm[T].  A slot's
+// SGMV rows take MFMA tiles when there are at least mfma_min of them; its BGMV
+// rows when there are at least bgmv_min of them and such runs hold at least
+// bgmv_total rows of the batch (values above T disable either).  Records past
+// the last tile have 0 rows.
 struct DevicePlanOut {
   int32_t* tiles;
   int32_t cap;
   int32_t* mtiles;
   int32_t mcap;
   int32_t mfma_min;
+  int32_t bgmv_min;
+  int32_t bgmv_total;
   int32_t* perm;
 };
 // Device-side builder (csrc/lora_meta.hip): lora_build_meta's arrays from

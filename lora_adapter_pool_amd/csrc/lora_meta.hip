@@ -16,6 +16,8 @@
 // id -1 (skipped by the kernels), and sgmv_perm past num_sgmv_rows is 0.
 #include <hip/hip_runtime.h>
 
+#include <climits>
+
 #include "lora_internal.h"
 #include "lora_kernels.h"
 
@@ -179,19 +181,40 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   // rows.  After placement each bin holds its slot's end position, and slots
   // are laid out back to back, so a slot's rows run from the previous slot's
   // end to its own.  A slot's SGMV rows take MFMA tiles when there are at
-  // least mfma_min of them.  Exclusive scans of both tile counts per slot give
+  // least mfma_min of them, its BGMV rows when there are at least bgmv_min of
+  // them and such runs hold at least bgmv_total rows of the batch (a block
+  // sum decides that first).  Exclusive scans of both tile counts per slot give
   // each slot's first records, and one thread per record finds its slot by
   // binary search.  Records from the last tile up to the capacity get 0 rows
   // (the kernels skip them), so launches can take the capacities as grids.
   __syncthreads();  // placement (wavefront 0) is complete
   int32_t* toff = lds + 2 * max_loras + kcap / 2;  // [max_loras + 1], after the keys
   int32_t* moff = toff + max_loras + 1;            // [max_loras + 1]
+  int lr = 0;  // BGMV rows in runs of at least bgmv_min rows
+  for (int a = a0; a < a1; ++a) {
+    const int bc = cb[a] - (a > 0 ? cb[a - 1] : 0);
+    lr += bc >= plan.bgmv_min ? bc : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lr += __shfl_xor(lr, o, 64);
+  if (lane == 0) s_wsum[wave][2] = lr;
+  __syncthreads();
+  int lrt = 0;
+  for (int w = 0; w < nw; ++w) lrt += s_wsum[w][2];
+  const int bmin = lrt >= plan.bgmv_total ? plan.bgmv_min : INT_MAX;  // uniform
+  auto tiles_of = [&](int sc, int bc, int& w8, int& w64) {
+    const bool ms = sc >= plan.mfma_min, mb = bc >= bmin;
+    w8 = (ms ? 0 : (sc + 7) / 8) + (mb ? 0 : (bc + 7) / 8);
+    w64 = (ms ? (sc + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS : 0) +
+          (mb ? (bc + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS : 0);
+  };
   int nt = 0, nmf = 0;
   for (int a = a0; a < a1; ++a) {
     const int sc = cs[a] - (a > 0 ? cs[a - 1] : 0), bc = cb[a] - (a > 0 ? cb[a - 1] : 0);
-    const bool mf = sc >= plan.mfma_min;
-    nt += (mf ? 0 : (sc + 7) / 8) + (bc + 7) / 8;
-    nmf += mf ? (sc + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS : 0;
+    int w8, w64;
+    tiles_of(sc, bc, w8, w64);
+    nt += w8;
+    nmf += w64;
   }
   int inct = nt, incm = nmf;
 #pragma unroll
@@ -218,11 +241,12 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   mb += incm - nmf;
   for (int a = a0; a < a1; ++a) {
     const int sc = cs[a] - (a > 0 ? cs[a - 1] : 0), bc = cb[a] - (a > 0 ? cb[a - 1] : 0);
-    const bool mf = sc >= plan.mfma_min;
+    int w8, w64;
+    tiles_of(sc, bc, w8, w64);
     toff[a] = tb;
     moff[a] = mb;
-    tb += (mf ? 0 : (sc + 7) / 8) + (bc + 7) / 8;
-    mb += mf ? (sc + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS : 0;
+    tb += w8;
+    mb += w64;
   }
   if (tid == 0) {
     toff[max_loras] = ttot;
@@ -247,6 +271,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       slot = owner(toff, f);
       const int s0 = slot > 0 ? cs[slot - 1] : 0, b0 = slot > 0 ? cb[slot - 1] : 0;
       const int sc = cs[slot] - s0;
+      // 8-row tiles: the SGMV rows' (unless on MFMA tiles), then the BGMV rows'
       const int lt = f - toff[slot], tsg = sc >= plan.mfma_min ? 0 : (sc + 7) / 8;
       if (lt < tsg) {
         vrow = s0 + LORA_PLAN_WAVE_ROWS * lt;
@@ -268,12 +293,28 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   for (int f = tid; f < plan.mcap; f += kMetaThreads) {
     int slot = 0, rows = 0, vrow = 0, tok0 = -1;
     if (f < mtot) {
+      // 64-row tiles: the SGMV rows' (if on MFMA tiles), then the BGMV rows'
       slot = owner(moff, f);
-      vrow = (slot > 0 ? cs[slot - 1] : 0) + LORA_PLAN_MFMA_ROWS * (f - moff[slot]);
-      rows = min(LORA_PLAN_MFMA_ROWS, cs[slot] - vrow);
-      const int t0 = m.sgmv_perm[vrow];
+      const int s0 = slot > 0 ? cs[slot - 1] : 0, b0 = slot > 0 ? cb[slot - 1] : 0;
+      const int sc = cs[slot] - s0;
+      const int lt = f - moff[slot];
+      const int msg = sc >= plan.mfma_min ? (sc + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS : 0;
+      const int32_t* src;
+      int first;
+      if (lt < msg) {
+        first = s0 + LORA_PLAN_MFMA_ROWS * lt;
+        rows = min(LORA_PLAN_MFMA_ROWS, cs[slot] - first);
+        vrow = first;
+        src = m.sgmv_perm + first;
+      } else {
+        first = b0 + LORA_PLAN_MFMA_ROWS * (lt - msg);
+        rows = min(LORA_PLAN_MFMA_ROWS, cb[slot] - first);
+        vrow = ns + first;
+        src = m.bgmv_tok + first;
+      }
+      const int t0 = src[0];
       bool consecutive = true;
-      for (int i = 1; i < rows; ++i) consecutive &= m.sgmv_perm[vrow + i] == t0 + i;
+      for (int i = 1; i < rows; ++i) consecutive &= src[i] == t0 + i;
       tok0 = consecutive ? t0 : -1;
     }
     int32_t* r = plan.mtiles + (size_t)f * LORA_PLAN_MFMA_WORDS;
@@ -298,7 +339,7 @@ int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_
   hipLaunchKernelGGL(build_meta_kernel, dim3(1), dim3(kMetaThreads),
                      (size_t)(bins + kcap * (int64_t)sizeof(int16_t) + toff), st, ids, prefill,
                      T, max_loras, all_sgmv ? 1 : 0, m, counts, (int32_t)kcap,
-                     plan ? *plan : DevicePlanOut{nullptr, 0, nullptr, 0, 0, nullptr});
+                     plan ? *plan : DevicePlanOut{nullptr, 0, nullptr, 0, 0, 0, 0, nullptr});
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(LORA_E_HIP, "build_meta launch: %s", hipGetErrorString(e));
   return LORA_OK;

@@ -320,7 +320,7 @@ def test_apply_device_validation_before_hip():
     meta = up(meta + 4 * 6, 16)
     perm = up(meta + 4 * T, 256)                 # v row -> token
     tiles = up(perm + cap * 16 * 4, 256)         # 8-row records
-    mcap = -(-T // 64) + min(6, T)
+    mcap = -(-T // 64) + 2 * min(6, T)
     mtiles = up(tiles + mcap * 4 * 4, 256)       # 64-row records
     assert need == mtiles + 8 * T * 2 * 16 * 4   # v: up to 8 partials of T x S x R fp32
     ok = [d, FAKE, FAKE, FAKE, FAKE + 4096, T, FAKE, None, 0, FAKE, need]

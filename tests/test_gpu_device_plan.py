@@ -187,3 +187,19 @@ def test_device_plan_one_launch_graph_replays():
         exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(case), wl.dtype)
         bad = np.argwhere(yd.float().cpu().numpy() != exp)
         assert bad.size == 0, f"replay {rep}: {len(bad)} mismatches, first {bad[:3]}"
+
+
+def test_device_plan_large_decode_mfma_runs():
+    """A large decode batch over few adapters: the device plan puts the long
+    runs on 64-row MFMA tiles, as the host plan does; exact on integer inputs
+    and within tolerance of the oracle on real-valued ones."""
+    wl = W.config_integer(seed=26, T=2600, K=520, outs=(264, 136), max_loras=4,
+                          max_lora_rank=64, ranks=(64, 16, 32, 8), prefill_frac=0.0,
+                          p_none=0.05, dtype="bf16")
+    p, _, _ = L.lora_apply_plan(make_pool(wl).desc, wl.ids, wl.prefill)
+    assert p["mfma_tiles"] > 0  # the host plan's rule sends these runs to MFMA tiles
+    exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(wl), "bf16")
+    bad = np.argwhere(_run(wl).float().cpu().numpy() != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+    real = W.config_bgmv_decode(seed=6, T=2304, K=1032, O=776, n_adapters=6, rank=16)
+    check_rows(real, _run(real), label="large decode, device plan")

@@ -278,25 +278,28 @@ def test_plan_entry_validation_before_hip():
     assert status(L.lora_plan_shrink, pm, desc=d32, T=40) == _lib.LORA_E_DTYPE
 
 
-def _device_plan_counts(ids, prefill, max_loras, R, mfma_min, bgmv_max_rank=64):
+def _device_plan_counts(ids, prefill, max_loras, R, mfma_min, bgmv_min, bgmv_total,
+                        bgmv_max_rank=64):
     """Records a device-built plan writes (lora_apply_device's rules): per slot,
-    SGMV rows on 64-row tiles when there are at least mfma_min of them, else
-    on 8-row tiles; BGMV rows always on 8-row tiles."""
+    SGMV rows on 64-row tiles when there are at least mfma_min of them, BGMV
+    rows when there are at least bgmv_min of them and such runs hold at least
+    bgmv_total rows of the batch; the rest on 8-row tiles."""
     m = L.lora_build_meta(ids, prefill, max_loras, R, bgmv_max_rank)
     sc = np.zeros(max_loras, np.int64)
     for a, ln in zip(m["seg_ids"], m["seg_lens"]):
         sc[a] += ln
     bc = np.bincount(m["bgmv_ids"], minlength=max_loras) if m["bgmv_ids"].size else \
         np.zeros(max_loras, np.int64)
-    mf = sc >= mfma_min
-    wave = int(np.sum(np.where(mf, 0, -(-sc // 8)) + -(-bc // 8)))
-    mfma = int(np.sum(np.where(mf, -(-sc // 64), 0)))
+    ms = sc >= mfma_min
+    mb = (bc >= bgmv_min) & (bc[bc >= bgmv_min].sum() >= bgmv_total)
+    wave = int(np.sum(np.where(ms, 0, -(-sc // 8)) + np.where(mb, 0, -(-bc // 8))))
+    mfma = int(np.sum(np.where(ms, -(-sc // 64), 0) + np.where(mb, -(-bc // 64), 0)))
     return wave, mfma
 
 
 def test_device_plan_capacity_bounds():
     """The device plan's record capacities, ceil(T/8) + 2 min(max_loras, T)
-    8-row records and ceil(T/64) + min(max_loras, T) 64-row records, cover
+    8-row records and ceil(T/64) + 2 min(max_loras, T) 64-row records, cover
     every batch: random mixes, one row per slot in each set, long runs."""
     rng = np.random.default_rng(3)
     cases = []
@@ -312,7 +315,7 @@ def test_device_plan_capacity_bounds():
         cases.append((ml, ids, np.tile(np.array([1, 0], np.uint8), ml)))
     for ml, ids, pre in cases:
         T = ids.size
-        for mfma_min in (16, 1, 2 ** 31 - 1):
-            wave, mfma = _device_plan_counts(ids, pre, ml, 16, mfma_min)
+        for mfma_min, bmin, btot in ((16, 48, 1024), (1, 1, 0), (2 ** 31 - 1,) * 3):
+            wave, mfma = _device_plan_counts(ids, pre, ml, 16, mfma_min, bmin, btot)
             assert wave <= -(-T // 8) + 2 * min(ml, T)
-            assert mfma <= -(-T // 64) + min(ml, T)
+            assert mfma <= -(-T // 64) + 2 * min(ml, T)
