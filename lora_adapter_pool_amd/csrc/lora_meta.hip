@@ -24,6 +24,12 @@
 namespace lora {
 
 constexpr int kMetaThreads = 1024;
+// Pools of at most this many slots place rows with all 16 wavefronts (each
+// with its own per-key counters in LDS: 16 x 2 x kParMaxLoras words).
+constexpr int kParMaxLoras = 256;
+// ... for blocks of more rows than this (smaller blocks: the three extra
+// barriers cost more than the single wavefront's chain).
+constexpr int kParMinRows = 1024;
 
 __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ prefill, int32_t T,
@@ -123,11 +129,20 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   if (tid == 0) counts[3] = s_bad;
 
   // 3. stable placement, by blocks of kcap rows: every thread stages the
-  // block's keys in LDS, then one wavefront places the rows 64 at a time.  A
-  // chunk gathers the next free position of each lane's key, ranks equal keys
-  // by lane order with ballots (registers only), and the first lane of each
-  // key writes the key's new next free position.
+  // block's keys in LDS, then the rows are placed 64 at a time.  A chunk
+  // gathers the next free position of each lane's key, ranks equal keys by
+  // lane order with ballots (registers only), and the first lane of each key
+  // writes the key's new next free position.  With at most kParMaxLoras slots
+  // and blocks of more than kParMinRows rows, each wavefront takes a
+  // contiguous sixteenth of the block: it counts its
+  // keys into its own counters, a prefix over the wavefronts per key turns the
+  // counts into each wavefront's first positions, and the wavefronts place
+  // their rows at once (rows keep token order, so the sort stays stable).
+  // Otherwise one wavefront places the whole block.
   int16_t* keys = reinterpret_cast<int16_t*>(lds + 2 * max_loras);
+  const bool par_slots = max_loras <= kParMaxLoras;  // uniform
+  const int nkeys = 2 * max_loras;
+  int32_t* wcnt = lds + 2 * max_loras + kcap / 2 + (plan.tiles ? 2 * (max_loras + 1) : 0);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int b0 = 0; b0 < T; b0 += kcap) {
     const int nbk = min(kcap, T - b0);
@@ -137,6 +152,60 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       const int a = ids[t];
       const bool ok = a >= 0 && a < max_loras;
       keys[i] = (int16_t)(ok ? 2 * a + ((all_sgmv || (prefill && prefill[t])) ? 1 : 0) : -1);
+    }
+    if (par_slots && nbk > kParMinRows) {  // uniform
+      int32_t* my = wcnt + wave * nkeys;
+      for (int k = lane; k < nkeys; k += 64) my[k] = 0;
+      __syncthreads();  // keys staged, counters cleared
+      const int sb = ((nbk + nw - 1) / nw + 63) / 64 * 64;
+      const int lo = min(nbk, wave * sb), hi = min(nbk, lo + sb);
+      for (int i = lo + lane; i < hi; i += 64) {
+        const int key = keys[i];
+        if (key >= 0) atomicAdd(&my[key], 1);
+      }
+      __syncthreads();
+      for (int k = tid; k < nkeys; k += kMetaThreads) {
+        int32_t* pos = (k & 1) ? &cs[k >> 1] : &cb[k >> 1];
+        int base = *pos;
+        for (int w = 0; w < nw; ++w) {
+          const int cnt = wcnt[w * nkeys + k];
+          wcnt[w * nkeys + k] = base;
+          base += cnt;
+        }
+        *pos = base;
+      }
+      __syncthreads();
+      for (int c = lo; c < hi; c += 64) {
+        const int i = c + lane;
+        const int key = i < hi ? keys[i] : -1;
+        const int p0 = key >= 0 ? my[key] : 0;
+        uint64_t pending = __ballot(key >= 0);
+        int rank = 0, cnt = 0;
+        bool first = false;
+        while (pending) {
+          const int leader = __builtin_ctzll(pending);
+          const int k = __builtin_amdgcn_readlane(key, leader);
+          const uint64_t mk = __ballot(key == k);
+          if (key == k) {
+            rank = __popcll(mk & below);
+            cnt = __popcll(mk);
+            first = lane == leader;
+          }
+          pending &= ~mk;
+        }
+        const int p = p0 + rank;
+        if (key >= 0 && p < T) {
+          const int t = b0 + i;
+          if (key & 1) {
+            m.sgmv_perm[p] = t;
+          } else {
+            m.bgmv_tok[p] = t;
+            m.bgmv_ids[p] = key >> 1;
+          }
+        }
+        if (first) my[key] = p0 + cnt;
+      }
+      continue;
     }
     __syncthreads();
     if (wave != 0) continue;
@@ -334,10 +403,14 @@ int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_
   // slot's first record of both kinds; up to 128 KB in all
   const int64_t bins = (int64_t)2 * max_loras * sizeof(int32_t);
   const int64_t toff = plan ? (int64_t)2 * (max_loras + 1) * sizeof(int32_t) : 0;
-  int64_t kcap = ((int64_t)128 * 1024 - bins - toff) / (int64_t)sizeof(int16_t) / 64 * 64;
+  const int64_t wcnt = max_loras <= kParMaxLoras
+                           ? (int64_t)(kMetaThreads / 64) * 2 * max_loras * sizeof(int32_t)
+                           : 0;
+  int64_t kcap = ((int64_t)128 * 1024 - bins - toff - wcnt) / (int64_t)sizeof(int16_t) / 64 * 64;
   kcap = std::max<int64_t>(64, std::min<int64_t>(kcap, ((int64_t)T + 63) / 64 * 64));
   hipLaunchKernelGGL(build_meta_kernel, dim3(1), dim3(kMetaThreads),
-                     (size_t)(bins + kcap * (int64_t)sizeof(int16_t) + toff), st, ids, prefill,
+                     (size_t)(bins + kcap * (int64_t)sizeof(int16_t) + toff + wcnt), st, ids,
+                     prefill,
                      T, max_loras, all_sgmv ? 1 : 0, m, counts, (int32_t)kcap,
                      plan ? *plan : DevicePlanOut{nullptr, 0, nullptr, 0, 0, 0, 0, nullptr});
   const hipError_t e = hipGetLastError();

@@ -56,7 +56,8 @@ def _check_against_host(ids, prefill, max_loras, R, bgmv_max_rank=0):
     (0, 4, False, "none", 16), (1, 1, False, "rand", 16), (63, 7, False, "rand", 16),
     (64, 8, False, "zero", 16), (65, 8, True, "rand", 16), (300, 64, False, "rand", 128),
     (1000, 1000, False, "rand", 16), (8772, 16, True, "one", 64), (4096, 8192, False, "rand", 16),
-    (3000, 33, True, "runs", 32)])
+    (3000, 33, True, "runs", 32), (5000, 200, False, "rand", 16), (2049, 256, False, "rand", 64),
+    (70000, 100, False, "rand", 16)])
 def test_device_builder_matches_host(T, max_loras, sorted_ids, pre_kind, R):
     rng = np.random.default_rng(T + max_loras)
     ids = rng.integers(-1, max_loras, size=T).astype(np.int32)
