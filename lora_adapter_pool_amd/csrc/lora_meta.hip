@@ -153,12 +153,15 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       const bool ok = a >= 0 && a < max_loras;
       keys[i] = (int16_t)(ok ? 2 * a + ((all_sgmv || (prefill && prefill[t])) ? 1 : 0) : -1);
     }
-    if (par_slots && nbk > kParMinRows) {  // uniform
-      int32_t* my = wcnt + wave * nkeys;
+    const bool par = par_slots && nbk > kParMinRows;  // uniform
+    int32_t* my = wcnt + wave * nkeys;  // this wavefront's counters (par)
+    int lo = 0, hi = 0;                  // the rows this wavefront places
+    if (par) {
       for (int k = lane; k < nkeys; k += 64) my[k] = 0;
       __syncthreads();  // keys staged, counters cleared
       const int sb = ((nbk + nw - 1) / nw + 63) / 64 * 64;
-      const int lo = min(nbk, wave * sb), hi = min(nbk, lo + sb);
+      lo = min(nbk, wave * sb);
+      hi = min(nbk, lo + sb);
       for (int i = lo + lane; i < hi; i += 64) {
         const int key = keys[i];
         if (key >= 0) atomicAdd(&my[key], 1);
@@ -167,6 +170,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       for (int k = tid; k < nkeys; k += kMetaThreads) {
         int32_t* pos = (k & 1) ? &cs[k >> 1] : &cb[k >> 1];
         int base = *pos;
+#pragma unroll 1
         for (int w = 0; w < nw; ++w) {
           const int cnt = wcnt[w * nkeys + k];
           wcnt[w * nkeys + k] = base;
@@ -174,45 +178,14 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
         }
         *pos = base;
       }
-      __syncthreads();
-      for (int c = lo; c < hi; c += 64) {
-        const int i = c + lane;
-        const int key = i < hi ? keys[i] : -1;
-        const int p0 = key >= 0 ? my[key] : 0;
-        uint64_t pending = __ballot(key >= 0);
-        int rank = 0, cnt = 0;
-        bool first = false;
-        while (pending) {
-          const int leader = __builtin_ctzll(pending);
-          const int k = __builtin_amdgcn_readlane(key, leader);
-          const uint64_t mk = __ballot(key == k);
-          if (key == k) {
-            rank = __popcll(mk & below);
-            cnt = __popcll(mk);
-            first = lane == leader;
-          }
-          pending &= ~mk;
-        }
-        const int p = p0 + rank;
-        if (key >= 0 && p < T) {
-          const int t = b0 + i;
-          if (key & 1) {
-            m.sgmv_perm[p] = t;
-          } else {
-            m.bgmv_tok[p] = t;
-            m.bgmv_ids[p] = key >> 1;
-          }
-        }
-        if (first) my[key] = p0 + cnt;
-      }
-      continue;
+    } else {
+      hi = wave == 0 ? nbk : 0;
     }
     __syncthreads();
-    if (wave != 0) continue;
-    for (int c = 0; c < nbk; c += 64) {
+    for (int c = lo; c < hi; c += 64) {
       const int i = c + lane;
-      const int key = i < nbk ? keys[i] : -1;
-      int32_t* pos = (key & 1) ? &cs[key >> 1] : &cb[key >> 1];
+      const int key = i < hi ? keys[i] : -1;
+      int32_t* pos = par ? &my[key] : (key & 1) ? &cs[key >> 1] : &cb[key >> 1];
       const int p0 = key >= 0 ? *pos : 0;
       uint64_t pending = __ballot(key >= 0);
       int rank = 0, cnt = 0;
@@ -228,9 +201,9 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
         }
         pending &= ~mk;
       }
-      if (key >= 0) {
+      const int p = p0 + rank;
+      if (key >= 0 && p < T) {
         const int t = b0 + i;
-        const int p = p0 + rank;
         if (key & 1) {
           m.sgmv_perm[p] = t;
         } else {
@@ -269,6 +242,8 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   if (lane == 0) s_wsum[wave][2] = lr;
   __syncthreads();
   int lrt = 0;
+  // (not unrolled: one lane mask live at a time)
+#pragma unroll 1
   for (int w = 0; w < nw; ++w) lrt += s_wsum[w][2];
   const int bmin = lrt >= plan.bgmv_total ? plan.bgmv_min : INT_MAX;  // uniform
   auto tiles_of = [&](int sc, int bc, int& w8, int& w64) {
@@ -300,6 +275,8 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   }
   __syncthreads();
   int tb = 0, ttot = 0, mb = 0, mtot = 0;
+  // (not unrolled: one lane mask live at a time)
+#pragma unroll 1
   for (int w = 0; w < nw; ++w) {
     tb += w < wave ? s_wsum[w][0] : 0;
     ttot += s_wsum[w][0];
