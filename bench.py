@@ -445,11 +445,35 @@ def device_meta_leg(s, steps, stream_ptr):
         plan_step(10 + i)
     torch.cuda.synchronize()
     plan_us = (time.perf_counter() - t0) / steps * 1e6
+    # the same calls captured in a graph (20 calls over 20 replicas), replayed
+    ncap = min(20, s.nrep)
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(graph, stream=gs):
+            cap_ptr = torch.cuda.current_stream().cuda_stream
+            for r in range(ncap):
+                if lib.lora_apply_device(d, s.pA[r], s.pB[r], s.px[r], s.py[r], T,
+                                         ids_d.data_ptr(), pre_d.data_ptr(), 0, ws.data_ptr(),
+                                         nws, cap_ptr):
+                    raise RuntimeError(f"lora_apply_device failed: {L.last_error()}")
+    torch.cuda.current_stream().wait_stream(gs)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(5, steps // ncap)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) / (reps * ncap) * 1e6
     a = algorithmic(wl)
     return {"builder_us": round(builder_us, 2), "step_us": round(step_us, 2),
             "tokens_per_s": a["Ta"] / (step_us * 1e-6), "launches_per_step": 5,
             "device_plan_step_us": round(plan_us, 2),
             "device_plan_tokens_per_s": a["Ta"] / (plan_us * 1e-6),
+            "device_plan_graph_step_us": round(graph_us, 2),
             "counts": counts.cpu().tolist()[:3]}
 
 
@@ -833,7 +857,8 @@ def main():
     dm = device_meta_leg(setups[0], max(20, args.steps // 4), stream_ptr)
     out["device_meta"] = dict(dm, workload=setups[0].wl.name)
     log(f"[bench] device metadata: builder {dm['builder_us']:.2f} us, step {dm['step_us']:.2f} us "
-        f"(5 launches); device plan (lora_apply_device) {dm['device_plan_step_us']:.2f} us")
+        f"(5 launches); device plan (lora_apply_device) {dm['device_plan_step_us']:.2f} us, "
+        f"replayed in a graph {dm['device_plan_graph_step_us']:.2f} us")
     del setups
     torch.cuda.empty_cache()
     if not args.no_secondary:
