@@ -7,10 +7,14 @@
 //      do not depend on their order);
 //   2. exclusive scans of both histograms and of the non-empty SGMV bins give
 //      every adapter its first position and its segment;
-//   3. the rows' keys are staged in LDS by blocks, and one wavefront places
-//      the rows in token order, 64 at a time: lanes with the same (adapter,
-//      set) key take consecutive positions in lane order, so the sort is
-//      stable and the result is the host builder's, bit for bit.
+//   3. the rows' keys are staged in LDS by blocks, and the rows are placed in
+//      token order, 64 at a time: lanes with the same (adapter, set) key take
+//      consecutive positions in lane order, so the sort is stable and the
+//      result is the host builder's, bit for bit.  One wavefront places a
+//      block, or, for pools of at most kParMaxLoras slots and large blocks,
+//      all 16 each place a contiguous sixteenth from their own positions;
+//   4. optionally (lora_apply_device), the tile records of a device-built
+//      plan in the host plan's format, up to fixed capacities.
 // Arrays are padded so the grouped entry points can take upper-bound sizes:
 // segments past num_segs have length 0, BGMV rows past num_bgmv_rows have
 // id -1 (skipped by the kernels), and sgmv_perm past num_sgmv_rows is 0.
