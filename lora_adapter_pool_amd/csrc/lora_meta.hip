@@ -55,15 +55,20 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // 1. histogram
+  // 1. histogram; a batch that fits one block of keys also stages its keys
+  //    here, so placement does not read the ids again
+  int16_t* keys = reinterpret_cast<int16_t*>(lds + 2 * max_loras);
+  const bool one_block = T <= kcap;
   for (int t = tid; t < T; t += kMetaThreads) {
     const int a = ids[t];
+    const bool ok = a >= 0 && a < max_loras;
+    const bool sg = ok && (all_sgmv || (prefill && prefill[t]));
+    if (one_block) keys[t] = (int16_t)(ok ? 2 * a + (sg ? 1 : 0) : -1);
     if (a < -1 || a >= max_loras) {
       atomicAdd(&s_bad, 1);
       continue;
     }
     if (a < 0) continue;
-    const bool sg = all_sgmv || (prefill && prefill[t]);
     atomicAdd(sg ? &cs[a] : &cb[a], 1);
   }
   __syncthreads();
@@ -143,7 +148,6 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   // counts into each wavefront's first positions, and the wavefronts place
   // their rows at once (rows keep token order, so the sort stays stable).
   // Otherwise one wavefront places the whole block.
-  int16_t* keys = reinterpret_cast<int16_t*>(lds + 2 * max_loras);
   const bool par_slots = max_loras <= kParMaxLoras;  // uniform
   const int nkeys = 2 * max_loras;
   int32_t* wcnt = lds + 2 * max_loras + kcap / 2 + (plan.tiles ? 2 * (max_loras + 1) : 0);
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   for (int b0 = 0; b0 < T; b0 += kcap) {
     const int nbk = min(kcap, T - b0);
     __syncthreads();  // the previous block's keys are placed
-    for (int i = tid; i < nbk; i += kMetaThreads) {
+    for (int i = tid; i < nbk && !one_block; i += kMetaThreads) {
       const int t = b0 + i;
       const int a = ids[t];
       const bool ok = a >= 0 && a < max_loras;
