@@ -90,3 +90,16 @@ def test_ragged_integer_exact():
     exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(wl), wl.dtype)
     bad = np.argwhere(y.float().cpu().numpy() != exp)
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
+@pytest.mark.parametrize("T,n", [(64, 8), (200, 6)])
+def test_ragged_small_plans_by_value(T, n):
+    # plans of at most 48 wavefront tiles travel in the kernel arguments (the
+    # one-launch decode kernel for at most 12): the rank field is not carried
+    # and the result is the padded path's
+    wl = W.config_bgmv_decode(seed=T, T=T, K=1032, O=776, n_adapters=n, rank=8)
+    import lora_adapter_pool_amd as L
+    d = L.make_desc(wl.dtype, wl.max_loras, 32, wl.in_features, wl.out_features)
+    p, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert p["mfma_tiles"] == 0 and p["wave_tiles"] <= 48
+    _ranked_vs_padded(wl, R=32, label=f"by-value plan T={T}")
