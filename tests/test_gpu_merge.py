@@ -122,3 +122,11 @@ def test_merged_base_product_matches_runtime_delta():
     err = float(np.max(np.abs(a - b) / (np.max(np.abs(b), axis=1, keepdims=True) + 1e-30)))
     say(f"  merged vs runtime: max row-relative difference {err:.2e}")
     assert err < 2e-2
+
+
+@pytest.mark.parametrize("K,out,R", [(8, 8, 8), (24, 16, 16)])
+def test_merge_smallest_shapes(K, out, R):
+    # one partial tile in both dimensions; exact on integer inputs
+    wl = W.config_integer(seed=K + out, T=4, K=K, outs=(out,), max_loras=2, max_lora_rank=R,
+                          ranks=(R, 8))
+    _merge_and_check(wl, integer=True, label=f"smallest K={K} out={out} R={R}")
