@@ -442,6 +442,19 @@ int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const 
                           const uint8_t* prefill, int32_t bgmv_max_rank, void* ws,
                           int64_t ws_bytes, void* stream);
 
+/* lora_apply_device with each slot's true rank, as lora_apply_ranked:
+ * slot_ranks is a device int32[max_loras] (0 = max_lora_rank; read by the
+ * GPU, so it is not validated on the host: a value outside [0,
+ * max_lora_rank] acts as max_lora_rank).  The tile records carry the ranks
+ * and the bf16 MFMA kernels skip the padded ones; plans small enough for the
+ * one-launch decode kernel use max_lora_rank.  Same result as
+ * lora_apply_device. */
+int32_t lora_apply_device_ranked(const lora_pool_desc* desc, const void* A_pool,
+                                 const void* B_pool, const void* x, void* y, int32_t T,
+                                 const int32_t* ids, const uint8_t* prefill,
+                                 int32_t bgmv_max_rank, const int32_t* slot_ranks, void* ws,
+                                 int64_t ws_bytes, void* stream);
+
 /* lora_apply with each slot's true rank (slot_ranks as in
  * lora_apply_plan_ranked, nullable): same result, padded ranks skipped. */
 int32_t lora_apply_ranked(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,

@@ -113,6 +113,8 @@ _SIGNATURES = {
     "lora_apply": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P, _I64, _P]),
     "lora_apply_device_workspace_bytes": (_I64, [_DP, _I32]),
     "lora_apply_device": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P]),
+    "lora_apply_device_ranked": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64,
+                                        _P]),
     "lora_merge_weights": (_I32, [_DP, _P, _P, _I32, _I32, _P, _P, _P]),
     "lora_apply_ranked": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P, _I64,
                                  _P]),
@@ -408,3 +410,12 @@ def lora_apply_device(desc, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank
     _check(lib().lora_apply_device(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), _ptr(x),
                                    _ptr(y), int(T), _ptr(ids), _ptr(prefill), int(bgmv_max_rank),
                                    _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def lora_apply_device_ranked(desc, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank,
+                             slot_ranks, ws, ws_bytes, stream=None) -> None:
+    """lora_apply_device with each slot's true rank (device int32[max_loras])."""
+    _check(lib().lora_apply_device_ranked(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool),
+                                          _ptr(x), _ptr(y), int(T), _ptr(ids), _ptr(prefill),
+                                          int(bgmv_max_rank), _ptr(slot_ranks), _ptr(ws),
+                                          int(ws_bytes), _stream(stream)))

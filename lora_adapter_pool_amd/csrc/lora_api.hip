@@ -367,6 +367,15 @@ int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const 
                           const void* x, void* y, int32_t T, const int32_t* ids,
                           const uint8_t* prefill, int32_t bgmv_max_rank, void* ws,
                           int64_t ws_bytes, void* stream) {
+  return lora_apply_device_ranked(desc, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank,
+                                  nullptr, ws, ws_bytes, stream);
+}
+
+int32_t lora_apply_device_ranked(const lora_pool_desc* desc, const void* A_pool,
+                                 const void* B_pool, const void* x, void* y, int32_t T,
+                                 const int32_t* ids, const uint8_t* prefill,
+                                 int32_t bgmv_max_rank, const int32_t* slot_ranks, void* ws,
+                                 int64_t ws_bytes, void* stream) {
   clear_error();
   Geo g;
   if (int32_t e = check_desc(desc, &g)) return e;
@@ -420,7 +429,9 @@ int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const 
                          mfma ? sgmv_mfma_min_rows() : INT32_MAX,
                          mfma ? bgmv_mfma_min_rows() : INT32_MAX,
                          bgmv_mfma_min_total(g.R),
-                         perm};
+                         perm,
+                         slot_ranks,
+                         g.R};
   if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, g.R > limit, m, counts, st,
                                         &po))
     return e;

@@ -129,6 +129,8 @@ struct DevicePlanOut {
   int32_t bgmv_min;
   int32_t bgmv_total;
   int32_t* perm;
+  const int32_t* slot_ranks;  // device int32[max_loras] or nullptr: records carry ranks
+  int32_t R;                  // the pool's rank (records carry 0 for it)
 };
 // Device-side builder (csrc/lora_meta.hip): lora_build_meta's arrays from
 // device ids, one workgroup on `st`; counts[4] = rows, segments, BGMV rows,

@@ -309,6 +309,14 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   __syncthreads();
   // the last slot whose first record is at or before f owns record f (empty
   // slots before it have smaller indices)
+  // rank a record carries: 0 = the pool's R, else the slot's rank rounded up
+  // to 8 (slot_ranks as lora_apply_ranked's; the kernels clamp any value)
+  auto rank_of = [&](int slot) {
+    if (plan.slot_ranks == nullptr) return 0;
+    const int r = plan.slot_ranks[slot];
+    const int r8 = (r + 7) / 8 * 8;
+    return r > 0 && r8 < plan.R ? r8 : 0;
+  };
   auto owner = [&](const int32_t* off, int f) {
     int lo = 0, hi = max_loras - 1;
     while (lo < hi) {
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     r[0] = slot;
     r[1] = rows;
     r[2] = vrow;
-    r[3] = 0;
+    r[3] = rows > 0 ? rank_of(slot) : 0;
     for (int i = 0; i < LORA_PLAN_WAVE_WORDS - 4; ++i) r[4 + i] = i < rows ? src[i] : -1;
   }
   for (int f = tid; f < plan.mcap; f += kMetaThreads) {
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     }
     int32_t* r = plan.mtiles + (size_t)f * LORA_PLAN_MFMA_WORDS;
     r[0] = slot;
-    r[1] = rows;
+    r[1] = rows > 0 ? rows | (rank_of(slot) << 16) : 0;
     r[2] = vrow;
     r[3] = tok0;
   }
@@ -397,7 +405,7 @@ int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_
                      (size_t)(bins + kcap * (int64_t)sizeof(int16_t) + toff + wcnt), st, ids,
                      prefill,
                      T, max_loras, all_sgmv ? 1 : 0, m, counts, (int32_t)kcap,
-                     plan ? *plan : DevicePlanOut{nullptr, 0, nullptr, 0, 0, 0, 0, nullptr});
+                     plan ? *plan : DevicePlanOut{nullptr, 0, nullptr, 0, 0, 0, 0, nullptr, nullptr, 0});
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(LORA_E_HIP, "build_meta launch: %s", hipGetErrorString(e));
   return LORA_OK;

@@ -203,3 +203,40 @@ def test_device_plan_large_decode_mfma_runs():
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
     real = W.config_bgmv_decode(seed=6, T=2304, K=1032, O=776, n_adapters=6, rank=16)
     check_rows(real, _run(real), label="large decode, device plan")
+
+
+def _device_ranked_vs_plain(wl, ranks, R=None, label=""):
+    import torch
+    pool = make_pool(wl, R=R)
+    buf, n = _ws(pool, wl.T)
+    xd = to_dev(wl.x, wl.dtype)
+    ids_d = torch.from_numpy(np.ascontiguousarray(wl.ids, dtype=np.int32)).cuda()
+    pre_d = torch.from_numpy(np.ascontiguousarray(wl.prefill, dtype=np.uint8)).cuda()
+    ranks_d = torch.from_numpy(np.ascontiguousarray(ranks, dtype=np.int32)).cuda()
+    ys = []
+    for ranked in (False, True):
+        y = to_dev(wl.y_in, wl.dtype)
+        if ranked:
+            L.lora_apply_device_ranked(pool.desc, pool.A, pool.B, xd, y, wl.T, ids_d, pre_d, 0,
+                                       ranks_d, buf, n)
+        else:
+            L.lora_apply_device(pool.desc, pool.A, pool.B, xd, y, wl.T, ids_d, pre_d, 0, buf, n)
+        torch.cuda.synchronize()
+        ys.append(y)
+    diff = int((ys[0].view(torch.int16) != ys[1].view(torch.int16)).sum().item())
+    say(f"  {label}: ranks {list(ranks)[:8]}, elements differing: {diff}")
+    assert diff == 0
+    check_rows(wl, ys[1], label=f"{label} ranked")
+
+
+def test_device_plan_ranked_equals_plain():
+    gu, dn = W.config_mlp_mixed(seed=5, n_prefill=4, len_lo=5, len_hi=90, n_decode=650,
+                                hidden=264, inter=520, n_adapters=8, rank_choices=(8, 16, 40, 64),
+                                max_lora_rank=64)
+    for wl in (gu, dn):
+        ranks = [wl.slots[a].rank if a in wl.slots else 0 for a in range(wl.max_loras)]
+        _device_ranked_vs_plain(wl, ranks, label=f"{wl.name}, device plan")
+    big = W.config_bgmv_decode(seed=6, T=2304, K=1032, O=776, n_adapters=6, rank=16)
+    _device_ranked_vs_plain(big, [16] * 6, R=64, label="large decode rank 16 in pool rank 64")
+    # values outside [0, max_lora_rank] act as the pool's rank
+    _device_ranked_vs_plain(big, [999, -3, 16, 0, 64, 16], R=64, label="out-of-range ranks")
