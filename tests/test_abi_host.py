@@ -346,3 +346,14 @@ def test_apply_device_validation_before_hip():
     assert st(*([big] + ok[1:])) == _lib.LORA_E_SHAPE
     with pytest.raises(L.LoraError):
         L.lora_apply_device_workspace_bytes(big, 10)
+
+    # the ranked form runs the same checks (its rank table is device memory)
+    def st_r(*a):
+        try:
+            L.lora_apply_device_ranked(*a[:9], FAKE, *a[9:], stream=0)
+            return 0
+        except L.LoraError as e:
+            return e.status
+    assert st_r(*with_(10, need - 1)) == _lib.LORA_E_WORKSPACE
+    assert st_r(*with_(6, None)) == _lib.LORA_E_ARG
+    assert st_r(*with_(5, 0)) == 0
