@@ -115,7 +115,9 @@ int32_t run_plan_onepass_list(const Geo& g, const void* x, const void* A, const 
 int32_t run_plan_apply(const Geo& g, const void* x, const void* A, const void* B, void* y,
                        const TilePlan& p, float* v, hipStream_t st);
 // Outputs of a device-built plan (lora_apply_device): cap 8-row tile records,
-// mcap 64-row MFMA tile records and the v-row -> token map perm[T].  A slot's
+// mcap 64-row MFMA tile records and the v-row -> token map perm[T] (written
+// during placement; entries past the batch's rows are left as they were and
+// no record reaches them).  A slot's
 // SGMV rows take MFMA tiles when there are at least mfma_min of them; its BGMV
 // rows when there are at least bgmv_min of them and such runs hold at least
 // bgmv_total rows of the batch (values above T disable either).  Records past

@@ -35,6 +35,19 @@ constexpr int kParMaxLoras = 256;
 // barriers cost more than the single wavefront's chain).
 constexpr int kParMinRows = 1024;
 
+// bins[key] += 1 for every active lane with key >= 0.  Sorted batches give
+// whole wavefronts of one key, whose atomics on one LDS word would serialize:
+// then the first lane adds the count once.
+__device__ __forceinline__ void count_keys(int32_t* bins, int key) {
+  const uint64_t active = __ballot(true);
+  const int k0 = __builtin_amdgcn_readlane(key, __builtin_ctzll(active));
+  if (k0 >= 0 && __ballot(key == k0) == active) {
+    if ((int)(threadIdx.x & 63) == __builtin_ctzll(active)) atomicAdd(&bins[k0], __popcll(active));
+  } else if (key >= 0) {
+    atomicAdd(&bins[key], 1);
+  }
+}
+
 __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ prefill, int32_t T,
     int32_t max_loras, int32_t all_sgmv, lora_meta m, int32_t* __restrict__ counts,
@@ -64,12 +77,9 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     const bool ok = a >= 0 && a < max_loras;
     const bool sg = ok && (all_sgmv || (prefill && prefill[t]));
     if (one_block) keys[t] = (int16_t)(ok ? 2 * a + (sg ? 1 : 0) : -1);
-    if (a < -1 || a >= max_loras) {
-      atomicAdd(&s_bad, 1);
-      continue;
-    }
-    if (a < 0) continue;
-    atomicAdd(sg ? &cs[a] : &cb[a], 1);
+    if (a < -1 || a >= max_loras) atomicAdd(&s_bad, 1);
+    // cs and cb are adjacent: bin max_loras + a is cb[a]
+    count_keys(cs, ok ? (sg ? a : max_loras + a) : -1);
   }
   __syncthreads();
 
@@ -170,10 +180,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       const int sb = ((nbk + nw - 1) / nw + 63) / 64 * 64;
       lo = min(nbk, wave * sb);
       hi = min(nbk, lo + sb);
-      for (int i = lo + lane; i < hi; i += 64) {
-        const int key = keys[i];
-        if (key >= 0) atomicAdd(&my[key], 1);
-      }
+      for (int i = lo + lane; i < hi; i += 64) count_keys(my, keys[i]);
       __syncthreads();
       for (int k = tid; k < nkeys; k += kMetaThreads) {
         int32_t* pos = (k & 1) ? &cs[k >> 1] : &cb[k >> 1];
@@ -218,6 +225,9 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
           m.bgmv_tok[p] = t;
           m.bgmv_ids[p] = key >> 1;
         }
+        // the device plan's v-row -> token map: SGMV rows, then BGMV rows
+        const int vr = (key & 1) ? p : ns + p;
+        if (plan.perm && vr < T) plan.perm[vr] = t;
       }
       if (first) *pos = p0 + cnt;
     }
@@ -385,8 +395,6 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     r[2] = vrow;
     r[3] = tok0;
   }
-  for (int i = tid; i < T; i += kMetaThreads)
-    plan.perm[i] = i < ns ? m.sgmv_perm[i] : i < ns + nb ? m.bgmv_tok[i - ns] : 0;
 }
 
 int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
