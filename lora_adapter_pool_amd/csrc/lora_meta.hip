@@ -384,10 +384,10 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
         vrow = ns + first;
         src = m.bgmv_tok + first;
       }
+      // a slot's rows of one set are in increasing token order (the sort is
+      // stable), so they are consecutive exactly when last - first = rows - 1
       const int t0 = src[0];
-      bool consecutive = true;
-      for (int i = 1; i < rows; ++i) consecutive &= src[i] == t0 + i;
-      tok0 = consecutive ? t0 : -1;
+      tok0 = src[rows - 1] - t0 == rows - 1 ? t0 : -1;
     }
     int32_t* r = plan.mtiles + (size_t)f * LORA_PLAN_MFMA_WORDS;
     r[0] = slot;
