@@ -502,7 +502,32 @@ def device_plan_leg(s, steps, stream_ptr):
     for i in range(steps):
         step(5 + i)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e6
+    step_us = (time.perf_counter() - t0) / steps * 1e6
+    # the metadata builder alone on the same batch (HIP events)
+    T, ML = s.T, s.wl.max_loras
+    meta = {k: torch.zeros(max(T if k in ("sgmv_perm", "bgmv_tok", "bgmv_ids") else ML, 1),
+                           dtype=torch.int32, device="cuda")
+            for k in ("sgmv_perm", "seg_starts", "seg_lens", "seg_ids", "bgmv_tok", "bgmv_ids")}
+    m = L._lib.lora_meta()
+    for k, t in meta.items():
+        setattr(m, k, ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32)))
+    counts = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def build():
+        if lib.lora_build_meta_device(ids_d.data_ptr(), pre_d.data_ptr(), T, ML,
+                                      s.wl.max_lora_rank, 0, ctypes.byref(m), counts.data_ptr(),
+                                      stream_ptr):
+            raise RuntimeError(f"lora_build_meta_device failed: {L.last_error()}")
+
+    for _ in range(3):
+        build()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        build()
+    e1.record()
+    torch.cuda.synchronize()
+    return step_us, e0.elapsed_time(e1) * 1e3 / 20
 
 
 def slot_load_leg(seed):
@@ -893,9 +918,11 @@ def main():
         for k, r in pk2.items():
             log(f"[bench] prefill {k}: {r['us']:.2f} us/launch, {r['GBs']:.0f} GB/s, "
                 f"{r['TFLOPs']:.1f} TFLOP/s")
-        dp = device_plan_leg(s2[0], max(20, args.steps // 10), stream_ptr)
+        dp, db = device_plan_leg(s2[0], max(20, args.steps // 10), stream_ptr)
         out["secondary"]["device_plan_step_us"] = round(dp, 2)
-        log(f"[bench] prefill from device ids (lora_apply_device): {dp:.1f} us/step")
+        out["secondary"]["device_builder_us"] = round(db, 2)
+        log(f"[bench] prefill from device ids (lora_apply_device): {dp:.1f} us/step, "
+            f"builder alone {db:.1f} us")
         del s2
         torch.cuda.empty_cache()
         # the same batch with each slot's true rank (lora_apply_ranked): the
