@@ -399,9 +399,13 @@ def slot_residency(batches: Sequence[Sequence[Optional[int]]], max_loras: int) -
 # What pins each function (tests/test_oracle_pins.py):
 PINS = {
     "scaling": "closed-form values (alpha/r, alpha/sqrt(r)); rsLoRA vs standard ratio",
-    "lora_forward_rows": "brute force; merged-weight closed form; hand worked example; "
-                         "B=0 and id=-1 invariants; linearity; permutation equivariance",
-    "lora_shrink_rows": "equals A x by brute force; zero beyond the adapter rank",
+    "slice_offsets": "hand-worked three-slice example of widths 2, 1, 3 "
+                     "(tests/golden/delta_slices_hand.json)",
+    "lora_forward_rows": "brute force; merged-weight closed form; hand worked examples "
+                         "(one slice; three slices of different widths); B=0 and id=-1 "
+                         "invariants; linearity; permutation equivariance",
+    "lora_shrink_rows": "equals A x by brute force; zero beyond the adapter rank; "
+                        "slice-by-slice layout from the three-slice hand example",
     "brute_force_rows": "hand worked example (tests/golden/delta_hand.json)",
     "merged_weight_rows": "hand worked example; agrees with lora_forward_rows",
     "f32_to_bf16_rne": "torch's float32 -> bfloat16 cast (a library routine), ties",

@@ -52,6 +52,46 @@ def pin_hand_example(O):
     assert np.array_equal(m[0], np.asarray(g["merged_t0"], np.float64)), m
 
 
+def slices_hand_workload(rslora_slot1=True, R=4):
+    g = _load("delta_slices_hand.json")
+    slots = {}
+    for k, s in g["slots"].items():
+        slots[int(k)] = W.AdapterSpec(
+            rank=s["rank"], alpha=s["alpha"],
+            use_rslora=(s["use_rslora"] if int(k) != 1 else rslora_slot1),
+            A=[np.asarray(a, np.float32) for a in s["A"]],
+            B=[np.asarray(b, np.float32) for b in s["B"]])
+    T = len(g["ids"])
+    return W.Workload("hand_slices", "f32", g["in_features"], g["out_features"], 2, R, slots,
+                      np.asarray(g["ids"], np.int32), np.zeros(T, np.uint8),
+                      np.asarray(g["x"], np.float32), np.asarray(g["y_in"], np.float32)), g
+
+
+def pin_slices_hand_example(O):
+    """Three output slices of widths 2, 1, 3, each with its own A and B: the
+    placement of every slice's delta in the fused output row is fixed by the
+    hand-worked values, so a reversed, shifted or collapsed slice layout, or
+    one slice's A used for another, fails here."""
+    wl, g = slices_hand_workload()
+    assert list(O.slice_offsets(wl.out_features)) == g["slice_offsets"]
+    want = np.asarray(g["y_out"], np.float64)
+    assert np.array_equal(O.lora_forward_rows(wl), want)
+    assert np.array_equal(np.asarray(O.brute_force_rows(wl, range(wl.T))), want)
+    wl2, _ = slices_hand_workload(rslora_slot1=False)
+    assert np.array_equal(O.lora_forward_rows(wl2, rows=[2])[0],
+                          np.asarray(g["y_out_t2_without_rslora"], np.float64))
+    # the padded, folded pool gives the same rows (scales 2 and 1 fold exactly)
+    pool = O.expected_pool(wl)
+    assert np.array_equal(O.forward_from_pool_rows(wl, pool, range(wl.T)), want)
+    # merging into a zero base weight leaves exactly the delta
+    d = O.merged_weight_rows(np.zeros((wl.O, wl.in_features)), wl, [0, 2, 3])
+    assert np.array_equal(d, want[[0, 2, 3]] - wl.y_in[[0, 2, 3]].astype(np.float64))
+    # the rank-space intermediate is laid out slice by slice, R values each:
+    # t0 (slot 0, rank 2): A_s x = [1, 2], [3, -1], [2, 2]
+    v = O.lora_shrink_rows(wl, [0, 1])
+    assert np.array_equal(v[0], [1, 2, 0, 0, 3, -1, 0, 0, 2, 2, 0, 0]) and not np.any(v[1])
+
+
 def pin_scaling(O):
     # alpha / r and alpha / sqrt(r); the values used by the named workloads
     assert O.scaling(8, 16.0, False) == 2.0

@@ -100,6 +100,50 @@ def _rne_trunc(a):
     return (a32.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
 
 
+def _offsets_reversed(out_features):
+    # slices laid out last to first (the last slice's delta in the first columns)
+    outs = [int(o) for o in out_features]
+    offs, acc = [0] * len(outs), 0
+    for i in reversed(range(len(outs))):
+        offs[i] = acc
+        acc += outs[i]
+    return offs
+
+
+def _offsets_all_zero(out_features):
+    return [0] * len(list(out_features))
+
+
+def _offsets_inclusive(out_features):
+    # each slice starts after its own width (an off-by-one in the prefix sum),
+    # clamped so the last slice still fits the row
+    outs = [int(o) for o in out_features]
+    total = sum(outs)
+    offs, acc = [], 0
+    for o in outs:
+        acc += o
+        offs.append(min(acc, total - o))
+    return offs
+
+
+def _forward_slice_A_rotated(wl, rows=None, y_in=None):
+    # each slice uses the next slice's A (shapes agree: [rank, in_features])
+    slots = {a: type(ad)(**{**ad.__dict__, "A": ad.A[1:] + ad.A[:1]}) for a, ad in wl.slots.items()}
+    wl2 = type(wl)(**{**wl.__dict__, "slots": slots})
+    return _ORIG_FORWARD(wl2, rows, y_in=y_in)
+
+
+def _shrink_rank_major(wl, rows):
+    # v laid out rank by rank (k * S + s) instead of slice by slice (s * R + k)
+    v = _ORIG_SHRINK(wl, rows)
+    R, S = wl.max_lora_rank, wl.num_slices
+    return v.reshape(v.shape[0], S, R).transpose(0, 2, 1).reshape(v.shape[0], S * R)
+
+
+_ORIG_FORWARD = O.lora_forward_rows
+_ORIG_SHRINK = O.lora_shrink_rows
+
+
 MUTATIONS = {
     "scale_padded_rank": ("scaling", mut_scale_padded_rank),
     "scale_no_sqrt": ("scaling", mut_scale_no_sqrt),
@@ -117,6 +161,11 @@ MUTATIONS = {
     "bf16_truncation": ("f32_to_bf16_rne", _rne_trunc),
     "bf16_double_rounding": ("f64_to_bf16_rne",
                              lambda a: O.f32_to_bf16_rne(np.asarray(a, np.float32)).astype(np.float64)),
+    "slices_reversed": ("slice_offsets", _offsets_reversed),
+    "slices_all_at_column_0": ("slice_offsets", _offsets_all_zero),
+    "slices_offset_by_own_width": ("slice_offsets", _offsets_inclusive),
+    "slice_A_rotated": ("lora_forward_rows", _forward_slice_A_rotated),
+    "shrink_rank_major_layout": ("lora_shrink_rows", _shrink_rank_major),
     "merge_sign": ("merged_weight",
                    lambda W, ps, sl, dt: np.asarray(W, np.float64) - ps["B"][sl] @ ps["A"][sl]),
     "merge_wrong_slice": ("merged_weight",
