@@ -37,7 +37,7 @@ def common_flags():
 def device_flags():
     # packed fp32 VALU forms stay off: every fp32 op is a plain scalar instruction
     return [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-            "-packed-fp32-ops", "-munsafe-fp-atomics"]
+            "-packed-fp32-ops"]
 
 
 def build_library(verbose: bool = False, jobs: int = 3) -> str:

@@ -146,13 +146,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 // read in parallel, one segment per thread per pass, and a block-wide prefix
 // sum of tile counts finds the segment holding tile f, so the lookup costs one
 // memory round trip rather than one per segment.  Returns false (uniformly)
-// past the last tile; the results are the same in every lane.
+// past the last tile; the results are the same in every lane.  The barrier at
+// entry keeps the reset of s_found from racing with waves that still read the
+// result of an earlier call, so a workgroup may call it more than once.
 template <int TM>
 __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int& cnt, int& sid) {
   __shared__ int s_found[4];
   __shared__ int s_wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nthr = blockDim.x, nw = nthr >> 6;
+  __syncthreads();
   if (tid == 0) s_found[3] = 0;
   int base = 0;
   bool found = false;
@@ -300,7 +303,10 @@ __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
       if (r0 >= L.num_rows) return false;
       cnt = min(TM, L.num_rows - r0);
     }
-    const int ri = r0 + min(lane, max(cnt, 1) - 1);
+    // r0 + cnt <= num_rows by construction (find_tile clamps segments to the
+    // row count; rows mode stops at it); the clamp keeps the load in bounds
+    // whatever the metadata holds.
+    const int ri = max(0, min(r0 + min(lane, max(cnt, 1) - 1), L.num_rows - 1));
     const int tv = L.tok[ri];
     const int av = MODE == kRows ? L.ids[ri] : sid;
     tr.cnt = cnt;

@@ -95,17 +95,48 @@ def plan_v(plan, S, R, fill=0.0):
     return torch.full((parts * max(rows, 1), S * R), fill, dtype=torch.float32, device="cuda")
 
 
-def sample_rows(wl, n=64, seed=0):
-    """Rows for full-size checks: first/last row of every adapter run plus random
-    rows (active and none)."""
-    rng = np.random.default_rng(seed)
-    ids = wl.ids
-    edges = [0, wl.T - 1]
-    change = np.where(np.diff(ids) != 0)[0]
-    edges += change.tolist() + (change + 1).tolist()
-    rows = set(int(r) for r in edges[: n // 2])
-    rows.update(int(r) for r in rng.choice(wl.T, size=min(wl.T, n), replace=False))
-    return sorted(rows)[: max(n, 8)]
+_ORACLE_CACHE = {}
+
+
+def _digest(wl):
+    import hashlib
+    h = hashlib.blake2b(digest_size=16)
+    for a in (wl.ids, wl.x, wl.y_in):
+        h.update(np.ascontiguousarray(a).tobytes())
+    for a in sorted(wl.slots):
+        ad = wl.slots[a]
+        h.update(repr((a, ad.rank, ad.alpha, ad.use_rslora)).encode())
+        for m in list(ad.A) + list(ad.B):
+            h.update(np.ascontiguousarray(m).tobytes())
+    return (wl.dtype, tuple(wl.out_features), h.hexdigest())
+
+
+def oracle_rows(wl, rows):
+    """The fp64 oracle on `rows`; the result for a whole workload is kept, so
+    tests that check the same batch (the same inputs) compute it once."""
+    key = _digest(wl)
+    full = _ORACLE_CACHE.get(key)
+    if full is None and len(rows) == wl.T:
+        full = oracle.lora_forward_rows(wl)
+        _ORACLE_CACHE.clear()       # one full-size batch at a time (memory)
+        _ORACLE_CACHE[key] = full
+    if full is not None:
+        return full[np.asarray(rows, np.int64)]
+    return oracle.lora_forward_rows(wl, rows)
+
+
+def zero_y(wl):
+    """The same batch with y_in = 0: y_out is then the delta alone, rounded once
+    to the dtype, so the tolerance measures the delta itself."""
+    import dataclasses
+    return dataclasses.replace(wl, y_in=np.zeros_like(wl.y_in), name=wl.name + "_y0")
+
+
+# Delta-only bar for bf16 outputs with y_in = 0: the one rounding of the
+# output is at most 2^-9 of each element, and the fp32 sums (and the hi + lo
+# bf16 pair that carries v into the MFMA expands, about 2^-17 of v) add far
+# less, so 2^-8 leaves a factor two over the rounding alone.
+DELTA_TOL_BF16 = 2.0 ** -8
 
 
 def check_rows(wl, y_gpu, rows=None, tol=None, label=""):
@@ -114,7 +145,7 @@ def check_rows(wl, y_gpu, rows=None, tol=None, label=""):
     rows = list(range(wl.T)) if rows is None else list(rows)
     idx = torch.as_tensor(rows, dtype=torch.long, device=y_gpu.device)
     yg = y_to_np(y_gpu.index_select(0, idx))
-    ref = oracle.lora_forward_rows(wl, rows)
+    ref = oracle_rows(wl, rows)
     act = np.asarray([wl.ids[r] >= 0 for r in rows])
     tol = TOL[wl.dtype] if tol is None else tol
     err = oracle.rel_err_rows(yg[act], ref[act]) if act.any() else 0.0

@@ -12,7 +12,7 @@ import pytest
 import lora_adapter_pool_amd as L
 import oracle
 import workloads as W
-from gpu_helpers import check_rows, make_pool, sample_rows, say, to_dev
+from gpu_helpers import check_rows, make_pool, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -54,9 +54,15 @@ def test_device_plan_qkv_decode_full():
     check_rows(wl, _run(wl), label="fused qkv decode, device plan")
 
 
-def test_device_plan_prefill_sampled():
+def test_device_plan_prefill_full():
     wl = W.config_sgmv_prefill(seed=0)
-    check_rows(wl, _run(wl), rows=sample_rows(wl, 64), label="sgmv prefill, device plan")
+    check_rows(wl, _run(wl), label="sgmv prefill, device plan (all rows)")
+
+
+def test_device_plan_mlp_mixed_full():
+    gu, dn = W.config_mlp_mixed(seed=0)
+    for wl in (gu, dn):
+        check_rows(wl, _run(wl), label=f"{wl.name}, device plan (all rows)")
 
 
 def test_device_plan_mixed_small():
