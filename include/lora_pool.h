@@ -455,6 +455,32 @@ int32_t lora_apply_device_ranked(const lora_pool_desc* desc, const void* A_pool,
                                  int32_t bgmv_max_rank, const int32_t* slot_ranks, void* ws,
                                  int64_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * path and result as lora_apply_device (bit for bit: the same kernels, plan
+ * and K splits), but the workspace is the library's own: a file-scope device
+ * array of LORA_NOALLOC_SCRATCH_BYTES bytes per GPU, created with the
+ * library's code object the first time the library runs on that GPU and held
+ * until the process ends.  The call allocates and frees nothing (no
+ * hipMalloc, no allocating library routine); the caller passes the pool, x, y,
+ * ids and prefill as for lora_apply_device.
+ *   Size limit: a batch whose lora_apply_device_workspace_bytes(desc, T)
+ *   exceeds LORA_NOALLOC_SCRATCH_BYTES is rejected with LORA_E_WORKSPACE
+ *   before any HIP call (for S * R = 16 that is about 130 000 rows, for
+ *   S * R = 128 about 16 000).
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ *   previous call's contents; nothing in it needs clearing (each call writes
+ *   every byte it reads before reading it).  Calls on one stream are ordered
+ *   and safe; calls that overlap on one GPU (other streams, other threads)
+ *   race on the array and give undefined results.
+ *   Errors: as lora_apply_device, plus LORA_E_WORKSPACE for the size limit and
+ *   LORA_E_HIP if the array's address cannot be obtained.  T = 0 is a no-op. */
+#define LORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int32_t lora_apply_device_noalloc(const lora_pool_desc* desc, const void* A_pool,
+                                  const void* B_pool, const void* x, void* y, int32_t T,
+                                  const int32_t* ids, const uint8_t* prefill,
+                                  int32_t bgmv_max_rank, void* stream);
+
 /* lora_apply with each slot's true rank (slot_ranks as in
  * lora_apply_plan_ranked, nullable): same result, padded ranks skipped. */
 int32_t lora_apply_ranked(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,

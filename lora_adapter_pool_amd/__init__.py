@@ -5,7 +5,8 @@ C ABI (include/lora_pool.h), with a thin ctypes binding.
 """
 from ._lib import (  # noqa: F401
     LORA_BF16, LORA_F32, LoraError, lib, make_desc, lora_apply, lora_apply_host_meta_bytes,
-    lora_apply_device, lora_apply_device_ranked, lora_apply_device_workspace_bytes,
+    lora_apply_device, lora_apply_device_noalloc, lora_apply_device_ranked,
+    lora_apply_device_workspace_bytes, NOALLOC_SCRATCH_BYTES,
     lora_apply_plan, lora_apply_ranked,
     lora_merge_weights, lora_plan_apply, lora_plan_expand, lora_plan_shrink, plan_struct,
     lora_apply_workspace_bytes, lora_bgmv_expand, lora_bgmv_shrink, lora_build_meta,

@@ -115,6 +115,7 @@ _SIGNATURES = {
     "lora_apply_device": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _I64, _P]),
     "lora_apply_device_ranked": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64,
                                         _P]),
+    "lora_apply_device_noalloc": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P]),
     "lora_merge_weights": (_I32, [_DP, _P, _P, _I32, _I32, _P, _P, _P]),
     "lora_apply_ranked": (_I32, [_DP, _P, _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P, _I64,
                                  _P]),
@@ -410,6 +411,19 @@ def lora_apply_device(desc, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank
     _check(lib().lora_apply_device(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), _ptr(x),
                                    _ptr(y), int(T), _ptr(ids), _ptr(prefill), int(bgmv_max_rank),
                                    _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # LORA_NOALLOC_SCRATCH_BYTES
+
+
+def lora_apply_device_noalloc(desc, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank,
+                              stream=None):
+    """lora_apply_device with the library's own per-GPU scratch as workspace:
+    allocates nothing; batches needing more than NOALLOC_SCRATCH_BYTES are
+    rejected.  Calls that overlap on one GPU race on the scratch."""
+    _check(lib().lora_apply_device_noalloc(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool),
+                                           _ptr(x), _ptr(y), int(T), _ptr(ids), _ptr(prefill),
+                                           int(bgmv_max_rank), _stream(stream)))
 
 
 def lora_apply_device_ranked(desc, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank,

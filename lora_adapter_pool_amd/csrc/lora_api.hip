@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "lora_internal.h"
@@ -371,33 +372,44 @@ int32_t lora_apply_device(const lora_pool_desc* desc, const void* A_pool, const 
                                   nullptr, ws, ws_bytes, stream);
 }
 
-int32_t lora_apply_device_ranked(const lora_pool_desc* desc, const void* A_pool,
-                                 const void* B_pool, const void* x, void* y, int32_t T,
-                                 const int32_t* ids, const uint8_t* prefill,
-                                 int32_t bgmv_max_rank, const int32_t* slot_ranks, void* ws,
-                                 int64_t ws_bytes, void* stream) {
-  clear_error();
-  Geo g;
-  if (int32_t e = check_desc(desc, &g)) return e;
+}  // extern "C"
+
+namespace {
+
+// Checks of lora_apply_device's arguments other than the workspace; fills g
+// (g.T = T).  Sets *noop for an empty batch.  No HIP call.
+int32_t device_args(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,
+                    const void* x, const void* y, int32_t T, const int32_t* ids, Geo* g,
+                    bool* noop) {
+  *noop = false;
+  if (int32_t e = check_desc(desc, g)) return e;
   if (T < 0) return fail(LORA_E_ARG, "T must be >= 0, got %d", T);
-  if (g.max_loras > LORA_META_DEVICE_MAX_LORAS)
+  if (g->max_loras > LORA_META_DEVICE_MAX_LORAS)
     return fail(LORA_E_SHAPE, "max_loras must be <= %d for the device plan, got %d",
-                LORA_META_DEVICE_MAX_LORAS, g.max_loras);
-  if (T == 0) return LORA_OK;
+                LORA_META_DEVICE_MAX_LORAS, g->max_loras);
+  if (T == 0) {
+    *noop = true;
+    return LORA_OK;
+  }
   if (int32_t e = need_ptr(A_pool, "A_pool")) return e;
   if (int32_t e = need_ptr(B_pool, "B_pool")) return e;
   if (int32_t e = need_ptr(x, "x")) return e;
   if (int32_t e = need_ptr(y, "y")) return e;
   if (int32_t e = need_ptr(ids, "ids")) return e;
-  if (int32_t e = need_ptr(ws, "ws")) return e;
-  if (!aligned16(x) || !aligned16(y) || !aligned16(A_pool) || !aligned16(B_pool) ||
-      ((uintptr_t)ws & 255u))
-    return fail(LORA_E_ALIGN, "x, y and the pool must be 16-byte aligned, ws 256-byte aligned");
-  g.T = T;
+  g->T = T;
+  return LORA_OK;
+}
+
+// lora_apply_device on validated arguments and a workspace of at least
+// device_layout(g, T).total bytes at `ws` (256-byte aligned).  Every byte of
+// the workspace the kernels read is written earlier in the same call (the
+// builder writes the metadata and every tile record up to the capacities, the
+// shrink every v row the expand reads), so it needs no clearing between calls.
+int32_t apply_device_run(const Geo& g, const void* A_pool, const void* B_pool, const void* x,
+                         void* y, int32_t T, const int32_t* ids, const uint8_t* prefill,
+                         int32_t bgmv_max_rank, const int32_t* slot_ranks, void* ws,
+                         hipStream_t st) {
   const DeviceLayout d = device_layout(g, T);
-  if (ws_bytes < d.total)
-    return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
-                (long long)d.total);
   char* w = (char*)ws;
   lora_meta m;
   m.num_sgmv_rows = m.num_segs = m.num_bgmv_rows = m.reserved = 0;
@@ -411,7 +423,6 @@ int32_t lora_apply_device_ranked(const lora_pool_desc* desc, const void* A_pool,
   int32_t* tiles = (int32_t*)(w + d.tiles);
   int32_t* mtiles = (int32_t*)(w + d.mtiles);
   int32_t* perm = (int32_t*)(w + d.perm);
-  hipStream_t st = (hipStream_t)stream;
   const int32_t limit = bgmv_max_rank > 0 ? bgmv_max_rank : LORA_BGMV_MAX_RANK_DEFAULT;
   // the plan's shape is known on the host only as capacities: cap 8-row
   // records and mcap 64-row records (surplus ones have 0 rows), T v rows.
@@ -441,6 +452,86 @@ int32_t lora_apply_device_ranked(const lora_pool_desc* desc, const void* A_pool,
   float* v = (float*)(w + d.v);
   if (int32_t e = run_plan_shrink(g, x, A_pool, v, tp, st)) return e;
   return run_plan_expand(g, v, B_pool, y, tp, st);
+}
+
+// Workspace of lora_apply_device_noalloc: one array per GPU, allocated with
+// the code object when the library is first used on that GPU and held until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on
+// the host that name is a stand-in, not a device address): it uses the
+// address hipGetSymbolAddress returns, looked up once per device with that
+// device current and kept in scratch_addr.
+__device__ __align__(256) unsigned char scratch[LORA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+int32_t scratch_addr(void** out) {
+  int dev = -1;
+  if (int32_t e = hip_ok(hipGetDevice(&dev), "hipGetDevice")) return e;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LORA_E_ARG, "device %d is outside the %d devices the scratch table covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (int32_t e = hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address"))
+      return e;
+    if (!p || ((uintptr_t)p & 255u))
+      return fail(LORA_E_HIP, "scratch address %p is not 256-byte aligned", p);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_apply_device_ranked(const lora_pool_desc* desc, const void* A_pool,
+                                 const void* B_pool, const void* x, void* y, int32_t T,
+                                 const int32_t* ids, const uint8_t* prefill,
+                                 int32_t bgmv_max_rank, const int32_t* slot_ranks, void* ws,
+                                 int64_t ws_bytes, void* stream) {
+  clear_error();
+  Geo g;
+  bool noop;
+  if (int32_t e = device_args(desc, A_pool, B_pool, x, y, T, ids, &g, &noop)) return e;
+  if (noop) return LORA_OK;
+  if (int32_t e = need_ptr(ws, "ws")) return e;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(A_pool) || !aligned16(B_pool) ||
+      ((uintptr_t)ws & 255u))
+    return fail(LORA_E_ALIGN, "x, y and the pool must be 16-byte aligned, ws 256-byte aligned");
+  const DeviceLayout d = device_layout(g, T);
+  if (ws_bytes < d.total)
+    return fail(LORA_E_WORKSPACE, "workspace has %lld bytes, needs %lld", (long long)ws_bytes,
+                (long long)d.total);
+  return apply_device_run(g, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank, slot_ranks,
+                          ws, (hipStream_t)stream);
+}
+
+int32_t lora_apply_device_noalloc(const lora_pool_desc* desc, const void* A_pool,
+                                  const void* B_pool, const void* x, void* y, int32_t T,
+                                  const int32_t* ids, const uint8_t* prefill,
+                                  int32_t bgmv_max_rank, void* stream) {
+  clear_error();
+  Geo g;
+  bool noop;
+  if (int32_t e = device_args(desc, A_pool, B_pool, x, y, T, ids, &g, &noop)) return e;
+  if (noop) return LORA_OK;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(A_pool) || !aligned16(B_pool))
+    return fail(LORA_E_ALIGN, "x, y and the pool must be 16-byte aligned");
+  const DeviceLayout d = device_layout(g, T);
+  if (d.total > (int64_t)LORA_NOALLOC_SCRATCH_BYTES)
+    return fail(LORA_E_WORKSPACE,
+                "the batch needs %lld bytes of workspace; the no-alloc scratch holds %lld "
+                "(use lora_apply_device with a workspace of the caller's)",
+                (long long)d.total, (long long)LORA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int32_t e = scratch_addr(&ws)) return e;
+  return apply_device_run(g, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank, nullptr, ws,
+                          (hipStream_t)stream);
 }
 
 int32_t lora_apply_ranked(const lora_pool_desc* desc, const void* A_pool, const void* B_pool,

@@ -357,3 +357,39 @@ def test_apply_device_validation_before_hip():
     assert st_r(*with_(10, need - 1)) == _lib.LORA_E_WORKSPACE
     assert st_r(*with_(6, None)) == _lib.LORA_E_ARG
     assert st_r(*with_(5, 0)) == 0
+
+
+def test_apply_device_noalloc_validation_before_hip():
+    """lora_apply_device_noalloc: a batch whose workspace exceeds the library's
+    scratch is rejected, and every argument is checked, before any GPU call."""
+    d = L.make_desc("bf16", 32, 64, 4096, [14336, 14336])      # S * R = 128
+    ok = [d, FAKE, FAKE, FAKE, FAKE + 4096, 100, FAKE, None, 0]
+
+    def st(*a):
+        try:
+            L.lora_apply_device_noalloc(*a, stream=0)
+            return 0
+        except L.LoraError as e:
+            return e.status
+    # the largest T that fits the scratch, found from the documented size
+    lo, hi = 1, 1 << 20
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if L.lora_apply_device_workspace_bytes(d, mid) <= L.NOALLOC_SCRATCH_BYTES:
+            lo = mid
+        else:
+            hi = mid - 1
+    assert 15000 < lo < 17000                     # about 16 000 rows at S * R = 128
+    big = list(ok)
+    big[5] = lo + 1
+    assert st(*big) == _lib.LORA_E_WORKSPACE
+    assert "scratch" in L.last_error()
+    for i, v in ((6, None), (1, None), (3, FAKE + 2), (5, -1)):
+        a = list(ok)
+        a[i] = v
+        assert st(*a) in (_lib.LORA_E_ARG, _lib.LORA_E_ALIGN)
+    a = list(ok)
+    a[5] = 0
+    assert st(*a) == 0                           # T = 0: no-op
+    big_pool = L.make_desc("bf16", 8193, 16, 256, [256])
+    assert st(*([big_pool] + ok[1:])) == _lib.LORA_E_SHAPE
