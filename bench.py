@@ -658,7 +658,7 @@ def stage_kernels(wl):
     if p["mfma_tiles"]:
         out["shrink"].append("shrink_mfma_kernel<2>")
         chunks = wl.max_lora_rank <= 64 and wl.T * wl.O * 2 < 2 ** 31
-        out["expand"].append("expand_mfma_chunks_kernel<2>" if chunks else "expand_mfma_kernel<2>")
+        out["expand"].append("expand_mfma_rows_kernel<2>" if chunks else "expand_mfma_kernel<2>")
     if p["wave_tiles"]:
         # modes 3 / 4: records in the kernel arguments (up to 12 / 48 tiles),
         # 2: device image

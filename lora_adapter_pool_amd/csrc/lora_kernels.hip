@@ -59,6 +59,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Streaming (non-temporal) forms for data a kernel touches once: the x rows
+// of a long segment, y rows of a read-modify-write.  On MI355X they sustain
+// about a tenth more HBM bandwidth than the default cache policy (6.9 against
+// 6.2 TB/s streaming reads, 6.0 against 5.4 TB/s in-place updates).
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // All-ones or all-zeros, to zero a loaded value with a bit-AND: a select on a
 // loaded value lets the compiler sink the load under a branch, after which it
@@ -76,6 +83,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, uint32_t
 constexpr uint32_t kDropOffset = 0x80000000u;  // past every buffer made by make_rsrc
 __device__ __forceinline__ void st16_buf(u32x4 val, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(val, r, (int)off, 0, 0);
+}
+// the same store with the non-temporal cache policy (aux bit 1)
+__device__ __forceinline__ void st16_buf_nt(u32x4 val, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(val, r, (int)off, 0, 2);
+}
+// 16-byte loads through a raw buffer: a 32-bit offset per lane instead of a
+// 64-bit address (fewer registers); the caller keeps every offset in bounds
+__device__ __forceinline__ u32x4 ld16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x4 ld16_buf_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
 }
 
 // Element access: 8 consecutive elements travel as one Raw (16 bytes of bf16
@@ -1172,7 +1191,7 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
     const int kc = in ? kk : 0;
     const uint32_t km = all_or_none(in);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) r[j] = ld16(xp[j] + kc) & (km & xm[j]);
+    for (int j = 0; j < 2; ++j) r[j] = ld16_nt(xp[j] + kc) & (km & xm[j]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) r[2 + j] = ld16(ap[j] + kc) & (km & am[j]);
   };
@@ -1405,36 +1424,38 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
 //
 // bf16, pools of rank R <= 64.  A workgroup covers a group of up to `cpw`
 // consecutive column chunks of 128 columns of one slice of its tile
-// (gr.start[s] is the first group of slice s).  v (the sum of the shrink's
-// partials in fixed order, split into hi + lo bf16) is staged in LDS once for
-// the group; per chunk only the B tile [128 columns][R] goes through LDS
-// (coalesced 16-byte loads, 8 lanes per 128-byte row).  Wave w computes
-// D = Btile * v^T for tokens 16 w .. +16 as eight 16 x 16 tiles, two MFMAs (hi,
-// lo) per tile and 32-rank chunk; inside a pair of tiles, MFMA row n of tile 2q
-// maps to column 32 q + 8 (n / 4) + n % 4 and of tile 2q+1 to the same + 4, so
-// lane (g, m) ends with columns 32 q + 8 g .. +8 of token m.  The lane reads
-// and writes those 8 y values directly (16 bytes; four lanes cover 64
-// contiguous bytes of a row), so y never passes through LDS and the workgroup
-// needs 36 KB of LDS, four per compute unit.  The next chunk's B and y are
-// loaded while the current one is computed; y leaves through raw buffer
-// stores (y must span less than 2 GiB): lanes without a row store to a
-// dropped offset, so no store sits under a branch and the next chunk's loads
-// are not held up by the previous chunk's stores.
+// (gr.start[s] is the first group of slice s).  Wave w owns tokens 16 w .. +16
+// of the tile and computes D = v * Btile^T with v as the MFMA's first operand
+// (D rows = tokens) and the B tile as its second (D columns = output
+// columns): in MFMA tile nt (of 8 per chunk), D column j reads B column
+// 8 j + nt.  Lane (g, j) then holds, over the 8 tiles, columns 8 j .. 8 j + 8
+// of tokens 4 g .. 4 g + 4, so for each of its four tokens it reads and writes
+// 16 contiguous bytes of y, and the 16 lanes of one g cover 256 contiguous
+// bytes of one token's row: every y load and store instruction moves whole
+// 128-byte lines, with the streaming (non-temporal) cache policy.
+// v (the sum of the shrink's partials in fixed order, split into hi + lo bf16,
+// two MFMAs per tile and 32-rank chunk) stays in registers for the whole
+// group: lane (g, j) holds ranks 32 kc + 8 g .. +8 of token row 16 w + j.
+// The B tile [128 columns][R] goes through LDS once per chunk (coalesced
+// 16-byte loads, 8 lanes per 128-byte row); column c is stored at LDS row
+// (c % 8) * 16 + c / 8, so the 16 lanes reading columns 8 j + nt hit 16
+// consecutive padded rows and no two of them share a bank.  The next chunk's
+// B and y are loaded while the current one is computed; y leaves through raw
+// buffer stores (y must span less than 2 GiB): lanes without a row store to a
+// dropped offset, so no store sits under a branch.
 template <int MODE>
-__global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
+__global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
     const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
     RowList L, Geo g, Chunks ch, Chunks gr, int ksplit, int v_rows, int cpw) {
   constexpr int TM = kMfmaTileRows, NC = kExpandMfmaCols, KB = 64;
   constexpr int LDK = KB + 8;
   static_assert(TM == 64 && NC == 128, "64 tokens x 128 columns per chunk");
   __shared__ __align__(16) uint16_t bs[NC * LDK];
-  __shared__ __align__(16) uint16_t vh[TM * LDK];
-  __shared__ __align__(16) uint16_t vl[TM * LDK];
   __shared__ int s_tok[TM];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
-  const int m16 = lane & 15, grp = lane >> 4;
+  const int j16 = lane & 15, grp = lane >> 4;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / gr.total;
   const int gidx = bid - f * gr.total;
@@ -1457,122 +1478,140 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_chunks_kernel(
     const int tk = tok0 >= 0 ? tok0 + min(tid, cnt - 1) : L.tok[r0 + min(tid, cnt - 1)];
     s_tok[tid] = (tid < cnt && tk >= 0 && tk < g.T) ? tk : -1;
   }
-  __syncthreads();
-  // this lane's token (MFMA column m16 of wave w) and its y row
-  const int my_tok = s_tok[16 * wave + m16];
-  const uint16_t* yrow = y + (size_t)(my_tok >= 0 ? my_tok : 0) * g.O + g.off[s];
-  const size_t yrow_off = ((size_t)(my_tok >= 0 ? my_tok : 0) * g.O + g.off[s]) * sizeof(uint16_t);
-  // staging lanes: v row (t / 16) + 16 j with ranks 4 (t % 16) .. +4; B column
-  // (t / 8) + 32 j with ranks 8 (t % 8) .. +8
-  const int q16 = tid & 15, srow = tid >> 4;
-  const int b8 = tid & 7, bcol = tid >> 3;
-  // loads of chunk c: B (masked where written to LDS) and this lane's y
-  auto load_chunk = [&](int c, u32x4(&br)[4], uint32_t(&bm)[4], u32x4(&yr)[4]) {
-    const int col0 = (c - ch.start[s]) * NC;
-    const uint16_t* Bt = B + ((size_t)sid * g.O + g.off[s] + col0) * R;
-    const bool bk_ok = 8 * b8 < rr;  // ranks past the adapter's are zero: not loaded
+  // v operands: token row 16 wave + j16, ranks 32 kc + 8 grp .. +8 (kc < 2);
+  // the partials are summed in order 0, 1, ... (missing ones load as zeros)
+  bf16x8 vh[2], vl[2];
+  {
+    const int row = 16 * wave + j16;
+    const bool row_ok = row < cnt;
+    u32x4 vr[2][kMaxKsplit][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int cc = bcol + 32 * j;
-      const bool ok = bk_ok && col0 + cc < out_s;
-      br[j] = ld16(Bt + (size_t)(ok ? cc : 0) * R + (ok ? 8 * b8 : 0));
-      bm[j] = all_or_none(ok);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = col0 + 32 * q + 8 * grp;
-      yr[q] = ld16(yrow + (col < out_s ? col : 0));
-    }
-  };
-  u32x4 br[4], yn[4];
-  uint32_t bm[4];
-  load_chunk(c_begin, br, bm, yn);
-  {  // v: sum of the partials in fixed order, split into hi + lo, once per workgroup
-    u32x4 vr[4][kMaxKsplit];
-    const bool vk_ok = 4 * q16 < R;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = srow + 16 * j;
-      const bool ok = vk_ok && s_tok[row] >= 0;
+    for (int kc = 0; kc < 2; ++kc) {
+      const int k0 = 32 * kc + 8 * grp;
+      const bool ok = row_ok && k0 < rr;
       const uint32_t m = all_or_none(ok);
 #pragma unroll
       for (int p = 0; p < kMaxKsplit; ++p) {
         const bool pin = p < ksplit;
-        const size_t off = ((size_t)(pin ? p : 0) * v_rows + r0 + (ok ? row : 0)) * SR + s * R +
-                           (ok ? 4 * q16 : 0);
-        vr[j][p] = ld16(v + off) & (m & all_or_none(pin));
+        const size_t off =
+            ((size_t)(pin ? p : 0) * v_rows + r0 + (ok ? row : 0)) * SR + s * R + (ok ? k0 : 0);
+        const uint32_t mm = m & all_or_none(pin);
+        vr[kc][p][0] = ld16(v + off) & mm;
+        vr[kc][p][1] = ld16(v + off + 4) & mm;
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float e[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < 2; ++kc) {
+      float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < kMaxKsplit; ++p) {
-        e[0] += __uint_as_float(vr[j][p].x);
-        e[1] += __uint_as_float(vr[j][p].y);
-        e[2] += __uint_as_float(vr[j][p].z);
-        e[3] += __uint_as_float(vr[j][p].w);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          e[4 * h + 0] += __uint_as_float(vr[kc][p][h].x);
+          e[4 * h + 1] += __uint_as_float(vr[kc][p][h].y);
+          e[4 * h + 2] += __uint_as_float(vr[kc][p][h].z);
+          e[4 * h + 3] += __uint_as_float(vr[kc][p][h].w);
+        }
       }
-      uint32_t h[4], l[4];
+      uint32_t hw[4], lw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        h[i] = f32_to_bf16_bits(e[i]);
-        l[i] = f32_to_bf16_bits(e[i] - __uint_as_float(h[i] << 16));
+        const uint32_t h0 = f32_to_bf16_bits(e[2 * i]), h1 = f32_to_bf16_bits(e[2 * i + 1]);
+        const uint32_t l0 = f32_to_bf16_bits(e[2 * i] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_bits(e[2 * i + 1] - __uint_as_float(h1 << 16));
+        hw[i] = h0 | (h1 << 16);
+        lw[i] = l0 | (l1 << 16);
       }
-      const int vo = (srow + 16 * j) * LDK + 4 * q16;
-      *reinterpret_cast<u32x2*>(&vh[vo]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *reinterpret_cast<u32x2*>(&vl[vo]) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      vh[kc] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+      vl[kc] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
     }
   }
+  __syncthreads();  // s_tok
+  // this lane's four tokens (rows 16 wave + 4 grp + r): the byte offset of
+  // each one's y row in this slice (token 0's for a missing row, which only
+  // feeds loads), and bit r of tok_ok set for a real token; y spans less
+  // than 2 GiB, so 32-bit offsets suffice
+  uint32_t yo[4];
+  uint32_t tok_ok = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tk = s_tok[16 * wave + 4 * grp + r];
+    tok_ok |= (tk >= 0 ? 1u : 0u) << r;
+    yo[r] = (uint32_t)(((size_t)(tk >= 0 ? tk : 0) * g.O + g.off[s]) * sizeof(uint16_t));
+  }
+  // staging lanes: B column (t / 8) + 32 q with ranks 8 (t % 8) .. +8; ranks
+  // past the adapter's are zero: not loaded
+  const int b8 = tid & 7, bcol = tid >> 3;
+  const bool bk_ok = 8 * b8 < rr;
+  // loads of chunk c: B (zeroed where written to LDS) and this lane's y
+  auto load_chunk = [&](int c, u32x4(&br)[4], u32x4(&yr)[4]) {
+    const int col0 = (c - ch.start[s]) * NC;
+    // the chunk's B block: NC columns of R ranks (at most 16 KB)
+    const __amdgpu_buffer_rsrc_t bt = make_rsrc(
+        const_cast<uint16_t*>(B) + ((size_t)sid * g.O + g.off[s] + col0) * R,
+        (uint32_t)(NC * R * sizeof(uint16_t)));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cc = bcol + 32 * q;
+      const bool ok = bk_ok && col0 + cc < out_s;
+      br[q] = ld16_buf(bt, ok ? (uint32_t)((cc * R + 8 * b8) * sizeof(uint16_t)) : 0u);
+    }
+    const int col = col0 + 8 * j16;
+    const uint32_t cb = (uint32_t)(col < out_s ? col : 0) * (uint32_t)sizeof(uint16_t);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yr[r] = ld16_buf_nt(yb, yo[r] + cb);
+  };
+  u32x4 br[4], yn[4];
+  load_chunk(c_begin, br, yn);
   for (int c = c_begin; c < c_end; ++c) {
     const int col0 = (c - ch.start[s]) * NC;
     u32x4 yc[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) yc[q] = yn[q];
+    for (int r = 0; r < 4; ++r) yc[r] = yn[r];
     if (c > c_begin) __syncthreads();  // MFMA readers of the previous chunk's bs are done
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(&bs[(bcol + 32 * j) * LDK + 8 * b8]) = br[j] & bm[j];
+    for (int q = 0; q < 4; ++q) {
+      const int cc = bcol + 32 * q;
+      const uint32_t m = all_or_none(bk_ok && col0 + cc < out_s);
+      *reinterpret_cast<u32x4*>(&bs[((cc & 7) * 16 + (cc >> 3)) * LDK + 8 * b8]) = br[q] & m;
+    }
     // the next chunk's loads overlap this one (the last chunk reloads itself:
     // unconditional loads keep the memory counters exact)
-    load_chunk(min(c + 1, c_end - 1), br, bm, yn);
+    load_chunk(min(c + 1, c_end - 1), br, yn);
     __syncthreads();
     f32x4 acc[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < rr; kk += 32) {
-      const int vo = (16 * wave + m16) * LDK + kk + 8 * grp;
-      const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vh[vo]));
-      const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vl[vo]));
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int q = nt >> 1, hi = nt & 1;
-        const int crow = 32 * q + 8 * (m16 >> 2) + 4 * hi + (m16 & 3);
-        const bf16x8 ba = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&bs[crow * LDK + kk + 8 * grp]));
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bh, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba, bl, acc[nt], 0, 0, 0);
+    for (int kc = 0; kc < 2; ++kc) {
+      if (32 * kc < rr) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          // B column 8 j16 + nt sits at LDS row nt * 16 + j16
+          const bf16x8 bb = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&bs[(nt * 16 + j16) * LDK + 32 * kc + 8 * grp]));
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[kc], bb, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl[kc], bb, acc[nt], 0, 0, 0);
+        }
       }
     }
-    // y update in registers: lane (grp, m16) owns token 16 wave + m16, columns
-    // col0 + 32 q + 8 grp .. +8 of pair q
+    // y update in registers: lane (grp, j16) owns columns col0 + 8 j16 .. +8 of
+    // its four tokens; acc[nt][r] is column col0 + 8 j16 + nt of token r
+    const int col = col0 + 8 * j16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 d0 = acc[2 * q], d1 = acc[2 * q + 1];
-      const float add[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-      const uint32_t wi[4] = {yc[q].x, yc[q].y, yc[q].z, yc[q].w};
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t wi[4] = {yc[r].x, yc[r].y, yc[r].z, yc[r].w};
       uint32_t o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(wi[i] << 16) + add[2 * i];
-        const float hi = __uint_as_float(wi[i] & 0xffff0000u) + add[2 * i + 1];
+        const float lo = __uint_as_float(wi[i] << 16) + acc[2 * i][r];
+        const float hi = __uint_as_float(wi[i] & 0xffff0000u) + acc[2 * i + 1][r];
         o[i] = pack_bf16x2(lo, hi);
       }
-      const int col = col0 + 32 * q + 8 * grp;
-      const uint32_t off = (my_tok >= 0 && col < out_s)
-                               ? (uint32_t)(yrow_off + (size_t)col * sizeof(uint16_t))
+      const uint32_t off = (((tok_ok >> r) & 1u) && col < out_s)
+                               ? yo[r] + (uint32_t)col * (uint32_t)sizeof(uint16_t)
                                : kDropOffset;
-      st16_buf(u32x4{o[0], o[1], o[2], o[3]}, yb, off);
+      st16_buf_nt(u32x4{o[0], o[1], o[2], o[3]}, yb, off);
     }
   }
 }
@@ -1843,10 +1882,10 @@ static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, v
       if (o >= 1 && o <= 8) cpw = (int)o;
     }
     const Chunks gr = make_groups(g, cpw);
-    hipLaunchKernelGGL(expand_mfma_chunks_kernel<MODE>, dim3(grid_of(tiles * gr.total)), dim3(256),
+    hipLaunchKernelGGL(expand_mfma_rows_kernel<MODE>, dim3(grid_of(tiles * gr.total)), dim3(256),
                        0, st, v, (const uint16_t*)B, (uint16_t*)y, L, g, ch, gr, ksplit, v_rows,
                        cpw);
-    return hip_check("expand_mfma_chunks launch");
+    return hip_check("expand_mfma_rows launch");
   }
   hipLaunchKernelGGL(expand_mfma_kernel<MODE>, dim3(grid_of(tiles * ch.total)), dim3(256), 0, st,
                      v, (const uint16_t*)B, (uint16_t*)y, L, g, ch, ksplit, v_rows);
