@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--replica-mib", type=float, default=1024.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="seconds of oracle time per CPU leg (all cores, then one thread)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--sweep", action="store_true",
                    help="also sweep BGMV decode over batch size, adapter count and rank")
@@ -70,6 +71,18 @@ def make_workloads(name, seed):
         return [W.config_qkv_decode(seed=seed)]
     gu, dn = W.config_mlp_mixed(seed=seed)
     return [gu, dn]
+
+
+WORKLOAD_DESC = {
+    "bgmv_decode": "BGMV decode bf16: in=out=3072, 64 single-token rows, 8 adapters rank 16 "
+                   "alpha 32, 10% rows without adapter",
+    "sgmv_prefill": "SGMV prefill bf16: in=out=4096, 16 sequences of 64..1024 tokens, 16 adapters "
+                    "ranks {8,16,32,64} padded to 64",
+    "qkv_decode": "fused QKV decode bf16: in=4096, q/k/v=4096/1024/1024, 256 tokens, 64 adapters "
+                  "rank 16 Zipf(1.1), rsLoRA",
+    "mlp_mixed": "mixed MLP bf16: gate_up 4096->2x14336 and down 14336->4096, 8 prefill sequences "
+                 "+ 256 decode tokens, 32 adapters",
+}
 
 
 def algorithmic(wl):
@@ -243,6 +256,67 @@ def measure(setups, steps, warmup, stream_ptr):
             s.apply_step(warmup + i, stream_ptr)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def mfma_cap_tflops(a):
+    """The MFMA rate a kernel group would need to run at the HBM roof: its
+    arithmetic intensity (algorithmic flops per algorithmic byte) times 8 TB/s."""
+    return a["flops"] / a["bytes"] * HBM_PEAK_GBS / 1e3
+
+
+def workload_leg(name, seed, steps, stream_ptr, replica_bytes):
+    """One named workload measured like the headline: whole lora_apply steps
+    (wall clock between two synchronizes) and each launch group on its own
+    (HIP events around back-to-back launches), with the algorithmic rate, its
+    fraction of 8 TB/s, the HBM traffic rocprofv3 counted for that group (when
+    recorded for the current kernel source) and the MFMA rate against both the
+    bf16 peak and the rate the workload's arithmetic intensity allows at the HBM
+    roof.  Returns (object, setups)."""
+    wls = make_workloads(name, seed)
+    setups = [Setup(w, replica_bytes / len(wls)) for w in wls]
+    el = measure(setups, steps, min(10, steps), stream_ptr)
+    st = el / steps
+    algs = [algorithmic(s.wl) for s in setups]
+    tot = {k: sum(a[k] for a in algs) for k in ("Ta", "bytes", "flops")}
+    dom, pk = kernel_roofline(setups, stream_ptr, 50)
+    kus = sum(r["step_us"] for r in pk.values())
+    cap = mfma_cap_tflops(tot)
+    tf = tot["flops"] / (kus * 1e-6) / 1e12
+    per = {}
+    for k, r in pk.items():
+        traffic = load_traffic(k, name)
+        per[k] = {"us": round(r["us"], 2), "GBs": round(r["GBs"], 1),
+                  "frac": round(r["GBs"] / HBM_PEAK_GBS, 3),
+                  "TFLOPs": round(r["TFLOPs"], 1),
+                  "traffic": traffic,
+                  "traffic_over_algorithmic": (round(traffic / r["bytes"], 3)
+                                               if traffic else None),
+                  "kernels": r["kernels"]}
+    obj = {
+        "workload": WORKLOAD_DESC[name],
+        "calls_per_step": len(setups),
+        "active_tokens": tot["Ta"],
+        "tokens_per_s": tot["Ta"] / st, "ms_per_step": st * 1e3,
+        "algorithmic_bytes_per_step": tot["bytes"],
+        "achieved_GBs_step": tot["bytes"] / st / 1e9,
+        "kernel_us_per_step": kus,
+        "achieved_GBs_kernels": tot["bytes"] / (kus * 1e-6) / 1e9,
+        "frac_hbm_peak_kernels": tot["bytes"] / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "arithmetic_intensity": tot["flops"] / tot["bytes"],
+        "mfma_tflops_kernels": tf,
+        "mfma_util_of_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+        "mfma_cap_tflops": cap,
+        "mfma_util_of_cap": tf / cap,
+        "per_kernel": per,
+        "dominant_kernel": dom,
+    }
+    for k, r in pk.items():
+        log(f"[bench] {name} {k}: {r['us']:.2f} us/launch, {r['GBs']:.0f} GB/s, "
+            f"{r['TFLOPs']:.1f} TFLOP/s")
+    log(f"[bench] {name}: {st * 1e6:.1f} us/step, kernels {kus:.1f} us, "
+        f"{obj['achieved_GBs_kernels']:.0f} GB/s ({obj['frac_hbm_peak_kernels']:.3f} of peak), "
+        f"MFMA {tf:.0f} TFLOP/s = {tf / cap:.2f} of the intensity cap")
+    return obj, setups
 
 
 def ragged_decode_leg(seed, steps, stream_ptr, replica_bytes):
@@ -731,9 +805,9 @@ def record_traffic(pmc_dir, workload, seed):
     print(json.dumps({k: v for k, v in data.items() if k.startswith(workload + ":")}, indent=1))
 
 
-def cpu_baseline(wl, seconds):
-    """The fp64 oracle as it stands, single BLAS thread, over whole batches of
-    the same workload until `seconds` of CPU time are used."""
+def _oracle_rate(wl, rows, seconds):
+    """The fp64 oracle on `rows` of `wl`, over and over on one BLAS thread,
+    until `seconds` have passed: (active rows done, seconds)."""
     try:
         from threadpoolctl import threadpool_limits
     except Exception:  # pragma: no cover
@@ -741,8 +815,7 @@ def cpu_baseline(wl, seconds):
     import oracle
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:
-        rows = list(range(wl.T))
-        Ta = int((wl.ids >= 0).sum())
+        act = int(sum(1 for t in rows if wl.ids[t] >= 0))
         t0 = time.perf_counter()
         n = 0
         while True:
@@ -754,6 +827,24 @@ def cpu_baseline(wl, seconds):
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
+    return n * act, el
+
+
+def _oracle_worker(job):
+    """One process of the all-core oracle run: the workload is drawn again from
+    its seed (the same values), then the oracle runs on this process's rows."""
+    name, seed, lo, hi, seconds = job
+    wl = make_workloads(name, seed)[0]
+    return _oracle_rate(wl, list(range(lo, hi)), seconds)
+
+
+def cpu_baseline(wl, seconds, name, seed):
+    """The fp64 oracle as it stands, timed on this host for about `seconds`:
+    once in one process per visible core (at most 16), each on a contiguous
+    share of the batch's rows (rows are independent), which is the baseline
+    reported; and once in this process on one thread."""
+    import multiprocessing as mp
+    ncores = min(16, len(os.sched_getaffinity(0)))
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -762,10 +853,30 @@ def cpu_baseline(wl, seconds):
                 break
     except OSError:
         pass
-    return {"value": n * Ta / el, "unit": "LoRA-delta tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full batches of the same workload ({n * Ta} active tokens) through "
-                      f"the per-token fp64 oracle in {el:.1f} s; one BLAS thread; host CPU: {cpu}; "
-                      f"{len(os.sched_getaffinity(0))} cores visible"}
+    nproc = max(1, min(ncores, wl.T))
+    bounds = [(wl.T * k // nproc, wl.T * (k + 1) // nproc) for k in range(nproc)]
+    # spawn: the workers start fresh interpreters and never touch the GPU
+    try:
+        with mp.get_context("spawn").Pool(nproc) as pool:
+            res = pool.map_async(_oracle_worker,
+                                 [(name, seed, lo, hi, seconds) for lo, hi in bounds]).get(
+                                     timeout=3 * seconds + 120)
+    except Exception as e:  # the workers did not finish: report the one-thread run only
+        res = None
+        log(f"[bench] all-core oracle run failed ({e!r}); reporting one thread")
+    n_one, el_one = _oracle_rate(wl, list(range(wl.T)), seconds)
+    one = {"value": n_one / el_one, "unit": "LoRA-delta tokens/s", "cores": 1,
+           "sample": f"{n_one} active rows (whole batches) in {el_one:.1f} s in one process on "
+                     f"one BLAS thread"}
+    if res is None:
+        return dict(one, kind="oracle", sample=one["sample"] + f"; host CPU: {cpu}")
+    v_all = sum(n / el for n, el in res)
+    done = sum(n for n, _ in res)
+    return {"value": v_all, "unit": "LoRA-delta tokens/s", "cores": nproc, "kind": "oracle",
+            "sample": f"the per-token fp64 oracle in {nproc} processes (one per visible core, "
+                      f"one BLAS thread each), each repeating its share of the rows of the same "
+                      f"workload for {seconds:.0f} s: {done} active rows in all; host CPU: {cpu}",
+            "single_thread": one}
 
 
 def bgmv_sweep(seed, stream_ptr):
@@ -851,15 +962,7 @@ def main():
         "dtype": wls[0].dtype,
         "data": "synthetic",
         "config": {
-            "workload": {"bgmv_decode": "BGMV decode bf16: in=out=3072, 64 single-token rows, "
-                                        "8 adapters rank 16 alpha 32, 10% rows without adapter",
-                         "sgmv_prefill": "SGMV prefill bf16: in=out=4096, 16 sequences of 64..1024 "
-                                         "tokens, 16 adapters ranks {8,16,32,64} padded to 64",
-                         "qkv_decode": "fused QKV decode bf16: in=4096, q/k/v=4096/1024/1024, 256 "
-                                       "tokens, 64 adapters rank 16 Zipf(1.1), rsLoRA",
-                         "mlp_mixed": "mixed MLP bf16: gate_up 4096->2x14336 and down 14336->4096, "
-                                      "8 prefill sequences + 256 decode tokens, 32 adapters"
-                         }[args.workload],
+            "workload": WORKLOAD_DESC[args.workload],
             "tokens": wls[0].T, "active_tokens": Ta, "adapters_active": algs[0]["n_act"],
             "replicas": setups[0].nrep, "seed": args.seed,
         },
@@ -896,28 +999,10 @@ def main():
 
     if not args.no_secondary and args.workload != "sgmv_prefill":
         wl2 = make_workloads("sgmv_prefill", args.seed)
-        s2 = [Setup(w, args.replica_mib * 2 ** 20) for w in wl2]
-        el2 = measure(s2, max(20, args.steps // 10), 5, stream_ptr)
-        st2 = el2 / max(20, args.steps // 10)
+        out["secondary"], s2 = workload_leg("sgmv_prefill", args.seed, max(20, args.steps // 10),
+                                            stream_ptr, args.replica_mib * 2 ** 20)
+        st2 = out["secondary"]["ms_per_step"] * 1e-3
         a2 = algorithmic(wl2[0])
-        dom2, pk2 = kernel_roofline(s2, stream_ptr, 50)
-        kus = sum(r["step_us"] for r in pk2.values())
-        out["secondary"] = {
-            "workload": "SGMV prefill bf16: in=out=4096, 16 sequences of 64..1024 tokens, "
-                        "16 adapters ranks {8,16,32,64} padded to 64",
-            "tokens_per_s": a2["Ta"] / st2, "ms_per_step": st2 * 1e3,
-            "achieved_GBs_step": a2["bytes"] / st2 / 1e9,
-            "achieved_GBs_kernels": a2["bytes"] / (kus * 1e-6) / 1e9,
-            "frac_hbm_peak_kernels": a2["bytes"] / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "mfma_tflops_kernels": a2["flops"] / (kus * 1e-6) / 1e12,
-            "mfma_util_of_peak": a2["flops"] / (kus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "per_kernel": {k: {"us": round(r["us"], 2), "GBs": round(r["GBs"], 1),
-                               "TFLOPs": round(r["TFLOPs"], 1)} for k, r in pk2.items()},
-            "dominant_kernel": dom2,
-        }
-        for k, r in pk2.items():
-            log(f"[bench] prefill {k}: {r['us']:.2f} us/launch, {r['GBs']:.0f} GB/s, "
-                f"{r['TFLOPs']:.1f} TFLOP/s")
         dp, db = device_plan_leg(s2[0], max(20, args.steps // 10), stream_ptr)
         out["secondary"]["device_plan_step_us"] = round(dp, 2)
         out["secondary"]["device_builder_us"] = round(db, 2)
@@ -942,12 +1027,23 @@ def main():
         del s3
         torch.cuda.empty_cache()
 
+    if not args.no_secondary:
+        # the other two named workloads, each measured the same way
+        for name in ("qkv_decode", "mlp_mixed"):
+            if name == args.workload:
+                continue
+            steps_w = max(20, args.steps // (10 if name == "qkv_decode" else 40))
+            out[name], sw = workload_leg(name, args.seed, steps_w, stream_ptr,
+                                         args.replica_mib * 2 ** 20)
+            del sw
+            torch.cuda.empty_cache()
+
     if args.sweep:
         out["bgmv_sweep"] = bgmv_sweep(args.seed, stream_ptr)
 
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(wls[0], args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wls[0], args.cpu_seconds, args.workload, args.seed)
     else:
         out["cpu_baseline"] = None
     out["wall_s"] = time.perf_counter() - t_start
