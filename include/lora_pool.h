@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define LORA_POOL_ABI_VERSION 2
+#define LORA_POOL_ABI_VERSION 3
 #define LORA_MAX_SLICES 8
 /* [TGI] step 4 names a BGMV rank limit without a value; 64 covers the ranks
  * the kernels are built for.  Pass bgmv_max_rank <= 0 to lora_build_meta /
@@ -273,9 +273,11 @@ int64_t lora_apply_host_meta_bytes(const lora_pool_desc* desc, int32_t T);
 #define LORA_PLAN_WAVE_ROWS 8
 #define LORA_PLAN_MFMA_ROWS 64
 /* most K-split partials of v a plan uses (LORA_PLAN_MAX_KSPLIT_MFMA for MFMA
- * tiles, LORA_PLAN_MAX_KSPLIT for wavefront tiles) */
+ * tiles, at most LORA_PLAN_MAX_KSPLIT_MFMA_WIDE of them when max_lora_rank >
+ * 32; LORA_PLAN_MAX_KSPLIT for wavefront tiles) */
 #define LORA_PLAN_MAX_KSPLIT 8
-#define LORA_PLAN_MAX_KSPLIT_MFMA 4
+#define LORA_PLAN_MAX_KSPLIT_MFMA 8
+#define LORA_PLAN_MAX_KSPLIT_MFMA_WIDE 4
 /* int32 words per tile record of a plan */
 #define LORA_PLAN_WAVE_WORDS 16
 #define LORA_PLAN_MFMA_WORDS 4
@@ -318,7 +320,9 @@ typedef struct {
   int32_t wave_tiles;
   int32_t mfma_tiles;
   int32_t mfma_min_rows;   /* INT32_MAX when no segment uses MFMA tiles */
-  int32_t ksplit;          /* in [1, LORA_PLAN_MAX_KSPLIT_MFMA] */
+  int32_t ksplit;          /* in [1, LORA_PLAN_MAX_KSPLIT_MFMA]; at most
+                              LORA_PLAN_MAX_KSPLIT_MFMA_WIDE when
+                              max_lora_rank > 32 */
   int32_t bgmv_mfma_min_rows;  /* INT32_MAX when no BGMV run uses MFMA tiles */
   int32_t ksplit_wave;     /* in [1, LORA_PLAN_MAX_KSPLIT] */
   int32_t reserved;        /* 0 */

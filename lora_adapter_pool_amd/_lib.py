@@ -75,7 +75,8 @@ class lora_plan(ctypes.Structure):
 PLAN_WAVE_ROWS = 8
 PLAN_MFMA_ROWS = 64
 PLAN_MAX_KSPLIT = 8        # partials of v (wavefront tiles)
-PLAN_MAX_KSPLIT_MFMA = 4   # partials of v (MFMA tiles)
+PLAN_MAX_KSPLIT_MFMA = 8   # partials of v (MFMA tiles, pools of rank <= 32)
+PLAN_MAX_KSPLIT_MFMA_WIDE = 4   # ... pools of rank > 32
 PLAN_WAVE_WORDS = 16
 PLAN_MFMA_WORDS = 4
 

@@ -73,9 +73,10 @@ int32_t sgmv_args(const int32_t* perm, const int32_t* seg_starts, const int32_t*
 int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const void* image_host,
                   TilePlan* tp) {
   if (!p) return fail(LORA_E_ARG, "plan is NULL");
-  if (p->ksplit < 1 || p->ksplit > LORA_PLAN_MAX_KSPLIT_MFMA)
-    return fail(LORA_E_ARG, "malformed plan (ksplit %d outside [1, %d])", p->ksplit,
-                LORA_PLAN_MAX_KSPLIT_MFMA);
+  const int32_t kmax = g.R > 32 ? LORA_PLAN_MAX_KSPLIT_MFMA_WIDE : LORA_PLAN_MAX_KSPLIT_MFMA;
+  if (p->ksplit < 1 || p->ksplit > kmax)
+    return fail(LORA_E_ARG, "malformed plan (ksplit %d outside [1, %d] for max_lora_rank %d)",
+                p->ksplit, kmax, g.R);
   if (p->ksplit_wave < 1 || p->ksplit_wave > LORA_PLAN_MAX_KSPLIT)
     return fail(LORA_E_ARG, "malformed plan (ksplit_wave %d outside [1, %d])", p->ksplit_wave,
                 LORA_PLAN_MAX_KSPLIT);

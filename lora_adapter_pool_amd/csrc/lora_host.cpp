@@ -289,17 +289,22 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
 // every v row.
 // K split of the MFMA shrink: doubled while the launch has fewer than two
 // workgroups per compute unit (256 CUs) and every split keeps at least four
-// 64-wide K steps
+// 64-wide K steps, up to 8 for pools of rank <= 32 (whose partials of v are
+// small next to x) and 4 above
+int32_t mfma_ksplit_max(const Geo& g) {
+  return g.R > 32 ? LORA_PLAN_MAX_KSPLIT_MFMA_WIDE : LORA_PLAN_MAX_KSPLIT_MFMA;
+}
+
 int32_t mfma_ksplit(const Geo& g, int64_t nm) {
   int32_t ksplit = 1;
   if (nm > 0) {
     const int64_t wgs = nm * g.S * ((g.R + 63) / 64);
     const int64_t ksteps = (g.K + 63) / 64;
-    while (ksplit < LORA_PLAN_MAX_KSPLIT_MFMA && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4)
-      ksplit *= 2;
-    if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1, 2 or 4
+    const int32_t top = mfma_ksplit_max(g);
+    while (ksplit < top && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4) ksplit *= 2;
+    if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1, 2, 4 or 8
       const long o = std::strtol(e, nullptr, 10);
-      if (o == 1 || o == 2 || o == 4) ksplit = (int32_t)o;
+      if ((o == 1 || o == 2 || o == 4 || o == 8) && o <= top) ksplit = (int32_t)o;
     }
   }
   return ksplit;

@@ -78,8 +78,11 @@ constexpr int32_t tile_kparts_max(int32_t R) { return R <= 16 ? LORA_PLAN_MAX_KS
 int32_t wave_ksplit(const Geo& g, int64_t nw);
 // K split of the 64-row MFMA tiles' shrink for a plan of nm such tiles: doubled
 // while the launch has fewer than two workgroups per compute unit and every
-// part keeps four 64-wide K steps, up to LORA_PLAN_MAX_KSPLIT_MFMA.
+// part keeps four 64-wide K steps, up to mfma_ksplit_max(g).
 int32_t mfma_ksplit(const Geo& g, int64_t nm);
+// most partials that split may use for this pool: LORA_PLAN_MAX_KSPLIT_MFMA
+// for R <= 32, LORA_PLAN_MAX_KSPLIT_MFMA_WIDE above
+int32_t mfma_ksplit_max(const Geo& g);
 
 // Device-built plan of lora_apply_device: capacities of its 8-row tile
 // records and of its 64-row MFMA tile records (each slot adds at most one

@@ -22,7 +22,8 @@ constexpr int kExpandMfmaCols = 128;   // output columns per MFMA expand workgro
 constexpr int kArgWords = 2 + LORA_PLAN_WAVE_ROWS;
 constexpr int kArgTilesS = 12;
 constexpr int kArgTilesL = 48;
-constexpr int kMaxKsplit = LORA_PLAN_MAX_KSPLIT_MFMA;  // K splits of the MFMA shrink
+constexpr int kMaxKsplit = LORA_PLAN_MAX_KSPLIT_MFMA;  // K splits of the MFMA shrink (R <= 32)
+constexpr int kMaxKsplitWide = LORA_PLAN_MAX_KSPLIT_MFMA_WIDE;  // ... for R > 32
 constexpr int kMaxKsplitWave = LORA_PLAN_MAX_KSPLIT;   // K splits of the wavefront tiles
 
 // A list of rows to process.  Row i reads token tok[i] of x / y and writes row i

@@ -1329,7 +1329,7 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
   const int b8 = tid & 7, bcol = tid >> 3;
   for (int kb0 = 0; kb0 < R; kb0 += KB) {
     const int kw = min(KB, R - kb0);  // multiple of 8
-    u32x4 vr[4][kMaxKsplit];
+    u32x4 vr[4][kMaxKsplitWide];
     const bool vk_ok = 4 * q16 < kw;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1337,7 +1337,7 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
       const bool ok = vk_ok && s_tok[row] >= 0;
       const uint32_t m = all_or_none(ok);
 #pragma unroll
-      for (int p = 0; p < kMaxKsplit; ++p) {
+      for (int p = 0; p < kMaxKsplitWide; ++p) {
         const bool pin = p < ksplit;
         const size_t off = ((size_t)(pin ? p : 0) * v_rows + r0 + (ok ? row : 0)) * SR + s * R +
                            kb0 + (ok ? 4 * q16 : 0);
@@ -1358,7 +1358,7 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
       *reinterpret_cast<u32x4*>(&bs[(bcol + 32 * j) * LDK + 8 * b8]) = br[j];
       float e[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < kMaxKsplit; ++p) {  // fixed order: partial 0, 1, ...
+      for (int p = 0; p < kMaxKsplitWide; ++p) {  // fixed order: partial 0, 1, ...
         e[0] += __uint_as_float(vr[j][p].x);
         e[1] += __uint_as_float(vr[j][p].y);
         e[2] += __uint_as_float(vr[j][p].z);
@@ -1443,12 +1443,16 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
 // B and y are loaded while the current one is computed; y leaves through raw
 // buffer stores (y must span less than 2 GiB): lanes without a row store to a
 // dropped offset, so no store sits under a branch.
-template <int MODE>
+template <int MODE, int KP>
 __global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
     const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
     RowList L, Geo g, Chunks ch, Chunks gr, int ksplit, int v_rows, int cpw) {
   constexpr int TM = kMfmaTileRows, NC = kExpandMfmaCols, KB = 64;
   constexpr int LDK = KB + 8;
+  // KP partials of v are loaded (those past ksplit as zeros); splits of more
+  // than kMaxKsplitWide happen only for pools of rank <= 32: one 32-rank chunk
+  constexpr int NKC = KP > kMaxKsplitWide ? 1 : 2;
+  static_assert(KP == kMaxKsplitWide || KP == kMaxKsplit, "four or eight partials");
   static_assert(TM == 64 && NC == 128, "64 tokens x 128 columns per chunk");
   __shared__ __align__(16) uint16_t bs[NC * LDK];
   __shared__ int s_tok[TM];
@@ -1480,18 +1484,18 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
   }
   // v operands: token row 16 wave + j16, ranks 32 kc + 8 grp .. +8 (kc < 2);
   // the partials are summed in order 0, 1, ... (missing ones load as zeros)
-  bf16x8 vh[2], vl[2];
+  bf16x8 vh[NKC], vl[NKC];
   {
     const int row = 16 * wave + j16;
     const bool row_ok = row < cnt;
-    u32x4 vr[2][kMaxKsplit][2];
+    u32x4 vr[NKC][KP][2];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc) {
       const int k0 = 32 * kc + 8 * grp;
       const bool ok = row_ok && k0 < rr;
       const uint32_t m = all_or_none(ok);
 #pragma unroll
-      for (int p = 0; p < kMaxKsplit; ++p) {
+      for (int p = 0; p < KP; ++p) {
         const bool pin = p < ksplit;
         const size_t off =
             ((size_t)(pin ? p : 0) * v_rows + r0 + (ok ? row : 0)) * SR + s * R + (ok ? k0 : 0);
@@ -1501,10 +1505,10 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
       }
     }
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc) {
       float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < kMaxKsplit; ++p) {
+      for (int p = 0; p < KP; ++p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           e[4 * h + 0] += __uint_as_float(vr[kc][p][h].x);
@@ -1583,7 +1587,7 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc) {
       if (32 * kc < rr) {
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
@@ -1840,7 +1844,8 @@ static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, fl
                                   const RowList& L, int64_t tiles, int ksplit, int v_rows,
                                   hipStream_t st) {
   if (tiles <= 0) return LORA_OK;
-  if (ksplit < 1 || ksplit > kMaxKsplit) return fail(LORA_E_ARG, "bad K split %d", ksplit);
+  if (ksplit < 1 || ksplit > (g.R > 32 ? kMaxKsplitWide : kMaxKsplit))
+    return fail(LORA_E_ARG, "bad K split %d", ksplit);
   if (tiles * g.S * ksplit > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
   const unsigned gy = (unsigned)((g.R + 63) / 64);
   hipLaunchKernelGGL(shrink_mfma_kernel<MODE>, dim3(grid_of(tiles * g.S * ksplit), gy), dim3(256),
@@ -1869,7 +1874,8 @@ static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, v
                                   const RowList& L, int64_t tiles, int ksplit, int v_rows,
                                   hipStream_t st) {
   if (tiles <= 0) return LORA_OK;
-  if (ksplit < 1 || ksplit > kMaxKsplit) return fail(LORA_E_ARG, "bad K split %d", ksplit);
+  if (ksplit < 1 || ksplit > (g.R > 32 ? kMaxKsplitWide : kMaxKsplit))
+    return fail(LORA_E_ARG, "bad K split %d", ksplit);
   const Chunks ch = make_chunks(g, kExpandMfmaCols);
   if (tiles * ch.total > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
   if (g.R <= 64 && (int64_t)g.T * g.O * 2 < (int64_t)kDropOffset) {
@@ -1882,9 +1888,14 @@ static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, v
       if (o >= 1 && o <= 8) cpw = (int)o;
     }
     const Chunks gr = make_groups(g, cpw);
-    hipLaunchKernelGGL(expand_mfma_rows_kernel<MODE>, dim3(grid_of(tiles * gr.total)), dim3(256),
-                       0, st, v, (const uint16_t*)B, (uint16_t*)y, L, g, ch, gr, ksplit, v_rows,
-                       cpw);
+    if (ksplit > kMaxKsplitWide)  // R <= 32 (checked above)
+      hipLaunchKernelGGL((expand_mfma_rows_kernel<MODE, kMaxKsplit>), dim3(grid_of(tiles * gr.total)),
+                         dim3(256), 0, st, v, (const uint16_t*)B, (uint16_t*)y, L, g, ch, gr,
+                         ksplit, v_rows, cpw);
+    else
+      hipLaunchKernelGGL((expand_mfma_rows_kernel<MODE, kMaxKsplitWide>),
+                         dim3(grid_of(tiles * gr.total)), dim3(256), 0, st, v, (const uint16_t*)B,
+                         (uint16_t*)y, L, g, ch, gr, ksplit, v_rows, cpw);
     return hip_check("expand_mfma_rows launch");
   }
   hipLaunchKernelGGL(expand_mfma_kernel<MODE>, dim3(grid_of(tiles * ch.total)), dim3(256), 0, st,

@@ -24,7 +24,7 @@ def test_library_exports_every_header_function(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
-    assert lib.lora_abi_version() == 2
+    assert lib.lora_abi_version() == 3
 
 
 def test_pool_geometry_and_bytes():

@@ -251,6 +251,31 @@ def test_exact_integer_split_k(cpw, monkeypatch):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
 
 
+@pytest.mark.parametrize("R", [16, 32])
+def test_exact_integer_split_k_eight(R):
+    """Pools of rank <= 32 let the MFMA shrink split K into eight partials (the
+    expand then sums eight); K = 4104 gives 65 steps of 64 and a ragged last
+    split.  Integer inputs make the result exact."""
+    wl = W.config_integer(seed=11, T=360, K=4104, outs=(264, 136), max_loras=6,
+                          max_lora_rank=R, ranks=(8, 16, R, 8, R, 16), dtype="bf16")
+    ids = np.full(wl.T, -1, np.int32)
+    pre = np.zeros(wl.T, np.uint8)
+    pos = 0
+    for i, n in enumerate((64, 65, 130, 17, 33)):
+        ids[pos:pos + n] = i % 6
+        pre[pos:pos + n] = 1
+        pos += n
+    ids[pos:] = np.random.default_rng(12).integers(-1, 6, size=wl.T - pos)
+    wl = dataclasses.replace(wl, ids=ids, prefill=pre)
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    plan, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert plan["ksplit"] == 8 and plan["mfma_tiles"] >= 5
+    exp = _exact_expected(wl)
+    y = run_apply(wl).float().cpu().numpy()
+    bad = np.argwhere(y != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
 def test_sgmv_equals_bgmv_exactly():
     import torch
     wl = _integer_workload("bf16", seed=1)

@@ -9,7 +9,8 @@ import lora_adapter_pool_amd as L
 from lora_adapter_pool_amd import _lib
 import workloads as W
 
-WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS, MAX_KSPLIT, MAX_KSPLIT_MFMA = 8, 64, 16, 8, 4
+WAVE_ROWS, MFMA_ROWS, MFMA_MIN_ROWS, MAX_KSPLIT, MAX_KSPLIT_MFMA = 8, 64, 16, 8, 8
+MAX_KSPLIT_MFMA_WIDE = 4   # pools of rank > 32
 BGMV_MFMA_MIN_ROWS = 48
 
 
@@ -116,12 +117,13 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0, slot_ranks=None):
     assert (p["wave_tiles"], p["mfma_tiles"]) == (want_wave, want_mfma)
     assert p["image_bytes"] == 4 * (p["off_mfma"] + 4 * p["mfma_tiles"])
     # K split: doubled while the MFMA shrink has < 512 workgroups and each
-    # split keeps >= 4 steps of 64
+    # split keeps >= 4 steps of 64, up to 8 for pools of rank <= 32, else 4
     want_split = 1
     if p["mfma_tiles"]:
         wgs = p["mfma_tiles"] * desc.num_slices * -(-R // 64)
         ksteps = -(-desc.in_features // 64)
-        while want_split < MAX_KSPLIT_MFMA and wgs * want_split < 512 and ksteps // (2 * want_split) >= 4:
+        top = MAX_KSPLIT_MFMA if R <= 32 else MAX_KSPLIT_MFMA_WIDE
+        while want_split < top and wgs * want_split < 512 and ksteps // (2 * want_split) >= 4:
             want_split *= 2
     assert p["ksplit"] == want_split
     # K split of the wavefront tiles (bf16, R <= 64): grown while the launch has
@@ -271,6 +273,11 @@ def test_plan_entry_validation_before_hip():
         assert status(fn, p, T=0) == 0  # no rows: no-op, nothing launched
         empty = dict(p, wave_tiles=0, mfma_tiles=0)
         assert status(fn, empty) == 0
+    # more than four partials of the MFMA shrink only for pools of rank <= 32
+    d64 = L.make_desc("bf16", 4, 64, 64, [64])
+    p64, _, _ = L.lora_apply_plan(d64, ids, np.ones(6, np.uint8))
+    for fn in (L.lora_plan_shrink, L.lora_plan_expand):
+        assert status(fn, dict(p64, ksplit=MAX_KSPLIT_MFMA_WIDE + 1), desc=d64) == _lib.LORA_E_ARG
     # MFMA tiles need a bf16 pool
     d32 = L.make_desc("f32", 4, 16, 64, [64])
     pm, _, _ = L.lora_apply_plan(d, np.zeros(40, np.int32), np.ones(40, np.uint8))
