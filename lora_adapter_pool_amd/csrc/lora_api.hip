@@ -104,7 +104,8 @@ int32_t plan_view(const Geo& g, const lora_plan* p, const void* image, const voi
   *tp = TilePlan{img ? img + p->off_perm : nullptr, img ? img + p->off_wave : nullptr,
                  p->wave_tiles, img ? img + p->off_mfma : nullptr, p->mfma_tiles,
                  host ? host + p->off_wave : nullptr, p->ksplit,
-                 p->num_sgmv_rows + p->num_bgmv_rows, p->ksplit_wave, nullptr, nullptr, nullptr};
+                 p->num_sgmv_rows + p->num_bgmv_rows, p->ksplit_wave, nullptr, nullptr, nullptr,
+                 /*walk=*/0};
   return LORA_OK;
 }
 
@@ -448,7 +449,7 @@ int32_t apply_device_run(const Geo& g, const void* A_pool, const void* B_pool, c
                                         &po))
     return e;
   TilePlan tp{perm, tiles, cap, mtiles, mcap, nullptr, mfma_ksplit(g, mcap), T,
-              wave_ksplit(g, cap), nullptr, nullptr, nullptr};
+              wave_ksplit(g, cap), nullptr, nullptr, nullptr, /*walk=*/1};
   if (onepass) return run_plan_onepass_list(g, x, A_pool, B_pool, y, tp, st);
   float* v = (float*)(w + d.v);
   if (int32_t e = run_plan_shrink(g, x, A_pool, v, tp, st)) return e;

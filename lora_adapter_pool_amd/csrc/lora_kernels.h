@@ -87,6 +87,9 @@ struct TilePlan {
   int32_t* copy_perm;
   int32_t* copy_wave;
   int32_t* copy_mfma;
+  // 1 when wave_tiles (and mfma_tiles) are capacities (a device-built plan):
+  // its records come first, then records without rows
+  int32_t walk;
 };
 
 // Enqueue the shrink / expand of one row list (segments or rows) on `st`;

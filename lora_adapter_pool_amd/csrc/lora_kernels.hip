@@ -227,7 +227,10 @@ __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int&
 
 // How a kernel finds its tile: device segments, device rows with ids, the
 // plan's device image, or records passed by value in two capacities.
-enum { kSegs = 0, kRows = 1, kList = 2, kArg = 3, kArgL = 4, kArgC = 5 };
+// kListWalk: the plan's device image, like kList, for a plan whose record
+// count is a capacity (a device-built plan: its records first, then empty
+// ones); the 8-row tile kernels then walk several records per workgroup.
+enum { kSegs = 0, kRows = 1, kList = 2, kArg = 3, kArgL = 4, kArgC = 5, kListWalk = 6 };
 
 // Tile records passed by value (kArg, kArgL): a small plan travels in the
 // kernel arguments, which the wavefronts read with scalar loads, so no copy of
@@ -295,7 +298,7 @@ __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
       tr.tok[r] = (int)((rec[1 + r / 2] >> (16 * (r & 1))) & 0xffffu);  // 0xffff: past T
       tr.aid[r] = sid;
     }
-  } else if constexpr (MODE == kList) {
+  } else if constexpr (MODE == kList || MODE == kListWalk) {
     if (f >= L.num_tiles) return false;
     const int w = L.tiles[(size_t)f * LORA_PLAN_WAVE_WORDS + (lane & 15)];
     if (copy && L.copy_tiles && threadIdx.x < LORA_PLAN_WAVE_WORDS)
@@ -869,12 +872,23 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
   __shared__ float red[NW][TM][RM + 1];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_tile = g.S * kparts;
-  const int f = bid / per_tile;
-  const int rem = bid - f * per_tile;
+  const int f0 = bid / per_tile;
+  const int rem = bid - f0 * per_tile;
   const int s = rem / kparts;
   const int part = rem - s * kparts;
+  // one record per workgroup, except for a device-built plan (kListWalk):
+  // records f0, f0 + G, ... (G = the grid's records) until the first one
+  // without rows (its records come first, then empty ones to its capacity)
+  constexpr bool kWalk = MODE == kListWalk;
+  const int G = kWalk ? (int)(gridDim.x / per_tile) : 1;
+  for (int f = f0;; f += G) {
+  if (kWalk && f != f0) __syncthreads();  // red of the previous record is read
   TileRows<TM> tr;
-  if (!tile_rows<TM, MODE>(L, g, f, pa, tr, s == 0 && part == 0) || tr.valid == 0) return;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr, s == 0 && part == 0) || tr.cnt <= 0) return;
+  if (tr.valid == 0) {
+    if (kWalk) continue;
+    return;
+  }
   const int a = tr.aid[0];  // one adapter per tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
@@ -941,6 +955,8 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
       v[((size_t)part * v_rows + tr.vrow0 + r) * SR + s * R + n] = n < tr.rank ? acc : 0.f;
     }
   }
+  if (!kWalk) return;
+  }
 }
 
 // ------------------------------- expand (MFMA, wavefront tiles, bf16, R <= 64)
@@ -972,16 +988,27 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
   __shared__ __align__(16) uint16_t vh[TM * LDV];
   __shared__ __align__(16) uint16_t vl[TM * LDV];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int f = bid / ch.total;
-  const int cidx = bid - f * ch.total;
+  const int f0 = bid / ch.total;
+  const int cidx = bid - f0 * ch.total;
   int s = 0;
 #pragma unroll
   for (int i = 1; i < LORA_MAX_SLICES; ++i)
     if (i < g.S && cidx >= ch.start[i]) s = i;
   const int col0 = (cidx - ch.start[s]) * kTileExpandCols;
   const int out_s = g.out[s];
+  // one record per workgroup, except for a device-built plan (kListWalk):
+  // records f0, f0 + G, ... (G = the grid's records) until the first one
+  // without rows (its records come first, then empty ones to its capacity)
+  constexpr bool kWalk = MODE == kListWalk;
+  const int G = kWalk ? (int)(gridDim.x / ch.total) : 1;
+  for (int f = f0;; f += G) {
+  if (kWalk && f != f0) __syncthreads();  // vh / vl of the previous record are read
   TileRows<TM> tr;
-  if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.valid == 0) return;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.cnt <= 0) return;
+  if (tr.valid == 0) {
+    if (kWalk) continue;
+    return;
+  }
   const int a = tr.aid[0];  // one adapter per tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
@@ -1086,6 +1113,8 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
                              ? (uint32_t)((yrow + (size_t)yc) * sizeof(uint16_t))
                              : kDropOffset;
     st16_buf(u32x4{o[0], o[1], o[2], o[3]}, yb, off);
+  }
+  if (!kWalk) return;
   }
 }
 
@@ -1669,6 +1698,19 @@ static unsigned grid_of(int64_t n) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(n, (int64_t)1 << 31));
 }
 
+// Records one launch of the 8-row tile kernels covers with its grid: every
+// record, except for a device-built plan (kListWalk), whose record count is a
+// capacity and mostly empty records for a prefill batch: there the grid holds
+// at most about kTileWalkWgs workgroups, each walking its records with that
+// stride (one workgroup per record would launch thousands that read one
+// record and exit).
+constexpr int64_t kTileWalkWgs = 2048;
+template <int MODE> static int64_t walk_records(int64_t tiles, int64_t per_record) {
+  if (MODE != kListWalk) return tiles;
+  return std::max<int64_t>(
+      1, std::min<int64_t>(tiles, kTileWalkWgs / std::max<int64_t>(1, per_record)));
+}
+
 // Upper bound on the tiles of `tm` rows in a device row list (segments or rows
 // mode); surplus workgroups exit after the lookup.
 static int64_t count_tiles(const RowList& L, int tm) {
@@ -1745,8 +1787,8 @@ static int32_t launch_expand_tile_k(const Geo& g, const float* v, const void* B,
                                     const RowList& L, int64_t tiles, int kparts, int v_rows,
                                     hipStream_t st, const PlanArg<MODE>& pa) {
   const Chunks ch = make_chunks(g, kTileExpandCols);
-  const int64_t grid = tiles * ch.total;
-  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one expand launch");
+  if (tiles * ch.total > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one expand launch");
+  const int64_t grid = walk_records<MODE>(tiles, ch.total) * ch.total;
   hipLaunchKernelGGL((expand_tile_mfma_kernel<NKC, KP, MODE>), dim3(grid_of(grid)),
                      dim3(64 * kTileExpandWaves), 0, st, v, (const uint16_t*)B, (uint16_t*)y, L,
                      g, ch, kparts, v_rows, pa);
@@ -1757,13 +1799,23 @@ template <int NKC, int MODE>
 static int32_t launch_expand_tile_nkc(const Geo& g, const float* v, const void* B, void* y,
                                       const RowList& L, int64_t tiles, int kparts, int v_rows,
                                       hipStream_t st, const PlanArg<MODE>& pa) {
-  if (kparts > 4)
-    return launch_expand_tile_k<NKC, 8, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
-  if (kparts > 2)
-    return launch_expand_tile_k<NKC, 4, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
-  if (kparts > 1)
-    return launch_expand_tile_k<NKC, 2, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
-  return launch_expand_tile_k<NKC, 1, MODE>(g, v, B, y, L, tiles, 1, v_rows, st, pa);
+  if constexpr (MODE == kListWalk) {
+    // the walk is built for one partial of v only (with more, its loop keeps
+    // too many scalar registers live).  Several partials mean the shrink's
+    // grid was small, so the plan is small and one record per workgroup does
+    if (kparts > 1)
+      return launch_expand_tile_nkc<NKC, kList>(g, v, B, y, L, tiles, kparts, v_rows, st,
+                                                PlanArg<kList>{});
+    return launch_expand_tile_k<NKC, 1, MODE>(g, v, B, y, L, tiles, 1, v_rows, st, pa);
+  } else {
+    if (kparts > 4)
+      return launch_expand_tile_k<NKC, 8, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+    if (kparts > 2)
+      return launch_expand_tile_k<NKC, 4, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+    if (kparts > 1)
+      return launch_expand_tile_k<NKC, 2, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+    return launch_expand_tile_k<NKC, 1, MODE>(g, v, B, y, L, tiles, 1, v_rows, st, pa);
+  }
 }
 
 template <int MODE>
@@ -1785,8 +1837,9 @@ static int32_t launch_shrink_tile_nt(const Geo& g, const void* x, const void* A,
                                      const RowList& L, int64_t tiles, int kparts, int v_rows,
                                      hipStream_t st, const PlanArg<MODE>& pa) {
   constexpr int CB = tile_shrink_cb(16 * NT);
-  const int64_t grid = tiles * g.S * kparts;
-  if (grid > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one shrink launch");
+  if (tiles * g.S * kparts > INT32_MAX)
+    return fail(LORA_E_SHAPE, "batch too large for one shrink launch");
+  const int64_t grid = walk_records<MODE>(tiles, (int64_t)g.S * kparts) * g.S * kparts;
   hipLaunchKernelGGL((shrink_tile_mfma_kernel<NT, CB, MODE>), dim3(grid_of(grid)),
                      dim3(64 * kTileShrinkWaves), 0, st, (const uint16_t*)x, (const uint16_t*)A,
                      v, L, g, kparts, v_rows, pa);
@@ -2017,6 +2070,10 @@ static bool use_tile_mfma_expand(const Geo& g) {
   return on && use_tile_mfma(g) && (int64_t)g.T * g.O * 2 < (int64_t)kDropOffset;
 }
 
+// kListWalk reaches only the MFMA tile kernels; the VALU kernels read the
+// same records one per workgroup (kList)
+template <int MODE> constexpr int valu_mode() { return MODE == kListWalk ? kList : MODE; }
+
 template <int MODE>
 static int32_t launch_plan_wave_expand(const Geo& g, const float* v, const void* B, void* y,
                                        const RowList& Lw, const TilePlan& p, hipStream_t st,
@@ -2024,10 +2081,15 @@ static int32_t launch_plan_wave_expand(const Geo& g, const float* v, const void*
   if (use_tile_mfma_expand(g))
     return launch_expand_tile<MODE>(g, v, B, y, Lw, p.wave_tiles, wave_kparts(g, p), p.num_rows,
                                     st, pa);
+  constexpr int VM = valu_mode<MODE>();
+  const PlanArg<VM> pv{};
+  const PlanArg<VM>& pav = [&]() -> const PlanArg<VM>& {
+    if constexpr (VM == MODE) return pa; else return pv;
+  }();
   return g.dtype == LORA_BF16
-             ? launch_expand_wave<uint16_t, MODE>(g, v, B, y, Lw, p.wave_tiles, st, pa,
-                                                  wave_kparts(g, p), p.num_rows)
-             : launch_expand_wave<float, MODE>(g, v, B, y, Lw, p.wave_tiles, st, pa);
+             ? launch_expand_wave<uint16_t, VM>(g, v, B, y, Lw, p.wave_tiles, st, pav,
+                                                wave_kparts(g, p), p.num_rows)
+             : launch_expand_wave<float, VM>(g, v, B, y, Lw, p.wave_tiles, st, pav);
 }
 
 template <int MODE>
@@ -2037,9 +2099,14 @@ static int32_t launch_plan_wave_shrink(const Geo& g, const void* x, const void* 
   if (use_tile_mfma(g))
     return launch_shrink_tile<MODE>(g, x, A, v, Lw, p.wave_tiles, p.ksplit_wave, p.num_rows, st,
                                     pa);
+  constexpr int VM = valu_mode<MODE>();
+  const PlanArg<VM> pv{};
+  const PlanArg<VM>& pav = [&]() -> const PlanArg<VM>& {
+    if constexpr (VM == MODE) return pa; else return pv;
+  }();
   return g.dtype == LORA_BF16
-             ? launch_shrink_wave<uint16_t, MODE>(g, x, A, v, Lw, p.wave_tiles, st, pa)
-             : launch_shrink_wave<float, MODE>(g, x, A, v, Lw, p.wave_tiles, st, pa);
+             ? launch_shrink_wave<uint16_t, VM>(g, x, A, v, Lw, p.wave_tiles, st, pav)
+             : launch_shrink_wave<float, VM>(g, x, A, v, Lw, p.wave_tiles, st, pav);
 }
 
 int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, const TilePlan& p,
@@ -2056,7 +2123,8 @@ int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, co
   if (int32_t e = launch_shrink_mfma<kList>(g, x, A, v, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
                                             st))
     return e;
-  return launch_plan_wave_shrink<kList>(g, x, A, v, Lw, p, st);
+  return p.walk ? launch_plan_wave_shrink<kListWalk>(g, x, A, v, Lw, p, st)
+                : launch_plan_wave_shrink<kList>(g, x, A, v, Lw, p, st);
 }
 
 int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, const TilePlan& p,
@@ -2073,7 +2141,8 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
   if (int32_t e = launch_expand_mfma<kList>(g, v, B, y, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
                                             st))
     return e;
-  return launch_plan_wave_expand<kList>(g, v, B, y, Lw, p, st);
+  return p.walk ? launch_plan_wave_expand<kListWalk>(g, v, B, y, Lw, p, st)
+                : launch_plan_wave_expand<kList>(g, v, B, y, Lw, p, st);
 }
 
 // One launch for both stages (decode_onepass_kernel) when the plan goes by
