@@ -67,6 +67,12 @@ __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3..0 and 15..14,
+// expcnt 6..4, lgkmcnt 11..8): at most 4 vector memory operations and no LDS
+// operation outstanding; no vector memory operation outstanding
+constexpr int kWaitVm4Lgkm0 = 0x0074;
+constexpr int kWaitVm0 = 0x0F70;
+
 // All-ones or all-zeros, to zero a loaded value with a bit-AND: a select on a
 // loaded value lets the compiler sink the load under a branch, after which it
 // has to drain every outstanding load before continuing.
@@ -1286,6 +1292,165 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
   }
 }
 
+// ------------------------------------------------- shrink (MFMA, LDS by DMA)
+//
+// The same work as shrink_mfma_kernel (bf16; grid.x = tiles * S * ksplit,
+// grid.y = ceil(R / 64); a workgroup computes 64 rows x 64 ranks over the K
+// steps of its split) for K a multiple of 64, with the tiles moved by gfx950's
+// direct global -> LDS loads (global_load_lds_dwordx4): no registers hold the
+// data in flight, so a ring of three stages keeps the next two K steps in
+// flight at every step, where the register-staged kernel holds one to two.
+//
+// A stage is the x tile [64 rows][64 k] and the adapter tile [64 ranks][64 k],
+// 8 KB each, rows of 128 bytes without padding (a DMA instruction writes 64
+// lanes x 16 bytes contiguously).  Wave w loads rows 16 w .. 16 w + 16 of
+// both with two instructions each; lane l of an instruction covers row
+// 8 b + l / 8 and 16-byte slot l % 8, which holds the row's k chunk
+// (l % 8) ^ swz(row).  The MFMA operand reads (16 lanes, 16 consecutive rows,
+// one k chunk) then fall into 16 different banks groups.
+//
+// Rows past the tile's rows and ranks past the adapter's are loaded from a
+// clamped address: each feeds only its own D row or column, which is never
+// stored (rows) or stored as zero (ranks), so no mask is needed; a K tail
+// would mix into every sum, hence K % 64 == 0.  Steps past the split's last
+// one re-read it (cache hits) so every wave issues four loads per step.  The
+// loads count on vmcnt: a step's data is in LDS once at most one later step's
+// four loads are outstanding, and the barrier after that wait (which also
+// waits for the wave's own LDS reads) publishes every wave's part and retires
+// the previous step's reads of the stage reloaded next.
+__device__ __forceinline__ int dma_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+constexpr int kDmaShrinkMaxK = 8192;
+
+template <int MODE>
+__global__ __launch_bounds__(256, 3) void shrink_mfma_dma_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ A,
+                                                                float* __restrict__ v, RowList L,
+                                                                Geo g, int ksplit, int v_rows) {
+  constexpr int TM = kMfmaTileRows, NR = 64, KS = 64, TILE = 64 * KS;
+  static_assert(TM == 64, "64 rows per tile");
+  // stage k: the x tile, then the adapter tile (one LDS object per stage)
+  __shared__ __align__(16) uint16_t st_0[2 * TILE], st_1[2 * TILE], st_2[2 * TILE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
+  const int wm = wave & 1, wr = wave >> 1;
+  const int i16 = lane & 15, grp = lane >> 4;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_tile = g.S * ksplit;
+  const int f = bid / per_tile;
+  const int rem = bid - f * per_tile;
+  const int s = rem / ksplit;
+  const int part = rem - s * ksplit;
+  int r0, cnt, sid, tok0;
+  const bool copy = s == 0 && part == 0 && blockIdx.y == 0;
+  int rk_rec;
+  if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0, rk_rec, copy)) return;
+  if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
+  const int rr = rk_rec > 0 && rk_rec < g.R ? rk_rec : g.R;  // the adapter's ranks
+  const int rank0 = blockIdx.y * NR;
+  const int nsteps = g.K / KS;
+  const int per = (nsteps + ksplit - 1) / ksplit;
+  const int st0 = min(nsteps, part * per), st1 = min(nsteps, st0 + per);
+
+  // DMA sources: rows 8 b + l / 8 of block b = 2 wave + j, k chunk (l % 8) ^ swz
+  const uint16_t* xsrc[2];
+  const uint16_t* asrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * (2 * wave + j) + (lane >> 3);
+    const int c = (lane & 7) ^ dma_swz(row);
+    const int rc = min(row, cnt - 1);
+    const int tk = tok0 >= 0 ? tok0 + rc : L.tok[r0 + rc];
+    if (copy && L.copy_tok && tok0 < 0 && (lane & 7) == 0 && row < cnt) L.copy_tok[r0 + row] = tk;
+    xsrc[j] = x + (size_t)(tk >= 0 && tk < g.T ? tk : 0) * g.K + 8 * c;
+    const int rk = rank0 + row;
+    asrc[j] = A + ((size_t)(sid * g.S + s) * g.R + (rk < rr ? rk : 0)) * g.K + 8 * c;
+  }
+  auto issue = [&](int st, uint16_t* sd) {
+    const int kk = min(st, st1 - 1) * KS;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_global_load_lds(xsrc[j] + kk, sd + (2 * wave + j) * 512, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(asrc[j] + kk, sd + TILE + (2 * wave + j) * 512, 16, 0, 0);
+    }
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const uint16_t* xt) {
+    const uint16_t* at = xt + TILE;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 xa[2], ab[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int row = 32 * wm + 16 * mt + i16;
+        const int slot = (4 * kc + grp) ^ dma_swz(row);
+        xa[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xt[row * KS + 8 * slot]));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = 32 * wr + 16 * nt + i16;
+        const int slot = (4 * kc + grp) ^ dma_swz(row);
+        ab[nt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&at[row * KS + 8 * slot]));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], ab[nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+  // one step: wait for its own four loads (the next step's four may stay
+  // outstanding), barrier, refill the stage the previous step read, compute
+  // (the empty asm statements keep the compiler from moving LDS accesses
+  // across the barrier, which it does not treat as a memory operation)
+  auto step = [&](int st, const uint16_t* cur, uint16_t* nxt) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(st + 2, nxt);
+    mma(cur);
+  };
+  if (st0 < st1) {  // a split past the last K step leaves its partial at zero
+    issue(st0, st_0);
+    issue(st0 + 1, st_1);
+    for (int st = st0; st < st1; st += 6) {
+      step(st, st_0, st_2);
+      if (st + 1 >= st1) break;
+      step(st + 1, st_1, st_0);
+      if (st + 2 >= st1) break;
+      step(st + 2, st_2, st_1);
+      if (st + 3 >= st1) break;
+      step(st + 3, st_0, st_2);
+      if (st + 4 >= st1) break;
+      step(st + 4, st_1, st_0);
+      if (st + 5 >= st1) break;
+      step(st + 5, st_2, st_1);
+    }
+    // every load has landed before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  }
+  // D layout: lane (grp, i16) holds rows 4 grp + j (j < 4) of rank column i16
+  const int SR = g.S * g.R;
+  float* vp = v + ((size_t)part * v_rows + r0) * SR + s * g.R;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int rk = rank0 + 32 * wr + 16 * nt + i16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 32 * wm + 16 * mt + 4 * grp + j;
+        if (row < cnt && rk < g.R) vp[(size_t)row * SR + rk] = rk < rr ? acc[mt][nt][j] : 0.f;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ expand (MFMA)
 //
 // bf16 only.  grid.x = tiles * column chunks of 128 (one slice each).  The
@@ -1901,6 +2066,16 @@ static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, fl
     return fail(LORA_E_ARG, "bad K split %d", ksplit);
   if (tiles * g.S * ksplit > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
   const unsigned gy = (unsigned)((g.R + 63) / 64);
+  // the DMA-staged form needs whole K steps; measured faster up to K = 4096
+  // (in = 4096 prefill 24.0 -> 23.0 us, gate_up 40.3 -> 31.1 us, a 4096-token
+  // decode 13.0 -> 11.2 us) and slower at K = 14336 (down 62.1 -> 66.3 us),
+  // so wider K keeps the register-staged kernel
+  if (g.K % 64 == 0 && g.K <= kDmaShrinkMaxK) {
+    hipLaunchKernelGGL(shrink_mfma_dma_kernel<MODE>, dim3(grid_of(tiles * g.S * ksplit), gy),
+                       dim3(256), 0, st, (const uint16_t*)x, (const uint16_t*)A, v, L, g, ksplit,
+                       v_rows);
+    return hip_check("shrink_mfma_dma launch");
+  }
   hipLaunchKernelGGL(shrink_mfma_kernel<MODE>, dim3(grid_of(tiles * g.S * ksplit), gy), dim3(256),
                      0, st, (const uint16_t*)x, (const uint16_t*)A, v, L, g, ksplit, v_rows);
   return hip_check("shrink_mfma launch");

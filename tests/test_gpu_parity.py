@@ -276,6 +276,34 @@ def test_exact_integer_split_k_eight(R):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
 
 
+@pytest.mark.parametrize("K,R", [(1024, 16), (1024, 64), (4096, 64), (4096, 32)])
+def test_exact_integer_dma_shrink(K, R):
+    """K a multiple of 64: the 64-row MFMA shrink stages its tiles by direct
+    global -> LDS loads.  Segments of 64, 65, 130, 17 and 33 rows (ragged last
+    tiles, rows past a tile's end), adapters of rank below the pool's (ranks
+    past the adapter's), K split into several partials; exact on integer
+    inputs, so any row, rank or k chunk that lands in the wrong place shows."""
+    ranks = tuple(min(r, R) for r in (8, 16, 64, 32, 48, 64))
+    wl = W.config_integer(seed=13, T=380, K=K, outs=(264, 136), max_loras=6,
+                          max_lora_rank=R, ranks=ranks, dtype="bf16")
+    ids = np.full(wl.T, -1, np.int32)
+    pre = np.zeros(wl.T, np.uint8)
+    pos = 0
+    for i, n in enumerate((64, 65, 130, 17, 33)):
+        ids[pos:pos + n] = i % 6
+        pre[pos:pos + n] = 1
+        pos += n
+    ids[pos:] = np.random.default_rng(14).integers(-1, 6, size=wl.T - pos)
+    wl = dataclasses.replace(wl, ids=ids, prefill=pre)
+    d = L.make_desc(wl.dtype, wl.max_loras, wl.max_lora_rank, wl.in_features, wl.out_features)
+    plan, _, _ = L.lora_apply_plan(d, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] >= 5 and plan["ksplit"] >= 2
+    exp = _exact_expected(wl)
+    y = run_apply(wl).float().cpu().numpy()
+    bad = np.argwhere(y != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
 def test_sgmv_equals_bgmv_exactly():
     import torch
     wl = _integer_workload("bf16", seed=1)
