@@ -429,9 +429,15 @@ int32_t lora_apply(const lora_pool_desc* desc, const void* A_pool, const void* B
  * adapter, then the tile kernels' shrink and expand, all on `stream`.
  *   ids, prefill  device arrays of T entries (prefill may be NULL = all 0);
  *                 ids outside [-1, max_loras) are skipped like -1 (the host
- *                 path rejects them instead)
+ *                 path rejects them with LORA_E_ID; here no host code sees
+ *                 the ids), and counted: see ws
  *   ws            device workspace of lora_apply_device_workspace_bytes(desc,
- *                 T) bytes, 256-byte aligned: metadata, the tile records, v
+ *                 T) bytes, 256-byte aligned: metadata, the tile records, v.
+ *                 Once the stream has passed the call, its first four int32
+ *                 words hold the batch's SGMV rows, SGMV segments, BGMV rows
+ *                 and the number of rows whose id was outside [-1, max_loras):
+ *                 a caller that must not serve such rows from the base model
+ *                 alone reads word 3 back and treats non-zero as an error
  * The result is lora_apply's (within rounding: the K split may differ).
  * The plan follows the host plan's rules except that decode rows always take
  * 8-row tiles; its record counts are known on the host only as capacities

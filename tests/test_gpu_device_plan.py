@@ -95,10 +95,19 @@ def test_device_plan_skips_out_of_range_ids():
     ids = wl.ids.copy()
     ids[::7] = 9      # outside [-1, max_loras): skipped like -1
     ids[3::11] = -5
-    y = _run(wl, ids=ids)
+    pool = make_pool(wl)
+    ws = _ws(pool, wl.T)
+    y = _run(wl, pool=pool, ids=ids, ws=ws)
     case = dataclasses.replace(wl, ids=np.where((ids < -1) | (ids >= 4), -1, ids).astype(np.int32))
     exp = oracle.round_exact_to_dtype(oracle.lora_forward_rows(case), "bf16")
     assert np.array_equal(y.float().cpu().numpy(), exp)
+    # the workspace's first four words report the batch: SGMV rows, segments,
+    # BGMV rows and the rows whose id was out of range (skipped)
+    import torch
+    counts = ws[0][:16].view(torch.int32).cpu().numpy()
+    bad = int(((ids < -1) | (ids >= 4)).sum())
+    m = oracle.build_meta(case.ids.tolist(), case.prefill.tolist(), 16)
+    assert counts.tolist() == [len(m["sgmv_perm"]), len(m["seg_ids"]), len(m["bgmv_tok"]), bad]
 
 
 def test_device_plan_workspace_reused_across_batches():
