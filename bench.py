@@ -730,9 +730,12 @@ def stage_kernels(wl):
         return {"apply": [f"decode_onepass_kernel<{nt}, {cb}, 5>"]}
     out = {"shrink": [], "expand": []}
     if p["mfma_tiles"]:
-        out["shrink"].append("shrink_mfma_kernel<2>")
-        chunks = wl.max_lora_rank <= 64 and wl.T * wl.O * 2 < 2 ** 31
-        out["expand"].append("expand_mfma_rows_kernel<2>" if chunks else "expand_mfma_kernel<2>")
+        # whole 64-wide K steps up to K = 8192: tiles staged by direct loads to LDS
+        dma = wl.in_features % 64 == 0 and wl.in_features <= 8192
+        out["shrink"].append("shrink_mfma_dma_kernel<2>" if dma else "shrink_mfma_kernel<2>")
+        rows = wl.max_lora_rank <= 64 and wl.T * wl.O * 2 < 2 ** 31
+        kp = 8 if p["ksplit"] > 4 else 4
+        out["expand"].append(f"expand_mfma_rows_kernel<2, {kp}>" if rows else "expand_mfma_kernel<2>")
     if p["wave_tiles"]:
         # modes 3 / 4: records in the kernel arguments (up to 12 / 48 tiles),
         # 2: device image
@@ -788,15 +791,22 @@ def record_traffic(pmc_dir, workload, seed):
     for wl in wls:
         for k, v in stage_kernels(wl).items():
             kern.setdefault(k, set()).update(v)
+    # calls of the workload whose launch group uses each kernel
+    users = {}
+    for wl in wls:
+        for k, v in stage_kernels(wl).items():
+            for n in v:
+                users[(k, n)] = users.get((k, n), 0) + 1
     for stage, names in kern.items():
         # one launch group = one dispatch of each of its kernels; averaged over
-        # the workload's calls like the algorithmic bytes
+        # the workload's calls like the algorithmic bytes (a kernel that only
+        # some calls use counts for those)
         tot = 0.0
         for n in names:
             f, w = fetch.get(n), write.get(n)
             if not f or not w:
                 raise SystemExit(f"no counters for {n} in {pmc_dir}")
-            tot += (sum(f) / len(f)) * cf + (sum(w) / len(w)) * cw
+            tot += ((sum(f) / len(f)) * cf + (sum(w) / len(w)) * cw) * users[(stage, n)] / len(wls)
         data[f"{workload}:{stage}"] = {
             "hbm_bytes_per_launch": tot, "kernels": sorted(names),
             "fetch_scale": cf, "write_scale": cw, "kernel_source_sha": sha}
