@@ -1868,8 +1868,10 @@ static unsigned grid_of(int64_t n) {
 // capacity and mostly empty records for a prefill batch: there the grid holds
 // at most about kTileWalkWgs workgroups, each walking its records with that
 // stride (one workgroup per record would launch thousands that read one
-// record and exit).
-constexpr int64_t kTileWalkWgs = 2048;
+// record and exit).  768 is one resident round of the tile kernels (three
+// 256-thread workgroups per compute unit, 256 compute units): a batch without
+// 8-row tiles then costs one round of workgroups that each read one record.
+constexpr int64_t kTileWalkWgs = 768;
 template <int MODE> static int64_t walk_records(int64_t tiles, int64_t per_record) {
   if (MODE != kListWalk) return tiles;
   return std::max<int64_t>(

@@ -34,6 +34,43 @@ constexpr int kParMaxLoras = 256;
 // ... for blocks of more rows than this (smaller blocks: the three extra
 // barriers cost more than the single wavefront's chain).
 constexpr int kParMinRows = 1024;
+constexpr int kMetaWaves = kMetaThreads / 64;
+// Rows per thread whose ids are loaded at once by the histogram loop.
+constexpr int kHistBatch = 8;
+
+using i32x4 = int32_t __attribute__((ext_vector_type(4)));
+static_assert(LORA_PLAN_WAVE_WORDS == 16 && LORA_PLAN_MFMA_WORDS == 4,
+              "records are written as 16-byte words");
+
+// The lanes of this wavefront whose key equals this lane's, for keys in
+// [0, 2^kbits): the AND, over the key's bits, of the ballot of lanes that agree
+// with this lane on that bit.  Lanes with a negative key are in no mask.  Its
+// cost does not depend on how many distinct keys the wavefront holds.
+__device__ __forceinline__ uint64_t same_key_lanes(int key, int kbits) {
+  uint64_t m = __ballot(key >= 0);
+  for (int b = 0; b < kbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+// Sum of per-wavefront values s[w * stride] over the wavefronts before `wave`
+// (excl) and over all of them (tot): lane w < kMetaWaves holds wavefront w's
+// value and a shuffle scan adds them up, so no wavefront walks the others'.
+__device__ __forceinline__ void wave_prefix(const int32_t* s, int stride, int wave, int lane,
+                                            int& excl, int& tot) {
+  int x = lane < kMetaWaves ? s[lane * stride] : 0;
+#pragma unroll
+  for (int o = 1; o < kMetaWaves; o <<= 1) {
+    const int u = __shfl_up(x, o, 64);
+    if (lane >= o) x += u;
+  }
+  tot = __shfl(x, kMetaWaves - 1, 64);
+  const int e = __shfl(x, wave > 0 ? wave - 1 : 0, 64);
+  excl = wave > 0 ? e : 0;
+}
 
 // bins[key] += 1 for every active lane with key >= 0.  Sorted batches give
 // whole wavefronts of one key, whose atomics on one LDS word would serialize:
@@ -69,17 +106,37 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   __syncthreads();
 
   // 1. histogram; a batch that fits one block of keys also stages its keys
-  //    here, so placement does not read the ids again
+  //    here, so placement does not read the ids again.  Each thread loads the
+  //    ids and flags of kHistBatch rows before it counts any of them, so the
+  //    loop waits on memory once per batch, not once per row.
   int16_t* keys = reinterpret_cast<int16_t*>(lds + 2 * max_loras);
   const bool one_block = T <= kcap;
-  for (int t = tid; t < T; t += kMetaThreads) {
-    const int a = ids[t];
-    const bool ok = a >= 0 && a < max_loras;
-    const bool sg = ok && (all_sgmv || (prefill && prefill[t]));
-    if (one_block) keys[t] = (int16_t)(ok ? 2 * a + (sg ? 1 : 0) : -1);
-    if (a < -1 || a >= max_loras) atomicAdd(&s_bad, 1);
-    // cs and cb are adjacent: bin max_loras + a is cb[a]
-    count_keys(cs, ok ? (sg ? a : max_loras + a) : -1);
+  // every lane loads (rows past T repeat row T - 1 and count as rows without
+  // adapter), so no branch waits on a load; without flags the loads of pf
+  // read the ids' bytes and pmask drops them
+  const uint8_t* pf = prefill != nullptr ? prefill : reinterpret_cast<const uint8_t*>(ids);
+  const uint32_t pmask = prefill != nullptr ? 0xffu : 0u;
+  for (int t0 = 0; t0 < T; t0 += kMetaThreads * kHistBatch) {
+    int av[kHistBatch];
+    uint32_t pv[kHistBatch];
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+      const int tc = min(t0 + u * kMetaThreads + tid, T - 1);
+      av[u] = ids[tc];
+      pv[u] = pf[tc];
+    }
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+      if (t0 + u * kMetaThreads >= T) break;  // uniform
+      const int t = t0 + u * kMetaThreads + tid;
+      const int a = t < T ? av[u] : -1;
+      const bool ok = a >= 0 && a < max_loras;
+      const bool sg = ok && (all_sgmv || (pv[u] & pmask) != 0);
+      if (one_block && t < T) keys[t] = (int16_t)(ok ? 2 * a + (sg ? 1 : 0) : -1);
+      if (a < -1 || a >= max_loras) atomicAdd(&s_bad, 1);
+      // cs and cb are adjacent: bin max_loras + a is cb[a]
+      count_keys(cs, ok ? (sg ? a : max_loras + a) : -1);
+    }
   }
   __syncthreads();
 
@@ -106,14 +163,9 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     for (int i = 0; i < 3; ++i) s_wsum[wave][i] = inc[i];
   }
   __syncthreads();
-  int base[3] = {0, 0, 0}, tot[3] = {0, 0, 0};
-  for (int w = 0; w < nw; ++w) {
+  int base[3], tot[3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      base[i] += w < wave ? s_wsum[w][i] : 0;
-      tot[i] += s_wsum[w][i];
-    }
-  }
+  for (int i = 0; i < 3; ++i) wave_prefix(&s_wsum[0][i], 3, wave, lane, base[i], tot[i]);
   int es = base[0] + inc[0] - v[0], eb = base[1] + inc[1] - v[1], eg = base[2] + inc[2] - v[2];
   for (int a = a0; a < a1; ++a) {
     const int c = cs[a], d = cb[a];
@@ -162,14 +214,27 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   const int nkeys = 2 * max_loras;
   int32_t* wcnt = lds + 2 * max_loras + kcap / 2 + (plan.tiles ? 2 * (max_loras + 1) : 0);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int kbits = 32 - __clz(2 * max_loras - 1);  // bits of the largest key
   for (int b0 = 0; b0 < T; b0 += kcap) {
     const int nbk = min(kcap, T - b0);
     __syncthreads();  // the previous block's keys are placed
-    for (int i = tid; i < nbk && !one_block; i += kMetaThreads) {
-      const int t = b0 + i;
-      const int a = ids[t];
-      const bool ok = a >= 0 && a < max_loras;
-      keys[i] = (int16_t)(ok ? 2 * a + ((all_sgmv || (prefill && prefill[t])) ? 1 : 0) : -1);
+    for (int i0 = 0; i0 < nbk && !one_block; i0 += kMetaThreads * kHistBatch) {
+      int av[kHistBatch];
+      uint32_t pv[kHistBatch];
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {  // unconditional loads, as in the histogram
+        const int tc = b0 + min(i0 + u * kMetaThreads + tid, nbk - 1);
+        av[u] = ids[tc];
+        pv[u] = pf[tc];
+      }
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        const int i = i0 + u * kMetaThreads + tid;
+        const int a = av[u];
+        const bool ok = a >= 0 && a < max_loras;
+        const bool sg = all_sgmv || (pv[u] & pmask) != 0;
+        if (i < nbk) keys[i] = (int16_t)(ok ? 2 * a + (sg ? 1 : 0) : -1);
+      }
     }
     const bool par = par_slots && nbk > kParMinRows;  // uniform
     int32_t* my = wcnt + wave * nkeys;  // this wavefront's counters (par)
@@ -185,11 +250,13 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       for (int k = tid; k < nkeys; k += kMetaThreads) {
         int32_t* pos = (k & 1) ? &cs[k >> 1] : &cb[k >> 1];
         int base = *pos;
-#pragma unroll 1
-        for (int w = 0; w < nw; ++w) {
-          const int cnt = wcnt[w * nkeys + k];
+        int c[kMetaWaves];  // all counts read before the first is replaced
+#pragma unroll
+        for (int w = 0; w < kMetaWaves; ++w) c[w] = wcnt[w * nkeys + k];
+#pragma unroll
+        for (int w = 0; w < kMetaWaves; ++w) {
           wcnt[w * nkeys + k] = base;
-          base += cnt;
+          base += c[w];
         }
         *pos = base;
       }
@@ -202,20 +269,11 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       const int key = i < hi ? keys[i] : -1;
       int32_t* pos = par ? &my[key] : (key & 1) ? &cs[key >> 1] : &cb[key >> 1];
       const int p0 = key >= 0 ? *pos : 0;
-      uint64_t pending = __ballot(key >= 0);
-      int rank = 0, cnt = 0;
-      bool first = false;
-      while (pending) {
-        const int leader = __builtin_ctzll(pending);
-        const int k = __builtin_amdgcn_readlane(key, leader);
-        const uint64_t mk = __ballot(key == k);
-        if (key == k) {
-          rank = __popcll(mk & below);
-          cnt = __popcll(mk);
-          first = lane == leader;
-        }
-        pending &= ~mk;
-      }
+      // equal keys take consecutive positions in lane order; the lowest lane
+      // of each key moves the key's next free position
+      const uint64_t mk = same_key_lanes(key, kbits);
+      const int rank = __popcll(mk & below), cnt = __popcll(mk);
+      const bool first = key >= 0 && (mk & below) == 0;
       const int p = p0 + rank;
       if (key >= 0 && p < T) {
         const int t = b0 + i;
@@ -259,10 +317,8 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   for (int o = 32; o > 0; o >>= 1) lr += __shfl_xor(lr, o, 64);
   if (lane == 0) s_wsum[wave][2] = lr;
   __syncthreads();
-  int lrt = 0;
-  // (not unrolled: one lane mask live at a time)
-#pragma unroll 1
-  for (int w = 0; w < nw; ++w) lrt += s_wsum[w][2];
+  int lr_before, lrt;
+  wave_prefix(&s_wsum[0][2], 3, wave, lane, lr_before, lrt);
   const int bmin = lrt >= plan.bgmv_total ? plan.bgmv_min : INT_MAX;  // uniform
   auto tiles_of = [&](int sc, int bc, int& w8, int& w64) {
     const bool ms = sc >= plan.mfma_min, mb = bc >= bmin;
@@ -292,15 +348,9 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     s_wsum[wave][1] = incm;
   }
   __syncthreads();
-  int tb = 0, ttot = 0, mb = 0, mtot = 0;
-  // (not unrolled: one lane mask live at a time)
-#pragma unroll 1
-  for (int w = 0; w < nw; ++w) {
-    tb += w < wave ? s_wsum[w][0] : 0;
-    ttot += s_wsum[w][0];
-    mb += w < wave ? s_wsum[w][1] : 0;
-    mtot += s_wsum[w][1];
-  }
+  int tb, ttot, mb, mtot;
+  wave_prefix(&s_wsum[0][0], 3, wave, lane, tb, ttot);
+  wave_prefix(&s_wsum[0][1], 3, wave, lane, mb, mtot);
   tb += inct - nt;
   mb += incm - nmf;
   for (int a = a0; a < a1; ++a) {
@@ -335,11 +385,13 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     }
     return lo;
   };
-  for (int f = tid; f < plan.cap; f += kMetaThreads) {
-    int32_t* r = plan.tiles + (size_t)f * LORA_PLAN_WAVE_WORDS;
+  // 8-row records: the real ones (16-byte stores), then the rest of the
+  // capacity (0 rows, tokens -1) as consecutive 16-byte words
+  const int nreal = min(ttot, plan.cap);
+  for (int f = tid; f < nreal; f += kMetaThreads) {
     int slot = 0, rows = 0, vrow = 0;
-    const int32_t* src = nullptr;
-    if (f < ttot) {
+    const int32_t* src = m.sgmv_perm;
+    {
       slot = owner(toff, f);
       const int s0 = slot > 0 ? cs[slot - 1] : 0, b0 = slot > 0 ? cb[slot - 1] : 0;
       const int sc = cs[slot] - s0;
@@ -356,11 +408,26 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
         src = m.bgmv_tok + first;
       }
     }
-    r[0] = slot;
-    r[1] = rows;
-    r[2] = vrow;
-    r[3] = rows > 0 ? rank_of(slot) : 0;
-    for (int i = 0; i < LORA_PLAN_WAVE_WORDS - 4; ++i) r[4 + i] = i < rows ? src[i] : -1;
+    // the tokens are loaded unconditionally (a real record has rows >= 1;
+    // lanes past it repeat its last row), so no branch waits on a load
+    const int last = max(rows, 1) - 1;
+    if (rows <= 0) src = m.sgmv_perm;  // (not expected) element 0 exists for T >= 1
+    int tk[LORA_PLAN_WAVE_ROWS];
+#pragma unroll
+    for (int i = 0; i < LORA_PLAN_WAVE_ROWS; ++i) tk[i] = src[min(i, last)];
+#pragma unroll
+    for (int i = 0; i < LORA_PLAN_WAVE_ROWS; ++i) tk[i] = i < rows ? tk[i] : -1;
+    i32x4* r4 = reinterpret_cast<i32x4*>(plan.tiles + (size_t)f * LORA_PLAN_WAVE_WORDS);
+    r4[0] = i32x4{slot, rows, vrow, rows > 0 ? rank_of(slot) : 0};
+    r4[1] = i32x4{tk[0], tk[1], tk[2], tk[3]};
+    r4[2] = i32x4{tk[4], tk[5], tk[6], tk[7]};
+    r4[3] = i32x4{-1, -1, -1, -1};
+  }
+  {
+    i32x4* r4 = reinterpret_cast<i32x4*>(plan.tiles);
+    const int64_t q1 = (int64_t)plan.cap * (LORA_PLAN_WAVE_WORDS / 4);
+    for (int64_t q = (int64_t)nreal * (LORA_PLAN_WAVE_WORDS / 4) + tid; q < q1; q += kMetaThreads)
+      r4[q] = (q & 3) == 0 ? i32x4{0, 0, 0, 0} : i32x4{-1, -1, -1, -1};
   }
   for (int f = tid; f < plan.mcap; f += kMetaThreads) {
     int slot = 0, rows = 0, vrow = 0, tok0 = -1;
@@ -389,11 +456,8 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       const int t0 = src[0];
       tok0 = src[rows - 1] - t0 == rows - 1 ? t0 : -1;
     }
-    int32_t* r = plan.mtiles + (size_t)f * LORA_PLAN_MFMA_WORDS;
-    r[0] = slot;
-    r[1] = rows > 0 ? rows | (rank_of(slot) << 16) : 0;
-    r[2] = vrow;
-    r[3] = tok0;
+    reinterpret_cast<i32x4*>(plan.mtiles)[f] =
+        i32x4{slot, rows > 0 ? rows | (rank_of(slot) << 16) : 0, vrow, tok0};
   }
 }
 
