@@ -434,7 +434,9 @@ int32_t apply_device_run(const Geo& g, const void* A_pool, const void* B_pool, c
   const int32_t cap = device_tile_cap(T, g.max_loras);
   const bool onepass = device_plan_is_onepass(g, cap);
   const bool mfma = g.dtype == LORA_BF16 && !onepass;
-  const int32_t mcap = mfma ? device_mfma_cap(T, g.max_loras) : 0;
+  const bool all_sgmv = g.R > limit;
+  // no flags and no forced SGMV: every row is a BGMV row
+  const int32_t mcap = mfma ? device_mfma_cap(g, T, prefill != nullptr || all_sgmv) : 0;
   const DevicePlanOut po{tiles,
                          cap,
                          mtiles,
@@ -445,11 +447,17 @@ int32_t apply_device_run(const Geo& g, const void* A_pool, const void* B_pool, c
                          perm,
                          slot_ranks,
                          g.R};
-  if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, g.R > limit, m, counts, st,
+  if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, all_sgmv, m, counts, st,
                                         &po))
     return e;
+  // the 8-row K split is chosen for the records such a batch typically makes
+  // (one partial tile per slot), not for the capacity (two per slot): the
+  // split changes only how the work is spread
+  const int64_t wave_est = std::min<int64_t>(
+      cap, ((int64_t)T + LORA_PLAN_WAVE_ROWS - 1) / LORA_PLAN_WAVE_ROWS +
+               std::min<int64_t>(g.max_loras, T));
   TilePlan tp{perm, tiles, cap, mtiles, mcap, nullptr, mfma_ksplit(g, mcap), T,
-              wave_ksplit(g, cap), nullptr, nullptr, nullptr, /*walk=*/1};
+              wave_ksplit(g, wave_est), nullptr, nullptr, nullptr, /*walk=*/1};
   if (onepass) return run_plan_onepass_list(g, x, A_pool, B_pool, y, tp, st);
   float* v = (float*)(w + d.v);
   if (int32_t e = run_plan_shrink(g, x, A_pool, v, tp, st)) return e;

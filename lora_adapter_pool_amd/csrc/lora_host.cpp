@@ -140,10 +140,20 @@ DeviceLayout device_layout(const Geo& g, int32_t T) {
   d.tiles = o;
   o = align_up(o + (int64_t)device_tile_cap(T, g.max_loras) * LORA_PLAN_WAVE_WORDS * 4, 256);
   d.mtiles = o;
-  o = align_up(o + (int64_t)device_mfma_cap(T, g.max_loras) * LORA_PLAN_MFMA_WORDS * 4, 256);
+  o = align_up(o + (int64_t)device_mfma_cap(g, T, true) * LORA_PLAN_MFMA_WORDS * 4, 256);
   d.v = o;
   d.total = o + (int64_t)LORA_PLAN_MAX_KSPLIT * rows * g.S * g.R * 4;
   return d;
+}
+
+int32_t device_mfma_cap(const Geo& g, int32_t T, bool sgmv) {
+  const int64_t ml = g.max_loras, t = T > 0 ? T : 0;
+  const int64_t pieces = (t + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS;
+  const int64_t slot_bound = pieces + 2 * std::min(t, ml);
+  int64_t runs = sgmv ? std::min(ml, t / sgmv_mfma_min_rows()) : 0;
+  if (t >= bgmv_mfma_min_total(g.R)) runs += std::min(ml, t / bgmv_mfma_min_rows());
+  const int64_t cap = runs > 0 ? std::min(slot_bound, pieces + runs) : 0;
+  return (int32_t)cap;
 }
 
 int32_t sgmv_mfma_min_rows() {

@@ -85,18 +85,22 @@ int32_t mfma_ksplit(const Geo& g, int64_t nm);
 int32_t mfma_ksplit_max(const Geo& g);
 
 // Device-built plan of lora_apply_device: capacities of its 8-row tile
-// records and of its 64-row MFMA tile records (each slot adds at most one
-// partial tile of each size to each of its two row sets), and its workspace
-// (byte offsets): the metadata
-// arrays, the v-row -> token map, both record arrays, then v
-// (LORA_PLAN_MAX_KSPLIT partials of T rows x S x R fp32).
+// records (each slot adds at most one partial tile to each of its two row
+// sets) and of its 64-row MFMA tile records, and its workspace (byte
+// offsets): the metadata arrays, the v-row -> token map, both record arrays,
+// then v (LORA_PLAN_MAX_KSPLIT partials of T rows x S x R fp32).
 inline int32_t device_tile_cap(int32_t T, int32_t max_loras) {
   return (T + LORA_PLAN_WAVE_ROWS - 1) / LORA_PLAN_WAVE_ROWS + 2 * (T < max_loras ? T : max_loras);
 }
-inline int32_t device_mfma_cap(int32_t T, int32_t max_loras) {
-  return (T + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS +
-         2 * (T < max_loras ? T : max_loras);
-}
+// Every MFMA record is a piece of a run of one slot's rows that takes MFMA
+// tiles: its SGMV rows when there are at least sgmv_mfma_min_rows() of them
+// (possible only when `sgmv` says the batch can hold SGMV rows) and, in
+// batches of at least bgmv_mfma_min_total(R) rows, its BGMV rows when there
+// are at least bgmv_mfma_min_rows().  The pieces of runs holding n rows in all
+// number at most ceil(n / 64) + runs, and at most min(max_loras, T / min rows)
+// runs of each kind exist; the count never exceeds the per-slot bound
+// ceil(T / 64) + 2 min(T, max_loras) either.
+int32_t device_mfma_cap(const Geo& g, int32_t T, bool sgmv);
 struct DeviceLayout {
   int64_t counts, sgmv_perm, bgmv_tok, bgmv_ids, seg_starts, seg_lens, seg_ids, perm, tiles,
       mtiles, v, total;

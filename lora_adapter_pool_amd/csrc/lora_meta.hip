@@ -56,20 +56,35 @@ __device__ __forceinline__ uint64_t same_key_lanes(int key, int kbits) {
   return m;
 }
 
+// Inclusive prefix sums over the lanes of each row of 16 (row_incl_scan) and
+// over the whole wavefront (wave_incl_scan), with DPP moves: shifts by 1, 2, 4
+// and 8 lanes within each row (lanes with no source add 0), then lane 15 of
+// rows 0 and 2 added to rows 1 and 3, and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int row_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x = row_incl_scan(x);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Sum of per-wavefront values s[w * stride] over the wavefronts before `wave`
 // (excl) and over all of them (tot): lane w < kMetaWaves holds wavefront w's
-// value and a shuffle scan adds them up, so no wavefront walks the others'.
+// value and a scan over the first row of lanes adds them up, so no wavefront
+// walks the others'.  `wave` is uniform.
 __device__ __forceinline__ void wave_prefix(const int32_t* s, int stride, int wave, int lane,
                                             int& excl, int& tot) {
+  static_assert(kMetaWaves == 16, "one value per lane of the first row");
   int x = lane < kMetaWaves ? s[lane * stride] : 0;
-#pragma unroll
-  for (int o = 1; o < kMetaWaves; o <<= 1) {
-    const int u = __shfl_up(x, o, 64);
-    if (lane >= o) x += u;
-  }
-  tot = __shfl(x, kMetaWaves - 1, 64);
-  const int e = __shfl(x, wave > 0 ? wave - 1 : 0, 64);
-  excl = wave > 0 ? e : 0;
+  x = row_incl_scan(x);
+  tot = __builtin_amdgcn_readlane(x, kMetaWaves - 1);
+  excl = wave > 0 ? __builtin_amdgcn_readlane(x, wave > 0 ? wave - 1 : 0) : 0;
 }
 
 // bins[key] += 1 for every active lane with key >= 0.  Sorted batches give
@@ -96,7 +111,8 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   __shared__ int32_t s_wsum[kMetaThreads / 64][3];
   int32_t* cs = lds;
   int32_t* cb = lds + max_loras;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int nw = kMetaThreads / 64;
   for (int a = tid; a < max_loras; a += kMetaThreads) {
     cs[a] = 0;
@@ -149,15 +165,9 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     v[1] += cb[a];
     v[2] += cs[a] > 0;
   }
-  int inc[3] = {v[0], v[1], v[2]};
+  int inc[3];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int u = __shfl_up(inc[i], o, 64);
-      if (lane >= o) inc[i] += u;
-    }
-  }
+  for (int i = 0; i < 3; ++i) inc[i] = wave_incl_scan(v[i]);
   if (lane == 63) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) s_wsum[wave][i] = inc[i];
@@ -264,16 +274,39 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       hi = wave == 0 ? nbk : 0;
     }
     __syncthreads();
+    // equal keys take consecutive positions in lane order; the lowest lane of
+    // each key moves the key's next free position.  A chunk whose rows all
+    // have one key (sorted batches) skips the per-bit ballots, and while
+    // consecutive such chunks share their key its next position stays in a
+    // register (ckey, cpos: uniform), so only the first of them reads it
+    int ckey = -1, cpos = 0;
     for (int c = lo; c < hi; c += 64) {
       const int i = c + lane;
       const int key = i < hi ? keys[i] : -1;
-      int32_t* pos = par ? &my[key] : (key & 1) ? &cs[key >> 1] : &cb[key >> 1];
-      const int p0 = key >= 0 ? *pos : 0;
-      // equal keys take consecutive positions in lane order; the lowest lane
-      // of each key moves the key's next free position
-      const uint64_t mk = same_key_lanes(key, kbits);
-      const int rank = __popcll(mk & below), cnt = __popcll(mk);
-      const bool first = key >= 0 && (mk & below) == 0;
+      const uint64_t valid = __ballot(key >= 0);
+      if (valid == 0) continue;  // uniform: no row of this chunk has an adapter
+      const int k0 = __builtin_amdgcn_readlane(key, __builtin_ctzll(valid));
+      const bool uni = __ballot(key == k0) == valid;  // uniform
+      int32_t* pos;
+      int p0, rank, cnt;
+      bool first;
+      if (uni) {
+        pos = par ? &my[k0] : (k0 & 1) ? &cs[k0 >> 1] : &cb[k0 >> 1];
+        p0 = k0 == ckey ? cpos : *pos;
+        rank = __popcll(valid & below);
+        cnt = __popcll(valid);
+        first = (int)lane == __builtin_ctzll(valid);
+        ckey = k0;
+        cpos = p0 + cnt;
+      } else {
+        ckey = -1;  // positions move through LDS only
+        pos = par ? &my[key] : (key & 1) ? &cs[key >> 1] : &cb[key >> 1];
+        p0 = key >= 0 ? *pos : 0;
+        const uint64_t mk = same_key_lanes(key, kbits);
+        rank = __popcll(mk & below);
+        cnt = __popcll(mk);
+        first = key >= 0 && (mk & below) == 0;
+      }
       const int p = p0 + rank;
       if (key >= 0 && p < T) {
         const int t = b0 + i;
@@ -313,8 +346,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     const int bc = cb[a] - (a > 0 ? cb[a - 1] : 0);
     lr += bc >= plan.bgmv_min ? bc : 0;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lr += __shfl_xor(lr, o, 64);
+  lr = __builtin_amdgcn_readlane(wave_incl_scan(lr), 63);
   if (lane == 0) s_wsum[wave][2] = lr;
   __syncthreads();
   int lr_before, lrt;
@@ -334,15 +366,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     nt += w8;
     nmf += w64;
   }
-  int inct = nt, incm = nmf;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int ut = __shfl_up(inct, o, 64), um = __shfl_up(incm, o, 64);
-    if (lane >= o) {
-      inct += ut;
-      incm += um;
-    }
-  }
+  const int inct = wave_incl_scan(nt), incm = wave_incl_scan(nmf);
   if (lane == 63) {
     s_wsum[wave][0] = inct;
     s_wsum[wave][1] = incm;

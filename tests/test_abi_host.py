@@ -303,26 +303,46 @@ def test_merge_validation_before_hip():
     assert "max_lora_rank" in L.last_error()
 
 
+def _device_ws_bytes(T, ML, R, S):
+    """lora_apply_device's workspace, written out from its documented layout:
+    count words, metadata, v-row map, 8-row records (one partial tile per slot
+    and row set), 64-row records (pieces of the runs that take MFMA tiles: SGMV
+    runs of >= 16 rows, and BGMV runs of >= 48 rows in batches of >= 2048 rows
+    for R <= 16, >= 1024 rows above), then 8 partials of v."""
+    up = lambda n, a: (n + a - 1) // a * a  # noqa: E731
+    meta = up(16, 256)
+    meta = up(meta + 4 * T, 16)
+    meta = up(meta + 4 * T, 16)
+    meta = up(meta + 4 * T, 16)
+    meta = up(meta + 4 * ML, 16)
+    meta = up(meta + 4 * ML, 16)
+    meta = up(meta + 4 * ML, 16)
+    perm = up(meta + 4 * T, 256)                 # v row -> token
+    cap = -(-T // 8) + 2 * min(ML, T)
+    tiles = up(perm + cap * 16 * 4, 256)         # 8-row records
+    runs = min(ML, T // 16) + (min(ML, T // 48) if T >= (2048 if R <= 16 else 1024) else 0)
+    mcap = min(-(-T // 64) + 2 * min(ML, T), -(-T // 64) + runs)
+    mtiles = up(tiles + mcap * 4 * 4, 256)       # 64-row records
+    return mtiles + 8 * T * S * R * 4            # v: up to 8 partials of T x S x R fp32
+
+
+def test_device_workspace_bytes():
+    """The device workspace follows its documented layout, including the MFMA
+    record capacity at sizes where its two bounds differ."""
+    for ML, R, outs, T in ((6, 16, [256, 128], 100), (64, 16, [512], 256), (64, 16, [512], 5000),
+                           (4, 64, [256], 3000), (300, 32, [256, 256, 64], 700)):
+        d = L.make_desc("bf16", ML, R, 256, outs)
+        assert L.lora_apply_device_workspace_bytes(d, T) == _device_ws_bytes(T, ML, R, len(outs)), \
+            (ML, R, T)
+
+
 def test_apply_device_validation_before_hip():
     """lora_apply_device: workspace size and every argument check on the host,
     before any GPU call."""
     d = L.make_desc("bf16", 6, 16, 256, [256, 128])
     T = 100
     need = L.lora_apply_device_workspace_bytes(d, T)
-    cap = -(-T // 8) + 2 * min(6, T)
-    up = lambda n, a: (n + a - 1) // a * a  # noqa: E731
-    meta = up(16, 256)
-    meta = up(meta + 4 * T, 16)
-    meta = up(meta + 4 * T, 16)
-    meta = up(meta + 4 * T, 16)
-    meta = up(meta + 4 * 6, 16)
-    meta = up(meta + 4 * 6, 16)
-    meta = up(meta + 4 * 6, 16)
-    perm = up(meta + 4 * T, 256)                 # v row -> token
-    tiles = up(perm + cap * 16 * 4, 256)         # 8-row records
-    mcap = -(-T // 64) + 2 * min(6, T)
-    mtiles = up(tiles + mcap * 4 * 4, 256)       # 64-row records
-    assert need == mtiles + 8 * T * 2 * 16 * 4   # v: up to 8 partials of T x S x R fp32
+    assert need == _device_ws_bytes(T, 6, 16, 2)
     ok = [d, FAKE, FAKE, FAKE, FAKE + 4096, T, FAKE, None, 0, FAKE, need]
 
     def with_(i, v):
