@@ -1677,51 +1677,26 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
     s_tok[tid] = (tid < cnt && tk >= 0 && tk < g.T) ? tk : -1;
   }
   // v operands: token row 16 wave + j16, ranks 32 kc + 8 grp .. +8 (kc < 2);
-  // the partials are summed in order 0, 1, ... (missing ones load as zeros)
-  bf16x8 vh[NKC], vl[NKC];
-  {
-    const int row = 16 * wave + j16;
-    const bool row_ok = row < cnt;
-    u32x4 vr[NKC][KP][2];
+  // the partials are summed in order 0, 1, ... (missing ones load as zeros).
+  // Their loads are issued first and summed only after the first chunk's y
+  // and B loads are issued, so the y round trip overlaps the v one (loads
+  // complete in order: waiting for v leaves the later ones in flight)
+  const int row = 16 * wave + j16;
+  const bool row_ok = row < cnt;
+  u32x4 vr[NKC][KP][2];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      const int k0 = 32 * kc + 8 * grp;
-      const bool ok = row_ok && k0 < rr;
-      const uint32_t m = all_or_none(ok);
+  for (int kc = 0; kc < NKC; ++kc) {
+    const int k0 = 32 * kc + 8 * grp;
+    const bool ok = row_ok && k0 < rr;
+    const uint32_t m = all_or_none(ok);
 #pragma unroll
-      for (int p = 0; p < KP; ++p) {
-        const bool pin = p < ksplit;
-        const size_t off =
-            ((size_t)(pin ? p : 0) * v_rows + r0 + (ok ? row : 0)) * SR + s * R + (ok ? k0 : 0);
-        const uint32_t mm = m & all_or_none(pin);
-        vr[kc][p][0] = ld16(v + off) & mm;
-        vr[kc][p][1] = ld16(v + off + 4) & mm;
-      }
-    }
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int p = 0; p < KP; ++p) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          e[4 * h + 0] += __uint_as_float(vr[kc][p][h].x);
-          e[4 * h + 1] += __uint_as_float(vr[kc][p][h].y);
-          e[4 * h + 2] += __uint_as_float(vr[kc][p][h].z);
-          e[4 * h + 3] += __uint_as_float(vr[kc][p][h].w);
-        }
-      }
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t h0 = f32_to_bf16_bits(e[2 * i]), h1 = f32_to_bf16_bits(e[2 * i + 1]);
-        const uint32_t l0 = f32_to_bf16_bits(e[2 * i] - __uint_as_float(h0 << 16));
-        const uint32_t l1 = f32_to_bf16_bits(e[2 * i + 1] - __uint_as_float(h1 << 16));
-        hw[i] = h0 | (h1 << 16);
-        lw[i] = l0 | (l1 << 16);
-      }
-      vh[kc] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-      vl[kc] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+    for (int p = 0; p < KP; ++p) {
+      const bool pin = p < ksplit;
+      const size_t off =
+          ((size_t)(pin ? p : 0) * v_rows + r0 + (ok ? row : 0)) * SR + s * R + (ok ? k0 : 0);
+      const uint32_t mm = m & all_or_none(pin);
+      vr[kc][p][0] = ld16(v + off) & mm;
+      vr[kc][p][1] = ld16(v + off + 4) & mm;
     }
   }
   __syncthreads();  // s_tok
@@ -1759,8 +1734,38 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) yr[r] = ld16_buf_nt(yb, yo[r] + cb);
   };
+  // a group holds at least one chunk (group gi < ceil(chunks / cpw)), so the
+  // first chunk's loads are not held back behind a loop-entry test
+  __builtin_assume(c_begin < c_end);
   u32x4 br[4], yn[4];
   load_chunk(c_begin, br, yn);
+  __builtin_amdgcn_sched_barrier(0);  // the chunk's loads stay ahead of the v sum
+  bf16x8 vh[NKC], vl[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        e[4 * h + 0] += __uint_as_float(vr[kc][p][h].x);
+        e[4 * h + 1] += __uint_as_float(vr[kc][p][h].y);
+        e[4 * h + 2] += __uint_as_float(vr[kc][p][h].z);
+        e[4 * h + 3] += __uint_as_float(vr[kc][p][h].w);
+      }
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h0 = f32_to_bf16_bits(e[2 * i]), h1 = f32_to_bf16_bits(e[2 * i + 1]);
+      const uint32_t l0 = f32_to_bf16_bits(e[2 * i] - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16_bits(e[2 * i + 1] - __uint_as_float(h1 << 16));
+      hw[i] = h0 | (h1 << 16);
+      lw[i] = l0 | (l1 << 16);
+    }
+    vh[kc] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+    vl[kc] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+  }
   for (int c = c_begin; c < c_end; ++c) {
     const int col0 = (c - ch.start[s]) * NC;
     u32x4 yc[4];
