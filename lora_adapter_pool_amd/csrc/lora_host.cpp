@@ -199,22 +199,26 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
                         lora_meta* out) {
   const int32_t limit = bgmv_max_rank > 0 ? bgmv_max_rank : LORA_BGMV_MAX_RANK_DEFAULT;
   const bool all_sgmv = max_lora_rank > limit;
-  // per-slot counters and positions: four arrays of max_loras ints, kept per
-  // thread and reused, so a call allocates nothing once it has seen its pool size
+  // per-slot counters and positions, kept per thread and reused, so a call
+  // allocates nothing once it has seen its pool size: four interleaved count
+  // tables of 2 max_loras + 1 keys (key 2 a + set, or 2 max_loras for a row
+  // without adapter), then the SGMV and BGMV positions
+  const size_t nk = 2 * (size_t)max_loras + 1;
   static thread_local std::vector<int32_t> scratch;
-  if (scratch.size() < 4 * (size_t)max_loras) scratch.resize(4 * (size_t)max_loras);
-  int32_t* cnt_s = scratch.data();
-  int32_t* cnt_b = cnt_s + max_loras;
-  int32_t* pos_s = cnt_b + max_loras;
+  if (scratch.size() < 4 * nk + 2 * (size_t)max_loras) scratch.resize(4 * nk + 2 * (size_t)max_loras);
+  int32_t* cnt4 = scratch.data();
+  int32_t* pos_s = cnt4 + 4 * nk;
   int32_t* pos_b = pos_s + max_loras;
-  std::fill(cnt_s, cnt_s + 2 * (size_t)max_loras, 0);
-  // rows go by runs of equal (id, set): one counter update per run rather than
-  // one per row, whose store-to-load chain on a single counter would
-  // serialise a sorted prefill batch.  Once a run's second row matches, the
-  // rest of the run is found 16 rows at a time (a compare the compiler
-  // vectorises), so long runs cost little and runs of one row cost one test.
+  std::fill(cnt4, cnt4 + 4 * nk, 0);
   const bool per_row_set = !all_sgmv && prefill != nullptr;
   auto in_sgmv = [&](int32_t t) { return all_sgmv || (prefill && prefill[t]); };
+  auto key_of = [&](int32_t t) {
+    const int32_t a = ids[t];
+    return a >= 0 ? 2 * a + (in_sgmv(t) ? 1 : 0) : 2 * max_loras;
+  };
+  // end of the run of rows with row t's key: once a run's second row matches,
+  // the rest of the run is found 16 rows at a time (a compare the compiler
+  // vectorises), so long runs cost little and runs of one row cost one test
   auto run_end = [&](int32_t t) {
     const int32_t a = ids[t];
     const bool sg = in_sgmv(t);
@@ -238,46 +242,84 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
     }
     return u;
   };
-  for (int32_t t = 0; t < T;) {
-    const int32_t u = run_end(t);
-    const int32_t a = ids[t];
-    if (a >= 0) (in_sgmv(t) ? cnt_s : cnt_b)[a] += u - t;
-    t = u;
+  // The first rows decide how the batch is walked.  Long runs of one key (a
+  // sorted prefill batch) go run by run: one counter or position update per
+  // run, where one per row would make a store-to-load chain on a single
+  // counter.  Short runs (mixed decode ids) go row by row, the run search
+  // being pure overhead there; the histogram then counts row t in table
+  // t % 4, so equal neighbours do not chain either.
+  bool by_runs;
+  {
+    const int32_t n = std::min<int32_t>(T, 512);
+    int32_t changes = 0;
+    for (int32_t t = 1; t < n; ++t) changes += key_of(t) != key_of(t - 1);
+    by_runs = (int64_t)changes * 8 < n;
+  }
+  // 1. histogram
+  if (by_runs) {
+    for (int32_t t = 0; t < T;) {
+      const int32_t u = run_end(t);
+      cnt4[key_of(t)] += u - t;
+      t = u;
+    }
+  } else {
+    for (int32_t t = 0; t < T; ++t) ++cnt4[(size_t)(t & 3) * nk + key_of(t)];
   }
   int32_t ns = 0, nb = 0, nseg = 0;
   for (int32_t a = 0; a < max_loras; ++a) {
+    int32_t cs = 0, cb = 0;
+    for (int i = 0; i < 4; ++i) {
+      cs += cnt4[(size_t)i * nk + 2 * a + 1];
+      cb += cnt4[(size_t)i * nk + 2 * a];
+    }
     pos_s[a] = ns;
     pos_b[a] = nb;
-    if (cnt_s[a] > 0) {
+    if (cs > 0) {
       out->seg_starts[nseg] = ns;
-      out->seg_lens[nseg] = cnt_s[a];
+      out->seg_lens[nseg] = cs;
       out->seg_ids[nseg] = a;
       ++nseg;
     }
-    ns += cnt_s[a];
-    nb += cnt_b[a];
+    ns += cs;
+    nb += cb;
   }
   int32_t* const perm = out->sgmv_perm;
   int32_t* const btok = out->bgmv_tok;
   int32_t* const bids = out->bgmv_ids;
-  for (int32_t t = 0; t < T;) {
-    const int32_t u = run_end(t);
-    const int32_t a = ids[t];
-    if (a >= 0) {
-      if (in_sgmv(t)) {
-        const int32_t p = pos_s[a];
-        for (int32_t v = t; v < u; ++v) perm[p + (v - t)] = v;
-        pos_s[a] = p + (u - t);
-      } else {
-        const int32_t p = pos_b[a];
-        for (int32_t v = t; v < u; ++v) {
-          btok[p + (v - t)] = v;
-          bids[p + (v - t)] = a;
+  // 2. placement in token order, which keeps the sort stable
+  if (by_runs) {
+    for (int32_t t = 0; t < T;) {
+      const int32_t u = run_end(t);
+      const int32_t a = ids[t];
+      if (a >= 0) {
+        if (in_sgmv(t)) {
+          const int32_t p = pos_s[a];
+          for (int32_t v = t; v < u; ++v) perm[p + (v - t)] = v;
+          pos_s[a] = p + (u - t);
+        } else {
+          const int32_t p = pos_b[a];
+          for (int32_t v = t; v < u; ++v) {
+            btok[p + (v - t)] = v;
+            bids[p + (v - t)] = a;
+          }
+          pos_b[a] = p + (u - t);
         }
-        pos_b[a] = p + (u - t);
+      }
+      t = u;
+    }
+  } else {
+    // short runs (mixed decode ids): row by row
+    for (int32_t t = 0; t < T; ++t) {
+      const int32_t a = ids[t];
+      if (a < 0) continue;
+      if (in_sgmv(t)) {
+        perm[pos_s[a]++] = t;
+      } else {
+        const int32_t p = pos_b[a]++;
+        btok[p] = t;
+        bids[p] = a;
       }
     }
-    t = u;
   }
   out->num_sgmv_rows = ns;
   out->num_segs = nseg;
@@ -369,11 +411,10 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   const int32_t ns = m.num_sgmv_rows, nb = m.num_bgmv_rows;
   const bool bf = g.dtype == LORA_BF16;
   const int32_t thr = bf ? sgmv_mfma_min_rows() : INT32_MAX;
-  // end of the BGMV run starting at row i
+  // end of the BGMV run starting at row i: the builder sorts the BGMV rows by
+  // id, so a binary search finds it
   auto run_end = [&](int32_t i) {
-    int32_t j = i + 1;
-    while (j < nb && m.bgmv_ids[j] == m.bgmv_ids[i]) ++j;
-    return j;
+    return (int32_t)(std::upper_bound(m.bgmv_ids + i, m.bgmv_ids + nb, m.bgmv_ids[i]) - m.bgmv_ids);
   };
   int32_t bthr = INT32_MAX;
   if (bf) {
@@ -420,14 +461,15 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   int32_t* mt = img + off_mfma;
   int64_t nm = 0;
   // word 3: the tile's first token when its tokens are consecutive (a prefill
-  // sequence usually is), so the kernels need not read them from perm; else -1
+  // sequence usually is), so the kernels need not read them from perm; else -1.
+  // A run's tokens increase (the sort is stable), so they are consecutive
+  // exactly when last - first = rows - 1
   auto emit_mfma = [&](int32_t slot, int32_t first, int32_t len) {
     for (int32_t j = 0; j < len; j += LORA_PLAN_MFMA_ROWS) {
       int32_t* r = mt + nm * LORA_PLAN_MFMA_WORDS;
       const int32_t rows = std::min(LORA_PLAN_MFMA_ROWS, len - j);
       const int32_t* tok = img + first + j;
-      bool consecutive = true;
-      for (int32_t i = 1; i < rows; ++i) consecutive &= tok[i] == tok[0] + i;
+      const bool consecutive = tok[rows - 1] - tok[0] == rows - 1;
       r[0] = slot;
       r[1] = rows | (rank_of(slot) << 16);
       r[2] = first + j;

@@ -94,6 +94,34 @@ def test_builder_long_runs_vs_oracle_fuzz():
         check_meta_properties(ids, (pre != 0).astype(np.uint8), R, got, 64)
 
 
+def test_builder_walk_choice_vs_oracle():
+    """The builder walks a batch by runs or row by row depending on its first
+    512 rows; batches whose head misleads that choice (a sorted head over a
+    mixed tail, a mixed head over long runs, runs crossing the 512-row mark)
+    still sort exactly as the oracle's builder does."""
+    rng = np.random.default_rng(9)
+    for trial in range(60):
+        n = int(rng.integers(1, 40))
+        head = int(rng.integers(400, 700))
+        tail = int(rng.integers(0, 3000))
+        sorted_ids = np.sort(rng.integers(-1, n, size=head)).astype(np.int32)
+        mixed_ids = rng.integers(-1, n, size=tail).astype(np.int32)
+        if trial % 2:
+            ids = np.concatenate([mixed_ids[: head], np.sort(rng.integers(-1, n, size=tail))])
+        else:
+            ids = np.concatenate([sorted_ids, mixed_ids])
+        ids = ids.astype(np.int32)
+        pre = (rng.random(ids.size) < (0.5 if trial % 3 else 0.0)).astype(np.uint8)
+        if trial % 3 == 1:  # flags in runs too
+            pre = np.repeat(rng.integers(0, 2, size=-(-ids.size // 64)), 64)[: ids.size].astype(np.uint8)
+        R = int(rng.choice([16, 64, 128]))
+        got = L.lora_build_meta(ids, pre, n, R, 0)
+        ref = oracle.build_meta(ids.tolist(), pre.tolist(), R, 64)
+        for k in META_KEYS:
+            assert got[k].tolist() == list(ref[k]), (trial, k)
+        check_meta_properties(ids, pre, R, got, 64)
+
+
 def test_device_builder_validates_before_hip():
     """lora_build_meta_device rejects bad arguments before any HIP call."""
     import ctypes
