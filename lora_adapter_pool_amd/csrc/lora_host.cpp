@@ -200,16 +200,15 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
   const int32_t limit = bgmv_max_rank > 0 ? bgmv_max_rank : LORA_BGMV_MAX_RANK_DEFAULT;
   const bool all_sgmv = max_lora_rank > limit;
   // per-slot counters and positions, kept per thread and reused, so a call
-  // allocates nothing once it has seen its pool size: four interleaved count
-  // tables of 2 max_loras + 1 keys (key 2 a + set, or 2 max_loras for a row
-  // without adapter), then the SGMV and BGMV positions
+  // allocates nothing once it has seen its pool size: up to four interleaved
+  // count tables of 2 max_loras + 1 keys (key 2 a + set, or 2 max_loras for a
+  // row without adapter), then the SGMV and BGMV positions
   const size_t nk = 2 * (size_t)max_loras + 1;
   static thread_local std::vector<int32_t> scratch;
   if (scratch.size() < 4 * nk + 2 * (size_t)max_loras) scratch.resize(4 * nk + 2 * (size_t)max_loras);
   int32_t* cnt4 = scratch.data();
   int32_t* pos_s = cnt4 + 4 * nk;
   int32_t* pos_b = pos_s + max_loras;
-  std::fill(cnt4, cnt4 + 4 * nk, 0);
   const bool per_row_set = !all_sgmv && prefill != nullptr;
   auto in_sgmv = [&](int32_t t) { return all_sgmv || (prefill && prefill[t]); };
   auto key_of = [&](int32_t t) {
@@ -246,29 +245,39 @@ int32_t build_meta_core(const int32_t* ids, const uint8_t* prefill, int32_t T,
   // sorted prefill batch) go run by run: one counter or position update per
   // run, where one per row would make a store-to-load chain on a single
   // counter.  Short runs (mixed decode ids) go row by row, the run search
-  // being pure overhead there; the histogram then counts row t in table
-  // t % 4, so equal neighbours do not chain either.
+  // being pure overhead there; in a batch that is large next to its count
+  // table the histogram then counts row t in table t % 4, so equal neighbours
+  // do not chain either.
   bool by_runs;
   {
     const int32_t n = std::min<int32_t>(T, 512);
     int32_t changes = 0;
-    for (int32_t t = 1; t < n; ++t) changes += key_of(t) != key_of(t - 1);
+    for (int32_t t = 1, prev = n > 0 ? key_of(0) : 0; t < n; ++t) {
+      const int32_t k = key_of(t);
+      changes += k != prev;
+      prev = k;
+    }
     by_runs = (int64_t)changes * 8 < n;
   }
-  // 1. histogram
+  // 1. histogram (four tables only for batches large next to them: clearing
+  //    and summing them costs more than the chains they break in small ones)
+  const int32_t ntab = !by_runs && (int64_t)T >= 8 * (int64_t)nk ? 4 : 1;
+  std::fill(cnt4, cnt4 + ntab * nk, 0);
   if (by_runs) {
     for (int32_t t = 0; t < T;) {
       const int32_t u = run_end(t);
       cnt4[key_of(t)] += u - t;
       t = u;
     }
-  } else {
+  } else if (ntab == 4) {
     for (int32_t t = 0; t < T; ++t) ++cnt4[(size_t)(t & 3) * nk + key_of(t)];
+  } else {
+    for (int32_t t = 0; t < T; ++t) ++cnt4[key_of(t)];
   }
   int32_t ns = 0, nb = 0, nseg = 0;
   for (int32_t a = 0; a < max_loras; ++a) {
     int32_t cs = 0, cb = 0;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < ntab; ++i) {
       cs += cnt4[(size_t)i * nk + 2 * a + 1];
       cb += cnt4[(size_t)i * nk + 2 * a];
     }
@@ -412,9 +421,16 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
   const bool bf = g.dtype == LORA_BF16;
   const int32_t thr = bf ? sgmv_mfma_min_rows() : INT32_MAX;
   // end of the BGMV run starting at row i: the builder sorts the BGMV rows by
-  // id, so a binary search finds it
+  // id, so past its first 16 rows (short runs of mixed decode ids end there,
+  // where a search's unpredictable branches would cost more) a binary search
+  // finds it
   auto run_end = [&](int32_t i) {
-    return (int32_t)(std::upper_bound(m.bgmv_ids + i, m.bgmv_ids + nb, m.bgmv_ids[i]) - m.bgmv_ids);
+    const int32_t a = m.bgmv_ids[i];
+    const int32_t lin = std::min(nb, i + 16);
+    int32_t j = i + 1;
+    while (j < lin && m.bgmv_ids[j] == a) ++j;
+    if (j < lin || j == nb) return j;
+    return (int32_t)(std::upper_bound(m.bgmv_ids + j, m.bgmv_ids + nb, a) - m.bgmv_ids);
   };
   int32_t bthr = INT32_MAX;
   if (bf) {
