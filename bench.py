@@ -157,20 +157,32 @@ class Setup:
         self.v = torch.zeros((parts * max(rows, 1), S * R), dtype=torch.float32,
                              device="cuda")
         self.bytes_per_rep = per
+        # the arguments of every call, converted once: a step is one ctypes
+        # call, as a caller's serving loop would make it (numpy's `.ctypes`
+        # and torch's data_ptr() build objects on every access)
+        self._desc_ref = ctypes.byref(self.desc)
+        self._ids_p = self.ids.ctypes.data
+        self._pre_p = self.pre.ctypes.data
+        self._ranks_p = self.slot_ranks.ctypes.data if self.slot_ranks is not None else None
+        self._ws_p = self.ws.data_ptr()
+        self._stage_p = [t.data_ptr() for t in self.stage]
+        self._plan_ref = ctypes.byref(self.plan)
+        self._image_p = self.image.data_ptr()
+        self._image_host_p = self.image_host.ctypes.data
+        self._v_p = self.v.data_ptr()
+        self._lib = L.lib()
         torch.cuda.synchronize()
 
     def _apply(self, r, stage_ptr, stream_ptr):
-        lib = self.L.lib()
-        if self.slot_ranks is None:
-            return lib.lora_apply(ctypes.byref(self.desc), self.pA[r], self.pB[r], self.px[r],
-                                  self.py[r], self.T, self.ids.ctypes.data, self.pre.ctypes.data,
-                                  0, self.ws.data_ptr(), self.ws_bytes, stage_ptr, self.mh_bytes,
-                                  stream_ptr)
-        return lib.lora_apply_ranked(ctypes.byref(self.desc), self.pA[r], self.pB[r], self.px[r],
-                                     self.py[r], self.T, self.ids.ctypes.data,
-                                     self.pre.ctypes.data, 0, self.slot_ranks.ctypes.data,
-                                     self.ws.data_ptr(), self.ws_bytes, stage_ptr, self.mh_bytes,
-                                     stream_ptr)
+        lib = self._lib
+        if self._ranks_p is None:
+            return lib.lora_apply(self._desc_ref, self.pA[r], self.pB[r], self.px[r], self.py[r],
+                                  self.T, self._ids_p, self._pre_p, 0, self._ws_p, self.ws_bytes,
+                                  stage_ptr, self.mh_bytes, stream_ptr)
+        return lib.lora_apply_ranked(self._desc_ref, self.pA[r], self.pB[r], self.px[r],
+                                     self.py[r], self.T, self._ids_p, self._pre_p, 0,
+                                     self._ranks_p, self._ws_p, self.ws_bytes, stage_ptr,
+                                     self.mh_bytes, stream_ptr)
 
     def apply_step(self, i, stream_ptr):
         import torch
@@ -179,14 +191,14 @@ class Setup:
         if self.small_plan:
             # the plan travels in the kernel arguments: the GPU never reads the
             # staging buffer, so one buffer serves every call without events
-            st = self._apply(r, self.stage[0].data_ptr(), stream_ptr)
+            st = self._apply(r, self._stage_p[0], stream_ptr)
             if st != 0:
                 raise RuntimeError(f"lora_apply failed: {L.last_error()}")
             return
         j = i % self.nstage
         if self.stage_ev[j] is not None:
             self.stage_ev[j].synchronize()
-        st = self._apply(r, self.stage[j].data_ptr(), stream_ptr)
+        st = self._apply(r, self._stage_p[j], stream_ptr)
         if st != 0:
             raise RuntimeError(f"lora_apply failed: {L.last_error()}")
         ev = self.stage_ev[j] or torch.cuda.Event()
@@ -197,25 +209,23 @@ class Setup:
         """One launch group of the plan (replica i): 'shrink', 'expand', or
         'apply' (both stages in the one launch lora_apply makes for a small
         decode plan)."""
-        L = self.L
-        lib = L.lib()
+        lib = self._lib
         r = i % self.nrep
-        d = ctypes.byref(self.desc)
+        d = self._desc_ref
         if which == "apply":
             st = lib.lora_plan_apply(d, self.px[r], self.pA[r], self.pB[r], self.py[r], self.T,
-                                     ctypes.byref(self.plan), self.image.data_ptr(),
-                                     self.image_host.ctypes.data, self.ws.data_ptr(),
-                                     self.ws_bytes, stream_ptr)
+                                     self._plan_ref, self._image_p, self._image_host_p,
+                                     self._ws_p, self.ws_bytes, stream_ptr)
         elif which == "shrink":
-            st = lib.lora_plan_shrink(d, self.px[r], self.pA[r], self.v.data_ptr(), self.T,
-                                      ctypes.byref(self.plan), self.image.data_ptr(),
-                                      self.image_host.ctypes.data, stream_ptr)
+            st = lib.lora_plan_shrink(d, self.px[r], self.pA[r], self._v_p, self.T,
+                                      self._plan_ref, self._image_p, self._image_host_p,
+                                      stream_ptr)
         else:
-            st = lib.lora_plan_expand(d, self.v.data_ptr(), self.pB[r], self.py[r], self.T,
-                                      ctypes.byref(self.plan), self.image.data_ptr(),
-                                      self.image_host.ctypes.data, stream_ptr)
+            st = lib.lora_plan_expand(d, self._v_p, self.pB[r], self.py[r], self.T,
+                                      self._plan_ref, self._image_p, self._image_host_p,
+                                      stream_ptr)
         if st != 0:
-            raise RuntimeError(f"{which} failed: {L.last_error()}")
+            raise RuntimeError(f"{which} failed: {self.L.last_error()}")
 
     def kernels(self):
         """Names of the kernels each launch group runs for this batch."""
@@ -563,10 +573,12 @@ def device_plan_leg(s, steps, stream_ptr):
     nws = L.lora_apply_device_workspace_bytes(s.desc, s.T)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
 
+    ids_p, pre_p, ws_p = ids_d.data_ptr(), pre_d.data_ptr(), ws.data_ptr()
+
     def step(i):
         r = i % s.nrep
-        if lib.lora_apply_device(d, s.pA[r], s.pB[r], s.px[r], s.py[r], s.T, ids_d.data_ptr(),
-                                 pre_d.data_ptr(), 0, ws.data_ptr(), nws, stream_ptr):
+        if lib.lora_apply_device(d, s.pA[r], s.pB[r], s.px[r], s.py[r], s.T, ids_p, pre_p, 0,
+                                 ws_p, nws, stream_ptr):
             raise RuntimeError(f"lora_apply_device failed: {L.last_error()}")
 
     for i in range(5):
