@@ -304,10 +304,24 @@ def _device_plan_counts(ids, prefill, max_loras, R, mfma_min, bgmv_min, bgmv_tot
     return wave, mfma
 
 
+def _mfma_cap(T, ml, sgmv, mfma_min, bmin, btot):
+    """The device plan's 64-row record capacity as documented: ceil(T/64) plus
+    the runs that can take MFMA tiles (at most min(ml, T // mfma_min) SGMV
+    runs when the batch can hold SGMV rows; in batches of at least btot rows,
+    at most min(ml, T // bmin) BGMV runs), and never more than the per-slot
+    bound ceil(T/64) + 2 min(ml, T)."""
+    runs = (min(ml, T // mfma_min) if sgmv else 0) + (min(ml, T // bmin) if T >= btot else 0)
+    if runs == 0:
+        return 0
+    return min(-(-T // 64) + 2 * min(ml, T), -(-T // 64) + runs)
+
+
 def test_device_plan_capacity_bounds():
     """The device plan's record capacities, ceil(T/8) + 2 min(max_loras, T)
-    8-row records and ceil(T/64) + 2 min(max_loras, T) 64-row records, cover
-    every batch: random mixes, one row per slot in each set, long runs."""
+    8-row records and the 64-row capacity above, cover every batch: random
+    mixes, one row per slot in each set, long runs, and batches built to reach
+    the 64-row bound (every slot with exactly the SGMV threshold's rows, BGMV
+    runs of exactly the run threshold in batches at the total threshold)."""
     rng = np.random.default_rng(3)
     cases = []
     for _ in range(300):
@@ -320,9 +334,20 @@ def test_device_plan_capacity_bounds():
     for ml in (1, 7, 64):  # every slot with one SGMV row and one BGMV row
         ids = np.repeat(np.arange(ml, dtype=np.int32), 2)
         cases.append((ml, ids, np.tile(np.array([1, 0], np.uint8), ml)))
+    for ml in (3, 40, 130):  # every slot at the SGMV threshold, then BGMV runs of 48
+        sg = np.repeat(np.arange(ml, dtype=np.int32), 16)
+        bg = np.repeat(np.arange(ml, dtype=np.int32), 48)
+        extra = np.zeros(max(0, 2048 - sg.size - bg.size), np.int32)  # reach the total threshold
+        ids = np.concatenate([sg, bg, extra])
+        pre = np.concatenate([np.ones(sg.size, np.uint8), np.zeros(bg.size + extra.size, np.uint8)])
+        cases.append((ml, ids, pre))
+        cases.append((ml, np.concatenate([bg, extra]), np.zeros(bg.size + extra.size, np.uint8)))
     for ml, ids, pre in cases:
         T = ids.size
-        for mfma_min, bmin, btot in ((16, 48, 1024), (1, 1, 0), (2 ** 31 - 1,) * 3):
+        for mfma_min, bmin, btot in ((16, 48, 1024), (16, 48, 2048), (1, 1, 0),
+                                     (2 ** 31 - 1,) * 3):
             wave, mfma = _device_plan_counts(ids, pre, ml, 16, mfma_min, bmin, btot)
             assert wave <= -(-T // 8) + 2 * min(ml, T)
-            assert mfma <= -(-T // 64) + 2 * min(ml, T)
+            assert mfma <= _mfma_cap(T, ml, True, mfma_min, bmin, btot), (ml, T, mfma_min)
+            if not pre.any():  # no SGMV row: the bound without flags holds too
+                assert mfma <= _mfma_cap(T, ml, False, mfma_min, bmin, btot), (ml, T, mfma_min)
