@@ -252,6 +252,47 @@ def config_mlp_mixed(seed: int = 0, n_prefill: int = 8, len_lo: int = 128, len_h
     return gu, dn
 
 
+def config_random(seed: int, max_T: int = 900) -> Workload:
+    """A seeded random shape and batch, for fuzzing the dispatch: dtype;
+    in_features and one to three slice widths (multiples of 8, most not of
+    64); slot count, padded rank and each slot's own rank; alpha and rsLoRA;
+    and a batch of sorted prefill segments and decode rows (uniform or Zipf
+    ids), with rows without adapter, in a random order of blocks."""
+    rng = np.random.default_rng(10_000 + seed)
+    dtype = "bf16" if rng.random() < 0.75 else "f32"
+    K = 8 * int(rng.integers(1, 513))
+    S = int(rng.integers(1, 4))
+    outs = [8 * int(rng.integers(1, 257)) for _ in range(S)]
+    R = int(rng.choice([8, 16, 24, 32, 40, 64, 72, 128]))
+    ML = int(rng.integers(1, 48))
+    rslora = bool(rng.random() < 0.3)
+    used = sorted(rng.choice(ML, size=int(rng.integers(1, ML + 1)), replace=False).tolist())
+    ranks = {a: int(rng.integers(1, R + 1)) for a in used}
+    alphas = {a: float(rng.choice([1.0, 8.0, 16.0, 2.0 * ranks[a]])) for a in used}
+    slots = _draw_slots(rng, dtype, K, outs, ranks, alphas, rslora)
+    p_none = float(rng.choice([0.0, 0.1, 0.5]))
+    probs = zipf_probs(len(used), 1.1) if rng.random() < 0.5 else np.full(len(used), 1.0 / len(used))
+    blocks = []  # (ids, flags)
+    budget = int(rng.integers(1, max_T + 1))
+    while budget > 0:
+        n = int(min(budget, rng.integers(1, 400)))
+        if rng.random() < 0.5:  # a prefill segment of one adapter (or none)
+            a = -1 if rng.random() < p_none else int(rng.choice(used))
+            blocks.append((np.full(n, a, np.int32), np.ones(n, np.uint8)))
+        else:  # decode rows
+            ids = rng.choice(np.asarray(used, np.int32), size=n, p=probs).astype(np.int32)
+            ids[rng.random(n) < p_none] = -1
+            blocks.append((ids, np.zeros(n, np.uint8)))
+        budget -= n
+    order = rng.permutation(len(blocks))
+    ids = np.concatenate([blocks[i][0] for i in order])
+    flags = np.concatenate([blocks[i][1] for i in order])
+    x, y = _draw_xy(rng, dtype, ids.size, K, sum(outs))
+    return Workload(name=f"random{seed}", dtype=dtype, in_features=K, out_features=outs,
+                    max_loras=ML, max_lora_rank=R, slots=slots, ids=ids, prefill=flags, x=x,
+                    y_in=y, info={"seed": seed, "bgmv_max_rank": int(rng.choice([0, 8, 16, 64, 128]))})
+
+
 def config_integer(seed: int = 0, T: int = 96, K: int = 520, outs: Sequence[int] = (264, 136),
                    max_loras: int = 6, max_lora_rank: int = 64,
                    ranks: Sequence[int] = (8, 16, 64, 32, 48, 64), prefill_frac: float = 0.5,
