@@ -4,7 +4,8 @@ lora_apply_device with a workspace of the caller's, on two calls in a row, the
 second with a smaller batch: equal bit for bit (the same kernels, plan and K
 splits), and within tolerance of the fp64 oracle.  The one-launch decode form,
 the two-stage 8-row tile form, 64-row MFMA prefill tiles and an fp32 pool are
-each covered; free device memory does not change across the second call."""
+each covered, and twelve pairs of random shapes and batches; free device
+memory does not change across the second call."""
 import numpy as np
 import pytest
 
@@ -71,11 +72,8 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("case", sorted(CASES))
-def test_noalloc_equals_device_path_twice(case):
+def _check_pair(case, first, second):
     import torch
-    say(f"[gpu] no-alloc entry point: {case}")
-    first, second = CASES[case]()
     assert second.T < first.T
     for k, wl in enumerate((first, second)):
         pool = make_pool(wl)
@@ -91,3 +89,25 @@ def test_noalloc_equals_device_path_twice(case):
             assert free1 == free0, "the no-alloc entry point changed free device memory"
         check_rows(wl, y_na, label=f"{case} call {k + 1} (no-alloc) vs oracle")
         del pool, y_ref, y_na
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_noalloc_equals_device_path_twice(case):
+    say(f"[gpu] no-alloc entry point: {case}")
+    _check_pair(case, *CASES[case]())
+
+
+def _random_pair(seed):
+    """A random shape and batch (workloads.config_random), then a smaller one
+    of another random shape."""
+    first = W.config_random(seed, 900)
+    return first, W.config_random(seed + 500, max(1, first.T - 1))
+
+
+RANDOM_SEEDS = list(range(12))  # (each first batch has more than one row)
+
+
+@pytest.mark.parametrize("seed", RANDOM_SEEDS)
+def test_noalloc_random_shapes_twice(seed):
+    say(f"[gpu] no-alloc entry point: random shapes, seed {seed}")
+    _check_pair(f"random {seed}", *_random_pair(seed))
