@@ -396,7 +396,7 @@ def merge_leg(seed, stream_ptr, cpu=True):
         nbytes = 2 * out_s * K * 2 + 64 * K * 2 + out_s * 64 * 2
         res[name] = {"us": round(us, 2), "GBs": round(nbytes / us / 1e3, 1),
                      "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3),
-                     "kernel": "merge_mfma_kernel"}
+                     "kernel": "merge_rows_kernel<2>"}  # (ranks <= 128; rank 64 here)
         del pool, A, B, W0, Ws, Wos
         torch.cuda.empty_cache()
     # one adapter for the whole batch: 16 sequences of 64..1024 tokens, in = out = 4096

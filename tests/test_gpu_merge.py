@@ -68,7 +68,7 @@ def _merge_and_check(wl, seeds=(0,), integer=False, in_place=False, label=""):
         f"R {wl.max_lora_rank}: worst {worst} ulp")
 
 
-@pytest.mark.parametrize("R", [16, 24, 64, 128])
+@pytest.mark.parametrize("R", [16, 24, 64, 96, 128, 256])
 def test_merge_bf16_ragged_tiles(R):
     # 520 x 1032 and 1032 x 520 weights: partial 128-row and 64-column tiles;
     # adapters of mixed ranks in a pool of rank R
@@ -77,6 +77,18 @@ def test_merge_bf16_ragged_tiles(R):
                                 rank_choices=(8, min(R, 16), R), max_lora_rank=R)
     for wl in (gu, dn):
         _merge_and_check(wl, label=f"{wl.name} bf16 R={R}")
+
+
+@pytest.mark.parametrize("nblk", ["1", "3", "8"])
+def test_merge_row_blocks_exact(nblk, monkeypatch):
+    # ranks <= 128: a workgroup walks several 64-row blocks of W over its 256
+    # columns; 1032 rows (17 blocks) and 2056 x 1032 leave the last workgroup a
+    # partial block and blocks past the end; exact on integer inputs
+    monkeypatch.setenv("LORA_MERGE_NBLK", nblk)
+    for K, out, R in ((520, 1032, 64), (1032, 2056, 128), (264, 520, 32)):
+        wl = W.config_integer(seed=K + out + R, T=4, K=K, outs=(out,), max_loras=2,
+                              max_lora_rank=R, ranks=(R, 8))
+        _merge_and_check(wl, integer=True, label=f"row blocks {nblk}: K={K} out={out} R={R}")
 
 
 def test_merge_exact_integer():
