@@ -69,9 +69,23 @@ __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3..0 and 15..14,
 // expcnt 6..4, lgkmcnt 11..8): at most 4 vector memory operations and no LDS
-// operation outstanding; no vector memory operation outstanding
+// operation outstanding; no vector memory operation outstanding; no LDS
+// operation outstanding (vector memory operations may be)
 constexpr int kWaitVm4Lgkm0 = 0x0074;
 constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// A workgroup barrier for the reuse of LDS only: each wave's LDS accesses
+// are complete, its global stores may still be in flight.  __syncthreads also
+// orders global memory at workgroup scope, so every wave would first wait for
+// its stores to land, a memory round trip per barrier.  (The empty asm
+// statements keep the compiler from moving LDS accesses across the barrier.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // All-ones or all-zeros, to zero a loaded value with a bit-AND: a select on a
 // loaded value lets the compiler sink the load under a branch, after which it
@@ -276,7 +290,7 @@ template <int TM> struct TileRows {
 template <int TM, int MODE>
 __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
                                           const PlanArg<MODE>& pa, TileRows<TM>& tr,
-                                          bool copy = false) {
+                                          bool copy = false, bool pre = false, int prew = 0) {
   static_assert(TM <= LORA_PLAN_WAVE_WORDS - 4, "a tile record holds at most 12 tokens");
   const int lane = threadIdx.x & 63;
   tr.rank = g.R;
@@ -306,7 +320,8 @@ __device__ __forceinline__ bool tile_rows(const RowList& L, const Geo& g, int f,
     }
   } else if constexpr (MODE == kList || MODE == kListWalk) {
     if (f >= L.num_tiles) return false;
-    const int w = L.tiles[(size_t)f * LORA_PLAN_WAVE_WORDS + (lane & 15)];
+    // (pre: prew is this lane's word of record f, loaded earlier by the caller)
+    const int w = pre ? prew : L.tiles[(size_t)f * LORA_PLAN_WAVE_WORDS + (lane & 15)];
     if (copy && L.copy_tiles && threadIdx.x < LORA_PLAN_WAVE_WORDS)
       L.copy_tiles[(size_t)f * LORA_PLAN_WAVE_WORDS + threadIdx.x] = w;
     const int sid = __builtin_amdgcn_readlane(w, 0);
@@ -868,15 +883,25 @@ __global__ __launch_bounds__(kOnepassCols) void decode_onepass_kernel(
 // waves' partial tiles are summed in a fixed order in LDS, so the result does
 // not depend on timing.  Splitting K over workgroups spreads the x and A
 // loads over more compute units.
+// (the body takes its workgroup index bid among nwg workgroups and its LDS,
+// tile_shrink_lds<NT>() 16-byte aligned floats, so that a combined launch can
+// run it beside the 64-row shrink)
+template <int NT> constexpr int tile_shrink_lds() {
+  return kTileShrinkWaves * kWaveTileRows * (16 * NT + 1);
+}
+
 template <int NT, int CB, int MODE>
-__global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, float* __restrict__ v,
-    RowList L, Geo g, int kparts, int v_rows, PlanArg<MODE> pa) {
+__device__ __forceinline__ void shrink_tile_mfma_body(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ A,
+                                                      float* __restrict__ v, const RowList& L,
+                                                      const Geo& g, int kparts, int v_rows,
+                                                      const PlanArg<MODE>& pa, int bid, int nwg,
+                                                      float* lds, bool pre = false,
+                                                      int prew = 0) {
   constexpr int TM = kWaveTileRows, NW = kTileShrinkWaves, RM = 16 * NT, SB = CB / 2;
   static_assert(TM == 8, "x rows fill lanes l % 8");
   static_assert(SB >= 1 && SB * (1 + 2 * NT) <= 18, "a batch keeps at most 18 loads per lane in flight");
-  __shared__ float red[NW][TM][RM + 1];
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  float (*red)[TM][RM + 1] = reinterpret_cast<float (*)[TM][RM + 1]>(lds);
   const int per_tile = g.S * kparts;
   const int f0 = bid / per_tile;
   const int rem = bid - f0 * per_tile;
@@ -886,11 +911,14 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
   // records f0, f0 + G, ... (G = the grid's records) until the first one
   // without rows (its records come first, then empty ones to its capacity)
   constexpr bool kWalk = MODE == kListWalk;
-  const int G = kWalk ? (int)(gridDim.x / per_tile) : 1;
+  const int G = kWalk ? nwg / per_tile : 1;
+  if (kWalk && f0 >= G) return;  // workgroups past whole groups of per_tile take no records
   for (int f = f0;; f += G) {
-  if (kWalk && f != f0) __syncthreads();  // red of the previous record is read
+  if (kWalk && f != f0) lds_barrier();  // red of the previous record is read
   TileRows<TM> tr;
-  if (!tile_rows<TM, MODE>(L, g, f, pa, tr, s == 0 && part == 0) || tr.cnt <= 0) return;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr, s == 0 && part == 0, pre && f == f0, prew) ||
+      tr.cnt <= 0)
+    return;
   if (tr.valid == 0) {
     if (kWalk) continue;
     return;
@@ -965,6 +993,15 @@ __global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel
   }
 }
 
+template <int NT, int CB, int MODE>
+__global__ __launch_bounds__(64 * kTileShrinkWaves) void shrink_tile_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, float* __restrict__ v,
+    RowList L, Geo g, int kparts, int v_rows, PlanArg<MODE> pa) {
+  __shared__ __align__(16) float red[tile_shrink_lds<NT>()];
+  shrink_tile_mfma_body<NT, CB, MODE>(x, A, v, L, g, kparts, v_rows, pa,
+                                      xcd_remap(blockIdx.x, gridDim.x), (int)gridDim.x, red);
+}
+
 // ------------------------------- expand (MFMA, wavefront tiles, bf16, R <= 64)
 //
 // grid = tiles * column chunks (kTileExpandCols columns of one slice each),
@@ -984,16 +1021,28 @@ constexpr int kTileExpandWaves = 4;
 constexpr int kTileExpandPairs = 4;  // pairs of 16-column tiles per wave
 constexpr int kTileExpandCols = 32 * kTileExpandPairs * kTileExpandWaves;
 
+// (the body takes its workgroup index bid among nwg workgroups and its LDS,
+// tile_expand_lds<NKC>() 16-byte aligned elements: the hi rows, then the lo
+// rows, so that a combined launch can run it beside the 64-row expand)
+template <int NKC> constexpr int tile_expand_ldv() { return 32 * NKC + 8; }
+template <int NKC> constexpr int tile_expand_lds() {
+  return 2 * kWaveTileRows * tile_expand_ldv<NKC>();
+}
+
 template <int NKC, int KP, int MODE>
-__global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel(
-    const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
-    RowList L, Geo g, Chunks ch, int kparts, int v_rows, PlanArg<MODE> pa) {
+__device__ __forceinline__ void expand_tile_mfma_body(const float* __restrict__ v,
+                                                      const uint16_t* __restrict__ B,
+                                                      uint16_t* __restrict__ y, const RowList& L,
+                                                      const Geo& g, const Chunks& ch, int kparts,
+                                                      int v_rows, const PlanArg<MODE>& pa, int bid,
+                                                      int nwg, uint16_t* lds, bool pre = false,
+                                                      int prew = 0) {
   constexpr int TM = kWaveTileRows, PPW = kTileExpandPairs, NW = kTileExpandWaves;
-  constexpr int LDV = 32 * NKC + 8;  // LDS row of v in bf16 (ranks covered + padding)
+  constexpr int LDV = tile_expand_ldv<NKC>();  // LDS row of v in bf16 (ranks covered + padding)
   static_assert(TM <= 16 && TM * 64 / 4 <= 64 * NW, "one v vector per thread");
-  __shared__ __align__(16) uint16_t vh[TM * LDV];
-  __shared__ __align__(16) uint16_t vl[TM * LDV];
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  static_assert((TM * LDV * 2) % 16 == 0, "the lo rows start 16-byte aligned");
+  uint16_t* vh = lds;
+  uint16_t* vl = lds + TM * LDV;
   const int f0 = bid / ch.total;
   const int cidx = bid - f0 * ch.total;
   int s = 0;
@@ -1006,17 +1055,24 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
   // records f0, f0 + G, ... (G = the grid's records) until the first one
   // without rows (its records come first, then empty ones to its capacity)
   constexpr bool kWalk = MODE == kListWalk;
-  const int G = kWalk ? (int)(gridDim.x / ch.total) : 1;
+  const int G = kWalk ? nwg / ch.total : 1;
+  if (kWalk && f0 >= G) return;  // workgroups past whole groups of ch.total take no records
   for (int f = f0;; f += G) {
-  if (kWalk && f != f0) __syncthreads();  // vh / vl of the previous record are read
+  if (kWalk && f != f0) lds_barrier();  // vh / vl of the previous record are read
   TileRows<TM> tr;
-  if (!tile_rows<TM, MODE>(L, g, f, pa, tr) || tr.cnt <= 0) return;
+  if (!tile_rows<TM, MODE>(L, g, f, pa, tr, false, pre && f == f0, prew) || tr.cnt <= 0)
+    return;
   if (tr.valid == 0) {
     if (kWalk) continue;
     return;
   }
   const int a = tr.aid[0];  // one adapter per tile
-  const int tid = threadIdx.x, lane = tid & 63;
+  // (in a walk the thread index passes through an empty asm statement, so the
+  // lane-dependent offsets below are recomputed per record rather than held
+  // in registers across the loop, which would not fit four workgroups per CU)
+  int tid = threadIdx.x;
+  if constexpr (kWalk) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int i16 = lane & 15, g4 = lane >> 4;
   const int R = g.R;
@@ -1124,6 +1180,15 @@ __global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel
   }
 }
 
+template <int NKC, int KP, int MODE>
+__global__ __launch_bounds__(64 * kTileExpandWaves) void expand_tile_mfma_kernel(
+    const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
+    RowList L, Geo g, Chunks ch, int kparts, int v_rows, PlanArg<MODE> pa) {
+  __shared__ __align__(16) uint16_t lds[tile_expand_lds<NKC>()];
+  expand_tile_mfma_body<NKC, KP, MODE>(v, B, y, L, g, ch, kparts, v_rows, pa,
+                                       xcd_remap(blockIdx.x, gridDim.x), (int)gridDim.x, lds);
+}
+
 // Tile lookup of the MFMA kernels (segments or tile-list mode): first row r0
 // of the row list, row count and adapter slot, the same in every lane.  The
 // tile-list record is (slot, rows, first row, tok0); tok0 >= 0 says the tile's
@@ -1167,33 +1232,38 @@ __device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int&
 // with one barrier per step.  Wave (wm, wr) multiplies rows 32 wm .. +32 by
 // ranks 32 wr .. +32 as 2 x 2 MFMA tiles of 16 x 16, two k-chunks of 32 per
 // step; fragments are 16-byte LDS reads (rows padded to 144 bytes).
+// (the body takes its workgroup index bid, its rank block rblk and its LDS,
+// kRegShrinkLds 16-byte aligned elements: x tiles, then adapter tiles)
+constexpr int kRegShrinkRow = 64 + 8;  // LDS row: 64 k plus padding
+constexpr int kRegShrinkLds = 2 * 2 * 64 * kRegShrinkRow;
+
 template <int MODE>
-__global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ A,
-                                                          float* __restrict__ v, RowList L,
-                                                          Geo g, int ksplit, int v_rows) {
-  constexpr int TM = kMfmaTileRows, NR = 64, KS = 64, LDS_ROW = KS + 8;
+__device__ __forceinline__ void shrink_mfma_body(const uint16_t* __restrict__ x,
+                                                 const uint16_t* __restrict__ A,
+                                                 float* __restrict__ v, const RowList& L,
+                                                 const Geo& g, int ksplit, int v_rows, int bid,
+                                                 int rblk, uint16_t* lds) {
+  constexpr int TM = kMfmaTileRows, NR = 64, KS = 64, LDS_ROW = kRegShrinkRow;
   static_assert(TM == 64, "staging covers 64 rows");
-  __shared__ __align__(16) uint16_t xs[2][TM * LDS_ROW];
-  __shared__ __align__(16) uint16_t as[2][NR * LDS_ROW];
+  uint16_t (*xs)[TM * LDS_ROW] = reinterpret_cast<uint16_t (*)[TM * LDS_ROW]>(lds);
+  uint16_t (*as)[NR * LDS_ROW] = reinterpret_cast<uint16_t (*)[NR * LDS_ROW]>(lds + 2 * TM * LDS_ROW);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int wm = wave & 1, wr = wave >> 1;
   const int i16 = lane & 15, grp = lane >> 4;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_tile = g.S * ksplit;
   const int f = bid / per_tile;
   const int rem = bid - f * per_tile;
   const int s = rem / ksplit;
   const int part = rem - s * ksplit;
   int r0, cnt, sid, tok0;
-  const bool copy = s == 0 && part == 0 && blockIdx.y == 0;
+  const bool copy = s == 0 && part == 0 && rblk == 0;
   int rk_rec;
   if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0, rk_rec, copy)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int rr = rk_rec > 0 && rk_rec < g.R ? rk_rec : g.R;  // the adapter's ranks
-  const int rank0 = blockIdx.y * NR;
+  const int rank0 = rblk * NR;
   // K steps of this split
   const int nsteps = (g.K + KS - 1) / KS;
   const int per = (nsteps + ksplit - 1) / ksplit;
@@ -1292,6 +1362,16 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
   }
 }
 
+template <int MODE>
+__global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ A,
+                                                          float* __restrict__ v, RowList L,
+                                                          Geo g, int ksplit, int v_rows) {
+  __shared__ __align__(16) uint16_t lds[kRegShrinkLds];
+  shrink_mfma_body<MODE>(x, A, v, L, g, ksplit, v_rows, xcd_remap(blockIdx.x, gridDim.x),
+                         blockIdx.y, lds);
+}
+
 // ------------------------------------------------- shrink (MFMA, LDS by DMA)
 //
 // The same work as shrink_mfma_kernel (bf16; grid.x = tiles * S * ksplit,
@@ -1321,33 +1401,37 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
 __device__ __forceinline__ int dma_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 constexpr int kDmaShrinkMaxK = 8192;
 
+// (the body takes its workgroup index bid, its rank block rblk and the three
+// stages, 16-byte aligned LDS arrays of kDmaStage elements, so that a combined
+// launch can run it beside the 8-row tile shrink)
+constexpr int kDmaStage = 2 * 64 * 64;  // one stage: the x tile, then the adapter tile
+
 template <int MODE>
-__global__ __launch_bounds__(256, 3) void shrink_mfma_dma_kernel(const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ A,
-                                                                float* __restrict__ v, RowList L,
-                                                                Geo g, int ksplit, int v_rows) {
+__device__ __forceinline__ void shrink_mfma_dma_body(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ A,
+                                                     float* __restrict__ v, const RowList& L,
+                                                     const Geo& g, int ksplit, int v_rows, int bid,
+                                                     int rblk, uint16_t* st_0, uint16_t* st_1,
+                                                     uint16_t* st_2) {
   constexpr int TM = kMfmaTileRows, NR = 64, KS = 64, TILE = 64 * KS;
-  static_assert(TM == 64, "64 rows per tile");
-  // stage k: the x tile, then the adapter tile (one LDS object per stage)
-  __shared__ __align__(16) uint16_t st_0[2 * TILE], st_1[2 * TILE], st_2[2 * TILE];
+  static_assert(TM == 64 && 2 * TILE == kDmaStage, "64 rows per tile");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int wm = wave & 1, wr = wave >> 1;
   const int i16 = lane & 15, grp = lane >> 4;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_tile = g.S * ksplit;
   const int f = bid / per_tile;
   const int rem = bid - f * per_tile;
   const int s = rem / ksplit;
   const int part = rem - s * ksplit;
   int r0, cnt, sid, tok0;
-  const bool copy = s == 0 && part == 0 && blockIdx.y == 0;
+  const bool copy = s == 0 && part == 0 && rblk == 0;
   int rk_rec;
   if (!mfma_tile<TM, MODE>(L, f, r0, cnt, sid, tok0, rk_rec, copy)) return;
   if (sid < 0 || sid >= g.max_loras || cnt < 1 || r0 < 0 || r0 + cnt > L.num_rows) return;
   const int rr = rk_rec > 0 && rk_rec < g.R ? rk_rec : g.R;  // the adapter's ranks
-  const int rank0 = blockIdx.y * NR;
+  const int rank0 = rblk * NR;
   const int nsteps = g.K / KS;
   const int per = (nsteps + ksplit - 1) / ksplit;
   const int st0 = min(nsteps, part * per), st1 = min(nsteps, st0 + per);
@@ -1449,6 +1533,16 @@ __global__ __launch_bounds__(256, 3) void shrink_mfma_dma_kernel(const uint16_t*
       }
     }
   }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 3) void shrink_mfma_dma_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ A,
+                                                                float* __restrict__ v, RowList L,
+                                                                Geo g, int ksplit, int v_rows) {
+  __shared__ __align__(16) uint16_t st_0[kDmaStage], st_1[kDmaStage], st_2[kDmaStage];
+  shrink_mfma_dma_body<MODE>(x, A, v, L, g, ksplit, v_rows, xcd_remap(blockIdx.x, gridDim.x),
+                             blockIdx.y, st_0, st_1, st_2);
 }
 
 // ------------------------------------------------------------ expand (MFMA)
@@ -1637,24 +1731,30 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(const float* __restric
 // B and y are loaded while the current one is computed; y leaves through raw
 // buffer stores (y must span less than 2 GiB): lanes without a row store to a
 // dropped offset, so no store sits under a branch.
+// (the body takes its workgroup index bid and its LDS, the B tile of
+// kExpandRowsLds 16-byte aligned elements and the tile's tokens, so that a
+// combined launch can run it beside the 8-row tile expand)
+constexpr int kExpandRowsLdk = 64 + 8;  // LDS row of the B tile: 64 ranks plus padding
+constexpr int kExpandRowsLds = kExpandMfmaCols * kExpandRowsLdk;
+
 template <int MODE, int KP>
-__global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
-    const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
-    RowList L, Geo g, Chunks ch, Chunks gr, int ksplit, int v_rows, int cpw) {
+__device__ __forceinline__ void expand_mfma_rows_body(const float* __restrict__ v,
+                                                      const uint16_t* __restrict__ B,
+                                                      uint16_t* __restrict__ y, const RowList& L,
+                                                      const Geo& g, const Chunks& ch,
+                                                      const Chunks& gr, int ksplit, int v_rows,
+                                                      int cpw, int bid, uint16_t* bs, int* s_tok) {
   constexpr int TM = kMfmaTileRows, NC = kExpandMfmaCols, KB = 64;
-  constexpr int LDK = KB + 8;
+  constexpr int LDK = kExpandRowsLdk;
   // KP partials of v are loaded (those past ksplit as zeros); splits of more
   // than kMaxKsplitWide happen only for pools of rank <= 32: one 32-rank chunk
   constexpr int NKC = KP > kMaxKsplitWide ? 1 : 2;
   static_assert(KP == kMaxKsplitWide || KP == kMaxKsplit, "four or eight partials");
-  static_assert(TM == 64 && NC == 128, "64 tokens x 128 columns per chunk");
-  __shared__ __align__(16) uint16_t bs[NC * LDK];
-  __shared__ int s_tok[TM];
+  static_assert(TM == 64 && NC == 128 && LDK == KB + 8, "64 tokens x 128 columns per chunk");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int j16 = lane & 15, grp = lane >> 4;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int f = bid / gr.total;
   const int gidx = bid - f * gr.total;
   int s = 0;
@@ -1817,6 +1917,94 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
       st16_buf_nt(u32x4{o[0], o[1], o[2], o[3]}, yb, off);
     }
   }
+}
+
+template <int MODE, int KP>
+__global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
+    const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
+    RowList L, Geo g, Chunks ch, Chunks gr, int ksplit, int v_rows, int cpw) {
+  __shared__ __align__(16) uint16_t bs[kExpandRowsLds];
+  __shared__ int s_tok[kMfmaTileRows];
+  expand_mfma_rows_body<MODE, KP>(v, B, y, L, g, ch, gr, ksplit, v_rows, cpw,
+                                  xcd_remap(blockIdx.x, gridDim.x), bs, s_tok);
+}
+
+// ------------------------------------------ one launch per stage (device plans)
+//
+// A device-built plan knows its record counts only on the GPU, so the host
+// launches its 64-row and its 8-row tiles at their capacities.  Launched apart,
+// every stage costs two launches even where one kind has no records (a
+// prefill batch has no 8-row tiles, a small decode batch no 64-row ones), and
+// the second waits for the first to drain.  These kernels run both in one
+// grid, in every workgroup one after the other: hardware workgroup ids below
+// nmp (nm rounded up to a multiple of the XCD count, so the ids below nm
+// spread over every XCD) first take their 64-row tile, then every workgroup
+// walks the 8-row records.  The walk's first record is loaded at the start,
+// so in a batch without 8-row tiles the check costs no round trip at the end.
+// Both bodies share one LDS array, with a barrier for LDS only between them
+// (the 64-row tile's last stores stay in flight).
+template <int MODE>
+__device__ __forceinline__ void walk_first_word(const RowList& Lw, int bid, int nwg, int per,
+                                                int& w, bool& pre) {
+  const int G = nwg / per;
+  const int f0 = bid / per;
+  pre = f0 < G && f0 < Lw.num_tiles;
+  w = 0;
+  if (pre) w = Lw.tiles[(size_t)f0 * LORA_PLAN_WAVE_WORDS + (threadIdx.x & 15)];
+}
+
+template <int NT, int CB, bool DMA>
+__global__ __launch_bounds__(256, 3) void shrink_combo_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, float* __restrict__ v,
+    RowList Lm, RowList Lw, Geo g, int ksplit, int kparts, int v_rows, int nm, int nmp) {
+  constexpr int kLds = DMA ? 3 * kDmaStage : kRegShrinkLds;  // uint16 elements
+  static_assert(tile_shrink_lds<NT>() * 4 <= kLds * 2, "the tile shrink's LDS fits");
+  static_assert(64 * kTileShrinkWaves == 256, "both bodies run 256 threads");
+  __shared__ __align__(16) uint16_t lds[kLds];
+  const int b = blockIdx.x, nwg = (int)gridDim.x;
+  const int bw = xcd_remap(b, nwg);
+  int w0;
+  bool pre;
+  walk_first_word<kListWalk>(Lw, bw, nwg, g.S * kparts, w0, pre);
+  if (b < nmp) {
+    const int bid = xcd_remap(b, nmp);
+    if (bid < nm) {
+      if constexpr (DMA)
+        shrink_mfma_dma_body<kList>(x, A, v, Lm, g, ksplit, v_rows, bid, 0, lds, lds + kDmaStage,
+                                    lds + 2 * kDmaStage);
+      else
+        shrink_mfma_body<kList>(x, A, v, Lm, g, ksplit, v_rows, bid, 0, lds);
+    }
+    lds_barrier();  // the 64-row tile's LDS accesses are done
+  }
+  shrink_tile_mfma_body<NT, CB, kListWalk>(x, A, v, Lw, g, kparts, v_rows, PlanArg<kListWalk>{},
+                                           bw, nwg, reinterpret_cast<float*>(lds), pre, w0);
+}
+
+// The expand's 8-row walk takes one partial of v (KP = 1).
+template <int NKC, int KPR>
+__global__ __launch_bounds__(256, 4) void expand_combo_kernel(
+    const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
+    RowList Lm, RowList Lw, Geo g, Chunks chm, Chunks gr, Chunks chw, int ksplit, int v_rows,
+    int cpw, int nm, int nmp) {
+  static_assert(tile_expand_lds<NKC>() <= kExpandRowsLds, "the tile expand's LDS fits");
+  static_assert(64 * kTileExpandWaves == 256, "both bodies run 256 threads");
+  __shared__ __align__(16) uint16_t lds[kExpandRowsLds];
+  __shared__ int s_tok[kMfmaTileRows];
+  const int b = blockIdx.x, nwg = (int)gridDim.x;
+  const int bw = xcd_remap(b, nwg);
+  int w0;
+  bool pre;
+  walk_first_word<kListWalk>(Lw, bw, nwg, chw.total, w0, pre);
+  if (b < nmp) {
+    const int bid = xcd_remap(b, nmp);
+    if (bid < nm)
+      expand_mfma_rows_body<kList, KPR>(v, B, y, Lm, g, chm, gr, ksplit, v_rows, cpw, bid, lds,
+                                        s_tok);
+    lds_barrier();  // the 64-row tile's LDS accesses are done
+  }
+  expand_tile_mfma_body<NKC, 1, kListWalk>(v, B, y, Lw, g, chw, 1, v_rows, PlanArg<kListWalk>{},
+                                           bw, nwg, lds, pre, w0);
 }
 
 // ------------------------------------------------------------ pool load
@@ -2291,6 +2479,102 @@ static int32_t launch_plan_wave_shrink(const Geo& g, const void* x, const void* 
              : launch_shrink_wave<float, VM>(g, x, A, v, Lw, p.wave_tiles, st, pav);
 }
 
+// One launch per stage for a device-built plan (p.walk) whose 8-row tiles take
+// the MFMA tile kernels: both tile kinds in one grid (shrink_combo_kernel,
+// expand_combo_kernel).  LORA_COMBINED_LAUNCH=0 turns it off (read on every
+// call, so a test can compare both forms in one process).
+static bool combo_enabled() {
+  const char* e = std::getenv("LORA_COMBINED_LAUNCH");
+  return !(e && e[0] == '0');
+}
+static bool combo_shrink_ok(const Geo& g, const TilePlan& p) {
+  return combo_enabled() && p.walk && p.mfma_tiles > 0 && p.wave_tiles > 0 && use_tile_mfma(g);
+}
+// ... the expand's walk takes one partial of v; its 64-row part needs y under
+// 2 GiB (raw buffer stores), as the 8-row part does
+static bool combo_expand_ok(const Geo& g, const TilePlan& p) {
+  return combo_shrink_ok(g, p) && use_tile_mfma_expand(g) && p.ksplit_wave == 1;
+}
+
+static int64_t round_xcd(int64_t n) { return (n + kNumXcd - 1) / kNumXcd * kNumXcd; }
+
+template <int NT, bool DMA>
+static int32_t launch_shrink_combo_k(const Geo& g, const void* x, const void* A, float* v,
+                                     const RowList& Lm, const RowList& Lw, const TilePlan& p,
+                                     hipStream_t st) {
+  constexpr int CB = tile_shrink_cb(16 * NT);
+  const int64_t nm = (int64_t)p.mfma_tiles * g.S * p.ksplit;
+  const int64_t per = (int64_t)g.S * p.ksplit_wave;
+  const int64_t nw = walk_records<kListWalk>(p.wave_tiles, per) * per;
+  const int64_t nmp = round_xcd(nm);
+  if (nmp > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one shrink launch");
+  // every workgroup walks the 8-row records after its 64-row tile (if any)
+  hipLaunchKernelGGL((shrink_combo_kernel<NT, CB, DMA>), dim3((unsigned)std::max(nmp, nw)),
+                     dim3(256), 0, st, (const uint16_t*)x, (const uint16_t*)A, v, Lm, Lw, g,
+                     p.ksplit, p.ksplit_wave, p.num_rows, (int)nm, (int)nmp);
+  return hip_check("shrink_combo launch");
+}
+
+template <int NT>
+static int32_t launch_shrink_combo_nt(const Geo& g, const void* x, const void* A, float* v,
+                                      const RowList& Lm, const RowList& Lw, const TilePlan& p,
+                                      hipStream_t st) {
+  // the 64-row part takes the DMA-staged body where launch_shrink_mfma would
+  return g.K % 64 == 0 && g.K <= kDmaShrinkMaxK
+             ? launch_shrink_combo_k<NT, true>(g, x, A, v, Lm, Lw, p, st)
+             : launch_shrink_combo_k<NT, false>(g, x, A, v, Lm, Lw, p, st);
+}
+
+static int32_t launch_shrink_combo(const Geo& g, const void* x, const void* A, float* v,
+                                   const RowList& Lm, const RowList& Lw, const TilePlan& p,
+                                   hipStream_t st) {
+  if (p.ksplit < 1 || p.ksplit > (g.R > 32 ? kMaxKsplitWide : kMaxKsplit))
+    return fail(LORA_E_ARG, "bad K split %d", p.ksplit);
+  if (p.ksplit_wave < 1 || p.ksplit_wave > tile_kparts_max(g.R))
+    return fail(LORA_E_ARG, "bad K split %d", p.ksplit_wave);
+  switch (tile_shrink_rank_tiles(g.R)) {
+    case 1: return launch_shrink_combo_nt<1>(g, x, A, v, Lm, Lw, p, st);
+    case 2: return launch_shrink_combo_nt<2>(g, x, A, v, Lm, Lw, p, st);
+    default: return launch_shrink_combo_nt<4>(g, x, A, v, Lm, Lw, p, st);
+  }
+}
+
+template <int NKC, int KPR>
+static int32_t launch_expand_combo_k(const Geo& g, const float* v, const void* B, void* y,
+                                     const RowList& Lm, const RowList& Lw, const TilePlan& p,
+                                     hipStream_t st) {
+  // the 64-row part as launch_expand_mfma lays it out
+  const Chunks chm = make_chunks(g, kExpandMfmaCols);
+  const int64_t work = (int64_t)p.mfma_tiles * chm.total;
+  int cpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, (work + 1023) / 1024));
+  if (const char* e = std::getenv("LORA_EXPAND_MFMA_CPW")) {  // tuning / test override
+    const long o = std::strtol(e, nullptr, 10);
+    if (o >= 1 && o <= 8) cpw = (int)o;
+  }
+  const Chunks gr = make_groups(g, cpw);
+  const Chunks chw = make_chunks(g, kTileExpandCols);
+  const int64_t nm = (int64_t)p.mfma_tiles * gr.total;
+  const int64_t nw = walk_records<kListWalk>(p.wave_tiles, chw.total) * chw.total;
+  const int64_t nmp = round_xcd(nm);
+  if (nmp > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one expand launch");
+  // every workgroup walks the 8-row records after its 64-row tile (if any)
+  hipLaunchKernelGGL((expand_combo_kernel<NKC, KPR>), dim3((unsigned)std::max(nmp, nw)),
+                     dim3(256), 0, st, v, (const uint16_t*)B, (uint16_t*)y, Lm, Lw, g, chm, gr,
+                     chw, p.ksplit, p.num_rows, cpw, (int)nm, (int)nmp);
+  return hip_check("expand_combo launch");
+}
+
+static int32_t launch_expand_combo(const Geo& g, const float* v, const void* B, void* y,
+                                   const RowList& Lm, const RowList& Lw, const TilePlan& p,
+                                   hipStream_t st) {
+  if (p.ksplit < 1 || p.ksplit > (g.R > 32 ? kMaxKsplitWide : kMaxKsplit))
+    return fail(LORA_E_ARG, "bad K split %d", p.ksplit);
+  if (g.R > 32) return launch_expand_combo_k<2, kMaxKsplitWide>(g, v, B, y, Lm, Lw, p, st);
+  return p.ksplit > kMaxKsplitWide
+             ? launch_expand_combo_k<1, kMaxKsplit>(g, v, B, y, Lm, Lw, p, st)
+             : launch_expand_combo_k<1, kMaxKsplitWide>(g, v, B, y, Lm, Lw, p, st);
+}
+
 int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, const TilePlan& p,
                         hipStream_t st) {
   const bool bf = g.dtype == LORA_BF16;
@@ -2302,6 +2586,7 @@ int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, co
       return launch_plan_wave_shrink<kArg>(g, x, A, v, Lw, p, st, pack_arg<kArg>(p));
     return launch_plan_wave_shrink<kArgL>(g, x, A, v, Lw, p, st, pack_arg<kArgL>(p));
   }
+  if (combo_shrink_ok(g, p)) return launch_shrink_combo(g, x, A, v, Lm, Lw, p, st);
   if (int32_t e = launch_shrink_mfma<kList>(g, x, A, v, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
                                             st))
     return e;
@@ -2320,6 +2605,7 @@ int32_t run_plan_expand(const Geo& g, const float* v, const void* B, void* y, co
       return launch_plan_wave_expand<kArg>(g, v, B, y, Lw, p, st, pack_arg<kArg>(p));
     return launch_plan_wave_expand<kArgL>(g, v, B, y, Lw, p, st, pack_arg<kArgL>(p));
   }
+  if (combo_expand_ok(g, p)) return launch_expand_combo(g, v, B, y, Lm, Lw, p, st);
   if (int32_t e = launch_expand_mfma<kList>(g, v, B, y, Lm, p.mfma_tiles, p.ksplit, p.num_rows,
                                             st))
     return e;

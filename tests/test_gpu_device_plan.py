@@ -255,3 +255,45 @@ def test_device_plan_ranked_equals_plain():
     _device_ranked_vs_plain(big, [16] * 6, R=64, label="large decode rank 16 in pool rank 64")
     # values outside [0, max_lora_rank] act as the pool's rank
     _device_ranked_vs_plain(big, [999, -3, 16, 0, 64, 16], R=64, label="out-of-range ranks")
+
+
+COMBO_CASES = {
+    # K not a multiple of 64: the register-staged 64-row shrink; ranks 8 / 16
+    "r16_regk": lambda: W.config_mlp_mixed(seed=8, n_prefill=3, len_lo=40, len_hi=200,
+                                           n_decode=300, hidden=264, inter=520, n_adapters=8,
+                                           rank_choices=(8, 16), max_lora_rank=16),
+    # K a multiple of 64: the DMA-staged 64-row shrink; ranks up to 32
+    "r32_dma": lambda: W.config_mlp_mixed(seed=9, n_prefill=3, len_lo=40, len_hi=200,
+                                          n_decode=300, hidden=512, inter=1024, n_adapters=8,
+                                          rank_choices=(16, 32), max_lora_rank=32),
+    # ranks up to 64 (two 32-rank chunks in the 8-row expand)
+    "r64_dma": lambda: W.config_mlp_mixed(seed=10, n_prefill=3, len_lo=40, len_hi=200,
+                                          n_decode=300, hidden=512, inter=1024, n_adapters=8,
+                                          rank_choices=(16, 64), max_lora_rank=64),
+    # a small batch: the 8-row tiles' shrink splits K (the expand then launches apart)
+    "r64_small": lambda: W.config_mlp_mixed(seed=11, n_prefill=1, len_lo=20, len_hi=60,
+                                            n_decode=24, hidden=512, inter=1024, n_adapters=4,
+                                            rank_choices=(16, 64), max_lora_rank=64),
+}
+
+
+@pytest.mark.parametrize("case", sorted(COMBO_CASES))
+def test_device_plan_combined_launch_matches_separate(case, monkeypatch):
+    """A device-built plan runs each stage's 64-row and 8-row tiles in one
+    launch; with LORA_COMBINED_LAUNCH=0 it launches them apart.  Both forms run
+    the same arithmetic on the same records: equal bit for bit, and within
+    tolerance of the oracle."""
+    import torch
+    for wl in COMBO_CASES[case]():
+        pool = make_pool(wl)
+        ws = _ws(pool, wl.T)
+        monkeypatch.delenv("LORA_COMBINED_LAUNCH", raising=False)
+        y1 = _run(wl, pool=pool, ws=ws)
+        monkeypatch.setenv("LORA_COMBINED_LAUNCH", "0")
+        y0 = _run(wl, pool=pool, ws=ws)
+        monkeypatch.delenv("LORA_COMBINED_LAUNCH", raising=False)
+        diff = int((y1.view(torch.int16) != y0.view(torch.int16)).sum().item())
+        say(f"  {case} {wl.name}: T={wl.T} K={wl.in_features} R={wl.max_lora_rank} "
+            f"elements differing between one and two launches per stage: {diff}")
+        assert diff == 0
+        check_rows(wl, y1, label=f"{case} {wl.name}, one launch per stage")
