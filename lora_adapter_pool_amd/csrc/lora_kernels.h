@@ -140,7 +140,8 @@ struct DevicePlanOut {
 };
 // Device-side builder (csrc/lora_meta.hip): lora_build_meta's arrays from
 // device ids, one workgroup on `st`; counts[4] = rows, segments, BGMV rows,
-// rejected ids.  With `plan`, the same launch then writes a device-built plan.
+// rejected ids.  With `plan` it writes a device-built plan (its v-row -> token
+// map and tile records) instead of those arrays, which m then need not hold.
 int32_t run_build_meta_device(const int32_t* ids, const uint8_t* prefill, int32_t T,
                               int32_t max_loras, bool all_sgmv, const lora_meta& m,
                               int32_t* counts, hipStream_t st,

@@ -14,7 +14,9 @@
 //      block, or, for pools of at most kParMaxLoras slots and large blocks,
 //      all 16 each place a contiguous sixteenth from their own positions;
 //   4. optionally (lora_apply_device), the tile records of a device-built
-//      plan in the host plan's format, up to fixed capacities.
+//      plan in the host plan's format, up to fixed capacities.  A plan's
+//      build writes its v-row -> token map in step 3 in place of the arrays
+//      above, and no segments or padding: its kernels read only the plan.
 // Arrays are padded so the grouped entry points can take upper-bound sizes:
 // segments past num_segs have length 0, BGMV rows past num_bgmv_rows have
 // id -1 (skipped by the kernels), and sgmv_perm past num_sgmv_rows is 0.
@@ -111,13 +113,26 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   __shared__ int32_t s_wsum[kMetaThreads / 64][3];
   int32_t* cs = lds;
   int32_t* cb = lds + max_loras;
+  // with a plan (lora_apply_device) only the plan is written: its v-row ->
+  // token map and records; the grouped entry points' arrays (m), which its
+  // kernels never read, are left alone
+  const bool meta_out = plan.tiles == nullptr;  // uniform
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int nw = kMetaThreads / 64;
+  const bool one_block = T <= kcap;
+  const bool par_slots = max_loras <= kParMaxLoras;  // uniform
+  const int nkeys = 2 * max_loras;
+  int32_t* wcnt = lds + 2 * max_loras + kcap / 2 + (plan.tiles ? 2 * (max_loras + 1) : 0);
+  // a batch of one block placed by all wavefronts counts each wavefront's
+  // keys in the histogram pass already, over the rows that wavefront places
+  const bool wave_hist = one_block && par_slots && T > kParMinRows;  // uniform
   for (int a = tid; a < max_loras; a += kMetaThreads) {
     cs[a] = 0;
     cb[a] = 0;
   }
+  if (wave_hist)
+    for (int k = tid; k < nw * nkeys; k += kMetaThreads) wcnt[k] = 0;
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
@@ -126,13 +141,41 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   //    ids and flags of kHistBatch rows before it counts any of them, so the
   //    loop waits on memory once per batch, not once per row.
   int16_t* keys = reinterpret_cast<int16_t*>(lds + 2 * max_loras);
-  const bool one_block = T <= kcap;
   // every lane loads (rows past T repeat row T - 1 and count as rows without
   // adapter), so no branch waits on a load; without flags the loads of pf
   // read the ids' bytes and pmask drops them
   const uint8_t* pf = prefill != nullptr ? prefill : reinterpret_cast<const uint8_t*>(ids);
   const uint32_t pmask = prefill != nullptr ? 0xffu : 0u;
-  for (int t0 = 0; t0 < T; t0 += kMetaThreads * kHistBatch) {
+  if (wave_hist) {
+    // wavefront w: rows [lo, hi), the contiguous share placement gives it,
+    // counted by key (2 id + set) into its own counters
+    const int sb = ((T + nw - 1) / nw + 63) / 64 * 64;
+    const int lo = min(T, wave * sb), hi = min(T, lo + sb);
+    int32_t* my = wcnt + wave * nkeys;
+    for (int i0 = lo; i0 < hi; i0 += 64 * kHistBatch) {  // uniform
+      int av[kHistBatch];
+      uint32_t pv[kHistBatch];
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        const int tc = min(i0 + 64 * u + lane, hi - 1);
+        av[u] = ids[tc];
+        pv[u] = pf[tc];
+      }
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        if (i0 + 64 * u >= hi) break;  // uniform
+        const int t = i0 + 64 * u + lane;
+        const int a = t < hi ? av[u] : -1;
+        const bool ok = a >= 0 && a < max_loras;
+        const bool sg = ok && (all_sgmv || (pv[u] & pmask) != 0);
+        const int key = ok ? 2 * a + (sg ? 1 : 0) : -1;
+        if (t < hi) keys[t] = (int16_t)key;
+        if (a < -1 || a >= max_loras) atomicAdd(&s_bad, 1);
+        count_keys(my, key);
+      }
+    }
+  }
+  for (int t0 = 0; t0 < T && !wave_hist; t0 += kMetaThreads * kHistBatch) {
     int av[kHistBatch];
     uint32_t pv[kHistBatch];
 #pragma unroll
@@ -156,9 +199,22 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   }
   __syncthreads();
 
-  // 2. exclusive scans over the bins; thread tid owns bins [a0, a1)
+  // 2. exclusive scans over the bins; thread tid owns bins [a0, a1) (the
+  // per-wavefront counts, if any, summed into them first)
   const int per = (max_loras + kMetaThreads - 1) / kMetaThreads;
   const int a0 = min(max_loras, tid * per), a1 = min(max_loras, a0 + per);
+  if (wave_hist) {
+    for (int a = a0; a < a1; ++a) {
+      int sgc = 0, bgc = 0;
+#pragma unroll
+      for (int w = 0; w < kMetaWaves; ++w) {
+        sgc += wcnt[w * nkeys + 2 * a + 1];
+        bgc += wcnt[w * nkeys + 2 * a];
+      }
+      cs[a] = sgc;
+      cb[a] = bgc;
+    }
+  }
   int v[3] = {0, 0, 0};  // SGMV rows, BGMV rows, SGMV segments
   for (int a = a0; a < a1; ++a) {
     v[0] += cs[a];
@@ -179,7 +235,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   int es = base[0] + inc[0] - v[0], eb = base[1] + inc[1] - v[1], eg = base[2] + inc[2] - v[2];
   for (int a = a0; a < a1; ++a) {
     const int c = cs[a], d = cb[a];
-    if (c > 0) {
+    if (c > 0 && meta_out) {
       m.seg_starts[eg] = es;
       m.seg_lens[eg] = c;
       m.seg_ids[eg] = a;
@@ -196,15 +252,17 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     counts[1] = nseg;
     counts[2] = nb;
   }
-  for (int i = nseg + tid; i < max_loras; i += kMetaThreads) {
-    m.seg_starts[i] = ns;
-    m.seg_lens[i] = 0;
-    m.seg_ids[i] = 0;
-  }
-  for (int i = ns + tid; i < T; i += kMetaThreads) m.sgmv_perm[i] = 0;
-  for (int i = nb + tid; i < T; i += kMetaThreads) {
-    m.bgmv_tok[i] = 0;
-    m.bgmv_ids[i] = -1;
+  if (meta_out) {
+    for (int i = nseg + tid; i < max_loras; i += kMetaThreads) {
+      m.seg_starts[i] = ns;
+      m.seg_lens[i] = 0;
+      m.seg_ids[i] = 0;
+    }
+    for (int i = ns + tid; i < T; i += kMetaThreads) m.sgmv_perm[i] = 0;
+    for (int i = nb + tid; i < T; i += kMetaThreads) {
+      m.bgmv_tok[i] = 0;
+      m.bgmv_ids[i] = -1;
+    }
   }
   __syncthreads();
   if (tid == 0) counts[3] = s_bad;
@@ -220,9 +278,6 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   // counts into each wavefront's first positions, and the wavefronts place
   // their rows at once (rows keep token order, so the sort stays stable).
   // Otherwise one wavefront places the whole block.
-  const bool par_slots = max_loras <= kParMaxLoras;  // uniform
-  const int nkeys = 2 * max_loras;
-  int32_t* wcnt = lds + 2 * max_loras + kcap / 2 + (plan.tiles ? 2 * (max_loras + 1) : 0);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int kbits = 32 - __clz(2 * max_loras - 1);  // bits of the largest key
   for (int b0 = 0; b0 < T; b0 += kcap) {
@@ -250,13 +305,15 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     int32_t* my = wcnt + wave * nkeys;  // this wavefront's counters (par)
     int lo = 0, hi = 0;                  // the rows this wavefront places
     if (par) {
-      for (int k = lane; k < nkeys; k += 64) my[k] = 0;
-      __syncthreads();  // keys staged, counters cleared
       const int sb = ((nbk + nw - 1) / nw + 63) / 64 * 64;
       lo = min(nbk, wave * sb);
       hi = min(nbk, lo + sb);
-      for (int i = lo + lane; i < hi; i += 64) count_keys(my, keys[i]);
-      __syncthreads();
+      if (!wave_hist) {  // (else counted by the histogram pass)
+        for (int k = lane; k < nkeys; k += 64) my[k] = 0;
+        __syncthreads();  // keys staged, counters cleared
+        for (int i = lo + lane; i < hi; i += 64) count_keys(my, keys[i]);
+        __syncthreads();
+      }
       for (int k = tid; k < nkeys; k += kMetaThreads) {
         int32_t* pos = (k & 1) ? &cs[k >> 1] : &cb[k >> 1];
         int base = *pos;
@@ -310,15 +367,16 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       const int p = p0 + rank;
       if (key >= 0 && p < T) {
         const int t = b0 + i;
-        if (key & 1) {
+        if (!meta_out) {
+          // the device plan's v-row -> token map: SGMV rows, then BGMV rows
+          const int vr = (key & 1) ? p : ns + p;
+          if (vr < T) plan.perm[vr] = t;
+        } else if (key & 1) {
           m.sgmv_perm[p] = t;
         } else {
           m.bgmv_tok[p] = t;
           m.bgmv_ids[p] = key >> 1;
         }
-        // the device plan's v-row -> token map: SGMV rows, then BGMV rows
-        const int vr = (key & 1) ? p : ns + p;
-        if (plan.perm && vr < T) plan.perm[vr] = t;
       }
       if (first) *pos = p0 + cnt;
     }
@@ -414,7 +472,6 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   const int nreal = min(ttot, plan.cap);
   for (int f = tid; f < nreal; f += kMetaThreads) {
     int slot = 0, rows = 0, vrow = 0;
-    const int32_t* src = m.sgmv_perm;
     {
       slot = owner(toff, f);
       const int s0 = slot > 0 ? cs[slot - 1] : 0, b0 = slot > 0 ? cb[slot - 1] : 0;
@@ -424,18 +481,17 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       if (lt < tsg) {
         vrow = s0 + LORA_PLAN_WAVE_ROWS * lt;
         rows = min(LORA_PLAN_WAVE_ROWS, cs[slot] - vrow);
-        src = m.sgmv_perm + vrow;
       } else {
         const int first = b0 + LORA_PLAN_WAVE_ROWS * (lt - tsg);
         rows = min(LORA_PLAN_WAVE_ROWS, cb[slot] - first);
         vrow = ns + first;
-        src = m.bgmv_tok + first;
       }
     }
-    // the tokens are loaded unconditionally (a real record has rows >= 1;
-    // lanes past it repeat its last row), so no branch waits on a load
+    // the tokens (the v-row map from vrow on) are loaded unconditionally (a
+    // real record has rows >= 1; lanes past it repeat its last row), so no
+    // branch waits on a load
     const int last = max(rows, 1) - 1;
-    if (rows <= 0) src = m.sgmv_perm;  // (not expected) element 0 exists for T >= 1
+    const int32_t* src = plan.perm + (rows > 0 ? vrow : 0);  // (rows 0 not expected)
     int tk[LORA_PLAN_WAVE_ROWS];
 #pragma unroll
     for (int i = 0; i < LORA_PLAN_WAVE_ROWS; ++i) tk[i] = src[min(i, last)];
@@ -462,19 +518,16 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       const int sc = cs[slot] - s0;
       const int lt = f - moff[slot];
       const int msg = sc >= plan.mfma_min ? (sc + LORA_PLAN_MFMA_ROWS - 1) / LORA_PLAN_MFMA_ROWS : 0;
-      const int32_t* src;
-      int first;
       if (lt < msg) {
-        first = s0 + LORA_PLAN_MFMA_ROWS * lt;
+        const int first = s0 + LORA_PLAN_MFMA_ROWS * lt;
         rows = min(LORA_PLAN_MFMA_ROWS, cs[slot] - first);
         vrow = first;
-        src = m.sgmv_perm + first;
       } else {
-        first = b0 + LORA_PLAN_MFMA_ROWS * (lt - msg);
+        const int first = b0 + LORA_PLAN_MFMA_ROWS * (lt - msg);
         rows = min(LORA_PLAN_MFMA_ROWS, cb[slot] - first);
         vrow = ns + first;
-        src = m.bgmv_tok + first;
       }
+      const int32_t* src = plan.perm + vrow;
       // a slot's rows of one set are in increasing token order (the sort is
       // stable), so they are consecutive exactly when last - first = rows - 1
       const int t0 = src[0];
