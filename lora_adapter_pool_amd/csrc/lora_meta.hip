@@ -37,8 +37,11 @@ constexpr int kParMaxLoras = 256;
 // barriers cost more than the single wavefront's chain).
 constexpr int kParMinRows = 1024;
 constexpr int kMetaWaves = kMetaThreads / 64;
-// Rows per thread whose ids are loaded at once by the histogram loop.
+// Rows per thread whose ids are loaded at once by the histogram loop, and by
+// the per-wavefront histogram (one memory round trip for batches of up to
+// 16 x 64 x 16 rows).
 constexpr int kHistBatch = 8;
+constexpr int kWaveHistBatch = 16;
 
 using i32x4 = int32_t __attribute__((ext_vector_type(4)));
 static_assert(LORA_PLAN_WAVE_WORDS == 16 && LORA_PLAN_MFMA_WORDS == 4,
@@ -87,6 +90,12 @@ __device__ __forceinline__ void wave_prefix(const int32_t* s, int stride, int wa
   x = row_incl_scan(x);
   tot = __builtin_amdgcn_readlane(x, kMetaWaves - 1);
   excl = wave > 0 ? __builtin_amdgcn_readlane(x, wave > 0 ? wave - 1 : 0) : 0;
+}
+
+// Set bits of m below this lane (popc(m & lanes below) with mbcnt).
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // bins[key] += 1 for every active lane with key >= 0.  Sorted batches give
@@ -152,17 +161,17 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
     const int sb = ((T + nw - 1) / nw + 63) / 64 * 64;
     const int lo = min(T, wave * sb), hi = min(T, lo + sb);
     int32_t* my = wcnt + wave * nkeys;
-    for (int i0 = lo; i0 < hi; i0 += 64 * kHistBatch) {  // uniform
-      int av[kHistBatch];
-      uint32_t pv[kHistBatch];
+    for (int i0 = lo; i0 < hi; i0 += 64 * kWaveHistBatch) {  // uniform
+      int av[kWaveHistBatch];
+      uint32_t pv[kWaveHistBatch];
 #pragma unroll
-      for (int u = 0; u < kHistBatch; ++u) {
+      for (int u = 0; u < kWaveHistBatch; ++u) {
         const int tc = min(i0 + 64 * u + lane, hi - 1);
         av[u] = ids[tc];
         pv[u] = pf[tc];
       }
 #pragma unroll
-      for (int u = 0; u < kHistBatch; ++u) {
+      for (int u = 0; u < kWaveHistBatch; ++u) {
         if (i0 + 64 * u >= hi) break;  // uniform
         const int t = i0 + 64 * u + lane;
         const int a = t < hi ? av[u] : -1;
@@ -278,7 +287,6 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
   // counts into each wavefront's first positions, and the wavefronts place
   // their rows at once (rows keep token order, so the sort stays stable).
   // Otherwise one wavefront places the whole block.
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int kbits = 32 - __clz(2 * max_loras - 1);  // bits of the largest key
   for (int b0 = 0; b0 < T; b0 += kcap) {
     const int nbk = min(kcap, T - b0);
@@ -350,7 +358,7 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
       if (uni) {
         pos = par ? &my[k0] : (k0 & 1) ? &cs[k0 >> 1] : &cb[k0 >> 1];
         p0 = k0 == ckey ? cpos : *pos;
-        rank = __popcll(valid & below);
+        rank = lanes_below(valid);
         cnt = __popcll(valid);
         first = (int)lane == __builtin_ctzll(valid);
         ckey = k0;
@@ -360,9 +368,9 @@ __global__ __launch_bounds__(kMetaThreads) void build_meta_kernel(
         pos = par ? &my[key] : (key & 1) ? &cs[key >> 1] : &cb[key >> 1];
         p0 = key >= 0 ? *pos : 0;
         const uint64_t mk = same_key_lanes(key, kbits);
-        rank = __popcll(mk & below);
+        rank = lanes_below(mk);
         cnt = __popcll(mk);
-        first = key >= 0 && (mk & below) == 0;
+        first = key >= 0 && rank == 0;
       }
       const int p = p0 + rank;
       if (key >= 0 && p < T) {
