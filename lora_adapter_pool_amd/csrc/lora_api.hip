@@ -450,14 +450,18 @@ int32_t apply_device_run(const Geo& g, const void* A_pool, const void* B_pool, c
   if (int32_t e = run_build_meta_device(ids, prefill, T, g.max_loras, all_sgmv, m, counts, st,
                                         &po))
     return e;
-  // the 8-row K split is chosen for the records such a batch typically makes
-  // (one partial tile per slot), not for the capacity (two per slot): the
+  // the 8-row K split is chosen for the records such a batch typically makes,
+  // not for the capacity: with 64-row tiles about two partial tiles per slot
+  // (long runs take 64-row tiles, as the rest of a flagged batch's rows
+  // mostly do), else one per slot besides the full tiles of every row.  The
   // split changes only how the work is spread
-  const int64_t wave_est = std::min<int64_t>(
-      cap, ((int64_t)T + LORA_PLAN_WAVE_ROWS - 1) / LORA_PLAN_WAVE_ROWS +
-               std::min<int64_t>(g.max_loras, T));
-  TilePlan tp{perm, tiles, cap, mtiles, mcap, nullptr, mfma_ksplit(g, mcap), T,
-              wave_ksplit(g, wave_est), nullptr, nullptr, nullptr, /*walk=*/1};
+  const int64_t wave_est =
+      mfma ? std::min<int64_t>(cap, 2 * std::min<int64_t>(g.max_loras, T))
+           : std::min<int64_t>(cap, ((int64_t)T + LORA_PLAN_WAVE_ROWS - 1) / LORA_PLAN_WAVE_ROWS +
+                                        std::min<int64_t>(g.max_loras, T));
+  const int32_t kw = std::min(wave_ksplit(g, wave_est), walk_kparts_max(g.R));
+  TilePlan tp{perm, tiles, cap, mtiles, mcap, nullptr, mfma_ksplit(g, mcap), T, kw, nullptr,
+              nullptr, nullptr, /*walk=*/1};
   if (onepass) return run_plan_onepass_list(g, x, A_pool, B_pool, y, tp, st);
   float* v = (float*)(w + d.v);
   if (int32_t e = run_plan_shrink(g, x, A_pool, v, tp, st)) return e;

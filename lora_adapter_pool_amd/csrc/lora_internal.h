@@ -70,6 +70,12 @@ constexpr int32_t kTileShrinkWaves = 4;  // waves per workgroup of that shrink
 // else 4 (the expand's staging of 8 partials of 64 ranks needs too many
 // scalar registers).
 constexpr int32_t tile_kparts_max(int32_t R) { return R <= 16 ? LORA_PLAN_MAX_KSPLIT : 4; }
+// ... for a device-built plan (its 8-row kernels walk their records), whose
+// walking expand sums at most this many partials for pools of rank above 32
+constexpr int32_t kMaxWalkKpartsWide = 2;
+constexpr int32_t walk_kparts_max(int32_t R) {
+  return R > 32 ? kMaxWalkKpartsWide : tile_kparts_max(R);
+}
 
 // K split of the wavefront tiles' MFMA shrink for a plan of nw such tiles
 // (bf16, R <= 64; else 1): grown while the launch has fewer than four

@@ -1981,12 +1981,13 @@ __global__ __launch_bounds__(256, 3) void shrink_combo_kernel(
                                            bw, nwg, reinterpret_cast<float*>(lds), pre, w0);
 }
 
-// The expand's 8-row walk takes one partial of v (KP = 1).
-template <int NKC, int KPR>
+// The 8-row walk sums kparts partials of v (KPW loads, those past kparts as
+// zeros), the 64-row part ksplit (KPR loads).
+template <int NKC, int KPR, int KPW>
 __global__ __launch_bounds__(256, 4) void expand_combo_kernel(
     const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
-    RowList Lm, RowList Lw, Geo g, Chunks chm, Chunks gr, Chunks chw, int ksplit, int v_rows,
-    int cpw, int nm, int nmp) {
+    RowList Lm, RowList Lw, Geo g, Chunks chm, Chunks gr, Chunks chw, int ksplit, int kparts,
+    int v_rows, int cpw, int nm, int nmp) {
   static_assert(tile_expand_lds<NKC>() <= kExpandRowsLds, "the tile expand's LDS fits");
   static_assert(64 * kTileExpandWaves == 256, "both bodies run 256 threads");
   __shared__ __align__(16) uint16_t lds[kExpandRowsLds];
@@ -2003,8 +2004,8 @@ __global__ __launch_bounds__(256, 4) void expand_combo_kernel(
                                         s_tok);
     lds_barrier();  // the 64-row tile's LDS accesses are done
   }
-  expand_tile_mfma_body<NKC, 1, kListWalk>(v, B, y, Lw, g, chw, 1, v_rows, PlanArg<kListWalk>{},
-                                           bw, nwg, lds, pre, w0);
+  expand_tile_mfma_body<NKC, KPW, kListWalk>(v, B, y, Lw, g, chw, kparts, v_rows,
+                                             PlanArg<kListWalk>{}, bw, nwg, lds, pre, w0);
 }
 
 // ------------------------------------------------------------ pool load
@@ -2159,23 +2160,22 @@ template <int NKC, int MODE>
 static int32_t launch_expand_tile_nkc(const Geo& g, const float* v, const void* B, void* y,
                                       const RowList& L, int64_t tiles, int kparts, int v_rows,
                                       hipStream_t st, const PlanArg<MODE>& pa) {
-  if constexpr (MODE == kListWalk) {
-    // the walk is built for one partial of v only (with more, its loop keeps
-    // too many scalar registers live).  Several partials mean the shrink's
-    // grid was small, so the plan is small and one record per workgroup does
-    if (kparts > 1)
-      return launch_expand_tile_nkc<NKC, kList>(g, v, B, y, L, tiles, kparts, v_rows, st,
-                                                PlanArg<kList>{});
-    return launch_expand_tile_k<NKC, 1, MODE>(g, v, B, y, L, tiles, 1, v_rows, st, pa);
-  } else {
+  // (eight partials occur only for pools of rank <= 16, one 32-rank chunk; a
+  // walk over two 32-rank chunks takes at most kMaxWalkKpartsWide: with more
+  // its loop runs out of scalar registers)
+  if constexpr (MODE != kListWalk || NKC == 1) {
     if (kparts > 4)
       return launch_expand_tile_k<NKC, 8, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+  }
+  if constexpr (MODE == kListWalk && NKC == 2) {
+    if (kparts > kMaxWalkKpartsWide) return fail(LORA_E_ARG, "bad K split %d", kparts);
+  } else {
     if (kparts > 2)
       return launch_expand_tile_k<NKC, 4, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
-    if (kparts > 1)
-      return launch_expand_tile_k<NKC, 2, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
-    return launch_expand_tile_k<NKC, 1, MODE>(g, v, B, y, L, tiles, 1, v_rows, st, pa);
   }
+  if (kparts > 1)
+    return launch_expand_tile_k<NKC, 2, MODE>(g, v, B, y, L, tiles, kparts, v_rows, st, pa);
+  return launch_expand_tile_k<NKC, 1, MODE>(g, v, B, y, L, tiles, 1, v_rows, st, pa);
 }
 
 template <int MODE>
@@ -2490,10 +2490,10 @@ static bool combo_enabled() {
 static bool combo_shrink_ok(const Geo& g, const TilePlan& p) {
   return combo_enabled() && p.walk && p.mfma_tiles > 0 && p.wave_tiles > 0 && use_tile_mfma(g);
 }
-// ... the expand's walk takes one partial of v; its 64-row part needs y under
-// 2 GiB (raw buffer stores), as the 8-row part does
+// ... the expand's 64-row part needs y under 2 GiB (raw buffer stores), as
+// the 8-row part does
 static bool combo_expand_ok(const Geo& g, const TilePlan& p) {
-  return combo_shrink_ok(g, p) && use_tile_mfma_expand(g) && p.ksplit_wave == 1;
+  return combo_shrink_ok(g, p) && use_tile_mfma_expand(g);
 }
 
 static int64_t round_xcd(int64_t n) { return (n + kNumXcd - 1) / kNumXcd * kNumXcd; }
@@ -2539,7 +2539,7 @@ static int32_t launch_shrink_combo(const Geo& g, const void* x, const void* A, f
   }
 }
 
-template <int NKC, int KPR>
+template <int NKC, int KPR, int KPW>
 static int32_t launch_expand_combo_k(const Geo& g, const float* v, const void* B, void* y,
                                      const RowList& Lm, const RowList& Lw, const TilePlan& p,
                                      hipStream_t st) {
@@ -2558,10 +2558,30 @@ static int32_t launch_expand_combo_k(const Geo& g, const float* v, const void* B
   const int64_t nmp = round_xcd(nm);
   if (nmp > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one expand launch");
   // every workgroup walks the 8-row records after its 64-row tile (if any)
-  hipLaunchKernelGGL((expand_combo_kernel<NKC, KPR>), dim3((unsigned)std::max(nmp, nw)),
+  hipLaunchKernelGGL((expand_combo_kernel<NKC, KPR, KPW>), dim3((unsigned)std::max(nmp, nw)),
                      dim3(256), 0, st, v, (const uint16_t*)B, (uint16_t*)y, Lm, Lw, g, chm, gr,
-                     chw, p.ksplit, p.num_rows, cpw, (int)nm, (int)nmp);
+                     chw, p.ksplit, p.ksplit_wave, p.num_rows, cpw, (int)nm, (int)nmp);
   return hip_check("expand_combo launch");
+}
+
+template <int NKC, int KPR>
+static int32_t launch_expand_combo_kpw(const Geo& g, const float* v, const void* B, void* y,
+                                       const RowList& Lm, const RowList& Lw, const TilePlan& p,
+                                       hipStream_t st) {
+  // the walk's partials as launch_expand_tile_nkc takes them (eight only with
+  // one 32-rank chunk)
+  if constexpr (NKC == 1) {
+    if (p.ksplit_wave > 4)
+      return launch_expand_combo_k<NKC, KPR, 8>(g, v, B, y, Lm, Lw, p, st);
+  }
+  if constexpr (NKC == 2) {
+    if (p.ksplit_wave > kMaxWalkKpartsWide)
+      return fail(LORA_E_ARG, "bad K split %d", p.ksplit_wave);
+  } else {
+    if (p.ksplit_wave > 2) return launch_expand_combo_k<NKC, KPR, 4>(g, v, B, y, Lm, Lw, p, st);
+  }
+  if (p.ksplit_wave > 1) return launch_expand_combo_k<NKC, KPR, 2>(g, v, B, y, Lm, Lw, p, st);
+  return launch_expand_combo_k<NKC, KPR, 1>(g, v, B, y, Lm, Lw, p, st);
 }
 
 static int32_t launch_expand_combo(const Geo& g, const float* v, const void* B, void* y,
@@ -2569,10 +2589,12 @@ static int32_t launch_expand_combo(const Geo& g, const float* v, const void* B, 
                                    hipStream_t st) {
   if (p.ksplit < 1 || p.ksplit > (g.R > 32 ? kMaxKsplitWide : kMaxKsplit))
     return fail(LORA_E_ARG, "bad K split %d", p.ksplit);
-  if (g.R > 32) return launch_expand_combo_k<2, kMaxKsplitWide>(g, v, B, y, Lm, Lw, p, st);
+  if (p.ksplit_wave < 1 || p.ksplit_wave > tile_kparts_max(g.R))
+    return fail(LORA_E_ARG, "bad K split %d", p.ksplit_wave);
+  if (g.R > 32) return launch_expand_combo_kpw<2, kMaxKsplitWide>(g, v, B, y, Lm, Lw, p, st);
   return p.ksplit > kMaxKsplitWide
-             ? launch_expand_combo_k<1, kMaxKsplit>(g, v, B, y, Lm, Lw, p, st)
-             : launch_expand_combo_k<1, kMaxKsplitWide>(g, v, B, y, Lm, Lw, p, st);
+             ? launch_expand_combo_kpw<1, kMaxKsplit>(g, v, B, y, Lm, Lw, p, st)
+             : launch_expand_combo_kpw<1, kMaxKsplitWide>(g, v, B, y, Lm, Lw, p, st);
 }
 
 int32_t run_plan_shrink(const Geo& g, const void* x, const void* A, float* v, const TilePlan& p,
