@@ -377,9 +377,22 @@ int32_t wave_ksplit(const Geo& g, int64_t nw) {
     const int64_t nk = (g.K + 31) / 32;
     const int64_t batch = (int64_t)kTileShrinkWaves * tile_shrink_cb(g.R);
     const int64_t wgs = nw * g.S;
-    while (ksplit_wave < tile_kparts_max(g.R) && wgs * ksplit_wave < 1024 &&
-           nk / (ksplit_wave + 1) >= batch)
-      ++ksplit_wave;
+    // a workgroup's rate is bounded by what its compute unit can pull, so the
+    // time follows the compute unit with the most workgroups: ceil(wgs k /
+    // kComputeUnits) workgroups of 1/k of a tile's K each.  Take the split
+    // with the least such load (the fewest parts on a tie), among those that
+    // keep at most four workgroups per compute unit and a full load batch per
+    // wave in every part
+    int64_t best_num = -1, best_den = 1;
+    for (int32_t k = 1; k <= tile_kparts_max(g.R); ++k) {
+      if (k > 1 && (wgs * k > 4 * kComputeUnits || nk / k < batch)) break;
+      const int64_t num = (wgs * k + kComputeUnits - 1) / kComputeUnits;  // load num / k
+      if (best_num < 0 || num * best_den < best_num * k) {
+        best_num = num;
+        best_den = k;
+        ksplit_wave = k;
+      }
+    }
     if (const char* e = std::getenv("LORA_WAVE_KSPLIT")) {  // tuning override
       const long o = std::strtol(e, nullptr, 10);
       if (o >= 1 && o <= tile_kparts_max(g.R)) ksplit_wave = (int32_t)o;

@@ -66,10 +66,10 @@ constexpr int32_t tile_shrink_cb(int32_t R) {
   return tile_shrink_rank_tiles(R) == 1 ? 8 : tile_shrink_rank_tiles(R) == 2 ? 6 : 4;
 }
 constexpr int32_t kTileShrinkWaves = 4;  // waves per workgroup of that shrink
-// Most partials of v that shrink writes: 8 (LORA_PLAN_MAX_KSPLIT) for R <= 16,
-// else 4 (the expand's staging of 8 partials of 64 ranks needs too many
-// scalar registers).
-constexpr int32_t tile_kparts_max(int32_t R) { return R <= 16 ? LORA_PLAN_MAX_KSPLIT : 4; }
+// Most partials of v that shrink writes: 8 (LORA_PLAN_MAX_KSPLIT).
+constexpr int32_t tile_kparts_max(int32_t R) { return R <= 64 ? LORA_PLAN_MAX_KSPLIT : 4; }
+// Compute units of an MI355X (the K splits balance workgroups over them).
+constexpr int64_t kComputeUnits = 256;
 // ... for a device-built plan (its 8-row kernels walk their records), whose
 // walking expand sums at most this many partials for pools of rank above 32
 constexpr int32_t kMaxWalkKpartsWide = 2;
@@ -78,9 +78,9 @@ constexpr int32_t walk_kparts_max(int32_t R) {
 }
 
 // K split of the wavefront tiles' MFMA shrink for a plan of nw such tiles
-// (bf16, R <= 64; else 1): grown while the launch has fewer than four
-// workgroups per compute unit and every part keeps one full load batch for
-// each of the workgroup's waves.
+// (bf16, R <= 64; else 1): the split that leaves the least work on the
+// busiest compute unit, with at most four workgroups per compute unit and one
+// full load batch per wave in every part.
 int32_t wave_ksplit(const Geo& g, int64_t nw);
 // K split of the 64-row MFMA tiles' shrink for a plan of nm such tiles: doubled
 // while the launch has fewer than two workgroups per compute unit and every

@@ -2,6 +2,8 @@
 is covered exactly once by the shrink tiles and once by the expand tiles, each
 tile holds consecutive rows of one adapter, and the records carry the tokens
 the metadata builder assigns to those rows."""
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -126,17 +128,23 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0, slot_ranks=None):
         while want_split < top and wgs * want_split < 512 and ksteps // (2 * want_split) >= 4:
             want_split *= 2
     assert p["ksplit"] == want_split
-    # K split of the wavefront tiles (bf16, R <= 64): grown while the launch has
-    # < 1024 workgroups and each part keeps one load batch (4 waves x CB chunks
-    # of 32; CB = 8, 6, 4 for R <= 16, 32, 64), up to 8 (R <= 16) or 4 parts
+    # K split of the wavefront tiles (bf16, R <= 64): of the splits k <= 8 that
+    # keep <= 1024 workgroups and one load batch per part (4 waves x CB chunks
+    # of 32; CB = 8, 6, 4 for R <= 16, 32, 64), the one with the least work on
+    # the busiest of 256 compute units, ceil(wgs k / 256) / k (fewest parts on
+    # a tie)
     want_wave = 1
     if desc.dtype == _lib.LORA_BF16 and p["wave_tiles"] and R <= 64:
         cb = 8 if R <= 16 else 6 if R <= 32 else 4
         nk = -(-desc.in_features // 32)
         wgs = p["wave_tiles"] * desc.num_slices
-        top = MAX_KSPLIT if R <= 16 else 4
-        while want_wave < top and wgs * want_wave < 1024 and nk // (want_wave + 1) >= 4 * cb:
-            want_wave += 1
+        best = None
+        for k in range(1, MAX_KSPLIT + 1):
+            if k > 1 and (wgs * k > 1024 or nk // k < 4 * cb):
+                break
+            load = Fraction(-(-wgs * k // 256), k)
+            if best is None or load < best:
+                best, want_wave = load, k
     assert p["ksplit_wave"] == want_wave and p["reserved"] == 0
     assert p["image_bytes"] + p["image_offset"] <= L.lora_apply_host_meta_bytes(desc, ids.size)
     return p
