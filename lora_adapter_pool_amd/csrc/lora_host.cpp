@@ -362,10 +362,25 @@ int32_t mfma_ksplit(const Geo& g, int64_t nm) {
     const int64_t wgs = nm * g.S * ((g.R + 63) / 64);
     const int64_t ksteps = (g.K + 63) / 64;
     const int32_t top = mfma_ksplit_max(g);
-    while (ksplit < top && wgs * ksplit < 512 && ksteps / (2 * ksplit) >= 4) ksplit *= 2;
-    if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1, 2, 4 or 8
+    // a workgroup's rate is bounded by what its compute unit can pull, so the
+    // time follows the compute unit with the most workgroups: ceil(wgs k /
+    // kComputeUnits) workgroups of 1/k of a tile's K each.  Of the splits
+    // that start below 512 workgroups (k - 1 parts of each tile fewer than
+    // 512) and keep at least 4 K steps per part, take the one with the least
+    // such load, the most parts on a tie (shorter workgroups)
+    int64_t best_num = -1, best_den = 1;
+    for (int32_t k = 1; k <= top; ++k) {
+      if (k > 1 && (wgs * (k - 1) >= 512 || ksteps / k < 4)) break;
+      const int64_t num = (wgs * k + kComputeUnits - 1) / kComputeUnits;  // load num / k
+      if (best_num < 0 || num * best_den <= best_num * k) {
+        best_num = num;
+        best_den = k;
+        ksplit = k;
+      }
+    }
+    if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1 .. top
       const long o = std::strtol(e, nullptr, 10);
-      if ((o == 1 || o == 2 || o == 4 || o == 8) && o <= top) ksplit = (int32_t)o;
+      if (o >= 1 && o <= top) ksplit = (int32_t)o;
     }
   }
   return ksplit;

@@ -82,9 +82,10 @@ constexpr int32_t walk_kparts_max(int32_t R) {
 // busiest compute unit, with at most four workgroups per compute unit and one
 // full load batch per wave in every part.
 int32_t wave_ksplit(const Geo& g, int64_t nw);
-// K split of the 64-row MFMA tiles' shrink for a plan of nm such tiles: doubled
-// while the launch has fewer than two workgroups per compute unit and every
-// part keeps four 64-wide K steps, up to mfma_ksplit_max(g).
+// K split of the 64-row MFMA tiles' shrink for a plan of nm such tiles: the
+// split that leaves the least work on the busiest compute unit (the most
+// parts on a tie), among those up to mfma_ksplit_max(g) that start below 512
+// workgroups and keep four 64-wide K steps per part.
 int32_t mfma_ksplit(const Geo& g, int64_t nm);
 // most partials that split may use for this pool: LORA_PLAN_MAX_KSPLIT_MFMA
 // for R <= 32, LORA_PLAN_MAX_KSPLIT_MFMA_WIDE above

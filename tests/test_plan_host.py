@@ -118,15 +118,22 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0, slot_ranks=None):
             want_wave += -(-ln // WAVE_ROWS)
     assert (p["wave_tiles"], p["mfma_tiles"]) == (want_wave, want_mfma)
     assert p["image_bytes"] == 4 * (p["off_mfma"] + 4 * p["mfma_tiles"])
-    # K split: doubled while the MFMA shrink has < 512 workgroups and each
-    # split keeps >= 4 steps of 64, up to 8 for pools of rank <= 32, else 4
+    # K split of the MFMA shrink: of the splits k up to 8 (rank <= 32, else 4)
+    # with wgs (k - 1) < 512 and >= 4 steps of 64 per part, the one with the
+    # least work on the busiest of 256 compute units, ceil(wgs k / 256) / k,
+    # the most parts on a tie
     want_split = 1
     if p["mfma_tiles"]:
         wgs = p["mfma_tiles"] * desc.num_slices * -(-R // 64)
         ksteps = -(-desc.in_features // 64)
         top = MAX_KSPLIT_MFMA if R <= 32 else MAX_KSPLIT_MFMA_WIDE
-        while want_split < top and wgs * want_split < 512 and ksteps // (2 * want_split) >= 4:
-            want_split *= 2
+        best = None
+        for k in range(1, top + 1):
+            if k > 1 and (wgs * (k - 1) >= 512 or ksteps // k < 4):
+                break
+            load = Fraction(-(-wgs * k // 256), k)
+            if best is None or load <= best:
+                best, want_split = load, k
     assert p["ksplit"] == want_split
     # K split of the wavefront tiles (bf16, R <= 64): of the splits k <= 8 that
     # keep <= 1024 workgroups and one load batch per part (4 waves x CB chunks
