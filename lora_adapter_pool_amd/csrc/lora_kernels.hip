@@ -1401,12 +1401,23 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
 __device__ __forceinline__ int dma_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 constexpr int kDmaShrinkMaxK = 8192;
 
-// (the body takes its workgroup index bid, its rank block rblk and the three
-// stages, 16-byte aligned LDS arrays of kDmaStage elements, so that a combined
+// A launch of at most one workgroup per compute unit takes four stages
+// instead, loads three steps ahead: a lone workgroup's loads in flight set
+// its compute unit's rate (a 3 967-token prefill shrink, 195 workgroups:
+// 14.3 -> 12.5 us; the 4096-token rank-64 decode shrink, 248: 12.2 -> 10.7
+// us), while where units hold two workgroups three stages keep enough in
+// flight (the 8 772-token prefill shrink, 435 workgroups: 20.8 -> 21.8 us
+// with four; gate_up, 618: 27.3 -> 30.3 us).
+// (the body takes its workgroup index bid, its rank block rblk and the
+// stages, 16-byte aligned LDS arrays of kDmaStage elements: st_0, st_1, st_2
+// for three, NST consecutive ones from st_0 above that, so that a combined
 // launch can run it beside the 8-row tile shrink)
 constexpr int kDmaStage = 2 * 64 * 64;  // one stage: the x tile, then the adapter tile
+// s_waitcnt operand: at most n vector memory operations and no LDS one
+// outstanding (vmcnt in bits 3:0 and 15:14, expcnt 7 = no wait)
+constexpr int vm_wait_lgkm0(int n) { return ((n >> 4) & 3) << 14 | 0x70 | (n & 15); }
 
-template <int MODE>
+template <int MODE, int NST = 3>
 __device__ __forceinline__ void shrink_mfma_dma_body(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ A,
                                                      float* __restrict__ v, const RowList& L,
@@ -1499,24 +1510,44 @@ __device__ __forceinline__ void shrink_mfma_dma_body(const uint16_t* __restrict_
     issue(st + 2, nxt);
     mma(cur);
   };
-  if (st0 < st1) {  // a split past the last K step leaves its partial at zero
-    issue(st0, st_0);
-    issue(st0 + 1, st_1);
-    for (int st = st0; st < st1; st += 6) {
-      step(st, st_0, st_2);
-      if (st + 1 >= st1) break;
-      step(st + 1, st_1, st_0);
-      if (st + 2 >= st1) break;
-      step(st + 2, st_2, st_1);
-      if (st + 3 >= st1) break;
-      step(st + 3, st_0, st_2);
-      if (st + 4 >= st1) break;
-      step(st + 4, st_1, st_0);
-      if (st + 5 >= st1) break;
-      step(st + 5, st_2, st_1);
+  if constexpr (NST == 3) {
+    if (st0 < st1) {  // a split past the last K step leaves its partial at zero
+      issue(st0, st_0);
+      issue(st0 + 1, st_1);
+      for (int st = st0; st < st1; st += 6) {
+        step(st, st_0, st_2);
+        if (st + 1 >= st1) break;
+        step(st + 1, st_1, st_0);
+        if (st + 2 >= st1) break;
+        step(st + 2, st_2, st_1);
+        if (st + 3 >= st1) break;
+        step(st + 3, st_0, st_2);
+        if (st + 4 >= st1) break;
+        step(st + 4, st_1, st_0);
+        if (st + 5 >= st1) break;
+        step(st + 5, st_2, st_1);
+      }
+      // every load has landed before the workgroup ends
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
-    // every load has landed before the workgroup ends
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  } else {
+    // the same with NST stages: wait until only the NST - 2 later steps' loads
+    // are outstanding, barrier, refill the stage step st - 1 read
+    static_assert(NST >= 4 && NST <= 6, "stages");
+    if (st0 < st1) {
+      for (int i = 0; i < NST - 1; ++i) issue(st0 + i, st_0 + i * kDmaStage);
+      int cur = 0;  // stage of step st
+      for (int st = st0; st < st1; ++st) {
+        __builtin_amdgcn_s_waitcnt(vm_wait_lgkm0(4 * (NST - 2)));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(st + NST - 1, st_0 + (cur == 0 ? NST - 1 : cur - 1) * kDmaStage);
+        mma(st_0 + cur * kDmaStage);
+        cur = cur == NST - 1 ? 0 : cur + 1;
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
   }
   // D layout: lane (grp, i16) holds rows 4 grp + j (j < 4) of rank column i16
   const int SR = g.S * g.R;
@@ -1535,14 +1566,14 @@ __device__ __forceinline__ void shrink_mfma_dma_body(const uint16_t* __restrict_
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256, 3) void shrink_mfma_dma_kernel(const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ A,
-                                                                float* __restrict__ v, RowList L,
-                                                                Geo g, int ksplit, int v_rows) {
-  __shared__ __align__(16) uint16_t st_0[kDmaStage], st_1[kDmaStage], st_2[kDmaStage];
-  shrink_mfma_dma_body<MODE>(x, A, v, L, g, ksplit, v_rows, xcd_remap(blockIdx.x, gridDim.x),
-                             blockIdx.y, st_0, st_1, st_2);
+template <int MODE, int NST>
+__global__ __launch_bounds__(256, NST == 3 ? 3 : 2) void shrink_mfma_dma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, float* __restrict__ v,
+    RowList L, Geo g, int ksplit, int v_rows) {
+  __shared__ __align__(16) uint16_t st[NST * kDmaStage];
+  shrink_mfma_dma_body<MODE, NST>(x, A, v, L, g, ksplit, v_rows,
+                                  xcd_remap(blockIdx.x, gridDim.x), blockIdx.y, st,
+                                  st + kDmaStage, st + 2 * kDmaStage);
 }
 
 // ------------------------------------------------------------ expand (MFMA)
@@ -2266,9 +2297,18 @@ static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, fl
   // decode 13.0 -> 11.2 us) and slower at K = 14336 (down 62.1 -> 66.3 us),
   // so wider K keeps the register-staged kernel
   if (g.K % 64 == 0 && g.K <= kDmaShrinkMaxK) {
-    hipLaunchKernelGGL(shrink_mfma_dma_kernel<MODE>, dim3(grid_of(tiles * g.S * ksplit), gy),
-                       dim3(256), 0, st, (const uint16_t*)x, (const uint16_t*)A, v, L, g, ksplit,
-                       v_rows);
+    // four stages when no compute unit gets a second workgroup
+    // (LORA_DMA_STAGES=3 or 4 overrides, for tuning)
+    bool four = tiles * g.S * ksplit * gy <= kComputeUnits;
+    if (const char* e = std::getenv("LORA_DMA_STAGES")) four = e[0] == '4';
+    if (four)
+      hipLaunchKernelGGL((shrink_mfma_dma_kernel<MODE, 4>),
+                         dim3(grid_of(tiles * g.S * ksplit), gy), dim3(256), 0, st,
+                         (const uint16_t*)x, (const uint16_t*)A, v, L, g, ksplit, v_rows);
+    else
+      hipLaunchKernelGGL((shrink_mfma_dma_kernel<MODE, 3>),
+                         dim3(grid_of(tiles * g.S * ksplit), gy), dim3(256), 0, st,
+                         (const uint16_t*)x, (const uint16_t*)A, v, L, g, ksplit, v_rows);
     return hip_check("shrink_mfma_dma launch");
   }
   hipLaunchKernelGGL(shrink_mfma_kernel<MODE>, dim3(grid_of(tiles * g.S * ksplit), gy), dim3(256),
