@@ -157,10 +157,16 @@ class Setup:
         self.v = torch.zeros((parts * max(rows, 1), S * R), dtype=torch.float32,
                              device="cuda")
         self.bytes_per_rep = per
-        # the arguments of every call, converted once: a step is one ctypes
-        # call, as a caller's serving loop would make it (numpy's `.ctypes`
-        # and torch's data_ptr() build objects on every access)
+        # the arguments of every call, converted once: a step is one call of
+        # the library's CPython binding, as a caller's serving loop would make
+        # it (numpy's `.ctypes` and torch's data_ptr() build objects on every
+        # access, and ctypes converts 14 arguments in about 1.6 us)
         self._desc_ref = ctypes.byref(self.desc)
+        self._desc_a = ctypes.addressof(self.desc)
+        from lora_adapter_pool_amd import _lib as LL
+        self._pc = LL.pycall()
+        self._fa = LL.entry_address("lora_apply")
+        self._fr = LL.entry_address("lora_apply_ranked")
         self._ids_p = self.ids.ctypes.data
         self._pre_p = self.pre.ctypes.data
         self._ranks_p = self.slot_ranks.ctypes.data if self.slot_ranks is not None else None
@@ -174,12 +180,11 @@ class Setup:
         torch.cuda.synchronize()
 
     def _apply(self, r, stage_ptr, stream_ptr):
-        lib = self._lib
         if self._ranks_p is None:
-            return lib.lora_apply(self._desc_ref, self.pA[r], self.pB[r], self.px[r], self.py[r],
-                                  self.T, self._ids_p, self._pre_p, 0, self._ws_p, self.ws_bytes,
-                                  stage_ptr, self.mh_bytes, stream_ptr)
-        return lib.lora_apply_ranked(self._desc_ref, self.pA[r], self.pB[r], self.px[r],
+            return self._pc.apply(self._fa, self._desc_a, self.pA[r], self.pB[r], self.px[r],
+                                  self.py[r], self.T, self._ids_p, self._pre_p, 0, self._ws_p,
+                                  self.ws_bytes, stage_ptr, self.mh_bytes, stream_ptr)
+        return self._pc.apply_ranked(self._fr, self._desc_a, self.pA[r], self.pB[r], self.px[r],
                                      self.py[r], self.T, self._ids_p, self._pre_p, 0,
                                      self._ranks_p, self._ws_p, self.ws_bytes, stage_ptr,
                                      self.mh_bytes, stream_ptr)
@@ -744,7 +749,12 @@ def stage_kernels(wl):
     if p["mfma_tiles"]:
         # whole 64-wide K steps up to K = 8192: tiles staged by direct loads to LDS
         dma = wl.in_features % 64 == 0 and wl.in_features <= 8192
-        out["shrink"].append("shrink_mfma_dma_kernel<2>" if dma else "shrink_mfma_kernel<2>")
+        # four LDS stages when the launch has at most one workgroup per compute
+        # unit (lora_apply's tile-list form)
+        grid = p["mfma_tiles"] * len(wl.out_features) * p["ksplit"] * -(-wl.max_lora_rank // 64)
+        stages = os.environ.get("LORA_DMA_STAGES")
+        nst = (4 if stages.startswith("4") else 3) if stages else 4 if grid <= 256 else 3
+        out["shrink"].append(f"shrink_mfma_dma_kernel<2, {nst}>" if dma else "shrink_mfma_kernel<2>")
         rows = wl.max_lora_rank <= 64 and wl.T * wl.O * 2 < 2 ** 31
         kp = 8 if p["ksplit"] > 4 else 4
         out["expand"].append(f"expand_mfma_rows_kernel<2, {kp}>" if rows else "expand_mfma_kernel<2>")

@@ -153,6 +153,37 @@ def lib() -> ctypes.CDLL:
     return h
 
 
+_pycall = None
+
+
+def pycall():
+    """The CPython binding of the per-call entry points (module _lora_call:
+    apply, apply_ranked, apply_device), built beside the library; raise if it
+    was not built.  Each function takes the entry point's address (see
+    entry_address) and then that entry point's arguments as Python ints."""
+    global _pycall
+    if _pycall is None:
+        try:
+            from . import _lora_call
+        except ImportError as e:
+            raise RuntimeError(
+                "the _lora_call binding is missing: build it with "
+                "`python -m lora_adapter_pool_amd.build`") from e
+        _pycall = _lora_call
+    return _pycall
+
+
+_addresses: dict = {}
+
+
+def entry_address(name: str) -> int:
+    """Address of an entry point of the loaded library (for pycall())."""
+    a = _addresses.get(name)
+    if a is None:
+        a = _addresses[name] = ctypes.cast(getattr(lib(), name), ctypes.c_void_p).value
+    return a
+
+
 def last_error() -> str:
     return lib().lora_last_error().decode("utf-8", "replace")
 
@@ -377,21 +408,21 @@ def lora_plan_apply(desc, x, A_pool, B_pool, y, T, plan, image, image_host=None,
 
 def lora_apply(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgmv_max_rank, ws,
                ws_bytes, meta_host, meta_host_bytes, stream=None) -> None:
-    _check(lib().lora_apply(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), _ptr(x), _ptr(y),
-                            int(T), _ptr(ids_host), _ptr(prefill_host), int(bgmv_max_rank),
-                            _ptr(ws), int(ws_bytes), _ptr(meta_host), int(meta_host_bytes),
-                            _stream(stream)))
+    _check(pycall().apply(entry_address("lora_apply"), ctypes.addressof(desc), _ptr(A_pool),
+                          _ptr(B_pool), _ptr(x), _ptr(y), int(T), _ptr(ids_host),
+                          _ptr(prefill_host), int(bgmv_max_rank), _ptr(ws), int(ws_bytes),
+                          _ptr(meta_host), int(meta_host_bytes), _stream(stream)))
 
 
 def lora_apply_ranked(desc, A_pool, B_pool, x, y, T, ids_host, prefill_host, bgmv_max_rank,
                       slot_ranks_host, ws, ws_bytes, meta_host, meta_host_bytes,
                       stream=None) -> None:
     """lora_apply with each slot's true rank (host int32[max_loras], 0 = max_lora_rank)."""
-    _check(lib().lora_apply_ranked(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), _ptr(x),
-                                   _ptr(y), int(T), _ptr(ids_host), _ptr(prefill_host),
-                                   int(bgmv_max_rank), _ptr(slot_ranks_host), _ptr(ws),
-                                   int(ws_bytes), _ptr(meta_host), int(meta_host_bytes),
-                                   _stream(stream)))
+    _check(pycall().apply_ranked(entry_address("lora_apply_ranked"), ctypes.addressof(desc),
+                                 _ptr(A_pool), _ptr(B_pool), _ptr(x), _ptr(y), int(T),
+                                 _ptr(ids_host), _ptr(prefill_host), int(bgmv_max_rank),
+                                 _ptr(slot_ranks_host), _ptr(ws), int(ws_bytes), _ptr(meta_host),
+                                 int(meta_host_bytes), _stream(stream)))
 
 
 def lora_merge_weights(desc, A_pool, B_pool, slot, slice_, W, W_out, stream=None) -> None:
@@ -409,9 +440,10 @@ def lora_apply_device(desc, A_pool, B_pool, x, y, T, ids, prefill, bgmv_max_rank
                       stream=None) -> None:
     """The delta path from device ids / prefill flags (device metadata and a
     device-built tile plan; graph-capturable)."""
-    _check(lib().lora_apply_device(ctypes.byref(desc), _ptr(A_pool), _ptr(B_pool), _ptr(x),
-                                   _ptr(y), int(T), _ptr(ids), _ptr(prefill), int(bgmv_max_rank),
-                                   _ptr(ws), int(ws_bytes), _stream(stream)))
+    _check(pycall().apply_device(entry_address("lora_apply_device"), ctypes.addressof(desc),
+                                 _ptr(A_pool), _ptr(B_pool), _ptr(x), _ptr(y), int(T), _ptr(ids),
+                                 _ptr(prefill), int(bgmv_max_rank), _ptr(ws), int(ws_bytes),
+                                 _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # LORA_NOALLOC_SCRATCH_BYTES

@@ -1,4 +1,5 @@
-"""Build liblora_pool.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Build liblora_pool.so (the C-ABI library) in-tree with hipcc for gfx950, and
+the CPython binding of its per-call entry points (_lora_call) with gcc.
 
 Usage: python -m lora_adapter_pool_amd.build   (or build_library() from Python)
 """
@@ -8,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+import sysconfig
 import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -75,9 +77,35 @@ def build_library(verbose: bool = False, jobs: int = 3) -> str:
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stdout)
         os.replace(out_tmp, LIB_PATH)
+        build_pycall(verbose)
         return LIB_PATH
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+PYCALL_SRC = os.path.join(CSRC, "lora_pycall.c")
+
+
+def pycall_path() -> str:
+    return os.path.join(PKG_DIR, "_lora_call" + sysconfig.get_config_var("EXT_SUFFIX"))
+
+
+def build_pycall(verbose: bool = False) -> str:
+    """The CPython binding of the per-call entry points (host code, gcc)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("gcc not found")
+    out = pycall_path()
+    tmp = out + ".tmp"
+    cmd = [cc, "-O2", "-std=gnu11", "-shared", "-fPIC", "-Wall", "-Werror",
+           f"-I{sysconfig.get_paths()['include']}", f"-I{INCLUDE}", PYCALL_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("gcc failed:\n" + r.stdout)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -2297,9 +2297,13 @@ static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, fl
   // decode 13.0 -> 11.2 us) and slower at K = 14336 (down 62.1 -> 66.3 us),
   // so wider K keeps the register-staged kernel
   if (g.K % 64 == 0 && g.K <= kDmaShrinkMaxK) {
-    // four stages when no compute unit gets a second workgroup
-    // (LORA_DMA_STAGES=3 or 4 overrides, for tuning)
-    bool four = tiles * g.S * ksplit * gy <= kComputeUnits;
+    // four stages when no compute unit gets a second workgroup, for tile
+    // lists (LORA_DMA_STAGES=3 or 4 overrides, for tuning).  The segments
+    // form compiles with a full drain of the loads after every step's barrier
+    // (a segment lookup's LDS array sits beside the stages), which leaves a
+    // deeper ring nothing to overlap: 34.1 -> 57.6 us with four on the
+    // prefill batch's 145 tiles
+    bool four = MODE == kList && tiles * g.S * ksplit * gy <= kComputeUnits;
     if (const char* e = std::getenv("LORA_DMA_STAGES")) four = e[0] == '4';
     if (four)
       hipLaunchKernelGGL((shrink_mfma_dma_kernel<MODE, 4>),

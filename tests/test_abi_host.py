@@ -308,6 +308,71 @@ def test_apply_ranked_validation_before_hip():
     assert _status(L.lora_apply_ranked, *with_(5, 0)) == 0  # T = 0: no-op
 
 
+def test_pycall_binding_matches_ctypes_before_hip():
+    """The CPython binding (_lora_call) of lora_apply, lora_apply_ranked and
+    lora_apply_device hands the same arguments to the same entry points as
+    ctypes: equal statuses and messages on every host-checked error; its own
+    argument errors raise before any call."""
+    lib = L.lib()
+    pc = _lib.pycall()
+    d = L.make_desc("bf16", 4, 16, 256, [256])
+    da = ctypes.addressof(d)
+    T = 6
+    ws_need = L.lora_apply_workspace_bytes(d, T)
+    mh_need = L.lora_apply_host_meta_bytes(d, T)
+    dws = L.lora_apply_device_workspace_bytes(d, T)
+    ids = np.array([0, 1, -1, 3, 2, 0], np.int32)
+    bad_ids = ids.copy()
+    bad_ids[3] = 4
+    ranks = np.array([8, 16, 0, 4], np.int32)
+    bad_ranks = np.array([8, 16, 17, 4], np.int32)
+    meta = _aligned_i32(mh_need // 4)
+    P = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+    # (T, ids, ranks, ws_bytes, meta_bytes, x): each fails on the host, before
+    # any GPU call, in every entry point it is passed to (the pointers are
+    # fake); the last one only in lora_apply_ranked
+    cases = [(-1, ids, ranks, ws_need, mh_need, FAKE), (T, bad_ids, ranks, ws_need, mh_need, FAKE),
+             (T, ids, ranks, ws_need - 1, mh_need, FAKE), (T, ids, ranks, ws_need, mh_need - 4, FAKE),
+             (T, ids, ranks, ws_need, mh_need, FAKE + 2), (T, None, ranks, ws_need, mh_need, FAKE),
+             (T, ids, bad_ranks, ws_need, mh_need, FAKE)]
+    for k, (t, i, r, wb, mb, x) in enumerate(cases):
+        args = (FAKE, FAKE, x, FAKE + 64, t, P(i), None, 0)
+        tail = (FAKE, wb, P(meta), mb, 0)
+        if k < len(cases) - 1:
+            want = lib.lora_apply(ctypes.byref(d), *args, *tail)
+            msg = L.last_error()
+            assert pc.apply(_lib.entry_address("lora_apply"), da, *args, *tail) == want < 0
+            assert L.last_error() == msg
+        want = lib.lora_apply_ranked(ctypes.byref(d), *args, P(r), *tail)
+        msg = L.last_error()
+        assert pc.apply_ranked(_lib.entry_address("lora_apply_ranked"), da, *args, P(r),
+                               *tail) == want < 0
+        assert L.last_error() == msg
+        # (the device path reads ids on the GPU: a workspace one byte short
+        # keeps every case on the host)
+        dargs = (FAKE, FAKE, x, FAKE + 64, t, P(i), None, 0, FAKE, dws - 1)
+        want = lib.lora_apply_device(ctypes.byref(d), *dargs, 0)
+        msg = L.last_error()
+        got = pc.apply_device(_lib.entry_address("lora_apply_device"), da, *dargs, 0)
+        assert got == want < 0 and L.last_error() == msg
+    # T = 0 is a no-op through both
+    assert pc.apply(_lib.entry_address("lora_apply"), da, FAKE, FAKE, FAKE, FAKE + 64, 0, None,
+                    None, 0, FAKE, ws_need, P(meta), mh_need, 0) == 0
+    # a NULL descriptor (None or 0) reaches the entry point as NULL
+    assert pc.apply(_lib.entry_address("lora_apply"), None, FAKE, FAKE, FAKE, FAKE, T, P(ids),
+                    None, 0, FAKE, ws_need, P(meta), mh_need, 0) == _lib.LORA_E_ARG
+    assert "NULL" in L.last_error()
+    # the binding's own checks: argument count, int32 range, entry address
+    with pytest.raises(TypeError):
+        pc.apply(_lib.entry_address("lora_apply"), da, FAKE)
+    with pytest.raises(OverflowError):
+        pc.apply(_lib.entry_address("lora_apply"), da, FAKE, FAKE, FAKE, FAKE, 1 << 31, P(ids),
+                 None, 0, FAKE, ws_need, P(meta), mh_need, 0)
+    with pytest.raises(ValueError):
+        pc.apply(0, da, FAKE, FAKE, FAKE, FAKE, T, P(ids), None, 0, FAKE, ws_need, P(meta),
+                 mh_need, 0)
+
+
 def test_merge_validation_before_hip():
     """lora_merge_weights rejects bad slots, slices, ranks, alignment and
     overlapping buffers on the host, before any GPU call."""
