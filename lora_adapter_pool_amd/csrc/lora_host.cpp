@@ -356,7 +356,7 @@ int32_t mfma_ksplit_max(const Geo& g) {
   return g.R > 32 ? LORA_PLAN_MAX_KSPLIT_MFMA_WIDE : LORA_PLAN_MAX_KSPLIT_MFMA;
 }
 
-int32_t mfma_ksplit(const Geo& g, int64_t nm) {
+int32_t mfma_ksplit(const Geo& g, int64_t nm, bool four_stages) {
   int32_t ksplit = 1;
   if (nm > 0) {
     const int64_t wgs = nm * g.S * ((g.R + 63) / 64);
@@ -369,15 +369,24 @@ int32_t mfma_ksplit(const Geo& g, int64_t nm) {
     // 512) and keep at least 4 K steps per part, take the one with the least
     // such load, the most parts on a tie (shorter workgroups)
     int64_t best_num = -1, best_den = 1;
+    int32_t lone = 0;  // the most parts of a tie at one workgroup per compute unit
     for (int32_t k = 1; k <= top; ++k) {
       if (k > 1 && (wgs * (k - 1) >= 512 || ksteps / k < 4)) break;
       const int64_t num = (wgs * k + kComputeUnits - 1) / kComputeUnits;  // load num / k
+      if (best_num >= 0 && num * best_den < best_num * k) lone = 0;  // a better load
       if (best_num < 0 || num * best_den <= best_num * k) {
         best_num = num;
         best_den = k;
         ksplit = k;
+        if (wgs * k <= kComputeUnits) lone = k;
       }
     }
+    // where the DMA-staged shrink runs four stages at one workgroup per unit,
+    // such a split beats a tie at two workgroups per unit, and its expand sums
+    // fewer partials (the 4096-row rank-16 decode: K split 8 -> 4, kernels
+    // 28.0 -> 27.0 us); at three per unit the concurrent workgroups win
+    // (gate_up: split 1 against 3, shrink 30.4 against 27.7 us)
+    if (four_stages && lone > 0 && wgs * ksplit <= 2 * kComputeUnits) ksplit = lone;
     if (const char* e = std::getenv("LORA_MFMA_KSPLIT")) {  // tuning override: 1 .. top
       const long o = std::strtol(e, nullptr, 10);
       if (o >= 1 && o <= top) ksplit = (int32_t)o;
@@ -530,7 +539,7 @@ int32_t plan_core(const Geo& g, int32_t T, const int32_t* ids, const uint8_t* pr
     i = j;
   }
   const int64_t words = off_mfma + nm * LORA_PLAN_MFMA_WORDS;
-  const int32_t ksplit = mfma_ksplit(g, nm);
+  const int32_t ksplit = mfma_ksplit(g, nm, g.K % 64 == 0 && g.K <= kDmaShrinkMaxK);
   const int32_t ksplit_wave = wave_ksplit(g, nw);
   if (words > sl.image_max_words)  // cannot happen: the bounds above hold for any batch
     return fail(LORA_E_WORKSPACE, "tile plan overflow (%lld words > %lld)", (long long)words,

@@ -85,8 +85,12 @@ int32_t wave_ksplit(const Geo& g, int64_t nw);
 // K split of the 64-row MFMA tiles' shrink for a plan of nm such tiles: the
 // split that leaves the least work on the busiest compute unit (the most
 // parts on a tie), among those up to mfma_ksplit_max(g) that start below 512
-// workgroups and keep four 64-wide K steps per part.
-int32_t mfma_ksplit(const Geo& g, int64_t nm);
+// workgroups and keep four 64-wide K steps per part.  four_stages (a host
+// plan whose shrink is DMA-staged): a tie between at most one workgroup per
+// compute unit and at most two goes to the former.
+int32_t mfma_ksplit(const Geo& g, int64_t nm, bool four_stages = false);
+// Widest K of the DMA-staged 64-row MFMA shrink (K a multiple of 64).
+constexpr int32_t kDmaShrinkMaxK = 8192;
 // most partials that split may use for this pool: LORA_PLAN_MAX_KSPLIT_MFMA
 // for R <= 32, LORA_PLAN_MAX_KSPLIT_MFMA_WIDE above
 int32_t mfma_ksplit_max(const Geo& g);

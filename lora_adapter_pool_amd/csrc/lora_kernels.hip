@@ -1399,7 +1399,6 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(const uint16_t* __rest
 // waits for the wave's own LDS reads) publishes every wave's part and retires
 // the previous step's reads of the stage reloaded next.
 __device__ __forceinline__ int dma_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-constexpr int kDmaShrinkMaxK = 8192;
 
 // A launch of at most one workgroup per compute unit takes four stages
 // instead, loads three steps ahead: a lone workgroup's loads in flight set

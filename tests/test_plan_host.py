@@ -128,12 +128,20 @@ def _check_plan(desc, ids, prefill, bgmv_max_rank=0, slot_ranks=None):
         ksteps = -(-desc.in_features // 64)
         top = MAX_KSPLIT_MFMA if R <= 32 else MAX_KSPLIT_MFMA_WIDE
         best = None
+        loads = {}
         for k in range(1, top + 1):
             if k > 1 and (wgs * (k - 1) >= 512 or ksteps // k < 4):
                 break
-            load = Fraction(-(-wgs * k // 256), k)
+            load = loads[k] = Fraction(-(-wgs * k // 256), k)
             if best is None or load <= best:
                 best, want_split = load, k
+        # with the DMA-staged shrink (K a multiple of 64 up to 8192), a tie at
+        # most two workgroups per compute unit goes to the most parts of the
+        # tie at one workgroup per unit (that shrink then runs four stages)
+        K = desc.in_features
+        lone = [k for k, v in loads.items() if v == best and wgs * k <= 256]
+        if K % 64 == 0 and K <= 8192 and lone and wgs * want_split <= 512:
+            want_split = max(lone)
     assert p["ksplit"] == want_split
     # K split of the wavefront tiles (bf16, R <= 64): of the splits k <= 8 that
     # keep <= 1024 workgroups and one load batch per part (4 waves x CB chunks
