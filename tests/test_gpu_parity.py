@@ -304,6 +304,43 @@ def test_exact_integer_dma_shrink(K, R):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:3]}"
 
 
+@pytest.mark.parametrize("case", ["ragged_small", "prefill_full"])
+def test_dma_shrink_stages_bit_identical(case, monkeypatch):
+    """The DMA-staged 64-row shrink with three LDS stages and with four
+    (LORA_DMA_STAGES forces either; the plan takes four only for launches of
+    at most one workgroup per compute unit) writes the same v bit for bit:
+    the stages change when loads are issued, not the order of the sums.
+    Both forms run on a small ragged plan (four by default) and on the full
+    prefill batch (three by default), real-valued inputs."""
+    import torch
+    if case == "ragged_small":
+        wl = W.config_sgmv_prefill(seed=21, n_seqs=6, len_lo=17, len_hi=200, K=1024, O=264,
+                                   n_adapters=6, rank_choices=(8, 16, 32, 64),
+                                   max_lora_rank=64)
+    else:
+        wl = W.config_sgmv_prefill(seed=0)
+    pool = make_pool(wl)
+    plan, img, _ = L.lora_apply_plan(pool.desc, wl.ids, wl.prefill)
+    assert plan["mfma_tiles"] > 0 and wl.in_features % 64 == 0
+    image = torch.from_numpy(img).cuda()
+    xd = to_dev(wl.x, wl.dtype)
+    vs = []
+    for stages in ("3", "4"):
+        monkeypatch.setenv("LORA_DMA_STAGES", stages)
+        v = plan_v(plan, wl.num_slices, pool.R, float("nan"))
+        L.lora_plan_shrink(pool.desc, xd, pool.A, v, wl.T, plan, image)
+        torch.cuda.synchronize()
+        vs.append(v)
+    rows = plan["num_sgmv_rows"] + plan["num_bgmv_rows"]
+    a, b = (t[: plan["ksplit"] * rows] for t in vs)
+    assert not torch.isnan(a).any(), "a partial of v was not written"
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32)), "three and four stages differ"
+    yd = to_dev(wl.y_in, wl.dtype)
+    L.lora_plan_expand(pool.desc, vs[1], pool.B, yd, wl.T, plan, image)
+    torch.cuda.synchronize()
+    check_rows(wl, yd, label=f"{case} with four stages")
+
+
 def test_sgmv_equals_bgmv_exactly():
     import torch
     wl = _integer_workload("bf16", seed=1)
