@@ -178,6 +178,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int x = bid % kNumXcd, k = bid / kNumXcd;
   return x * q + min(x, r) + k;
 }
+// The same dealing in chunks of c consecutive logical ids, chunk j to XCD
+// j % 8 (ids past the last whole round of 8 chunks keep their place): a
+// bijection on [0, n) that spreads any prefix of the ids over every XCD.
+__device__ __forceinline__ int xcd_remap_chunks(int bid, int n, int c) {
+  if (c <= 0) return xcd_remap(bid, n);
+  const int n0 = n / (kNumXcd * c) * (kNumXcd * c);
+  if (bid >= n0) return bid;
+  const int x = bid % kNumXcd, k = bid / kNumXcd;
+  return ((k / c) * kNumXcd + x) * c + k % c;
+}
 
 // Segments mode: locate tile `f` (tiles of TM rows inside each segment whose
 // clamped length lies in [seg_min, seg_max], in segment order).  Called by
@@ -1972,7 +1982,14 @@ __global__ __launch_bounds__(256, 4) void expand_mfma_rows_kernel(
 // walks the 8-row records.  The walk's first record is loaded at the start,
 // so in a batch without 8-row tiles the check costs no round trip at the end.
 // Both bodies share one LDS array, with a barrier for LDS only between them
-// (the 64-row tile's last stores stay in flight).
+// (the 64-row tile's last stores stay in flight).  The 64-row workgroups are
+// dealt to the XCDs in chunks of kComboXcdChunk consecutive ids
+// (xcd_remap_chunks): the records past the real ones are empty, and one
+// contiguous range per XCD would leave them all to the last XCDs.  Measured
+// from device ids (both calls of the mixed MLP, 8 prefill sequences + 256
+// decode rows): 499 -> 434 us with chunks of 8 to 32; the prefill batch,
+// fused QKV and 64-row decode unchanged.
+constexpr int kComboXcdChunk = 16;
 template <int MODE>
 __device__ __forceinline__ void walk_first_word(const RowList& Lw, int bid, int nwg, int per,
                                                 int& w, bool& pre) {
@@ -1986,7 +2003,8 @@ __device__ __forceinline__ void walk_first_word(const RowList& Lw, int bid, int 
 template <int NT, int CB, bool DMA>
 __global__ __launch_bounds__(256, 3) void shrink_combo_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, float* __restrict__ v,
-    RowList Lm, RowList Lw, Geo g, int ksplit, int kparts, int v_rows, int nm, int nmp) {
+    RowList Lm, RowList Lw, Geo g, int ksplit, int kparts, int v_rows, int nm, int nmp,
+    int xchunk) {
   constexpr int kLds = DMA ? 3 * kDmaStage : kRegShrinkLds;  // uint16 elements
   static_assert(tile_shrink_lds<NT>() * 4 <= kLds * 2, "the tile shrink's LDS fits");
   static_assert(64 * kTileShrinkWaves == 256, "both bodies run 256 threads");
@@ -1997,7 +2015,7 @@ __global__ __launch_bounds__(256, 3) void shrink_combo_kernel(
   bool pre;
   walk_first_word<kListWalk>(Lw, bw, nwg, g.S * kparts, w0, pre);
   if (b < nmp) {
-    const int bid = xcd_remap(b, nmp);
+    const int bid = xcd_remap_chunks(b, nmp, xchunk);
     if (bid < nm) {
       if constexpr (DMA)
         shrink_mfma_dma_body<kList>(x, A, v, Lm, g, ksplit, v_rows, bid, 0, lds, lds + kDmaStage,
@@ -2017,7 +2035,7 @@ template <int NKC, int KPR, int KPW>
 __global__ __launch_bounds__(256, 4) void expand_combo_kernel(
     const float* __restrict__ v, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
     RowList Lm, RowList Lw, Geo g, Chunks chm, Chunks gr, Chunks chw, int ksplit, int kparts,
-    int v_rows, int cpw, int nm, int nmp) {
+    int v_rows, int cpw, int nm, int nmp, int xchunk) {
   static_assert(tile_expand_lds<NKC>() <= kExpandRowsLds, "the tile expand's LDS fits");
   static_assert(64 * kTileExpandWaves == 256, "both bodies run 256 threads");
   __shared__ __align__(16) uint16_t lds[kExpandRowsLds];
@@ -2028,7 +2046,7 @@ __global__ __launch_bounds__(256, 4) void expand_combo_kernel(
   bool pre;
   walk_first_word<kListWalk>(Lw, bw, nwg, chw.total, w0, pre);
   if (b < nmp) {
-    const int bid = xcd_remap(b, nmp);
+    const int bid = xcd_remap_chunks(b, nmp, xchunk);
     if (bid < nm)
       expand_mfma_rows_body<kList, KPR>(v, B, y, Lm, g, chm, gr, ksplit, v_rows, cpw, bid, lds,
                                         s_tok);
@@ -2554,7 +2572,7 @@ static int32_t launch_shrink_combo_k(const Geo& g, const void* x, const void* A,
   // every workgroup walks the 8-row records after its 64-row tile (if any)
   hipLaunchKernelGGL((shrink_combo_kernel<NT, CB, DMA>), dim3((unsigned)std::max(nmp, nw)),
                      dim3(256), 0, st, (const uint16_t*)x, (const uint16_t*)A, v, Lm, Lw, g,
-                     p.ksplit, p.ksplit_wave, p.num_rows, (int)nm, (int)nmp);
+                     p.ksplit, p.ksplit_wave, p.num_rows, (int)nm, (int)nmp, kComboXcdChunk);
   return hip_check("shrink_combo launch");
 }
 
@@ -2603,7 +2621,8 @@ static int32_t launch_expand_combo_k(const Geo& g, const float* v, const void* B
   // every workgroup walks the 8-row records after its 64-row tile (if any)
   hipLaunchKernelGGL((expand_combo_kernel<NKC, KPR, KPW>), dim3((unsigned)std::max(nmp, nw)),
                      dim3(256), 0, st, v, (const uint16_t*)B, (uint16_t*)y, Lm, Lw, g, chm, gr,
-                     chw, p.ksplit, p.ksplit_wave, p.num_rows, cpw, (int)nm, (int)nmp);
+                     chw, p.ksplit, p.ksplit_wave, p.num_rows, cpw, (int)nm, (int)nmp,
+                     kComboXcdChunk);
   return hip_check("expand_combo launch");
 }
 
