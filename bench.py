@@ -750,7 +750,7 @@ def stage_kernels(wl):
         # whole 64-wide K steps up to K = 8192: tiles staged by direct loads to LDS
         dma = wl.in_features % 64 == 0 and wl.in_features <= 8192
         # four LDS stages when the launch has at most one workgroup per compute
-        # unit (lora_apply's tile-list form)
+        # unit
         grid = p["mfma_tiles"] * len(wl.out_features) * p["ksplit"] * -(-wl.max_lora_rank // 64)
         stages = os.environ.get("LORA_DMA_STAGES")
         nst = (4 if stages.startswith("4") else 3) if stages else 4 if grid <= 256 else 3

@@ -255,6 +255,51 @@ __device__ __forceinline__ bool find_tile(const RowList& L, int f, int& r0, int&
   return true;
 }
 
+// The same lookup within one wavefront (every wavefront of the workgroup
+// computes it for itself, 64 segments per pass, a shuffle prefix sum and a
+// ballot): no LDS and no barrier.  The 64-row MFMA kernels use it: beside
+// the block-wide lookup's LDS array the compiler drains every outstanding
+// load before each LDS read of the DMA-staged shrink's loop, which cannot
+// then keep loads in flight across its steps.
+template <int TM>
+__device__ __forceinline__ bool find_tile_wave(const RowList& L, int f, int& r0, int& cnt,
+                                               int& sid) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int c0 = 0; c0 < L.num_segs; c0 += 64) {
+    const int gi = c0 + lane;
+    int nt = 0, st = 0, ln = 0, id = -1;
+    if (gi < L.num_segs) {
+      st = L.seg_starts[gi];
+      ln = L.seg_lens[gi];
+      id = L.seg_ids[gi];
+      if (st >= 0 && st < L.num_rows && ln > 0) {
+        ln = min(ln, L.num_rows - st);
+        if (ln >= L.seg_min && ln <= L.seg_max) nt = (ln + TM - 1) / TM;
+      }
+    }
+    int inc = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    const int excl = base + inc - nt;
+    const unsigned long long hit = __ballot(nt > 0 && f >= excl && f < excl + nt);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      const int j = f - __shfl(excl, src, 64);
+      r0 = __builtin_amdgcn_readfirstlane(__shfl(st, src, 64) + j * TM);
+      cnt = __builtin_amdgcn_readfirstlane(min(TM, __shfl(ln, src, 64) - j * TM));
+      sid = __builtin_amdgcn_readfirstlane(__shfl(id, src, 64));
+      return true;
+    }
+    base += __shfl(inc, 63, 64);
+    if (f < base) break;
+  }
+  return false;
+}
+
 // How a kernel finds its tile: device segments, device rows with ids, the
 // plan's device image, or records passed by value in two capacities.
 // kListWalk: the plan's device image, like kList, for a plan whose record
@@ -1221,10 +1266,7 @@ __device__ __forceinline__ bool mfma_tile(const RowList& L, int f, int& r0, int&
     r0 = __builtin_amdgcn_readlane(w, 2);
     tok0 = __builtin_amdgcn_readlane(w, 3);
   } else {
-    if (!find_tile<TMR>(L, f, r0, cnt, sid)) return false;
-    r0 = __builtin_amdgcn_readfirstlane(r0);
-    cnt = __builtin_amdgcn_readfirstlane(cnt);
-    sid = __builtin_amdgcn_readfirstlane(sid);
+    if (!find_tile_wave<TMR>(L, f, r0, cnt, sid)) return false;
   }
   cnt = min(cnt, TMR);
   return true;
@@ -2314,13 +2356,9 @@ static int32_t launch_shrink_mfma(const Geo& g, const void* x, const void* A, fl
   // decode 13.0 -> 11.2 us) and slower at K = 14336 (down 62.1 -> 66.3 us),
   // so wider K keeps the register-staged kernel
   if (g.K % 64 == 0 && g.K <= kDmaShrinkMaxK) {
-    // four stages when no compute unit gets a second workgroup, for tile
-    // lists (LORA_DMA_STAGES=3 or 4 overrides, for tuning).  The segments
-    // form compiles with a full drain of the loads after every step's barrier
-    // (a segment lookup's LDS array sits beside the stages), which leaves a
-    // deeper ring nothing to overlap: 34.1 -> 57.6 us with four on the
-    // prefill batch's 145 tiles
-    bool four = MODE == kList && tiles * g.S * ksplit * gy <= kComputeUnits;
+    // four stages when no compute unit gets a second workgroup
+    // (LORA_DMA_STAGES=3 or 4 overrides, for tuning)
+    bool four = tiles * g.S * ksplit * gy <= kComputeUnits;
     if (const char* e = std::getenv("LORA_DMA_STAGES")) four = e[0] == '4';
     if (four)
       hipLaunchKernelGGL((shrink_mfma_dma_kernel<MODE, 4>),
