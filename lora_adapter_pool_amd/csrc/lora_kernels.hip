@@ -2391,6 +2391,45 @@ static Chunks make_groups(const Geo& g, int cpw) {
   return c;
 }
 
+// Column chunks per workgroup of the 64-row expand (R <= 64) for `tiles`
+// records whose v has `ksplit` partials: the count, 1 to 8, that leaves the
+// least on the busiest compute unit (the most chunks on a tie), ceil(wgs /
+// 256) workgroups of
+//   v partials (64 rows x R x 4 bytes each) + cpw x (the chunk's y read and
+//   written, 64 x 128 elements each way, and its B block, 128 x R)
+//   + 192 KB, the fixed cost of a workgroup (its prologue's round trips),
+// a workgroup alone on its compute unit counted 1.25 times (it pulls more
+// slowly than several together).  Fitted to measurements of every count
+// (expand, us): the 8 772-token prefill takes 7 (38.3 against 38.8 at 5,
+// 40.0 at 8); a 3 967-token prefill 5 (19.9; 20.6 at 3, 22.6 at 4); the
+// 4096-row decodes 8 (rank 16: 16.7, 16.2 at 4, 17.7 at 2; rank 64: 17.4,
+// 18.2 at 4, 21.8 at 2); gate_up 8 (191; 194 at 7, 198 at 5); down 8 (36.1;
+// 37.7 at 5, 39.7 at 4).
+static int expand_cpw(const Geo& g, int64_t tiles, int ksplit) {
+  const int64_t eb = elem_bytes(g.dtype);
+  const int64_t vbytes = (int64_t)kMfmaTileRows * g.R * 4 * ksplit;
+  const int64_t cbytes = (int64_t)kMfmaTileRows * kExpandMfmaCols * eb * 2 +
+                         (int64_t)kExpandMfmaCols * g.R * eb;
+  constexpr int64_t kFixed = 192 * 1024;
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int cpw = 1; cpw <= 8; ++cpw) {
+    const int64_t wgs = tiles * make_groups(g, cpw).total;
+    const int64_t per_cu = (wgs + kComputeUnits - 1) / kComputeUnits;
+    int64_t cost = per_cu * (vbytes + cpw * cbytes + kFixed);
+    if (wgs <= kComputeUnits) cost = cost * 5 / 4;
+    if (best_cost < 0 || cost <= best_cost) {  // a tie goes to fewer workgroups
+      best_cost = cost;
+      best = cpw;
+    }
+  }
+  if (const char* e = std::getenv("LORA_EXPAND_MFMA_CPW")) {  // tuning / test override
+    const long o = std::strtol(e, nullptr, 10);
+    if (o >= 1 && o <= 8) best = (int)o;
+  }
+  return best;
+}
+
 template <int MODE>
 static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, void* y,
                                   const RowList& L, int64_t tiles, int ksplit, int v_rows,
@@ -2401,14 +2440,7 @@ static int32_t launch_expand_mfma(const Geo& g, const float* v, const void* B, v
   const Chunks ch = make_chunks(g, kExpandMfmaCols);
   if (tiles * ch.total > INT32_MAX) return fail(LORA_E_SHAPE, "batch too large for one launch");
   if (g.R <= 64 && (int64_t)g.T * g.O * 2 < (int64_t)kDropOffset) {
-    // chunks per workgroup: at most about one resident round of workgroups
-    // (four per compute unit, 1024), at most 8 chunks each
-    const int64_t work = tiles * ch.total;
-    int cpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, (work + 1023) / 1024));
-    if (const char* e = std::getenv("LORA_EXPAND_MFMA_CPW")) {  // tuning / test override
-      const long o = std::strtol(e, nullptr, 10);
-      if (o >= 1 && o <= 8) cpw = (int)o;
-    }
+    const int cpw = expand_cpw(g, tiles, ksplit);
     const Chunks gr = make_groups(g, cpw);
     if (ksplit > kMaxKsplitWide)  // R <= 32 (checked above)
       hipLaunchKernelGGL((expand_mfma_rows_kernel<MODE, kMaxKsplit>), dim3(grid_of(tiles * gr.total)),
@@ -2644,12 +2676,7 @@ static int32_t launch_expand_combo_k(const Geo& g, const float* v, const void* B
                                      hipStream_t st) {
   // the 64-row part as launch_expand_mfma lays it out
   const Chunks chm = make_chunks(g, kExpandMfmaCols);
-  const int64_t work = (int64_t)p.mfma_tiles * chm.total;
-  int cpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, (work + 1023) / 1024));
-  if (const char* e = std::getenv("LORA_EXPAND_MFMA_CPW")) {  // tuning / test override
-    const long o = std::strtol(e, nullptr, 10);
-    if (o >= 1 && o <= 8) cpw = (int)o;
-  }
+  const int cpw = expand_cpw(g, p.mfma_tiles, p.ksplit);
   const Chunks gr = make_groups(g, cpw);
   const Chunks chw = make_chunks(g, kTileExpandCols);
   const int64_t nm = (int64_t)p.mfma_tiles * gr.total;
