@@ -144,6 +144,22 @@ def test_entry_points_bf16(mode):
     check_rows(wl, y, label=f"entry points bf16 {mode}")
 
 
+def test_entry_points_many_segments():
+    """The grouped SGMV entry points with 150 segments (more than one pass of
+    the 64-row kernels' wavefront-local segment lookup, 64 segments a pass):
+    segments of 1 to 140 rows, so short ones go to the wavefront tiles and
+    long ones to 64-row MFMA tiles found past the first pass; against the
+    oracle on every row."""
+    wl = W.config_sgmv_prefill(seed=41, n_seqs=150, len_lo=1, len_hi=140, K=256, O=136,
+                               n_adapters=150, rank_choices=(8, 16), max_lora_rank=16)
+    pool = make_pool(wl)
+    y, _, _, m = run_entry_points(wl, pool, "sgmv")
+    nseg = int(m["seg_ids"].size)
+    long_segs = int(np.sum(m["seg_lens"] >= 16))
+    assert nseg > 128 and long_segs > 64, (nseg, long_segs)
+    check_rows(wl, y, label=f"{nseg} segments ({long_segs} on 64-row tiles)")
+
+
 # ------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("R", [24, 80, 128])
